@@ -1,0 +1,241 @@
+/*
+ * eagle.h - C interface of one EAGLE / EAGLE-2 draft-and-verify cycle at
+ * batch 1 on one AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute (the method, from the source pages):
+ *  - "Lesson 13.11 - EAGLE: Feature-Level Drafting for Faster Inference",
+ *    section "Speculative decoding in four moves": draft, verify the drafts in
+ *    one target pass, accept from the left while the draft equals the
+ *    target's greedy choice, correct with the target's token.
+ *  - same page, "The big idea: draft at the feature level" and "Resolving the
+ *    uncertainty by feeding back the token": the draft row pairs the target
+ *    feature f (the vector fed to the LM head) with the next token's
+ *    embedding, an FC maps [emb; f] (2H) to H, one decoder layer predicts
+ *    the next feature, and the target's frozen LM head gives probabilities.
+ *  - "EAGLE-2: Context-Aware Dynamic Draft Trees", sections "Path Value Ranks
+ *    Prefixes", "Global Reranking Separates Exploration from Verification",
+ *    "The Mask Preserves Tree Semantics in One Target Pass" and the actor
+ *    table in "Putting It Together": path value = product of draft
+ *    confidences (kept as a sum of logs), expand the top-k newest nodes,
+ *    rerank everything to the best m, flatten with an ancestry mask, verify.
+ *  - "05 - EAGLE 三代", section 2.3 (draft compute flow: features [B,S,H],
+ *    shifted tokens, one draft step per tree level), section 4.3 (EAGLE-3
+ *    fusion g = FC([l;m;h]) for verified rows, the draft's own output a for
+ *    later steps) and section 3 (the three engine options: branches per
+ *    level, tree depth, number of verified draft tokens).
+ *
+ * Conventions
+ *  - Batch 1. One context belongs to one host thread; all device work is
+ *    ordered on the stream given to eagle_load. Token ids are int32 in
+ *    [0, vocab). Positions are 0-based.
+ *  - Memory: the library allocates no device memory. The caller allocates
+ *    the three device buffers whose sizes eagle_query reports and keeps them
+ *    alive until eagle_free. Host pointers are only read during the call.
+ *  - Errors: every call returns an eagle_status. Argument, state and
+ *    capacity checks run on the host before any device work, so a rejected
+ *    call leaves the context unchanged. After EAGLE_E_HIP or EAGLE_E_DEVICE
+ *    the context is FAILED: only eagle_prefill (which resets it) and
+ *    eagle_free are accepted. eagle_last_error gives a message.
+ *  - Greedy (temperature 0) only: the committed stream equals plain greedy
+ *    decoding of the target (ties to the lowest token id).
+ */
+#ifndef EAGLE_H
+#define EAGLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum eagle_status {
+  EAGLE_OK = 0,
+  EAGLE_E_INVALID = 1,   /* bad argument or configuration */
+  EAGLE_E_STATE = 2,     /* call not allowed in the context's current state */
+  EAGLE_E_CAPACITY = 3,  /* would exceed max_ctx or a fixed limit below */
+  EAGLE_E_BUFFER = 4,    /* a caller buffer is missing or too small */
+  EAGLE_E_HIP = 5,       /* a HIP runtime call failed */
+  EAGLE_E_DEVICE = 6     /* a device-side check failed */
+} eagle_status;
+
+enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 };
+enum { EAGLE_HEAD_E1 = 0, EAGLE_HEAD_E3 = 1 };
+enum { EAGLE_TREE_DYNAMIC = 0, EAGLE_TREE_STATIC = 1 };
+
+#define EAGLE_MAX_STATIC 64   /* nodes of a static tree */
+#define EAGLE_MAX_DEPTH 16    /* draft passes per cycle */
+#define EAGLE_MAX_VERIFY 128  /* verify rows = 1 + budget */
+#define EAGLE_MAX_NODES 1024  /* generated nodes per cycle */
+#define EAGLE_MAX_TOPK 16     /* children per expanded row */
+
+/* Model and policy. Shapes follow the Llama layout: RMSNorm (gain tensors),
+ * rotate-half RoPE, GQA attention, SwiGLU FFN, untied LM head. */
+typedef struct eagle_config {
+  int32_t n_layers, hidden, n_heads, n_kv_heads, ffn, vocab;
+  float rope_base;             /* theta_i = rope_base^(-2i/head_dim) */
+  float rms_eps;               /* RMSNorm epsilon */
+  int32_t dtype;               /* EAGLE_F32 or EAGLE_BF16 (weights, KV, operands) */
+  int32_t head;                /* EAGLE_HEAD_E1 or EAGLE_HEAD_E3 */
+  int32_t feat_layers[3];      /* E3: target layers (0-based) fused as [l;m;h] */
+  int32_t tree;                /* EAGLE_TREE_DYNAMIC or EAGLE_TREE_STATIC */
+  int32_t topk;                /* children kept per expanded row (branching) */
+  int32_t expand;              /* dynamic: nodes expanded per level (0 = topk) */
+  int32_t depth;               /* draft passes per cycle = deepest node */
+  int32_t budget;              /* dynamic: kept nodes m (verify rows = 1 + m);
+                                  0 = plain greedy decode, one token per pass */
+  int32_t n_static;            /* static: node count (ignored when dynamic) */
+  int32_t static_parent[EAGLE_MAX_STATIC]; /* static: parent node, -1 = root;
+                                              breadth-first order */
+  int32_t static_rank[EAGLE_MAX_STATIC];   /* static: child rank in the
+                                              parent's draft top-k */
+  int32_t max_ctx;             /* capacity: prompt + generated tokens */
+  int32_t prefill_chunk;       /* rows per prefill pass (0 = 256) */
+} eagle_config;
+
+/* Sizes of the caller-owned device buffers, in bytes. */
+typedef struct eagle_sizes {
+  uint64_t weight_bytes;   /* every weight tensor, at eagle_tensor offsets */
+  uint64_t kv_bytes;       /* paged target KV (all layers) + draft KV */
+  uint64_t scratch_bytes;  /* activations, partial sums, tree and state */
+  int32_t n_tensors;       /* entries of the weight table */
+  int32_t verify_rows;     /* 1 + kept nodes */
+  int32_t max_nodes;       /* generated nodes per cycle */
+  int32_t kv_page;         /* slots per KV page */
+} eagle_sizes;
+
+/* Weight tensor kinds (one table entry each). */
+enum {
+  EAGLE_T_EMBED = 0,      /* [vocab, hidden] token embedding (shared) */
+  EAGLE_T_LM_HEAD = 1,    /* [vocab, hidden] LM head (shared) */
+  EAGLE_T_FINAL_NORM = 2, /* [hidden] fp32 gain */
+  EAGLE_T_ATTN_NORM = 3,  /* [hidden] fp32 gain (E3 draft: [2*hidden]) */
+  EAGLE_T_WQ = 4,         /* [n_heads*head_dim, in] */
+  EAGLE_T_WK = 5,         /* [n_kv_heads*head_dim, in] */
+  EAGLE_T_WV = 6,         /* [n_kv_heads*head_dim, in] */
+  EAGLE_T_WO = 7,         /* [hidden, n_heads*head_dim] */
+  EAGLE_T_FFN_NORM = 8,   /* [hidden] fp32 gain */
+  EAGLE_T_WGATE = 9,      /* [ffn, hidden] */
+  EAGLE_T_WUP = 10,       /* [ffn, hidden] */
+  EAGLE_T_WDOWN = 11,     /* [hidden, ffn] */
+  EAGLE_T_FC = 12         /* E1: [hidden, 2*hidden] on [emb; f];
+                             E3: [hidden, 3*hidden] on [l; m; h] */
+};
+enum { EAGLE_G_GLOBAL = 0, EAGLE_G_TARGET = 1, EAGLE_G_DRAFT = 2 };
+
+/* One weight tensor: row-major [rows, cols] at `offset` in the weight
+ * buffer. Matrices are stored as in y = x W^T (rows = outputs). Element
+ * type is the config dtype, except norm gains, which are always fp32. */
+typedef struct eagle_tensor {
+  int32_t kind;     /* EAGLE_T_* */
+  int32_t group;    /* EAGLE_G_* */
+  int32_t layer;    /* target layer index (0 for global and draft) */
+  int32_t dtype;    /* EAGLE_F32 or EAGLE_BF16 */
+  int64_t rows, cols;
+  uint64_t offset;  /* bytes from the start of the weight buffer */
+} eagle_tensor;
+
+/* Caller-owned device memory (hipMalloc'd or from a framework allocator). */
+typedef struct eagle_buffers {
+  void* weights;  uint64_t weight_bytes;
+  void* kv;       uint64_t kv_bytes;
+  void* scratch;  uint64_t scratch_bytes;
+} eagle_buffers;
+
+/* Host view of one drafted tree (eagle_draft_tree) or a caller-planted tree
+ * (eagle_verify). Rows are the verify rows: row 0 is the root (the last
+ * committed token); every other row's parent row is smaller than itself. */
+typedef struct eagle_tree {
+  int32_t n_rows;                      /* 1 + kept nodes */
+  int32_t token[EAGLE_MAX_VERIFY];
+  int32_t parent[EAGLE_MAX_VERIFY];    /* row index, -1 for row 0 */
+  int32_t depth[EAGLE_MAX_VERIFY];     /* 0 for row 0 */
+  float logv[EAGLE_MAX_VERIFY];        /* log path value (0 for row 0) */
+  int32_t node[EAGLE_MAX_VERIFY];      /* generated-node index, -1 for row 0 */
+  /* every generated node of the cycle, in generation order (output only) */
+  int32_t n_nodes;
+  int32_t node_token[EAGLE_MAX_NODES];
+  int32_t node_parent[EAGLE_MAX_NODES]; /* node index, -1 = child of the root */
+  int32_t node_depth[EAGLE_MAX_NODES];
+  float node_logv[EAGLE_MAX_NODES];
+  float node_logp[EAGLE_MAX_NODES];     /* the node's own draft log-prob */
+} eagle_tree;
+
+typedef struct eagle_stats {
+  int64_t cycles;                         /* verify passes */
+  int64_t committed;                      /* tokens committed (incl. prefill's) */
+  int64_t accept_hist[EAGLE_MAX_DEPTH + 1]; /* cycles by accepted length L */
+  double seconds;                         /* device time of the cycle loop */
+} eagle_stats;
+
+typedef struct eagle_ctx eagle_ctx;
+
+/* Sizes of the three device buffers for `cfg`; validates `cfg`.
+ * Pure host call. EAGLE_E_INVALID on a bad config. */
+eagle_status eagle_query(const eagle_config* cfg, eagle_sizes* out);
+
+/* Entry `index` (0 <= index < n_tensors) of the weight table of `cfg`.
+ * Pure host call. The caller writes each tensor at its offset. */
+eagle_status eagle_tensor_info(const eagle_config* cfg, int32_t index, eagle_tensor* out);
+
+/* Creates a context over caller-owned buffers (sizes >= eagle_query's) on
+ * HIP stream `hip_stream` (NULL = the default stream). The weights must be
+ * in place before eagle_prefill. Binds to the device current at this call.
+ * EAGLE_E_BUFFER if a buffer is NULL or too small. *out is a host object. */
+eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void* hip_stream,
+                        eagle_ctx** out);
+
+/* Starts a sequence: target prefill over prompt[0..n), the first committed
+ * token b = greedy choice after the prompt, and the draft's catch-up over
+ * the n (feature, next-token) pairs, which leaves the depth-1 candidates
+ * ready. Resets any earlier sequence. If first_token is not NULL the call
+ * synchronises the stream and writes b. EAGLE_E_CAPACITY if
+ * n + 1 > max_ctx. */
+eagle_status eagle_prefill(eagle_ctx* ctx, const int32_t* prompt, int32_t n,
+                           int32_t* first_token);
+
+/* Runs the draft passes and the rerank of one cycle (state READY ->
+ * DRAFTED). If `out` is not NULL the call synchronises and fills it. */
+eagle_status eagle_draft_tree(eagle_ctx* ctx, eagle_tree* out);
+
+/* Verifies the drafted tree (state DRAFTED), or `planted` when not NULL
+ * (state READY or DRAFTED; only n_rows, token and parent are read, rows must
+ * be in order with parent[r] < r, siblings with distinct tokens, n_rows <=
+ * 1 + budget, depth <= the config depth; token[0] is ignored and taken as
+ * the root). Target pass over the rows with the ancestry mask, greedy
+ * acceptance, KV compaction of the accepted path, and the draft catch-up.
+ * State -> READY. If out_tokens (capacity EAGLE_MAX_DEPTH + 1) or
+ * n_committed is not NULL the call synchronises and writes the L + 1
+ * tokens committed by this cycle. EAGLE_E_CAPACITY if the context could
+ * exceed max_ctx. */
+eagle_status eagle_verify(eagle_ctx* ctx, const eagle_tree* planted, int32_t* out_tokens,
+                          int32_t* n_committed);
+
+/* eagle_prefill, then cycles until at least max_new tokens are committed
+ * (the prefill's token is the first); writes exactly max_new tokens to out
+ * (capacity max_new) and their count to n_out. stats may be NULL. */
+eagle_status eagle_generate(eagle_ctx* ctx, const int32_t* prompt, int32_t n, int32_t max_new,
+                            int32_t* out, int32_t* n_out, eagle_stats* stats);
+
+/* Copies the committed tokens of the current sequence (prefill's first) to
+ * out (capacity cap); *n gets the total count. Synchronises. */
+eagle_status eagle_committed(eagle_ctx* ctx, int32_t* out, int32_t cap, int32_t* n);
+
+/* Debug read-back of the last target or draft pass, for parity tests:
+ * what = 0: target features f [rows, hidden] fp32 of the last target pass;
+ * what = 1: target logits [rows, vocab] fp32 of the last verify pass
+ *           (recorded only after eagle_set_debug(ctx, 1));
+ * what = 2: greedy choice g [rows] int32 of the last verify pass;
+ * what = 3: top-1 minus top-2 logit [rows] fp32 of the last verify pass.
+ * Copies min(bytes, available) and writes the row count. Synchronises. */
+eagle_status eagle_debug_read(eagle_ctx* ctx, int32_t what, void* host_dst, uint64_t bytes,
+                              int32_t* rows);
+eagle_status eagle_set_debug(eagle_ctx* ctx, int32_t on);
+
+void eagle_free(eagle_ctx* ctx);
+const char* eagle_last_error(const eagle_ctx* ctx);
+const char* eagle_status_string(eagle_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_H */

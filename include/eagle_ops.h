@@ -1,0 +1,62 @@
+/*
+ * eagle_ops.h - kernel-level entry points of libeagle.so on caller device
+ * pointers, for composing other pipelines and for parity testing of the
+ * kernels on their own. All calls enqueue on `stream` (NULL = default)
+ * and do not synchronise; pointers are device pointers unless stated.
+ * Element type `dtype` is EAGLE_F32 or EAGLE_BF16 (raw bf16 bits).
+ */
+#ifndef EAGLE_OPS_H
+#define EAGLE_OPS_H
+
+#include <stdint.h>
+
+#include "eagle.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { EAGLE_EPI_STORE = 0, EAGLE_EPI_ADD = 1, EAGLE_EPI_SWIGLU = 2 };
+
+/* Workspace bytes eagle_op_linear needs for this shape (may be 0). The
+ * workspace must be zero-filled before its first use; calls leave its
+ * counters at zero, so it can be reused without clearing. */
+uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K);
+
+/* Projection of M activation rows by a weight W, as in a Linear layer
+ * (y = x W^T; the decode/verify projections of the target and draft
+ * decoder layers, "Lesson 13.11 - EAGLE", section "The big idea").
+ *   x: [M, K] dtype, row-major. W: [N, K] dtype (EPI_SWIGLU: [2N, K], the
+ *   N gate rows then the N up rows).
+ *   EPI_STORE : y fp32 [M, N],  y  = x W^T
+ *   EPI_ADD   : y fp32 [M, N],  y += x W^T  (residual update)
+ *   EPI_SWIGLU: y dtype [M, N], y  = silu(x Wg^T) * (x Wu^T)
+ * Accumulation is fp32; summation order is fixed, so results repeat
+ * bit for bit. Requires K a multiple of 32 (bf16) or 16 (fp32), M >= 1.
+ * EAGLE_E_INVALID on bad sizes, EAGLE_E_BUFFER if the workspace is too
+ * small, EAGLE_E_HIP on a launch failure. */
+eagle_status eagle_op_linear(int32_t dtype, int32_t epilogue, const void* x, const void* w, void* y,
+                             int32_t M, int32_t N, int32_t K, void* workspace, uint64_t ws_bytes,
+                             void* stream);
+
+/* Workspace bytes of eagle_op_lmhead (k = 0 for the greedy variant). */
+uint64_t eagle_op_lmhead_workspace(int32_t M, int32_t V, int32_t k);
+
+/* LM head over M feature rows x [M, H] with W_lm [V, H] ("Lesson 13.11",
+ * section "The big idea": the LM head turns a feature into probabilities).
+ *   k = 0 (verify): out_ids[m] = argmax_v logits (lowest id on ties),
+ *          out_vals[m] = top-1 minus top-2 logit; logits [M, V] fp32 are
+ *          also written when `logits` is not NULL.
+ *   k >= 1 (draft): out_ids [M, k] = the k best ids by (logit desc, id asc),
+ *          out_vals [M, k] = their log-probabilities over the full vocabulary
+ *          (EAGLE-2 page, "Calibration Makes Acceptance Estimation Cheap":
+ *          the draft confidence is the draft probability).
+ * Requires H a multiple of 32 (bf16) or 16 (fp32), 1 <= k <= 16. */
+eagle_status eagle_op_lmhead(int32_t dtype, int32_t k, const void* x, const void* w_lm, int32_t M,
+                             int32_t V, int32_t H, int32_t* out_ids, float* out_vals, float* logits,
+                             void* workspace, uint64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_OPS_H */

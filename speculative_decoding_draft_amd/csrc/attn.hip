@@ -1,0 +1,505 @@
+// Attention over a paged KV cache with an ancestry bitmask, plus the small
+// per-row kernels around it (embedding, RMSNorm, RoPE + KV append, draft
+// input assembly, row gathers, KV compaction).
+//
+// bf16 attention (head_dim 128): one wave per (key chunk, query head, 16
+// query rows). S^T = K Q^T and O^T = V^T P^T run on 16x16x32 bf16 MFMA;
+// keys are loaded in an order that makes each lane's 8 scores exactly the
+// P^T operand of the PV product, so P never leaves registers. P is split
+// into bf16 hi + lo parts (two MFMAs) so it keeps ~16 mantissa bits. Chunks
+// are combined with their (max, sum) pairs in a second kernel.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int CHUNK = 128;
+
+template <typename T>
+__device__ __forceinline__ T* kv_ptr(const KVView& v, int slot, int sel, int h) {
+  const int pg = v.page_table[slot / v.page];
+  return (T*)v.base + (int64_t)pg * v.page_elems +
+         ((int64_t)(sel * v.n_kv + h) * v.page + slot % v.page) * v.d;
+}
+
+__device__ __forceinline__ bool row_sees(const RowVis& rv, int prehi, uint64_t m0, uint64_t m1,
+                                         int key) {
+  if (key >= rv.pre_lo && key < prehi) return true;
+  const int j = key - rv.tree_base;
+  if (j < 0 || j >= rv.n_tree) return false;
+  return ((j < 64 ? (m0 >> j) : (m1 >> (j - 64))) & 1ull) != 0;
+}
+
+struct AttnArgs {
+  const bf16_t* q;
+  KVView kv;
+  RowVis vis;
+  int M, nq, group;
+  float scale;
+  float* opart;
+  float* mlpart;
+};
+
+__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int D = 128;
+  __shared__ bf16_t vt[D][40];   // V^T block: [d][32 keys] (+8 pad)
+  const int chunk = blockIdx.x, h = blockIdx.y, rt = blockIdx.z;
+  const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
+  const int hk = h / a.group;
+  const int k0 = a.vis.pre_lo + chunk * CHUNK;
+  const int k1 = min(a.vis.key_end, k0 + CHUNK);
+  const int row = rt * 16 + lr;
+  const int rowc = min(row, a.M - 1);
+
+  uint4 qf[4];
+  const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qf[s] = ld16(qp + 32 * s);
+  const int prehi = a.vis.prehi[rowc];
+  const uint64_t mk0 = a.vis.mask[2 * rowc], mk1 = a.vis.mask[2 * rowc + 1];
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = k0; kb < k1; kb += 32) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int key = min(kb + 8 * (lr >> 2) + 4 * hh + (lr & 3), k1 - 1);
+      const bf16_t* kp = kv_ptr<bf16_t>(a.kv, key, 0, hk) + 8 * g;
+      sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Mma<bf16_t>::mma(ld16(kp + 32 * s), qf[s], sc[hh]);
+    }
+    float p[8];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = kb + 8 * g + 4 * hh + e;
+        const bool ok = key < k1 && row_sees(a.vis, prehi, mk0, mk1, key);
+        p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
+        bm = fmaxf(bm, p[4 * hh + e]);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float m_new = fmaxf(m_run, bm);
+    float alpha = 1.f, ps = 0.f;
+    if (m_new != -INFINITY) {
+      alpha = expf(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = expf(p[i] - m_new);
+        ps += p[i];
+      }
+      m_run = m_new;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = 0.f;
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = l_run * alpha + ps;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+
+    // V block (32 keys x 128) -> LDS, transposed
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int idx = it * 64 + lane;
+      const int kl = idx >> 4, dc = idx & 15;
+      const int key = min(kb + kl, k1 - 1);
+      const uint4 v = ld16(kv_ptr<bf16_t>(a.kv, key, 1, hk) + 8 * dc);
+      const bf16_t* vv = reinterpret_cast<const bf16_t*>(&v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vt[8 * dc + j][kl] = vv[j];
+    }
+    __syncthreads();
+    bf16_t ph[8], pl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ph[i] = f32_to_bf16(p[i]);
+      pl[i] = f32_to_bf16(p[i] - bf16_to_f32(ph[i]));
+    }
+    const uint4 phi = *reinterpret_cast<const uint4*>(ph);
+    const uint4 plo = *reinterpret_cast<const uint4*>(pl);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint4 va = *reinterpret_cast<const uint4*>(&vt[16 * dt + lr][8 * g]);
+      Mma<bf16_t>::mma(va, phi, o[dt]);
+      Mma<bf16_t>::mma(va, plo, o[dt]);
+    }
+  }
+  if (row < a.M) {
+    float* op = a.opart + (((int64_t)chunk * a.M + row) * a.nq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) op[16 * dt + 4 * g + e] = o[dt][e];
+    if (g == 0) {
+      float* ml = a.mlpart + (((int64_t)chunk * a.M + row) * a.nq + h) * 2;
+      ml[0] = m_run;
+      ml[1] = l_run;
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* opart, const float* mlpart,
+                                                           int n_chunks, int M, int nq, int d,
+                                                           T* out) {
+  const int r = blockIdx.x, h = blockIdx.y;
+  float gm = -INFINITY;
+  for (int c = 0; c < n_chunks; ++c) gm = fmaxf(gm, mlpart[(((int64_t)c * M + r) * nq + h) * 2]);
+  for (int j = threadIdx.x; j < d; j += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int c = 0; c < n_chunks; ++c) {
+      const float* ml = mlpart + (((int64_t)c * M + r) * nq + h) * 2;
+      if (ml[1] == 0.f) continue;
+      const float w = expf(ml[0] - gm);
+      den += w * ml[1];
+      num += w * opart[(((int64_t)c * M + r) * nq + h) * d + j];
+    }
+    out[((int64_t)r * nq + h) * d + j] = Elem<T>::from_f(num / den);
+  }
+}
+
+// fp32 path: one 64-lane wave per (row, head), keys in order, online softmax.
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, KVView kv, RowVis vis, int M,
+                                                      int nq, int group, int d, float scale,
+                                                      float* out) {
+  const int r = blockIdx.x, h = blockIdx.y, hk = h / group;
+  const int lane = threadIdx.x;
+  const int prehi = vis.prehi[r];
+  const uint64_t mk0 = vis.mask[2 * r], mk1 = vis.mask[2 * r + 1];
+  const float* qr = q + ((int64_t)r * nq + h) * d;
+  float qv[4], ov[4] = {0.f, 0.f, 0.f, 0.f};
+  const int nper = (d + 63) / 64;
+  for (int i = 0; i < nper; ++i) qv[i] = (lane + 64 * i < d) ? qr[lane + 64 * i] : 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int key = vis.pre_lo; key < vis.key_end; ++key) {
+    if (!row_sees(vis, prehi, mk0, mk1, key)) continue;
+    const float* kp = kv_ptr<float>(kv, key, 0, hk);
+    const float* vp = kv_ptr<float>(kv, key, 1, hk);
+    float part = 0.f;
+    for (int i = 0; i < nper; ++i)
+      if (lane + 64 * i < d) part += qv[i] * kp[lane + 64 * i];
+    const float s = wave_sum(part) * scale;
+    const float m_new = fmaxf(m_run, s);
+    const float alpha = expf(m_run - m_new);
+    const float pexp = expf(s - m_new);
+    l_run = l_run * alpha + pexp;
+    for (int i = 0; i < nper; ++i)
+      if (lane + 64 * i < d) ov[i] = ov[i] * alpha + pexp * vp[lane + 64 * i];
+    m_run = m_new;
+  }
+  for (int i = 0; i < nper; ++i)
+    if (lane + 64 * i < d) out[((int64_t)r * nq + h) * d + lane + 64 * i] = ov[i] / l_run;
+}
+
+// ---------------------------------------------------------------- rows
+template <typename T>
+__global__ void embed_kernel(const T* E, int H, const int32_t* tok, float* h) {
+  const int r = blockIdx.x;
+  const T* e = E + (int64_t)tok[r] * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) h[(int64_t)r * H + i] = Elem<T>::to_f(e[i]);
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* sh) {
+  // fixed-order block reduction (256 threads)
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) sh[threadIdx.x] = sh[threadIdx.x] + sh[threadIdx.x + o];
+    __syncthreads();
+  }
+  const float s = sh[0];
+  __syncthreads();
+  return s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, int64_t ldh, const float* gain,
+                                                      int K, float eps, T* out_t, int64_t ldo,
+                                                      float* out_f, int64_t ldf) {
+  __shared__ float sh[256];
+  const int r = blockIdx.x;
+  const float* x = h + (int64_t)r * ldh;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < K; i += 256) ss += x[i] * x[i];
+  ss = block_sum_256(ss, sh);
+  const float inv = 1.0f / sqrtf(ss / (float)K + eps);
+  for (int i = threadIdx.x; i < K; i += 256) {
+    const float v = x[i] * inv * gain[i];
+    if (out_f) out_f[(int64_t)r * ldf + i] = v;
+    out_t[(int64_t)r * ldo + i] = Elem<T>::from_f(v);
+  }
+}
+
+template <typename T>
+__global__ void cast_kernel(const float* h, int H, T* out) {
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    out[(int64_t)r * H + i] = Elem<T>::from_f(h[(int64_t)r * H + i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int nq, int nkv, int d,
+                                                      const int32_t* pos, const int32_t* slot,
+                                                      const float* cos_t, const float* sin_t,
+                                                      T* q_out, KVView kv) {
+  const int r = blockIdx.x;
+  const int half = d / 2;
+  const int width = (nq + 2 * nkv) * d;
+  const float* x = qkv + (int64_t)r * width;
+  const float* c = cos_t + (int64_t)pos[r] * half;
+  const float* s = sin_t + (int64_t)pos[r] * half;
+  const int sl = slot[r];
+  for (int idx = threadIdx.x; idx < (nq + nkv) * half; idx += blockDim.x) {
+    const int head = idx / half, i = idx % half;
+    const float* src = x + head * d;
+    const float x1 = src[i], x2 = src[i + half];
+    const float y1 = x1 * c[i] - x2 * s[i];
+    const float y2 = x2 * c[i] + x1 * s[i];
+    if (head < nq) {
+      T* dst = q_out + ((int64_t)r * nq + head) * d;
+      dst[i] = Elem<T>::from_f(y1);
+      dst[i + half] = Elem<T>::from_f(y2);
+    } else {
+      T* dst = kv_ptr<T>(kv, sl, 0, head - nq);
+      dst[i] = Elem<T>::from_f(y1);
+      dst[i + half] = Elem<T>::from_f(y2);
+    }
+  }
+  const float* vsrc = x + (nq + nkv) * d;
+  for (int idx = threadIdx.x; idx < nkv * d; idx += blockDim.x) {
+    const int head = idx / d, i = idx % d;
+    kv_ptr<T>(kv, sl, 1, head)[i] = Elem<T>::from_f(vsrc[idx]);
+  }
+}
+
+template <typename T>
+__global__ void draft_input_e1_kernel(const T* E, const int32_t* tok, const float* feat,
+                                      const int32_t* idx, int H, T* x) {
+  const int r = blockIdx.x;
+  const T* e = E + (int64_t)tok[r] * H;
+  const float* f = feat + (int64_t)idx[r] * H;
+  T* xr = x + (int64_t)r * 2 * H;
+  for (int i = threadIdx.x; i < H; i += blockDim.x) {
+    xr[i] = e[i];
+    xr[H + i] = Elem<T>::from_f(f[i]);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void draft_input_e3_kernel(const T* E, const int32_t* tok,
+                                                             const float* feat, const int32_t* idx,
+                                                             const float* gain, float eps, int H,
+                                                             T* x, float* h) {
+  __shared__ float sh[256];
+  const int r = blockIdx.x;
+  const T* e = E + (int64_t)tok[r] * H;
+  const float* f = feat + (int64_t)idx[r] * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    const float a = Elem<T>::to_f(e[i]);
+    ss += a * a;
+  }
+  for (int i = threadIdx.x; i < H; i += 256) ss += f[i] * f[i];
+  ss = block_sum_256(ss, sh);
+  const float inv = 1.0f / sqrtf(ss / (float)(2 * H) + eps);
+  T* xr = x + (int64_t)r * 2 * H;
+  for (int i = threadIdx.x; i < H; i += 256) {
+    xr[i] = Elem<T>::from_f(Elem<T>::to_f(e[i]) * inv * gain[i]);
+    xr[H + i] = Elem<T>::from_f(f[i] * inv * gain[H + i]);
+    h[(int64_t)r * H + i] = f[i];
+  }
+}
+
+__global__ void gather_f32_kernel(const float* src, int64_t ld, const int32_t* idx, int W, float* dst) {
+  const int r = blockIdx.x;
+  const float* s = src + (int64_t)idx[r] * ld;
+  for (int i = threadIdx.x; i < W; i += blockDim.x) dst[(int64_t)r * W + i] = s[i];
+}
+
+template <typename T>
+__global__ void gather_t_kernel(const T* src, int64_t ld, const int32_t* idx, int W, T* dst) {
+  const int r = blockIdx.x;
+  const T* s = src + (int64_t)idx[r] * ld;
+  for (int i = threadIdx.x; i < W; i += blockDim.x) dst[(int64_t)r * W + i] = s[i];
+}
+
+template <typename T>
+__global__ void store_feat_kernel(const float* h, int H, T* dst, int64_t ldd) {
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    dst[(int64_t)r * ldd + i] = Elem<T>::from_f(h[(int64_t)r * H + i]);
+}
+
+__global__ void rows_causal_kernel(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
+                                   uint64_t* mask) {
+  for (int r = threadIdx.x + blockIdx.x * blockDim.x; r < M; r += blockDim.x * gridDim.x) {
+    pos[r] = first + r;
+    slot[r] = first + r;
+    prehi[r] = first + r + 1;
+    mask[2 * r] = 0;
+    mask[2 * r + 1] = 0;
+  }
+}
+
+// Moves the K/V rows of the accepted path (tree slots ctx + path[j]) to
+// slots ctx + 1 + j in every layer. Each thread owns one element of one
+// (layer, kv head) and reads all sources before writing any destination,
+// since a destination may be an earlier source.
+template <typename T>
+__global__ void kv_compact_kernel(KVView v, int64_t layer_elems, const int32_t* Lp,
+                                  const int32_t* path, int ctx) {
+  const int layer = blockIdx.x, h = blockIdx.y;
+  const int L = *Lp;
+  if (L <= 0) return;
+  KVView lv = v;
+  lv.base = (T*)v.base + (int64_t)layer * layer_elems;
+  for (int e = threadIdx.x; e < 2 * v.d; e += blockDim.x) {
+    const int sel = e / v.d, i = e % v.d;
+    T vals[EAGLE_COMPACT_MAX];
+    for (int j = 0; j < L; ++j) vals[j] = kv_ptr<T>(lv, ctx + path[j], sel, h)[i];
+    for (int j = 0; j < L; ++j) kv_ptr<T>(lv, ctx + 1 + j, sel, h)[i] = vals[j];
+  }
+}
+
+}  // namespace
+
+int attn_chunk_keys() { return CHUNK; }
+
+uint64_t attn_part_floats(int max_chunks, int M, int nq, int d) {
+  return (uint64_t)max_chunks * M * nq * (d + 2);
+}
+
+#define DT_DISPATCH(dtype, KERNEL_CALL_BF16, KERNEL_CALL_F32) \
+  do {                                                        \
+    if ((dtype) == 1) { KERNEL_CALL_BF16; } else { KERNEL_CALL_F32; } \
+  } while (0)
+
+hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int M, float* h,
+                        hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, H, tok, h),
+              hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, H, tok, h));
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int dtype, const float* h, int64_t ldh, const float* gain, int K, float eps,
+                          int M, void* out_t, int64_t ldo, float* out_f, int64_t ldf,
+                          hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (bf16_t*)out_t, ldo, out_f, ldf),
+              hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (float*)out_t, ldo, out_f, ldf));
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, (bf16_t*)out_t),
+              hipLaunchKernelGGL(cast_kernel<float>, dim3(M), dim3(256), 0, st, h, H, (float*)out_t));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_kv(int dtype, const float* qkv, int M, int nq, int nkv, int d,
+                          const int32_t* pos, const int32_t* slot, const float* cos_t,
+                          const float* sin_t, void* q_out, KVView kv, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, kv),
+              hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, kv));
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(int dtype, const void* q, KVView kv, RowVis vis, int M, int nq, int d,
+                            float scale, float* opart, float* mlpart, void* out_t,
+                            hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const int group = nq / kv.n_kv;
+  if (dtype == 1) {
+    if (d != 128) return hipErrorInvalidValue;
+    const int n_chunks = (vis.key_end - vis.pre_lo + CHUNK - 1) / CHUNK;
+    if (n_chunks <= 0) return hipErrorInvalidValue;
+    AttnArgs a{(const bf16_t*)q, kv, vis, M, nq, group, scale, opart, mlpart};
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, nq, (M + 15) / 16), dim3(64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(M, nq), dim3(128), 0, st, opart, mlpart,
+                       n_chunks, M, nq, d, (bf16_t*)out_t);
+  } else {
+    if (d > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(M, nq), dim3(64), 0, st, (const float*)q, kv, vis, M,
+                       nq, group, d, scale, (float*)out_t);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_input_e1(int dtype, const void* E, const int32_t* tok, const float* feat,
+                                 const int32_t* idx, int M, int H, void* x, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(draft_input_e1_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, H, (bf16_t*)x),
+              hipLaunchKernelGGL(draft_input_e1_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, H, (float*)x));
+  return hipGetLastError();
+}
+
+hipError_t launch_draft_input_e3(int dtype, const void* E, const int32_t* tok, const float* feat,
+                                 const int32_t* idx, const float* gain, float eps, int M, int H,
+                                 void* x, float* h, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(draft_input_e3_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, gain, eps, H, (bf16_t*)x, h),
+              hipLaunchKernelGGL(draft_input_e3_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, gain, eps, H, (float*)x, h));
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_f32(const float* src, int64_t ld, const int32_t* idx, int M, int W,
+                             float* dst, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_f32_kernel, dim3(M), dim3(256), 0, st, src, ld, idx, W, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, const int32_t* idx, int M, int W,
+                           void* dst, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(gather_t_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)src, ld, idx, W, (bf16_t*)dst),
+              hipLaunchKernelGGL(gather_t_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)src, ld, idx, W, (float*)dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_store_feat(int dtype, const float* h, int H, int M, void* dst, int64_t ldd,
+                             hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(store_feat_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, (bf16_t*)dst, ldd),
+              hipLaunchKernelGGL(store_feat_kernel<float>, dim3(M), dim3(256), 0, st, h, H, (float*)dst, ldd));
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_causal(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
+                              uint64_t* mask, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rows_causal_kernel, dim3((M + 255) / 256), dim3(256), 0, st, first, M, pos,
+                     slot, prehi, mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int n_layers,
+                             const int32_t* L, const int32_t* path, int ctx, hipStream_t st) {
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv), dim3(256), 0, st, layer0, layer_elems, L, path, ctx),
+              hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(n_layers, layer0.n_kv), dim3(256), 0, st, layer0, layer_elems, L, path, ctx));
+  return hipGetLastError();
+}

@@ -1,0 +1,86 @@
+// Shared device definitions of the gfx950 kernels: element types, rounding,
+// MFMA fragments, small warp helpers. Host-visible launcher prototypes live
+// in kernels.h.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;                       // raw bfloat16 bits
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+#define WAVE 64
+#define EAGLE_COMPACT_MAX 16   // longest accepted path (= max draft depth)
+
+// ---------------------------------------------------------------- rounding
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Element type T of weights / KV / matrix operands: float or bf16_t.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static float to_f(float v) { return v; }
+  __device__ static float from_f(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  __device__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ static float to_f(bf16_t v) { return bf16_to_f32(v); }
+  __device__ static bf16_t from_f(float v) { return f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------- MFMA
+// One "step" is 16 bytes per lane along K: 8 bf16 or 4 fp32 elements.
+// 16x16 tiles: lane l owns row (l & 15) of the A operand and column (l & 15)
+// of the B operand; lane group (l >> 4) owns a 16-byte slice of K. The
+// result D[i][j] sits in lane j + 16*(i/4), element i%4. Within a step, K
+// may be permuted arbitrarily as long as A and B use the same permutation.
+template <typename T> struct Mma;
+template <> struct Mma<bf16_t> {
+  static constexpr int EPL = 8;          // elements per lane per step
+  static constexpr int KSTEP = 32;       // K covered by one step (4 lane groups)
+  __device__ __forceinline__ static void mma(const uint4& a, const uint4& b, f32x4& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  static constexpr int EPL = 4;
+  static constexpr int KSTEP = 16;
+  // four 16x16x4 MFMAs; element e of every lane covers k = 4*(l>>4) + e
+  __device__ __forceinline__ static void mma(const uint4& a, const uint4& b, f32x4& c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Total order of floats as unsigned keys (ascending float -> ascending key).
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}

@@ -1,0 +1,886 @@
+// Host side of the C interface in include/eagle.h: configuration checks,
+// the weight table, carving of the caller's buffers, and the sequence of
+// kernel launches for prefill, the draft passes and the verify pass.
+#include "eagle.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int KV_PAGE = 64;
+constexpr uint64_t ALIGN = 256;
+
+enum { ST_EMPTY = 0, ST_READY = 1, ST_DRAFTED = 2, ST_FAILED = 3 };
+
+uint64_t align_up(uint64_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// ------------------------------------------------------------ derived shape
+struct Derived {
+  int H, nq, nkv, d, F, V, NL, dt, esz;
+  int qkv_rows, kin_draft, fc_in;
+  int k_b, k_e, D, budget, dynamic;
+  int Mv, n_nodes_max, tree_rows_max;
+  int chunk, Mmax;
+  int t_slots, d_slots, t_pages, d_pages, max_pos, max_chunks;
+  int rows_per_pass[EAGLE_MAX_DEPTH + 1];   // rows of draft pass p (p >= 2)
+  // static plan
+  int s_depth[EAGLE_MAX_STATIC], s_prow[EAGLE_MAX_STATIC];
+  int s_nexp[EAGLE_MAX_DEPTH + 1];
+  int s_exp[EAGLE_MAX_DEPTH + 1][TREE_MAXEXP];
+};
+
+bool fail(std::string* why, const char* fmt, ...) {
+  if (why) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    *why = buf;
+  }
+  return false;
+}
+
+bool derive(const eagle_config* c, Derived* z, std::string* why) {
+  if (!c) return fail(why, "config is NULL");
+  std::memset(z, 0, sizeof(*z));
+  if (c->dtype != EAGLE_F32 && c->dtype != EAGLE_BF16) return fail(why, "dtype must be EAGLE_F32 or EAGLE_BF16");
+  if (c->head != EAGLE_HEAD_E1 && c->head != EAGLE_HEAD_E3) return fail(why, "head must be E1 or E3");
+  if (c->n_layers < 1) return fail(why, "n_layers must be >= 1");
+  if (c->hidden < 64 || c->hidden % 64) return fail(why, "hidden must be a positive multiple of 64");
+  if (c->n_heads < 1 || c->hidden % c->n_heads) return fail(why, "n_heads must divide hidden");
+  if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return fail(why, "n_kv_heads must divide n_heads");
+  const int d = c->hidden / c->n_heads;
+  if (d % 2) return fail(why, "head_dim must be even");
+  if (c->dtype == EAGLE_BF16 && d != 128) return fail(why, "bf16 path needs head_dim 128");
+  if (c->dtype == EAGLE_F32 && d > 256) return fail(why, "fp32 path needs head_dim <= 256");
+  const int kq = c->dtype == EAGLE_BF16 ? 32 : 16;
+  if (c->ffn < kq || c->ffn % kq) return fail(why, "ffn must be a positive multiple of %d", kq);
+  if (c->vocab < 2) return fail(why, "vocab must be >= 2");
+  if (!(c->rope_base > 0.f) || !(c->rms_eps > 0.f)) return fail(why, "rope_base and rms_eps must be > 0");
+  if (c->max_ctx < 2) return fail(why, "max_ctx must be >= 2");
+  if (c->prefill_chunk < 0 || c->prefill_chunk > 1024) return fail(why, "prefill_chunk must be in [0, 1024]");
+  if (c->head == EAGLE_HEAD_E3)
+    for (int i = 0; i < 3; ++i)
+      if (c->feat_layers[i] < 0 || c->feat_layers[i] >= c->n_layers)
+        return fail(why, "feat_layers[%d] out of range", i);
+  if (c->topk < 1 || c->topk > EAGLE_MAX_TOPK) return fail(why, "topk must be in [1, %d]", EAGLE_MAX_TOPK);
+  if (c->topk > c->vocab) return fail(why, "topk must be <= vocab");
+  if (c->depth < 1 || c->depth > EAGLE_MAX_DEPTH) return fail(why, "depth must be in [1, %d]", EAGLE_MAX_DEPTH);
+
+  z->H = c->hidden; z->nq = c->n_heads; z->nkv = c->n_kv_heads; z->d = d; z->F = c->ffn;
+  z->V = c->vocab; z->NL = c->n_layers; z->dt = c->dtype; z->esz = c->dtype == EAGLE_BF16 ? 2 : 4;
+  z->qkv_rows = (z->nq + 2 * z->nkv) * d;
+  z->kin_draft = c->head == EAGLE_HEAD_E3 ? 2 * z->H : z->H;
+  z->fc_in = c->head == EAGLE_HEAD_E3 ? 3 * z->H : 2 * z->H;
+  z->k_b = c->topk; z->D = c->depth;
+  z->dynamic = c->tree == EAGLE_TREE_DYNAMIC;
+  if (c->tree == EAGLE_TREE_DYNAMIC) {
+    z->k_e = c->expand > 0 ? c->expand : c->topk;
+    if (z->k_e > TREE_MAXEXP) return fail(why, "expand must be <= %d", TREE_MAXEXP);
+    if (c->budget < 0 || c->budget > EAGLE_MAX_VERIFY - 1)
+      return fail(why, "budget must be in [0, %d]", EAGLE_MAX_VERIFY - 1);
+    z->budget = c->budget;
+    long nodes = z->k_b;
+    int tree_rows = 0, width = z->k_b;
+    for (int p = 2; p <= z->D; ++p) {
+      const int rows = std::min(z->k_e, width);
+      z->rows_per_pass[p] = rows;
+      tree_rows += rows;
+      nodes += (long)rows * z->k_b;
+      width = rows * z->k_b;
+    }
+    if (nodes > EAGLE_MAX_NODES) return fail(why, "tree generates %ld nodes (> %d)", nodes, EAGLE_MAX_NODES);
+    if (tree_rows > TREE_MAXROWS) return fail(why, "tree uses %d draft rows (> %d)", tree_rows, TREE_MAXROWS);
+    z->n_nodes_max = (int)nodes;
+    z->tree_rows_max = tree_rows;
+    z->Mv = 1 + std::min<long>(z->budget, nodes);
+    if (z->budget == 0) z->tree_rows_max = 0;
+  } else if (c->tree == EAGLE_TREE_STATIC) {
+    const int n = c->n_static;
+    if (n < 1 || n > EAGLE_MAX_STATIC) return fail(why, "n_static must be in [1, %d]", EAGLE_MAX_STATIC);
+    int maxd = 0;
+    for (int j = 0; j < n; ++j) {
+      const int p = c->static_parent[j], r = c->static_rank[j];
+      if (p < -1 || p >= j) return fail(why, "static_parent[%d] must be -1 or an earlier node", j);
+      if (r < 0 || r >= c->topk) return fail(why, "static_rank[%d] must be in [0, topk)", j);
+      for (int i = 0; i < j; ++i)
+        if (c->static_parent[i] == p && c->static_rank[i] == r) return fail(why, "static node %d duplicates node %d", j, i);
+      z->s_depth[j] = p < 0 ? 1 : z->s_depth[p] + 1;
+      if (j > 0 && z->s_depth[j] < z->s_depth[j - 1]) return fail(why, "static tree must be in breadth-first order");
+      maxd = std::max(maxd, z->s_depth[j]);
+    }
+    if (maxd != z->D) return fail(why, "depth must equal the static tree's depth (%d)", maxd);
+    int tree_rows = 0;
+    for (int dd = 1; dd < z->D; ++dd) {
+      int cnt = 0;
+      for (int j = 0; j < n; ++j) {
+        if (z->s_depth[j] != dd) continue;
+        bool has = false;
+        for (int i = j + 1; i < n; ++i) has |= c->static_parent[i] == j;
+        if (has) {
+          if (cnt >= TREE_MAXEXP) return fail(why, "static tree expands more than %d nodes per level", TREE_MAXEXP);
+          z->s_exp[dd][cnt++] = j;
+        }
+      }
+      z->s_nexp[dd] = cnt;
+      z->rows_per_pass[dd + 1] = cnt;
+      tree_rows += cnt;
+    }
+    for (int j = 0; j < n; ++j) {
+      const int p = c->static_parent[j];
+      z->s_prow[j] = 0;
+      if (p >= 0)
+        for (int i = 0; i < z->s_nexp[z->s_depth[p]]; ++i)
+          if (z->s_exp[z->s_depth[p]][i] == p) z->s_prow[j] = i;
+    }
+    z->k_e = TREE_MAXEXP;
+    z->budget = n;
+    z->n_nodes_max = n;
+    z->tree_rows_max = tree_rows;
+    z->Mv = 1 + n;
+  } else {
+    return fail(why, "tree must be EAGLE_TREE_DYNAMIC or EAGLE_TREE_STATIC");
+  }
+  z->chunk = c->prefill_chunk > 0 ? c->prefill_chunk : 256;
+  int pass_rows = 1;
+  for (int p = 2; p <= z->D; ++p) pass_rows = std::max(pass_rows, z->rows_per_pass[p]);
+  z->Mmax = std::max({z->chunk, z->Mv, z->D + 1, pass_rows});
+  z->t_slots = c->max_ctx + z->Mv + 1;
+  z->d_slots = c->max_ctx + 2 + z->tree_rows_max + z->D + 1;
+  z->t_pages = (z->t_slots + KV_PAGE - 1) / KV_PAGE;
+  z->d_pages = (z->d_slots + KV_PAGE - 1) / KV_PAGE;
+  z->max_pos = std::max(z->t_slots, z->d_slots) + z->D + 2;
+  const int ck = attn_chunk_keys();
+  z->max_chunks = (std::max(z->t_pages, z->d_pages) * KV_PAGE + ck - 1) / ck + 1;
+  return true;
+}
+
+// ------------------------------------------------------------ weight table
+std::vector<eagle_tensor> tensor_table(const eagle_config* c, const Derived& z) {
+  std::vector<eagle_tensor> t;
+  uint64_t off = 0;
+  auto add = [&](int kind, int group, int layer, int dtype, int64_t rows, int64_t cols) {
+    eagle_tensor e;
+    e.kind = kind; e.group = group; e.layer = layer; e.dtype = dtype;
+    e.rows = rows; e.cols = cols;
+    e.offset = off;
+    off = align_up(off + (uint64_t)rows * cols * (dtype == EAGLE_BF16 ? 2 : 4));
+    t.push_back(e);
+  };
+  const int dt = c->dtype;
+  add(EAGLE_T_EMBED, EAGLE_G_GLOBAL, 0, dt, z.V, z.H);
+  add(EAGLE_T_LM_HEAD, EAGLE_G_GLOBAL, 0, dt, z.V, z.H);
+  add(EAGLE_T_FINAL_NORM, EAGLE_G_GLOBAL, 0, EAGLE_F32, 1, z.H);
+  auto layer = [&](int group, int l, int kin) {
+    add(EAGLE_T_ATTN_NORM, group, l, EAGLE_F32, 1, kin);
+    add(EAGLE_T_WQ, group, l, dt, (int64_t)z.nq * z.d, kin);
+    add(EAGLE_T_WK, group, l, dt, (int64_t)z.nkv * z.d, kin);
+    add(EAGLE_T_WV, group, l, dt, (int64_t)z.nkv * z.d, kin);
+    add(EAGLE_T_WO, group, l, dt, z.H, (int64_t)z.nq * z.d);
+    add(EAGLE_T_FFN_NORM, group, l, EAGLE_F32, 1, z.H);
+    add(EAGLE_T_WGATE, group, l, dt, z.F, z.H);
+    add(EAGLE_T_WUP, group, l, dt, z.F, z.H);
+    add(EAGLE_T_WDOWN, group, l, dt, z.H, z.F);
+  };
+  for (int l = 0; l < z.NL; ++l) layer(EAGLE_G_TARGET, l, z.H);
+  add(EAGLE_T_FC, EAGLE_G_GLOBAL, 0, dt, z.H, z.fc_in);
+  layer(EAGLE_G_DRAFT, 0, z.kin_draft);
+  return t;
+}
+
+uint64_t table_bytes(const std::vector<eagle_tensor>& t) {
+  const eagle_tensor& e = t.back();
+  return align_up(e.offset + (uint64_t)e.rows * e.cols * (e.dtype == EAGLE_BF16 ? 2 : 4));
+}
+
+// ------------------------------------------------------------ scratch plan
+struct Carve {
+  uint64_t off = 0;
+  char* base = nullptr;
+  template <typename T>
+  T* take(uint64_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off = align_up(off + count * sizeof(T));
+    return p;
+  }
+};
+
+uint64_t gemm_ws_floats(const Derived& z) {
+  // split-K workspace: max over the projections of splits * M * rows
+  struct S { int rows, K, epi; };
+  const S shapes[] = {{z.qkv_rows, z.H, EPI_STORE}, {z.H, z.nq * z.d, EPI_ADD},
+                      {2 * z.F, z.H, EPI_SWIGLU}, {z.H, z.F, EPI_ADD},
+                      {z.qkv_rows, z.kin_draft, EPI_STORE}, {z.H, z.fc_in, EPI_STORE}};
+  uint64_t mx = 0;
+  for (const S& s : shapes) {
+    for (int M : {z.Mmax, z.Mv, 1}) {
+      GemmPlan p = gemm_plan(M, s.rows, s.K, z.dt, s.epi);
+      mx = std::max(mx, gemm_part_floats(p, s.rows, std::min(M, 80)) * (uint64_t)p.m_chunks);
+      mx = std::max(mx, (uint64_t)p.splits * M * s.rows);
+    }
+  }
+  return mx;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ context
+struct eagle_ctx {
+  eagle_config cfg;
+  Derived z;
+  hipStream_t st = nullptr;
+  int device = 0;
+  char *W = nullptr, *KV = nullptr, *S = nullptr;
+  struct LW {
+    const float *attn_norm, *ffn_norm;
+    const void *wqkv, *wo, *wgu, *wdown;
+  };
+  std::vector<LW> tl;
+  LW dl;
+  const void *embed, *lm, *fc;
+  const float* final_norm;
+  KVView tkv0, dkv;
+  int64_t t_layer_elems = 0;
+  // scratch
+  float *cos_t, *sin_t;
+  int32_t *tpt, *dpt;
+  float *h, *qkv, *tfeat, *gbuf, *hcat, *dout, *opart, *mlpart, *gpart, *hpart, *logits, *margin, *logp;
+  void *xop, *qop, *aop, *fop, *lmh, *lmh2;
+  int32_t *counters, *g, *ids, *acc, *new_tok, *cu_src, *iota, *seq;
+  int32_t *rpos, *rslot, *rprehi;
+  uint64_t* rmask;
+  TreeDev t;
+  TreeParams tp;
+  // host state
+  int state = ST_EMPTY;
+  int ctx_len = 0;
+  std::vector<int32_t> committed;
+  bool debug = false;
+  int last_target_rows = 0, last_verify_rows = 0;
+  std::string err;
+};
+
+namespace {
+
+#define TAKE(field, T, count)                      \
+  do {                                             \
+    T* p_ = cv.take<T>((uint64_t)(count));         \
+    if (x) x->field = p_;                          \
+  } while (0)
+
+uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
+  Carve cv;
+  cv.base = x ? x->S : nullptr;
+  const int M = z.Mmax;
+  const uint64_t kmax = std::max({z.H, z.fc_in, z.kin_draft, z.F, z.nq * z.d});
+  const uint64_t es = z.esz;
+  TAKE(cos_t, float, (uint64_t)z.max_pos * z.d / 2);
+  TAKE(sin_t, float, (uint64_t)z.max_pos * z.d / 2);
+  TAKE(tpt, int32_t, z.t_pages);
+  TAKE(dpt, int32_t, z.d_pages);
+  TAKE(h, float, (uint64_t)M * z.H);
+  TAKE(qkv, float, (uint64_t)M * z.qkv_rows);
+  TAKE(tfeat, float, (uint64_t)M * z.H);
+  TAKE(gbuf, float, (uint64_t)M * z.H);
+  TAKE(hcat, float, (uint64_t)M * z.H);
+  TAKE(dout, float, (uint64_t)(1 + z.tree_rows_max) * z.H);
+  TAKE(opart, float, (uint64_t)z.max_chunks * M * z.nq * z.d);
+  TAKE(mlpart, float, (uint64_t)z.max_chunks * M * z.nq * 2);
+  TAKE(gpart, float, gemm_ws_floats(z));
+  TAKE(hpart, float, lmhead_part_floats(std::max(z.Mv, TREE_MAXEXP), z.V, z.k_b));
+  TAKE(logits, float, (uint64_t)z.Mv * z.V);
+  TAKE(margin, float, z.Mv);
+  TAKE(logp, float, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
+  TAKE(xop, char, (uint64_t)M * kmax * es);
+  TAKE(qop, char, (uint64_t)M * z.nq * z.d * es);
+  TAKE(aop, char, (uint64_t)M * z.nq * z.d * es);
+  TAKE(fop, char, (uint64_t)M * z.F * es);
+  TAKE(lmh, char, (uint64_t)M * 3 * z.H * es);
+  TAKE(lmh2, char, (uint64_t)(z.D + 1) * 3 * z.H * es);
+  TAKE(counters, int32_t, 65536);
+  TAKE(g, int32_t, z.Mv);
+  TAKE(ids, int32_t, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
+  TAKE(acc, int32_t, 2 + EAGLE_MAX_DEPTH + 2);
+  TAKE(new_tok, int32_t, EAGLE_MAX_DEPTH + 2);
+  TAKE(cu_src, int32_t, EAGLE_MAX_DEPTH + 2);
+  TAKE(iota, int32_t, M);
+  TAKE(seq, int32_t, (uint64_t)z.t_slots + z.D + 4);
+  TAKE(rpos, int32_t, M);
+  TAKE(rslot, int32_t, M);
+  TAKE(rprehi, int32_t, M);
+  TAKE(rmask, uint64_t, 2 * (uint64_t)M);
+  // tree state
+  TAKE(t.tok, int32_t, TREE_MAXN);
+  TAKE(t.parent, int32_t, TREE_MAXN);
+  TAKE(t.depth, int32_t, TREE_MAXN);
+  TAKE(t.srcrow, int32_t, TREE_MAXN);
+  TAKE(t.rank, int32_t, TREE_MAXN);
+  TAKE(t.row_of_node, int32_t, TREE_MAXN);
+  TAKE(t.v_row_of_node, int32_t, TREE_MAXN);
+  TAKE(t.logv, float, TREE_MAXN);
+  TAKE(t.logp, float, TREE_MAXN);
+  TAKE(t.counts, int32_t, 8);
+  TAKE(t.exp_nodes, int32_t, TREE_MAXEXP);
+  TAKE(t.row_tok, int32_t, TREE_MAXEXP);
+  TAKE(t.row_src, int32_t, TREE_MAXEXP);
+  TAKE(t.row_pos, int32_t, TREE_MAXEXP);
+  TAKE(t.row_slot, int32_t, TREE_MAXEXP);
+  TAKE(t.row_prehi, int32_t, TREE_MAXEXP);
+  TAKE(t.row_mask, uint64_t, 2 * TREE_MAXEXP);
+  TAKE(t.tmask, uint64_t, 2 * TREE_MAXROWS);
+  TAKE(t.v_tok, int32_t, TREE_MAXROWS);
+  TAKE(t.v_parent, int32_t, TREE_MAXROWS);
+  TAKE(t.v_depth, int32_t, TREE_MAXROWS);
+  TAKE(t.v_node, int32_t, TREE_MAXROWS);
+  TAKE(t.v_pos, int32_t, TREE_MAXROWS);
+  TAKE(t.v_slot, int32_t, TREE_MAXROWS);
+  TAKE(t.v_prehi, int32_t, TREE_MAXROWS);
+  TAKE(t.v_logv, float, TREE_MAXROWS);
+  TAKE(t.v_mask, uint64_t, 2 * TREE_MAXROWS);
+  TAKE(t.s_parent, int32_t, EAGLE_MAX_STATIC);
+  TAKE(t.s_rank, int32_t, EAGLE_MAX_STATIC);
+  TAKE(t.s_depth, int32_t, EAGLE_MAX_STATIC);
+  TAKE(t.s_prow, int32_t, EAGLE_MAX_STATIC);
+  TAKE(t.s_exp, int32_t, (EAGLE_MAX_DEPTH + 1) * TREE_MAXEXP);
+  TAKE(t.s_nexp, int32_t, EAGLE_MAX_DEPTH + 1);
+  return cv.off;
+}
+#undef TAKE
+
+uint64_t kv_bytes_of(const Derived& z) {
+  const uint64_t page_elems = 2ull * z.nkv * KV_PAGE * z.d;
+  return align_up((uint64_t)z.NL * z.t_pages * page_elems * z.esz) +
+         align_up((uint64_t)z.d_pages * page_elems * z.esz);
+}
+
+eagle_status set_err(eagle_ctx* c, eagle_status s, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    c->err = buf;
+    if (s == EAGLE_E_HIP || s == EAGLE_E_DEVICE) c->state = ST_FAILED;
+  }
+  return s;
+}
+
+#define HCHK(expr)                                                                      \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return set_err(c, EAGLE_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));    \
+  } while (0)
+
+#define SCHK(expr)                       \
+  do {                                   \
+    eagle_status s_ = (expr);            \
+    if (s_ != EAGLE_OK) return s_;       \
+  } while (0)
+
+// ------------------------------------------------------------ passes
+// One decoder layer over M rows with residual stream h. If x_ready, the
+// first norm was already applied and its output sits in xop (EAGLE-3).
+eagle_status layer_forward(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, float* h,
+                           bool x_ready, const int32_t* pos, const int32_t* slot, KVView kv,
+                           RowVis vis) {
+  const Derived& z = c->z;
+  const int dt = z.dt;
+  if (!x_ready)
+    HCHK(launch_rmsnorm(dt, h, z.H, w.attn_norm, z.H, c->cfg.rms_eps, M, c->xop, kin, nullptr, 0, c->st));
+  HCHK(launch_gemm(dt, EPI_STORE, w.wqkv, c->xop, M, z.qkv_rows, kin, c->qkv, z.qkv_rows, nullptr,
+                   c->gpart, c->counters, c->st));
+  HCHK(launch_rope_kv(dt, c->qkv, M, z.nq, z.nkv, z.d, pos, slot, c->cos_t, c->sin_t, c->qop, kv, c->st));
+  HCHK(launch_attention(dt, c->qop, kv, vis, M, z.nq, z.d, 1.0f / std::sqrt((float)z.d), c->opart,
+                        c->mlpart, c->aop, c->st));
+  HCHK(launch_gemm(dt, EPI_ADD, w.wo, c->aop, M, z.H, z.nq * z.d, h, z.H, nullptr, c->gpart,
+                   c->counters, c->st));
+  HCHK(launch_rmsnorm(dt, h, z.H, w.ffn_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H, nullptr, 0, c->st));
+  HCHK(launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, M, z.F, z.H, nullptr, 0, c->fop, c->gpart,
+                   c->counters, c->st));
+  HCHK(launch_gemm(dt, EPI_ADD, w.wdown, c->fop, M, z.H, z.F, h, z.H, nullptr, c->gpart,
+                   c->counters, c->st));
+  return EAGLE_OK;
+}
+
+// Target forward over M rows; leaves f in tfeat and its operand in xop.
+eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t* pos,
+                         const int32_t* slot, RowVis vis) {
+  const Derived& z = c->z;
+  HCHK(launch_embed(z.dt, c->embed, z.H, tok, M, c->h, c->st));
+  for (int l = 0; l < z.NL; ++l) {
+    KVView kv = c->tkv0;
+    kv.base = (char*)c->tkv0.base + (int64_t)l * c->t_layer_elems * z.esz;
+    SCHK(layer_forward(c, c->tl[l], z.H, M, c->h, false, pos, slot, kv, vis));
+    if (c->cfg.head == EAGLE_HEAD_E3)
+      for (int j = 0; j < 3; ++j)
+        if (c->cfg.feat_layers[j] == l)
+          HCHK(launch_store_feat(z.dt, c->h, z.H, M, (char*)c->lmh + (int64_t)j * z.H * z.esz,
+                                 3 * z.H, c->st));
+  }
+  HCHK(launch_rmsnorm(z.dt, c->h, z.H, c->final_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H,
+                      c->tfeat, z.H, c->st));
+  c->last_target_rows = M;
+  return EAGLE_OK;
+}
+
+// Draft rows (feature feat[idx[r]], token tok[r]) -> residual stream hout;
+// leaves the LM-head operand of every row in xop.
+eagle_status draft_pass(eagle_ctx* c, int M, const int32_t* tok, const float* feat,
+                        const int32_t* idx, const int32_t* pos, const int32_t* slot, RowVis vis,
+                        float* hout) {
+  const Derived& z = c->z;
+  bool x_ready = false;
+  if (c->cfg.head == EAGLE_HEAD_E1) {
+    HCHK(launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->st));
+    HCHK(launch_gemm(z.dt, EPI_STORE, c->fc, c->xop, M, z.H, 2 * z.H, hout, z.H, nullptr, c->gpart,
+                     c->counters, c->st));
+  } else {
+    HCHK(launch_draft_input_e3(z.dt, c->embed, tok, feat, idx, c->dl.attn_norm, c->cfg.rms_eps, M,
+                               z.H, c->xop, hout, c->st));
+    x_ready = true;
+  }
+  SCHK(layer_forward(c, c->dl, z.kin_draft, M, hout, x_ready, pos, slot, c->dkv, vis));
+  HCHK(launch_cast(z.dt, hout, z.H, M, c->xop, c->st));
+  return EAGLE_OK;
+}
+
+// Draft catch-up over M committed pairs at positions first..first+M-1; the
+// features are feat[idx[r]] (true target features, EAGLE-3: fused). If
+// final, the last row becomes the root row: its top-k are the depth-1 nodes.
+eagle_status catch_up(eagle_ctx* c, int M, int first, const int32_t* tok, const float* feat,
+                      const int32_t* idx, bool final, int ctx_after) {
+  const Derived& z = c->z;
+  HCHK(launch_rows_causal(first, M, c->rpos, c->rslot, c->rprehi, c->rmask, c->st));
+  RowVis vis{c->rprehi, c->rmask, 1, 0, 0, first + M};
+  SCHK(draft_pass(c, M, tok, feat, idx, c->rpos, c->rslot, vis, c->hcat));
+  if (!final) return EAGLE_OK;
+  HCHK(hipMemcpyAsync(c->dout, c->hcat + (int64_t)(M - 1) * z.H, sizeof(float) * z.H,
+                      hipMemcpyDeviceToDevice, c->st));
+  HCHK(launch_cast(z.dt, c->dout, z.H, 1, c->xop, c->st));
+  HCHK(launch_lmhead_topk(z.dt, c->lm, c->xop, 1, z.V, z.H, z.k_b, c->hpart, c->ids, c->logp, c->st));
+  HCHK(launch_tree_append(c->t, c->tp, c->ids, c->logp, 1, ctx_after, c->st));
+  return EAGLE_OK;
+}
+
+// E3: g = FC([l;m;h]) for M committed rows whose [l;m;h] operands are at src.
+eagle_status fuse_rows(eagle_ctx* c, int M, const void* src) {
+  const Derived& z = c->z;
+  HCHK(launch_gemm(z.dt, EPI_STORE, c->fc, src, M, z.H, 3 * z.H, c->gbuf, z.H, nullptr, c->gpart,
+                   c->counters, c->st));
+  return EAGLE_OK;
+}
+
+eagle_status check_ready(eagle_ctx* c) {
+  if (!c) return EAGLE_E_INVALID;
+  if (c->state == ST_FAILED) return set_err(c, EAGLE_E_STATE, "context failed earlier; call eagle_prefill");
+  return EAGLE_OK;
+}
+
+bool plain_mode(const eagle_ctx* c) { return c->z.dynamic && c->z.budget == 0; }
+
+}  // namespace
+
+// ============================================================ C interface
+extern "C" {
+
+const char* eagle_status_string(eagle_status s) {
+  switch (s) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_E_INVALID: return "invalid argument";
+    case EAGLE_E_STATE: return "wrong state";
+    case EAGLE_E_CAPACITY: return "capacity exceeded";
+    case EAGLE_E_BUFFER: return "buffer missing or too small";
+    case EAGLE_E_HIP: return "HIP error";
+    case EAGLE_E_DEVICE: return "device check failed";
+  }
+  return "unknown status";
+}
+
+eagle_status eagle_query(const eagle_config* cfg, eagle_sizes* out) {
+  Derived z;
+  if (!out) return EAGLE_E_INVALID;
+  if (!derive(cfg, &z, nullptr)) return EAGLE_E_INVALID;
+  std::vector<eagle_tensor> t = tensor_table(cfg, z);
+  out->weight_bytes = table_bytes(t);
+  out->kv_bytes = kv_bytes_of(z);
+  out->scratch_bytes = plan_scratch(z, nullptr);
+  out->n_tensors = (int32_t)t.size();
+  out->verify_rows = z.Mv;
+  out->max_nodes = z.n_nodes_max;
+  out->kv_page = KV_PAGE;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_tensor_info(const eagle_config* cfg, int32_t index, eagle_tensor* out) {
+  Derived z;
+  if (!out || !derive(cfg, &z, nullptr)) return EAGLE_E_INVALID;
+  std::vector<eagle_tensor> t = tensor_table(cfg, z);
+  if (index < 0 || index >= (int32_t)t.size()) return EAGLE_E_INVALID;
+  *out = t[index];
+  return EAGLE_OK;
+}
+
+eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void* hip_stream,
+                        eagle_ctx** out) {
+  if (!out) return EAGLE_E_INVALID;
+  *out = nullptr;
+  Derived z;
+  std::string why;
+  if (!derive(cfg, &z, &why)) return EAGLE_E_INVALID;
+  if (!bufs || !bufs->weights || !bufs->kv || !bufs->scratch) return EAGLE_E_BUFFER;
+  std::vector<eagle_tensor> tab = tensor_table(cfg, z);
+  if (bufs->weight_bytes < table_bytes(tab) || bufs->kv_bytes < kv_bytes_of(z) ||
+      bufs->scratch_bytes < plan_scratch(z, nullptr))
+    return EAGLE_E_BUFFER;
+  eagle_ctx* c = new eagle_ctx();
+  c->cfg = *cfg;
+  c->z = z;
+  c->st = (hipStream_t)hip_stream;
+  c->W = (char*)bufs->weights;
+  c->KV = (char*)bufs->kv;
+  c->S = (char*)bufs->scratch;
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    delete c;
+    return EAGLE_E_HIP;
+  }
+  // weights
+  auto ptr = [&](int kind, int group, int layer) -> const void* {
+    for (const eagle_tensor& e : tab)
+      if (e.kind == kind && e.group == group && e.layer == layer) return c->W + e.offset;
+    return nullptr;
+  };
+  c->embed = ptr(EAGLE_T_EMBED, EAGLE_G_GLOBAL, 0);
+  c->lm = ptr(EAGLE_T_LM_HEAD, EAGLE_G_GLOBAL, 0);
+  c->final_norm = (const float*)ptr(EAGLE_T_FINAL_NORM, EAGLE_G_GLOBAL, 0);
+  c->fc = ptr(EAGLE_T_FC, EAGLE_G_GLOBAL, 0);
+  auto lw = [&](int group, int l) {
+    eagle_ctx::LW w;
+    w.attn_norm = (const float*)ptr(EAGLE_T_ATTN_NORM, group, l);
+    w.ffn_norm = (const float*)ptr(EAGLE_T_FFN_NORM, group, l);
+    w.wqkv = ptr(EAGLE_T_WQ, group, l);   // WQ | WK | WV are contiguous
+    w.wo = ptr(EAGLE_T_WO, group, l);
+    w.wgu = ptr(EAGLE_T_WGATE, group, l); // WGATE | WUP are contiguous
+    w.wdown = ptr(EAGLE_T_WDOWN, group, l);
+    return w;
+  };
+  for (int l = 0; l < z.NL; ++l) c->tl.push_back(lw(EAGLE_G_TARGET, l));
+  c->dl = lw(EAGLE_G_DRAFT, 0);
+  // KV views
+  const int64_t page_elems = 2ll * z.nkv * KV_PAGE * z.d;
+  c->t_layer_elems = (int64_t)z.t_pages * page_elems;
+  plan_scratch(z, c);
+  c->tkv0 = KVView{c->KV, c->tpt, page_elems, KV_PAGE, z.nkv, z.d};
+  c->dkv = KVView{c->KV + align_up((uint64_t)z.NL * c->t_layer_elems * z.esz), c->dpt, page_elems,
+                  KV_PAGE, z.nkv, z.d};
+  c->tp = TreeParams{z.dynamic, z.k_b, z.k_e, z.D, z.budget, cfg->tree == EAGLE_TREE_STATIC ? cfg->n_static : 0};
+  // host-built tables: RoPE, page tables (identity), iota, static plan
+  {
+    const int half = z.d / 2;
+    std::vector<float> cs((size_t)z.max_pos * half), sn((size_t)z.max_pos * half);
+    for (int p = 0; p < z.max_pos; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double theta = std::pow((double)cfg->rope_base, -2.0 * i / z.d);
+        const double ang = (double)p * theta;
+        cs[(size_t)p * half + i] = (float)std::cos(ang);
+        sn[(size_t)p * half + i] = (float)std::sin(ang);
+      }
+    std::vector<int32_t> tp(z.t_pages), dp(z.d_pages), io(z.Mmax);
+    for (int i = 0; i < z.t_pages; ++i) tp[i] = i;
+    for (int i = 0; i < z.d_pages; ++i) dp[i] = i;
+    for (int i = 0; i < z.Mmax; ++i) io[i] = i;
+    std::vector<int32_t> sp(EAGLE_MAX_STATIC, -1), sr(EAGLE_MAX_STATIC, 0), sd(EAGLE_MAX_STATIC, 0),
+        sw(EAGLE_MAX_STATIC, 0), se((EAGLE_MAX_DEPTH + 1) * TREE_MAXEXP, -1), sne(EAGLE_MAX_DEPTH + 1, 0);
+    if (cfg->tree == EAGLE_TREE_STATIC) {
+      for (int j = 0; j < cfg->n_static; ++j) {
+        sp[j] = cfg->static_parent[j];
+        sr[j] = cfg->static_rank[j];
+        sd[j] = z.s_depth[j];
+        sw[j] = z.s_prow[j];
+      }
+      for (int dd = 0; dd <= EAGLE_MAX_DEPTH; ++dd) {
+        sne[dd] = z.s_nexp[dd];
+        for (int i = 0; i < z.s_nexp[dd]; ++i) se[dd * TREE_MAXEXP + i] = z.s_exp[dd][i];
+      }
+    }
+    hipError_t e = hipSuccess;
+    auto up = [&](void* dst, const void* src, size_t n) {
+      if (e == hipSuccess) e = hipMemcpy(dst, src, n, hipMemcpyHostToDevice);
+    };
+    up(c->cos_t, cs.data(), cs.size() * 4);
+    up(c->sin_t, sn.data(), sn.size() * 4);
+    up(c->tpt, tp.data(), tp.size() * 4);
+    up(c->dpt, dp.data(), dp.size() * 4);
+    up(c->iota, io.data(), io.size() * 4);
+    up(c->t.s_parent, sp.data(), sp.size() * 4);
+    up(c->t.s_rank, sr.data(), sr.size() * 4);
+    up(c->t.s_depth, sd.data(), sd.size() * 4);
+    up(c->t.s_prow, sw.data(), sw.size() * 4);
+    up(c->t.s_exp, se.data(), se.size() * 4);
+    up(c->t.s_nexp, sne.data(), sne.size() * 4);
+    if (e == hipSuccess) e = hipMemset(c->counters, 0, 65536 * 4);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      delete c;
+      return EAGLE_E_HIP;
+    }
+  }
+  *out = c;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32_t* first_token) {
+  if (!c) return EAGLE_E_INVALID;
+  const Derived& z = c->z;
+  if (!prompt || n < 1) return set_err(c, EAGLE_E_INVALID, "prompt must hold at least one token");
+  if (n + 1 > c->cfg.max_ctx) return set_err(c, EAGLE_E_CAPACITY, "prompt of %d tokens exceeds max_ctx", n);
+  for (int i = 0; i < n; ++i)
+    if (prompt[i] < 0 || prompt[i] >= z.V) return set_err(c, EAGLE_E_INVALID, "prompt[%d] = %d is not in [0, vocab)", i, prompt[i]);
+  c->state = ST_EMPTY;
+  c->committed.clear();
+  HCHK(hipMemcpyAsync(c->seq, prompt, sizeof(int32_t) * n, hipMemcpyHostToDevice, c->st));
+  for (int c0 = 0; c0 < n; c0 += z.chunk) {
+    const int M = std::min(z.chunk, n - c0);
+    const bool last = c0 + M == n;
+    HCHK(launch_rows_causal(c0, M, c->rpos, c->rslot, c->rprehi, c->rmask, c->st));
+    RowVis vis{c->rprehi, c->rmask, 0, 0, 0, c0 + M};
+    SCHK(target_pass(c, M, c->seq + c0, c->rpos, c->rslot, vis));
+    if (last) {
+      const void* xl = (const char*)c->xop + (int64_t)(M - 1) * z.H * z.esz;
+      HCHK(launch_lmhead_argmax(z.dt, c->lm, xl, 1, z.V, z.H, c->hpart, c->g, c->margin, nullptr, c->st));
+      HCHK(hipMemcpyAsync(c->seq + n, c->g, 4, hipMemcpyDeviceToDevice, c->st));
+    }
+    if (plain_mode(c)) continue;
+    const float* feat = c->tfeat;
+    if (c->cfg.head == EAGLE_HEAD_E3) {
+      SCHK(fuse_rows(c, M, c->lmh));
+      feat = c->gbuf;
+    }
+    SCHK(catch_up(c, M, c0 + 1, c->seq + c0 + 1, feat, c->iota, last, n));
+  }
+  int32_t b = 0;
+  HCHK(hipMemcpyAsync(&b, c->seq + n, 4, hipMemcpyDeviceToHost, c->st));
+  HCHK(hipStreamSynchronize(c->st));
+  c->committed.push_back(b);
+  c->ctx_len = n;
+  c->state = ST_READY;
+  if (first_token) *first_token = b;
+  return EAGLE_OK;
+}
+
+namespace {
+eagle_status copy_tree_out(eagle_ctx* c, eagle_tree* out) {
+  const Derived& z = c->z;
+  int32_t counts[8];
+  HCHK(hipMemcpyAsync(counts, c->t.counts, sizeof(counts), hipMemcpyDeviceToHost, c->st));
+  HCHK(hipStreamSynchronize(c->st));
+  std::memset(out, 0, sizeof(*out));
+  const int nr = counts[3], nn = counts[0];
+  out->n_rows = nr;
+  out->n_nodes = nn;
+  auto d2h = [&](void* dst, const void* src, size_t bytes) {
+    return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, c->st);
+  };
+  HCHK(d2h(out->token, c->t.v_tok, 4 * nr));
+  HCHK(d2h(out->parent, c->t.v_parent, 4 * nr));
+  HCHK(d2h(out->depth, c->t.v_depth, 4 * nr));
+  HCHK(d2h(out->logv, c->t.v_logv, 4 * nr));
+  HCHK(d2h(out->node, c->t.v_node, 4 * nr));
+  if (nn > 0) {
+    HCHK(d2h(out->node_token, c->t.tok, 4 * nn));
+    HCHK(d2h(out->node_parent, c->t.parent, 4 * nn));
+    HCHK(d2h(out->node_depth, c->t.depth, 4 * nn));
+    HCHK(d2h(out->node_logv, c->t.logv, 4 * nn));
+    HCHK(d2h(out->node_logp, c->t.logp, 4 * nn));
+  }
+  HCHK(hipStreamSynchronize(c->st));
+  (void)z;
+  return EAGLE_OK;
+}
+}  // namespace
+
+eagle_status eagle_draft_tree(eagle_ctx* c, eagle_tree* out) {
+  SCHK(check_ready(c));
+  if (c->state != ST_READY) return set_err(c, EAGLE_E_STATE, "eagle_draft_tree needs a READY context (call eagle_prefill / eagle_verify)");
+  const Derived& z = c->z;
+  const int ctx = c->ctx_len;
+  if (plain_mode(c)) {
+    HCHK(launch_tree_masks(c->t, 1, ctx, c->seq + ctx, c->st));
+  } else {
+    int t0 = 0;
+    for (int pass = 2; pass <= z.D; ++pass) {
+      const int M = z.rows_per_pass[pass];
+      if (M <= 0) break;
+      RowVis vis{c->t.row_prehi, c->t.row_mask, 1, ctx + 1, t0 + M, ctx + 1 + t0 + M};
+      SCHK(draft_pass(c, M, c->t.row_tok, c->dout, c->t.row_src, c->t.row_pos, c->t.row_slot, vis,
+                      c->dout + (int64_t)(1 + t0) * z.H));
+      HCHK(launch_lmhead_topk(z.dt, c->lm, c->xop, M, z.V, z.H, z.k_b, c->hpart, c->ids, c->logp, c->st));
+      HCHK(launch_tree_append(c->t, c->tp, c->ids, c->logp, pass, ctx, c->st));
+      t0 += M;
+    }
+    HCHK(launch_tree_finalize(c->t, c->tp, ctx, c->seq + ctx, c->st));
+  }
+  c->state = ST_DRAFTED;
+  if (out) SCHK(copy_tree_out(c, out));
+  return EAGLE_OK;
+}
+
+eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_tokens,
+                          int32_t* n_committed) {
+  SCHK(check_ready(c));
+  const Derived& z = c->z;
+  if (planted ? (c->state != ST_READY && c->state != ST_DRAFTED) : c->state != ST_DRAFTED)
+    return set_err(c, EAGLE_E_STATE, "eagle_verify needs a drafted tree (or a planted tree after prefill)");
+  const int ctx = c->ctx_len;
+  int Mv;
+  if (planted) {
+    const int n = planted->n_rows;
+    if (n < 1 || n > z.Mv) return set_err(c, EAGLE_E_INVALID, "planted tree must have 1..%d rows", z.Mv);
+    std::vector<int> depth(n, 0);
+    for (int r = 1; r < n; ++r) {
+      const int p = planted->parent[r];
+      if (p < 0 || p >= r) return set_err(c, EAGLE_E_INVALID, "planted parent[%d] must be in [0, %d)", r, r);
+      if (planted->token[r] < 0 || planted->token[r] >= z.V) return set_err(c, EAGLE_E_INVALID, "planted token[%d] out of range", r);
+      depth[r] = depth[p] + 1;
+      if (depth[r] > z.D) return set_err(c, EAGLE_E_INVALID, "planted tree deeper than depth");
+      for (int s = 1; s < r; ++s)
+        if (planted->parent[s] == p && planted->token[s] == planted->token[r])
+          return set_err(c, EAGLE_E_INVALID, "planted rows %d and %d are siblings with one token", s, r);
+    }
+    Mv = n;
+  } else {
+    Mv = z.Mv;
+  }
+  // the cycle may commit up to depth + 1 tokens after the root at ctx
+  if (ctx + z.D + 2 > c->cfg.max_ctx)
+    return set_err(c, EAGLE_E_CAPACITY, "sequence would exceed max_ctx (%d)", c->cfg.max_ctx);
+  if (planted) {
+    std::vector<int32_t> par(planted->parent, planted->parent + Mv);
+    par[0] = -1;
+    HCHK(hipMemcpyAsync(c->t.v_tok, planted->token, 4 * Mv, hipMemcpyHostToDevice, c->st));
+    HCHK(hipMemcpyAsync(c->t.v_parent, par.data(), 4 * Mv, hipMemcpyHostToDevice, c->st));
+    HCHK(launch_tree_masks(c->t, Mv, ctx, c->seq + ctx, c->st));
+  }
+  RowVis vis{c->t.v_prehi, c->t.v_mask, 0, ctx, Mv, ctx + Mv};
+  SCHK(target_pass(c, Mv, c->t.v_tok, c->t.v_pos, c->t.v_slot, vis));
+  HCHK(launch_lmhead_argmax(z.dt, c->lm, c->xop, Mv, z.V, z.H, c->hpart, c->g, c->margin,
+                            c->debug ? c->logits : nullptr, c->st));
+  c->last_verify_rows = Mv;
+  HCHK(launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->st));
+  HCHK(launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, c->acc, c->acc + 2, ctx, c->st));
+  int32_t acc[2 + EAGLE_MAX_DEPTH + 2];
+  int32_t nt[EAGLE_MAX_DEPTH + 2];
+  HCHK(hipMemcpyAsync(acc, c->acc, sizeof(acc), hipMemcpyDeviceToHost, c->st));
+  HCHK(hipMemcpyAsync(nt, c->new_tok, sizeof(nt), hipMemcpyDeviceToHost, c->st));
+  HCHK(hipStreamSynchronize(c->st));
+  const int L = acc[0];
+  if (L < 0 || L > z.D) return set_err(c, EAGLE_E_DEVICE, "acceptance length %d out of range", L);
+  HCHK(hipMemcpyAsync(c->seq + ctx + 1, c->new_tok, 4 * (L + 1), hipMemcpyDeviceToDevice, c->st));
+  const int ctx_new = ctx + L + 1;
+  if (!plain_mode(c)) {
+    const float* feat = c->tfeat;
+    const int32_t* idx = c->cu_src;
+    if (c->cfg.head == EAGLE_HEAD_E3) {
+      HCHK(launch_gather_t(z.dt, c->lmh, 3 * z.H, c->cu_src, L + 1, 3 * z.H, c->lmh2, c->st));
+      SCHK(fuse_rows(c, L + 1, c->lmh2));
+      feat = c->gbuf;
+      idx = c->iota;
+    }
+    SCHK(catch_up(c, L + 1, ctx + 1, c->new_tok, feat, idx, true, ctx_new));
+  }
+  for (int i = 0; i <= L; ++i) c->committed.push_back(nt[i]);
+  c->ctx_len = ctx_new;
+  c->state = ST_READY;
+  if (out_tokens) std::memcpy(out_tokens, nt, sizeof(int32_t) * (L + 1));
+  if (n_committed) *n_committed = L + 1;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_generate(eagle_ctx* c, const int32_t* prompt, int32_t n, int32_t max_new,
+                            int32_t* out, int32_t* n_out, eagle_stats* stats) {
+  if (!c) return EAGLE_E_INVALID;
+  if (max_new < 1 || !out) return set_err(c, EAGLE_E_INVALID, "max_new must be >= 1 and out non-NULL");
+  if (n + max_new + c->z.D > c->cfg.max_ctx)
+    return set_err(c, EAGLE_E_CAPACITY, "prompt + max_new + depth exceeds max_ctx");
+  SCHK(eagle_prefill(c, prompt, n, nullptr));
+  eagle_stats s;
+  std::memset(&s, 0, sizeof(s));
+  hipEvent_t e0, e1;
+  HCHK(hipEventCreate(&e0));
+  HCHK(hipEventCreate(&e1));
+  HCHK(hipEventRecord(e0, c->st));
+  while ((int)c->committed.size() < max_new) {
+    SCHK(eagle_draft_tree(c, nullptr));
+    int32_t cnt = 0;
+    SCHK(eagle_verify(c, nullptr, nullptr, &cnt));
+    s.cycles++;
+    s.accept_hist[std::min(cnt - 1, EAGLE_MAX_DEPTH)]++;
+  }
+  HCHK(hipEventRecord(e1, c->st));
+  HCHK(hipEventSynchronize(e1));
+  float ms = 0.f;
+  HCHK(hipEventElapsedTime(&ms, e0, e1));
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  s.seconds = ms * 1e-3;
+  s.committed = (int64_t)c->committed.size();
+  std::memcpy(out, c->committed.data(), sizeof(int32_t) * max_new);
+  if (n_out) *n_out = max_new;
+  if (stats) *stats = s;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_committed(eagle_ctx* c, int32_t* out, int32_t cap, int32_t* n) {
+  if (!c || (!out && cap > 0)) return EAGLE_E_INVALID;
+  const int k = std::min<int>(cap, (int)c->committed.size());
+  if (k > 0) std::memcpy(out, c->committed.data(), sizeof(int32_t) * k);
+  if (n) *n = (int32_t)c->committed.size();
+  return EAGLE_OK;
+}
+
+eagle_status eagle_set_debug(eagle_ctx* c, int32_t on) {
+  if (!c) return EAGLE_E_INVALID;
+  c->debug = on != 0;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_debug_read(eagle_ctx* c, int32_t what, void* host_dst, uint64_t bytes,
+                              int32_t* rows) {
+  if (!c || !host_dst) return EAGLE_E_INVALID;
+  const Derived& z = c->z;
+  const void* src;
+  uint64_t avail;
+  int r;
+  switch (what) {
+    case 0: src = c->tfeat; r = c->last_target_rows; avail = (uint64_t)r * z.H * 4; break;
+    case 1: src = c->logits; r = c->last_verify_rows; avail = c->debug ? (uint64_t)r * z.V * 4 : 0; break;
+    case 2: src = c->g; r = c->last_verify_rows; avail = (uint64_t)r * 4; break;
+    case 3: src = c->margin; r = c->last_verify_rows; avail = (uint64_t)r * 4; break;
+    default: return set_err(c, EAGLE_E_INVALID, "unknown debug buffer %d", what);
+  }
+  if (rows) *rows = r;
+  const uint64_t n = std::min(bytes, avail);
+  if (n) {
+    HCHK(hipMemcpyAsync(host_dst, src, n, hipMemcpyDeviceToHost, c->st));
+    HCHK(hipStreamSynchronize(c->st));
+  }
+  return EAGLE_OK;
+}
+
+void eagle_free(eagle_ctx* c) { delete c; }
+
+const char* eagle_last_error(const eagle_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+}  // extern "C"

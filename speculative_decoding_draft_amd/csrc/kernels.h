@@ -1,0 +1,130 @@
+// Host launchers of the gfx950 kernels (all enqueue on `stream`, no sync).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
+
+// ---------------------------------------------------------------- GEMM
+// y = x W^T for a skinny x (M rows) and a weight W [N, K] streamed from HBM.
+//   EPI_STORE : Y[m, n]  = acc            (fp32, row stride ldy)
+//   EPI_ADD   : Y[m, n] += acc            (fp32 residual update)
+//   EPI_SWIGLU: W = [gate (N rows); up (N rows)], Yt[m, n] = T(silu(g) * u)
+// dtype 0 = fp32, 1 = bf16 for W, x and Yt. `part`/`counters` is the split-K
+// workspace (gemm_workspace_bytes); counters must start at zero and are left
+// at zero.
+struct GemmPlan { int mt, nb, splits, m_chunks, n_tiles; };
+GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi);
+uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M);
+hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int M, int N, int K,
+                       float* Y, int64_t ldy, void* Yt, float* part, int* counters,
+                       hipStream_t stream);
+
+// ---------------------------------------------------------------- LM head
+// Verify: g[m] = argmax_v (x W^T)[m, v] (lowest id on ties), margin[m] =
+// top-1 minus top-2; logits stored to `logits` [M, V] when not null.
+hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int M, int V, int H,
+                                float* part, int32_t* g, float* margin, float* logits,
+                                hipStream_t stream);
+// Draft: per row the k best ids by (logit desc, id asc) and their
+// log-probabilities l - max - log(sum exp(l - max)) over the full vocabulary.
+hipError_t launch_lmhead_topk(int dtype, const void* W, const void* x, int M, int V, int H,
+                              int k, float* part, int32_t* ids, float* logp, hipStream_t stream);
+uint64_t lmhead_part_floats(int M, int V, int k);
+
+// ---------------------------------------------------------------- paged KV
+// One layer of a paged KV cache. Element (slot, K|V, kv head h, i) lives at
+//   base + page_table[slot / page] * page_elems
+//        + ((kv * n_kv + h) * page + slot % page) * d + i
+// so each (page, K|V, head) is a contiguous [page, d] tile.
+struct KVView {
+  void* base;
+  const int32_t* page_table;
+  int64_t page_elems;   // 2 * n_kv * page * d
+  int page, n_kv, d;
+};
+
+// ---------------------------------------------------------------- rows
+// Attention visibility of row r: key slots [pre_lo, prehi[r]) plus the
+// tree slots tree_base + j whose bit j is set in mask[2r..2r+1].
+struct RowVis {
+  const int32_t* prehi;
+  const uint64_t* mask;
+  int pre_lo, tree_base, n_tree, key_end;
+};
+
+hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int M, float* h,
+                        hipStream_t st);
+hipError_t launch_rmsnorm(int dtype, const float* h, int64_t ldh, const float* gain, int K, float eps,
+                          int M, void* out_t, int64_t ldo, float* out_f, int64_t ldf,
+                          hipStream_t st);
+hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, hipStream_t st);
+hipError_t launch_rope_kv(int dtype, const float* qkv, int M, int nq, int nkv, int d,
+                          const int32_t* pos, const int32_t* slot, const float* cos_t,
+                          const float* sin_t, void* q_out, KVView kv, hipStream_t st);
+uint64_t attn_part_floats(int max_chunks, int M, int nq, int d);
+int attn_chunk_keys();
+hipError_t launch_attention(int dtype, const void* q, KVView kv, RowVis vis, int M, int nq, int d,
+                            float scale, float* opart, float* mlpart, void* out_t,
+                            hipStream_t st);
+hipError_t launch_draft_input_e1(int dtype, const void* E, const int32_t* tok, const float* feat,
+                                 const int32_t* idx, int M, int H, void* x, hipStream_t st);
+hipError_t launch_draft_input_e3(int dtype, const void* E, const int32_t* tok, const float* feat,
+                                 const int32_t* idx, const float* gain, float eps, int M, int H,
+                                 void* x, float* h, hipStream_t st);
+hipError_t launch_gather_f32(const float* src, int64_t ld, const int32_t* idx, int M, int W,
+                             float* dst, hipStream_t st);
+hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, const int32_t* idx, int M, int W,
+                           void* dst, hipStream_t st);
+hipError_t launch_store_feat(int dtype, const float* h, int H, int M, void* dst, int64_t ldd,
+                             hipStream_t st);
+hipError_t launch_rows_causal(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
+                              uint64_t* mask, hipStream_t st);
+hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int n_layers,
+                             const int32_t* L, const int32_t* path, int ctx, hipStream_t st);
+
+// ---------------------------------------------------------------- tree
+#define TREE_MAXN 1024
+#define TREE_MAXROWS 128     // verify rows and tree rows (bit masks of 128)
+#define TREE_MAXEXP 16       // rows per draft pass
+
+// Device-side tree state (all arrays in the scratch buffer).
+struct TreeDev {
+  int32_t *tok, *parent, *depth, *srcrow, *rank, *row_of_node, *v_row_of_node;  // [TREE_MAXN]
+  float *logv, *logp;                                                           // [TREE_MAXN]
+  int32_t* counts;     // [0] nodes, [1] rows of the next pass, [2] tree rows used, [3] verify rows
+  int32_t* exp_nodes;  // [TREE_MAXEXP] nodes expanded by the next pass, in order
+  int32_t *row_tok, *row_src, *row_pos, *row_slot, *row_prehi;  // [TREE_MAXEXP]
+  uint64_t* row_mask;  // [2 * TREE_MAXEXP]
+  uint64_t* tmask;     // [2 * TREE_MAXROWS] visibility mask of each tree row
+  int32_t *v_tok, *v_parent, *v_depth, *v_node, *v_pos, *v_slot, *v_prehi;  // [TREE_MAXROWS]
+  float* v_logv;
+  uint64_t* v_mask;    // [2 * TREE_MAXROWS]
+  // static plan (uploaded at load): per static node
+  int32_t *s_parent, *s_rank, *s_depth, *s_prow;  // s_prow: row of the parent in its pass
+  int32_t *s_exp;      // [EAGLE depth][TREE_MAXEXP] nodes expanded at each depth (-1 padded)
+  int32_t* s_nexp;     // [depth] count
+};
+
+struct TreeParams {
+  int dynamic, k_b, k_e, depth, budget, n_static;
+};
+
+// Append the children produced by the last draft pass (pass 1 = the root
+// row) and, if pass < depth, choose the nodes the next pass expands and
+// write its row descriptors. ids/logp: [rows of the pass, k_b].
+hipError_t launch_tree_append(TreeDev t, TreeParams p, const int32_t* ids, const float* logp,
+                              int pass, int ctx, hipStream_t st);
+// Rerank to the best `budget` nodes, flatten to verify rows (root first,
+// then by depth and rerank order), build positions and ancestry masks.
+// root_token: device pointer to the last committed token.
+hipError_t launch_tree_finalize(TreeDev t, TreeParams p, int ctx, const int32_t* root_token,
+                                hipStream_t st);
+// Masks/positions for verify rows already in v_tok / v_parent (planted tree).
+hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root_token,
+                             hipStream_t st);
+// Greedy acceptance walk over the verify rows given the target's choices g.
+// acc[0] = L, acc[1] = bonus, acc[2..2+L) = accepted rows; new_tok[0..L]
+// = the committed tokens; cu_src[0..L] = feature rows feeding the catch-up.
+hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
+                         int32_t* new_tok, int32_t* cu_src, hipStream_t st);

@@ -1,0 +1,74 @@
+// Kernel-level entry points (include/eagle_ops.h).
+#include "eagle_ops.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace {
+constexpr uint64_t kCounterBytes = 65536 * 4;
+
+uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
+
+bool linear_ok(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K) {
+  if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return false;
+  if (epi < EAGLE_EPI_STORE || epi > EAGLE_EPI_SWIGLU) return false;
+  const int ks = dtype == EAGLE_BF16 ? 32 : 16;
+  return M >= 1 && N >= 1 && K >= ks && K % ks == 0;
+}
+}  // namespace
+
+extern "C" {
+
+uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K) {
+  if (!linear_ok(dtype, epi, M, N, K)) return 0;
+  const int rows = epi == EAGLE_EPI_SWIGLU ? 2 * N : N;
+  GemmPlan p = gemm_plan(M, rows, K, dtype, epi);
+  if (p.splits == 1) return 0;
+  return kCounterBytes + align256((uint64_t)p.splits * M * rows * 4);
+}
+
+eagle_status eagle_op_linear(int32_t dtype, int32_t epi, const void* x, const void* w, void* y,
+                             int32_t M, int32_t N, int32_t K, void* workspace, uint64_t ws_bytes,
+                             void* stream) {
+  if (!linear_ok(dtype, epi, M, N, K) || !x || !w || !y) return EAGLE_E_INVALID;
+  const uint64_t need = eagle_op_linear_workspace(dtype, epi, M, N, K);
+  if (need > 0 && (!workspace || ws_bytes < need)) return EAGLE_E_BUFFER;
+  int* counters = need ? (int*)workspace : nullptr;
+  float* part = need ? (float*)((char*)workspace + kCounterBytes) : nullptr;
+  hipError_t e;
+  if (epi == EAGLE_EPI_SWIGLU)
+    e = launch_gemm(dtype, EPI_SWIGLU, w, x, M, N, K, nullptr, 0, y, part, counters, (hipStream_t)stream);
+  else
+    e = launch_gemm(dtype, epi == EAGLE_EPI_ADD ? EPI_ADD : EPI_STORE, w, x, M, N, K, (float*)y, N,
+                    nullptr, part, counters, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
+}
+
+uint64_t eagle_op_lmhead_workspace(int32_t M, int32_t V, int32_t k) {
+  if (M < 1 || V < 1 || k < 0 || k > EAGLE_MAX_TOPK) return 0;
+  return align256(lmhead_part_floats(M, V, k) * 4);
+}
+
+eagle_status eagle_op_lmhead(int32_t dtype, int32_t k, const void* x, const void* w_lm, int32_t M,
+                             int32_t V, int32_t H, int32_t* out_ids, float* out_vals, float* logits,
+                             void* workspace, uint64_t ws_bytes, void* stream) {
+  if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return EAGLE_E_INVALID;
+  const int ks = dtype == EAGLE_BF16 ? 32 : 16;
+  if (!x || !w_lm || !out_ids || !out_vals || M < 1 || V < 1 || H < ks || H % ks || k < 0 ||
+      k > EAGLE_MAX_TOPK || (k > 0 && k > V))
+    return EAGLE_E_INVALID;
+  if (!workspace || ws_bytes < eagle_op_lmhead_workspace(M, V, k)) return EAGLE_E_BUFFER;
+  hipError_t e;
+  if (k == 0)
+    e = launch_lmhead_argmax(dtype, w_lm, x, M, V, H, (float*)workspace, out_ids, out_vals, logits,
+                             (hipStream_t)stream);
+  else
+    e = launch_lmhead_topk(dtype, w_lm, x, M, V, H, k, (float*)workspace, out_ids, out_vals,
+                           (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,285 @@
+// EAGLE-2 tree policy on the device: path values in log space, expansion
+// of the best newest nodes, global rerank to a connected top-m, flattening
+// with ancestry masks, and the greedy acceptance walk. Each kernel is one
+// workgroup; all decisions use fixed total orders on fp32 keys:
+//   expansion: (log V desc, generation asc)
+//   rerank:    (log V desc, depth asc, generation asc)
+//   rows:      (depth asc, rerank order)
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+__device__ __forceinline__ void set_bit(uint64_t* m, int j) {
+  if (j < 64) m[0] |= (1ull << j);
+  else m[1] |= (1ull << (j - 64));
+}
+
+__global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams p,
+                                                          const int32_t* ids, const float* lps,
+                                                          int pass, int ctx) {
+  __shared__ int s_base, s_nrows, s_nnew, s_nsel, s_tbase;
+  __shared__ int sel[TREE_MAXEXP];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    if (pass == 1) {
+      t.counts[0] = 0;
+      t.counts[1] = 1;
+      t.counts[2] = 0;
+      t.counts[3] = 0;
+    }
+    s_base = t.counts[0];
+    s_nrows = t.counts[1];
+    s_tbase = t.counts[2];
+  }
+  __syncthreads();
+  const int base = s_base, nrows = s_nrows;
+  const int k = p.k_b;
+
+  if (p.dynamic) {
+    // children of row i: generation base + i*k + r
+    for (int e = tid; e < nrows * k; e += blockDim.x) {
+      const int i = e / k, r = e % k;
+      const int gen = base + e;
+      const int par = (pass == 1) ? -1 : t.exp_nodes[i];
+      const float lp = lps[i * k + r];
+      t.tok[gen] = ids[i * k + r];
+      t.parent[gen] = par;
+      t.depth[gen] = pass;
+      t.rank[gen] = r;
+      t.logp[gen] = lp;
+      t.logv[gen] = (par < 0) ? lp : (t.logv[par] + lp);
+      t.srcrow[gen] = (par < 0) ? 0 : 1 + t.row_of_node[par];
+      t.row_of_node[gen] = -1;
+    }
+    if (tid == 0) { s_nnew = nrows * k; t.counts[0] = base + nrows * k; }
+  } else {
+    // static: nodes of depth `pass`, in list order
+    for (int j = tid; j < p.n_static; j += blockDim.x) {
+      if (t.s_depth[j] != pass) continue;
+      const int par = t.s_parent[j];
+      const int i = t.s_prow[j];
+      const int r = t.s_rank[j];
+      const float lp = lps[i * k + r];
+      t.tok[j] = ids[i * k + r];
+      t.parent[j] = par;
+      t.depth[j] = pass;
+      t.rank[j] = r;
+      t.logp[j] = lp;
+      t.logv[j] = (par < 0) ? lp : (t.logv[par] + lp);
+      t.srcrow[j] = (par < 0) ? 0 : 1 + t.row_of_node[par];
+      t.row_of_node[j] = -1;
+    }
+    if (tid == 0) {
+      int n = 0;
+      for (int j = 0; j < p.n_static; ++j) n += (t.s_depth[j] <= pass);
+      t.counts[0] = n;
+    }
+  }
+  __syncthreads();
+  if (pass >= p.depth) return;
+
+  // choose the nodes the next pass expands
+  if (p.dynamic) {
+    const int nnew = s_nnew;
+    if (tid == 0) s_nsel = min(p.k_e, nnew);
+    for (int e = tid; e < nnew; e += blockDim.x) {
+      const int gi = base + e;
+      const uint32_t ki = ~float_key(t.logv[gi]);
+      int rank = 0;
+      for (int f = 0; f < nnew; ++f) {
+        const uint32_t kf = ~float_key(t.logv[base + f]);
+        rank += (kf < ki) || (kf == ki && f < e);
+      }
+      if (rank < p.k_e) sel[rank] = gi;
+    }
+  } else {
+    if (tid == 0) s_nsel = t.s_nexp[pass];
+    for (int i = tid; i < TREE_MAXEXP; i += blockDim.x)
+      if (i < t.s_nexp[pass]) sel[i] = t.s_exp[pass * TREE_MAXEXP + i];
+  }
+  __syncthreads();
+  const int nsel = s_nsel;
+  // tree rows are appended in order; masks need the parent row's mask,
+  // which belongs to an earlier pass, so rows of this pass are independent
+  for (int i = tid; i < nsel; i += blockDim.x) {
+    const int e = sel[i];
+    const int tr = s_tbase + i;
+    t.exp_nodes[i] = e;
+    t.row_of_node[e] = tr;
+    t.row_tok[i] = t.tok[e];
+    t.row_src[i] = t.srcrow[e];
+    t.row_pos[i] = ctx + t.depth[e];
+    t.row_slot[i] = ctx + 1 + tr;
+    t.row_prehi[i] = ctx + 1;
+    uint64_t m[2] = {0ull, 0ull};
+    const int src = t.srcrow[e];
+    if (src > 0) { m[0] = t.tmask[2 * (src - 1)]; m[1] = t.tmask[2 * (src - 1) + 1]; }
+    set_bit(m, tr);
+    t.tmask[2 * tr] = m[0];
+    t.tmask[2 * tr + 1] = m[1];
+    t.row_mask[2 * i] = m[0];
+    t.row_mask[2 * i + 1] = m[1];
+  }
+  if (tid == 0) {
+    t.counts[1] = nsel;
+    t.counts[2] = s_tbase + nsel;
+  }
+}
+
+// masks for verify rows whose parents precede them (level order not needed)
+__device__ void build_masks(TreeDev& t, int n, int ctx) {
+  // depth by pointer chasing (n <= 128, depth <= 16)
+  for (int r = threadIdx.x; r < n; r += blockDim.x) {
+    uint64_t m[2] = {0ull, 0ull};
+    int d = 0;
+    for (int a = r; a >= 0; a = t.v_parent[a]) {
+      set_bit(m, a);
+      if (a != 0) ++d;
+      if (a == 0) break;
+    }
+    t.v_mask[2 * r] = m[0];
+    t.v_mask[2 * r + 1] = m[1];
+    t.v_depth[r] = d;
+    t.v_pos[r] = ctx + d;
+    t.v_slot[r] = ctx + r;
+    t.v_prehi[r] = ctx;
+  }
+}
+
+__global__ __launch_bounds__(1024) void tree_finalize_kernel(TreeDev t, TreeParams p, int ctx,
+                                                             const int32_t* root_token) {
+  __shared__ uint64_t keys[TREE_MAXN];
+  __shared__ int kept[TREE_MAXROWS];
+  __shared__ int s_n, s_m;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    s_n = t.counts[0];
+    s_m = p.dynamic ? min(p.budget, s_n) : s_n;
+  }
+  __syncthreads();
+  const int n = s_n, m = s_m;
+  if (p.dynamic) {
+    for (int i = tid; i < TREE_MAXN; i += blockDim.x) {
+      keys[i] = (i < n) ? (((uint64_t)(~float_key(t.logv[i])) << 32) |
+                           ((uint64_t)t.depth[i] << 20) | (uint64_t)i)
+                        : ~0ull;
+    }
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int size = 2; size <= TREE_MAXN; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int i = tid; i < TREE_MAXN; i += blockDim.x) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const bool up = (i & size) == 0;
+            const uint64_t a = keys[i], b = keys[j];
+            if ((a > b) == up) { keys[i] = b; keys[j] = a; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < m; i += blockDim.x) kept[i] = (int)(keys[i] & 0xFFFFF);
+  } else {
+    for (int i = tid; i < m; i += blockDim.x) kept[i] = i;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += blockDim.x) t.v_row_of_node[i] = -1;
+  __syncthreads();
+  // row of kept node i: 1 + #{kept j with (depth, order) smaller}
+  for (int i = tid; i < m; i += blockDim.x) {
+    const int di = t.depth[kept[i]];
+    int c = 0;
+    for (int j = 0; j < m; ++j) {
+      const int dj = t.depth[kept[j]];
+      c += (dj < di) || (dj == di && j < i);
+    }
+    t.v_row_of_node[kept[i]] = 1 + c;
+  }
+  __syncthreads();
+  for (int i = tid; i < m; i += blockDim.x) {
+    const int nd = kept[i];
+    const int r = t.v_row_of_node[nd];
+    const int par = t.parent[nd];
+    t.v_tok[r] = t.tok[nd];
+    t.v_node[r] = nd;
+    t.v_logv[r] = t.logv[nd];
+    t.v_parent[r] = (par < 0) ? 0 : t.v_row_of_node[par];
+  }
+  if (tid == 0) {
+    t.v_tok[0] = *root_token;
+    t.v_node[0] = -1;
+    t.v_logv[0] = 0.f;
+    t.v_parent[0] = -1;
+    t.counts[3] = 1 + m;
+  }
+  __syncthreads();
+  build_masks(t, 1 + m, ctx);
+}
+
+__global__ __launch_bounds__(128) void tree_masks_kernel(TreeDev t, int n_rows, int ctx,
+                                                        const int32_t* root) {
+  if (threadIdx.x == 0) {
+    t.v_tok[0] = *root;
+    t.v_parent[0] = -1;
+    t.counts[3] = n_rows;
+  }
+  __syncthreads();
+  build_masks(t, n_rows, ctx);
+}
+
+__global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g, int max_depth,
+                                                    int32_t* acc, int32_t* new_tok, int32_t* cu_src) {
+  const int lane = threadIdx.x;
+  const int n = t.counts[3];
+  int cur = 0, L = 0;
+  for (int step = 0; step < max_depth; ++step) {
+    const int want = g[cur];
+    int found = 0x7fffffff;
+    for (int r = 1 + lane; r < n; r += 64)
+      if (t.v_parent[r] == cur && t.v_tok[r] == want) found = min(found, r);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) found = min(found, __shfl_xor(found, o));
+    if (found == 0x7fffffff) break;
+    if (lane == 0) {
+      acc[2 + L] = found;
+      new_tok[L] = want;
+      cu_src[L + 1] = found;
+    }
+    cur = found;
+    ++L;
+  }
+  if (lane == 0) {
+    acc[0] = L;
+    acc[1] = g[cur];
+    new_tok[L] = g[cur];
+    cu_src[0] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tree_append(TreeDev t, TreeParams p, const int32_t* ids, const float* logp,
+                              int pass, int ctx, hipStream_t st) {
+  hipLaunchKernelGGL(tree_append_kernel, dim3(1), dim3(256), 0, st, t, p, ids, logp, pass, ctx);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_finalize(TreeDev t, TreeParams p, int ctx, const int32_t* root_token,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(tree_finalize_kernel, dim3(1), dim3(1024), 0, st, t, p, ctx, root_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root_token,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(tree_masks_kernel, dim3(1), dim3(128), 0, st, t, n_rows, ctx, root_token);
+  return hipGetLastError();
+}
+
+hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
+                         int32_t* new_tok, int32_t* cu_src, hipStream_t st) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, t, g, max_depth, acc, new_tok, cu_src);
+  return hipGetLastError();
+}

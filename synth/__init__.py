@@ -159,3 +159,17 @@ def gpu_fill_const(dst_ptr: int, n: int, value: float, stream_ptr: int) -> None:
     rc = _load_gpu().synth_gpu_fill_const_f32(n, value, dst_ptr, stream_ptr)
     if rc != 0:
         raise RuntimeError(f"synth_gpu_fill_const_f32 failed: hipError {rc}")
+
+
+def fill_weights(table, base_ptr: int, seed: int, stream_ptr: int) -> None:
+    """Write every tensor of a weight table (list of dicts with kind, group,
+    layer, dtype (0 fp32 / 1 bf16), rows, cols, offset) into device memory at
+    base_ptr: norm gains are 1, every matrix is its own seeded stream."""
+    for t in table:
+        n = int(t["rows"]) * int(t["cols"])
+        dst = base_ptr + int(t["offset"])
+        if t["kind"] in NORM_KINDS:
+            gpu_fill_const(dst, n, 1.0, stream_ptr)
+        else:
+            gpu_fill(dst, n, seed, stream_id(t["kind"], t["group"], t["layer"]),
+                     "bf16" if t["dtype"] == 1 else "f32", stream_ptr)

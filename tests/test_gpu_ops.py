@@ -1,0 +1,125 @@
+"""Kernel-level parity of the projection and LM-head kernels (eagle_ops.h)
+against fp64 numpy on the same bf16 / fp32 inputs."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+E = pytest.importorskip("speculative_decoding_draft_amd")
+
+BF16, F32 = 1, 0
+
+
+def _rand(shape, gen, scale, dtype):
+    t = torch.randn(shape, generator=gen, dtype=torch.float32) * scale
+    return t.to(torch.bfloat16) if dtype == BF16 else t
+
+
+def _ws(nbytes):
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
+
+
+def _rel(got, ref):
+    """max over rows of |got - ref|_inf / |ref|_inf"""
+    num = np.abs(got - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1) + 1e-30
+    return float((num / den).max())
+
+
+LINEAR = [  # (dtype, M, N, K): split-K, tails, several M tiles, prefill-sized M
+    (BF16, 1, 4096, 4096), (BF16, 10, 4096, 8192), (BF16, 27, 12288, 4096),
+    (BF16, 61, 4096, 11008), (BF16, 65, 1000, 1024), (BF16, 100, 256, 512),
+    (BF16, 256, 512, 4096), (F32, 17, 256, 256), (F32, 17, 256, 688), (F32, 33, 1024, 512),
+]
+
+
+@pytest.mark.parametrize("dtype,M,N,K", LINEAR)
+@pytest.mark.parametrize("epi", [0, 1])
+def test_linear(dtype, M, N, K, epi):
+    print(f"linear dtype={dtype} M={M} N={N} K={K} epi={epi}", flush=True)
+    gen = torch.Generator().manual_seed(M * 131 + N * 7 + K + epi)
+    x = _rand((M, K), gen, 1.0, dtype)
+    w = _rand((N, K), gen, 0.02, dtype)
+    y0 = torch.randn((M, N), generator=gen)
+    ref = x.double().numpy() @ w.double().numpy().T
+    y = (y0.clone() if epi == 1 else torch.zeros(M, N)).cuda()
+    ws = _ws(E.op_linear_workspace(dtype, epi, M, N, K))
+    E.op_linear(dtype, epi, x.cuda(), w.cuda(), y, M, N, K, ws)
+    torch.cuda.synchronize()
+    got = y.cpu().double().numpy()
+    if epi == 1:
+        got = got - y0.double().numpy()
+    assert _rel(got, ref) < 1e-4
+    if epi == 0:   # same bits on a second run
+        y2 = torch.zeros(M, N, device="cuda")
+        E.op_linear(dtype, epi, x.cuda(), w.cuda(), y2, M, N, K, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y2.cpu(), y.cpu())
+
+
+@pytest.mark.parametrize("dtype,M,N,K", [(BF16, 61, 11008, 4096), (BF16, 10, 1376, 1024),
+                                         (BF16, 1, 11008, 4096), (F32, 17, 688, 256)])
+def test_swiglu(dtype, M, N, K):
+    print(f"swiglu dtype={dtype} M={M} N={N} K={K}", flush=True)
+    gen = torch.Generator().manual_seed(M + N + K)
+    x = _rand((M, K), gen, 1.0, dtype)
+    w = _rand((2 * N, K), gen, 0.02, dtype)
+    g = x.double().numpy() @ w[:N].double().numpy().T
+    u = x.double().numpy() @ w[N:].double().numpy().T
+    ref = g / (1 + np.exp(-g)) * u
+    out = torch.zeros((M, N), dtype=torch.bfloat16 if dtype == BF16 else torch.float32, device="cuda")
+    ws = _ws(E.op_linear_workspace(dtype, 2, M, N, K))
+    E.op_linear(dtype, 2, x.cuda(), w.cuda(), out, M, N, K, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().double().numpy()
+    tol = (2.0 ** -8 if dtype == BF16 else 1e-5) * np.abs(ref) + 1e-4 * np.abs(ref).max()
+    assert np.all(np.abs(got - ref) <= tol)
+
+
+@pytest.mark.parametrize("dtype,M,V,H,k", [(BF16, 1, 32000, 4096, 10), (BF16, 10, 32000, 4096, 10),
+                                           (BF16, 8, 5000, 1024, 8), (F32, 4, 1024, 256, 4),
+                                           (F32, 1, 1000, 256, 16)])
+def test_lmhead_topk(dtype, M, V, H, k):
+    print(f"topk dtype={dtype} M={M} V={V} H={H} k={k}", flush=True)
+    gen = torch.Generator().manual_seed(M + V + H + k)
+    x = _rand((M, H), gen, 1.0, dtype)
+    w = _rand((V, H), gen, 0.02, dtype)
+    lg = x.double().numpy() @ w.double().numpy().T
+    ids = torch.zeros((M, k), dtype=torch.int32, device="cuda")
+    lp = torch.zeros((M, k), dtype=torch.float32, device="cuda")
+    ws = _ws(E.op_lmhead_workspace(M, V, k))
+    E.op_lmhead(dtype, k, x.cuda(), w.cuda(), M, V, H, ids, lp, None, ws)
+    torch.cuda.synchronize()
+    ids, lp = ids.cpu().numpy(), lp.cpu().numpy()
+    for r in range(M):
+        order = np.lexsort((np.arange(V), -lg[r]))
+        srt = lg[r][order]
+        if np.min(srt[:k] - srt[1:k + 1]) < 1e-4:
+            continue      # near-tie inside the top k+1: the order is not determined
+        assert list(ids[r]) == list(order[:k])
+        ref_lp = lg[r] - lg[r].max() - np.log(np.exp(lg[r] - lg[r].max()).sum())
+        assert np.allclose(lp[r], ref_lp[ids[r]], atol=2e-5)
+
+
+@pytest.mark.parametrize("dtype,M,V,H", [(BF16, 61, 32000, 4096), (BF16, 100, 3000, 1024),
+                                         (F32, 17, 1024, 256)])
+def test_lmhead_argmax(dtype, M, V, H):
+    print(f"argmax dtype={dtype} M={M} V={V} H={H}", flush=True)
+    gen = torch.Generator().manual_seed(M * V + H)
+    x = _rand((M, H), gen, 1.0, dtype)
+    w = _rand((V, H), gen, 0.02, dtype)
+    lg = x.double().numpy() @ w.double().numpy().T
+    g = torch.zeros(M, dtype=torch.int32, device="cuda")
+    mg = torch.zeros(M, dtype=torch.float32, device="cuda")
+    logits = torch.zeros((M, V), dtype=torch.float32, device="cuda")
+    ws = _ws(E.op_lmhead_workspace(M, V, 0))
+    E.op_lmhead(dtype, 0, x.cuda(), w.cuda(), M, V, H, g, mg, logits, ws)
+    torch.cuda.synchronize()
+    g, mg, logits = g.cpu().numpy(), mg.cpu().numpy(), logits.cpu().double().numpy()
+    assert _rel(logits, lg) < 1e-4
+    srt = np.sort(lg, axis=1)
+    ref_margin = srt[:, -1] - srt[:, -2]
+    ok = ref_margin > 1e-4
+    assert np.array_equal(g[ok], np.argmax(lg, axis=1)[ok])
+    assert np.allclose(mg, ref_margin, atol=2e-4)
