@@ -231,6 +231,29 @@ eagle_status eagle_debug_read(eagle_ctx* ctx, int32_t what, void* host_dst, uint
                               int32_t* rows);
 eagle_status eagle_set_debug(eagle_ctx* ctx, int32_t on);
 
+/* Profiling: while enabled, every kernel launch of the context is bracketed
+ * by HIP events on its stream and attributed to a class; eagle_profile_read
+ * synchronises and reports, per class, launches, summed device time and the
+ * algorithmic bytes those launches must move (weights read once, activation
+ * operands and outputs). Enabling resets the counters. The events add host
+ * work per launch, so timed runs keep profiling off. */
+enum {
+  EAGLE_PROF_GEMM = 0,      /* projections (target and draft layers, draft FC) */
+  EAGLE_PROF_ATTN = 1,      /* tree-masked attention and its chunk combine */
+  EAGLE_PROF_LMHEAD = 2,    /* LM head with argmax or softmax/top-k */
+  EAGLE_PROF_ROWS = 3,      /* embedding, norms, RoPE + KV append, gathers */
+  EAGLE_PROF_TREE = 4,      /* tree expansion/rerank and acceptance */
+  EAGLE_PROF_KV = 5,        /* KV compaction */
+  EAGLE_PROF_CLASSES = 6
+};
+typedef struct eagle_profile {
+  int64_t launches[EAGLE_PROF_CLASSES];
+  double ms[EAGLE_PROF_CLASSES];
+  double bytes[EAGLE_PROF_CLASSES];
+} eagle_profile;
+eagle_status eagle_profile_enable(eagle_ctx* ctx, int32_t on);
+eagle_status eagle_profile_read(eagle_ctx* ctx, eagle_profile* out);
+
 void eagle_free(eagle_ctx* ctx);
 const char* eagle_last_error(const eagle_ctx* ctx);
 const char* eagle_status_string(eagle_status s);

@@ -3,7 +3,10 @@
  * pointers, for composing other pipelines and for parity testing of the
  * kernels on their own. All calls enqueue on `stream` (NULL = default)
  * and do not synchronise; pointers are device pointers unless stated.
- * Element type `dtype` is EAGLE_F32 or EAGLE_BF16 (raw bf16 bits).
+ * Element type `dtype` is EAGLE_F32 or EAGLE_BF16 (raw bf16 bits) of the
+ * weights. Activations are fp32 values: for EAGLE_F32 one fp32 array; for
+ * EAGLE_BF16 two bf16 planes of the same shape, back to back, hi = bf16(v)
+ * then lo = bf16(v - hi), which the kernels multiply as hi*w + lo*w.
  */
 #ifndef EAGLE_OPS_H
 #define EAGLE_OPS_H
@@ -26,11 +29,11 @@ uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, i
 /* Projection of M activation rows by a weight W, as in a Linear layer
  * (y = x W^T; the decode/verify projections of the target and draft
  * decoder layers, "Lesson 13.11 - EAGLE", section "The big idea").
- *   x: [M, K] dtype, row-major. W: [N, K] dtype (EPI_SWIGLU: [2N, K], the
- *   N gate rows then the N up rows).
+ *   x: [M, K] activations, row-major. W: [N, K] dtype (EPI_SWIGLU: [2N, K],
+ *   the N gate rows then the N up rows).
  *   EPI_STORE : y fp32 [M, N],  y  = x W^T
  *   EPI_ADD   : y fp32 [M, N],  y += x W^T  (residual update)
- *   EPI_SWIGLU: y dtype [M, N], y  = silu(x Wg^T) * (x Wu^T)
+ *   EPI_SWIGLU: y [M, N] activations, y = silu(x Wg^T) * (x Wu^T)
  * Accumulation is fp32; summation order is fixed, so results repeat
  * bit for bit. Requires K a multiple of 32 (bf16) or 16 (fp32), M >= 1.
  * EAGLE_E_INVALID on bad sizes, EAGLE_E_BUFFER if the workspace is too
@@ -42,7 +45,7 @@ eagle_status eagle_op_linear(int32_t dtype, int32_t epilogue, const void* x, con
 /* Workspace bytes of eagle_op_lmhead (k = 0 for the greedy variant). */
 uint64_t eagle_op_lmhead_workspace(int32_t M, int32_t V, int32_t k);
 
-/* LM head over M feature rows x [M, H] with W_lm [V, H] ("Lesson 13.11",
+/* LM head over M feature rows x [M, H] (activations) with W_lm [V, H] ("Lesson 13.11",
  * section "The big idea": the LM head turns a feature into probabilities).
  *   k = 0 (verify): out_ids[m] = argmax_v logits (lowest id on ties),
  *          out_vals[m] = top-1 minus top-2 logit; logits [M, V] fp32 are

@@ -8,12 +8,16 @@ GPU library (only the seeded input generators in ``synth/`` serve both).
 It is a plain, slow, obviously correct implementation in numpy, accumulating
 in fp64 and rounding at the points fixed by the numerics contract:
 
-* fp32 configs: every tensor is rounded to fp32 where it is produced.
-* bf16 configs: weights, embedding rows, the K/V cache and every matrix-product
-  operand that is an activation (normed activations, query, attention output,
-  SwiGLU product, draft FC inputs, features fed to the LM head) are rounded
-  to bf16 (round-to-nearest-even of the fp32 value); accumulations, the
-  residual stream, RoPE, softmax, logits and log-probabilities are fp32.
+* every activation is rounded to fp32 where it is produced (normed
+  activations, q/k/v, attention output, SwiGLU product, residual stream,
+  features, logits, log-probabilities);
+* bf16 configs store the weights (embedding and LM head included) in bf16
+  (round-to-nearest-even of the generated fp32 value); activations and the
+  K/V cache stay fp32. Rounding activations or K/V to bf16 would make any
+  two implementations that sum in different orders drift apart to the bf16
+  noise floor within a few layers (a rounding flip moves the next layer's
+  values by far more than the accumulation difference that caused it), so
+  it is not part of the contract.
 
 Sources (web pages on EAGLE, EAGLE-2 and EAGLE-3):
   [L13] "Lesson 13.11 - EAGLE: Feature-Level Drafting for Faster Inference"

@@ -61,8 +61,8 @@ class Session:
         vis = causal_vis(M, first, self.dkv[0].shape[0], prefix_from=1)
         out = self.draft.rows(s, tokens, slots, slots, vis, self.dkv)
         self.root_out = out[-1]
-        ids, lp, _ = self.draft.topk(out[-1:], self.k)
-        self.root_ids, self.root_logp = ids[0], lp[0]
+        ids, lp, lg = self.draft.topk(out[-1:], self.k)
+        self.root_ids, self.root_logp, self.root_logits = ids[0], lp[0], lg[0]
 
     # ------------------------------------------------------------ prefill
     def prefill(self, prompt):
@@ -100,6 +100,9 @@ class Session:
             return out
 
         t = T.Tree()
+        # draft logits of the row expanding each node (-1: the root row), kept
+        # so that tests can tell near-ties from real differences
+        self.row_logits = {-1: self.root_logits}
 
         def expand(chosen):
             nodes = t.nodes
@@ -120,7 +123,9 @@ class Session:
             out = self.draft.rows(np.stack(s), toks, np.array(pos), slots, vis, self.dkv)
             for i, e in enumerate(chosen):
                 row_out[e] = out[i]
-            ids, lp, _ = self.draft.topk(out, k)
+            ids, lp, lg = self.draft.topk(out, k)
+            for i, e in enumerate(chosen):
+                self.row_logits[e] = lg[i]
             return ids, lp
 
         if self.budget == 0:
@@ -151,7 +156,9 @@ class Session:
                 vis[r, ctx + a] = True
         keep = self.cfg.feat_layers if self.cfg.head == "e3" else ()
         f, kept = self.target.forward(rows["token"], pos, slots, vis, self.kv, keep)
-        g, margin = argmax_lowest(self.target.logits(f))
+        logits = self.target.logits(f)
+        self.last_logits, self.last_features = logits, f
+        g, margin = argmax_lowest(logits)
         path, bonus = T.accept(rows["token"], rows["parent"], g)
         L = len(path)
         new = [rows["token"][r] for r in path] + [bonus]

@@ -33,7 +33,7 @@ import synth
 from synth import (ATTN_NORM, DRAFT, EMBED, FC, FFN_NORM, FINAL_NORM, GLOBAL,
                    LM_HEAD, TARGET, WDOWN, WGATE, WK, WO, WQ, WUP, WV)
 
-from .numerics import apply_rope, log_softmax, operand, rmsnorm, rope_tables, silu, to_f32
+from .numerics import apply_rope, kv_store, log_softmax, operand, rmsnorm, rope_tables, silu, to_f32
 
 
 class Config:
@@ -142,8 +142,8 @@ def decoder_layer(cfg: Config, W: Weights, group: int, layer: int, h, pos,
     cos, sin = rope_tables(pos, d, cfg.rope_base)
     q = to_f32(apply_rope(q, cos, sin))
     k = to_f32(apply_rope(k, cos, sin))
-    kc[slots] = operand(k, dt)
-    vc[slots] = operand(v, dt)
+    kc[slots] = kv_store(k, dt)
+    vc[slots] = kv_store(v, dt)
     o = to_f32(attention(operand(q, dt), kc, vc, vis, 1.0 / math.sqrt(d)))
     h = to_f32(h + to_f32(matmul_t(operand(o.reshape(M, -1), dt), W.get(WO, group, layer))))
     x2 = operand(rmsnorm(h, W.get(FFN_NORM, group, layer), cfg.eps), dt)

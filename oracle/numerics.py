@@ -22,8 +22,14 @@ def to_bf16(x):
 
 
 def operand(x, dtype: str):
-    """Rounding applied to an activation before it enters a matrix product."""
-    return to_bf16(x) if dtype == "bf16" else to_f32(x)
+    """An activation entering a matrix product: fp32 for both dtypes (only
+    the weights are stored in bf16)."""
+    return to_f32(x)
+
+
+def kv_store(x, dtype: str):
+    """K and V as written to the cache: fp32 for both dtypes."""
+    return to_f32(x)
 
 
 def rmsnorm(h, gain, eps: float):

@@ -60,6 +60,13 @@ class Tree(ctypes.Structure):
                 ("node_logp", f32 * MAX_NODES)]
 
 
+PROF_CLASSES = ["gemm", "attention", "lmhead", "rows", "tree", "kv"]
+
+
+class Profile(ctypes.Structure):
+    _fields_ = [("launches", i64 * 6), ("ms", ctypes.c_double * 6), ("bytes", ctypes.c_double * 6)]
+
+
 class Stats(ctypes.Structure):
     _fields_ = [("cycles", i64), ("committed", i64), ("accept_hist", i64 * (MAX_DEPTH + 1)),
                 ("seconds", ctypes.c_double)]
@@ -89,6 +96,8 @@ def lib():
         L.eagle_committed.argtypes = [vp, P(i32), i32, P(i32)]
         L.eagle_debug_read.argtypes = [vp, i32, vp, u64, P(i32)]
         L.eagle_set_debug.argtypes = [vp, i32]
+        L.eagle_profile_enable.argtypes = [vp, i32]
+        L.eagle_profile_read.argtypes = [vp, P(Profile)]
         L.eagle_free.argtypes = [vp]
         L.eagle_free.restype = None
         L.eagle_last_error.argtypes = [vp]
@@ -251,6 +260,15 @@ class Engine:
         self._check(lib().eagle_committed(self.ctx, _i32p(out), n.value, ctypes.byref(n)),
                     "eagle_committed")
         return out[:n.value].tolist()
+
+    def profile(self, on: bool = True):
+        self._check(lib().eagle_profile_enable(self.ctx, 1 if on else 0), "eagle_profile_enable")
+
+    def profile_read(self) -> dict:
+        p = Profile()
+        self._check(lib().eagle_profile_read(self.ctx, ctypes.byref(p)), "eagle_profile_read")
+        return {name: dict(launches=p.launches[i], ms=p.ms[i], bytes=p.bytes[i])
+                for i, name in enumerate(PROF_CLASSES)}
 
     def set_debug(self, on: bool = True):
         self._check(lib().eagle_set_debug(self.ctx, 1 if on else 0), "eagle_set_debug")

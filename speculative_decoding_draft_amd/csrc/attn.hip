@@ -6,7 +6,8 @@
 // query rows). S^T = K Q^T and O^T = V^T P^T run on 16x16x32 bf16 MFMA;
 // keys are loaded in an order that makes each lane's 8 scores exactly the
 // P^T operand of the PV product, so P never leaves registers. P is split
-// into bf16 hi + lo parts (two MFMAs) so it keeps ~16 mantissa bits. Chunks
+// into bf16 hi + lo parts (two MFMAs) so it keeps ~16 mantissa bits, and
+// the query arrives the same way (an fp32 activation as two bf16 planes). Chunks
 // are combined with their (max, sum) pairs in a second kernel.
 #include "common.h"
 #include "kernels.h"
@@ -22,6 +23,21 @@ __device__ __forceinline__ T* kv_ptr(const KVView& v, int slot, int sel, int h) 
          ((int64_t)(sel * v.n_kv + h) * v.page + slot % v.page) * v.d;
 }
 
+// K (which = 0) or V (which = 1) element of one cache row.
+template <typename T> struct KVStore;
+template <> struct KVStore<float> {
+  __device__ static void put(const KVView& v, int slot, int which, int h, int i, float x) {
+    kv_ptr<float>(v, slot, which, h)[i] = x;
+  }
+};
+template <> struct KVStore<bf16_t> {
+  __device__ static void put(const KVView& v, int slot, int which, int h, int i, float x) {
+    const bf16_t hi = f32_to_bf16(x);
+    kv_ptr<bf16_t>(v, slot, 2 * which, h)[i] = hi;
+    kv_ptr<bf16_t>(v, slot, 2 * which + 1, h)[i] = f32_to_bf16(x - bf16_to_f32(hi));
+  }
+};
+
 __device__ __forceinline__ bool row_sees(const RowVis& rv, int prehi, uint64_t m0, uint64_t m1,
                                          int key) {
   if (key >= rv.pre_lo && key < prehi) return true;
@@ -31,7 +47,7 @@ __device__ __forceinline__ bool row_sees(const RowVis& rv, int prehi, uint64_t m
 }
 
 struct AttnArgs {
-  const bf16_t* q;
+  const bf16_t* q; int64_t qlo;
   KVView kv;
   RowVis vis;
   int M, nq, group;
@@ -42,7 +58,7 @@ struct AttnArgs {
 
 __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
   constexpr int D = 128;
-  __shared__ bf16_t vt[D][40];   // V^T block: [d][32 keys] (+8 pad)
+  __shared__ bf16_t vt[2][D][40];   // V^T block, hi and lo: [d][32 keys] (+8 pad)
   const int chunk = blockIdx.x, h = blockIdx.y, rt = blockIdx.z;
   const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
   const int hk = h / a.group;
@@ -51,10 +67,13 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
   const int row = rt * 16 + lr;
   const int rowc = min(row, a.M - 1);
 
-  uint4 qf[4];
+  uint4 qf[4], ql[4];   // query as hi + lo bf16 planes
   const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qf[s] = ld16(qp + 32 * s);
+  for (int s = 0; s < 4; ++s) {
+    qf[s] = ld16(qp + 32 * s);
+    ql[s] = ld16(qp + a.qlo + 32 * s);
+  }
   const int prehi = a.vis.prehi[rowc];
   const uint64_t mk0 = a.vis.mask[2 * rowc], mk1 = a.vis.mask[2 * rowc + 1];
 
@@ -69,9 +88,16 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
     for (int hh = 0; hh < 2; ++hh) {
       const int key = min(kb + 8 * (lr >> 2) + 4 * hh + (lr & 3), k1 - 1);
       const bf16_t* kp = kv_ptr<bf16_t>(a.kv, key, 0, hk) + 8 * g;
+      const bf16_t* kpl = kv_ptr<bf16_t>(a.kv, key, 1, hk) + 8 * g;
       sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) Mma<bf16_t>::mma(ld16(kp + 32 * s), qf[s], sc[hh]);
+      for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+        const uint4 kf = ld16(kp + 32 * s);
+        const uint4 kl = ld16(kpl + 32 * s);
+        Mma<bf16_t>::mma(kf, qf[s], sc[hh]);
+        Mma<bf16_t>::mma(kf, ql[s], sc[hh]);
+        Mma<bf16_t>::mma(kl, qf[s], sc[hh]);
+      }
     }
     float p[8];
     float bm = -INFINITY;
@@ -113,10 +139,15 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
       const int idx = it * 64 + lane;
       const int kl = idx >> 4, dc = idx & 15;
       const int key = min(kb + kl, k1 - 1);
-      const uint4 v = ld16(kv_ptr<bf16_t>(a.kv, key, 1, hk) + 8 * dc);
+      const uint4 v = ld16(kv_ptr<bf16_t>(a.kv, key, 2, hk) + 8 * dc);
+      const uint4 vl = ld16(kv_ptr<bf16_t>(a.kv, key, 3, hk) + 8 * dc);
       const bf16_t* vv = reinterpret_cast<const bf16_t*>(&v);
+      const bf16_t* vvl = reinterpret_cast<const bf16_t*>(&vl);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) vt[8 * dc + j][kl] = vv[j];
+      for (int j = 0; j < 8; ++j) {
+        vt[0][8 * dc + j][kl] = vv[j];
+        vt[1][8 * dc + j][kl] = vvl[j];
+      }
     }
     __syncthreads();
     bf16_t ph[8], pl[8];
@@ -128,10 +159,12 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
     const uint4 phi = *reinterpret_cast<const uint4*>(ph);
     const uint4 plo = *reinterpret_cast<const uint4*>(pl);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint4 va = *reinterpret_cast<const uint4*>(&vt[16 * dt + lr][8 * g]);
+    for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+      const uint4 va = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][8 * g]);
+      const uint4 val = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][8 * g]);
       Mma<bf16_t>::mma(va, phi, o[dt]);
       Mma<bf16_t>::mma(va, plo, o[dt]);
+      Mma<bf16_t>::mma(val, phi, o[dt]);
     }
   }
   if (row < a.M) {
@@ -151,7 +184,7 @@ __global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* opart, const float* mlpart,
                                                            int n_chunks, int M, int nq, int d,
-                                                           T* out) {
+                                                           T* out, int64_t lo) {
   const int r = blockIdx.x, h = blockIdx.y;
   float gm = -INFINITY;
   for (int c = 0; c < n_chunks; ++c) gm = fmaxf(gm, mlpart[(((int64_t)c * M + r) * nq + h) * 2]);
@@ -164,7 +197,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* opart, c
       den += w * ml[1];
       num += w * opart[(((int64_t)c * M + r) * nq + h) * d + j];
     }
-    out[((int64_t)r * nq + h) * d + j] = Elem<T>::from_f(num / den);
+    Opnd<T>::store(out, lo, ((int64_t)r * nq + h) * d + j, num / den);
   }
 }
 
@@ -225,7 +258,7 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, int64_t ldh, const float* gain,
                                                       int K, float eps, T* out_t, int64_t ldo,
-                                                      float* out_f, int64_t ldf) {
+                                                      int64_t lo, float* out_f, int64_t ldf) {
   __shared__ float sh[256];
   const int r = blockIdx.x;
   const float* x = h + (int64_t)r * ldh;
@@ -236,22 +269,22 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, int64_t ld
   for (int i = threadIdx.x; i < K; i += 256) {
     const float v = x[i] * inv * gain[i];
     if (out_f) out_f[(int64_t)r * ldf + i] = v;
-    out_t[(int64_t)r * ldo + i] = Elem<T>::from_f(v);
+    Opnd<T>::store(out_t, lo, (int64_t)r * ldo + i, v);
   }
 }
 
 template <typename T>
-__global__ void cast_kernel(const float* h, int H, T* out) {
+__global__ void cast_kernel(const float* h, int H, T* out, int64_t lo) {
   const int r = blockIdx.x;
   for (int i = threadIdx.x; i < H; i += blockDim.x)
-    out[(int64_t)r * H + i] = Elem<T>::from_f(h[(int64_t)r * H + i]);
+    Opnd<T>::store(out, lo, (int64_t)r * H + i, h[(int64_t)r * H + i]);
 }
 
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int nq, int nkv, int d,
                                                       const int32_t* pos, const int32_t* slot,
                                                       const float* cos_t, const float* sin_t,
-                                                      T* q_out, KVView kv) {
+                                                      T* q_out, int64_t qlo, KVView kv) {
   const int r = blockIdx.x;
   const int half = d / 2;
   const int width = (nq + 2 * nkv) * d;
@@ -266,32 +299,31 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int nq, 
     const float y1 = x1 * c[i] - x2 * s[i];
     const float y2 = x2 * c[i] + x1 * s[i];
     if (head < nq) {
-      T* dst = q_out + ((int64_t)r * nq + head) * d;
-      dst[i] = Elem<T>::from_f(y1);
-      dst[i + half] = Elem<T>::from_f(y2);
+      const int64_t base = ((int64_t)r * nq + head) * d;
+      Opnd<T>::store(q_out, qlo, base + i, y1);
+      Opnd<T>::store(q_out, qlo, base + i + half, y2);
     } else {
-      T* dst = kv_ptr<T>(kv, sl, 0, head - nq);
-      dst[i] = Elem<T>::from_f(y1);
-      dst[i + half] = Elem<T>::from_f(y2);
+      KVStore<T>::put(kv, sl, 0, head - nq, i, y1);
+      KVStore<T>::put(kv, sl, 0, head - nq, i + half, y2);
     }
   }
   const float* vsrc = x + (nq + nkv) * d;
   for (int idx = threadIdx.x; idx < nkv * d; idx += blockDim.x) {
     const int head = idx / d, i = idx % d;
-    kv_ptr<T>(kv, sl, 1, head)[i] = Elem<T>::from_f(vsrc[idx]);
+    KVStore<T>::put(kv, sl, 1, head, i, vsrc[idx]);
   }
 }
 
 template <typename T>
 __global__ void draft_input_e1_kernel(const T* E, const int32_t* tok, const float* feat,
-                                      const int32_t* idx, int H, T* x) {
+                                      const int32_t* idx, int H, T* x, int64_t lo) {
   const int r = blockIdx.x;
   const T* e = E + (int64_t)tok[r] * H;
   const float* f = feat + (int64_t)idx[r] * H;
-  T* xr = x + (int64_t)r * 2 * H;
+  const int64_t row = (int64_t)r * 2 * H;
   for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    xr[i] = e[i];
-    xr[H + i] = Elem<T>::from_f(f[i]);
+    Opnd<T>::store(x, lo, row + i, Elem<T>::to_f(e[i]));
+    Opnd<T>::store(x, lo, row + H + i, f[i]);
   }
 }
 
@@ -299,7 +331,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void draft_input_e3_kernel(const T* E, const int32_t* tok,
                                                              const float* feat, const int32_t* idx,
                                                              const float* gain, float eps, int H,
-                                                             T* x, float* h) {
+                                                             T* x, int64_t lo, float* h) {
   __shared__ float sh[256];
   const int r = blockIdx.x;
   const T* e = E + (int64_t)tok[r] * H;
@@ -312,10 +344,10 @@ __global__ __launch_bounds__(256) void draft_input_e3_kernel(const T* E, const i
   for (int i = threadIdx.x; i < H; i += 256) ss += f[i] * f[i];
   ss = block_sum_256(ss, sh);
   const float inv = 1.0f / sqrtf(ss / (float)(2 * H) + eps);
-  T* xr = x + (int64_t)r * 2 * H;
+  const int64_t row = (int64_t)r * 2 * H;
   for (int i = threadIdx.x; i < H; i += 256) {
-    xr[i] = Elem<T>::from_f(Elem<T>::to_f(e[i]) * inv * gain[i]);
-    xr[H + i] = Elem<T>::from_f(f[i] * inv * gain[H + i]);
+    Opnd<T>::store(x, lo, row + i, Elem<T>::to_f(e[i]) * inv * gain[i]);
+    Opnd<T>::store(x, lo, row + H + i, f[i] * inv * gain[H + i]);
     h[(int64_t)r * H + i] = f[i];
   }
 }
@@ -327,17 +359,21 @@ __global__ void gather_f32_kernel(const float* src, int64_t ld, const int32_t* i
 }
 
 template <typename T>
-__global__ void gather_t_kernel(const T* src, int64_t ld, const int32_t* idx, int W, T* dst) {
+__global__ void gather_t_kernel(const T* src, int64_t ld, int64_t src_lo, const int32_t* idx, int W,
+                                T* dst, int64_t dst_lo) {
   const int r = blockIdx.x;
   const T* s = src + (int64_t)idx[r] * ld;
-  for (int i = threadIdx.x; i < W; i += blockDim.x) dst[(int64_t)r * W + i] = s[i];
+  for (int i = threadIdx.x; i < W; i += blockDim.x) {
+    dst[(int64_t)r * W + i] = s[i];
+    if (Opnd<T>::SPLIT) dst[dst_lo + (int64_t)r * W + i] = s[src_lo + i];
+  }
 }
 
 template <typename T>
-__global__ void store_feat_kernel(const float* h, int H, T* dst, int64_t ldd) {
+__global__ void store_feat_kernel(const float* h, int H, T* dst, int64_t ldd, int64_t lo) {
   const int r = blockIdx.x;
   for (int i = threadIdx.x; i < H; i += blockDim.x)
-    dst[(int64_t)r * ldd + i] = Elem<T>::from_f(h[(int64_t)r * H + i]);
+    Opnd<T>::store(dst, lo, (int64_t)r * ldd + i, h[(int64_t)r * H + i]);
 }
 
 __global__ void rows_causal_kernel(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
@@ -357,13 +393,13 @@ __global__ void rows_causal_kernel(int first, int M, int32_t* pos, int32_t* slot
 // since a destination may be an earlier source.
 template <typename T>
 __global__ void kv_compact_kernel(KVView v, int64_t layer_elems, const int32_t* Lp,
-                                  const int32_t* path, int ctx) {
+                                  const int32_t* path, int ctx, int planes) {
   const int layer = blockIdx.x, h = blockIdx.y;
   const int L = *Lp;
   if (L <= 0) return;
   KVView lv = v;
   lv.base = (T*)v.base + (int64_t)layer * layer_elems;
-  for (int e = threadIdx.x; e < 2 * v.d; e += blockDim.x) {
+  for (int e = threadIdx.x; e < planes * v.d; e += blockDim.x) {
     const int sel = e / v.d, i = e % v.d;
     T vals[EAGLE_COMPACT_MAX];
     for (int j = 0; j < L; ++j) vals[j] = kv_ptr<T>(lv, ctx + path[j], sel, h)[i];
@@ -394,48 +430,49 @@ hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int
 }
 
 hipError_t launch_rmsnorm(int dtype, const float* h, int64_t ldh, const float* gain, int K, float eps,
-                          int M, void* out_t, int64_t ldo, float* out_f, int64_t ldf,
+                          int M, void* out_t, int64_t ldo, int64_t lo, float* out_f, int64_t ldf,
                           hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (bf16_t*)out_t, ldo, out_f, ldf),
-              hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (float*)out_t, ldo, out_f, ldf));
+              hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (bf16_t*)out_t, ldo, lo, out_f, ldf),
+              hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (float*)out_t, ldo, lo, out_f, ldf));
   return hipGetLastError();
 }
 
-hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, hipStream_t st) {
+hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, int64_t lo,
+                       hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, (bf16_t*)out_t),
-              hipLaunchKernelGGL(cast_kernel<float>, dim3(M), dim3(256), 0, st, h, H, (float*)out_t));
+              hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, (bf16_t*)out_t, lo),
+              hipLaunchKernelGGL(cast_kernel<float>, dim3(M), dim3(256), 0, st, h, H, (float*)out_t, lo));
   return hipGetLastError();
 }
 
 hipError_t launch_rope_kv(int dtype, const float* qkv, int M, int nq, int nkv, int d,
                           const int32_t* pos, const int32_t* slot, const float* cos_t,
-                          const float* sin_t, void* q_out, KVView kv, hipStream_t st) {
+                          const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, kv),
-              hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, kv));
+              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv),
+              hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv));
   return hipGetLastError();
 }
 
-hipError_t launch_attention(int dtype, const void* q, KVView kv, RowVis vis, int M, int nq, int d,
-                            float scale, float* opart, float* mlpart, void* out_t,
-                            hipStream_t st) {
+hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, RowVis vis, int M,
+                            int nq, int d, float scale, float* opart, float* mlpart, void* out_t,
+                            int64_t olo, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const int group = nq / kv.n_kv;
   if (dtype == 1) {
     if (d != 128) return hipErrorInvalidValue;
     const int n_chunks = (vis.key_end - vis.pre_lo + CHUNK - 1) / CHUNK;
     if (n_chunks <= 0) return hipErrorInvalidValue;
-    AttnArgs a{(const bf16_t*)q, kv, vis, M, nq, group, scale, opart, mlpart};
+    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, scale, opart, mlpart};
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, nq, (M + 15) / 16), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(M, nq), dim3(128), 0, st, opart, mlpart,
-                       n_chunks, M, nq, d, (bf16_t*)out_t);
+                       n_chunks, M, nq, d, (bf16_t*)out_t, olo);
   } else {
     if (d > 256) return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_f32_kernel, dim3(M, nq), dim3(64), 0, st, (const float*)q, kv, vis, M,
@@ -445,21 +482,22 @@ hipError_t launch_attention(int dtype, const void* q, KVView kv, RowVis vis, int
 }
 
 hipError_t launch_draft_input_e1(int dtype, const void* E, const int32_t* tok, const float* feat,
-                                 const int32_t* idx, int M, int H, void* x, hipStream_t st) {
+                                 const int32_t* idx, int M, int H, void* x, int64_t lo,
+                                 hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(draft_input_e1_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, H, (bf16_t*)x),
-              hipLaunchKernelGGL(draft_input_e1_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, H, (float*)x));
+              hipLaunchKernelGGL(draft_input_e1_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, H, (bf16_t*)x, lo),
+              hipLaunchKernelGGL(draft_input_e1_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, H, (float*)x, lo));
   return hipGetLastError();
 }
 
 hipError_t launch_draft_input_e3(int dtype, const void* E, const int32_t* tok, const float* feat,
                                  const int32_t* idx, const float* gain, float eps, int M, int H,
-                                 void* x, float* h, hipStream_t st) {
+                                 void* x, int64_t lo, float* h, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(draft_input_e3_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, gain, eps, H, (bf16_t*)x, h),
-              hipLaunchKernelGGL(draft_input_e3_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, gain, eps, H, (float*)x, h));
+              hipLaunchKernelGGL(draft_input_e3_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, gain, eps, H, (bf16_t*)x, lo, h),
+              hipLaunchKernelGGL(draft_input_e3_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, gain, eps, H, (float*)x, lo, h));
   return hipGetLastError();
 }
 
@@ -470,21 +508,21 @@ hipError_t launch_gather_f32(const float* src, int64_t ld, const int32_t* idx, i
   return hipGetLastError();
 }
 
-hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, const int32_t* idx, int M, int W,
-                           void* dst, hipStream_t st) {
+hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, int64_t src_lo, const int32_t* idx,
+                           int M, int W, void* dst, int64_t dst_lo, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(gather_t_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)src, ld, idx, W, (bf16_t*)dst),
-              hipLaunchKernelGGL(gather_t_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)src, ld, idx, W, (float*)dst));
+              hipLaunchKernelGGL(gather_t_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)src, ld, src_lo, idx, W, (bf16_t*)dst, dst_lo),
+              hipLaunchKernelGGL(gather_t_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)src, ld, src_lo, idx, W, (float*)dst, dst_lo));
   return hipGetLastError();
 }
 
 hipError_t launch_store_feat(int dtype, const float* h, int H, int M, void* dst, int64_t ldd,
-                             hipStream_t st) {
+                             int64_t lo, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(store_feat_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, (bf16_t*)dst, ldd),
-              hipLaunchKernelGGL(store_feat_kernel<float>, dim3(M), dim3(256), 0, st, h, H, (float*)dst, ldd));
+              hipLaunchKernelGGL(store_feat_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, (bf16_t*)dst, ldd, lo),
+              hipLaunchKernelGGL(store_feat_kernel<float>, dim3(M), dim3(256), 0, st, h, H, (float*)dst, ldd, lo));
   return hipGetLastError();
 }
 
@@ -499,7 +537,7 @@ hipError_t launch_rows_causal(int first, int M, int32_t* pos, int32_t* slot, int
 hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int n_layers,
                              const int32_t* L, const int32_t* path, int ctx, hipStream_t st) {
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv), dim3(256), 0, st, layer0, layer_elems, L, path, ctx),
-              hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(n_layers, layer0.n_kv), dim3(256), 0, st, layer0, layer_elems, L, path, ctx));
+              hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv), dim3(512), 0, st, layer0, layer_elems, L, path, ctx, 4),
+              hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(n_layers, layer0.n_kv), dim3(256), 0, st, layer0, layer_elems, L, path, ctx, 2));
   return hipGetLastError();
 }

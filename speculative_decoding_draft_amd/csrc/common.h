@@ -36,6 +36,25 @@ template <> struct Elem<bf16_t> {
   __device__ static bf16_t from_f(float v) { return f32_to_bf16(v); }
 };
 
+// Activation operands of the matrix cores. fp32 configs keep one fp32 plane.
+// bf16 configs keep each value v as two bf16 planes, hi = bf16(v) and
+// lo = bf16(v - hi), the lo plane `lo` elements after the hi plane: 16
+// significant bits, and hi*w + lo*w on the bf16 MFMA gives the product of
+// the fp32 activation with a bf16 weight to that precision.
+template <typename T> struct Opnd;
+template <> struct Opnd<float> {
+  static constexpr bool SPLIT = false;
+  __device__ static void store(float* p, int64_t, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Opnd<bf16_t> {
+  static constexpr bool SPLIT = true;
+  __device__ static void store(bf16_t* p, int64_t lo, int64_t i, float v) {
+    const bf16_t h = f32_to_bf16(v);
+    p[i] = h;
+    p[lo + i] = f32_to_bf16(v - bf16_to_f32(h));
+  }
+};
+
 // ---------------------------------------------------------------- MFMA
 // One "step" is 16 bytes per lane along K: 8 bf16 or 4 fp32 elements.
 // 16x16 tiles: lane l owns row (l & 15) of the A operand and column (l & 15)

@@ -256,7 +256,8 @@ struct eagle_ctx {
   float *cos_t, *sin_t;
   int32_t *tpt, *dpt;
   float *h, *qkv, *tfeat, *gbuf, *hcat, *dout, *opart, *mlpart, *gpart, *hpart, *logits, *margin, *logp;
-  void *xop, *qop, *aop, *fop, *lmh, *lmh2;
+  void *xop, *qop, *aop, *fop, *lmh, *lmh2;   // activation operands (two planes for bf16)
+  int64_t xlo = 0, qlo = 0, alo = 0, flo = 0, lmhlo = 0, lmh2lo = 0;  // lo-plane offsets (elements)
   int32_t *counters, *g, *ids, *acc, *new_tok, *cu_src, *iota, *seq;
   int32_t *rpos, *rslot, *rprehi;
   uint64_t* rmask;
@@ -269,6 +270,12 @@ struct eagle_ctx {
   bool debug = false;
   int last_target_rows = 0, last_verify_rows = 0;
   std::string err;
+  // profiling (eagle_profile_enable)
+  bool prof = false;
+  struct ProfRec { int cls; double bytes; hipEvent_t a, b; };
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+  size_t pool_used = 0;
 };
 
 namespace {
@@ -302,12 +309,19 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
   TAKE(logits, float, (uint64_t)z.Mv * z.V);
   TAKE(margin, float, z.Mv);
   TAKE(logp, float, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
-  TAKE(xop, char, (uint64_t)M * kmax * es);
-  TAKE(qop, char, (uint64_t)M * z.nq * z.d * es);
-  TAKE(aop, char, (uint64_t)M * z.nq * z.d * es);
-  TAKE(fop, char, (uint64_t)M * z.F * es);
-  TAKE(lmh, char, (uint64_t)M * 3 * z.H * es);
-  TAKE(lmh2, char, (uint64_t)(z.D + 1) * 3 * z.H * es);
+  TAKE(xop, char, 2 * (uint64_t)M * kmax * es);
+  TAKE(qop, char, 2 * (uint64_t)M * z.nq * z.d * es);
+  TAKE(aop, char, 2 * (uint64_t)M * z.nq * z.d * es);
+  TAKE(fop, char, 2 * (uint64_t)M * z.F * es);
+  TAKE(lmh, char, 2 * (uint64_t)M * 3 * z.H * es);
+  TAKE(lmh2, char, 2 * (uint64_t)(z.D + 1) * 3 * z.H * es);
+  if (x) {
+    x->xlo = (int64_t)M * kmax;
+    x->qlo = x->alo = (int64_t)M * z.nq * z.d;
+    x->flo = (int64_t)M * z.F;
+    x->lmhlo = (int64_t)M * 3 * z.H;
+    x->lmh2lo = (int64_t)(z.D + 1) * 3 * z.H;
+  }
   TAKE(counters, int32_t, 65536);
   TAKE(g, int32_t, z.Mv);
   TAKE(ids, int32_t, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
@@ -359,7 +373,7 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
 #undef TAKE
 
 uint64_t kv_bytes_of(const Derived& z) {
-  const uint64_t page_elems = 2ull * z.nkv * KV_PAGE * z.d;
+  const uint64_t page_elems = (uint64_t)kv_planes(z.dt) * z.nkv * KV_PAGE * z.d;
   return align_up((uint64_t)z.NL * z.t_pages * page_elems * z.esz) +
          align_up((uint64_t)z.d_pages * page_elems * z.esz);
 }
@@ -390,6 +404,53 @@ eagle_status set_err(eagle_ctx* c, eagle_status s, const char* fmt, ...) {
     if (s_ != EAGLE_OK) return s_;       \
   } while (0)
 
+hipEvent_t take_event(eagle_ctx* c) {
+  if (c->pool_used == c->pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    c->pool.push_back(e);
+  }
+  return c->pool[c->pool_used++];
+}
+
+// Brackets the launches of its scope with events when profiling is on.
+struct Prof {
+  eagle_ctx* c;
+  int cls;
+  double bytes;
+  hipEvent_t a = nullptr;
+  Prof(eagle_ctx* c_, int cls_, double bytes_) : c(c_), cls(cls_), bytes(bytes_) {
+    if (c->prof && (a = take_event(c))) (void)hipEventRecord(a, c->st);
+  }
+  ~Prof() {
+    if (!c->prof || !a) return;
+    hipEvent_t b = take_event(c);
+    if (!b) return;
+    (void)hipEventRecord(b, c->st);
+    c->recs.push_back({cls, bytes, a, b});
+  }
+};
+
+#define PROFILED(cls, bytes, expr)        \
+  do {                                    \
+    Prof p_(c, (cls), (double)(bytes));   \
+    HCHK(expr);                           \
+  } while (0)
+
+// Algorithmic bytes: each weight byte once, activation operands (two bf16
+// planes or fp32), outputs (read and written for residual updates).
+double opnd_bytes(const Derived& z) { return z.dt == 1 ? 4.0 : 4.0; }
+double gemm_bytes(const Derived& z, int M, int rows, int K, int n_out, int epi) {
+  const double w = (double)rows * K * z.esz;
+  const double x = (double)M * K * opnd_bytes(z);
+  const double y = (double)M * n_out * (epi == EPI_ADD ? 8.0 : 4.0);
+  return w + x + y;
+}
+double attn_bytes(const Derived& z, int M, const RowVis& v) {
+  const double keys = (double)(v.key_end - v.pre_lo);
+  return keys * z.nkv * z.d * 2.0 * (z.dt == 1 ? 4.0 : 4.0) + 2.0 * M * z.nq * z.d * 4.0;
+}
+
 // ------------------------------------------------------------ passes
 // One decoder layer over M rows with residual stream h. If x_ready, the
 // first norm was already applied and its output sits in xop (EAGLE-3).
@@ -398,20 +459,33 @@ eagle_status layer_forward(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M,
                            RowVis vis) {
   const Derived& z = c->z;
   const int dt = z.dt;
+  const double rowb = (double)M * z.H * 8.0;
   if (!x_ready)
-    HCHK(launch_rmsnorm(dt, h, z.H, w.attn_norm, z.H, c->cfg.rms_eps, M, c->xop, kin, nullptr, 0, c->st));
-  HCHK(launch_gemm(dt, EPI_STORE, w.wqkv, c->xop, M, z.qkv_rows, kin, c->qkv, z.qkv_rows, nullptr,
-                   c->gpart, c->counters, c->st));
-  HCHK(launch_rope_kv(dt, c->qkv, M, z.nq, z.nkv, z.d, pos, slot, c->cos_t, c->sin_t, c->qop, kv, c->st));
-  HCHK(launch_attention(dt, c->qop, kv, vis, M, z.nq, z.d, 1.0f / std::sqrt((float)z.d), c->opart,
-                        c->mlpart, c->aop, c->st));
-  HCHK(launch_gemm(dt, EPI_ADD, w.wo, c->aop, M, z.H, z.nq * z.d, h, z.H, nullptr, c->gpart,
-                   c->counters, c->st));
-  HCHK(launch_rmsnorm(dt, h, z.H, w.ffn_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H, nullptr, 0, c->st));
-  HCHK(launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, M, z.F, z.H, nullptr, 0, c->fop, c->gpart,
-                   c->counters, c->st));
-  HCHK(launch_gemm(dt, EPI_ADD, w.wdown, c->fop, M, z.H, z.F, h, z.H, nullptr, c->gpart,
-                   c->counters, c->st));
+    PROFILED(EAGLE_PROF_ROWS, rowb,
+             launch_rmsnorm(dt, h, z.H, w.attn_norm, z.H, c->cfg.rms_eps, M, c->xop, kin, c->xlo,
+                            nullptr, 0, c->st));
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.qkv_rows, kin, z.qkv_rows, EPI_STORE),
+           launch_gemm(dt, EPI_STORE, w.wqkv, c->xop, c->xlo, M, z.qkv_rows, kin, c->qkv,
+                       z.qkv_rows, nullptr, 0, c->gpart, c->counters, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.qkv_rows * 8.0,
+           launch_rope_kv(dt, c->qkv, M, z.nq, z.nkv, z.d, pos, slot, c->cos_t, c->sin_t, c->qop,
+                          c->qlo, kv, c->st));
+  PROFILED(EAGLE_PROF_ATTN, attn_bytes(z, M, vis),
+           launch_attention(dt, c->qop, c->qlo, kv, vis, M, z.nq, z.d,
+                            1.0f / std::sqrt((float)z.d), c->opart, c->mlpart, c->aop, c->alo,
+                            c->st));
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.nq * z.d, z.H, EPI_ADD),
+           launch_gemm(dt, EPI_ADD, w.wo, c->aop, c->alo, M, z.H, z.nq * z.d, h, z.H, nullptr, 0,
+                       c->gpart, c->counters, c->st));
+  PROFILED(EAGLE_PROF_ROWS, rowb,
+           launch_rmsnorm(dt, h, z.H, w.ffn_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H, c->xlo,
+                          nullptr, 0, c->st));
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, 2 * z.F, z.H, z.F, EPI_SWIGLU),
+           launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, c->xlo, M, z.F, z.H, nullptr, 0, c->fop,
+                       c->flo, c->gpart, c->counters, c->st));
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.F, z.H, EPI_ADD),
+           launch_gemm(dt, EPI_ADD, w.wdown, c->fop, c->flo, M, z.H, z.F, h, z.H, nullptr, 0,
+                       c->gpart, c->counters, c->st));
   return EAGLE_OK;
 }
 
@@ -419,7 +493,8 @@ eagle_status layer_forward(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M,
 eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t* pos,
                          const int32_t* slot, RowVis vis) {
   const Derived& z = c->z;
-  HCHK(launch_embed(z.dt, c->embed, z.H, tok, M, c->h, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 4.0,
+           launch_embed(z.dt, c->embed, z.H, tok, M, c->h, c->st));
   for (int l = 0; l < z.NL; ++l) {
     KVView kv = c->tkv0;
     kv.base = (char*)c->tkv0.base + (int64_t)l * c->t_layer_elems * z.esz;
@@ -427,11 +502,13 @@ eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t*
     if (c->cfg.head == EAGLE_HEAD_E3)
       for (int j = 0; j < 3; ++j)
         if (c->cfg.feat_layers[j] == l)
-          HCHK(launch_store_feat(z.dt, c->h, z.H, M, (char*)c->lmh + (int64_t)j * z.H * z.esz,
-                                 3 * z.H, c->st));
+          PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 8.0,
+                   launch_store_feat(z.dt, c->h, z.H, M, (char*)c->lmh + (int64_t)j * z.H * z.esz,
+                                     3 * z.H, c->lmhlo, c->st));
   }
-  HCHK(launch_rmsnorm(z.dt, c->h, z.H, c->final_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H,
-                      c->tfeat, z.H, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
+           launch_rmsnorm(z.dt, c->h, z.H, c->final_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H,
+                          c->xlo, c->tfeat, z.H, c->st));
   c->last_target_rows = M;
   return EAGLE_OK;
 }
@@ -444,16 +521,20 @@ eagle_status draft_pass(eagle_ctx* c, int M, const int32_t* tok, const float* fe
   const Derived& z = c->z;
   bool x_ready = false;
   if (c->cfg.head == EAGLE_HEAD_E1) {
-    HCHK(launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->st));
-    HCHK(launch_gemm(z.dt, EPI_STORE, c->fc, c->xop, M, z.H, 2 * z.H, hout, z.H, nullptr, c->gpart,
-                     c->counters, c->st));
+    PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
+             launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->xlo, c->st));
+    PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_STORE),
+             launch_gemm(z.dt, EPI_STORE, c->fc, c->xop, c->xlo, M, z.H, 2 * z.H, hout, z.H,
+                         nullptr, 0, c->gpart, c->counters, c->st));
   } else {
-    HCHK(launch_draft_input_e3(z.dt, c->embed, tok, feat, idx, c->dl.attn_norm, c->cfg.rms_eps, M,
-                               z.H, c->xop, hout, c->st));
+    PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 16.0,
+             launch_draft_input_e3(z.dt, c->embed, tok, feat, idx, c->dl.attn_norm,
+                                   c->cfg.rms_eps, M, z.H, c->xop, c->xlo, hout, c->st));
     x_ready = true;
   }
   SCHK(layer_forward(c, c->dl, z.kin_draft, M, hout, x_ready, pos, slot, c->dkv, vis));
-  HCHK(launch_cast(z.dt, hout, z.H, M, c->xop, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 8.0,
+           launch_cast(z.dt, hout, z.H, M, c->xop, c->xlo, c->st));
   return EAGLE_OK;
 }
 
@@ -469,17 +550,21 @@ eagle_status catch_up(eagle_ctx* c, int M, int first, const int32_t* tok, const 
   if (!final) return EAGLE_OK;
   HCHK(hipMemcpyAsync(c->dout, c->hcat + (int64_t)(M - 1) * z.H, sizeof(float) * z.H,
                       hipMemcpyDeviceToDevice, c->st));
-  HCHK(launch_cast(z.dt, c->dout, z.H, 1, c->xop, c->st));
-  HCHK(launch_lmhead_topk(z.dt, c->lm, c->xop, 1, z.V, z.H, z.k_b, c->hpart, c->ids, c->logp, c->st));
-  HCHK(launch_tree_append(c->t, c->tp, c->ids, c->logp, 1, ctx_after, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
+           launch_cast(z.dt, c->dout, z.H, 1, c->xop, c->xlo, c->st));
+  PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)z.H * 4.0,
+           launch_lmhead_topk(z.dt, c->lm, c->xop, c->xlo, 1, z.V, z.H, z.k_b, c->hpart, c->ids,
+                              c->logp, c->st));
+  PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_append(c->t, c->tp, c->ids, c->logp, 1, ctx_after, c->st));
   return EAGLE_OK;
 }
 
 // E3: g = FC([l;m;h]) for M committed rows whose [l;m;h] operands are at src.
-eagle_status fuse_rows(eagle_ctx* c, int M, const void* src) {
+eagle_status fuse_rows(eagle_ctx* c, int M, const void* src, int64_t src_lo) {
   const Derived& z = c->z;
-  HCHK(launch_gemm(z.dt, EPI_STORE, c->fc, src, M, z.H, 3 * z.H, c->gbuf, z.H, nullptr, c->gpart,
-                   c->counters, c->st));
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 3 * z.H, z.H, EPI_STORE),
+           launch_gemm(z.dt, EPI_STORE, c->fc, src, src_lo, M, z.H, 3 * z.H, c->gbuf, z.H, nullptr,
+                       0, c->gpart, c->counters, c->st));
   return EAGLE_OK;
 }
 
@@ -579,7 +664,7 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
   for (int l = 0; l < z.NL; ++l) c->tl.push_back(lw(EAGLE_G_TARGET, l));
   c->dl = lw(EAGLE_G_DRAFT, 0);
   // KV views
-  const int64_t page_elems = 2ll * z.nkv * KV_PAGE * z.d;
+  const int64_t page_elems = (int64_t)kv_planes(z.dt) * z.nkv * KV_PAGE * z.d;
   c->t_layer_elems = (int64_t)z.t_pages * page_elems;
   plan_scratch(z, c);
   c->tkv0 = KVView{c->KV, c->tpt, page_elems, KV_PAGE, z.nkv, z.d};
@@ -659,13 +744,14 @@ eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32
     SCHK(target_pass(c, M, c->seq + c0, c->rpos, c->rslot, vis));
     if (last) {
       const void* xl = (const char*)c->xop + (int64_t)(M - 1) * z.H * z.esz;
-      HCHK(launch_lmhead_argmax(z.dt, c->lm, xl, 1, z.V, z.H, c->hpart, c->g, c->margin, nullptr, c->st));
+      HCHK(launch_lmhead_argmax(z.dt, c->lm, xl, c->xlo, 1, z.V, z.H, c->hpart, c->g, c->margin,
+                                nullptr, c->st));
       HCHK(hipMemcpyAsync(c->seq + n, c->g, 4, hipMemcpyDeviceToDevice, c->st));
     }
     if (plain_mode(c)) continue;
     const float* feat = c->tfeat;
     if (c->cfg.head == EAGLE_HEAD_E3) {
-      SCHK(fuse_rows(c, M, c->lmh));
+      SCHK(fuse_rows(c, M, c->lmh, c->lmhlo));
       feat = c->gbuf;
     }
     SCHK(catch_up(c, M, c0 + 1, c->seq + c0 + 1, feat, c->iota, last, n));
@@ -726,11 +812,13 @@ eagle_status eagle_draft_tree(eagle_ctx* c, eagle_tree* out) {
       RowVis vis{c->t.row_prehi, c->t.row_mask, 1, ctx + 1, t0 + M, ctx + 1 + t0 + M};
       SCHK(draft_pass(c, M, c->t.row_tok, c->dout, c->t.row_src, c->t.row_pos, c->t.row_slot, vis,
                       c->dout + (int64_t)(1 + t0) * z.H));
-      HCHK(launch_lmhead_topk(z.dt, c->lm, c->xop, M, z.V, z.H, z.k_b, c->hpart, c->ids, c->logp, c->st));
-      HCHK(launch_tree_append(c->t, c->tp, c->ids, c->logp, pass, ctx, c->st));
+      PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)M * z.H * 4.0,
+               launch_lmhead_topk(z.dt, c->lm, c->xop, c->xlo, M, z.V, z.H, z.k_b, c->hpart,
+                                  c->ids, c->logp, c->st));
+      PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_append(c->t, c->tp, c->ids, c->logp, pass, ctx, c->st));
       t0 += M;
     }
-    HCHK(launch_tree_finalize(c->t, c->tp, ctx, c->seq + ctx, c->st));
+    PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_finalize(c->t, c->tp, ctx, c->seq + ctx, c->st));
   }
   c->state = ST_DRAFTED;
   if (out) SCHK(copy_tree_out(c, out));
@@ -775,11 +863,13 @@ eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_
   }
   RowVis vis{c->t.v_prehi, c->t.v_mask, 0, ctx, Mv, ctx + Mv};
   SCHK(target_pass(c, Mv, c->t.v_tok, c->t.v_pos, c->t.v_slot, vis));
-  HCHK(launch_lmhead_argmax(z.dt, c->lm, c->xop, Mv, z.V, z.H, c->hpart, c->g, c->margin,
-                            c->debug ? c->logits : nullptr, c->st));
+  PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)Mv * z.H * 4.0,
+           launch_lmhead_argmax(z.dt, c->lm, c->xop, c->xlo, Mv, z.V, z.H, c->hpart, c->g,
+                                c->margin, c->debug ? c->logits : nullptr, c->st));
   c->last_verify_rows = Mv;
-  HCHK(launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->st));
-  HCHK(launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, c->acc, c->acc + 2, ctx, c->st));
+  PROFILED(EAGLE_PROF_TREE, 0.0, launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->st));
+  PROFILED(EAGLE_PROF_KV, 0.0,
+           launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, c->acc, c->acc + 2, ctx, c->st));
   int32_t acc[2 + EAGLE_MAX_DEPTH + 2];
   int32_t nt[EAGLE_MAX_DEPTH + 2];
   HCHK(hipMemcpyAsync(acc, c->acc, sizeof(acc), hipMemcpyDeviceToHost, c->st));
@@ -793,8 +883,9 @@ eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_
     const float* feat = c->tfeat;
     const int32_t* idx = c->cu_src;
     if (c->cfg.head == EAGLE_HEAD_E3) {
-      HCHK(launch_gather_t(z.dt, c->lmh, 3 * z.H, c->cu_src, L + 1, 3 * z.H, c->lmh2, c->st));
-      SCHK(fuse_rows(c, L + 1, c->lmh2));
+      HCHK(launch_gather_t(z.dt, c->lmh, 3 * z.H, c->lmhlo, c->cu_src, L + 1, 3 * z.H, c->lmh2,
+                           c->lmh2lo, c->st));
+      SCHK(fuse_rows(c, L + 1, c->lmh2, c->lmh2lo));
       feat = c->gbuf;
       idx = c->iota;
     }
@@ -879,7 +970,33 @@ eagle_status eagle_debug_read(eagle_ctx* c, int32_t what, void* host_dst, uint64
   return EAGLE_OK;
 }
 
-void eagle_free(eagle_ctx* c) { delete c; }
+eagle_status eagle_profile_enable(eagle_ctx* c, int32_t on) {
+  if (!c) return EAGLE_E_INVALID;
+  c->prof = on != 0;
+  c->recs.clear();
+  c->pool_used = 0;
+  return EAGLE_OK;
+}
+
+eagle_status eagle_profile_read(eagle_ctx* c, eagle_profile* out) {
+  if (!c || !out) return EAGLE_E_INVALID;
+  std::memset(out, 0, sizeof(*out));
+  HCHK(hipStreamSynchronize(c->st));
+  for (const eagle_ctx::ProfRec& r : c->recs) {
+    float ms = 0.f;
+    HCHK(hipEventElapsedTime(&ms, r.a, r.b));
+    out->launches[r.cls]++;
+    out->ms[r.cls] += ms;
+    out->bytes[r.cls] += r.bytes;
+  }
+  return EAGLE_OK;
+}
+
+void eagle_free(eagle_ctx* c) {
+  if (!c) return;
+  for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
+  delete c;
+}
 
 const char* eagle_last_error(const eagle_ctx* c) { return c ? c->err.c_str() : "null context"; }
 

@@ -21,11 +21,11 @@ constexpr int PREF = 8;   // W steps issued before consuming them
 
 struct GemmArgs {
   const void* W; int64_t ldw;
-  const void* X; int64_t ldx;
+  const void* X; int64_t ldx; int64_t xlo;
   int M, N, K;          // N = output columns (SwiGLU: F)
   int n_tiles, splits, steps_per_split;
   float* Y; int64_t ldy;
-  void* Yt;
+  void* Yt; int64_t ytlo;
   float* part; int* counters;
 };
 
@@ -43,8 +43,8 @@ __device__ __forceinline__ int block_row(int tile, int b, int N) {
 template <typename T, int MT, int NB>
 __device__ __forceinline__ void tile_compute(const T* __restrict__ W, int64_t ldw,
                                              const int (&wrow)[NB], const T* __restrict__ X,
-                                             int64_t ldx, int M, int m0, int s_lo, int s_hi,
-                                             float* red, float* tile_out) {
+                                             int64_t ldx, int64_t xlo, int M, int m0, int s_lo,
+                                             int s_hi, float* red, float* tile_out) {
   using MM = Mma<T>;
   constexpr int EPL = MM::EPL, KS = MM::KSTEP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -83,13 +83,19 @@ __device__ __forceinline__ void tile_compute(const T* __restrict__ W, int64_t ld
 #pragma unroll
     for (int u = 0; u < PREF; ++u)
       if (u < cnt) {
-        uint4 xf[MT];
+        uint4 xf[MT], xl[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) xf[t] = ld16(xp[t] + (int64_t)(s + u) * KS);
+        for (int t = 0; t < MT; ++t) {
+          xf[t] = ld16(xp[t] + (int64_t)(s + u) * KS);
+          if (Opnd<T>::SPLIT) xl[t] = ld16(xp[t] + xlo + (int64_t)(s + u) * KS);
+        }
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
-          for (int t = 0; t < MT; ++t) MM::mma(wf[u][b], xf[t], acc[b][t]);
+          for (int t = 0; t < MT; ++t) {
+            MM::mma(wf[u][b], xf[t], acc[b][t]);
+            if (Opnd<T>::SPLIT) MM::mma(wf[u][b], xl[t], acc[b][t]);
+          }
       }
   }
 
@@ -159,8 +165,8 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs a) {
   const int total = a.K / Mma<T>::KSTEP;
   const int s_lo = split * a.steps_per_split;
   const int s_hi = min(total, s_lo + a.steps_per_split);
-  tile_compute<T, MT, NB>((const T*)a.W, a.ldw, wrow_l, (const T*)a.X, a.ldx, a.M, m0, s_lo,
-                          s_hi, red, tile_out);
+  tile_compute<T, MT, NB>((const T*)a.W, a.ldw, wrow_l, (const T*)a.X, a.ldx, a.xlo, a.M, m0,
+                          s_lo, s_hi, red, tile_out);
 
   const int mrows = min(C, a.M - m0);
   if (a.splits > 1) {
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs a) {
       const float g = tile_out[nl * C + ml];
       const float u = tile_out[(nl + HALF) * C + ml];
       const float v = g / (1.0f + expf(-g)) * u;
-      ((T*)a.Yt)[(int64_t)(m0 + ml) * a.N + col] = Elem<T>::from_f(v);
+      Opnd<T>::store((T*)a.Yt, a.ytlo, (int64_t)(m0 + ml) * a.N + col, v);
     }
   } else {
     for (int e = threadIdx.x; e < R * C; e += NTHREADS) {
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------- LM head
 struct HeadArgs {
-  const void* W; const void* X;
+  const void* W; const void* X; int64_t xlo;
   int M, V, H, k;
   float* part;      // per workgroup and row: argmax {max1, id1, max2} or topk {max, sum, k vals, k ids}
   float* logits;    // optional [M, V]
@@ -240,8 +246,8 @@ __global__ __launch_bounds__(NTHREADS) void lmhead_kernel(HeadArgs a) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) wrow[b] = min(tile * R + 16 * b + lr, a.V - 1) - lr;
   const int total = a.H / Mma<T>::KSTEP;
-  tile_compute<T, MT, NB>((const T*)a.W, a.H, wrow, (const T*)a.X, a.H, a.M, 0, 0, total, red,
-                          tile_out);
+  tile_compute<T, MT, NB>((const T*)a.W, a.H, wrow, (const T*)a.X, a.H, a.xlo, a.M, 0, 0, total,
+                          red, tile_out);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nvalid = min(R, a.V - tile * R);
   if (a.logits) {
@@ -443,18 +449,18 @@ uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M) {
   return p.splits > 1 ? (uint64_t)p.splits * M * N_rows : 0;
 }
 
-hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int M, int N, int K,
-                       float* Y, int64_t ldy, void* Yt, float* part, int* counters,
-                       hipStream_t stream) {
+hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
+                       int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, float* part,
+                       int* counters, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int rows = (epi == EPI_SWIGLU) ? 2 * N : N;
   GemmPlan p = gemm_plan(M, rows, K, dtype, epi);
   GemmArgs a;
-  a.W = W; a.ldw = K; a.X = x; a.ldx = K; a.M = M; a.N = N; a.K = K;
+  a.W = W; a.ldw = K; a.X = x; a.ldx = K; a.xlo = xlo; a.M = M; a.N = N; a.K = K;
   a.n_tiles = p.n_tiles; a.splits = p.splits;
   const int steps = K / (dtype == 1 ? 32 : 16);
   a.steps_per_split = (steps + p.splits - 1) / p.splits;
-  a.Y = Y; a.ldy = ldy; a.Yt = Yt; a.part = part; a.counters = counters;
+  a.Y = Y; a.ldy = ldy; a.Yt = Yt; a.ytlo = ytlo; a.part = part; a.counters = counters;
   if (dtype == 1) {
     switch (epi) {
       case EPI_STORE: return gemm_dispatch<bf16_t, EPI_STORE>(p, a, stream);
@@ -475,22 +481,22 @@ uint64_t lmhead_part_floats(int M, int V, int k) {
   return (uint64_t)n_tiles * M * (k > 0 ? (2 + 2 * k) : 3);
 }
 
-hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int M, int V, int H,
-                                float* part, int32_t* g, float* margin, float* logits,
+hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int64_t xlo, int M, int V,
+                                int H, float* part, int32_t* g, float* margin, float* logits,
                                 hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   if (M > 80) {  // rows in passes of 64 (the weight is re-read per pass)
     const int esz = dtype == 1 ? 2 : 4;
     for (int m0 = 0; m0 < M; m0 += 64) {
       const int mc = M - m0 < 64 ? M - m0 : 64;
-      hipError_t e = launch_lmhead_argmax(dtype, W, (const char*)x + (int64_t)m0 * H * esz, mc, V, H,
-                                          part, g + m0, margin + m0,
+      hipError_t e = launch_lmhead_argmax(dtype, W, (const char*)x + (int64_t)m0 * H * esz, xlo, mc, V,
+                                          H, part, g + m0, margin + m0,
                                           logits ? logits + (int64_t)m0 * V : nullptr, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }
-  HeadArgs a{W, x, M, V, H, 0, part, logits};
+  HeadArgs a{W, x, xlo, M, V, H, 0, part, logits};
   const int n_tiles = (V + 31) / 32;
   const int mt = (M + 15) / 16;
   hipError_t e = dtype == 1 ? head_dispatch<bf16_t, false>(mt, n_tiles, a, stream)
@@ -500,21 +506,23 @@ hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int M, 
   return hipGetLastError();
 }
 
-hipError_t launch_lmhead_topk(int dtype, const void* W, const void* x, int M, int V, int H,
-                              int k, float* part, int32_t* ids, float* logp, hipStream_t stream) {
+hipError_t launch_lmhead_topk(int dtype, const void* W, const void* x, int64_t xlo, int M, int V,
+                              int H, int k, float* part, int32_t* ids, float* logp,
+                              hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   if (k < 1 || k > 16) return hipErrorInvalidValue;
   if (M > 80) {
     const int esz = dtype == 1 ? 2 : 4;
     for (int m0 = 0; m0 < M; m0 += 64) {
       const int mc = M - m0 < 64 ? M - m0 : 64;
-      hipError_t e = launch_lmhead_topk(dtype, W, (const char*)x + (int64_t)m0 * H * esz, mc, V, H,
-                                        k, part, ids + (int64_t)m0 * k, logp + (int64_t)m0 * k, stream);
+      hipError_t e = launch_lmhead_topk(dtype, W, (const char*)x + (int64_t)m0 * H * esz, xlo, mc, V,
+                                        H, k, part, ids + (int64_t)m0 * k, logp + (int64_t)m0 * k,
+                                        stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
   }
-  HeadArgs a{W, x, M, V, H, k, part, nullptr};
+  HeadArgs a{W, x, xlo, M, V, H, k, part, nullptr};
   const int n_tiles = (V + 31) / 32;
   const int mt = (M + 15) / 16;
   hipError_t e = dtype == 1 ? head_dispatch<bf16_t, true>(mt, n_tiles, a, stream)

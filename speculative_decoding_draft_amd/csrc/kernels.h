@@ -10,39 +10,45 @@ enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
 //   EPI_STORE : Y[m, n]  = acc            (fp32, row stride ldy)
 //   EPI_ADD   : Y[m, n] += acc            (fp32 residual update)
 //   EPI_SWIGLU: W = [gate (N rows); up (N rows)], Yt[m, n] = T(silu(g) * u)
-// dtype 0 = fp32, 1 = bf16 for W, x and Yt. `part`/`counters` is the split-K
+// dtype 0 = fp32, 1 = bf16 for W. Activations x and Yt are operands (see
+// Opnd in common.h): for bf16 two planes, the lo plane xlo / ytlo elements
+// after the hi plane. `part`/`counters` is the split-K
 // workspace (gemm_workspace_bytes); counters must start at zero and are left
 // at zero.
 struct GemmPlan { int mt, nb, splits, m_chunks, n_tiles; };
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi);
 uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M);
-hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int M, int N, int K,
-                       float* Y, int64_t ldy, void* Yt, float* part, int* counters,
-                       hipStream_t stream);
+hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
+                       int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, float* part,
+                       int* counters, hipStream_t stream);
 
 // ---------------------------------------------------------------- LM head
 // Verify: g[m] = argmax_v (x W^T)[m, v] (lowest id on ties), margin[m] =
 // top-1 minus top-2; logits stored to `logits` [M, V] when not null.
-hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int M, int V, int H,
-                                float* part, int32_t* g, float* margin, float* logits,
+hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int64_t xlo, int M, int V,
+                                int H, float* part, int32_t* g, float* margin, float* logits,
                                 hipStream_t stream);
 // Draft: per row the k best ids by (logit desc, id asc) and their
 // log-probabilities l - max - log(sum exp(l - max)) over the full vocabulary.
-hipError_t launch_lmhead_topk(int dtype, const void* W, const void* x, int M, int V, int H,
-                              int k, float* part, int32_t* ids, float* logp, hipStream_t stream);
+hipError_t launch_lmhead_topk(int dtype, const void* W, const void* x, int64_t xlo, int M, int V,
+                              int H, int k, float* part, int32_t* ids, float* logp,
+                              hipStream_t stream);
 uint64_t lmhead_part_floats(int M, int V, int k);
 
 // ---------------------------------------------------------------- paged KV
-// One layer of a paged KV cache. Element (slot, K|V, kv head h, i) lives at
+// One layer of a paged KV cache. Element (slot, plane, kv head h, i) lives at
 //   base + page_table[slot / page] * page_elems
-//        + ((kv * n_kv + h) * page + slot % page) * d + i
-// so each (page, K|V, head) is a contiguous [page, d] tile.
+//        + ((plane * n_kv + h) * page + slot % page) * d + i
+// so each (page, plane, head) is a contiguous [page, d] tile. fp32 caches
+// have planes K, V; bf16 caches keep each fp32 value as a hi + lo pair with
+// planes K_hi, K_lo, V_hi, V_lo (16 significant bits).
 struct KVView {
   void* base;
   const int32_t* page_table;
-  int64_t page_elems;   // 2 * n_kv * page * d
+  int64_t page_elems;   // planes * n_kv * page * d
   int page, n_kv, d;
 };
+inline int kv_planes(int dtype) { return dtype == 1 ? 4 : 2; }
 
 // ---------------------------------------------------------------- rows
 // Attention visibility of row r: key slots [pre_lo, prehi[r]) plus the
@@ -55,29 +61,33 @@ struct RowVis {
 
 hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int M, float* h,
                         hipStream_t st);
+// Operand outputs (out_t, q_out, x, dst of store_feat / gather_t) take
+// their lo-plane offset `lo` in elements (ignored for fp32).
 hipError_t launch_rmsnorm(int dtype, const float* h, int64_t ldh, const float* gain, int K, float eps,
-                          int M, void* out_t, int64_t ldo, float* out_f, int64_t ldf,
+                          int M, void* out_t, int64_t ldo, int64_t lo, float* out_f, int64_t ldf,
                           hipStream_t st);
-hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, hipStream_t st);
+hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, int64_t lo,
+                       hipStream_t st);
 hipError_t launch_rope_kv(int dtype, const float* qkv, int M, int nq, int nkv, int d,
                           const int32_t* pos, const int32_t* slot, const float* cos_t,
-                          const float* sin_t, void* q_out, KVView kv, hipStream_t st);
+                          const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st);
 uint64_t attn_part_floats(int max_chunks, int M, int nq, int d);
 int attn_chunk_keys();
-hipError_t launch_attention(int dtype, const void* q, KVView kv, RowVis vis, int M, int nq, int d,
-                            float scale, float* opart, float* mlpart, void* out_t,
-                            hipStream_t st);
+hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, RowVis vis, int M,
+                            int nq, int d, float scale, float* opart, float* mlpart, void* out_t,
+                            int64_t olo, hipStream_t st);
 hipError_t launch_draft_input_e1(int dtype, const void* E, const int32_t* tok, const float* feat,
-                                 const int32_t* idx, int M, int H, void* x, hipStream_t st);
+                                 const int32_t* idx, int M, int H, void* x, int64_t lo,
+                                 hipStream_t st);
 hipError_t launch_draft_input_e3(int dtype, const void* E, const int32_t* tok, const float* feat,
                                  const int32_t* idx, const float* gain, float eps, int M, int H,
-                                 void* x, float* h, hipStream_t st);
+                                 void* x, int64_t lo, float* h, hipStream_t st);
 hipError_t launch_gather_f32(const float* src, int64_t ld, const int32_t* idx, int M, int W,
                              float* dst, hipStream_t st);
-hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, const int32_t* idx, int M, int W,
-                           void* dst, hipStream_t st);
+hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, int64_t src_lo, const int32_t* idx,
+                           int M, int W, void* dst, int64_t dst_lo, hipStream_t st);
 hipError_t launch_store_feat(int dtype, const float* h, int H, int M, void* dst, int64_t ldd,
-                             hipStream_t st);
+                             int64_t lo, hipStream_t st);
 hipError_t launch_rows_causal(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
                               uint64_t* mask, hipStream_t st);
 hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int n_layers,

@@ -39,11 +39,13 @@ eagle_status eagle_op_linear(int32_t dtype, int32_t epi, const void* x, const vo
   int* counters = need ? (int*)workspace : nullptr;
   float* part = need ? (float*)((char*)workspace + kCounterBytes) : nullptr;
   hipError_t e;
+  const int64_t xlo = (int64_t)M * K;   // bf16: lo plane follows the hi plane
   if (epi == EAGLE_EPI_SWIGLU)
-    e = launch_gemm(dtype, EPI_SWIGLU, w, x, M, N, K, nullptr, 0, y, part, counters, (hipStream_t)stream);
+    e = launch_gemm(dtype, EPI_SWIGLU, w, x, xlo, M, N, K, nullptr, 0, y, (int64_t)M * N, part,
+                    counters, (hipStream_t)stream);
   else
-    e = launch_gemm(dtype, epi == EAGLE_EPI_ADD ? EPI_ADD : EPI_STORE, w, x, M, N, K, (float*)y, N,
-                    nullptr, part, counters, (hipStream_t)stream);
+    e = launch_gemm(dtype, epi == EAGLE_EPI_ADD ? EPI_ADD : EPI_STORE, w, x, xlo, M, N, K, (float*)y,
+                    N, nullptr, 0, part, counters, (hipStream_t)stream);
   return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
 }
 
@@ -63,11 +65,11 @@ eagle_status eagle_op_lmhead(int32_t dtype, int32_t k, const void* x, const void
   if (!workspace || ws_bytes < eagle_op_lmhead_workspace(M, V, k)) return EAGLE_E_BUFFER;
   hipError_t e;
   if (k == 0)
-    e = launch_lmhead_argmax(dtype, w_lm, x, M, V, H, (float*)workspace, out_ids, out_vals, logits,
-                             (hipStream_t)stream);
+    e = launch_lmhead_argmax(dtype, w_lm, x, (int64_t)M * H, M, V, H, (float*)workspace, out_ids,
+                             out_vals, logits, (hipStream_t)stream);
   else
-    e = launch_lmhead_topk(dtype, w_lm, x, M, V, H, k, (float*)workspace, out_ids, out_vals,
-                           (hipStream_t)stream);
+    e = launch_lmhead_topk(dtype, w_lm, x, (int64_t)M * H, M, V, H, k, (float*)workspace, out_ids,
+                           out_vals, (hipStream_t)stream);
   return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
 }
 

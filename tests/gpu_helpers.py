@@ -32,18 +32,45 @@ def gpu_tree_check(tree: dict, k: int, depth: int, budget: int, static=None):
             ids.append([nt[c] for c in ch])
             lps.append([lp[c] for c in ch])
         return ids, lps
-    root = kids[-1]
     if static is not None:
-        ids0 = {}
-        # static: children are listed by rank; rebuild rank-indexed lists
-        raise NotImplementedError
-    T.grow_dynamic([nt[c] for c in root], [lp[c] for c in root], expand, k, k, depth, t)
+        # static tree: GPU nodes follow the list; give each parent a rank-indexed list
+        rank = [p[-1] for p in static]
+
+        def rank_list(children):
+            ids, lps = [0] * k, [np.float32(-np.inf)] * k
+            for c in children:
+                ids[rank[c]], lps[rank[c]] = nt[c], lp[c]
+            return ids, lps
+
+        def expand_static(chosen):
+            out = [rank_list(kids.get(e, [])) for e in chosen]
+            return [o[0] for o in out], [o[1] for o in out]
+        r_ids, r_lps = rank_list(kids[-1])
+        T.grow_static(r_ids, r_lps, expand_static, [tuple(p) for p in static], t)
+        kept = list(range(len(t.nodes)))
+    else:
+        root = kids[-1]
+        T.grow_dynamic([nt[c] for c in root], [lp[c] for c in root], expand, k, k, depth, t)
+        kept = T.rerank(t.nodes, budget)
     assert [n.token for n in t.nodes] == list(nt)
     assert [n.parent for n in t.nodes] == list(npar)
     assert np.array_equal(np.array([n.logv for n in t.nodes], dtype=np.float32), tree["node_logv"])
-    kept = T.rerank(t.nodes, budget)
     rows = T.flatten(t.nodes, kept, tree["token"][0])
     assert rows["token"] == tree["token"]
     assert rows["parent"] == tree["parent"]
     assert rows["node"] == tree["node"]
     return rows
+
+
+def stream_check(w, prompt, stream, weights=None, tol=1e-3):
+    """Teacher-forced check: every token is the oracle's greedy choice on the
+    GPU's own prefix, or sits where the oracle's top-1/top-2 margin < tol.
+    Returns the number of such near-tie positions (a mismatch elsewhere fails)."""
+    from oracle.loop import teacher_forced
+    g, margin = teacher_forced(w, prompt, stream, weights)
+    near = 0
+    for i, tok in enumerate(stream):
+        if tok != int(g[i]):
+            assert margin[i] < tol, f"token {i}: gpu {tok} oracle {int(g[i])} margin {margin[i]}"
+            near += 1
+    return near

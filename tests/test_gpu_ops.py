@@ -16,6 +16,24 @@ def _rand(shape, gen, scale, dtype):
     return t.to(torch.bfloat16) if dtype == BF16 else t
 
 
+def _act(shape, gen, dtype):
+    """fp32 activations and their device operand (bf16: hi plane then lo plane)."""
+    x = torch.randn(shape, generator=gen, dtype=torch.float32)
+    if dtype != BF16:
+        return x, x.cuda()
+    hi = x.to(torch.bfloat16)
+    lo = (x - hi.float()).to(torch.bfloat16)
+    return x, torch.cat([hi.reshape(-1), lo.reshape(-1)]).cuda()
+
+
+def _from_planes(t, shape, dtype):
+    t = t.cpu()
+    if dtype != BF16:
+        return t.double().numpy().reshape(shape)
+    n = int(np.prod(shape))
+    return (t[:n].double() + t[n:].double()).numpy().reshape(shape)
+
+
 def _ws(nbytes):
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
 
@@ -39,13 +57,13 @@ LINEAR = [  # (dtype, M, N, K): split-K, tails, several M tiles, prefill-sized M
 def test_linear(dtype, M, N, K, epi):
     print(f"linear dtype={dtype} M={M} N={N} K={K} epi={epi}", flush=True)
     gen = torch.Generator().manual_seed(M * 131 + N * 7 + K + epi)
-    x = _rand((M, K), gen, 1.0, dtype)
+    x, xd = _act((M, K), gen, dtype)
     w = _rand((N, K), gen, 0.02, dtype)
     y0 = torch.randn((M, N), generator=gen)
     ref = x.double().numpy() @ w.double().numpy().T
     y = (y0.clone() if epi == 1 else torch.zeros(M, N)).cuda()
     ws = _ws(E.op_linear_workspace(dtype, epi, M, N, K))
-    E.op_linear(dtype, epi, x.cuda(), w.cuda(), y, M, N, K, ws)
+    E.op_linear(dtype, epi, xd, w.cuda(), y, M, N, K, ws)
     torch.cuda.synchronize()
     got = y.cpu().double().numpy()
     if epi == 1:
@@ -53,7 +71,7 @@ def test_linear(dtype, M, N, K, epi):
     assert _rel(got, ref) < 1e-4
     if epi == 0:   # same bits on a second run
         y2 = torch.zeros(M, N, device="cuda")
-        E.op_linear(dtype, epi, x.cuda(), w.cuda(), y2, M, N, K, ws)
+        E.op_linear(dtype, epi, xd, w.cuda(), y2, M, N, K, ws)
         torch.cuda.synchronize()
         assert torch.equal(y2.cpu(), y.cpu())
 
@@ -63,17 +81,19 @@ def test_linear(dtype, M, N, K, epi):
 def test_swiglu(dtype, M, N, K):
     print(f"swiglu dtype={dtype} M={M} N={N} K={K}", flush=True)
     gen = torch.Generator().manual_seed(M + N + K)
-    x = _rand((M, K), gen, 1.0, dtype)
+    x, xd = _act((M, K), gen, dtype)
     w = _rand((2 * N, K), gen, 0.02, dtype)
     g = x.double().numpy() @ w[:N].double().numpy().T
     u = x.double().numpy() @ w[N:].double().numpy().T
     ref = g / (1 + np.exp(-g)) * u
-    out = torch.zeros((M, N), dtype=torch.bfloat16 if dtype == BF16 else torch.float32, device="cuda")
+    planes = 2 if dtype == BF16 else 1
+    out = torch.zeros(planes * M * N, dtype=torch.bfloat16 if dtype == BF16 else torch.float32,
+                      device="cuda")
     ws = _ws(E.op_linear_workspace(dtype, 2, M, N, K))
-    E.op_linear(dtype, 2, x.cuda(), w.cuda(), out, M, N, K, ws)
+    E.op_linear(dtype, 2, xd, w.cuda(), out, M, N, K, ws)
     torch.cuda.synchronize()
-    got = out.cpu().double().numpy()
-    tol = (2.0 ** -8 if dtype == BF16 else 1e-5) * np.abs(ref) + 1e-4 * np.abs(ref).max()
+    got = _from_planes(out, (M, N), dtype)
+    tol = 1e-5 * np.abs(ref) + 1e-4 * np.abs(ref).max()
     assert np.all(np.abs(got - ref) <= tol)
 
 
@@ -83,13 +103,13 @@ def test_swiglu(dtype, M, N, K):
 def test_lmhead_topk(dtype, M, V, H, k):
     print(f"topk dtype={dtype} M={M} V={V} H={H} k={k}", flush=True)
     gen = torch.Generator().manual_seed(M + V + H + k)
-    x = _rand((M, H), gen, 1.0, dtype)
+    x, xd = _act((M, H), gen, dtype)
     w = _rand((V, H), gen, 0.02, dtype)
     lg = x.double().numpy() @ w.double().numpy().T
     ids = torch.zeros((M, k), dtype=torch.int32, device="cuda")
     lp = torch.zeros((M, k), dtype=torch.float32, device="cuda")
     ws = _ws(E.op_lmhead_workspace(M, V, k))
-    E.op_lmhead(dtype, k, x.cuda(), w.cuda(), M, V, H, ids, lp, None, ws)
+    E.op_lmhead(dtype, k, xd, w.cuda(), M, V, H, ids, lp, None, ws)
     torch.cuda.synchronize()
     ids, lp = ids.cpu().numpy(), lp.cpu().numpy()
     for r in range(M):
@@ -107,14 +127,14 @@ def test_lmhead_topk(dtype, M, V, H, k):
 def test_lmhead_argmax(dtype, M, V, H):
     print(f"argmax dtype={dtype} M={M} V={V} H={H}", flush=True)
     gen = torch.Generator().manual_seed(M * V + H)
-    x = _rand((M, H), gen, 1.0, dtype)
+    x, xd = _act((M, H), gen, dtype)
     w = _rand((V, H), gen, 0.02, dtype)
     lg = x.double().numpy() @ w.double().numpy().T
     g = torch.zeros(M, dtype=torch.int32, device="cuda")
     mg = torch.zeros(M, dtype=torch.float32, device="cuda")
     logits = torch.zeros((M, V), dtype=torch.float32, device="cuda")
     ws = _ws(E.op_lmhead_workspace(M, V, 0))
-    E.op_lmhead(dtype, 0, x.cuda(), w.cuda(), M, V, H, g, mg, logits, ws)
+    E.op_lmhead(dtype, 0, xd, w.cuda(), M, V, H, g, mg, logits, ws)
     torch.cuda.synchronize()
     g, mg, logits = g.cpu().numpy(), mg.cpu().numpy(), logits.cpu().double().numpy()
     assert _rel(logits, lg) < 1e-4
