@@ -256,39 +256,66 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, int64_t ldh, const float* gain,
-                                                      int K, float eps, T* out_t, int64_t ldo,
-                                                      int64_t lo, float* out_f, int64_t ldf) {
+__global__ __launch_bounds__(256) void resnorm_kernel(float* h, int H, const float* part, int S,
+                                                      int64_t plane, int set, const float* gain,
+                                                      float eps, T* out_t, int64_t lo, float* out_f) {
   __shared__ float sh[256];
   const int r = blockIdx.x;
-  const float* x = h + (int64_t)r * ldh;
+  float* x = h + (int64_t)r * H;
+  const float* pr = part + (int64_t)r * H;
   float ss = 0.f;
-  for (int i = threadIdx.x; i < K; i += 256) ss += x[i] * x[i];
-  ss = block_sum_256(ss, sh);
-  const float inv = 1.0f / sqrtf(ss / (float)K + eps);
-  for (int i = threadIdx.x; i < K; i += 256) {
-    const float v = x[i] * inv * gain[i];
-    if (out_f) out_f[(int64_t)r * ldf + i] = v;
-    Opnd<T>::store(out_t, lo, (int64_t)r * ldo + i, v);
+  for (int i = threadIdx.x; i < H; i += 256) {
+    float v = set ? 0.f : x[i];
+    if (S > 0) {
+      float acc = pr[i];
+      for (int s = 1; s < S; ++s) acc += pr[(int64_t)s * plane + i];
+      v += acc;
+    }
+    if (S > 0 || set) x[i] = v;
+    ss += v * v;
+  }
+  if (gain) {
+    ss = block_sum_256(ss, sh);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    for (int i = threadIdx.x; i < H; i += 256) {
+      const float v = x[i] * inv * gain[i];
+      if (out_f) out_f[(int64_t)r * H + i] = v;
+      Opnd<T>::store(out_t, lo, (int64_t)r * H + i, v);
+    }
+  } else {
+    __syncthreads();
+    for (int i = threadIdx.x; i < H; i += 256) Opnd<T>::store(out_t, lo, (int64_t)r * H + i, x[i]);
+  }
+}
+
+__global__ void sum_planes_kernel(const float* part, int S, int64_t plane, int W, float* dst, int add) {
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < W; i += blockDim.x) {
+    float acc = part[(int64_t)r * W + i];
+    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * plane + (int64_t)r * W + i];
+    dst[(int64_t)r * W + i] = add ? dst[(int64_t)r * W + i] + acc : acc;
   }
 }
 
 template <typename T>
-__global__ void cast_kernel(const float* h, int H, T* out, int64_t lo) {
-  const int r = blockIdx.x;
-  for (int i = threadIdx.x; i < H; i += blockDim.x)
-    Opnd<T>::store(out, lo, (int64_t)r * H + i, h[(int64_t)r * H + i]);
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int nq, int nkv, int d,
-                                                      const int32_t* pos, const int32_t* slot,
+__global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, int64_t plane, int nq,
+                                                      int nkv, int d, const int32_t* pos,
+                                                      const int32_t* slot,
                                                       const float* cos_t, const float* sin_t,
                                                       T* q_out, int64_t qlo, KVView kv) {
   const int r = blockIdx.x;
   const int half = d / 2;
   const int width = (nq + 2 * nkv) * d;
-  const float* x = qkv + (int64_t)r * width;
+  // sum the split-K partial planes of this row into LDS first
+  __shared__ float xsum[EAGLE_QKV_MAX];
+  for (int i = threadIdx.x; i < width; i += blockDim.x) {
+    const float* p = qkv + (int64_t)r * width + i;
+    float acc = p[0];
+    for (int s = 1; s < S; ++s) acc += p[(int64_t)s * plane];
+    xsum[i] = acc;
+  }
+  __syncthreads();
+  const float* x = xsum;
   const float* c = cos_t + (int64_t)pos[r] * half;
   const float* s = sin_t + (int64_t)pos[r] * half;
   const int sl = slot[r];
@@ -429,32 +456,31 @@ hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(int dtype, const float* h, int64_t ldh, const float* gain, int K, float eps,
-                          int M, void* out_t, int64_t ldo, int64_t lo, float* out_f, int64_t ldf,
-                          hipStream_t st) {
+hipError_t launch_resnorm(int dtype, float* h, int H, int M, const float* part, int S,
+                          int64_t plane, int set, const float* gain, float eps, void* out_t,
+                          int64_t lo, float* out_f, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(rmsnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (bf16_t*)out_t, ldo, lo, out_f, ldf),
-              hipLaunchKernelGGL(rmsnorm_kernel<float>, dim3(M), dim3(256), 0, st, h, ldh, gain, K, eps, (float*)out_t, ldo, lo, out_f, ldf));
+              hipLaunchKernelGGL(resnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, part, S, plane, set, gain, eps, (bf16_t*)out_t, lo, out_f),
+              hipLaunchKernelGGL(resnorm_kernel<float>, dim3(M), dim3(256), 0, st, h, H, part, S, plane, set, gain, eps, (float*)out_t, lo, out_f));
   return hipGetLastError();
 }
 
-hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, int64_t lo,
-                       hipStream_t st) {
+hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int W, float* dst,
+                             int add, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(cast_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, (bf16_t*)out_t, lo),
-              hipLaunchKernelGGL(cast_kernel<float>, dim3(M), dim3(256), 0, st, h, H, (float*)out_t, lo));
+  hipLaunchKernelGGL(sum_planes_kernel, dim3(M), dim3(256), 0, st, part, S, plane, W, dst, add);
   return hipGetLastError();
 }
 
-hipError_t launch_rope_kv(int dtype, const float* qkv, int M, int nq, int nkv, int d,
-                          const int32_t* pos, const int32_t* slot, const float* cos_t,
+hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int M, int nq, int nkv,
+                          int d, const int32_t* pos, const int32_t* slot, const float* cos_t,
                           const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st) {
   if (M <= 0) return hipSuccess;
+  if ((nq + 2 * nkv) * d > EAGLE_QKV_MAX) return hipErrorInvalidValue;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv),
-              hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(M), dim3(256), 0, st, qkv, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv));
+              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(M), dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv),
+              hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(M), dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv));
   return hipGetLastError();
 }
 

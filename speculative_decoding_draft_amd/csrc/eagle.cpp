@@ -64,6 +64,8 @@ bool derive(const eagle_config* c, Derived* z, std::string* why) {
   if (d % 2) return fail(why, "head_dim must be even");
   if (c->dtype == EAGLE_BF16 && d != 128) return fail(why, "bf16 path needs head_dim 128");
   if (c->dtype == EAGLE_F32 && d > 256) return fail(why, "fp32 path needs head_dim <= 256");
+  if ((c->n_heads + 2 * c->n_kv_heads) * d > EAGLE_QKV_MAX)
+    return fail(why, "q|k|v width exceeds %d", EAGLE_QKV_MAX);
   const int kq = c->dtype == EAGLE_BF16 ? 32 : 16;
   if (c->ffn < kq || c->ffn % kq) return fail(why, "ffn must be a positive multiple of %d", kq);
   if (c->vocab < 2) return fail(why, "vocab must be >= 2");
@@ -217,19 +219,17 @@ struct Carve {
 };
 
 uint64_t gemm_ws_floats(const Derived& z) {
-  // split-K workspace: max over the projections of splits * M * rows
-  struct S { int rows, K, epi; };
-  const S shapes[] = {{z.qkv_rows, z.H, EPI_STORE}, {z.H, z.nq * z.d, EPI_ADD},
-                      {2 * z.F, z.H, EPI_SWIGLU}, {z.H, z.F, EPI_ADD},
-                      {z.qkv_rows, z.kin_draft, EPI_STORE}, {z.H, z.fc_in, EPI_STORE}};
+  // split-K partial planes: max over the projections and row counts of
+  // splits * M * output width
+  struct S { int rows, K; };
+  const S shapes[] = {{z.qkv_rows, z.H}, {z.H, z.nq * z.d}, {z.H, z.F},
+                      {z.qkv_rows, z.kin_draft}, {z.H, z.fc_in}};
   uint64_t mx = 0;
-  for (const S& s : shapes) {
-    for (int M : {z.Mmax, z.Mv, 1}) {
-      GemmPlan p = gemm_plan(M, s.rows, s.K, z.dt, s.epi);
-      mx = std::max(mx, gemm_part_floats(p, s.rows, std::min(M, 80)) * (uint64_t)p.m_chunks);
-      mx = std::max(mx, (uint64_t)p.splits * M * s.rows);
+  for (const S& s : shapes)
+    for (int M = 1; M <= z.Mmax; ++M) {
+      GemmPlan p = gemm_plan(M, s.rows, s.K, z.dt, EPI_PART);
+      mx = std::max(mx, gemm_part_floats(p, s.rows, M));
     }
-  }
   return mx;
 }
 
@@ -255,10 +255,10 @@ struct eagle_ctx {
   // scratch
   float *cos_t, *sin_t;
   int32_t *tpt, *dpt;
-  float *h, *qkv, *tfeat, *gbuf, *hcat, *dout, *opart, *mlpart, *gpart, *hpart, *logits, *margin, *logp;
+  float *h, *tfeat, *gbuf, *hcat, *dout, *opart, *mlpart, *gpart, *hpart, *logits, *margin, *logp;
   void *xop, *qop, *aop, *fop, *lmh, *lmh2;   // activation operands (two planes for bf16)
   int64_t xlo = 0, qlo = 0, alo = 0, flo = 0, lmhlo = 0, lmh2lo = 0;  // lo-plane offsets (elements)
-  int32_t *counters, *g, *ids, *acc, *new_tok, *cu_src, *iota, *seq;
+  int32_t *g, *ids, *acc, *new_tok, *cu_src, *iota, *seq;
   int32_t *rpos, *rslot, *rprehi;
   uint64_t* rmask;
   TreeDev t;
@@ -297,7 +297,6 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
   TAKE(tpt, int32_t, z.t_pages);
   TAKE(dpt, int32_t, z.d_pages);
   TAKE(h, float, (uint64_t)M * z.H);
-  TAKE(qkv, float, (uint64_t)M * z.qkv_rows);
   TAKE(tfeat, float, (uint64_t)M * z.H);
   TAKE(gbuf, float, (uint64_t)M * z.H);
   TAKE(hcat, float, (uint64_t)M * z.H);
@@ -322,7 +321,6 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
     x->lmhlo = (int64_t)M * 3 * z.H;
     x->lmh2lo = (int64_t)(z.D + 1) * 3 * z.H;
   }
-  TAKE(counters, int32_t, 65536);
   TAKE(g, int32_t, z.Mv);
   TAKE(ids, int32_t, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
   TAKE(acc, int32_t, 2 + EAGLE_MAX_DEPTH + 2);
@@ -439,53 +437,60 @@ struct Prof {
 
 // Algorithmic bytes: each weight byte once, activation operands (two bf16
 // planes or fp32), outputs (read and written for residual updates).
-double opnd_bytes(const Derived& z) { return z.dt == 1 ? 4.0 : 4.0; }
+double opnd_bytes(const Derived&) { return 4.0; }   // fp32 or bf16 hi + lo
 double gemm_bytes(const Derived& z, int M, int rows, int K, int n_out, int epi) {
   const double w = (double)rows * K * z.esz;
   const double x = (double)M * K * opnd_bytes(z);
-  const double y = (double)M * n_out * (epi == EPI_ADD ? 8.0 : 4.0);
+  const double y = (double)M * n_out * 4.0;
   return w + x + y;
 }
 double attn_bytes(const Derived& z, int M, const RowVis& v) {
   const double keys = (double)(v.key_end - v.pre_lo);
-  return keys * z.nkv * z.d * 2.0 * (z.dt == 1 ? 4.0 : 4.0) + 2.0 * M * z.nq * z.d * 4.0;
+  return keys * z.nkv * z.d * 2.0 * 4.0 + 2.0 * M * z.nq * z.d * 4.0;   // K,V: fp32 or hi + lo
 }
 
 // ------------------------------------------------------------ passes
-// One decoder layer over M rows with residual stream h. If x_ready, the
-// first norm was already applied and its output sits in xop (EAGLE-3).
-eagle_status layer_forward(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, float* h,
-                           bool x_ready, const int32_t* pos, const int32_t* slot, KVView kv,
-                           RowVis vis) {
+// Applies the pending split-K partial planes of a projection to the
+// residual stream h (or sets h to their sum) and writes the next operand:
+// RMSNorm(h) * gain, or h itself when gain is null.
+eagle_status resnorm(eagle_ctx* c, float* h, int M, int S, bool set, const float* gain,
+                     float* out_f) {
+  const Derived& z = c->z;
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * (12.0 + 4.0 * S),
+           launch_resnorm(z.dt, h, z.H, M, c->gpart, S, (int64_t)M * z.H, set ? 1 : 0, gain,
+                          c->cfg.rms_eps, c->xop, c->xlo, out_f, c->st));
+  return EAGLE_OK;
+}
+
+// One decoder layer over M rows. On entry xop holds the normed layer input
+// (row width kin); on exit the down-projection partials are pending in gpart
+// (*s_down planes) for the caller's resnorm.
+eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, float* h,
+                        const int32_t* pos, const int32_t* slot, KVView kv, RowVis vis,
+                        int* s_down) {
   const Derived& z = c->z;
   const int dt = z.dt;
-  const double rowb = (double)M * z.H * 8.0;
-  if (!x_ready)
-    PROFILED(EAGLE_PROF_ROWS, rowb,
-             launch_rmsnorm(dt, h, z.H, w.attn_norm, z.H, c->cfg.rms_eps, M, c->xop, kin, c->xlo,
-                            nullptr, 0, c->st));
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.qkv_rows, kin, z.qkv_rows, EPI_STORE),
-           launch_gemm(dt, EPI_STORE, w.wqkv, c->xop, c->xlo, M, z.qkv_rows, kin, c->qkv,
-                       z.qkv_rows, nullptr, 0, c->gpart, c->counters, c->st));
-  PROFILED(EAGLE_PROF_ROWS, (double)M * z.qkv_rows * 8.0,
-           launch_rope_kv(dt, c->qkv, M, z.nq, z.nkv, z.d, pos, slot, c->cos_t, c->sin_t, c->qop,
-                          c->qlo, kv, c->st));
+  int S = 1;
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.qkv_rows, kin, z.qkv_rows, EPI_PART),
+           launch_gemm(dt, EPI_PART, w.wqkv, c->xop, c->xlo, M, z.qkv_rows, kin, c->gpart,
+                       z.qkv_rows, nullptr, 0, &S, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.qkv_rows * 4.0 * (S + 1),
+           launch_rope_kv(dt, c->gpart, S, (int64_t)M * z.qkv_rows, M, z.nq, z.nkv, z.d, pos, slot,
+                          c->cos_t, c->sin_t, c->qop, c->qlo, kv, c->st));
   PROFILED(EAGLE_PROF_ATTN, attn_bytes(z, M, vis),
            launch_attention(dt, c->qop, c->qlo, kv, vis, M, z.nq, z.d,
                             1.0f / std::sqrt((float)z.d), c->opart, c->mlpart, c->aop, c->alo,
                             c->st));
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.nq * z.d, z.H, EPI_ADD),
-           launch_gemm(dt, EPI_ADD, w.wo, c->aop, c->alo, M, z.H, z.nq * z.d, h, z.H, nullptr, 0,
-                       c->gpart, c->counters, c->st));
-  PROFILED(EAGLE_PROF_ROWS, rowb,
-           launch_rmsnorm(dt, h, z.H, w.ffn_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H, c->xlo,
-                          nullptr, 0, c->st));
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.nq * z.d, z.H, EPI_PART),
+           launch_gemm(dt, EPI_PART, w.wo, c->aop, c->alo, M, z.H, z.nq * z.d, c->gpart, z.H,
+                       nullptr, 0, &S, c->st));
+  SCHK(resnorm(c, h, M, S, false, w.ffn_norm, nullptr));
   PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, 2 * z.F, z.H, z.F, EPI_SWIGLU),
            launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, c->xlo, M, z.F, z.H, nullptr, 0, c->fop,
-                       c->flo, c->gpart, c->counters, c->st));
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.F, z.H, EPI_ADD),
-           launch_gemm(dt, EPI_ADD, w.wdown, c->fop, c->flo, M, z.H, z.F, h, z.H, nullptr, 0,
-                       c->gpart, c->counters, c->st));
+                       c->flo, nullptr, c->st));
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.F, z.H, EPI_PART),
+           launch_gemm(dt, EPI_PART, w.wdown, c->fop, c->flo, M, z.H, z.F, c->gpart, z.H, nullptr,
+                       0, s_down, c->st));
   return EAGLE_OK;
 }
 
@@ -495,10 +500,15 @@ eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t*
   const Derived& z = c->z;
   PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 4.0,
            launch_embed(z.dt, c->embed, z.H, tok, M, c->h, c->st));
+  SCHK(resnorm(c, c->h, M, 0, false, c->tl[0].attn_norm, nullptr));
   for (int l = 0; l < z.NL; ++l) {
     KVView kv = c->tkv0;
     kv.base = (char*)c->tkv0.base + (int64_t)l * c->t_layer_elems * z.esz;
-    SCHK(layer_forward(c, c->tl[l], z.H, M, c->h, false, pos, slot, kv, vis));
+    int sd = 1;
+    SCHK(layer_core(c, c->tl[l], z.H, M, c->h, pos, slot, kv, vis, &sd));
+    const bool last = l + 1 == z.NL;
+    SCHK(resnorm(c, c->h, M, sd, false, last ? c->final_norm : c->tl[l + 1].attn_norm,
+                 last ? c->tfeat : nullptr));
     if (c->cfg.head == EAGLE_HEAD_E3)
       for (int j = 0; j < 3; ++j)
         if (c->cfg.feat_layers[j] == l)
@@ -506,9 +516,6 @@ eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t*
                    launch_store_feat(z.dt, c->h, z.H, M, (char*)c->lmh + (int64_t)j * z.H * z.esz,
                                      3 * z.H, c->lmhlo, c->st));
   }
-  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
-           launch_rmsnorm(z.dt, c->h, z.H, c->final_norm, z.H, c->cfg.rms_eps, M, c->xop, z.H,
-                          c->xlo, c->tfeat, z.H, c->st));
   c->last_target_rows = M;
   return EAGLE_OK;
 }
@@ -519,22 +526,22 @@ eagle_status draft_pass(eagle_ctx* c, int M, const int32_t* tok, const float* fe
                         const int32_t* idx, const int32_t* pos, const int32_t* slot, RowVis vis,
                         float* hout) {
   const Derived& z = c->z;
-  bool x_ready = false;
   if (c->cfg.head == EAGLE_HEAD_E1) {
+    int S = 1;
     PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
              launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->xlo, c->st));
-    PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_STORE),
-             launch_gemm(z.dt, EPI_STORE, c->fc, c->xop, c->xlo, M, z.H, 2 * z.H, hout, z.H,
-                         nullptr, 0, c->gpart, c->counters, c->st));
+    PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_PART),
+             launch_gemm(z.dt, EPI_PART, c->fc, c->xop, c->xlo, M, z.H, 2 * z.H, c->gpart, z.H,
+                         nullptr, 0, &S, c->st));
+    SCHK(resnorm(c, hout, M, S, true, c->dl.attn_norm, nullptr));
   } else {
     PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 16.0,
              launch_draft_input_e3(z.dt, c->embed, tok, feat, idx, c->dl.attn_norm,
                                    c->cfg.rms_eps, M, z.H, c->xop, c->xlo, hout, c->st));
-    x_ready = true;
   }
-  SCHK(layer_forward(c, c->dl, z.kin_draft, M, hout, x_ready, pos, slot, c->dkv, vis));
-  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 8.0,
-           launch_cast(z.dt, hout, z.H, M, c->xop, c->xlo, c->st));
+  int sd = 1;
+  SCHK(layer_core(c, c->dl, z.kin_draft, M, hout, pos, slot, c->dkv, vis, &sd));
+  SCHK(resnorm(c, hout, M, sd, false, nullptr, nullptr));
   return EAGLE_OK;
 }
 
@@ -550,10 +557,9 @@ eagle_status catch_up(eagle_ctx* c, int M, int first, const int32_t* tok, const 
   if (!final) return EAGLE_OK;
   HCHK(hipMemcpyAsync(c->dout, c->hcat + (int64_t)(M - 1) * z.H, sizeof(float) * z.H,
                       hipMemcpyDeviceToDevice, c->st));
-  PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
-           launch_cast(z.dt, c->dout, z.H, 1, c->xop, c->xlo, c->st));
+  const void* xl = (const char*)c->xop + (int64_t)(M - 1) * z.H * z.esz;
   PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)z.H * 4.0,
-           launch_lmhead_topk(z.dt, c->lm, c->xop, c->xlo, 1, z.V, z.H, z.k_b, c->hpart, c->ids,
+           launch_lmhead_topk(z.dt, c->lm, xl, c->xlo, 1, z.V, z.H, z.k_b, c->hpart, c->ids,
                               c->logp, c->st));
   PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_append(c->t, c->tp, c->ids, c->logp, 1, ctx_after, c->st));
   return EAGLE_OK;
@@ -562,9 +568,12 @@ eagle_status catch_up(eagle_ctx* c, int M, int first, const int32_t* tok, const 
 // E3: g = FC([l;m;h]) for M committed rows whose [l;m;h] operands are at src.
 eagle_status fuse_rows(eagle_ctx* c, int M, const void* src, int64_t src_lo) {
   const Derived& z = c->z;
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 3 * z.H, z.H, EPI_STORE),
-           launch_gemm(z.dt, EPI_STORE, c->fc, src, src_lo, M, z.H, 3 * z.H, c->gbuf, z.H, nullptr,
-                       0, c->gpart, c->counters, c->st));
+  int S = 1;
+  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 3 * z.H, z.H, EPI_PART),
+           launch_gemm(z.dt, EPI_PART, c->fc, src, src_lo, M, z.H, 3 * z.H, c->gpart, z.H, nullptr,
+                       0, &S, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 4.0 * (S + 1),
+           launch_sum_planes(c->gpart, S, (int64_t)M * z.H, M, z.H, c->gbuf, 0, c->st));
   return EAGLE_OK;
 }
 
@@ -715,7 +724,6 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
     up(c->t.s_prow, sw.data(), sw.size() * 4);
     up(c->t.s_exp, se.data(), se.size() * 4);
     up(c->t.s_nexp, sne.data(), sne.size() * 4);
-    if (e == hipSuccess) e = hipMemset(c->counters, 0, 65536 * 4);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
       delete c;

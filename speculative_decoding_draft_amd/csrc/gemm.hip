@@ -1,293 +1,315 @@
-// Skinny MFMA GEMM for decode-time projections (M <= 80 rows per pass) and
-// the fused LM-head reductions. Every projection here reads each weight
-// byte once per pass, so the kernel is organised around streaming W:
-//  * a 512-thread workgroup owns 16*NB output columns; its 8 waves split
-//    the K range and issue up to 8 steps (16 B per lane each) of W loads
-//    before the first MFMA, so each CU keeps ~64 KB of weights in flight;
-//  * the activation x (bf16 or fp32, a few MB at most) is read from L2 per
-//    step; rows beyond M read row M-1 and are discarded;
-//  * the 8 partial accumulators are summed in LDS in a fixed order; when a
-//    tile is further split over workgroups (narrow N), partials go to a
-//    workspace and the last workgroup to arrive sums them in split order,
-//    so results are deterministic.
+// Weight-streaming projections (M <= 80 activation rows per pass) and the
+// fused LM-head reductions.
+//
+// Every projection of a decode/verify pass reads each weight byte once, so
+// the kernel is built around streaming W from HBM:
+//  * a workgroup of NW waves owns NW*16 consecutive weight rows (one 16-row
+//    MFMA block per wave) and a K range; the K range is walked in chunks of
+//    CS steps (16 bytes of W per lane per step);
+//  * the activation chunk x[M, chunk] (fp32 values kept as bf16 hi + lo
+//    planes, or one fp32 plane) is staged once per workgroup into LDS in an
+//    XOR-swizzled layout (conflict-free 16-byte reads) and shared by all
+//    waves, so x is read from L2 once per NW*16 weight rows;
+//  * the next chunk's W fragments and x chunk are loaded while the current
+//    chunk is multiplied (double buffering in registers and LDS);
+//  * narrow outputs are split over K across workgroups; each split writes
+//    its own fp32 partial plane and the consumer of the result (the residual
+//    + RMSNorm kernel, or RoPE) sums the planes in a fixed order, so no
+//    cross-workgroup synchronisation is needed and results are repeatable.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int NWAVES = 8;
-constexpr int NTHREADS = NWAVES * WAVE;
-constexpr int PREF = 8;   // W steps issued before consuming them
-
-struct GemmArgs {
-  const void* W; int64_t ldw;
-  const void* X; int64_t ldx; int64_t xlo;
-  int M, N, K;          // N = output columns (SwiGLU: F)
-  int n_tiles, splits, steps_per_split;
-  float* Y; int64_t ldy;
-  void* Yt; int64_t ytlo;
-  float* part; int* counters;
-};
-
-// Rows of W read by n-block b of tile `tile`.
-template <int NB, int EPI>
-__device__ __forceinline__ int block_row(int tile, int b, int N) {
-  if (EPI == EPI_SWIGLU) {
-    return (b < NB / 2) ? tile * 8 * NB + 16 * b : N + tile * 8 * NB + 16 * (b - NB / 2);
-  }
-  return tile * 16 * NB + 16 * b;
+// LDS address (elements) of 16-byte chunk q of staged row r. Rows are KCH
+// elements wide; the chunk index is XOR-swizzled with the row.
+template <typename T, int KCH>
+__device__ __forceinline__ int xs_addr(int r, int q) {
+  constexpr int EPL = 16 / sizeof(T);
+  constexpr int QM = KCH / EPL - 1;
+  return r * KCH + ((q ^ (((r & 15) << 1) & QM)) * EPL);
 }
 
-// Streams this workgroup's K range and leaves the reduced tile in
-// `tile_out[n_local][m_local]` (16*NB x 16*MT floats, LDS).
-template <typename T, int MT, int NB>
-__device__ __forceinline__ void tile_compute(const T* __restrict__ W, int64_t ldw,
-                                             const int (&wrow)[NB], const T* __restrict__ X,
-                                             int64_t ldx, int64_t xlo, int M, int m0, int s_lo,
-                                             int s_hi, float* red, float* tile_out) {
-  using MM = Mma<T>;
-  constexpr int EPL = MM::EPL, KS = MM::KSTEP;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int lr = lane & 15, lg = lane >> 4;
+struct ProjArgs {
+  const void* W;        // [rows, K]
+  const void* X;        // [M, K] operand (lo plane at X + xlo)
+  int64_t xlo;
+  int M, rows, K;       // rows of W (SwiGLU: 2F, gate rows then up rows)
+  int F;                // SwiGLU: output columns
+  int splits, steps_per_split;
+  float* Y;             // EPI_PART: partial planes [split][M][ldy]
+  int64_t ldy, plane;
+  void* Yt;             // EPI_SWIGLU: operand [M, F] (lo plane at Yt + ytlo)
+  int64_t ytlo;
+};
 
-  const T* wp[NB];
+template <typename T, int MT, int NW, int CS>
+struct ProjShape {
+  static constexpr int EPL = 16 / sizeof(T);
+  static constexpr int KS = Mma<T>::KSTEP;              // k per step
+  static constexpr int KCH = CS * KS;                   // k per chunk
+  static constexpr int MP = 16 * MT;                    // staged activation rows
+  static constexpr int PLANES = Opnd<T>::SPLIT ? 2 : 1;
+  static constexpr int PIECES = PLANES * MP * KCH / EPL;  // 16-byte pieces per chunk
+  static constexpr int NX = (PIECES + NW * 64 - 1) / (NW * 64);
+  static constexpr int LDS_ELEMS = PLANES * MP * KCH;   // one buffer
+};
+
+// Loads this thread's pieces of the activation chunk starting at step s0.
+template <typename T, int MT, int NW, int CS>
+__device__ __forceinline__ void stage_load(const ProjArgs& a, int s0, int s_hi, uint4 (&xr)[ProjShape<T, MT, NW, CS>::NX]) {
+  using S = ProjShape<T, MT, NW, CS>;
+  const T* X = (const T*)a.X;
 #pragma unroll
-  for (int b = 0; b < NB; ++b) wp[b] = W + (int64_t)(wrow[b] + lr) * ldw + lg * EPL;
-  const T* xp[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    int m = min(m0 + 16 * t + lr, M - 1);
-    xp[t] = X + (int64_t)m * ldx + lg * EPL;
+  for (int i = 0; i < S::NX; ++i) {
+    const int p = min((int)threadIdx.x + i * NW * 64, S::PIECES - 1);
+    const int plane = p / (S::MP * S::KCH / S::EPL);
+    const int rem = p % (S::MP * S::KCH / S::EPL);
+    const int row = min(rem / (S::KCH / S::EPL), a.M - 1);
+    const int col = min(s0 * S::KS + (rem % (S::KCH / S::EPL)) * S::EPL, s_hi * S::KS - S::EPL);
+    xr[i] = ld16(X + plane * a.xlo + (int64_t)row * a.K + col);
   }
+}
 
-  const int n = max(0, s_hi - s_lo);
-  const int q = n / NWAVES, r = n % NWAVES;
-  const int ws = s_lo + wave * q + min(wave, r);
-  const int we = ws + q + (wave < r ? 1 : 0);
+template <typename T, int MT, int NW, int CS>
+__device__ __forceinline__ void stage_store(T* xs, const uint4 (&xr)[ProjShape<T, MT, NW, CS>::NX]) {
+  using S = ProjShape<T, MT, NW, CS>;
+#pragma unroll
+  for (int i = 0; i < S::NX; ++i) {
+    const int p = threadIdx.x + i * NW * 64;
+    if (p >= S::PIECES) break;
+    const int plane = p / (S::MP * S::KCH / S::EPL);
+    const int rem = p % (S::MP * S::KCH / S::EPL);
+    const int row = rem / (S::KCH / S::EPL);
+    const int q = rem % (S::KCH / S::EPL);
+    *reinterpret_cast<uint4*>(xs + xs_addr<T, S::KCH>(plane * S::MP + row, q)) = xr[i];
+  }
+}
 
-  f32x4 acc[NB][MT];
+// Streams rows [row0, row0 + 16) of W over steps [s_lo, s_hi) against the
+// staged activations; acc[t] holds the 16 x 16 tile of m-tile t.
+template <typename T, int MT, int NW, int CS>
+__device__ __forceinline__ void proj_core(const ProjArgs& a, int row0, int s_lo, int s_hi, T* xs,
+                                          f32x4 (&acc)[MT]) {
+  using S = ProjShape<T, MT, NW, CS>;
+  using MM = Mma<T>;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const T* wp = (const T*)a.W + (int64_t)min(row0 + lr, a.rows - 1) * a.K + lg * S::EPL;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[b][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = (s_hi - s_lo + CS - 1) / CS;
+  uint4 wA[CS], wB[CS], xr[S::NX];
+  T* xs0 = xs;
+  T* xs1 = xs + S::LDS_ELEMS;
 
-  for (int s = ws; s < we; s += PREF) {
-    const int cnt = we - s;
-    uint4 wf[PREF][NB];
+  auto load_w = [&](uint4 (&w)[CS], int c) {
 #pragma unroll
-    for (int u = 0; u < PREF; ++u)
-      if (u < cnt) {
+    for (int u = 0; u < CS; ++u) w[u] = ld16(wp + (int64_t)min(s_lo + c * CS + u, s_hi - 1) * S::KS);
+  };
+  auto compute = [&](const uint4 (&w)[CS], const T* x, int c) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) wf[u][b] = ld16(wp[b] + (int64_t)(s + u) * KS);
-      }
-#pragma unroll
-    for (int u = 0; u < PREF; ++u)
-      if (u < cnt) {
-        uint4 xf[MT], xl[MT];
+    for (int u = 0; u < CS; ++u) {
+      if (s_lo + c * CS + u < s_hi) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          xf[t] = ld16(xp[t] + (int64_t)(s + u) * KS);
-          if (Opnd<T>::SPLIT) xl[t] = ld16(xp[t] + xlo + (int64_t)(s + u) * KS);
-        }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            MM::mma(wf[u][b], xf[t], acc[b][t]);
-            if (Opnd<T>::SPLIT) MM::mma(wf[u][b], xl[t], acc[b][t]);
+          const uint4 xh = *reinterpret_cast<const uint4*>(x + xs_addr<T, S::KCH>(16 * t + lr, 4 * u + lg));
+          MM::mma(w[u], xh, acc[t]);
+          if (Opnd<T>::SPLIT) {
+            const uint4 xl = *reinterpret_cast<const uint4*>(x + xs_addr<T, S::KCH>(S::MP + 16 * t + lr, 4 * u + lg));
+            MM::mma(w[u], xl, acc[t]);
           }
+        }
       }
+    }
+  };
+  if (nch <= 0) return;
+  load_w(wA, 0);
+  stage_load<T, MT, NW, CS>(a, s_lo, s_hi, xr);
+  stage_store<T, MT, NW, CS>(xs0, xr);
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) {
+      stage_load<T, MT, NW, CS>(a, s_lo + (c + 1) * CS, s_hi, xr);
+      load_w(wB, c + 1);
+    }
+    __syncthreads();
+    compute(wA, xs0, c);
+    if (c + 1 < nch) stage_store<T, MT, NW, CS>(xs1, xr);
+    if (c + 1 >= nch) break;
+    if (c + 2 < nch) {
+      stage_load<T, MT, NW, CS>(a, s_lo + (c + 2) * CS, s_hi, xr);
+      load_w(wA, c + 2);
+    }
+    __syncthreads();
+    compute(wB, xs1, c + 1);
+    if (c + 2 < nch) stage_store<T, MT, NW, CS>(xs0, xr);
   }
+}
 
-  // fixed-order reduction of the 8 waves: (w + w+4) then ((0+1) + (2+3))
-  constexpr int NV = NB * MT * 4;
-  if (wave >= 4) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
+template <typename T, int MT, int NW, int CS, int EPI>
+__global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
+  using S = ProjShape<T, MT, NW, CS>;
+  __shared__ __attribute__((aligned(16))) T xs[2 * S::LDS_ELEMS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tile = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+  const int m0 = blockIdx.y * S::MP;
+  ProjArgs b = a;
+  b.X = (const T*)a.X + (int64_t)m0 * a.K;
+  b.M = min(S::MP, a.M - m0);
+  const int total = a.K / S::KS;
+  const int s_lo = split * a.steps_per_split;
+  const int s_hi = min(total, s_lo + a.steps_per_split);
+  // SwiGLU tiles: waves [0, NW/2) take gate rows, waves [NW/2, NW) the
+  // matching up rows, so one tile yields NW/2 * 16 output columns.
+  int row0;
+  if (EPI == EPI_SWIGLU) {
+    const int half = NW / 2;
+    const int col0 = tile * half * 16 + (wave % half) * 16;
+    row0 = (wave < half) ? col0 : a.F + col0;
+  } else {
+    row0 = (tile * NW + wave) * 16;
+  }
+  f32x4 acc[MT];
+  proj_core<T, MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc);
+
+  if (EPI == EPI_SWIGLU) {
+    constexpr int half = NW / 2;
+    __syncthreads();   // xs is reused for the gate values
+    float* gate = reinterpret_cast<float*>(xs);   // [half*16 cols][MP]
+    if (wave < half) {
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) red[((wave - 4) * NV + (b * MT + t) * 4 + j) * WAVE + lane] = acc[b][t][j];
-  }
-  __syncthreads();
-  if (wave < 4) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
+        for (int j = 0; j < 4; ++j) gate[(wave * 16 + 4 * lg + j) * S::MP + 16 * t + lr] = acc[t][j];
+    }
+    __syncthreads();
+    if (wave >= half) {
+      const int w2 = wave - half;
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float* p = &red[(wave * NV + (b * MT + t) * 4 + j) * WAVE + lane];
-          *p = acc[b][t][j] + *p;
+          const int c = w2 * 16 + 4 * lg + j;
+          const int col = tile * half * 16 + c;
+          const int m = 16 * t + lr;
+          if (m < b.M && col < a.F) {
+            const float g = gate[c * S::MP + m];
+            const float v = g / (1.0f + expf(-g)) * acc[t][j];
+            Opnd<T>::store((T*)a.Yt, a.ytlo, (int64_t)(m0 + m) * a.F + col, v);
+          }
         }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < NV * WAVE; e += NTHREADS) {
-    const int v = e / WAVE, ln = e % WAVE;
-    const float val = (red[(0 * NV + v) * WAVE + ln] + red[(1 * NV + v) * WAVE + ln]) +
-                      (red[(2 * NV + v) * WAVE + ln] + red[(3 * NV + v) * WAVE + ln]);
-    const int b = v / (MT * 4), t = (v / 4) % MT, j = v % 4;
-    const int nl = 16 * b + 4 * (ln >> 4) + j;
-    const int ml = 16 * t + (ln & 15);
-    tile_out[nl * (16 * MT) + ml] = val;
-  }
-  __syncthreads();
-}
-
-template <typename T, int MT, int NB, int EPI>
-__global__ __launch_bounds__(NTHREADS) void gemm_kernel(GemmArgs a) {
-  __shared__ float red[4 * NB * MT * 4 * WAVE];
-  __shared__ float tile_out[16 * NB * 16 * MT];
-  __shared__ int s_last;
-  constexpr int R = 16 * NB, C = 16 * MT;
-
-  int tile, split;
-  if (a.splits == 1) {
-    tile = blockIdx.x;
-    split = 0;
-  } else {  // the splits of one tile land on the same XCD (round-robin of 8)
-    const int idx = blockIdx.x;
-    split = (idx / 8) % a.splits;
-    tile = (idx % 8) + 8 * (idx / (8 * a.splits));
-    if (tile >= a.n_tiles) return;
-  }
-  const int m0 = blockIdx.y * C;
-  const int rows_total = (EPI == EPI_SWIGLU) ? 2 * a.N : a.N;
-  // per-lane clamping for partial blocks
-  int wrow_l[NB];
-  const int lr = threadIdx.x & 15;
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    int r0 = block_row<NB, EPI>(tile, b, a.N);
-    int lim = (EPI == EPI_SWIGLU) ? ((b < NB / 2) ? a.N : rows_total) : rows_total;
-    wrow_l[b] = min(r0 + lr, lim - 1) - lr;
-  }
-  const int total = a.K / Mma<T>::KSTEP;
-  const int s_lo = split * a.steps_per_split;
-  const int s_hi = min(total, s_lo + a.steps_per_split);
-  tile_compute<T, MT, NB>((const T*)a.W, a.ldw, wrow_l, (const T*)a.X, a.ldx, a.xlo, a.M, m0,
-                          s_lo, s_hi, red, tile_out);
-
-  const int mrows = min(C, a.M - m0);
-  if (a.splits > 1) {
-    // partial tile -> workspace [split][M][rows_total]; the last arriver sums
-    for (int e = threadIdx.x; e < R * C; e += NTHREADS) {
-      const int ml = e / R, nl = e % R;
-      if (ml >= mrows) continue;
-      const int b = nl / 16;
-      const int row = block_row<NB, EPI>(tile, b, a.N) + (nl % 16);
-      if (row >= rows_total) continue;
-      a.part[((int64_t)split * a.M + m0 + ml) * rows_total + row] = tile_out[nl * C + ml];
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const int prev = atomicAdd(&a.counters[blockIdx.y * a.n_tiles + tile], 1);
-      s_last = (prev == a.splits - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    for (int e = threadIdx.x; e < R * C; e += NTHREADS) {
-      const int ml = e / R, nl = e % R;
-      if (ml >= mrows) continue;
-      const int b = nl / 16;
-      const int row = block_row<NB, EPI>(tile, b, a.N) + (nl % 16);
-      if (row >= rows_total) continue;
-      float s = 0.f;
-      for (int sp = 0; sp < a.splits; ++sp)
-        s += __builtin_nontemporal_load(&a.part[((int64_t)sp * a.M + m0 + ml) * rows_total + row]);
-      tile_out[nl * C + ml] = s;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) a.counters[blockIdx.y * a.n_tiles + tile] = 0;
-  }
-
-  if (EPI == EPI_SWIGLU) {
-    constexpr int HALF = R / 2;
-    for (int e = threadIdx.x; e < HALF * C; e += NTHREADS) {
-      const int ml = e / HALF, nl = e % HALF;
-      const int col = tile * HALF + nl;
-      if (ml >= mrows || col >= a.N) continue;
-      const float g = tile_out[nl * C + ml];
-      const float u = tile_out[(nl + HALF) * C + ml];
-      const float v = g / (1.0f + expf(-g)) * u;
-      Opnd<T>::store((T*)a.Yt, a.ytlo, (int64_t)(m0 + ml) * a.N + col, v);
     }
   } else {
-    for (int e = threadIdx.x; e < R * C; e += NTHREADS) {
-      const int ml = e / R, nl = e % R;
-      const int col = tile * R + nl;
-      if (ml >= mrows || col >= a.N) continue;
-      float* y = &a.Y[(int64_t)(m0 + ml) * a.ldy + col];
-      const float v = tile_out[nl * C + ml];
-      if (EPI == EPI_ADD) *y = *y + v;
-      else *y = v;
-    }
+    float* Y = a.Y + (int64_t)split * a.plane;
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = row0 + 4 * lg + j;
+        const int m = 16 * t + lr;
+        if (m < b.M && row < a.rows) Y[(int64_t)(m0 + m) * a.ldy + row] = acc[t][j];
+      }
   }
 }
 
 // ---------------------------------------------------------------- LM head
 struct HeadArgs {
-  const void* W; const void* X; int64_t xlo;
-  int M, V, H, k;
-  float* part;      // per workgroup and row: argmax {max1, id1, max2} or topk {max, sum, k vals, k ids}
-  float* logits;    // optional [M, V]
+  ProjArgs p;     // W = LM head [V, H], X = features
+  int k;
+  float* part;    // per tile and row: argmax {max1, id1, max2} or topk {max, sum, k vals, k ids}
+  float* logits;  // optional [M, V]
 };
 
-template <typename T, int MT, int NB, bool TOPK>
-__global__ __launch_bounds__(NTHREADS) void lmhead_kernel(HeadArgs a) {
-  __shared__ float red[4 * NB * MT * 4 * WAVE];
-  __shared__ float tile_out[16 * NB * 16 * MT];
-  constexpr int R = 16 * NB, C = 16 * MT;
+template <typename T, int MT, int NW, int CS, bool TOPK>
+__global__ __launch_bounds__(NW * 64) void lmhead_kernel(HeadArgs h) {
+  using S = ProjShape<T, MT, NW, CS>;
+  __shared__ __attribute__((aligned(16))) T xs[2 * S::LDS_ELEMS];
+  const ProjArgs& a = h.p;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
   const int tile = blockIdx.x;
-  const int lr = threadIdx.x & 15;
-  int wrow[NB];
+  const int R = NW * 16;
+  const int row0 = tile * R + wave * 16;
+  f32x4 acc[MT];
+  proj_core<T, MT, NW, CS>(a, row0, 0, a.K / S::KS, xs, acc);
+  __syncthreads();
+  float* vals = reinterpret_cast<float*>(xs);   // [R][MP]
 #pragma unroll
-  for (int b = 0; b < NB; ++b) wrow[b] = min(tile * R + 16 * b + lr, a.V - 1) - lr;
-  const int total = a.H / Mma<T>::KSTEP;
-  tile_compute<T, MT, NB>((const T*)a.W, a.H, wrow, (const T*)a.X, a.H, a.xlo, a.M, 0, 0, total,
-                          red, tile_out);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nvalid = min(R, a.V - tile * R);
-  if (a.logits) {
-    for (int e = threadIdx.x; e < R * C; e += NTHREADS) {
-      const int ml = e / R, nl = e % R;
-      if (ml < a.M && nl < nvalid)
-        a.logits[(int64_t)ml * a.V + tile * R + nl] = tile_out[nl * C + ml];
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vals[(wave * 16 + 4 * lg + j) * S::MP + 16 * t + lr] = acc[t][j];
+  __syncthreads();
+  const int nvalid = min(R, a.rows - tile * R);
+  if (h.logits) {
+    for (int e = threadIdx.x; e < R * S::MP; e += NW * 64) {
+      const int m = e / R, n = e % R;
+      if (m < a.M && n < nvalid) h.logits[(int64_t)m * a.rows + tile * R + n] = vals[n * S::MP + m];
     }
   }
-  const int stride = TOPK ? (2 + 2 * a.k) : 3;
-  for (int m = wave; m < a.M; m += NWAVES) {
-    const bool ok = lane < nvalid;
-    float v = ok ? tile_out[lane * C + m] : -INFINITY;
-    int id = tile * R + lane;
-    float* out = a.part + ((int64_t)tile * a.M + m) * stride;
+  // each lane holds RPL of the tile's R vocabulary rows: lane + 64 * u
+  constexpr int RPL = (NW * 16) / 64;
+  static_assert(RPL * 64 == NW * 16, "tile rows must be a multiple of the wave width");
+  static_assert(NW * 16 * S::MP * 4 <= (int)sizeof(xs), "row values must fit the staging buffer");
+  const int stride = TOPK ? (2 + 2 * h.k) : 3;
+  for (int m = wave; m < a.M; m += NW) {
+    float v[RPL];
+    int id[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int n = lane + 64 * u;
+      const bool ok = n < nvalid;
+      v[u] = ok ? vals[n * S::MP + m] : -INFINITY;
+      id[u] = ok ? tile * R + n : 0x7fffffff;
+    }
+    float* out = h.part + ((int64_t)tile * a.M + m) * stride;
     if (!TOPK) {
-      // max with lowest id, then second max
-      float bv = v; int bi = ok ? id : 0x7fffffff;
+      float bv = v[0];
+      int bi = id[0];
+#pragma unroll
+      for (int u = 1; u < RPL; ++u)
+        if (v[u] > bv || (v[u] == bv && id[u] < bi)) { bv = v[u]; bi = id[u]; }
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) {
-        float ov = __shfl_xor(bv, o); int oi = __shfl_xor(bi, o);
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
         if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
       }
-      float sv = (ok && id != bi) ? v : -INFINITY;
-      sv = wave_max(sv);
+      float lv = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < RPL; ++u)
+        if (id[u] != bi) lv = fmaxf(lv, v[u]);
+      const float sv = wave_max(lv);
       if (lane == 0) { out[0] = bv; out[1] = __int_as_float(bi); out[2] = sv; }
     } else {
-      const float mx = wave_max(v);
-      const float se = wave_sum(ok ? expf(v - mx) : 0.f);
+      float lm = v[0];
+#pragma unroll
+      for (int u = 1; u < RPL; ++u) lm = fmaxf(lm, v[u]);
+      const float mx = wave_max(lm);
+      float le = 0.f;
+#pragma unroll
+      for (int u = 0; u < RPL; ++u) le += (id[u] != 0x7fffffff) ? expf(v[u] - mx) : 0.f;
+      const float se = wave_sum(le);
       if (lane == 0) { out[0] = mx; out[1] = se; }
-      float cur = v; int cid = ok ? id : 0x7fffffff;
-      for (int i = 0; i < a.k; ++i) {
-        float bv = cur; int bi = cid;
+      for (int i = 0; i < h.k; ++i) {
+        // this lane's best remaining candidate, then the wave's
+        float bv = v[0];
+        int bi = id[0];
+#pragma unroll
+        for (int u = 1; u < RPL; ++u)
+          if (v[u] > bv || (v[u] == bv && id[u] < bi)) { bv = v[u]; bi = id[u]; }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
-          float ov = __shfl_xor(bv, o); int oi = __shfl_xor(bi, o);
+          const float ov = __shfl_xor(bv, o);
+          const int oi = __shfl_xor(bi, o);
           if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
         }
-        if (lane == 0) { out[2 + i] = bv; out[2 + a.k + i] = __int_as_float(bi); }
-        if (cid == bi) { cur = -INFINITY; cid = 0x7fffffff; }
+        if (lane == 0) { out[2 + i] = bv; out[2 + h.k + i] = __int_as_float(bi); }
+#pragma unroll
+        for (int u = 0; u < RPL; ++u)
+          if (id[u] == bi) { v[u] = -INFINITY; id[u] = 0x7fffffff; }
       }
     }
   }
@@ -297,20 +319,25 @@ __global__ __launch_bounds__(NTHREADS) void lmhead_kernel(HeadArgs a) {
 __global__ __launch_bounds__(256) void argmax_combine(const float* part, int n_tiles, int M,
                                                       int32_t* g, float* margin) {
   const int m = blockIdx.x;
-  float b1 = -INFINITY, b2 = -INFINITY; int i1 = 0x7fffffff;
+  float b1 = -INFINITY, b2 = -INFINITY;
+  int i1 = 0x7fffffff;
   for (int t = threadIdx.x; t < n_tiles; t += blockDim.x) {
     const float* p = part + ((int64_t)t * M + m) * 3;
-    float p1 = p[0], p2 = p[2]; int pi = __float_as_int(p[1]);
+    const float p1 = p[0], p2 = p[2];
+    const int pi = __float_as_int(p[1]);
     if (p1 > b1 || (p1 == b1 && pi < i1)) { b2 = fmaxf(b1, p2); b1 = p1; i1 = pi; }
     else b2 = fmaxf(b2, p1);
   }
-  __shared__ float s1[256], s2[256]; __shared__ int si[256];
+  __shared__ float s1[256], s2[256];
+  __shared__ int si[256];
   s1[threadIdx.x] = b1; s2[threadIdx.x] = b2; si[threadIdx.x] = i1;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
     if ((int)threadIdx.x < o) {
-      float a1 = s1[threadIdx.x], a2 = s2[threadIdx.x]; int ai = si[threadIdx.x];
-      float c1 = s1[threadIdx.x + o], c2 = s2[threadIdx.x + o]; int ci = si[threadIdx.x + o];
+      float a1 = s1[threadIdx.x], a2 = s2[threadIdx.x];
+      int ai = si[threadIdx.x];
+      const float c1 = s1[threadIdx.x + o], c2 = s2[threadIdx.x + o];
+      const int ci = si[threadIdx.x + o];
       if (c1 > a1 || (c1 == a1 && ci < ai)) { a2 = fmaxf(a1, c2); a1 = c1; ai = ci; }
       else a2 = fmaxf(a2, c1);
       s1[threadIdx.x] = a1; s2[threadIdx.x] = a2; si[threadIdx.x] = ai;
@@ -327,7 +354,6 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
   const int stride = 2 + 2 * k;
   __shared__ float sred[256];
   __shared__ float s_gmax, s_lse;
-  // global max
   float mx = -INFINITY;
   for (int t = threadIdx.x; t < n_tiles; t += 256) mx = fmaxf(mx, part[((int64_t)t * M + m) * stride]);
   sred[threadIdx.x] = mx;
@@ -353,15 +379,15 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
   }
   if (threadIdx.x == 0) s_lse = logf(sred[0]);
   __syncthreads();
-  // per-thread sorted candidate list
-  float lv[16]; int li[16];
+  float lv[16];
+  int li[16];
   for (int i = 0; i < k; ++i) { lv[i] = -INFINITY; li[i] = 0x7fffffff; }
   for (int t = threadIdx.x; t < n_tiles; t += 256) {
     const float* p = part + ((int64_t)t * M + m) * stride;
     for (int i = 0; i < k; ++i) {
-      float v = p[2 + i]; int id = __float_as_int(p[2 + k + i]);
+      const float v = p[2 + i];
+      const int id = __float_as_int(p[2 + k + i]);
       if (id == 0x7fffffff) break;
-      // insert if better than the last
       if (v > lv[k - 1] || (v == lv[k - 1] && id < li[k - 1])) {
         int j = k - 1;
         while (j > 0 && (v > lv[j - 1] || (v == lv[j - 1] && id < li[j - 1]))) {
@@ -369,11 +395,12 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
         }
         lv[j] = v; li[j] = id;
       } else {
-        break;  // the tile's list is sorted: nothing later can enter
+        break;   // the tile's list is sorted: nothing later can enter
       }
     }
   }
-  __shared__ float hv[256]; __shared__ int hi[256], ht[256];
+  __shared__ float hv[256];
+  __shared__ int hi[256], ht[256];
   int head = 0;
   for (int r = 0; r < k; ++r) {
     hv[threadIdx.x] = head < k ? lv[head] : -INFINITY;
@@ -382,7 +409,8 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
       if ((int)threadIdx.x < o) {
-        float c = hv[threadIdx.x + o]; int ci = hi[threadIdx.x + o];
+        const float c = hv[threadIdx.x + o];
+        const int ci = hi[threadIdx.x + o];
         if (c > hv[threadIdx.x] || (c == hv[threadIdx.x] && ci < hi[threadIdx.x])) {
           hv[threadIdx.x] = c; hi[threadIdx.x] = ci; ht[threadIdx.x] = ht[threadIdx.x + o];
         }
@@ -399,86 +427,131 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
   }
 }
 
+// ---------------------------------------------------------------- dispatch
+// Launch shape per m-tile count: waves per workgroup and steps per chunk.
+template <int MT> struct Cfg;
+template <> struct Cfg<1> { static constexpr int NW = 4, CS = 16; };
+template <> struct Cfg<2> { static constexpr int NW = 4, CS = 8; };
+template <> struct Cfg<3> { static constexpr int NW = 8, CS = 4; };
+template <> struct Cfg<4> { static constexpr int NW = 8, CS = 4; };
+template <> struct Cfg<5> { static constexpr int NW = 8, CS = 4; };
+
+template <typename T, int MT, int EPI>
+hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st) {
+  constexpr int NW = Cfg<MT>::NW, CS = Cfg<MT>::CS;
+  hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, EPI>), dim3(tiles * a.splits, m_chunks), dim3(NW * 64), 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int EPI>
-hipError_t gemm_dispatch(const GemmPlan& p, const GemmArgs& a, hipStream_t st) {
-  dim3 grid(p.splits == 1 ? p.n_tiles : ((p.n_tiles + 7) / 8) * 8 * p.splits, p.m_chunks);
-#define GEMM_CASE(MT_)                                                                  \
-  case MT_:                                                                             \
-    hipLaunchKernelGGL((gemm_kernel<T, MT_, 2, EPI>), grid, dim3(NTHREADS), 0, st, a); \
-    break;
-  switch (p.mt) {
-    GEMM_CASE(1) GEMM_CASE(2) GEMM_CASE(3) GEMM_CASE(4) GEMM_CASE(5)
-    default: return hipErrorInvalidValue;
+hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hipStream_t st) {
+  switch (mt) {
+    case 1: return launch_proj_mt<T, 1, EPI>(a, tiles, m_chunks, st);
+    case 2: return launch_proj_mt<T, 2, EPI>(a, tiles, m_chunks, st);
+    case 3: return launch_proj_mt<T, 3, EPI>(a, tiles, m_chunks, st);
+    case 4: return launch_proj_mt<T, 4, EPI>(a, tiles, m_chunks, st);
+    default: return launch_proj_mt<T, 5, EPI>(a, tiles, m_chunks, st);
   }
-#undef GEMM_CASE
+}
+
+int waves_for(int mt) {
+  switch (mt) {
+    case 1: return Cfg<1>::NW;
+    case 2: return Cfg<2>::NW;
+    default: return Cfg<4>::NW;
+  }
+}
+
+template <typename T, bool TOPK, int MT>
+hipError_t launch_head_mt(const HeadArgs& h, int tiles, hipStream_t st) {
+  constexpr int NW = Cfg<MT>::NW, CS = Cfg<MT>::CS;
+  hipLaunchKernelGGL((lmhead_kernel<T, MT, NW, CS, TOPK>), dim3(tiles), dim3(NW * 64), 0, st, h);
   return hipGetLastError();
 }
 
 template <typename T, bool TOPK>
-hipError_t head_dispatch(int mt, int n_tiles, const HeadArgs& a, hipStream_t st) {
-#define HEAD_CASE(MT_)                                                                           \
-  case MT_:                                                                                      \
-    hipLaunchKernelGGL((lmhead_kernel<T, MT_, 2, TOPK>), dim3(n_tiles), dim3(NTHREADS), 0, st, a); \
-    break;
+hipError_t launch_head_t(int mt, const HeadArgs& h, int tiles, hipStream_t st) {
   switch (mt) {
-    HEAD_CASE(1) HEAD_CASE(2) HEAD_CASE(3) HEAD_CASE(4) HEAD_CASE(5)
-    default: return hipErrorInvalidValue;
+    case 1: return launch_head_mt<T, TOPK, 1>(h, tiles, st);
+    case 2: return launch_head_mt<T, TOPK, 2>(h, tiles, st);
+    case 3: return launch_head_mt<T, TOPK, 3>(h, tiles, st);
+    case 4: return launch_head_mt<T, TOPK, 4>(h, tiles, st);
+    default: return launch_head_mt<T, TOPK, 5>(h, tiles, st);
   }
-#undef HEAD_CASE
-  return hipGetLastError();
 }
+
+int head_rows(int M) { return 16 * waves_for(M > 64 ? 5 : (M + 15) / 16); }
 
 }  // namespace
 
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
   GemmPlan p;
-  p.nb = 2;
   if (M <= 80) { p.mt = (M + 15) / 16; p.m_chunks = 1; }
   else { p.mt = 4; p.m_chunks = (M + 63) / 64; }
-  const int R = 16 * p.nb;
-  const int outs = (epi == EPI_SWIGLU) ? N_rows / 2 : N_rows;
-  p.n_tiles = (epi == EPI_SWIGLU) ? (outs + R / 2 - 1) / (R / 2) : (outs + R - 1) / R;
-  const int steps = K / (dtype == 1 ? 32 : 16);
-  int s = 1;
-  while (p.n_tiles * s < 256 && s < 8 && steps / (2 * s) >= NWAVES) s *= 2;
-  p.splits = s;
+  const int nw = waves_for(p.mt);
+  const int rows_per_tile = 16 * nw;
+  p.nb = 1;
+  if (epi == EPI_SWIGLU) {
+    const int F = N_rows / 2;
+    p.n_tiles = (F + rows_per_tile / 2 - 1) / (rows_per_tile / 2);
+    p.splits = 1;
+  } else {
+    p.n_tiles = (N_rows + rows_per_tile - 1) / rows_per_tile;
+    const int steps = K / (dtype == 1 ? 32 : 16);
+    const int cs = p.mt == 1 ? Cfg<1>::CS : (p.mt == 2 ? Cfg<2>::CS : Cfg<4>::CS);
+    int s = 1;
+    while (p.n_tiles * s < 384 && s < 16 && steps / (2 * s) >= 2 * cs) s *= 2;
+    p.splits = s;
+  }
   return p;
 }
 
 uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M) {
-  return p.splits > 1 ? (uint64_t)p.splits * M * N_rows : 0;
+  return (uint64_t)p.splits * M * N_rows;
 }
 
 hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
-                       int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, float* part,
-                       int* counters, hipStream_t stream) {
+                       int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int splits_out[1],
+                       hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int rows = (epi == EPI_SWIGLU) ? 2 * N : N;
   GemmPlan p = gemm_plan(M, rows, K, dtype, epi);
-  GemmArgs a;
-  a.W = W; a.ldw = K; a.X = x; a.ldx = K; a.xlo = xlo; a.M = M; a.N = N; a.K = K;
-  a.n_tiles = p.n_tiles; a.splits = p.splits;
+  ProjArgs a;
+  a.W = W; a.X = x; a.xlo = xlo; a.M = M; a.rows = rows; a.K = K; a.F = N;
+  a.splits = p.splits;
   const int steps = K / (dtype == 1 ? 32 : 16);
   a.steps_per_split = (steps + p.splits - 1) / p.splits;
-  a.Y = Y; a.ldy = ldy; a.Yt = Yt; a.ytlo = ytlo; a.part = part; a.counters = counters;
+  a.Y = Y; a.ldy = ldy; a.plane = (int64_t)M * ldy;
+  a.Yt = Yt; a.ytlo = ytlo;
+  if (splits_out) splits_out[0] = p.splits;
   if (dtype == 1) {
-    switch (epi) {
-      case EPI_STORE: return gemm_dispatch<bf16_t, EPI_STORE>(p, a, stream);
-      case EPI_ADD: return gemm_dispatch<bf16_t, EPI_ADD>(p, a, stream);
-      default: return gemm_dispatch<bf16_t, EPI_SWIGLU>(p, a, stream);
-    }
+    return epi == EPI_SWIGLU ? launch_proj_t<bf16_t, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream)
+                             : launch_proj_t<bf16_t, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream);
   }
-  switch (epi) {
-    case EPI_STORE: return gemm_dispatch<float, EPI_STORE>(p, a, stream);
-    case EPI_ADD: return gemm_dispatch<float, EPI_ADD>(p, a, stream);
-    default: return gemm_dispatch<float, EPI_SWIGLU>(p, a, stream);
-  }
+  return epi == EPI_SWIGLU ? launch_proj_t<float, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream)
+                           : launch_proj_t<float, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream);
 }
 
 uint64_t lmhead_part_floats(int M, int V, int k) {
-  const int n_tiles = (V + 31) / 32;
   if (M > 80) M = 64;
+  const int n_tiles = (V + head_rows(M) - 1) / head_rows(M);
   return (uint64_t)n_tiles * M * (k > 0 ? (2 + 2 * k) : 3);
+}
+
+static hipError_t head_launch(int dtype, bool topk, const void* W, const void* x, int64_t xlo, int M, int V,
+                              int H, int k, float* part, float* logits, int* n_tiles_out,
+                              hipStream_t stream) {
+  HeadArgs h;
+  h.p.W = W; h.p.X = x; h.p.xlo = xlo; h.p.M = M; h.p.rows = V; h.p.K = H; h.p.F = 0;
+  h.p.splits = 1; h.p.steps_per_split = H / (dtype == 1 ? 32 : 16);
+  h.p.Y = nullptr; h.p.ldy = 0; h.p.plane = 0; h.p.Yt = nullptr; h.p.ytlo = 0;
+  h.k = k; h.part = part; h.logits = logits;
+  const int mt = (M + 15) / 16;
+  const int tiles = (V + head_rows(M) - 1) / head_rows(M);
+  *n_tiles_out = tiles;
+  if (dtype == 1)
+    return topk ? launch_head_t<bf16_t, true>(mt, h, tiles, stream) : launch_head_t<bf16_t, false>(mt, h, tiles, stream);
+  return topk ? launch_head_t<float, true>(mt, h, tiles, stream) : launch_head_t<float, false>(mt, h, tiles, stream);
 }
 
 hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int64_t xlo, int M, int V,
@@ -496,13 +569,10 @@ hipError_t launch_lmhead_argmax(int dtype, const void* W, const void* x, int64_t
     }
     return hipSuccess;
   }
-  HeadArgs a{W, x, xlo, M, V, H, 0, part, logits};
-  const int n_tiles = (V + 31) / 32;
-  const int mt = (M + 15) / 16;
-  hipError_t e = dtype == 1 ? head_dispatch<bf16_t, false>(mt, n_tiles, a, stream)
-                            : head_dispatch<float, false>(mt, n_tiles, a, stream);
+  int tiles = 0;
+  hipError_t e = head_launch(dtype, false, W, x, xlo, M, V, H, 0, part, logits, &tiles, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(argmax_combine, dim3(M), dim3(256), 0, stream, part, n_tiles, M, g, margin);
+  hipLaunchKernelGGL(argmax_combine, dim3(M), dim3(256), 0, stream, part, tiles, M, g, margin);
   return hipGetLastError();
 }
 
@@ -522,12 +592,9 @@ hipError_t launch_lmhead_topk(int dtype, const void* W, const void* x, int64_t x
     }
     return hipSuccess;
   }
-  HeadArgs a{W, x, xlo, M, V, H, k, part, nullptr};
-  const int n_tiles = (V + 31) / 32;
-  const int mt = (M + 15) / 16;
-  hipError_t e = dtype == 1 ? head_dispatch<bf16_t, true>(mt, n_tiles, a, stream)
-                            : head_dispatch<float, true>(mt, n_tiles, a, stream);
+  int tiles = 0;
+  hipError_t e = head_launch(dtype, true, W, x, xlo, M, V, H, k, part, nullptr, &tiles, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_combine, dim3(M), dim3(256), 0, stream, part, n_tiles, M, k, ids, logp);
+  hipLaunchKernelGGL(topk_combine, dim3(M), dim3(256), 0, stream, part, tiles, M, k, ids, logp);
   return hipGetLastError();
 }

@@ -3,24 +3,24 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-enum { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2 };
+enum { EPI_PART = 0, EPI_SWIGLU = 2 };
+
+#define EAGLE_QKV_MAX 12288   // widest q|k|v row handled by the RoPE kernel (fp32 in LDS)
 
 // ---------------------------------------------------------------- GEMM
 // y = x W^T for a skinny x (M rows) and a weight W [N, K] streamed from HBM.
-//   EPI_STORE : Y[m, n]  = acc            (fp32, row stride ldy)
-//   EPI_ADD   : Y[m, n] += acc            (fp32 residual update)
-//   EPI_SWIGLU: W = [gate (N rows); up (N rows)], Yt[m, n] = T(silu(g) * u)
-// dtype 0 = fp32, 1 = bf16 for W. Activations x and Yt are operands (see
-// Opnd in common.h): for bf16 two planes, the lo plane xlo / ytlo elements
-// after the hi plane. `part`/`counters` is the split-K
-// workspace (gemm_workspace_bytes); counters must start at zero and are left
-// at zero.
+//   EPI_PART  : fp32 partial planes Y[split][M][ldy] (split over K; the
+//               consumer sums *splits_out planes in order; plane = M * ldy)
+//   EPI_SWIGLU: W = [gate (N rows); up (N rows)], Yt[m, n] = silu(g) * u
+//               written as an operand (two bf16 planes, lo at Yt + ytlo)
+// dtype 0 = fp32, 1 = bf16 for W. x is an operand (see Opnd in common.h):
+// for bf16 two planes, the lo plane xlo elements after the hi plane.
 struct GemmPlan { int mt, nb, splits, m_chunks, n_tiles; };
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi);
 uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M);
 hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
-                       int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, float* part,
-                       int* counters, hipStream_t stream);
+                       int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int* splits_out,
+                       hipStream_t stream);
 
 // ---------------------------------------------------------------- LM head
 // Verify: g[m] = argmax_v (x W^T)[m, v] (lowest id on ties), margin[m] =
@@ -63,13 +63,20 @@ hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int
                         hipStream_t st);
 // Operand outputs (out_t, q_out, x, dst of store_feat / gather_t) take
 // their lo-plane offset `lo` in elements (ignored for fp32).
-hipError_t launch_rmsnorm(int dtype, const float* h, int64_t ldh, const float* gain, int K, float eps,
-                          int M, void* out_t, int64_t ldo, int64_t lo, float* out_f, int64_t ldf,
-                          hipStream_t st);
-hipError_t launch_cast(int dtype, const float* h, int H, int M, void* out_t, int64_t lo,
-                       hipStream_t st);
-hipError_t launch_rope_kv(int dtype, const float* qkv, int M, int nq, int nkv, int d,
-                          const int32_t* pos, const int32_t* slot, const float* cos_t,
+//
+// Residual update + RMSNorm of M rows of width H:
+//   h[r] = (set ? 0 : h[r]) + sum_{s < S} part[s][r]   (fixed order; S may be 0)
+//   out = gain ? RMSNorm(h[r]) * gain : h[r]   -> operand out_t (and fp32 out_f)
+hipError_t launch_resnorm(int dtype, float* h, int H, int M, const float* part, int S,
+                          int64_t plane, int set, const float* gain, float eps, void* out_t,
+                          int64_t lo, float* out_f, hipStream_t st);
+// dst[r] = (add ? dst[r] : 0) + sum_s part[s][r] for M rows of width W.
+hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int W, float* dst,
+                             int add, hipStream_t st);
+// RoPE on q and k and append of k, v to the cache; qkv = sum of S partial
+// planes [M, (nq + 2 nkv) d].
+hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int M, int nq, int nkv,
+                          int d, const int32_t* pos, const int32_t* slot, const float* cos_t,
                           const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st);
 uint64_t attn_part_floats(int max_chunks, int M, int nq, int d);
 int attn_chunk_keys();

@@ -8,7 +8,6 @@
 #include "kernels.h"
 
 namespace {
-constexpr uint64_t kCounterBytes = 65536 * 4;
 
 uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
 
@@ -24,10 +23,9 @@ extern "C" {
 
 uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K) {
   if (!linear_ok(dtype, epi, M, N, K)) return 0;
-  const int rows = epi == EAGLE_EPI_SWIGLU ? 2 * N : N;
-  GemmPlan p = gemm_plan(M, rows, K, dtype, epi);
-  if (p.splits == 1) return 0;
-  return kCounterBytes + align256((uint64_t)p.splits * M * rows * 4);
+  if (epi == EAGLE_EPI_SWIGLU) return 0;
+  GemmPlan p = gemm_plan(M, N, K, dtype, EPI_PART);
+  return align256(gemm_part_floats(p, N, M) * 4);
 }
 
 eagle_status eagle_op_linear(int32_t dtype, int32_t epi, const void* x, const void* w, void* y,
@@ -36,16 +34,18 @@ eagle_status eagle_op_linear(int32_t dtype, int32_t epi, const void* x, const vo
   if (!linear_ok(dtype, epi, M, N, K) || !x || !w || !y) return EAGLE_E_INVALID;
   const uint64_t need = eagle_op_linear_workspace(dtype, epi, M, N, K);
   if (need > 0 && (!workspace || ws_bytes < need)) return EAGLE_E_BUFFER;
-  int* counters = need ? (int*)workspace : nullptr;
-  float* part = need ? (float*)((char*)workspace + kCounterBytes) : nullptr;
-  hipError_t e;
   const int64_t xlo = (int64_t)M * K;   // bf16: lo plane follows the hi plane
-  if (epi == EAGLE_EPI_SWIGLU)
-    e = launch_gemm(dtype, EPI_SWIGLU, w, x, xlo, M, N, K, nullptr, 0, y, (int64_t)M * N, part,
-                    counters, (hipStream_t)stream);
-  else
-    e = launch_gemm(dtype, epi == EAGLE_EPI_ADD ? EPI_ADD : EPI_STORE, w, x, xlo, M, N, K, (float*)y,
-                    N, nullptr, 0, part, counters, (hipStream_t)stream);
+  hipStream_t st = (hipStream_t)stream;
+  if (epi == EAGLE_EPI_SWIGLU) {
+    hipError_t e = launch_gemm(dtype, EPI_SWIGLU, w, x, xlo, M, N, K, nullptr, 0, y, (int64_t)M * N,
+                               nullptr, st);
+    return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
+  }
+  float* part = (float*)workspace;
+  int S = 1;
+  hipError_t e = launch_gemm(dtype, EPI_PART, w, x, xlo, M, N, K, part, N, nullptr, 0, &S, st);
+  if (e == hipSuccess)
+    e = launch_sum_planes(part, S, (int64_t)M * N, M, N, (float*)y, epi == EAGLE_EPI_ADD ? 1 : 0, st);
   return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
 }
 
