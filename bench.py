@@ -5,9 +5,10 @@ the target verify pass, acceptance, KV compaction and the draft catch-up
 (eagle_verify), on seeded synthetic weights and prompts already resident in
 HBM. Prints one JSON line (see README of the driver contract):
   value       committed tokens/s (tau x cycles/s; tau ~ 1 with random weights)
-  roofline    the dominant kernel class (weight-streaming projections):
-              algorithmic bytes / summed device time from HIP events in a
-              profiled window of the same cycles, against 8 TB/s
+  roofline    the dominant kernel: the split-K projection of the target
+              layers (q|k|v, o and down at M = tree rows), its algorithmic
+              bytes / its device time from HIP events recorded around each of
+              its launches inside the timed region, against 8 TB/s
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
 """
 from __future__ import annotations
@@ -22,6 +23,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBPS = 8000.0
+# one in ROOF_EVERY dispatches of the roofline kernel carries HIP events in the
+# timed region; 4 is coprime with the three projections of a layer, so q|k|v,
+# o and down are sampled equally, and the events cost ~1.5% of a cycle
+ROOF_EVERY = 4
 
 WORKLOAD_TEXT = {
     "c1": "tiny fp32 Llama target (2 layers, H=256, V=1024), EAGLE-1 head, dynamic tree k=4 D=3 m=16, prompt 32",
@@ -84,6 +89,10 @@ def cpu_baseline(w: dict, budget_layers: int = 2) -> dict:
     t4 = time.perf_counter()
     per_cycle = (t1 - t0) + (t2 - t1) + (w["n_layers"] - budget_layers) * (t4 - t3)
     cores = len(os.sched_getaffinity(0))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        if os.environ.get(var, "").isdigit():
+            cores = min(cores, int(os.environ[var]))   # BLAS threads actually used
+            break
     return {"value": round(1.0 / per_cycle, 5), "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": (f"one cycle of {w['name']} (tau=1): draft passes {t1 - t0:.2f}s and verify "
@@ -113,7 +122,7 @@ def main():
     import speculative_decoding_draft_amd as E
 
     w = synth.workloads.get(args.config)
-    cycles_needed = args.warmup + args.steps + args.profile_cycles + 2
+    cycles_needed = args.warmup + args.steps + max(0, args.profile_cycles) + 2
     max_new = max(w["gen"], cycles_needed * (w["depth"] + 1))
     max_ctx = w["prompt_len"] + max_new + w["depth"] + 2
     eng = E.Engine(w, max_ctx=max_ctx)
@@ -128,9 +137,13 @@ def main():
         eng.draft_tree(want=False)
         return len(eng.verify())
 
+    # the dominant kernel's launches carry HIP events from warmup on, so the
+    # event pool is allocated before the timed region
+    eng.profile(["gemm"], every=ROOF_EVERY)
     for _ in range(args.warmup):
         cycle()
     torch.cuda.synchronize()
+    eng.profile(["gemm"], every=ROOF_EVERY)   # reset the counters; keep the class enabled
     ctx0 = len(eng.committed()) + len(prompt) - 1
     t0 = time.perf_counter()
     committed = 0
@@ -139,21 +152,26 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     dt = t1 - t0
+    g = eng.profile_read()["gemm"]
+    eng.profile(False)
     ctx1 = len(eng.committed()) + len(prompt) - 1
     print(f"# timed {args.steps} cycles in {dt * 1e3:.1f} ms", file=sys.stderr, flush=True)
 
     # algorithmic bytes of the timed cycles (context grows by L+1 per cycle)
     avg_ctx = 0.5 * (ctx0 + ctx1)
     bytes_cycle = cycle_bytes(w, int(avg_ctx))
-
-    # profiled window: same cycles with HIP events around every launch
-    eng.profile(True)
-    for _ in range(args.profile_cycles):
-        cycle()
-    prof = eng.profile_read()
-    eng.profile(False)
-    g = prof["gemm"]
     gemm_gbps = g["bytes"] / (g["ms"] * 1e-3) / 1e9 if g["ms"] > 0 else 0.0
+    mv = 1 + w["budget"]
+    mt = (mv + 15) // 16 if mv <= 80 else 4
+
+    # breakdown window after the timed region: events around every launch
+    prof = None
+    if args.profile_cycles > 0:
+        eng.profile(True)
+        for _ in range(args.profile_cycles):
+            cycle()
+        prof = eng.profile_read()
+        eng.profile(False)
     cycles_s = args.steps / dt
     tau = committed / args.steps
     out = {
@@ -172,13 +190,16 @@ def main():
         "cycle_hbm": {"bytes_per_cycle": bytes_cycle,
                       "achieved_GBps": round(bytes_cycle * cycles_s / 1e9, 1),
                       "frac": round(bytes_cycle * cycles_s / 1e9 / PEAK_GBPS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "gemm (weight-streaming projections)",
+        "roofline": {"bound": "hbm",
+                     "kernel": (f"proj_kernel<{'bf16' if w['dtype'] == 'bf16' else 'f32'}, MT={mt}, EPI_PART>: "
+                                f"target q|k|v, o and down projections at M={mv}"),
                      "achieved": round(gemm_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gemm_gbps / PEAK_GBPS, 4), "traffic": None,
                      "launches": g["launches"], "avg_launch_us": round(g["ms"] * 1e3 / max(1, g["launches"]), 2),
                      "bytes_per_launch": round(g["bytes"] / max(1, g["launches"]))},
-        "profile_ms_per_cycle": {k: round(v["ms"] / args.profile_cycles, 4) for k, v in prof.items()},
     }
+    if prof is not None:
+        out["profile_ms_per_cycle"] = {k: round(v["ms"] / args.profile_cycles, 4) for k, v in prof.items()}
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))

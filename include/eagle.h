@@ -231,27 +231,35 @@ eagle_status eagle_debug_read(eagle_ctx* ctx, int32_t what, void* host_dst, uint
                               int32_t* rows);
 eagle_status eagle_set_debug(eagle_ctx* ctx, int32_t on);
 
-/* Profiling: while enabled, every kernel launch of the context is bracketed
- * by HIP events on its stream and attributed to a class; eagle_profile_read
- * synchronises and reports, per class, launches, summed device time and the
+/* Profiling: launches of the enabled classes are bracketed by HIP events on
+ * the context's stream; eagle_profile_read synchronises and reports, per
+ * class, the bracketed launches, their summed device time and the
  * algorithmic bytes those launches must move (weights read once, activation
- * operands and outputs). Enabling resets the counters. The events add host
- * work per launch, so timed runs keep profiling off. */
+ * operands and outputs). eagle_profile_enable takes a bit mask of classes
+ * (bit i enables class i; 0 turns profiling off, EAGLE_PROF_ALL enables every
+ * class) and a stride `every` >= 1: only one launch in `every` of each class
+ * is bracketed, which bounds the cost on a timed run (each bracketed launch
+ * adds a few microseconds of stream time). Enabling resets the totals. The
+ * single-dispatch projection classes (GEMM, SWIGLU, DRAFT) carry their events
+ * on the dispatch itself, so their interval is the kernel's own run time. */
 enum {
-  EAGLE_PROF_GEMM = 0,      /* projections (target and draft layers, draft FC) */
+  EAGLE_PROF_GEMM = 0,      /* target layers: q|k|v, o and down projections (split-K planes) */
   EAGLE_PROF_ATTN = 1,      /* tree-masked attention and its chunk combine */
   EAGLE_PROF_LMHEAD = 2,    /* LM head with argmax or softmax/top-k */
   EAGLE_PROF_ROWS = 3,      /* embedding, norms, RoPE + KV append, gathers */
   EAGLE_PROF_TREE = 4,      /* tree expansion/rerank and acceptance */
   EAGLE_PROF_KV = 5,        /* KV compaction */
-  EAGLE_PROF_CLASSES = 6
+  EAGLE_PROF_SWIGLU = 6,    /* target layers: fused gate/up projection and SiLU product */
+  EAGLE_PROF_DRAFT = 7,     /* draft head projections: FC, q|k|v, o, gate/up, down */
+  EAGLE_PROF_CLASSES = 8
 };
+#define EAGLE_PROF_ALL 0xffffffffu
 typedef struct eagle_profile {
   int64_t launches[EAGLE_PROF_CLASSES];
   double ms[EAGLE_PROF_CLASSES];
   double bytes[EAGLE_PROF_CLASSES];
 } eagle_profile;
-eagle_status eagle_profile_enable(eagle_ctx* ctx, int32_t on);
+eagle_status eagle_profile_enable(eagle_ctx* ctx, uint32_t class_mask, int32_t every);
 eagle_status eagle_profile_read(eagle_ctx* ctx, eagle_profile* out);
 
 void eagle_free(eagle_ctx* ctx);

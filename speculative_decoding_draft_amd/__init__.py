@@ -60,11 +60,14 @@ class Tree(ctypes.Structure):
                 ("node_logp", f32 * MAX_NODES)]
 
 
-PROF_CLASSES = ["gemm", "attention", "lmhead", "rows", "tree", "kv"]
+# profile classes, in the order of the EAGLE_PROF_* constants
+PROF_CLASSES = ["gemm", "attention", "lmhead", "rows", "tree", "kv", "swiglu", "draft"]
+PROF_ALL = 0xFFFFFFFF
 
 
 class Profile(ctypes.Structure):
-    _fields_ = [("launches", i64 * 6), ("ms", ctypes.c_double * 6), ("bytes", ctypes.c_double * 6)]
+    _n = len(PROF_CLASSES)
+    _fields_ = [("launches", i64 * _n), ("ms", ctypes.c_double * _n), ("bytes", ctypes.c_double * _n)]
 
 
 class Stats(ctypes.Structure):
@@ -96,7 +99,7 @@ def lib():
         L.eagle_committed.argtypes = [vp, P(i32), i32, P(i32)]
         L.eagle_debug_read.argtypes = [vp, i32, vp, u64, P(i32)]
         L.eagle_set_debug.argtypes = [vp, i32]
-        L.eagle_profile_enable.argtypes = [vp, i32]
+        L.eagle_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
         L.eagle_profile_read.argtypes = [vp, P(Profile)]
         L.eagle_free.argtypes = [vp]
         L.eagle_free.restype = None
@@ -261,8 +264,20 @@ class Engine:
                     "eagle_committed")
         return out[:n.value].tolist()
 
-    def profile(self, on: bool = True):
-        self._check(lib().eagle_profile_enable(self.ctx, 1 if on else 0), "eagle_profile_enable")
+    def profile(self, on=True, every: int = 1):
+        """Enable profiling: True for every class, False to stop, or an iterable of
+        class names (PROF_CLASSES) to bracket only those launches; one launch in
+        `every` of each class is bracketed."""
+        if on is True:
+            mask = PROF_ALL
+        elif not on:
+            mask = 0
+        else:
+            mask = 0
+            for name in on:
+                mask |= 1 << PROF_CLASSES.index(name)
+        self._check(lib().eagle_profile_enable(self.ctx, ctypes.c_uint32(mask), int(every)),
+                    "eagle_profile_enable")
 
     def profile_read(self) -> dict:
         p = Profile()

@@ -255,89 +255,146 @@ __device__ __forceinline__ float block_sum_256(float v, float* sh) {
   return s;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void resnorm_kernel(float* h, int H, const float* part, int S,
-                                                      int64_t plane, int set, const float* gain,
-                                                      float eps, T* out_t, int64_t lo, float* out_f) {
-  __shared__ float sh[256];
+// One workgroup of 1024 threads per row; thread t owns float4 groups t + 1024 u.
+// h <- (set ? 0 : h) + sum of the S partial planes; then either the RMS-normalised
+// row times gain (to out_t, and to out_f if given) or h itself is written as an operand.
+template <typename T, int NV>
+__global__ __launch_bounds__(1024) void resnorm_kernel(float* h, int H, const float* part, int S,
+                                                       int64_t plane, int set, const float* gain,
+                                                       float eps, T* out_t, int64_t lo, float* out_f) {
+  __shared__ float sh[16];
   const int r = blockIdx.x;
+  const int n4 = H / 4;
   float* x = h + (int64_t)r * H;
-  const float* pr = part + (int64_t)r * H;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += 256) {
-    float v = set ? 0.f : x[i];
-    if (S > 0) {
-      float acc = pr[i];
-      for (int s = 1; s < S; ++s) acc += pr[(int64_t)s * plane + i];
-      v += acc;
-    }
-    if (S > 0 || set) x[i] = v;
-    ss += v * v;
+  const float* p[NV];
+  bool ok[NV];
+  float4 v[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int j = threadIdx.x + 1024 * u;
+    ok[u] = j < n4;
+    p[u] = part + (int64_t)r * H + 4 * j;
   }
-  if (gain) {
-    ss = block_sum_256(ss, sh);
-    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
-    for (int i = threadIdx.x; i < H; i += 256) {
-      const float v = x[i] * inv * gain[i];
-      if (out_f) out_f[(int64_t)r * H + i] = v;
-      Opnd<T>::store(out_t, lo, (int64_t)r * H + i, v);
+  if (S > 0) {
+    float4 acc[NV];
+    plane_sums<NV>(p, ok, S, plane, acc);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      v[u] = (set || !ok[u]) ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(x + 4 * (threadIdx.x + 1024 * u));
+      add4(v[u], acc[u]);
     }
   } else {
-    __syncthreads();
-    for (int i = threadIdx.x; i < H; i += 256) Opnd<T>::store(out_t, lo, (int64_t)r * H + i, x[i]);
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      v[u] = (set || !ok[u]) ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(x + 4 * (threadIdx.x + 1024 * u));
+  }
+  const int64_t rb = (int64_t)r * H;
+  if (S > 0 || set) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      if (ok[u]) *reinterpret_cast<float4*>(x + 4 * (threadIdx.x + 1024 * u)) = v[u];
+  }
+  if (!gain) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      if (ok[u]) opnd_store4(out_t, lo, rb + 4 * (threadIdx.x + 1024 * u), v[u]);
+    return;
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) tot += sh[w];   // fixed order: identical in every thread
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    if (!ok[u]) continue;
+    const int i = 4 * (threadIdx.x + 1024 * u);
+    const float4 g = ld4(gain + i);
+    const float4 y = make_float4(v[u].x * inv * g.x, v[u].y * inv * g.y, v[u].z * inv * g.z, v[u].w * inv * g.w);
+    if (out_f) *reinterpret_cast<float4*>(out_f + rb + i) = y;
+    opnd_store4(out_t, lo, rb + i, y);
   }
 }
 
-__global__ void sum_planes_kernel(const float* part, int S, int64_t plane, int W, float* dst, int add) {
+// dst[r, :W] (+)= sum of the S partial planes; grid (rows, W / 1024 rounded up), 256 threads
+// each owning 4 consecutive columns.
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float* part, int S, int64_t plane, int W,
+                                                         float* dst, int add) {
   const int r = blockIdx.x;
-  for (int i = threadIdx.x; i < W; i += blockDim.x) {
-    float acc = part[(int64_t)r * W + i];
-    for (int s = 1; s < S; ++s) acc += part[(int64_t)s * plane + (int64_t)r * W + i];
-    dst[(int64_t)r * W + i] = add ? dst[(int64_t)r * W + i] + acc : acc;
+  const int c = 4 * (blockIdx.y * 256 + threadIdx.x);
+  if (c >= W) return;
+  const int64_t o = (int64_t)r * W + c;
+  if ((W & 3) == 0) {
+    const float* p[1] = {part + o};
+    const bool ok[1] = {true};
+    float4 acc[1];
+    plane_sums<1>(p, ok, S, plane, acc);
+    if (add) add4(acc[0], ld4(dst + o));
+    *reinterpret_cast<float4*>(dst + o) = acc[0];
+  } else {
+    for (int e = 0; e < 4 && c + e < W; ++e) {
+      float acc = part[o + e];
+      for (int s = 1; s < S; ++s) acc += part[(int64_t)s * plane + o + e];
+      dst[o + e] = add ? dst[o + e] + acc : acc;
+    }
   }
 }
 
+// Sums the split-K planes of the fused q|k|v projection, applies the rotary
+// embedding (rotate-half pairing) to q and k, writes q as an operand and k, v
+// into the cache slot of each row. Grid (rows, head groups): a workgroup of 256
+// threads covers 1024 / d consecutive heads of the q|k|v row.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, int64_t plane, int nq,
                                                       int nkv, int d, const int32_t* pos,
                                                       const int32_t* slot,
                                                       const float* cos_t, const float* sin_t,
                                                       T* q_out, int64_t qlo, KVView kv) {
+  __shared__ float xs[1024];
   const int r = blockIdx.x;
   const int half = d / 2;
-  const int width = (nq + 2 * nkv) * d;
-  // sum the split-K partial planes of this row into LDS first
-  __shared__ float xsum[EAGLE_QKV_MAX];
-  for (int i = threadIdx.x; i < width; i += blockDim.x) {
-    const float* p = qkv + (int64_t)r * width + i;
-    float acc = p[0];
-    for (int s = 1; s < S; ++s) acc += p[(int64_t)s * plane];
-    xsum[i] = acc;
+  const int hpw = 1024 / d;
+  const int n_heads = nq + 2 * nkv;
+  const int h0 = blockIdx.y * hpw;
+  const int nh = min(hpw, n_heads - h0);
+  const int width = n_heads * d;
+  {
+    const int e = 4 * threadIdx.x;
+    const bool ok[1] = {e < nh * d};
+    const float* p[1] = {qkv + (int64_t)r * width + h0 * d + e};
+    float4 acc[1];
+    plane_sums<1>(p, ok, S, plane, acc);
+    if (ok[0]) *reinterpret_cast<float4*>(xs + e) = acc[0];
   }
   __syncthreads();
-  const float* x = xsum;
   const float* c = cos_t + (int64_t)pos[r] * half;
   const float* s = sin_t + (int64_t)pos[r] * half;
   const int sl = slot[r];
-  for (int idx = threadIdx.x; idx < (nq + nkv) * half; idx += blockDim.x) {
-    const int head = idx / half, i = idx % half;
-    const float* src = x + head * d;
-    const float x1 = src[i], x2 = src[i + half];
-    const float y1 = x1 * c[i] - x2 * s[i];
-    const float y2 = x2 * c[i] + x1 * s[i];
-    if (head < nq) {
-      const int64_t base = ((int64_t)r * nq + head) * d;
-      Opnd<T>::store(q_out, qlo, base + i, y1);
-      Opnd<T>::store(q_out, qlo, base + i + half, y2);
+  for (int idx = threadIdx.x; idx < nh * half; idx += 256) {
+    const int lh = idx / half, i = idx % half;
+    const int head = h0 + lh;
+    const float* src = xs + lh * d;
+    if (head < nq + nkv) {
+      const float x1 = src[i], x2 = src[i + half];
+      const float y1 = x1 * c[i] - x2 * s[i];
+      const float y2 = x2 * c[i] + x1 * s[i];
+      if (head < nq) {
+        const int64_t base = ((int64_t)r * nq + head) * d;
+        Opnd<T>::store(q_out, qlo, base + i, y1);
+        Opnd<T>::store(q_out, qlo, base + i + half, y2);
+      } else {
+        KVStore<T>::put(kv, sl, 0, head - nq, i, y1);
+        KVStore<T>::put(kv, sl, 0, head - nq, i + half, y2);
+      }
     } else {
-      KVStore<T>::put(kv, sl, 0, head - nq, i, y1);
-      KVStore<T>::put(kv, sl, 0, head - nq, i + half, y2);
+      KVStore<T>::put(kv, sl, 1, head - nq - nkv, i, src[i]);
+      KVStore<T>::put(kv, sl, 1, head - nq - nkv, i + half, src[i + half]);
     }
-  }
-  const float* vsrc = x + (nq + nkv) * d;
-  for (int idx = threadIdx.x; idx < nkv * d; idx += blockDim.x) {
-    const int head = idx / d, i = idx % d;
-    KVStore<T>::put(kv, sl, 1, head, i, vsrc[idx]);
   }
 }
 
@@ -460,16 +517,29 @@ hipError_t launch_resnorm(int dtype, float* h, int H, int M, const float* part, 
                           int64_t plane, int set, const float* gain, float eps, void* out_t,
                           int64_t lo, float* out_f, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(resnorm_kernel<bf16_t>, dim3(M), dim3(256), 0, st, h, H, part, S, plane, set, gain, eps, (bf16_t*)out_t, lo, out_f),
-              hipLaunchKernelGGL(resnorm_kernel<float>, dim3(M), dim3(256), 0, st, h, H, part, S, plane, set, gain, eps, (float*)out_t, lo, out_f));
+  if (H % 4 != 0 || H > 4 * 4096) return hipErrorInvalidValue;
+  const int nv = (H / 4 + 1023) / 1024;
+#define RN(NV)                                                                                   \
+  DT_DISPATCH(dtype,                                                                             \
+              hipLaunchKernelGGL((resnorm_kernel<bf16_t, NV>), dim3(M), dim3(1024), 0, st, h, H, \
+                                 part, S, plane, set, gain, eps, (bf16_t*)out_t, lo, out_f),     \
+              hipLaunchKernelGGL((resnorm_kernel<float, NV>), dim3(M), dim3(1024), 0, st, h, H,  \
+                                 part, S, plane, set, gain, eps, (float*)out_t, lo, out_f))
+  switch (nv) {
+    case 1: RN(1); break;
+    case 2: RN(2); break;
+    case 3: RN(3); break;
+    default: RN(4); break;
+  }
+#undef RN
   return hipGetLastError();
 }
 
 hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int W, float* dst,
                              int add, hipStream_t st) {
-  if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sum_planes_kernel, dim3(M), dim3(256), 0, st, part, S, plane, W, dst, add);
+  if (M <= 0 || W <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sum_planes_kernel, dim3(M, (W + 1023) / 1024), dim3(256), 0, st, part, S, plane,
+                     W, dst, add);
   return hipGetLastError();
 }
 
@@ -477,10 +547,12 @@ hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int
                           int d, const int32_t* pos, const int32_t* slot, const float* cos_t,
                           const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  if ((nq + 2 * nkv) * d > EAGLE_QKV_MAX) return hipErrorInvalidValue;
+  if (d < 4 || d > 1024 || 1024 % d != 0 || ((nq + 2 * nkv) * d) % 4 != 0) return hipErrorInvalidValue;
+  const int hpw = 1024 / d;
+  const dim3 grid(M, (nq + 2 * nkv + hpw - 1) / hpw);
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, dim3(M), dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv),
-              hipLaunchKernelGGL(rope_kv_kernel<float>, dim3(M), dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv));
+              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv),
+              hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv));
   return hipGetLastError();
 }
 

@@ -55,6 +55,54 @@ template <> struct Opnd<bf16_t> {
   }
 };
 
+// Four consecutive operand values from element i (i a multiple of 4).
+__device__ __forceinline__ void opnd_store4(float* p, int64_t, int64_t i, float4 v) {
+  *reinterpret_cast<float4*>(p + i) = v;
+}
+__device__ __forceinline__ void opnd_store4(bf16_t* p, int64_t lo, int64_t i, float4 v) {
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t hw[2], lw[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const bf16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
+    const bf16_t l0 = f32_to_bf16(f[2 * e] - bf16_to_f32(h0));
+    const bf16_t l1 = f32_to_bf16(f[2 * e + 1] - bf16_to_f32(h1));
+    hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  *reinterpret_cast<uint2*>(p + i) = make_uint2(hw[0], hw[1]);
+  *reinterpret_cast<uint2*>(p + lo + i) = make_uint2(lw[0], lw[1]);
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void add4(float4& a, const float4& b) {
+  a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+}
+
+// Sums of split-K partial planes: acc[u] = sum over s ascending of p[u][s * plane],
+// with NV * B independent 16-byte loads in flight per thread.
+template <int NV>
+__device__ __forceinline__ void plane_sums(const float* const (&p)[NV], const bool (&ok)[NV], int S,
+                                           int64_t plane, float4 (&acc)[NV]) {
+  constexpr int B = NV >= 8 ? 1 : 8 / NV;
+#pragma unroll
+  for (int u = 0; u < NV; ++u) acc[u] = ok[u] ? ld4(p[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 1; s0 < S; s0 += B) {
+    float4 t[B][NV];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        t[b][u] = (ok[u] && s0 + b < S) ? ld4(p[u] + (int64_t)(s0 + b) * plane)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        if (s0 + b < S) add4(acc[u], t[b][u]);
+  }
+}
+
 // ---------------------------------------------------------------- MFMA
 // One "step" is 16 bytes per lane along K: 8 bf16 or 4 fp32 elements.
 // 16x16 tiles: lane l owns row (l & 15) of the A operand and column (l & 15)

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <deque>
 #include <string>
 #include <vector>
 
@@ -57,15 +58,15 @@ bool derive(const eagle_config* c, Derived* z, std::string* why) {
   if (c->dtype != EAGLE_F32 && c->dtype != EAGLE_BF16) return fail(why, "dtype must be EAGLE_F32 or EAGLE_BF16");
   if (c->head != EAGLE_HEAD_E1 && c->head != EAGLE_HEAD_E3) return fail(why, "head must be E1 or E3");
   if (c->n_layers < 1) return fail(why, "n_layers must be >= 1");
-  if (c->hidden < 64 || c->hidden % 64) return fail(why, "hidden must be a positive multiple of 64");
+  if (c->hidden < 64 || c->hidden % 64 || c->hidden > 16384)
+    return fail(why, "hidden must be a multiple of 64 in [64, 16384]");
   if (c->n_heads < 1 || c->hidden % c->n_heads) return fail(why, "n_heads must divide hidden");
   if (c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads) return fail(why, "n_kv_heads must divide n_heads");
   const int d = c->hidden / c->n_heads;
   if (d % 2) return fail(why, "head_dim must be even");
   if (c->dtype == EAGLE_BF16 && d != 128) return fail(why, "bf16 path needs head_dim 128");
   if (c->dtype == EAGLE_F32 && d > 256) return fail(why, "fp32 path needs head_dim <= 256");
-  if ((c->n_heads + 2 * c->n_kv_heads) * d > EAGLE_QKV_MAX)
-    return fail(why, "q|k|v width exceeds %d", EAGLE_QKV_MAX);
+  if (1024 % d) return fail(why, "head_dim must divide 1024");
   const int kq = c->dtype == EAGLE_BF16 ? 32 : 16;
   if (c->ffn < kq || c->ffn % kq) return fail(why, "ffn must be a positive multiple of %d", kq);
   if (c->vocab < 2) return fail(why, "vocab must be >= 2");
@@ -271,11 +272,14 @@ struct eagle_ctx {
   int last_target_rows = 0, last_verify_rows = 0;
   std::string err;
   // profiling (eagle_profile_enable)
-  bool prof = false;
+  uint32_t prof = 0;   // class mask
+  int prof_every = 1;  // bracket one launch in prof_every of each class
+  int64_t prof_seen[EAGLE_PROF_CLASSES] = {};
   struct ProfRec { int cls; double bytes; hipEvent_t a, b; };
-  std::vector<ProfRec> recs;
-  std::vector<hipEvent_t> pool;
-  size_t pool_used = 0;
+  std::deque<ProfRec> recs;            // recorded, not yet read back (oldest first)
+  std::vector<hipEvent_t> free_ev;     // events ready for reuse
+  std::vector<hipEvent_t> all_ev;      // every event created; destroyed with the context
+  eagle_profile ptot{};                // totals of the records already read back
 };
 
 namespace {
@@ -402,13 +406,48 @@ eagle_status set_err(eagle_ctx* c, eagle_status s, const char* fmt, ...) {
     if (s_ != EAGLE_OK) return s_;       \
   } while (0)
 
+// Moves finished records into the totals and their events back to the free
+// list; with wait, first waits for every recorded event.
+void prof_settle(eagle_ctx* c, bool wait) {
+  while (!c->recs.empty()) {
+    const eagle_ctx::ProfRec r = c->recs.front();
+    if (wait) {
+      if (hipEventSynchronize(r.b) != hipSuccess) break;
+    } else if (hipEventQuery(r.b) != hipSuccess) {
+      break;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      c->ptot.launches[r.cls]++;
+      c->ptot.ms[r.cls] += ms;
+      c->ptot.bytes[r.cls] += r.bytes;
+    }
+    c->free_ev.push_back(r.a);
+    c->free_ev.push_back(r.b);
+    c->recs.pop_front();
+  }
+}
+
+// An event for a profile record: reused once its record has been read back,
+// so the number of events stays near the number of launches in flight.
 hipEvent_t take_event(eagle_ctx* c) {
-  if (c->pool_used == c->pool.size()) {
+  if (c->free_ev.empty()) prof_settle(c, false);
+  if (c->free_ev.empty()) {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
-    c->pool.push_back(e);
+    c->all_ev.push_back(e);
+    return e;
   }
-  return c->pool[c->pool_used++];
+  hipEvent_t e = c->free_ev.back();
+  c->free_ev.pop_back();
+  return e;
+}
+
+// Whether this launch of class cls is bracketed (class enabled, and the
+// launch falls on the sampling stride).
+bool prof_pick(eagle_ctx* c, int cls) {
+  if (!((c->prof >> cls) & 1u)) return false;
+  return c->prof_seen[cls]++ % c->prof_every == 0;
 }
 
 // Brackets the launches of its scope with events when profiling is on.
@@ -418,10 +457,10 @@ struct Prof {
   double bytes;
   hipEvent_t a = nullptr;
   Prof(eagle_ctx* c_, int cls_, double bytes_) : c(c_), cls(cls_), bytes(bytes_) {
-    if (c->prof && (a = take_event(c))) (void)hipEventRecord(a, c->st);
+    if (prof_pick(c, cls) && (a = take_event(c))) (void)hipEventRecord(a, c->st);
   }
   ~Prof() {
-    if (!c->prof || !a) return;
+    if (!a) return;
     hipEvent_t b = take_event(c);
     if (!b) return;
     (void)hipEventRecord(b, c->st);
@@ -433,6 +472,25 @@ struct Prof {
   do {                                    \
     Prof p_(c, (cls), (double)(bytes));   \
     HCHK(expr);                           \
+  } while (0)
+
+// Events for a class that is one kernel dispatch: they are handed to the
+// launch (tm_), which attaches them to the dispatch packet, so no extra
+// packets enter the stream and the interval is the kernel's own.
+const KTiming* prof_kernel(eagle_ctx* c, int cls, double bytes, KTiming* t) {
+  if (!prof_pick(c, cls)) return nullptr;
+  t->start = take_event(c);
+  t->stop = take_event(c);
+  if (!t->start || !t->stop) return nullptr;
+  c->recs.push_back({cls, bytes, t->start, t->stop});
+  return t;
+}
+
+#define PROFILED_KERNEL(cls, bytes, expr)                                   \
+  do {                                                                      \
+    KTiming t_;                                                             \
+    const KTiming* tm_ = prof_kernel(c, (cls), (double)(bytes), &t_);       \
+    HCHK(expr);                                                             \
   } while (0)
 
 // Algorithmic bytes: each weight byte once, activation operands (two bf16
@@ -467,13 +525,15 @@ eagle_status resnorm(eagle_ctx* c, float* h, int M, int S, bool set, const float
 // (*s_down planes) for the caller's resnorm.
 eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, float* h,
                         const int32_t* pos, const int32_t* slot, KVView kv, RowVis vis,
-                        int* s_down) {
+                        bool target, int* s_down) {
   const Derived& z = c->z;
   const int dt = z.dt;
+  const int cls_part = target ? EAGLE_PROF_GEMM : EAGLE_PROF_DRAFT;
+  const int cls_glu = target ? EAGLE_PROF_SWIGLU : EAGLE_PROF_DRAFT;
   int S = 1;
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.qkv_rows, kin, z.qkv_rows, EPI_PART),
+  PROFILED_KERNEL(cls_part, gemm_bytes(z, M, z.qkv_rows, kin, z.qkv_rows, EPI_PART),
            launch_gemm(dt, EPI_PART, w.wqkv, c->xop, c->xlo, M, z.qkv_rows, kin, c->gpart,
-                       z.qkv_rows, nullptr, 0, &S, c->st));
+                       z.qkv_rows, nullptr, 0, &S, c->st, tm_));
   PROFILED(EAGLE_PROF_ROWS, (double)M * z.qkv_rows * 4.0 * (S + 1),
            launch_rope_kv(dt, c->gpart, S, (int64_t)M * z.qkv_rows, M, z.nq, z.nkv, z.d, pos, slot,
                           c->cos_t, c->sin_t, c->qop, c->qlo, kv, c->st));
@@ -481,16 +541,16 @@ eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, fl
            launch_attention(dt, c->qop, c->qlo, kv, vis, M, z.nq, z.d,
                             1.0f / std::sqrt((float)z.d), c->opart, c->mlpart, c->aop, c->alo,
                             c->st));
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.nq * z.d, z.H, EPI_PART),
+  PROFILED_KERNEL(cls_part, gemm_bytes(z, M, z.H, z.nq * z.d, z.H, EPI_PART),
            launch_gemm(dt, EPI_PART, w.wo, c->aop, c->alo, M, z.H, z.nq * z.d, c->gpart, z.H,
-                       nullptr, 0, &S, c->st));
+                       nullptr, 0, &S, c->st, tm_));
   SCHK(resnorm(c, h, M, S, false, w.ffn_norm, nullptr));
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, 2 * z.F, z.H, z.F, EPI_SWIGLU),
+  PROFILED_KERNEL(cls_glu, gemm_bytes(z, M, 2 * z.F, z.H, z.F, EPI_SWIGLU),
            launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, c->xlo, M, z.F, z.H, nullptr, 0, c->fop,
-                       c->flo, nullptr, c->st));
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, z.F, z.H, EPI_PART),
+                       c->flo, nullptr, c->st, tm_));
+  PROFILED_KERNEL(cls_part, gemm_bytes(z, M, z.H, z.F, z.H, EPI_PART),
            launch_gemm(dt, EPI_PART, w.wdown, c->fop, c->flo, M, z.H, z.F, c->gpart, z.H, nullptr,
-                       0, s_down, c->st));
+                       0, s_down, c->st, tm_));
   return EAGLE_OK;
 }
 
@@ -505,7 +565,7 @@ eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t*
     KVView kv = c->tkv0;
     kv.base = (char*)c->tkv0.base + (int64_t)l * c->t_layer_elems * z.esz;
     int sd = 1;
-    SCHK(layer_core(c, c->tl[l], z.H, M, c->h, pos, slot, kv, vis, &sd));
+    SCHK(layer_core(c, c->tl[l], z.H, M, c->h, pos, slot, kv, vis, true, &sd));
     const bool last = l + 1 == z.NL;
     SCHK(resnorm(c, c->h, M, sd, false, last ? c->final_norm : c->tl[l + 1].attn_norm,
                  last ? c->tfeat : nullptr));
@@ -530,9 +590,9 @@ eagle_status draft_pass(eagle_ctx* c, int M, const int32_t* tok, const float* fe
     int S = 1;
     PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
              launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->xlo, c->st));
-    PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_PART),
+    PROFILED_KERNEL(EAGLE_PROF_DRAFT, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_PART),
              launch_gemm(z.dt, EPI_PART, c->fc, c->xop, c->xlo, M, z.H, 2 * z.H, c->gpart, z.H,
-                         nullptr, 0, &S, c->st));
+                         nullptr, 0, &S, c->st, tm_));
     SCHK(resnorm(c, hout, M, S, true, c->dl.attn_norm, nullptr));
   } else {
     PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 16.0,
@@ -540,7 +600,7 @@ eagle_status draft_pass(eagle_ctx* c, int M, const int32_t* tok, const float* fe
                                    c->cfg.rms_eps, M, z.H, c->xop, c->xlo, hout, c->st));
   }
   int sd = 1;
-  SCHK(layer_core(c, c->dl, z.kin_draft, M, hout, pos, slot, c->dkv, vis, &sd));
+  SCHK(layer_core(c, c->dl, z.kin_draft, M, hout, pos, slot, c->dkv, vis, false, &sd));
   SCHK(resnorm(c, hout, M, sd, false, nullptr, nullptr));
   return EAGLE_OK;
 }
@@ -569,9 +629,9 @@ eagle_status catch_up(eagle_ctx* c, int M, int first, const int32_t* tok, const 
 eagle_status fuse_rows(eagle_ctx* c, int M, const void* src, int64_t src_lo) {
   const Derived& z = c->z;
   int S = 1;
-  PROFILED(EAGLE_PROF_GEMM, gemm_bytes(z, M, z.H, 3 * z.H, z.H, EPI_PART),
+  PROFILED_KERNEL(EAGLE_PROF_DRAFT, gemm_bytes(z, M, z.H, 3 * z.H, z.H, EPI_PART),
            launch_gemm(z.dt, EPI_PART, c->fc, src, src_lo, M, z.H, 3 * z.H, c->gpart, z.H, nullptr,
-                       0, &S, c->st));
+                       0, &S, c->st, tm_));
   PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 4.0 * (S + 1),
            launch_sum_planes(c->gpart, S, (int64_t)M * z.H, M, z.H, c->gbuf, 0, c->st));
   return EAGLE_OK;
@@ -978,31 +1038,28 @@ eagle_status eagle_debug_read(eagle_ctx* c, int32_t what, void* host_dst, uint64
   return EAGLE_OK;
 }
 
-eagle_status eagle_profile_enable(eagle_ctx* c, int32_t on) {
-  if (!c) return EAGLE_E_INVALID;
-  c->prof = on != 0;
-  c->recs.clear();
-  c->pool_used = 0;
+eagle_status eagle_profile_enable(eagle_ctx* c, uint32_t class_mask, int32_t every) {
+  if (!c || every < 1) return EAGLE_E_INVALID;
+  prof_settle(c, true);
+  c->prof = class_mask;
+  c->prof_every = every;
+  std::memset(c->prof_seen, 0, sizeof(c->prof_seen));
+  std::memset(&c->ptot, 0, sizeof(c->ptot));
   return EAGLE_OK;
 }
 
 eagle_status eagle_profile_read(eagle_ctx* c, eagle_profile* out) {
   if (!c || !out) return EAGLE_E_INVALID;
-  std::memset(out, 0, sizeof(*out));
   HCHK(hipStreamSynchronize(c->st));
-  for (const eagle_ctx::ProfRec& r : c->recs) {
-    float ms = 0.f;
-    HCHK(hipEventElapsedTime(&ms, r.a, r.b));
-    out->launches[r.cls]++;
-    out->ms[r.cls] += ms;
-    out->bytes[r.cls] += r.bytes;
-  }
+  prof_settle(c, true);
+  *out = c->ptot;
   return EAGLE_OK;
 }
 
 void eagle_free(eagle_ctx* c) {
   if (!c) return;
-  for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
+  if (c->st) (void)hipStreamSynchronize(c->st);
+  for (hipEvent_t e : c->all_ev) (void)hipEventDestroy(e);
   delete c;
 }
 

@@ -16,6 +16,8 @@
 //    its own fp32 partial plane and the consumer of the result (the residual
 //    + RMSNorm kernel, or RoPE) sums the planes in a fixed order, so no
 //    cross-workgroup synchronisation is needed and results are repeatable.
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -437,20 +439,25 @@ template <> struct Cfg<4> { static constexpr int NW = 8, CS = 4; };
 template <> struct Cfg<5> { static constexpr int NW = 8, CS = 4; };
 
 template <typename T, int MT, int EPI>
-hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st) {
+hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st, const KTiming* tm) {
   constexpr int NW = Cfg<MT>::NW, CS = Cfg<MT>::CS;
-  hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, EPI>), dim3(tiles * a.splits, m_chunks), dim3(NW * 64), 0, st, a);
+  const dim3 grid(tiles * a.splits, m_chunks), block(NW * 64);
+  if (tm)
+    hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, EPI>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+  else
+    hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, EPI>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int EPI>
-hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hipStream_t st) {
+hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hipStream_t st,
+                         const KTiming* tm) {
   switch (mt) {
-    case 1: return launch_proj_mt<T, 1, EPI>(a, tiles, m_chunks, st);
-    case 2: return launch_proj_mt<T, 2, EPI>(a, tiles, m_chunks, st);
-    case 3: return launch_proj_mt<T, 3, EPI>(a, tiles, m_chunks, st);
-    case 4: return launch_proj_mt<T, 4, EPI>(a, tiles, m_chunks, st);
-    default: return launch_proj_mt<T, 5, EPI>(a, tiles, m_chunks, st);
+    case 1: return launch_proj_mt<T, 1, EPI>(a, tiles, m_chunks, st, tm);
+    case 2: return launch_proj_mt<T, 2, EPI>(a, tiles, m_chunks, st, tm);
+    case 3: return launch_proj_mt<T, 3, EPI>(a, tiles, m_chunks, st, tm);
+    case 4: return launch_proj_mt<T, 4, EPI>(a, tiles, m_chunks, st, tm);
+    default: return launch_proj_mt<T, 5, EPI>(a, tiles, m_chunks, st, tm);
   }
 }
 
@@ -512,7 +519,7 @@ uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M) {
 
 hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
                        int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int splits_out[1],
-                       hipStream_t stream) {
+                       hipStream_t stream, const KTiming* tm) {
   if (M <= 0) return hipSuccess;
   const int rows = (epi == EPI_SWIGLU) ? 2 * N : N;
   GemmPlan p = gemm_plan(M, rows, K, dtype, epi);
@@ -525,11 +532,11 @@ hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t
   a.Yt = Yt; a.ytlo = ytlo;
   if (splits_out) splits_out[0] = p.splits;
   if (dtype == 1) {
-    return epi == EPI_SWIGLU ? launch_proj_t<bf16_t, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream)
-                             : launch_proj_t<bf16_t, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream);
+    return epi == EPI_SWIGLU ? launch_proj_t<bf16_t, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm)
+                             : launch_proj_t<bf16_t, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm);
   }
-  return epi == EPI_SWIGLU ? launch_proj_t<float, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream)
-                           : launch_proj_t<float, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream);
+  return epi == EPI_SWIGLU ? launch_proj_t<float, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm)
+                           : launch_proj_t<float, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm);
 }
 
 uint64_t lmhead_part_floats(int M, int V, int k) {

@@ -5,8 +5,6 @@
 
 enum { EPI_PART = 0, EPI_SWIGLU = 2 };
 
-#define EAGLE_QKV_MAX 12288   // widest q|k|v row handled by the RoPE kernel (fp32 in LDS)
-
 // ---------------------------------------------------------------- GEMM
 // y = x W^T for a skinny x (M rows) and a weight W [N, K] streamed from HBM.
 //   EPI_PART  : fp32 partial planes Y[split][M][ldy] (split over K; the
@@ -18,9 +16,15 @@ enum { EPI_PART = 0, EPI_SWIGLU = 2 };
 struct GemmPlan { int mt, nb, splits, m_chunks, n_tiles; };
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi);
 uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M);
+// Optional device timestamps of one kernel dispatch: the events ride on the
+// dispatch itself (hipExtLaunchKernel), so they time that kernel alone.
+struct KTiming {
+  hipEvent_t start, stop;
+};
+
 hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
                        int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int* splits_out,
-                       hipStream_t stream);
+                       hipStream_t stream, const KTiming* tm = nullptr);
 
 // ---------------------------------------------------------------- LM head
 // Verify: g[m] = argmax_v (x W^T)[m, v] (lowest id on ties), margin[m] =
