@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libeagle.so")
 
 MAX_STATIC, MAX_DEPTH, MAX_VERIFY, MAX_NODES, MAX_TOPK = 64, 16, 128, 1024, 16
 F32, BF16 = 0, 1
+OK, E_INVALID, E_STATE, E_CAPACITY, E_BUFFER, E_HIP, E_DEVICE = range(7)
 HEAD_E1, HEAD_E3 = 0, 1
 TREE_DYNAMIC, TREE_STATIC = 0, 1
 STATUS = {0: "EAGLE_OK", 1: "EAGLE_E_INVALID", 2: "EAGLE_E_STATE", 3: "EAGLE_E_CAPACITY",
