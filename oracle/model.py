@@ -69,30 +69,60 @@ class Weights:
     """Weight tensors regenerated from the seeded generator (cached as fp32).
 
     A byte budget bounds the cache, so 7B-70B shapes are rebuilt layer by
-    layer instead of being held whole.
+    layer instead of being held whole. Evicted arrays are kept for reuse by
+    the next tensor of the same shape (layers repeat shapes), because writing
+    into fresh memory costs more than generating the values.
     """
 
     def __init__(self, cfg: Config, cache_bytes: int = 24 << 30):
         self.cfg = cfg
         self.cache = OrderedDict()
+        self.spare = []          # evicted arrays, reusable as output buffers
         self.budget = cache_bytes
-        self.used = 0
+        self.used = 0            # bytes in cache and spare
+
+    def _buffer(self, shape, nb):
+        for i, a in enumerate(self.spare):
+            if a.shape == tuple(shape):
+                return self.spare.pop(i)
+        while self.used + nb > self.budget and (self.cache or self.spare):
+            if self.spare:
+                self.used -= self.spare.pop(0).nbytes
+            else:
+                _, old = self.cache.popitem(last=False)
+                if old.shape == tuple(shape):
+                    return old
+                self.spare.append(old)
+        self.used += nb
+        return np.empty(shape, dtype=np.float32)
 
     def get(self, kind: int, group: int, layer: int = 0) -> np.ndarray:
         key = (kind, group, layer)
         if key in self.cache:
             self.cache.move_to_end(key)
             return self.cache[key]
-        arr = synth.tensor_values(self.cfg.seed, kind, group, layer,
-                                  self.cfg.shape(kind, group), self.cfg.dtype)
-        nb = arr.nbytes
-        while self.cache and self.used + nb > self.budget:
-            _, old = self.cache.popitem(last=False)
-            self.used -= old.nbytes
-        if nb <= self.budget:
-            self.cache[key] = arr
-            self.used += nb
+        shape = tuple(self.cfg.shape(kind, group))
+        nb = int(np.prod(shape)) * 4
+        if nb > self.budget:
+            return synth.tensor_values(self.cfg.seed, kind, group, layer, shape, self.cfg.dtype)
+        out = self._buffer(shape, nb)
+        arr = synth.tensor_values(self.cfg.seed, kind, group, layer, shape, self.cfg.dtype, out=out)
+        self.cache[key] = arr
         return arr
+
+
+_F64 = {}
+
+
+def _f64_buffer(shape) -> np.ndarray:
+    """A persistent fp64 scratch array (reused across calls, so the weight
+    chunks below are widened into memory that is already mapped)."""
+    n = int(np.prod(shape))
+    buf = _F64.get("w")
+    if buf is None or buf.size < n:
+        buf = np.empty(n, dtype=np.float64)
+        _F64["w"] = buf
+    return buf[:n].reshape(shape)
 
 
 def matmul_t(x, w32, chunk: int = 2048):
@@ -100,7 +130,10 @@ def matmul_t(x, w32, chunk: int = 2048):
     x = np.asarray(x, dtype=np.float64)
     out = np.empty((x.shape[0], w32.shape[0]), dtype=np.float64)
     for n0 in range(0, w32.shape[0], chunk):
-        out[:, n0:n0 + chunk] = x @ w32[n0:n0 + chunk].astype(np.float64).T
+        wc = w32[n0:n0 + chunk]
+        w64 = _f64_buffer(wc.shape)
+        np.copyto(w64, wc)          # exact widening of fp32 to fp64
+        out[:, n0:n0 + chunk] = x @ w64.T
     return out
 
 

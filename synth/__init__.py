@@ -61,12 +61,12 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build()
+        build()   # rebuilds only when synth.c is newer than the library
         lib = ctypes.CDLL(_LIB_PATH)
         u64, p = ctypes.c_uint64, ctypes.c_void_p
         lib.synth_normal_f32.argtypes = [u64, u64, u64, u64, p]
         lib.synth_normal_bf16.argtypes = [u64, u64, u64, u64, p]
+        lib.synth_normal_bf16_f32.argtypes = [u64, u64, u64, u64, p]
         lib.synth_tokens.argtypes = [u64, u64, u64, ctypes.c_uint32, p]
         lib.synth_key.argtypes = [u64, u64]
         lib.synth_key.restype = u64
@@ -76,8 +76,15 @@ def _load():
     return _lib
 
 
-def normal_f32(seed: int, sid: int, n: int, offset: int = 0) -> np.ndarray:
-    out = np.empty(n, dtype=np.float32)
+def _out(n, dtype, out):
+    if out is None:
+        return np.empty(n, dtype=dtype)
+    assert out.dtype == dtype and out.flags.c_contiguous and out.size == n
+    return out.reshape(n)
+
+
+def normal_f32(seed: int, sid: int, n: int, offset: int = 0, out=None) -> np.ndarray:
+    out = _out(n, np.float32, out)
     _load().synth_normal_f32(seed, sid, offset, n, out.ctypes.data)
     return out
 
@@ -88,20 +95,31 @@ def normal_bf16_bits(seed: int, sid: int, n: int, offset: int = 0) -> np.ndarray
     return out
 
 
+def normal_bf16_f32(seed: int, sid: int, n: int, offset: int = 0, out=None) -> np.ndarray:
+    """The bf16 values of normal_bf16_bits, as float32 (one pass)."""
+    out = _out(n, np.float32, out)
+    _load().synth_normal_bf16_f32(seed, sid, offset, n, out.ctypes.data)
+    return out
+
+
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32)
 
 
 def tensor_values(seed: int, kind: int, group: int, layer: int, shape,
-                  dtype: str) -> np.ndarray:
-    """Values of one weight tensor as float32 (bf16-representable if bf16)."""
+                  dtype: str, out=None) -> np.ndarray:
+    """Values of one weight tensor as float32 (bf16-representable if bf16),
+    written into `out` (float32, that shape) when given."""
     n = int(np.prod(shape))
     if kind in NORM_KINDS:
-        return np.ones(shape, dtype=np.float32)
+        if out is None:
+            return np.ones(shape, dtype=np.float32)
+        out[...] = 1.0
+        return out
     sid = stream_id(kind, group, layer)
     if dtype == "bf16":
-        return bf16_bits_to_f32(normal_bf16_bits(seed, sid, n)).reshape(shape)
-    return normal_f32(seed, sid, n).reshape(shape)
+        return normal_bf16_f32(seed, sid, n, out=out).reshape(shape)
+    return normal_f32(seed, sid, n, out=out).reshape(shape)
 
 
 def prompt(seed: int, n: int, vocab: int) -> np.ndarray:

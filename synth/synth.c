@@ -76,6 +76,18 @@ void synth_normal_bf16(uint64_t seed, uint64_t stream_id, uint64_t offset,
     out[i] = f32_to_bf16_rne(elem(key, offset + (uint64_t)i));
 }
 
+/* Same bf16 values widened back to fp32 (exactly representable), in one pass. */
+void synth_normal_bf16_f32(uint64_t seed, uint64_t stream_id, uint64_t offset,
+                           uint64_t n, float *out) {
+  uint64_t key = synth_key(seed, stream_id);
+  int64_t nn = (int64_t)n;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nn; ++i) {
+    uint32_t u = (uint32_t)f32_to_bf16_rne(elem(key, offset + (uint64_t)i)) << 16;
+    memcpy(&out[i], &u, 4);
+  }
+}
+
 /* n token ids uniform in [0, vocab). */
 void synth_tokens(uint64_t seed, uint64_t stream_id, uint64_t n, uint32_t vocab,
                   int32_t *out) {

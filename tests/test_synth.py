@@ -51,6 +51,9 @@ def test_bf16_is_round_to_nearest_even():
     b = synth.bf16_bits_to_f32(synth.normal_bf16_bits(0, 9, 100_000))
     ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float32).numpy()
     assert np.array_equal(b, ref)
+    # the one-pass fp32 form holds the same bf16 values, also at an offset
+    assert np.array_equal(synth.normal_bf16_f32(0, 9, 100_000), ref)
+    assert np.array_equal(synth.normal_bf16_f32(0, 9, 1000, offset=777), ref[777:1777])
 
 
 def test_prompt_ids():
