@@ -430,17 +430,50 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
 }
 
 // ---------------------------------------------------------------- dispatch
-// Launch shape per m-tile count: waves per workgroup and steps per chunk.
-template <int MT> struct Cfg;
-template <> struct Cfg<1> { static constexpr int NW = 4, CS = 16; };
-template <> struct Cfg<2> { static constexpr int NW = 4, CS = 8; };
-template <> struct Cfg<3> { static constexpr int NW = 8, CS = 4; };
-template <> struct Cfg<4> { static constexpr int NW = 8, CS = 4; };
-template <> struct Cfg<5> { static constexpr int NW = 8, CS = 4; };
+// Launch shape per m-tile count and kernel kind (partial-plane projection,
+// SwiGLU, LM head): waves per workgroup and steps per staged chunk. Small
+// chunks keep the LDS footprint low so several workgroups share a CU, which
+// the weight stream needs more than a deep per-wave prefetch (measured on
+// the 7B shapes).
+constexpr int KIND_HEAD = 3;
+template <int MT, int KIND> struct Cfg { static constexpr int NW = 8, CS = 4; };
+template <> struct Cfg<1, EPI_PART> { static constexpr int NW = 4, CS = 4; };
+template <> struct Cfg<1, EPI_SWIGLU> { static constexpr int NW = 8, CS = 8; };
+template <> struct Cfg<1, KIND_HEAD> { static constexpr int NW = 4, CS = 16; };
+template <> struct Cfg<2, EPI_PART> { static constexpr int NW = 4, CS = 4; };
+template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 4, CS = 4; };
+template <> struct Cfg<2, KIND_HEAD> { static constexpr int NW = 4, CS = 8; };
+
+template <int KIND>
+int waves_t(int mt) {
+  switch (mt) {
+    case 1: return Cfg<1, KIND>::NW;
+    case 2: return Cfg<2, KIND>::NW;
+    case 3: return Cfg<3, KIND>::NW;
+    case 4: return Cfg<4, KIND>::NW;
+    default: return Cfg<5, KIND>::NW;
+  }
+}
+template <int KIND>
+int chunk_t(int mt) {
+  switch (mt) {
+    case 1: return Cfg<1, KIND>::CS;
+    case 2: return Cfg<2, KIND>::CS;
+    case 3: return Cfg<3, KIND>::CS;
+    case 4: return Cfg<4, KIND>::CS;
+    default: return Cfg<5, KIND>::CS;
+  }
+}
+int waves_for(int mt, int kind) {
+  return kind == EPI_SWIGLU ? waves_t<EPI_SWIGLU>(mt) : kind == KIND_HEAD ? waves_t<KIND_HEAD>(mt) : waves_t<EPI_PART>(mt);
+}
+int chunk_for(int mt, int kind) {
+  return kind == EPI_SWIGLU ? chunk_t<EPI_SWIGLU>(mt) : kind == KIND_HEAD ? chunk_t<KIND_HEAD>(mt) : chunk_t<EPI_PART>(mt);
+}
 
 template <typename T, int MT, int EPI>
 hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st, const KTiming* tm) {
-  constexpr int NW = Cfg<MT>::NW, CS = Cfg<MT>::CS;
+  constexpr int NW = Cfg<MT, EPI>::NW, CS = Cfg<MT, EPI>::CS;
   const dim3 grid(tiles * a.splits, m_chunks), block(NW * 64);
   if (tm)
     hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, EPI>), grid, block, 0, st, tm->start, tm->stop, 0, a);
@@ -461,17 +494,9 @@ hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hip
   }
 }
 
-int waves_for(int mt) {
-  switch (mt) {
-    case 1: return Cfg<1>::NW;
-    case 2: return Cfg<2>::NW;
-    default: return Cfg<4>::NW;
-  }
-}
-
 template <typename T, bool TOPK, int MT>
 hipError_t launch_head_mt(const HeadArgs& h, int tiles, hipStream_t st) {
-  constexpr int NW = Cfg<MT>::NW, CS = Cfg<MT>::CS;
+  constexpr int NW = Cfg<MT, KIND_HEAD>::NW, CS = Cfg<MT, KIND_HEAD>::CS;
   hipLaunchKernelGGL((lmhead_kernel<T, MT, NW, CS, TOPK>), dim3(tiles), dim3(NW * 64), 0, st, h);
   return hipGetLastError();
 }
@@ -487,7 +512,7 @@ hipError_t launch_head_t(int mt, const HeadArgs& h, int tiles, hipStream_t st) {
   }
 }
 
-int head_rows(int M) { return 16 * waves_for(M > 64 ? 5 : (M + 15) / 16); }
+int head_rows(int M) { return 16 * waves_for(M > 64 ? 5 : (M + 15) / 16, KIND_HEAD); }
 
 }  // namespace
 
@@ -495,7 +520,7 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
   GemmPlan p;
   if (M <= 80) { p.mt = (M + 15) / 16; p.m_chunks = 1; }
   else { p.mt = 4; p.m_chunks = (M + 63) / 64; }
-  const int nw = waves_for(p.mt);
+  const int nw = waves_for(p.mt, epi);
   const int rows_per_tile = 16 * nw;
   p.nb = 1;
   if (epi == EPI_SWIGLU) {
@@ -505,9 +530,11 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
   } else {
     p.n_tiles = (N_rows + rows_per_tile - 1) / rows_per_tile;
     const int steps = K / (dtype == 1 ? 32 : 16);
-    const int cs = p.mt == 1 ? Cfg<1>::CS : (p.mt == 2 ? Cfg<2>::CS : Cfg<4>::CS);
+    // enough workgroups to fill the chip three times over, while every
+    // split keeps at least four chunks
+    const int cs = chunk_for(p.mt, epi);
     int s = 1;
-    while (p.n_tiles * s < 384 && s < 16 && steps / (2 * s) >= 2 * cs) s *= 2;
+    while (p.n_tiles * s < 768 && s < 16 && steps / (2 * s) >= 4 * cs) s *= 2;
     p.splits = s;
   }
   return p;
