@@ -2,19 +2,23 @@
 // per-row kernels around it (embedding, RMSNorm, RoPE + KV append, draft
 // input assembly, row gathers, KV compaction).
 //
-// bf16 attention (head_dim 128): one wave per (key chunk, query head, 16
-// query rows). S^T = K Q^T and O^T = V^T P^T run on 16x16x32 bf16 MFMA;
-// keys are loaded in an order that makes each lane's 8 scores exactly the
-// P^T operand of the PV product, so P never leaves registers. P is split
-// into bf16 hi + lo parts (two MFMAs) so it keeps ~16 mantissa bits, and
-// the query arrives the same way (an fp32 activation as two bf16 planes). Chunks
-// are combined with their (max, sum) pairs in a second kernel.
+// bf16 attention (head_dim 128): one workgroup of four waves per (KV head,
+// chunk of 64 keys). The chunk's K (hi and lo planes, XOR-swizzled rows) and
+// V^T (hi and lo) are staged in LDS once and shared by every query head of
+// the GQA group and every block of 16 query rows. Per 32-key block a wave
+// computes S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA; keys are
+// read in an order that makes each lane's 8 scores exactly the P^T operand
+// of the PV product, so P never leaves registers. Q, K, V and P are carried
+// as bf16 hi + lo parts (three products; lo*lo dropped), which keeps ~16
+// mantissa bits. When a chunk has fewer (head, row block) pairs than waves,
+// the waves split its keys and merge through LDS, so each chunk leaves one
+// (max, sum, O) partial per row and head; a second kernel merges chunks.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int CHUNK = 128;
+constexpr int CHUNK = 64;     // keys per attention workgroup
 
 template <typename T>
 __device__ __forceinline__ T* kv_ptr(const KVView& v, int slot, int sel, int h) {
@@ -56,127 +60,194 @@ struct AttnArgs {
   float* mlpart;
 };
 
-__global__ __launch_bounds__(64) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int D = 128;
-  __shared__ bf16_t vt[2][D][40];   // V^T block, hi and lo: [d][32 keys] (+8 pad)
-  const int chunk = blockIdx.x, h = blockIdx.y, rt = blockIdx.z;
-  const int lane = threadIdx.x, lr = lane & 15, g = lane >> 4;
-  const int hk = h / a.group;
-  const int k0 = a.vis.pre_lo + chunk * CHUNK;
-  const int k1 = min(a.vis.key_end, k0 + CHUNK);
-  const int row = rt * 16 + lr;
-  const int rowc = min(row, a.M - 1);
+// 16-byte column c of a staged K row of key index `key`: XOR-swizzled so the
+// 16 keys read by one MFMA operand load fall in distinct LDS banks.
+__device__ __forceinline__ int k_swz(int key) { return (key & 3) | ((key >> 1) & 12); }
 
-  uint4 qf[4], ql[4];   // query as hi + lo bf16 planes
-  const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qf[s] = ld16(qp + 32 * s);
-    ql[s] = ld16(qp + a.qlo + 32 * s);
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int D = 128, CK = CHUNK, VP = CK + 8;   // V^T row pitch (elements)
+  __shared__ uint4 ks[2][CK][16];                  // K hi/lo: [key][16-byte column ^ swz]
+  __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];   // V^T hi/lo
+  const int chunk = blockIdx.x, hk = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+  const int k0 = a.vis.pre_lo + chunk * CK;
+  const int k1 = min(a.vis.key_end, k0 + CK);
+
+  // ---- stage the chunk (keys past k1 repeat the last key; they are masked)
+  for (int i = tid; i < 2 * CK * 16; i += 256) {
+    const int plane = i / (CK * 16), key = (i / 16) % CK, c = i % 16;
+    const int kk = min(k0 + key, k1 - 1);
+    ks[plane][key][c ^ k_swz(key)] = ld16(kv_ptr<bf16_t>(a.kv, kk, plane, hk) + 8 * c);
   }
-  const int prehi = a.vis.prehi[rowc];
-  const uint64_t mk0 = a.vis.mask[2 * rowc], mk1 = a.vis.mask[2 * rowc + 1];
-
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[8];
+  for (int i = tid; i < 2 * (CK / 2) * 16; i += 256) {
+    const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
+    const int ka = min(k0 + 2 * kp, k1 - 1), kb = min(k0 + 2 * kp + 1, k1 - 1);
+    const uint4 va = ld16(kv_ptr<bf16_t>(a.kv, ka, 2 + plane, hk) + 8 * c);
+    const uint4 vb = ld16(kv_ptr<bf16_t>(a.kv, kb, 2 + plane, hk) + 8 * c);
+    const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = k0; kb < k1; kb += 32) {
-    f32x4 sc[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int key = min(kb + 8 * (lr >> 2) + 4 * hh + (lr & 3), k1 - 1);
-      const bf16_t* kp = kv_ptr<bf16_t>(a.kv, key, 0, hk) + 8 * g;
-      const bf16_t* kpl = kv_ptr<bf16_t>(a.kv, key, 1, hk) + 8 * g;
-      sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
-        const uint4 kf = ld16(kp + 32 * s);
-        const uint4 kl = ld16(kpl + 32 * s);
-        Mma<bf16_t>::mma(kf, qf[s], sc[hh]);
-        Mma<bf16_t>::mma(kf, ql[s], sc[hh]);
-        Mma<bf16_t>::mma(kl, qf[s], sc[hh]);
-      }
+    for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
+      *reinterpret_cast<uint32_t*>(&vt[plane][8 * c + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
+      *reinterpret_cast<uint32_t*>(&vt[plane][8 * c + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
     }
-    float p[8];
-    float bm = -INFINITY;
+  }
+  __syncthreads();
+
+  // ---- (query head, row block) pairs; fewer pairs than waves: split keys
+  const int nrb = (a.M + 15) / 16, P = a.group * nrb;
+  int kw = 1;
+  while (P * kw * 2 <= 4 && kw * 2 <= CK / 32) kw *= 2;
+  const int kg = wave / P;                 // key group of this wave (kw > 1)
+  const int nblk = CK / 32 / kw;           // 32-key blocks per key group
+  float m_keep = -INFINITY, l_keep = 0.f;
+  f32x4 o[8];
+  int pair_keep = -1;
+  for (int pr = (kw > 1 ? wave % P : wave); pr < P && kg < kw; pr += (kw > 1 ? P : 4)) {
+    const int h = hk * a.group + pr / nrb, rb = pr % nrb;
+    const int row = rb * 16 + lr, rowc = min(row, a.M - 1);
+    uint4 qf[4], ql[4];
+    const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int s = 0; s < 4; ++s) {
+      qf[s] = ld16(qp + 32 * s);
+      ql[s] = ld16(qp + a.qlo + 32 * s);
+    }
+    const int prehi = a.vis.prehi[rowc];
+    const uint64_t mk0 = a.vis.mask[2 * rowc], mk1 = a.vis.mask[2 * rowc + 1];
+    float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = kb + 8 * g + 4 * hh + e;
-        const bool ok = key < k1 && row_sees(a.vis, prehi, mk0, mk1, key);
-        p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
-        bm = fmaxf(bm, p[4 * hh + e]);
+    for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bi = 0; bi < nblk; ++bi) {
+      const int kb0 = (kg * nblk + bi) * 32;   // block start within the chunk
+      f32x4 sc[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
+        const int sw = k_swz(key);
+        sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+          const uint4 kf = ks[0][key][(4 * s + g) ^ sw];
+          const uint4 kl = ks[1][key][(4 * s + g) ^ sw];
+          Mma<bf16_t>::mma(kf, qf[s], sc[hh]);
+          Mma<bf16_t>::mma(kf, ql[s], sc[hh]);
+          Mma<bf16_t>::mma(kl, qf[s], sc[hh]);
+        }
       }
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
-    const float m_new = fmaxf(m_run, bm);
-    float alpha = 1.f, ps = 0.f;
-    if (m_new != -INFINITY) {
-      alpha = expf(m_run - m_new);
+      float p[8];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = k0 + kb0 + 8 * g + 4 * hh + e;
+          const bool ok = key < k1 && row_sees(a.vis, prehi, mk0, mk1, key);
+          p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
+          bm = fmaxf(bm, p[4 * hh + e]);
+        }
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m_run, bm);
+      float alpha = 1.f, ps = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = expf(m_run - m_new);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p[i] = expf(p[i] - m_new);
+          ps += p[i];
+        }
+        m_run = m_new;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = 0.f;
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run = l_run * alpha + ps;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      bf16_t ph[8], pl[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = expf(p[i] - m_new);
-        ps += p[i];
+        ph[i] = f32_to_bf16(p[i]);
+        pl[i] = f32_to_bf16(p[i] - bf16_to_f32(ph[i]));
       }
-      m_run = m_new;
+      const uint4 phi = *reinterpret_cast<const uint4*>(ph);
+      const uint4 plo = *reinterpret_cast<const uint4*>(pl);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+        const uint4 va = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
+        const uint4 val = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
+        Mma<bf16_t>::mma(va, phi, o[dt]);
+        Mma<bf16_t>::mma(va, plo, o[dt]);
+        Mma<bf16_t>::mma(val, phi, o[dt]);
+      }
+    }
+    if (kw == 1) {
+      if (row < a.M) {
+        float* op = a.opart + (((int64_t)chunk * a.M + row) * a.nq + h) * D;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) op[16 * dt + 4 * g + e] = o[dt][e];
+        if (g == 0) {
+          float* ml = a.mlpart + (((int64_t)chunk * a.M + row) * a.nq + h) * 2;
+          ml[0] = m_run;
+          ml[1] = l_run;
+        }
+      }
     } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
-    }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l_run = l_run * alpha + ps;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
-
-    // V block (32 keys x 128) -> LDS, transposed
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int idx = it * 64 + lane;
-      const int kl = idx >> 4, dc = idx & 15;
-      const int key = min(kb + kl, k1 - 1);
-      const uint4 v = ld16(kv_ptr<bf16_t>(a.kv, key, 2, hk) + 8 * dc);
-      const uint4 vl = ld16(kv_ptr<bf16_t>(a.kv, key, 3, hk) + 8 * dc);
-      const bf16_t* vv = reinterpret_cast<const bf16_t*>(&v);
-      const bf16_t* vvl = reinterpret_cast<const bf16_t*>(&vl);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        vt[0][8 * dc + j][kl] = vv[j];
-        vt[1][8 * dc + j][kl] = vvl[j];
-      }
-    }
-    __syncthreads();
-    bf16_t ph[8], pl[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ph[i] = f32_to_bf16(p[i]);
-      pl[i] = f32_to_bf16(p[i] - bf16_to_f32(ph[i]));
-    }
-    const uint4 phi = *reinterpret_cast<const uint4*>(ph);
-    const uint4 plo = *reinterpret_cast<const uint4*>(pl);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
-      const uint4 va = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][8 * g]);
-      const uint4 val = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][8 * g]);
-      Mma<bf16_t>::mma(va, phi, o[dt]);
-      Mma<bf16_t>::mma(va, plo, o[dt]);
-      Mma<bf16_t>::mma(val, phi, o[dt]);
+      m_keep = m_run;
+      l_keep = l_run;
+      pair_keep = pr;
     }
   }
-  if (row < a.M) {
-    float* op = a.opart + (((int64_t)chunk * a.M + row) * a.nq + h) * D;
+  if (kw == 1) return;   // uniform across the workgroup
+
+  // ---- merge the key groups of each pair through LDS (reuses the K area)
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(&ks[0][0][0]);     // [wave][16 rows][128]
+  float* mm = reinterpret_cast<float*>(&vt[0][0][0]);     // [wave][16 rows][2]
+  static_assert(4 * 16 * D * 4 <= (int)sizeof(ks), "merge buffer must fit");
+  if (pair_keep >= 0) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) op[16 * dt + 4 * g + e] = o[dt][e];
+      for (int e = 0; e < 4; ++e) mo[(wave * 16 + lr) * D + 16 * dt + 4 * g + e] = o[dt][e];
     if (g == 0) {
-      float* ml = a.mlpart + (((int64_t)chunk * a.M + row) * a.nq + h) * 2;
-      ml[0] = m_run;
-      ml[1] = l_run;
+      mm[(wave * 16 + lr) * 2] = m_keep;
+      mm[(wave * 16 + lr) * 2 + 1] = l_keep;
+    }
+  }
+  __syncthreads();
+  if (pair_keep >= 0 && kg == 0) {
+    const int h = hk * a.group + pair_keep / nrb, rb = pair_keep % nrb;
+    const int row = rb * 16 + lr;
+    float gm = -INFINITY;
+    for (int k = 0; k < kw; ++k) gm = fmaxf(gm, mm[((wave + k * P) * 16 + lr) * 2]);
+    float lsum = 0.f, wk[4];
+    for (int k = 0; k < kw; ++k) {
+      const float mk = mm[((wave + k * P) * 16 + lr) * 2];
+      wk[k] = mk == -INFINITY ? 0.f : expf(mk - gm);
+      lsum += wk[k] * mm[((wave + k * P) * 16 + lr) * 2 + 1];
+    }
+    if (row < a.M) {
+      float* op = a.opart + (((int64_t)chunk * a.M + row) * a.nq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int dd = 16 * dt + 4 * g + e;
+          float acc = 0.f;
+          for (int k = 0; k < kw; ++k) acc += wk[k] * mo[((wave + k * P) * 16 + lr) * D + dd];
+          op[dd] = acc;
+        }
+      if (g == 0) {
+        float* ml = a.mlpart + (((int64_t)chunk * a.M + row) * a.nq + h) * 2;
+        ml[0] = gm;
+        ml[1] = lsum;
+      }
     }
   }
 }
@@ -566,7 +637,7 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
     const int n_chunks = (vis.key_end - vis.pre_lo + CHUNK - 1) / CHUNK;
     if (n_chunks <= 0) return hipErrorInvalidValue;
     AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, scale, opart, mlpart};
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, nq, (M + 15) / 16), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(M, nq), dim3(128), 0, st, opart, mlpart,
