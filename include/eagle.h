@@ -179,8 +179,15 @@ eagle_status eagle_tensor_info(const eagle_config* cfg, int32_t index, eagle_ten
 
 /* Creates a context over caller-owned buffers (sizes >= eagle_query's) on
  * HIP stream `hip_stream` (NULL = the default stream). The weights must be
- * in place before eagle_prefill. Binds to the device current at this call.
- * EAGLE_E_BUFFER if a buffer is NULL or too small. *out is a host object. */
+ * in place, in the row-major layout of eagle_tensor, before this call: for
+ * EAGLE_BF16 it rewrites every matrix except the embedding, in place, into
+ * the fragment-packed form its kernels stream (each full block of 16 rows
+ * keeps its byte range; see eagle_op_pack in eagle_ops.h), using the
+ * scratch buffer as staging, and synchronises the stream. A weight buffer
+ * is therefore loaded by one context once; the caller must not write it
+ * afterwards. Binds to the device current at this call. EAGLE_E_BUFFER if
+ * a buffer is NULL or too small, EAGLE_E_HIP if packing fails. *out is a
+ * host object. */
 eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void* hip_stream,
                         eagle_ctx** out);
 

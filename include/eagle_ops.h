@@ -4,7 +4,8 @@
  * kernels on their own. All calls enqueue on `stream` (NULL = default)
  * and do not synchronise; pointers are device pointers unless stated.
  * Element type `dtype` is EAGLE_F32 or EAGLE_BF16 (raw bf16 bits) of the
- * weights. Activations are fp32 values: for EAGLE_F32 one fp32 array; for
+ * weights; bf16 weights are passed fragment-packed (eagle_op_pack), fp32
+ * weights row-major. Activations are fp32 values: for EAGLE_F32 one fp32 array; for
  * EAGLE_BF16 two bf16 planes of the same shape, back to back, hi = bf16(v)
  * then lo = bf16(v - hi), which the kernels multiply as hi*w + lo*w.
  */
@@ -21,6 +22,19 @@ extern "C" {
 
 enum { EAGLE_EPI_STORE = 0, EAGLE_EPI_ADD = 1, EAGLE_EPI_SWIGLU = 2 };
 
+/* Fragment packing of a bf16 weight W [N, K] (K a multiple of 32), the form
+ * every bf16 weight argument below must be in. Row block b (rows 16b ..
+ * 16b+15, for b < N/16) keeps its row-major byte range and is stored as K/32
+ * fragments of 16 x 32 elements, fragment s at element offset
+ * (16 b K + 512 s): lane l = r + 16 g of the fragment (r < 16, g < 4) holds
+ * the 8 elements W[16b + r][32s + 8g .. 32s + 8g + 7] at offset 8 l. The
+ * last N % 16 rows are copied unchanged (they stay row-major). src and dst
+ * are device pointers to non-overlapping N*K-element buffers. The kernels
+ * stream one 1 KB fragment per wave load, which the 16x16x32 bf16 MFMA takes
+ * as its A operand without reshuffling. EAGLE_E_INVALID on bad sizes or
+ * overlapping buffers, EAGLE_E_HIP on a launch failure. */
+eagle_status eagle_op_pack(const void* src, void* dst, int32_t N, int32_t K, void* stream);
+
 /* Workspace bytes eagle_op_linear needs for this shape (may be 0). The
  * workspace must be zero-filled before its first use; calls leave its
  * counters at zero, so it can be reused without clearing. */
@@ -35,7 +49,8 @@ uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, i
  *   EPI_ADD   : y fp32 [M, N],  y += x W^T  (residual update)
  *   EPI_SWIGLU: y [M, N] activations, y = silu(x Wg^T) * (x Wu^T)
  * Accumulation is fp32; summation order is fixed, so results repeat
- * bit for bit. Requires K a multiple of 32 (bf16) or 16 (fp32), M >= 1.
+ * bit for bit. Requires K a multiple of 32 (bf16) or 16 (fp32), M >= 1,
+ * and for bf16 EPI_SWIGLU N a multiple of 16 (gate and up blocks align).
  * EAGLE_E_INVALID on bad sizes, EAGLE_E_BUFFER if the workspace is too
  * small, EAGLE_E_HIP on a launch failure. */
 eagle_status eagle_op_linear(int32_t dtype, int32_t epilogue, const void* x, const void* w, void* y,

@@ -312,6 +312,16 @@ def tree_to_dict(t: Tree) -> dict:
 
 
 # ---------------------------------------------------------------- kernel ops
+def op_pack(src, dst, N: int, K: int, stream=None):
+    """eagle_op_pack: fragment-pack the bf16 weight src [N, K] into dst."""
+    L = lib()
+    L.eagle_op_pack.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i32, i32, ctypes.c_void_p]
+    st = stream.cuda_stream if stream is not None else _torch_stream()
+    rc = L.eagle_op_pack(src.data_ptr(), dst.data_ptr(), N, K, st)
+    if rc:
+        raise EagleError(rc, "eagle_op_pack")
+
+
 def op_linear(dtype: int, epilogue: int, x, w, y, M: int, N: int, K: int, workspace=None,
               stream=None):
     """eagle_op_linear on torch tensors (device pointers)."""

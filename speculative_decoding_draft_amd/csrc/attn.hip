@@ -74,18 +74,36 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int k0 = a.vis.pre_lo + chunk * CK;
   const int k1 = min(a.vis.key_end, k0 + CK);
 
-  // ---- stage the chunk (keys past k1 repeat the last key; they are masked)
-  for (int i = tid; i < 2 * CK * 16; i += 256) {
+  // ---- stage the chunk (keys past k1 repeat the last key; they are masked).
+  // Every load of this thread is issued before the first LDS store, so the
+  // workgroup waits for one memory latency instead of one per piece.
+  static_assert(2 * CK * 16 == 8 * 256 && 2 * (CK / 2) * 16 == 4 * 256, "staging assumes 256 threads");
+  uint4 kr[8], va[4], vb[4];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int i = tid + 256 * it;
     const int plane = i / (CK * 16), key = (i / 16) % CK, c = i % 16;
-    const int kk = min(k0 + key, k1 - 1);
-    ks[plane][key][c ^ k_swz(key)] = ld16(kv_ptr<bf16_t>(a.kv, kk, plane, hk) + 8 * c);
+    kr[it] = ld16(kv_ptr<bf16_t>(a.kv, min(k0 + key, k1 - 1), plane, hk) + 8 * c);
   }
-  for (int i = tid; i < 2 * (CK / 2) * 16; i += 256) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = tid + 256 * it;
     const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
-    const int ka = min(k0 + 2 * kp, k1 - 1), kb = min(k0 + 2 * kp + 1, k1 - 1);
-    const uint4 va = ld16(kv_ptr<bf16_t>(a.kv, ka, 2 + plane, hk) + 8 * c);
-    const uint4 vb = ld16(kv_ptr<bf16_t>(a.kv, kb, 2 + plane, hk) + 8 * c);
-    const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+    va[it] = ld16(kv_ptr<bf16_t>(a.kv, min(k0 + 2 * kp, k1 - 1), 2 + plane, hk) + 8 * c);
+    vb[it] = ld16(kv_ptr<bf16_t>(a.kv, min(k0 + 2 * kp + 1, k1 - 1), 2 + plane, hk) + 8 * c);
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int i = tid + 256 * it;
+    const int plane = i / (CK * 16), key = (i / 16) % CK, c = i % 16;
+    ks[plane][key][c ^ k_swz(key)] = kr[it];
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = tid + 256 * it;
+    const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
+    const uint32_t wa[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
+    const uint32_t wb[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
       *reinterpret_cast<uint32_t*>(&vt[plane][8 * c + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);

@@ -370,7 +370,9 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
   TAKE(t.s_prow, int32_t, EAGLE_MAX_STATIC);
   TAKE(t.s_exp, int32_t, (EAGLE_MAX_DEPTH + 1) * TREE_MAXEXP);
   TAKE(t.s_nexp, int32_t, EAGLE_MAX_DEPTH + 1);
-  return cv.off;
+  // eagle_load stages weight blocks of 16 rows through scratch when it
+  // packs bf16 matrices: keep room for at least one block of the widest.
+  return std::max<uint64_t>(cv.off, 16 * kmax * es);
 }
 #undef TAKE
 
@@ -739,6 +741,33 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
   c->tkv0 = KVView{c->KV, c->tpt, page_elems, KV_PAGE, z.nkv, z.d};
   c->dkv = KVView{c->KV + align_up((uint64_t)z.NL * c->t_layer_elems * z.esz), c->dpt, page_elems,
                   KV_PAGE, z.nkv, z.d};
+  // bf16 matrices the GEMM and LM-head kernels stream are fragment-packed in
+  // place, a batch of 16-row blocks at a time through the (still unused)
+  // scratch buffer; the embedding stays row-major (rows are gathered).
+  if (z.dt == 1) {
+    hipError_t e = hipSuccess;
+    for (const eagle_tensor& t : tab) {
+      if (t.dtype != EAGLE_BF16 || t.kind == EAGLE_T_EMBED || t.rows < 16) continue;
+      const uint64_t blk = 16ull * (uint64_t)t.cols * 2;
+      const int64_t nrb = t.rows / 16;
+      const int64_t per = (int64_t)(bufs->scratch_bytes / blk);
+      if (per < 1 || t.cols % 32) {
+        delete c;
+        return EAGLE_E_BUFFER;
+      }
+      for (int64_t b0 = 0; b0 < nrb && e == hipSuccess; b0 += per) {
+        const int64_t nb = std::min(per, nrb - b0);
+        char* p = c->W + t.offset + (uint64_t)b0 * blk;
+        e = hipMemcpyAsync(c->S, p, (size_t)nb * blk, hipMemcpyDeviceToDevice, c->st);
+        if (e == hipSuccess) e = launch_pack_frag(c->S, p, nb, (int)t.cols, c->st);
+      }
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(c->st);
+    if (e != hipSuccess) {
+      delete c;
+      return EAGLE_E_HIP;
+    }
+  }
   c->tp = TreeParams{z.dynamic, z.k_b, z.k_e, z.D, z.budget, cfg->tree == EAGLE_TREE_STATIC ? cfg->n_static : 0};
   // host-built tables: RoPE, page tables (identity), iota, static plan
   {

@@ -97,7 +97,24 @@ __device__ __forceinline__ void proj_core(const ProjArgs& a, int row0, int s_lo,
   using MM = Mma<T>;
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const T* wp = (const T*)a.W + (int64_t)min(row0 + lr, a.rows - 1) * a.K + lg * S::EPL;
+  const T* wp;
+  int64_t wstep;   // elements between consecutive K steps of this lane's piece
+  if constexpr (Opnd<T>::SPLIT) {
+    // bf16 weights are fragment-packed (see pack_frag_kernel): a full
+    // 16-row block is a run of 1 KB fragments, one per K step, lane-ordered;
+    // rows of a ragged last block stay row-major.
+    const int rb = min(row0, a.rows - 1) >> 4;
+    if ((rb + 1) * 16 <= a.rows) {
+      wp = (const T*)a.W + (int64_t)rb * 16 * a.K + lane * S::EPL;
+      wstep = 16 * S::KS;
+    } else {
+      wp = (const T*)a.W + (int64_t)min(row0 + lr, a.rows - 1) * a.K + lg * S::EPL;
+      wstep = S::KS;
+    }
+  } else {
+    wp = (const T*)a.W + (int64_t)min(row0 + lr, a.rows - 1) * a.K + lg * S::EPL;
+    wstep = S::KS;
+  }
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nch = (s_hi - s_lo + CS - 1) / CS;
@@ -107,7 +124,7 @@ __device__ __forceinline__ void proj_core(const ProjArgs& a, int row0, int s_lo,
 
   auto load_w = [&](uint4 (&w)[CS], int c) {
 #pragma unroll
-    for (int u = 0; u < CS; ++u) w[u] = ld16(wp + (int64_t)min(s_lo + c * CS + u, s_hi - 1) * S::KS);
+    for (int u = 0; u < CS; ++u) w[u] = ld16(wp + (int64_t)min(s_lo + c * CS + u, s_hi - 1) * wstep);
   };
   auto compute = [&](const uint4 (&w)[CS], const T* x, int c) {
 #pragma unroll
@@ -213,6 +230,28 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
         const int m = 16 * t + lr;
         if (m < b.M && row < a.rows) Y[(int64_t)(m0 + m) * a.ldy + row] = acc[t][j];
       }
+  }
+}
+
+// ---------------------------------------------------------------- packing
+// Fragment packing of a bf16 matrix [rows, K] (K a multiple of 32): full
+// 16-row block rb is stored as K/32 fragments of 1 KB, fragment s holding
+// rows 16rb..16rb+15 x columns 32s..32s+31 in the order the 16x16x32 MFMA
+// A operand is loaded (lane l = r + 16g: row 16rb + r, columns 32s + 8g ..
+// 32s + 8g + 7). A block keeps its row-major byte range, so the first
+// 16*nrb rows pack in place through a staging copy; one wave load then reads
+// 1 KB of contiguous HBM instead of sixteen 64-byte pieces.
+__global__ __launch_bounds__(256) void pack_frag_kernel(const bf16_t* __restrict__ src,
+                                                        bf16_t* __restrict__ dst, int64_t pieces,
+                                                        int K) {
+  const int steps = K >> 5;
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < pieces; p += (int64_t)gridDim.x * 256) {
+    const int64_t f = p >> 6;
+    const int l = (int)(p & 63);
+    const int64_t rb = f / steps;
+    const int s = (int)(f % steps);
+    const uint4 v = ld16(src + (rb * 16 + (l & 15)) * K + s * 32 + 8 * (l >> 4));
+    *reinterpret_cast<uint4*>(dst + p * 8) = v;
   }
 }
 
@@ -630,5 +669,16 @@ hipError_t launch_lmhead_topk(int dtype, const void* W, const void* x, int64_t x
   hipError_t e = head_launch(dtype, true, W, x, xlo, M, V, H, k, part, nullptr, &tiles, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_combine, dim3(M), dim3(256), 0, stream, part, tiles, M, k, ids, logp);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_frag(const void* src, void* dst, int64_t n_blocks, int K, hipStream_t st) {
+  if (n_blocks <= 0) return hipSuccess;
+  if (K <= 0 || K % 32) return hipErrorInvalidValue;
+  const int64_t pieces = n_blocks * (K / 32) * 64;
+  const int64_t want = (pieces + 255) / 256;
+  const int grid = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(pack_frag_kernel, dim3(grid), dim3(256), 0, st, (const bf16_t*)src, (bf16_t*)dst,
+                     pieces, K);
   return hipGetLastError();
 }

@@ -26,6 +26,11 @@ hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t
                        int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int* splits_out,
                        hipStream_t stream, const KTiming* tm = nullptr);
 
+// Fragment packing of the first 16*n_blocks rows of a bf16 [*, K] matrix
+// from row-major `src` to `dst` (non-overlapping; same byte range per block).
+// Every bf16 weight the GEMM and LM-head kernels stream is in this form.
+hipError_t launch_pack_frag(const void* src, void* dst, int64_t n_blocks, int K, hipStream_t stream);
+
 // ---------------------------------------------------------------- LM head
 // Verify: g[m] = argmax_v (x W^T)[m, v] (lowest id on ties), margin[m] =
 // top-1 minus top-2; logits stored to `logits` [M, V] when not null.

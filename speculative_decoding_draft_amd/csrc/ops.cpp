@@ -14,12 +14,28 @@ uint64_t align256(uint64_t x) { return (x + 255) / 256 * 256; }
 bool linear_ok(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K) {
   if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return false;
   if (epi < EAGLE_EPI_STORE || epi > EAGLE_EPI_SWIGLU) return false;
+  if (dtype == EAGLE_BF16 && epi == EAGLE_EPI_SWIGLU && N % 16) return false;
   const int ks = dtype == EAGLE_BF16 ? 32 : 16;
   return M >= 1 && N >= 1 && K >= ks && K % ks == 0;
 }
 }  // namespace
 
 extern "C" {
+
+eagle_status eagle_op_pack(const void* src, void* dst, int32_t N, int32_t K, void* stream) {
+  if (!src || !dst || N < 1 || K < 32 || K % 32) return EAGLE_E_INVALID;
+  const uint64_t bytes = (uint64_t)N * K * 2;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return EAGLE_E_INVALID;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t nrb = N / 16;
+  const uint64_t packed = (uint64_t)nrb * 16 * K * 2;
+  hipError_t e = launch_pack_frag(src, dst, nrb, K, st);
+  if (e == hipSuccess && packed < bytes)
+    e = hipMemcpyAsync((char*)dst + packed, (const char*)src + packed, bytes - packed,
+                       hipMemcpyDeviceToDevice, st);
+  return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
+}
 
 uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K) {
   if (!linear_ok(dtype, epi, M, N, K)) return 0;

@@ -34,6 +34,39 @@ def _from_planes(t, shape, dtype):
     return (t[:n].double() + t[n:].double()).numpy().reshape(shape)
 
 
+def _dev_weight(w, dtype):
+    """Device copy of a weight in the layout the kernels take: fp32 row-major,
+    bf16 fragment-packed by eagle_op_pack."""
+    wd = w.cuda()
+    if dtype != BF16:
+        return wd
+    packed = torch.empty_like(wd)
+    E.op_pack(wd, packed, w.shape[0], w.shape[1])
+    return packed
+
+
+def _pack_ref(w):
+    """The packed layout written out with numpy (rows % 16 == 0 part, then the
+    row-major tail), for a bit-exact check of eagle_op_pack."""
+    a = w.view(torch.int16).numpy()
+    N, K = a.shape
+    n16 = N // 16 * 16
+    head = a[:n16].reshape(N // 16, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    return np.concatenate([head, a[n16:].reshape(-1)])
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (48, 96), (4096, 4096), (1000, 1024), (5, 64)])
+def test_pack_layout(N, K):
+    print(f"pack N={N} K={K}", flush=True)
+    gen = torch.Generator().manual_seed(N * 3 + K)
+    w = _rand((N, K), gen, 0.02, BF16)
+    src = w.cuda()
+    dst = torch.empty_like(src)
+    E.op_pack(src, dst, N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().view(torch.int16).numpy().reshape(-1), _pack_ref(w))
+
+
 def _ws(nbytes):
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device="cuda")
 
@@ -63,7 +96,8 @@ def test_linear(dtype, M, N, K, epi):
     ref = x.double().numpy() @ w.double().numpy().T
     y = (y0.clone() if epi == 1 else torch.zeros(M, N)).cuda()
     ws = _ws(E.op_linear_workspace(dtype, epi, M, N, K))
-    E.op_linear(dtype, epi, xd, w.cuda(), y, M, N, K, ws)
+    wd = _dev_weight(w, dtype)
+    E.op_linear(dtype, epi, xd, wd, y, M, N, K, ws)
     torch.cuda.synchronize()
     got = y.cpu().double().numpy()
     if epi == 1:
@@ -71,7 +105,7 @@ def test_linear(dtype, M, N, K, epi):
     assert _rel(got, ref) < 1e-4
     if epi == 0:   # same bits on a second run
         y2 = torch.zeros(M, N, device="cuda")
-        E.op_linear(dtype, epi, xd, w.cuda(), y2, M, N, K, ws)
+        E.op_linear(dtype, epi, xd, wd, y2, M, N, K, ws)
         torch.cuda.synchronize()
         assert torch.equal(y2.cpu(), y.cpu())
 
@@ -90,7 +124,7 @@ def test_swiglu(dtype, M, N, K):
     out = torch.zeros(planes * M * N, dtype=torch.bfloat16 if dtype == BF16 else torch.float32,
                       device="cuda")
     ws = _ws(E.op_linear_workspace(dtype, 2, M, N, K))
-    E.op_linear(dtype, 2, xd, w.cuda(), out, M, N, K, ws)
+    E.op_linear(dtype, 2, xd, _dev_weight(w, dtype), out, M, N, K, ws)
     torch.cuda.synchronize()
     got = _from_planes(out, (M, N), dtype)
     tol = 1e-5 * np.abs(ref) + 1e-4 * np.abs(ref).max()
@@ -110,7 +144,7 @@ def test_lmhead_topk(dtype, M, V, H, k):
     ids = torch.zeros((M, k), dtype=torch.int32, device="cuda")
     lp = torch.zeros((M, k), dtype=torch.float32, device="cuda")
     ws = _ws(E.op_lmhead_workspace(M, V, k))
-    E.op_lmhead(dtype, k, xd, w.cuda(), M, V, H, ids, lp, None, ws)
+    E.op_lmhead(dtype, k, xd, _dev_weight(w, dtype), M, V, H, ids, lp, None, ws)
     torch.cuda.synchronize()
     ids, lp = ids.cpu().numpy(), lp.cpu().numpy()
     for r in range(M):
@@ -136,7 +170,7 @@ def test_lmhead_argmax(dtype, M, V, H):
     mg = torch.zeros(M, dtype=torch.float32, device="cuda")
     logits = torch.zeros((M, V), dtype=torch.float32, device="cuda")
     ws = _ws(E.op_lmhead_workspace(M, V, 0))
-    E.op_lmhead(dtype, 0, xd, w.cuda(), M, V, H, g, mg, logits, ws)
+    E.op_lmhead(dtype, 0, xd, _dev_weight(w, dtype), M, V, H, g, mg, logits, ws)
     torch.cuda.synchronize()
     g, mg, logits = g.cpu().numpy(), mg.cpu().numpy(), logits.cpu().double().numpy()
     assert _rel(logits, lg) < 1e-4
