@@ -165,6 +165,95 @@ __device__ __forceinline__ void proj_core(const ProjArgs& a, int row0, int s_lo,
   }
 }
 
+__device__ __forceinline__ void lds_barrier() {
+  // Workgroup barrier that waits only for this wave's LDS operations: the
+  // weight and activation loads still in flight stay in flight across it.
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// bf16 version of proj_core with a software pipeline the compiler can keep
+// full: chunk c is multiplied while the weight fragments of chunks c+1 and
+// c+2 and the activations of chunk c+1 are in flight. Buffers form static
+// rings (weights 4, activation registers 2, LDS 2) walked by a loop unrolled
+// four times; loads past the last chunk re-read it (cache hits) instead of
+// sitting under a branch, so every wait is a partial vmcnt and one
+// LDS-only barrier per chunk orders the activation buffers.
+template <int MT, int NW, int CS>
+__device__ __forceinline__ void proj_core_bf16(const ProjArgs& a, int row0, int s_lo, int s_hi,
+                                               bf16_t* xs, f32x4 (&acc)[MT]) {
+  using S = ProjShape<bf16_t, MT, NW, CS>;
+  constexpr int PPL = S::MP * S::KCH / S::EPL;   // 16-byte pieces per plane
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const bf16_t* W = (const bf16_t*)a.W;
+  const bf16_t* X = (const bf16_t*)a.X;
+  const bf16_t* wp;
+  int64_t wstep;
+  {
+    const int rb = min(row0, a.rows - 1) >> 4;
+    if ((rb + 1) * 16 <= a.rows) {   // fragment-packed block
+      wp = W + (int64_t)rb * 16 * a.K + lane * S::EPL;
+      wstep = 16 * S::KS;
+    } else {                         // ragged last block: row-major rows
+      wp = W + (int64_t)min(row0 + lr, a.rows - 1) * a.K + lg * S::EPL;
+      wstep = S::KS;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = (s_hi - s_lo + CS - 1) / CS;
+  if (nch <= 0) return;
+  auto xload = [&](uint4 (&xr)[S::NX], int c) {
+    const int cc = min(c, nch - 1);
+#pragma unroll
+    for (int i = 0; i < S::NX; ++i) {
+      const int p = min(tid + i * NW * 64, S::PIECES - 1);
+      const int plane = p / PPL, rem = p % PPL;
+      const int row = min(rem / (S::KCH / S::EPL), a.M - 1), q = rem % (S::KCH / S::EPL);
+      const int col = min((s_lo + cc * CS) * S::KS + q * S::EPL, s_hi * S::KS - S::EPL);
+      xr[i] = ld16(X + plane * a.xlo + (int64_t)row * a.K + col);
+    }
+  };
+  auto wload = [&](uint4 (&w)[CS], int c) {
+    const int cc = min(c, nch - 1);
+#pragma unroll
+    for (int u = 0; u < CS; ++u) w[u] = ld16(wp + (int64_t)min(s_lo + cc * CS + u, s_hi - 1) * wstep);
+  };
+  auto compute = [&](const uint4 (&w)[CS], const bf16_t* x, int c) {
+#pragma unroll
+    for (int u = 0; u < CS; ++u) {
+      if (s_lo + c * CS + u < s_hi) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const uint4 xh = *reinterpret_cast<const uint4*>(x + xs_addr<bf16_t, S::KCH>(16 * t + lr, 4 * u + lg));
+          const uint4 xl = *reinterpret_cast<const uint4*>(x + xs_addr<bf16_t, S::KCH>(S::MP + 16 * t + lr, 4 * u + lg));
+          Mma<bf16_t>::mma(w[u], xh, acc[t]);
+          Mma<bf16_t>::mma(w[u], xl, acc[t]);
+        }
+      }
+    }
+  };
+  uint4 w[4][CS], xr[2][S::NX];
+  xload(xr[0], 0);
+  wload(w[0], 0);
+  xload(xr[1], 1);
+  wload(w[1], 1);
+  stage_store<bf16_t, MT, NW, CS>(xs, xr[0]);
+  lds_barrier();
+  for (int c0 = 0; c0 < nch; c0 += 4) {
+#define PROJ_STEP(J)                                                                  \
+    {                                                                                 \
+      const int c = c0 + J;                                                           \
+      xload(xr[J % 2], c + 2);                                                        \
+      wload(w[(J + 2) % 4], c + 2);                                                   \
+      if (c < nch) compute(w[J], xs + (J % 2) * S::LDS_ELEMS, c);                     \
+      stage_store<bf16_t, MT, NW, CS>(xs + ((J + 1) % 2) * S::LDS_ELEMS, xr[(J + 1) % 2]); \
+      lds_barrier();                                                                  \
+    }
+    PROJ_STEP(0) PROJ_STEP(1) PROJ_STEP(2) PROJ_STEP(3)
+#undef PROJ_STEP
+  }
+}
+
 template <typename T, int MT, int NW, int CS, int EPI>
 __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   using S = ProjShape<T, MT, NW, CS>;
@@ -191,7 +280,10 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
     row0 = (tile * NW + wave) * 16;
   }
   f32x4 acc[MT];
-  proj_core<T, MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc);
+  if constexpr (Opnd<T>::SPLIT)
+    proj_core_bf16<MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc);
+  else
+    proj_core<T, MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc);
 
   if (EPI == EPI_SWIGLU) {
     constexpr int half = NW / 2;
@@ -222,14 +314,23 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
     }
   } else {
     float* Y = a.Y + (int64_t)split * a.plane;
+    // one 16-byte store per lane and m-tile (four consecutive rows) when the
+    // plane allows it: scalar stores cost a measurable share of the kernel
+    const bool vec = (a.ldy & 3) == 0 && (a.plane & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 &&
+                     row0 + 16 <= a.rows;
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int t = 0; t < MT; ++t) {
+      const int m = 16 * t + lr;
+      if (m >= b.M) continue;
+      float* yr = Y + (int64_t)(m0 + m) * a.ldy + row0 + 4 * lg;
+      if (vec) {
+        *reinterpret_cast<f32x4*>(yr) = acc[t];
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = row0 + 4 * lg + j;
-        const int m = 16 * t + lr;
-        if (m < b.M && row < a.rows) Y[(int64_t)(m0 + m) * a.ldy + row] = acc[t][j];
+        for (int j = 0; j < 4; ++j)
+          if (row0 + 4 * lg + j < a.rows) yr[j] = acc[t][j];
       }
+    }
   }
 }
 
@@ -477,11 +578,17 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
 constexpr int KIND_HEAD = 3;
 template <int MT, int KIND> struct Cfg { static constexpr int NW = 8, CS = 4; };
 template <> struct Cfg<1, EPI_PART> { static constexpr int NW = 4, CS = 4; };
-template <> struct Cfg<1, EPI_SWIGLU> { static constexpr int NW = 8, CS = 8; };
+template <> struct Cfg<1, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4; };
 template <> struct Cfg<1, KIND_HEAD> { static constexpr int NW = 4, CS = 16; };
 template <> struct Cfg<2, EPI_PART> { static constexpr int NW = 4, CS = 4; };
-template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 4, CS = 4; };
+template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4; };
 template <> struct Cfg<2, KIND_HEAD> { static constexpr int NW = 4, CS = 8; };
+template <> struct Cfg<3, EPI_PART> { static constexpr int NW = 4, CS = 2; };
+template <> struct Cfg<3, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2; };
+template <> struct Cfg<4, EPI_PART> { static constexpr int NW = 8, CS = 2; };
+template <> struct Cfg<4, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2; };
+template <> struct Cfg<5, EPI_PART> { static constexpr int NW = 4, CS = 2; };
+template <> struct Cfg<5, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2; };
 
 template <int KIND>
 int waves_t(int mt) {
@@ -569,11 +676,17 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
   } else {
     p.n_tiles = (N_rows + rows_per_tile - 1) / rows_per_tile;
     const int steps = K / (dtype == 1 ? 32 : 16);
-    // enough workgroups to fill the chip three times over, while every
-    // split keeps at least four chunks
+    // Split K as little as keeps each workgroup's pipeline long (>= 8 chunks
+    // at one or two m-tiles, 16 above), then widen until the grid covers
+    // every CU, and cap it at four workgroups per CU: each split adds an
+    // [M, N] fp32 plane of HBM writes (measured on the 7B shapes).
     const int cs = chunk_for(p.mt, epi);
+    const int chunks = (steps + cs - 1) / cs;
+    const int target = p.mt <= 2 ? 8 : 16;
     int s = 1;
-    while (p.n_tiles * s < 768 && s < 16 && steps / (2 * s) >= 4 * cs) s *= 2;
+    while (s < 16 && chunks / (2 * s) >= target) s *= 2;
+    while (p.n_tiles * s < 256 && s < 16 && chunks / (2 * s) >= 4) s *= 2;
+    while (p.n_tiles * s > 1024 && s > 1) s /= 2;
     p.splits = s;
   }
   return p;
