@@ -20,11 +20,16 @@ namespace {
 
 constexpr int CHUNK = 64;     // keys per attention workgroup
 
+// Pages hold a power-of-two number of slots (the launchers check it), so
+// slot -> (page, offset) is a shift and a mask, not an integer division.
+__device__ __forceinline__ int page_shift(const KVView& v) { return __ffs(v.page) - 1; }
+
 template <typename T>
 __device__ __forceinline__ T* kv_ptr(const KVView& v, int slot, int sel, int h) {
-  const int pg = v.page_table[slot / v.page];
+  const int sh = page_shift(v);
+  const int pg = v.page_table[slot >> sh];
   return (T*)v.base + (int64_t)pg * v.page_elems +
-         ((int64_t)(sel * v.n_kv + h) * v.page + slot % v.page) * v.d;
+         ((int64_t)(sel * v.n_kv + h) * v.page + (slot & (v.page - 1))) * v.d;
 }
 
 // K (which = 0) or V (which = 1) element of one cache row.
@@ -78,19 +83,56 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   // Every load of this thread is issued before the first LDS store, so the
   // workgroup waits for one memory latency instead of one per piece.
   static_assert(2 * CK * 16 == 8 * 256 && 2 * (CK / 2) * 16 == 4 * 256, "staging assumes 256 threads");
+  // A chunk spans at most two KV pages (the launcher checks page >= CHUNK):
+  // both page-table entries are read once, up front, so no KV address waits
+  // on a per-element table load.
+  const int pgsz = a.kv.page, psh = page_shift(a.kv), pA = k0 >> psh;
+  const int pgA = a.kv.page_table[pA], pgB = a.kv.page_table[(k1 - 1) >> psh];
+  auto kvp = [&](int key, int plane) {
+    const int pg = ((key >> psh) == pA) ? pgA : pgB;
+    return (const bf16_t*)a.kv.base + (int64_t)pg * a.kv.page_elems +
+           ((int64_t)(plane * a.kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
+  };
+  // (query head, row block) pairs; fewer pairs than waves: split keys
+  const int nrb = (a.M + 15) / 16, P = a.group * nrb;
+  int kw = 1;
+  while (P * kw * 2 <= 4 && kw * 2 <= CK / 32) kw *= 2;
+  const int kg = wave / P;                 // key group of this wave (kw > 1)
+  const int nblk = CK / 32 / kw;           // 32-key blocks per key group
+  const int pr0 = kw > 1 ? wave % P : wave, pstep = kw > 1 ? P : 4;
+  const bool active = pr0 < P && kg < kw;
+  // the query fragments and ancestry masks of this wave's next pair; the first
+  // pair's are requested here, before the chunk, so both latencies overlap
+  uint4 qf[4], ql[4];
+  int prehi = 0;
+  uint64_t mk0 = 0, mk1 = 0;
+  auto load_pair = [&](int pr) {
+    const int h = hk * a.group + pr / nrb, rb = pr % nrb;
+    const int rowc = min(rb * 16 + lr, a.M - 1);
+    const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[s] = ld16(qp + 32 * s);
+      ql[s] = ld16(qp + a.qlo + 32 * s);
+    }
+    prehi = a.vis.prehi[rowc];
+    mk0 = a.vis.mask[2 * rowc];
+    mk1 = a.vis.mask[2 * rowc + 1];
+  };
+  if (active) load_pair(pr0);
   uint4 kr[8], va[4], vb[4];
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int i = tid + 256 * it;
     const int plane = i / (CK * 16), key = (i / 16) % CK, c = i % 16;
-    kr[it] = ld16(kv_ptr<bf16_t>(a.kv, min(k0 + key, k1 - 1), plane, hk) + 8 * c);
+    kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c);
   }
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int i = tid + 256 * it;
     const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
-    va[it] = ld16(kv_ptr<bf16_t>(a.kv, min(k0 + 2 * kp, k1 - 1), 2 + plane, hk) + 8 * c);
-    vb[it] = ld16(kv_ptr<bf16_t>(a.kv, min(k0 + 2 * kp + 1, k1 - 1), 2 + plane, hk) + 8 * c);
+    va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c);
+    vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c);
   }
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
@@ -112,27 +154,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- (query head, row block) pairs; fewer pairs than waves: split keys
-  const int nrb = (a.M + 15) / 16, P = a.group * nrb;
-  int kw = 1;
-  while (P * kw * 2 <= 4 && kw * 2 <= CK / 32) kw *= 2;
-  const int kg = wave / P;                 // key group of this wave (kw > 1)
-  const int nblk = CK / 32 / kw;           // 32-key blocks per key group
   float m_keep = -INFINITY, l_keep = 0.f;
   f32x4 o[8];
   int pair_keep = -1;
-  for (int pr = (kw > 1 ? wave % P : wave); pr < P && kg < kw; pr += (kw > 1 ? P : 4)) {
+  for (int pr = pr0; active && pr < P; pr += pstep) {
     const int h = hk * a.group + pr / nrb, rb = pr % nrb;
-    const int row = rb * 16 + lr, rowc = min(row, a.M - 1);
-    uint4 qf[4], ql[4];
-    const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qf[s] = ld16(qp + 32 * s);
-      ql[s] = ld16(qp + a.qlo + 32 * s);
-    }
-    const int prehi = a.vis.prehi[rowc];
-    const uint64_t mk0 = a.vis.mask[2 * rowc], mk1 = a.vis.mask[2 * rowc + 1];
+    const int row = rb * 16 + lr;
     float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -220,6 +247,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       l_keep = l_run;
       pair_keep = pr;
     }
+    if (pr + pstep < P) load_pair(pr + pstep);
   }
   if (kw == 1) return;   // uniform across the workgroup
 
@@ -270,22 +298,50 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+constexpr int ATTN_MAX_CHUNKS = 2048;
+
+// Merges the per-chunk (max, sum, O) partials of one (row, head): the chunk
+// weights exp(m_c - max) are computed once into LDS, then each thread sums
+// its output element over the chunks in chunk order, eight loads in flight.
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* opart, const float* mlpart,
                                                            int n_chunks, int M, int nq, int d,
                                                            T* out, int64_t lo) {
-  const int r = blockIdx.x, h = blockIdx.y;
-  float gm = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) gm = fmaxf(gm, mlpart[(((int64_t)c * M + r) * nq + h) * 2]);
-  for (int j = threadIdx.x; j < d; j += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float* ml = mlpart + (((int64_t)c * M + r) * nq + h) * 2;
-      if (ml[1] == 0.f) continue;
-      const float w = expf(ml[0] - gm);
-      den += w * ml[1];
-      num += w * opart[(((int64_t)c * M + r) * nq + h) * d + j];
+  __shared__ float sw[ATTN_MAX_CHUNKS];
+  __shared__ float red[4];
+  const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t cs = (int64_t)M * nq;   // (row, head) records per chunk
+  const float* ml0 = mlpart + ((int64_t)r * nq + h) * 2;
+  float mx = -INFINITY;
+  for (int c = tid; c < n_chunks; c += 128) mx = fmaxf(mx, ml0[c * cs * 2]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  const float gm = fmaxf(red[0], red[1]);
+  float den = 0.f;
+  for (int c = tid; c < n_chunks; c += 128) {
+    const float m_c = ml0[c * cs * 2], l_c = ml0[c * cs * 2 + 1];
+    const float w = l_c == 0.f ? 0.f : expf(m_c - gm);
+    sw[c] = w;
+    den += w * l_c;
+  }
+  den = wave_sum(den);
+  __syncthreads();   // red[0..1] read above; sw complete below
+  if (lane == 0) red[2 + wave] = den;
+  __syncthreads();
+  den = red[2] + red[3];
+  const float* o0 = opart + ((int64_t)r * nq + h) * d;
+  for (int j = tid; j < d; j += 128) {
+    float num = 0.f;
+    int c = 0;
+    for (; c + 8 <= n_chunks; c += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = o0[(c + u) * cs * d + j];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) num += sw[c + u] * v[u];
     }
+    for (; c < n_chunks; ++c) num += sw[c] * o0[c * cs * d + j];
     Opnd<T>::store(out, lo, ((int64_t)r * nq + h) * d + j, num / den);
   }
 }
@@ -365,13 +421,15 @@ __global__ __launch_bounds__(1024) void resnorm_kernel(float* h, int H, const fl
     p[u] = part + (int64_t)r * H + 4 * j;
   }
   if (S > 0) {
+    // the residual row is requested before the partial planes so the two
+    // loads overlap
+#pragma unroll
+    for (int u = 0; u < NV; ++u)
+      v[u] = (set || !ok[u]) ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(x + 4 * (threadIdx.x + 1024 * u));
     float4 acc[NV];
     plane_sums<NV>(p, ok, S, plane, acc);
 #pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      v[u] = (set || !ok[u]) ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(x + 4 * (threadIdx.x + 1024 * u));
-      add4(v[u], acc[u]);
-    }
+    for (int u = 0; u < NV; ++u) add4(v[u], acc[u]);
   } else {
 #pragma unroll
     for (int u = 0; u < NV; ++u)
@@ -494,9 +552,28 @@ __global__ void draft_input_e1_kernel(const T* E, const int32_t* tok, const floa
   const T* e = E + (int64_t)tok[r] * H;
   const float* f = feat + (int64_t)idx[r] * H;
   const int64_t row = (int64_t)r * 2 * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) {
-    Opnd<T>::store(x, lo, row + i, Elem<T>::to_f(e[i]));
-    Opnd<T>::store(x, lo, row + H + i, f[i]);
+  if constexpr (Opnd<T>::SPLIT) {
+    // bf16 (H a multiple of 8): eight elements per thread and step, one
+    // 16-byte embedding load and two 16-byte feature loads
+    for (int i = threadIdx.x * 8; i < H; i += blockDim.x * 8) {
+      const uint4 ev = ld16(e + i);
+      const float4 f0 = ld4(f + i), f1 = ld4(f + i + 4);
+      const uint32_t w[4] = {ev.x, ev.y, ev.z, ev.w};
+      float4 e0, e1;
+      e0.x = __uint_as_float(w[0] << 16); e0.y = __uint_as_float(w[0] & 0xffff0000u);
+      e0.z = __uint_as_float(w[1] << 16); e0.w = __uint_as_float(w[1] & 0xffff0000u);
+      e1.x = __uint_as_float(w[2] << 16); e1.y = __uint_as_float(w[2] & 0xffff0000u);
+      e1.z = __uint_as_float(w[3] << 16); e1.w = __uint_as_float(w[3] & 0xffff0000u);
+      opnd_store4(x, lo, row + i, e0);
+      opnd_store4(x, lo, row + i + 4, e1);
+      opnd_store4(x, lo, row + H + i, f0);
+      opnd_store4(x, lo, row + H + i + 4, f1);
+    }
+  } else {
+    for (int i = threadIdx.x; i < H; i += blockDim.x) {
+      Opnd<T>::store(x, lo, row + i, Elem<T>::to_f(e[i]));
+      Opnd<T>::store(x, lo, row + H + i, f[i]);
+    }
   }
 }
 
@@ -583,6 +660,7 @@ __global__ void kv_compact_kernel(KVView v, int64_t layer_elems, const int32_t* 
 }  // namespace
 
 int attn_chunk_keys() { return CHUNK; }
+int attn_max_chunks() { return ATTN_MAX_CHUNKS; }
 
 uint64_t attn_part_floats(int max_chunks, int M, int nq, int d) {
   return (uint64_t)max_chunks * M * nq * (d + 2);
@@ -592,6 +670,8 @@ uint64_t attn_part_floats(int max_chunks, int M, int nq, int d) {
   do {                                                        \
     if ((dtype) == 1) { KERNEL_CALL_BF16; } else { KERNEL_CALL_F32; } \
   } while (0)
+
+static bool kv_page_bad(const KVView& v) { return v.page <= 0 || (v.page & (v.page - 1)) != 0; }
 
 hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int M, float* h,
                         hipStream_t st) {
@@ -635,6 +715,7 @@ hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int
 hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int M, int nq, int nkv,
                           int d, const int32_t* pos, const int32_t* slot, const float* cos_t,
                           const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st) {
+  if (kv_page_bad(kv)) return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
   if (d < 4 || d > 1024 || 1024 % d != 0 || ((nq + 2 * nkv) * d) % 4 != 0) return hipErrorInvalidValue;
   const int hpw = 1024 / d;
@@ -648,12 +729,13 @@ hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int
 hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, RowVis vis, int M,
                             int nq, int d, float scale, float* opart, float* mlpart, void* out_t,
                             int64_t olo, hipStream_t st) {
+  if (kv_page_bad(kv)) return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
   const int group = nq / kv.n_kv;
   if (dtype == 1) {
     if (d != 128) return hipErrorInvalidValue;
     const int n_chunks = (vis.key_end - vis.pre_lo + CHUNK - 1) / CHUNK;
-    if (n_chunks <= 0) return hipErrorInvalidValue;
+    if (n_chunks <= 0 || n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK) return hipErrorInvalidValue;
     AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, scale, opart, mlpart};
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
@@ -723,6 +805,7 @@ hipError_t launch_rows_causal(int first, int M, int32_t* pos, int32_t* slot, int
 
 hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int n_layers,
                              const int32_t* L, const int32_t* path, int ctx, hipStream_t st) {
+  if (kv_page_bad(layer0)) return hipErrorInvalidValue;
   DT_DISPATCH(dtype,
               hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv), dim3(512), 0, st, layer0, layer_elems, L, path, ctx, 4),
               hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(n_layers, layer0.n_kv), dim3(256), 0, st, layer0, layer_elems, L, path, ctx, 2));

@@ -135,15 +135,78 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 }
 
 // ---------------------------------------------------------------- reductions
+// Wave-wide reductions: four DPP steps combine the 16 lanes of each row (quad
+// xor 1, quad xor 2, half-row mirror, row mirror: every pairing joins two
+// disjoint groups, so each lane of a row ends with the row's value), then the
+// four row values are read into scalar registers and combined. DPP moves are
+// register-to-register; a __shfl_xor chain goes through the LDS crossbar
+// (ds_bpermute) with a round trip per step. Results are wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1, DPP_QUAD_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141,
+              DPP_MIRROR = 0x140;
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f<DPP_QUAD_XOR1>(v);
+  v += dpp_f<DPP_QUAD_XOR2>(v);
+  v += dpp_f<DPP_HALF_MIRROR>(v);
+  v += dpp_f<DPP_MIRROR>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<DPP_QUAD_XOR1>(v));
+  v = min(v, dpp_i<DPP_QUAD_XOR2>(v));
+  v = min(v, dpp_i<DPP_HALF_MIRROR>(v));
+  v = min(v, dpp_i<DPP_MIRROR>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Wave-wide argmax of (v desc, id asc, src asc): every lane passes its
+// candidate and gets the winner back (wave-uniform). src breaks exact ties
+// (e.g. empty candidates) so the order is total and all lanes agree.
+__device__ __forceinline__ bool argmax_better(float ov, int oi, int os, float v, int i, int s) {
+  return ov > v || (ov == v && (oi < i || (oi == i && os < s)));
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i, int& s) {
+  const float ov = dpp_f<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i), os = dpp_i<CTRL>(s);
+  if (argmax_better(ov, oi, os, v, i, s)) { v = ov; i = oi; s = os; }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i, int& s) {
+  argmax_step<DPP_QUAD_XOR1>(v, i, s);
+  argmax_step<DPP_QUAD_XOR2>(v, i, s);
+  argmax_step<DPP_HALF_MIRROR>(v, i, s);
+  argmax_step<DPP_MIRROR>(v, i, s);
+  float bv = lane_f(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0), bs = __builtin_amdgcn_readlane(s, 0);
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  for (int r = 1; r < 4; ++r) {
+    const float rv = lane_f(v, 16 * r);
+    const int ri = __builtin_amdgcn_readlane(i, 16 * r), rs = __builtin_amdgcn_readlane(s, 16 * r);
+    if (argmax_better(rv, ri, rs, bv, bi, bs)) { bv = rv; bi = ri; bs = rs; }
+  }
+  v = bv;
+  i = bi;
+  s = bs;
 }
 
 // Total order of floats as unsigned keys (ascending float -> ascending key).

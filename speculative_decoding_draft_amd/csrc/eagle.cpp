@@ -166,6 +166,7 @@ bool derive(const eagle_config* c, Derived* z, std::string* why) {
   z->max_pos = std::max(z->t_slots, z->d_slots) + z->D + 2;
   const int ck = attn_chunk_keys();
   z->max_chunks = (std::max(z->t_pages, z->d_pages) * KV_PAGE + ck - 1) / ck + 1;
+  if (z->max_chunks > attn_max_chunks()) return fail(why, "max_ctx too large for the attention combine (%d key chunks max)", attn_max_chunks());
   return true;
 }
 

@@ -357,6 +357,12 @@ __global__ __launch_bounds__(256) void pack_frag_kernel(const bf16_t* __restrict
 }
 
 // ---------------------------------------------------------------- LM head
+// Per-tile top-k record of the draft LM head: {max, sum of exp, k values,
+// k ids}, padded to a multiple of four floats so a row's records (stored
+// row-major: record (m, tile) at (m * n_tiles + tile) * rec) copy with
+// 16-byte loads.
+__host__ __device__ constexpr int topk_record(int k) { return (2 + 2 * k + 3) & ~3; }
+
 struct HeadArgs {
   ProjArgs p;     // W = LM head [V, H], X = features
   int k;
@@ -395,7 +401,7 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(HeadArgs h) {
   constexpr int RPL = (NW * 16) / 64;
   static_assert(RPL * 64 == NW * 16, "tile rows must be a multiple of the wave width");
   static_assert(NW * 16 * S::MP * 4 <= (int)sizeof(xs), "row values must fit the staging buffer");
-  const int stride = TOPK ? (2 + 2 * h.k) : 3;
+  const int stride = TOPK ? topk_record(h.k) : 3;
   for (int m = wave; m < a.M; m += NW) {
     float v[RPL];
     int id[RPL];
@@ -406,19 +412,16 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(HeadArgs h) {
       v[u] = ok ? vals[n * S::MP + m] : -INFINITY;
       id[u] = ok ? tile * R + n : 0x7fffffff;
     }
-    float* out = h.part + ((int64_t)tile * a.M + m) * stride;
+    float* out = TOPK ? h.part + ((int64_t)m * gridDim.x + tile) * stride
+                      : h.part + ((int64_t)tile * a.M + m) * stride;
     if (!TOPK) {
       float bv = v[0];
       int bi = id[0];
 #pragma unroll
       for (int u = 1; u < RPL; ++u)
         if (v[u] > bv || (v[u] == bv && id[u] < bi)) { bv = v[u]; bi = id[u]; }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
+      int bl = lane;
+      wave_argmax(bv, bi, bl);
       float lv = -INFINITY;
 #pragma unroll
       for (int u = 0; u < RPL; ++u)
@@ -442,12 +445,8 @@ __global__ __launch_bounds__(NW * 64) void lmhead_kernel(HeadArgs h) {
 #pragma unroll
         for (int u = 1; u < RPL; ++u)
           if (v[u] > bv || (v[u] == bv && id[u] < bi)) { bv = v[u]; bi = id[u]; }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          const float ov = __shfl_xor(bv, o);
-          const int oi = __shfl_xor(bi, o);
-          if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-        }
+        int bl = lane;
+        wave_argmax(bv, bi, bl);
         if (lane == 0) { out[2 + i] = bv; out[2 + h.k + i] = __int_as_float(bi); }
 #pragma unroll
         for (int u = 0; u < RPL; ++u)
@@ -489,84 +488,144 @@ __global__ __launch_bounds__(256) void argmax_combine(const float* part, int n_t
   if (threadIdx.x == 0) { g[m] = si[0]; margin[m] = s1[0] - s2[0]; }
 }
 
-// one workgroup per row: global max, sum of exp, and the k best (val desc, id asc)
+// One workgroup of four waves per row: the global max and log-sum-exp over
+// the vocabulary tiles, then the k best (val desc, id asc) merged from the
+// tiles' sorted lists. The row's records are first copied to LDS with
+// 16-byte loads, sixteen in flight per thread (in segments when they exceed
+// the buffer). A threshold T, the k-th largest of the tile maxima, bounds the
+// merge: k distinct values are >= T, so no value below T is among the k
+// best, and since every tile list is sorted a tile stops at its first
+// candidate under T. Each thread keeps its best candidates in registers
+// (bubble insertion with static indices); each wave pops its k best with
+// wave-wide argmax rounds (shuffles), and wave 0 merges the four lists.
 __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_tiles, int M, int k,
                                                     int32_t* ids, float* logp) {
-  const int m = blockIdx.x;
-  const int stride = 2 + 2 * k;
-  __shared__ float sred[256];
-  __shared__ float s_gmax, s_lse;
-  float mx = -INFINITY;
-  for (int t = threadIdx.x; t < n_tiles; t += 256) mx = fmaxf(mx, part[((int64_t)t * M + m) * stride]);
-  sred[threadIdx.x] = mx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) sred[threadIdx.x] = fmaxf(sred[threadIdx.x], sred[threadIdx.x + o]);
+  constexpr int KMAX = 16, BUF = 16384, NT = 256, NWV = NT / 64;
+  __shared__ __attribute__((aligned(16))) float buf[BUF];
+  __shared__ float s_red[2 * NWV];
+  __shared__ float s_cv[NWV * KMAX];
+  __shared__ int s_ci[NWV * KMAX];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rec = topk_record(k), seg = BUF / rec;
+  const float* row = part + (int64_t)m * n_tiles * rec;
+  auto stage = [&](int t0, int nt) {
+    __syncthreads();   // earlier reads of buf are done
+    const float4* src = reinterpret_cast<const float4*>(row + (int64_t)t0 * rec);
+    float4* dst = reinterpret_cast<float4*>(buf);
+    const int n4 = nt * rec / 4;
+    for (int i0 = 0; i0 < n4; i0 += NT * 16) {
+      // all sixteen loads are issued before the first store: threads past
+      // the end re-copy the last piece (same value, same place) instead of
+      // branching, so no load is sunk into a conditional store
+      float4 v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = src[min(i0 + NT * u + tid, n4 - 1)];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) dst[min(i0 + NT * u + tid, n4 - 1)] = v[u];
+    }
     __syncthreads();
+  };
+  float lv[KMAX];
+  int li[KMAX];
+  auto reset = [&]() {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) { lv[i] = -INFINITY; li[i] = 0x7fffffff; }
+  };
+  // (value desc, id asc) insertion of (cv, ci) into the sorted list lv/li
+  auto insert = [&](float cv, int ci) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if (i < k) {
+        const bool better = cv > lv[i] || (cv == lv[i] && ci < li[i]);
+        const float tv = better ? lv[i] : cv;
+        const int ti = better ? li[i] : ci;
+        lv[i] = better ? cv : lv[i];
+        li[i] = better ? ci : li[i];
+        cv = tv;
+        ci = ti;
+      }
+    }
+  };
+  // k rounds of a wave-wide argmax over the lanes' list heads; emit(r, v, id)
+  auto pop_k = [&](auto&& emit) {
+    for (int r = 0; r < k; ++r) {
+      float bv = lv[0];
+      int bi = li[0], bl = lane;
+      wave_argmax(bv, bi, bl);
+      emit(r, bv, bi);
+      if (lane == bl) {
+#pragma unroll
+        for (int i = 0; i + 1 < KMAX; ++i) { lv[i] = lv[i + 1]; li[i] = li[i + 1]; }
+        lv[KMAX - 1] = -INFINITY;
+        li[KMAX - 1] = 0x7fffffff;
+      }
+    }
+  };
+  // every wave's k best go to LDS; wave 0 then holds them one per lane
+  // (4k <= 64) and pops the k best of the workgroup
+  auto merge_waves = [&](auto&& emit) {
+    pop_k([&](int r, float v, int id) {
+      if (lane == 0) { s_cv[wave * KMAX + r] = v; s_ci[wave * KMAX + r] = id; }
+    });
+    __syncthreads();
+    if (wave == 0) {
+      reset();
+      const int w = lane / KMAX, r = lane % KMAX;
+      if (r < k) { lv[0] = s_cv[w * KMAX + r]; li[0] = s_ci[w * KMAX + r]; }
+      pop_k(emit);
+    }
+    __syncthreads();
+  };
+  // pass 1: the global max and the threshold T from the tile maxima
+  reset();
+  float mx = -INFINITY, kth = -INFINITY;   // kth: this thread's k-th largest so far
+  for (int t0 = 0; t0 < n_tiles; t0 += seg) {
+    const int nt = min(seg, n_tiles - t0);
+    stage(t0, nt);
+    for (int t = tid; t < nt; t += NT) {
+      const float v = buf[t * rec];
+      mx = fmaxf(mx, v);
+      if (v > kth) {
+        insert(v, t0 + t);
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i)
+          if (i == k - 1) kth = lv[i];
+      }
+    }
   }
-  if (threadIdx.x == 0) s_gmax = sred[0];
-  __syncthreads();
-  const float gmax = s_gmax;
+  mx = wave_max(mx);
+  if (lane == 0) s_red[wave] = mx;
+  merge_waves([&](int r, float v, int) { if (r == k - 1 && lane == 0) s_red[NWV] = v; });
+  const float gmax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float thr = s_red[NWV];
+  // pass 2: sum of exp and the k best among candidates >= T
+  reset();
   float se = 0.f;
-  for (int t = threadIdx.x; t < n_tiles; t += 256) {
-    const float* p = part + ((int64_t)t * M + m) * stride;
-    se += p[1] * expf(p[0] - gmax);
-  }
-  __syncthreads();
-  sred[threadIdx.x] = se;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if ((int)threadIdx.x < o) sred[threadIdx.x] = sred[threadIdx.x] + sred[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) s_lse = logf(sred[0]);
-  __syncthreads();
-  float lv[16];
-  int li[16];
-  for (int i = 0; i < k; ++i) { lv[i] = -INFINITY; li[i] = 0x7fffffff; }
-  for (int t = threadIdx.x; t < n_tiles; t += 256) {
-    const float* p = part + ((int64_t)t * M + m) * stride;
-    for (int i = 0; i < k; ++i) {
-      const float v = p[2 + i];
-      const int id = __float_as_int(p[2 + k + i]);
-      if (id == 0x7fffffff) break;
-      if (v > lv[k - 1] || (v == lv[k - 1] && id < li[k - 1])) {
-        int j = k - 1;
-        while (j > 0 && (v > lv[j - 1] || (v == lv[j - 1] && id < li[j - 1]))) {
-          lv[j] = lv[j - 1]; li[j] = li[j - 1]; --j;
-        }
-        lv[j] = v; li[j] = id;
-      } else {
-        break;   // the tile's list is sorted: nothing later can enter
+  for (int t0 = 0; t0 < n_tiles; t0 += seg) {
+    const int nt = min(seg, n_tiles - t0);
+    if (n_tiles > seg) stage(t0, nt);   // a single segment is still staged
+    for (int t = tid; t < nt; t += NT) {
+      const float* p = buf + t * rec;
+      se += p[1] * expf(p[0] - gmax);
+      for (int c = 0; c < k; ++c) {
+        const float cv = p[2 + c];
+        const int ci = __float_as_int(p[2 + k + c]);
+        if (ci == 0x7fffffff || cv < thr) break;   // tile lists are sorted
+        insert(cv, ci);
       }
     }
   }
-  __shared__ float hv[256];
-  __shared__ int hi[256], ht[256];
-  int head = 0;
-  for (int r = 0; r < k; ++r) {
-    hv[threadIdx.x] = head < k ? lv[head] : -INFINITY;
-    hi[threadIdx.x] = head < k ? li[head] : 0x7fffffff;
-    ht[threadIdx.x] = threadIdx.x;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-      if ((int)threadIdx.x < o) {
-        const float c = hv[threadIdx.x + o];
-        const int ci = hi[threadIdx.x + o];
-        if (c > hv[threadIdx.x] || (c == hv[threadIdx.x] && ci < hi[threadIdx.x])) {
-          hv[threadIdx.x] = c; hi[threadIdx.x] = ci; ht[threadIdx.x] = ht[threadIdx.x + o];
-        }
-      }
-      __syncthreads();
+  se = wave_sum(se);
+  __syncthreads();   // s_red reads above are done
+  if (lane == 0) s_red[wave] = se;
+  __syncthreads();
+  const float lse = logf((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
+  merge_waves([&](int r, float v, int id) {
+    if (lane == 0) {
+      ids[m * k + r] = id;
+      logp[m * k + r] = (v - gmax) - lse;
     }
-    if (threadIdx.x == 0) {
-      ids[m * k + r] = hi[0];
-      logp[m * k + r] = (hv[0] - gmax) - s_lse;
-    }
-    const int winner = ht[0];
-    __syncthreads();
-    if ((int)threadIdx.x == winner) ++head;
-  }
+  });
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -721,7 +780,7 @@ hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t
 uint64_t lmhead_part_floats(int M, int V, int k) {
   if (M > 80) M = 64;
   const int n_tiles = (V + head_rows(M) - 1) / head_rows(M);
-  return (uint64_t)n_tiles * M * (k > 0 ? (2 + 2 * k) : 3);
+  return (uint64_t)n_tiles * M * (k > 0 ? topk_record(k) : 3);
 }
 
 static hipError_t head_launch(int dtype, bool topk, const void* W, const void* x, int64_t xlo, int M, int V,

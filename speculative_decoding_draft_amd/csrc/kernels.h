@@ -89,6 +89,8 @@ hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int
                           const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st);
 uint64_t attn_part_floats(int max_chunks, int M, int nq, int d);
 int attn_chunk_keys();
+// Most key chunks one attention call may split a row's keys into.
+int attn_max_chunks();
 hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, RowVis vis, int M,
                             int nq, int d, float scale, float* opart, float* mlpart, void* out_t,
                             int64_t olo, hipStream_t st);

@@ -239,8 +239,7 @@ __global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g,
     int found = 0x7fffffff;
     for (int r = 1 + lane; r < n; r += 64)
       if (t.v_parent[r] == cur && t.v_tok[r] == want) found = min(found, r);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) found = min(found, __shfl_xor(found, o));
+    found = wave_min_i(found);
     if (found == 0x7fffffff) break;
     if (lane == 0) {
       acc[2 + L] = found;
