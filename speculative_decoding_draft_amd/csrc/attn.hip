@@ -163,6 +163,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int pmin = wave_min_i(prehi);   // smallest visible-prefix end of the pair's rows
     for (int bi = 0; bi < nblk; ++bi) {
       const int kb0 = (kg * nblk + bi) * 32;   // block start within the chunk
       f32x4 sc[2];
@@ -182,24 +183,33 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       }
       float p[8];
       float bm = -INFINITY;
+      if (k0 + kb0 + 32 <= min(pmin, k1)) {
+        // every key of the block is in every row's visible prefix
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = k0 + kb0 + 8 * g + 4 * hh + e;
-          const bool ok = key < k1 && row_sees(a.vis, prehi, mk0, mk1, key);
-          p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
-          bm = fmaxf(bm, p[4 * hh + e]);
+        for (int i = 0; i < 8; ++i) {
+          p[i] = sc[i >> 2][i & 3] * a.scale;
+          bm = fmaxf(bm, p[i]);
         }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = k0 + kb0 + 8 * g + 4 * hh + e;
+            const bool ok = key < k1 && row_sees(a.vis, prehi, mk0, mk1, key);
+            p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
+            bm = fmaxf(bm, p[4 * hh + e]);
+          }
+      }
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       const float m_new = fmaxf(m_run, bm);
       float alpha = 1.f, ps = 0.f;
       if (m_new != -INFINITY) {
-        alpha = expf(m_run - m_new);
+        alpha = exp2f(m_run - m_new);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          p[i] = expf(p[i] - m_new);
+          p[i] = exp2f(p[i] - m_new);
           ps += p[i];
         }
         m_run = m_new;
@@ -212,14 +222,14 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       l_run = l_run * alpha + ps;
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] *= alpha;
-      bf16_t ph[8], pl[8];
+      uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ph[i] = f32_to_bf16(p[i]);
-        pl[i] = f32_to_bf16(p[i] - bf16_to_f32(ph[i]));
+      for (int j = 0; j < 4; ++j) {
+        ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
       }
-      const uint4 phi = *reinterpret_cast<const uint4*>(ph);
-      const uint4 plo = *reinterpret_cast<const uint4*>(pl);
+      const uint4 phi = uint4{ph[0], ph[1], ph[2], ph[3]};
+      const uint4 plo = uint4{pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
         const uint4 va = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     float lsum = 0.f, wk[4];
     for (int k = 0; k < kw; ++k) {
       const float mk = mm[((wave + k * P) * 16 + lr) * 2];
-      wk[k] = mk == -INFINITY ? 0.f : expf(mk - gm);
+      wk[k] = mk == -INFINITY ? 0.f : exp2f(mk - gm);
       lsum += wk[k] * mm[((wave + k * P) * 16 + lr) * 2 + 1];
     }
     if (row < a.M) {
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* opart, c
   float den = 0.f;
   for (int c = tid; c < n_chunks; c += 128) {
     const float m_c = ml0[c * cs * 2], l_c = ml0[c * cs * 2 + 1];
-    const float w = l_c == 0.f ? 0.f : expf(m_c - gm);
+    const float w = l_c == 0.f ? 0.f : exp2f(m_c - gm);
     sw[c] = w;
     den += w * l_c;
   }
@@ -736,7 +746,9 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
     if (d != 128) return hipErrorInvalidValue;
     const int n_chunks = (vis.key_end - vis.pre_lo + CHUNK - 1) / CHUNK;
     if (n_chunks <= 0 || n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK) return hipErrorInvalidValue;
-    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, scale, opart, mlpart};
+    // scores are taken in log2 units (scale * log2 e) so the softmax uses the
+    // native exp2; chunk maxima in mlpart are in the same units
+    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, scale * 1.4426950408889634f, opart, mlpart};
     hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -16,12 +16,20 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
-// Round-to-nearest-even fp32 -> bf16 (finite inputs).
+// Round-to-nearest-even fp32 -> bf16 with the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32; the same bits as adding 0x7fff plus the lsb to the
+// fp32 pattern and truncating, for finite inputs).
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
+// Two values in one 32-bit word, element a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_hw v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf16_lo_f(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Element type T of weights / KV / matrix operands: float or bf16_t.
 template <typename T> struct Elem;
@@ -64,11 +72,8 @@ __device__ __forceinline__ void opnd_store4(bf16_t* p, int64_t lo, int64_t i, fl
   uint32_t hw[2], lw[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
-    const bf16_t h0 = f32_to_bf16(f[2 * e]), h1 = f32_to_bf16(f[2 * e + 1]);
-    const bf16_t l0 = f32_to_bf16(f[2 * e] - bf16_to_f32(h0));
-    const bf16_t l1 = f32_to_bf16(f[2 * e + 1] - bf16_to_f32(h1));
-    hw[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lw[e] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    hw[e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+    lw[e] = pack_bf16x2(f[2 * e] - bf16_lo_f(hw[e]), f[2 * e + 1] - bf16_hi_f(hw[e]));
   }
   *reinterpret_cast<uint2*>(p + i) = make_uint2(hw[0], hw[1]);
   *reinterpret_cast<uint2*>(p + lo + i) = make_uint2(lw[0], lw[1]);
