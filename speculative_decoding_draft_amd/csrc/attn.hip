@@ -3,9 +3,10 @@
 // input assembly, row gathers, KV compaction).
 //
 // bf16 attention (head_dim 128): one workgroup of four waves per (KV head,
-// chunk of 64 keys). The chunk's K (hi and lo planes, XOR-swizzled rows) and
-// V^T (hi and lo) are staged in LDS once and shared by every query head of
-// the GQA group and every block of 16 query rows. Per 32-key block a wave
+// chunk of 64 keys, group of four (query head, 16-row block) pairs). The
+// chunk's K (hi and lo planes, XOR-swizzled rows) and V^T (hi and lo) are
+// staged in LDS once and shared by the group's pairs; a GQA head with more
+// pairs spreads them over several workgroups. Per 32-key block a wave
 // computes S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA; keys are
 // read in an order that makes each lane's 8 scores exactly the P^T operand
 // of the PV product, so P never leaves registers. Q, K, V and P are carried
@@ -60,6 +61,7 @@ struct AttnArgs {
   KVView kv;
   RowVis vis;
   int M, nq, group;
+  int ppg;   // (query head, row block) pairs per workgroup
   float scale;
   float* opart;
   float* mlpart;
@@ -94,7 +96,11 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
            ((int64_t)(plane * a.kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
   };
   // (query head, row block) pairs; fewer pairs than waves: split keys
-  const int nrb = (a.M + 15) / 16, P = a.group * nrb;
+  // pairs of this workgroup: group blockIdx.z of a.ppg (query head, row
+  // block) pairs; a GQA head with many pairs and few chunks spreads its pairs
+  // over several workgroups
+  const int nrb = (a.M + 15) / 16, pbase = blockIdx.z * a.ppg;
+  const int P = min(a.ppg, a.group * nrb - pbase);
   int kw = 1;
   while (P * kw * 2 <= 4 && kw * 2 <= CK / 32) kw *= 2;
   const int kg = wave / P;                 // key group of this wave (kw > 1)
@@ -107,7 +113,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   int prehi = 0;
   uint64_t mk0 = 0, mk1 = 0;
   auto load_pair = [&](int pr) {
-    const int h = hk * a.group + pr / nrb, rb = pr % nrb;
+    const int h = hk * a.group + (pbase + pr) / nrb, rb = (pbase + pr) % nrb;
     const int rowc = min(rb * 16 + lr, a.M - 1);
     const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
 #pragma unroll
@@ -158,7 +164,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   f32x4 o[8];
   int pair_keep = -1;
   for (int pr = pr0; active && pr < P; pr += pstep) {
-    const int h = hk * a.group + pr / nrb, rb = pr % nrb;
+    const int h = hk * a.group + (pbase + pr) / nrb, rb = (pbase + pr) % nrb;
     const int row = rb * 16 + lr;
     float m_run = -INFINITY, l_run = 0.f;
 #pragma unroll
@@ -278,7 +284,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
   if (pair_keep >= 0 && kg == 0) {
-    const int h = hk * a.group + pair_keep / nrb, rb = pair_keep % nrb;
+    const int h = hk * a.group + (pbase + pair_keep) / nrb, rb = (pbase + pair_keep) % nrb;
     const int row = rb * 16 + lr;
     float gm = -INFINITY;
     for (int k = 0; k < kw; ++k) gm = fmaxf(gm, mm[((wave + k * P) * 16 + lr) * 2]);
@@ -748,8 +754,16 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
     if (n_chunks <= 0 || n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK) return hipErrorInvalidValue;
     // scores are taken in log2 units (scale * log2 e) so the softmax uses the
     // native exp2; chunk maxima in mlpart are in the same units
-    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, scale * 1.4426950408889634f, opart, mlpart};
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv), dim3(256), 0, st, a);
+    // split a head's pairs over more workgroups only while the (chunk, KV
+    // head) grid is short of two workgroups per CU: every extra group stages
+    // the chunk again
+    const int pairs = group * ((M + 15) / 16);
+    const int want = (512 + n_chunks * kv.n_kv - 1) / (n_chunks * kv.n_kv);
+    int n_groups = std::max(1, std::min((pairs + 3) / 4, want));
+    const int ppg = (pairs + n_groups - 1) / n_groups;
+    n_groups = (pairs + ppg - 1) / ppg;
+    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, ppg, scale * 1.4426950408889634f, opart, mlpart};
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv, n_groups), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(M, nq), dim3(128), 0, st, opart, mlpart,
