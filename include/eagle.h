@@ -31,6 +31,10 @@
  *  - Memory: the library allocates no device memory. The caller allocates
  *    the three device buffers whose sizes eagle_query reports and keeps them
  *    alive until eagle_free. Host pointers are only read during the call.
+ *    eagle_load allocates one small pinned host block (freed by eagle_free)
+ *    through which eagle_verify receives the acceptance result; eagle_verify
+ *    returns once that result is known, with its catch-up work still queued
+ *    on the stream.
  *  - Errors: every call returns an eagle_status. Argument, state and
  *    capacity checks run on the host before any device work, so a rejected
  *    call leaves the context unchanged. After EAGLE_E_HIP or EAGLE_E_DEVICE

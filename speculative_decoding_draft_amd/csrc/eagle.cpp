@@ -265,6 +265,11 @@ struct eagle_ctx {
   uint64_t* rmask;
   TreeDev t;
   TreeParams tp;
+  // acceptance result in pinned, coherent host memory: [0] tag, [1] L,
+  // [2 ..] committed tokens; written by the acceptance kernel through hres_dev
+  int32_t* hres = nullptr;
+  int32_t* hres_dev = nullptr;
+  int32_t verify_tag = 0;
   // host state
   int state = ST_EMPTY;
   int ctx_len = 0;
@@ -281,6 +286,9 @@ struct eagle_ctx {
   std::vector<hipEvent_t> free_ev;     // events ready for reuse
   std::vector<hipEvent_t> all_ev;      // every event created; destroyed with the context
   eagle_profile ptot{};                // totals of the records already read back
+  ~eagle_ctx() {
+    if (hres) (void)hipHostFree(hres);
+  }
 };
 
 namespace {
@@ -709,10 +717,14 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
   c->W = (char*)bufs->weights;
   c->KV = (char*)bufs->kv;
   c->S = (char*)bufs->scratch;
-  if (hipGetDevice(&c->device) != hipSuccess) {
+  if (hipGetDevice(&c->device) != hipSuccess ||
+      hipHostMalloc((void**)&c->hres, sizeof(int32_t) * (2 + EAGLE_MAX_DEPTH + 2),
+                    hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
+      hipHostGetDevicePointer((void**)&c->hres_dev, c->hres, 0) != hipSuccess) {
     delete c;
     return EAGLE_E_HIP;
   }
+  std::memset(c->hres, 0, sizeof(int32_t) * (2 + EAGLE_MAX_DEPTH + 2));
   // weights
   auto ptr = [&](int kind, int group, int layer) -> const void* {
     for (const eagle_tensor& e : tab)
@@ -923,6 +935,25 @@ eagle_status eagle_draft_tree(eagle_ctx* c, eagle_tree* out) {
   return EAGLE_OK;
 }
 
+namespace {
+// Spins until the acceptance kernel has posted `tag` to the pinned result
+// block. Every 4096 polls it asks whether the stream has drained: a drained
+// stream without the tag (an earlier kernel failed) or a stream error ends
+// the wait with an error instead of spinning forever.
+eagle_status wait_result(eagle_ctx* c, int32_t tag) {
+  for (uint32_t spin = 1;; ++spin) {
+    if (__atomic_load_n(c->hres, __ATOMIC_ACQUIRE) == tag) return EAGLE_OK;
+    if ((spin & 4095) == 0) {
+      const hipError_t q = hipStreamQuery(c->st);
+      if (q == hipErrorNotReady) continue;
+      if (__atomic_load_n(c->hres, __ATOMIC_ACQUIRE) == tag) return EAGLE_OK;
+      if (q != hipSuccess) return set_err(c, EAGLE_E_HIP, "stream failed during verify: %s", hipGetErrorString(q));
+      return set_err(c, EAGLE_E_DEVICE, "acceptance result was not posted");
+    }
+  }
+}
+}  // namespace
+
 eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_tokens,
                           int32_t* n_committed) {
   SCHK(check_ready(c));
@@ -965,17 +996,21 @@ eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_
            launch_lmhead_argmax(z.dt, c->lm, c->xop, c->xlo, Mv, z.V, z.H, c->hpart, c->g,
                                 c->margin, c->debug ? c->logits : nullptr, c->st));
   c->last_verify_rows = Mv;
-  PROFILED(EAGLE_PROF_TREE, 0.0, launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->st));
+  // The acceptance kernel commits the tokens into seq on the device and posts
+  // (L, tokens) to pinned host memory under a fresh tag. The host waits for
+  // that tag only, so the KV compaction queued behind it overlaps the wait and
+  // the catch-up launches queue behind it with no stream drain in between.
+  const int32_t tag = c->verify_tag = c->verify_tag == INT32_MAX ? 1 : c->verify_tag + 1;
+  PROFILED(EAGLE_PROF_TREE, 0.0,
+           launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->seq + ctx + 1,
+                         c->hres_dev, tag, c->st));
   PROFILED(EAGLE_PROF_KV, 0.0,
            launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, c->acc, c->acc + 2, ctx, c->st));
-  int32_t acc[2 + EAGLE_MAX_DEPTH + 2];
+  SCHK(wait_result(c, tag));
   int32_t nt[EAGLE_MAX_DEPTH + 2];
-  HCHK(hipMemcpyAsync(acc, c->acc, sizeof(acc), hipMemcpyDeviceToHost, c->st));
-  HCHK(hipMemcpyAsync(nt, c->new_tok, sizeof(nt), hipMemcpyDeviceToHost, c->st));
-  HCHK(hipStreamSynchronize(c->st));
-  const int L = acc[0];
+  const int L = c->hres[1];
   if (L < 0 || L > z.D) return set_err(c, EAGLE_E_DEVICE, "acceptance length %d out of range", L);
-  HCHK(hipMemcpyAsync(c->seq + ctx + 1, c->new_tok, 4 * (L + 1), hipMemcpyDeviceToDevice, c->st));
+  std::memcpy(nt, c->hres + 2, sizeof(int32_t) * (L + 1));
   const int ctx_new = ctx + L + 1;
   if (!plain_mode(c)) {
     const float* feat = c->tfeat;

@@ -154,5 +154,8 @@ hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root
 // Greedy acceptance walk over the verify rows given the target's choices g.
 // acc[0] = L, acc[1] = bonus, acc[2..2+L) = accepted rows; new_tok[0..L]
 // = the committed tokens; cu_src[0..L] = feature rows feeding the catch-up.
+// The tokens are also written to seq_out[0..L]. host (mapped host memory, or
+// NULL) receives host[1] = L and host[2..2+L] = the tokens, then host[0] = tag.
 hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
-                         int32_t* new_tok, int32_t* cu_src, hipStream_t st);
+                         int32_t* new_tok, int32_t* cu_src, int32_t* seq_out, int32_t* host,
+                         int32_t tag, hipStream_t st);

@@ -229,8 +229,15 @@ __global__ __launch_bounds__(128) void tree_masks_kernel(TreeDev t, int n_rows, 
   build_masks(t, n_rows, ctx);
 }
 
+// Walks the verified tree from the root: at each step the child whose token
+// equals the target's greedy choice at the current row is accepted. Besides
+// the device copies (acc, new_tok, cu_src) lane 0 writes the committed tokens
+// into the sequence (seq_out) and, when `host` is not NULL, the length and the
+// tokens into mapped host memory, then raises host[0] to `tag` after a
+// system-scope fence, so the host can read the result while the stream runs on.
 __global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g, int max_depth,
-                                                    int32_t* acc, int32_t* new_tok, int32_t* cu_src) {
+                                                    int32_t* acc, int32_t* new_tok, int32_t* cu_src,
+                                                    int32_t* seq_out, int32_t* host, int32_t tag) {
   const int lane = threadIdx.x;
   const int n = t.counts[3];
   int cur = 0, L = 0;
@@ -245,15 +252,25 @@ __global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g,
       acc[2 + L] = found;
       new_tok[L] = want;
       cu_src[L + 1] = found;
+      seq_out[L] = want;
+      if (host) host[2 + L] = want;
     }
     cur = found;
     ++L;
   }
   if (lane == 0) {
+    const int bonus = g[cur];
     acc[0] = L;
-    acc[1] = g[cur];
-    new_tok[L] = g[cur];
+    acc[1] = bonus;
+    new_tok[L] = bonus;
     cu_src[0] = 0;
+    seq_out[L] = bonus;
+    if (host) {
+      host[2 + L] = bonus;
+      host[1] = L;
+      __threadfence_system();
+      *reinterpret_cast<volatile int32_t*>(host) = tag;
+    }
   }
 }
 
@@ -278,7 +295,9 @@ hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root
 }
 
 hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
-                         int32_t* new_tok, int32_t* cu_src, hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, t, g, max_depth, acc, new_tok, cu_src);
+                         int32_t* new_tok, int32_t* cu_src, int32_t* seq_out, int32_t* host,
+                         int32_t tag, hipStream_t st) {
+  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, t, g, max_depth, acc, new_tok, cu_src,
+                     seq_out, host, tag);
   return hipGetLastError();
 }
