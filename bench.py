@@ -163,7 +163,7 @@ def main():
     import speculative_decoding_draft_amd as E
 
     w = synth.workloads.get(args.config)
-    cycles_needed = args.warmup + args.steps + max(0, args.profile_cycles) + 2
+    cycles_needed = args.warmup + args.steps + max(0, args.profile_cycles) + 2 + 5   # + speedup-model cycles
     max_new = max(w["gen"], cycles_needed * (w["depth"] + 1))
     max_ctx = w["prompt_len"] + max_new + w["depth"] + 2
     eng = E.Engine(w, max_ctx=max_ctx)
@@ -171,8 +171,15 @@ def main():
     torch.cuda.synchronize()
     eng.load()
     prompt = synth.prompt(args.seed, w["prompt_len"], w["vocab"])
+    # the first prefill loads the kernels; the second (it restarts the
+    # sequence) is the timed one
     eng.prefill(prompt)
-    print(f"# {args.config}: prefill done, ctx {len(prompt)}", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    eng.prefill(prompt)
+    torch.cuda.synchronize()
+    prefill_ms = (time.perf_counter() - tp0) * 1e3
+    print(f"# {args.config}: prefill done, ctx {len(prompt)}, {prefill_ms:.1f} ms", file=sys.stderr, flush=True)
 
     def cycle():
         eng.draft_tree(want=False)
@@ -213,6 +220,27 @@ def main():
             cycle()
         prof = eng.profile_read()
         eng.profile(False)
+    # draft-pass and target-pass times for the speedup model: D - 1 tree
+    # passes in eagle_draft_tree; the target pass plus one catch-up draft
+    # pass in eagle_verify
+    model = None
+    if w["depth"] >= 2 and w["budget"] > 0:
+        from speculative_decoding_draft_amd import speedup as spm
+        td = tv = 0.0
+        n_model = 5
+        for _ in range(n_model):
+            torch.cuda.synchronize()
+            a0 = time.perf_counter()
+            eng.draft_tree(want=False)
+            torch.cuda.synchronize()
+            a1 = time.perf_counter()
+            eng.verify()
+            torch.cuda.synchronize()
+            a2 = time.perf_counter()
+            td += a1 - a0
+            tv += a2 - a1
+        t_draft = td / n_model / (w["depth"] - 1)
+        model = spm.report(t_draft, tv / n_model - t_draft, w["depth"])
     cycles_s = args.steps / dt
     tau = committed / args.steps
     roof_key = (f"proj_kernel<{'bf16' if w['dtype'] == 'bf16' else 'f32'}, MT={mt}, EPI_PART> M={mv}")
@@ -241,6 +269,9 @@ def main():
                      "launches": g["launches"], "avg_launch_us": round(g["ms"] * 1e3 / max(1, g["launches"]), 2),
                      "bytes_per_launch": round(g["bytes"] / max(1, g["launches"]))},
     }
+    out["prefill_ms"] = round(prefill_ms, 3)
+    if model is not None:
+        out["speedup_model"] = model
     if prof is not None:
         out["profile_ms_per_cycle"] = {k: round(v["ms"] / args.profile_cycles, 4) for k, v in prof.items()}
     if not args.no_cpu:
