@@ -29,6 +29,8 @@ Modules:
   model     Llama-style target, EAGLE-1 and EAGLE-3 draft heads
   tree      path values, expansion, rerank, flattening, ancestry masks
   loop      plain greedy decode, the speculative loop, acceptance, commit
+  sampling  temperature > 0: Philox4x32-10 draws and the lossless tree
+            rejection-sampling acceptance
   speedup   the lesson's expected-tokens / speedup formula
 
 Parity status: every function is pinned by a test in ``tests/`` except where

@@ -27,6 +27,7 @@ from __future__ import annotations
 import numpy as np
 
 from .model import Config, Draft, Target, Weights, argmax_lowest, causal_vis
+from . import sampling as SMP
 from . import tree as T
 
 
@@ -44,6 +45,10 @@ class Session:
         self.budget = int(w["budget"])
         self.static = w.get("static") if w.get("tree") == "static" else None
         self.max_new = int(max_new if max_new is not None else w["gen"])
+        # sampling mode (oracle/sampling.py) when temperature > 0
+        self.temperature = float(w.get("temperature", 0.0))
+        self.seed = int(w.get("seed", 0))
+        self.n_verify = 0
         self.history = []
 
     # ------------------------------------------------------------ helpers
@@ -75,8 +80,12 @@ class Session:
         keep = self.cfg.feat_layers if self.cfg.head == "e3" else ()
         pos = np.arange(n)
         f, kept = self.target.forward(prompt, pos, pos, causal_vis(n, 0, n_slots), self.kv, keep)
-        g, margin = argmax_lowest(self.target.logits(f[-1:]))
+        last = self.target.logits(f[-1:])
+        g, margin = argmax_lowest(last)
         b = int(g[0])
+        self.n_verify = 0
+        if self.temperature > 0:   # sampling mode: the prefill's token is draw step 0
+            b = SMP.sample_token(last[0], self.temperature, self.seed, 0)
         self.prefill_margin = float(margin[0])
         self.tokens = prompt + [b]
         self.committed = [b]
@@ -159,7 +168,12 @@ class Session:
         logits = self.target.logits(f)
         self.last_logits, self.last_features = logits, f
         g, margin = argmax_lowest(logits)
-        path, bonus = T.accept(rows["token"], rows["parent"], g)
+        self.n_verify += 1
+        if self.temperature > 0:
+            path, bonus = SMP.accept_sample(rows["token"], rows["parent"], logits, self.temperature,
+                                            self.seed, self.n_verify, self.depth)
+        else:
+            path, bonus = T.accept(rows["token"], rows["parent"], g)
         L = len(path)
         new = [rows["token"][r] for r in path] + [bonus]
         # KV compaction: row path[j-1] -> position ctx + j (read all, then write)
