@@ -136,6 +136,8 @@ def main():
     ap.add_argument("--profile-cycles", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="> 0: sampling-mode verification (rejection sampling over the tree)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (the known-size "
                          "kernel that scales the HBM byte counters) and exit")
@@ -163,6 +165,8 @@ def main():
     import speculative_decoding_draft_amd as E
 
     w = synth.workloads.get(args.config)
+    if args.temperature > 0:
+        w.update(temperature=args.temperature, seed=args.seed)
     cycles_needed = args.warmup + args.steps + max(0, args.profile_cycles) + 2 + 5   # + speedup-model cycles
     max_new = max(w["gen"], cycles_needed * (w["depth"] + 1))
     max_ctx = w["prompt_len"] + max_new + w["depth"] + 2
@@ -254,7 +258,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w["dtype"],
         "data": "synthetic (seeded N(0,0.02)-like weights, uniform random prompt)",
-        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}",
+        "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}"
+                               + (f"; sampling at temperature {args.temperature}" if args.temperature > 0 else ""),
                    "global_batch": 1, "seq_len": int(avg_ctx), "parallelism": "none (1 GPU)"},
         "cycles_per_s": round(cycles_s, 3),
         "tau": round(tau, 4),

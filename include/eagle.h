@@ -94,6 +94,19 @@ typedef struct eagle_config {
                                               parent's draft top-k */
   int32_t max_ctx;             /* capacity: prompt + generated tokens */
   int32_t prefill_chunk;       /* rows per prefill pass (0 = 256) */
+  /* Sampling. temperature 0 = greedy verification (the default). temperature
+   * > 0 = sampling from softmax(logits / temperature): the prefill's token is
+   * drawn, and verify tests the tree's candidates by rejection sampling, so
+   * the committed stream is distributed as plain sampling from the target
+   * ("EAGLE: Feature-Level Drafting for Faster Inference", section
+   * "Speculative decoding in four moves"; EAGLE-2 page, "How it works").
+   * Draws come from Philox4x32-10 keyed by (seed_lo, seed_hi) with counter
+   * (step, depth, draw, 0): step 0 is the prefill's token, step i the i-th
+   * verify after it; draw j tests child j, 0xFFFF draws the residual token.
+   * The draft tree is built as in greedy mode. vocab <= 131072 when
+   * sampling. */
+  float temperature;
+  uint32_t seed_lo, seed_hi;
 } eagle_config;
 
 /* Sizes of the caller-owned device buffers, in bytes. */
@@ -234,13 +247,22 @@ eagle_status eagle_committed(eagle_ctx* ctx, int32_t* out, int32_t cap, int32_t*
 /* Debug read-back of the last target or draft pass, for parity tests:
  * what = 0: target features f [rows, hidden] fp32 of the last target pass;
  * what = 1: target logits [rows, vocab] fp32 of the last verify pass
- *           (recorded only after eagle_set_debug(ctx, 1));
+ *           (recorded after eagle_set_debug(ctx, 1), and always when
+ *           sampling);
  * what = 2: greedy choice g [rows] int32 of the last verify pass;
  * what = 3: top-1 minus top-2 logit [rows] fp32 of the last verify pass.
  * Copies min(bytes, available) and writes the row count. Synchronises. */
 eagle_status eagle_debug_read(eagle_ctx* ctx, int32_t what, void* host_dst, uint64_t bytes,
                               int32_t* rows);
 eagle_status eagle_set_debug(eagle_ctx* ctx, int32_t on);
+
+/* Changes the sampling temperature and seed of a loaded context (the fields
+ * of eagle_config of the same names; temperature 0 = greedy). Takes effect
+ * at the next call; eagle_prefill restarts the draw steps at 0, a change
+ * between cycles keeps the step count. EAGLE_E_INVALID for a temperature
+ * outside [0, 1e4] or, when > 0, a vocabulary above 131072. */
+eagle_status eagle_set_sampling(eagle_ctx* ctx, float temperature, uint32_t seed_lo,
+                                uint32_t seed_hi);
 
 /* Profiling: launches of the enabled classes are bracketed by HIP events on
  * the context's stream; eagle_profile_read synchronises and reports, per

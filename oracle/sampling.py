@@ -36,9 +36,11 @@ Precision (the GPU takes these decisions in fp32, so the oracle takes them
 in the same precision): e(v) = exp((l(v) - max l) / T) in float32, Z = the
 float64 sum of e rounded to float32, p(v) = e(v) / Z in float32; the child
 test is u * S < p(x) with S in float32; the residual draw walks the tokens
-in id order accumulating p(v) in float64 and takes the first v whose running
-sum exceeds u * S (the last token left with e(v) > 0 if rounding leaves the
-sum short).
+in id order accumulating e(v) in float64 and takes the first v whose running
+sum exceeds (u * S) * Z (the product u * S in float32, then times Z in
+float64), or the last token left with e(v) > 0 if rounding leaves the sum
+short. (In exact arithmetic this is the walk over p = e / Z with target
+u * S; counting in units of e spares a division per token.)
 """
 from __future__ import annotations
 
@@ -81,8 +83,7 @@ def row_probs(logits_row, temperature: float):
 
 def residual_draw(e, z, removed, S: np.float32, u: np.float32) -> int:
     """Token drawn from p = e / Z restricted to tokens not in `removed`."""
-    t = float(np.float32(u * S))
-    p = (e / z).astype(np.float32)
+    t = float(np.float32(u * S)) * float(z)
     keep = np.ones(len(e), dtype=bool)
     keep[list(removed)] = False
     cum = 0.0
@@ -92,7 +93,7 @@ def residual_draw(e, z, removed, S: np.float32, u: np.float32) -> int:
             continue
         if e[v] > 0:
             last = v
-        cum += float(p[v])
+        cum += float(e[v])
         if cum > t:
             return v
     return last

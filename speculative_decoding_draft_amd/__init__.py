@@ -33,7 +33,8 @@ class Config(ctypes.Structure):
                 ("dtype", i32), ("head", i32), ("feat_layers", i32 * 3), ("tree", i32),
                 ("topk", i32), ("expand", i32), ("depth", i32), ("budget", i32),
                 ("n_static", i32), ("static_parent", i32 * MAX_STATIC),
-                ("static_rank", i32 * MAX_STATIC), ("max_ctx", i32), ("prefill_chunk", i32)]
+                ("static_rank", i32 * MAX_STATIC), ("max_ctx", i32), ("prefill_chunk", i32),
+                ("temperature", f32), ("seed_lo", ctypes.c_uint32), ("seed_hi", ctypes.c_uint32)]
 
 
 class Sizes(ctypes.Structure):
@@ -100,6 +101,7 @@ def lib():
         L.eagle_committed.argtypes = [vp, P(i32), i32, P(i32)]
         L.eagle_debug_read.argtypes = [vp, i32, vp, u64, P(i32)]
         L.eagle_set_debug.argtypes = [vp, i32]
+        L.eagle_set_sampling.argtypes = [vp, f32, ctypes.c_uint32, ctypes.c_uint32]
         L.eagle_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
         L.eagle_profile_read.argtypes = [vp, P(Profile)]
         L.eagle_free.argtypes = [vp]
@@ -143,6 +145,9 @@ def make_config(w: dict, max_ctx: int = None, prefill_chunk: int = 0) -> Config:
         max_ctx = w["prompt_len"] + w["gen"] + w["depth"] + 2
     c.max_ctx = int(max_ctx)
     c.prefill_chunk = int(prefill_chunk)
+    c.temperature = float(w.get("temperature", 0.0))
+    seed = int(w.get("seed", 0))
+    c.seed_lo, c.seed_hi = seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF
     return c
 
 
@@ -285,6 +290,11 @@ class Engine:
         self._check(lib().eagle_profile_read(self.ctx, ctypes.byref(p)), "eagle_profile_read")
         return {name: dict(launches=p.launches[i], ms=p.ms[i], bytes=p.bytes[i])
                 for i, name in enumerate(PROF_CLASSES)}
+
+    def set_sampling(self, temperature: float, seed: int = 0):
+        """Temperature (0 = greedy) and seed of the draws, from the next call."""
+        self._check(lib().eagle_set_sampling(self.ctx, float(temperature), seed & 0xFFFFFFFF,
+                                             (seed >> 32) & 0xFFFFFFFF), "eagle_set_sampling")
 
     def set_debug(self, on: bool = True):
         self._check(lib().eagle_set_debug(self.ctx, 1 if on else 0), "eagle_set_debug")

@@ -73,6 +73,10 @@ bool derive(const eagle_config* c, Derived* z, std::string* why) {
   if (!(c->rope_base > 0.f) || !(c->rms_eps > 0.f)) return fail(why, "rope_base and rms_eps must be > 0");
   if (c->max_ctx < 2) return fail(why, "max_ctx must be >= 2");
   if (c->prefill_chunk < 0 || c->prefill_chunk > 1024) return fail(why, "prefill_chunk must be in [0, 1024]");
+  if (!(c->temperature >= 0.f) || !(c->temperature <= 1e4f))
+    return fail(why, "temperature must be in [0, 1e4] (0 = greedy)");
+  if (c->temperature > 0.f && !sample_vocab_ok(c->vocab))
+    return fail(why, "sampling supports vocab <= 131072");
   if (c->head == EAGLE_HEAD_E3)
     for (int i = 0; i < 3; ++i)
       if (c->feat_layers[i] < 0 || c->feat_layers[i] >= c->n_layers)
@@ -258,6 +262,8 @@ struct eagle_ctx {
   float *cos_t, *sin_t;
   int32_t *tpt, *dpt;
   float *h, *tfeat, *gbuf, *hcat, *dout, *opart, *mlpart, *gpart, *hpart, *logits, *margin, *logp;
+  float* ebuf;
+  double* zpart;
   void *xop, *qop, *aop, *fop, *lmh, *lmh2;   // activation operands (two planes for bf16)
   int64_t xlo = 0, qlo = 0, alo = 0, flo = 0, lmhlo = 0, lmh2lo = 0;  // lo-plane offsets (elements)
   int32_t *g, *ids, *acc, *new_tok, *cu_src, *iota, *seq;
@@ -270,6 +276,7 @@ struct eagle_ctx {
   int32_t* hres = nullptr;
   int32_t* hres_dev = nullptr;
   int32_t verify_tag = 0;
+  uint32_t step = 0;   // sampling draw step: 0 = the prefill's token, i = the i-th verify
   // host state
   int state = ST_EMPTY;
   int ctx_len = 0;
@@ -319,6 +326,8 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
   TAKE(gpart, float, gemm_ws_floats(z));
   TAKE(hpart, float, lmhead_part_floats(std::max(z.Mv, TREE_MAXEXP), z.V, z.k_b));
   TAKE(logits, float, (uint64_t)z.Mv * z.V);
+  TAKE(ebuf, float, (uint64_t)z.Mv * z.V);                        // sampling: exp((l - max) / T)
+  TAKE(zpart, double, sample_zpart_doubles(z.Mv, z.V));            // sampling: block sums of e
   TAKE(margin, float, z.Mv);
   TAKE(logp, float, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
   TAKE(xop, char, 2 * (uint64_t)M * kmax * es);
@@ -655,6 +664,8 @@ eagle_status check_ready(eagle_ctx* c) {
 }
 
 bool plain_mode(const eagle_ctx* c) { return c->z.dynamic && c->z.budget == 0; }
+bool sampling(const eagle_ctx* c) { return c->cfg.temperature > 0.f; }
+uint64_t seed_of(const eagle_ctx* c) { return ((uint64_t)c->cfg.seed_hi << 32) | c->cfg.seed_lo; }
 
 }  // namespace
 
@@ -845,6 +856,7 @@ eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32
     if (prompt[i] < 0 || prompt[i] >= z.V) return set_err(c, EAGLE_E_INVALID, "prompt[%d] = %d is not in [0, vocab)", i, prompt[i]);
   c->state = ST_EMPTY;
   c->committed.clear();
+  c->step = 0;
   HCHK(hipMemcpyAsync(c->seq, prompt, sizeof(int32_t) * n, hipMemcpyHostToDevice, c->st));
   for (int c0 = 0; c0 < n; c0 += z.chunk) {
     const int M = std::min(z.chunk, n - c0);
@@ -854,9 +866,15 @@ eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32
     SCHK(target_pass(c, M, c->seq + c0, c->rpos, c->rslot, vis));
     if (last) {
       const void* xl = (const char*)c->xop + (int64_t)(M - 1) * z.H * z.esz;
+      const bool smp = sampling(c);
       HCHK(launch_lmhead_argmax(z.dt, c->lm, xl, c->xlo, 1, z.V, z.H, c->hpart, c->g, c->margin,
-                                nullptr, c->st));
-      HCHK(hipMemcpyAsync(c->seq + n, c->g, 4, hipMemcpyDeviceToDevice, c->st));
+                                smp ? c->logits : nullptr, c->st));
+      if (smp) {
+        HCHK(launch_row_exp(c->logits, c->g, 1, z.V, c->cfg.temperature, c->ebuf, c->zpart, c->st));
+        HCHK(launch_sample_token(c->ebuf, c->zpart, z.V, seed_of(c), 0, c->seq + n, c->st));
+      }
+      else
+        HCHK(hipMemcpyAsync(c->seq + n, c->g, 4, hipMemcpyDeviceToDevice, c->st));
     }
     if (plain_mode(c)) continue;
     const float* feat = c->tfeat;
@@ -992,18 +1010,29 @@ eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_
   }
   RowVis vis{c->t.v_prehi, c->t.v_mask, 0, ctx, Mv, ctx + Mv};
   SCHK(target_pass(c, Mv, c->t.v_tok, c->t.v_pos, c->t.v_slot, vis));
+  const bool smp = sampling(c);
   PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)Mv * z.H * 4.0,
            launch_lmhead_argmax(z.dt, c->lm, c->xop, c->xlo, Mv, z.V, z.H, c->hpart, c->g,
-                                c->margin, c->debug ? c->logits : nullptr, c->st));
+                                c->margin, (c->debug || smp) ? c->logits : nullptr, c->st));
   c->last_verify_rows = Mv;
   // The acceptance kernel commits the tokens into seq on the device and posts
   // (L, tokens) to pinned host memory under a fresh tag. The host waits for
   // that tag only, so the KV compaction queued behind it overlaps the wait and
   // the catch-up launches queue behind it with no stream drain in between.
   const int32_t tag = c->verify_tag = c->verify_tag == INT32_MAX ? 1 : c->verify_tag + 1;
-  PROFILED(EAGLE_PROF_TREE, 0.0,
-           launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->seq + ctx + 1,
-                         c->hres_dev, tag, c->st));
+  if (smp) {
+    ++c->step;
+    PROFILED(EAGLE_PROF_TREE, 0.0,
+             launch_row_exp(c->logits, c->g, Mv, z.V, c->cfg.temperature, c->ebuf, c->zpart, c->st));
+    PROFILED(EAGLE_PROF_TREE, 0.0,
+             launch_accept_sample(c->t, c->ebuf, c->zpart, z.V, seed_of(c), c->step, z.D, c->acc,
+                                  c->new_tok, c->cu_src, c->seq + ctx + 1, c->hres_dev, tag,
+                                  c->st));
+  } else {
+    PROFILED(EAGLE_PROF_TREE, 0.0,
+             launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->seq + ctx + 1,
+                           c->hres_dev, tag, c->st));
+  }
   PROFILED(EAGLE_PROF_KV, 0.0,
            launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, c->acc, c->acc + 2, ctx, c->st));
   SCHK(wait_result(c, tag));
@@ -1074,6 +1103,19 @@ eagle_status eagle_committed(eagle_ctx* c, int32_t* out, int32_t cap, int32_t* n
   return EAGLE_OK;
 }
 
+eagle_status eagle_set_sampling(eagle_ctx* c, float temperature, uint32_t seed_lo,
+                                uint32_t seed_hi) {
+  if (!c) return EAGLE_E_INVALID;
+  if (!(temperature >= 0.f) || !(temperature <= 1e4f))
+    return set_err(c, EAGLE_E_INVALID, "temperature must be in [0, 1e4] (0 = greedy)");
+  if (temperature > 0.f && !sample_vocab_ok(c->z.V))
+    return set_err(c, EAGLE_E_INVALID, "sampling supports vocab <= 131072");
+  c->cfg.temperature = temperature;
+  c->cfg.seed_lo = seed_lo;
+  c->cfg.seed_hi = seed_hi;
+  return EAGLE_OK;
+}
+
 eagle_status eagle_set_debug(eagle_ctx* c, int32_t on) {
   if (!c) return EAGLE_E_INVALID;
   c->debug = on != 0;
@@ -1089,7 +1131,7 @@ eagle_status eagle_debug_read(eagle_ctx* c, int32_t what, void* host_dst, uint64
   int r;
   switch (what) {
     case 0: src = c->tfeat; r = c->last_target_rows; avail = (uint64_t)r * z.H * 4; break;
-    case 1: src = c->logits; r = c->last_verify_rows; avail = c->debug ? (uint64_t)r * z.V * 4 : 0; break;
+    case 1: src = c->logits; r = c->last_verify_rows; avail = (c->debug || sampling(c)) ? (uint64_t)r * z.V * 4 : 0; break;
     case 2: src = c->g; r = c->last_verify_rows; avail = (uint64_t)r * 4; break;
     case 3: src = c->margin; r = c->last_verify_rows; avail = (uint64_t)r * 4; break;
     default: return set_err(c, EAGLE_E_INVALID, "unknown debug buffer %d", what);

@@ -156,6 +156,25 @@ hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root
 // = the committed tokens; cu_src[0..L] = feature rows feeding the catch-up.
 // The tokens are also written to seq_out[0..L]. host (mapped host memory, or
 // NULL) receives host[1] = L and host[2..2+L] = the tokens, then host[0] = tag.
+// Sampling mode (temperature > 0). launch_row_exp: for each of `rows`
+// logit rows (logits [rows, V] fp32, g = each row's argmax), e = exp((l -
+// max) / T) into ebuf [rows, V] and fp64 sums of e per 1024-token block into
+// zpart [rows, sample_zpart_doubles / rows]. launch_accept_sample: the same
+// outputs as launch_accept, with the tree's candidates tested by rejection
+// sampling against e / Z of each verify row and the last token drawn from
+// what is left; draws from Philox4x32-10 keyed by seed, counter (step, depth,
+// draw, 0). launch_sample_token draws one token from row 0 (counter (step,
+// 0, 0xFFFF, 0)) into out[0]. V must pass sample_vocab_ok.
+bool sample_vocab_ok(int V);
+uint64_t sample_zpart_doubles(int rows, int V);
+hipError_t launch_row_exp(const float* logits, const int32_t* g, int rows, int V, float temperature,
+                          float* ebuf, double* zpart, hipStream_t st);
+hipError_t launch_accept_sample(TreeDev t, const float* ebuf, const double* zpart, int V,
+                                uint64_t seed, uint32_t step, int max_depth, int32_t* acc,
+                                int32_t* new_tok, int32_t* cu_src, int32_t* seq_out,
+                                int32_t* host, int32_t tag, hipStream_t st);
+hipError_t launch_sample_token(const float* ebuf, const double* zpart, int V, uint64_t seed,
+                               uint32_t step, int32_t* out, hipStream_t st);
 hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
                          int32_t* new_tok, int32_t* cu_src, int32_t* seq_out, int32_t* host,
                          int32_t tag, hipStream_t st);

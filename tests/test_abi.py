@@ -54,7 +54,8 @@ def test_library_exports_every_declared_function():
 STRUCTS = {
     "eagle_config": (E.Config, ["n_layers", "hidden", "rope_base", "dtype", "head", "feat_layers",
                                 "tree", "topk", "expand", "depth", "budget", "n_static",
-                                "static_parent", "static_rank", "max_ctx", "prefill_chunk"]),
+                                "static_parent", "static_rank", "max_ctx", "prefill_chunk",
+                                "temperature", "seed_lo", "seed_hi"]),
     "eagle_sizes": (E.Sizes, ["weight_bytes", "kv_bytes", "scratch_bytes", "n_tensors",
                               "verify_rows", "max_nodes", "kv_page"]),
     "eagle_tensor": (E.Tensor, ["kind", "group", "layer", "dtype", "rows", "cols", "offset"]),
