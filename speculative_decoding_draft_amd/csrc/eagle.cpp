@@ -645,6 +645,32 @@ eagle_status catch_up(eagle_ctx* c, int M, int first, const int32_t* tok, const 
   return EAGLE_OK;
 }
 
+// The verify's catch-up before the acceptance length is known on the host:
+// all depth + 1 rows after the root are drafted (rows past the committed
+// ones read the filler the acceptance kernel wrote and only touch draft KV
+// slots that the next cycle overwrites before reading; every row attends
+// causally, so the committed rows are exactly what a catch-up over them
+// alone computes). The new root row is row L = acc[0], picked on the device
+// for the LM head, and the tree is restarted at position ctx + L + 1.
+eagle_status catch_up_fixed(eagle_ctx* c, int ctx, const float* feat, const int32_t* idx) {
+  const Derived& z = c->z;
+  const int M = z.D + 1;
+  HCHK(launch_rows_causal(ctx + 1, M, c->rpos, c->rslot, c->rprehi, c->rmask, c->st));
+  RowVis vis{c->rprehi, c->rmask, 1, 0, 0, ctx + 1 + M};
+  SCHK(draft_pass(c, M, c->new_tok, feat, idx, c->rpos, c->rslot, vis, c->hcat));
+  PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
+           launch_gather_f32(c->hcat, z.H, c->acc, 1, z.H, c->dout, c->st));
+  // the root row's LM-head operand, gathered to the (now free) q operand buffer
+  PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
+           launch_gather_t(z.dt, c->xop, z.H, c->xlo, c->acc, 1, z.H, c->qop, c->qlo, c->st));
+  PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)z.H * 4.0,
+           launch_lmhead_topk(z.dt, c->lm, c->qop, c->qlo, 1, z.V, z.H, z.k_b, c->hpart, c->ids,
+                              c->logp, c->st));
+  PROFILED(EAGLE_PROF_TREE, 0.0,
+           launch_tree_append(c->t, c->tp, c->ids, c->logp, 1, ctx, c->st, c->acc));
+  return EAGLE_OK;
+}
+
 // E3: g = FC([l;m;h]) for M committed rows whose [l;m;h] operands are at src.
 eagle_status fuse_rows(eagle_ctx* c, int M, const void* src, int64_t src_lo) {
   const Derived& z = c->z;
@@ -1035,24 +1061,26 @@ eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_
   }
   PROFILED(EAGLE_PROF_KV, 0.0,
            launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, c->acc, c->acc + 2, ctx, c->st));
+  if (!plain_mode(c)) {
+    // the catch-up is queued before the host learns L, so the GPU runs on
+    // while the host waits for the acceptance result
+    const float* feat = c->tfeat;
+    const int32_t* idx = c->cu_src;
+    if (c->cfg.head == EAGLE_HEAD_E3) {
+      HCHK(launch_gather_t(z.dt, c->lmh, 3 * z.H, c->lmhlo, c->cu_src, z.D + 1, 3 * z.H, c->lmh2,
+                           c->lmh2lo, c->st));
+      SCHK(fuse_rows(c, z.D + 1, c->lmh2, c->lmh2lo));
+      feat = c->gbuf;
+      idx = c->iota;
+    }
+    SCHK(catch_up_fixed(c, ctx, feat, idx));
+  }
   SCHK(wait_result(c, tag));
   int32_t nt[EAGLE_MAX_DEPTH + 2];
   const int L = c->hres[1];
   if (L < 0 || L > z.D) return set_err(c, EAGLE_E_DEVICE, "acceptance length %d out of range", L);
   std::memcpy(nt, c->hres + 2, sizeof(int32_t) * (L + 1));
   const int ctx_new = ctx + L + 1;
-  if (!plain_mode(c)) {
-    const float* feat = c->tfeat;
-    const int32_t* idx = c->cu_src;
-    if (c->cfg.head == EAGLE_HEAD_E3) {
-      HCHK(launch_gather_t(z.dt, c->lmh, 3 * z.H, c->lmhlo, c->cu_src, L + 1, 3 * z.H, c->lmh2,
-                           c->lmh2lo, c->st));
-      SCHK(fuse_rows(c, L + 1, c->lmh2, c->lmh2lo));
-      feat = c->gbuf;
-      idx = c->iota;
-    }
-    SCHK(catch_up(c, L + 1, ctx + 1, c->new_tok, feat, idx, true, ctx_new));
-  }
   for (int i = 0; i <= L; ++i) c->committed.push_back(nt[i]);
   c->ctx_len = ctx_new;
   c->state = ST_READY;

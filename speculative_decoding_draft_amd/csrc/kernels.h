@@ -140,9 +140,11 @@ struct TreeParams {
 
 // Append the children produced by the last draft pass (pass 1 = the root
 // row) and, if pass < depth, choose the nodes the next pass expands and
-// write its row descriptors. ids/logp: [rows of the pass, k_b].
+// write its row descriptors. ids/logp: [rows of the pass, k_b]. The root
+// sits at position ctx, or at ctx + ctx_len[0] + 1 when ctx_len (a device
+// int, the acceptance length) is given.
 hipError_t launch_tree_append(TreeDev t, TreeParams p, const int32_t* ids, const float* logp,
-                              int pass, int ctx, hipStream_t st);
+                              int pass, int ctx, hipStream_t st, const int32_t* ctx_len = nullptr);
 // Rerank to the best `budget` nodes, flatten to verify rows (root first,
 // then by depth and rerank order), build positions and ancestry masks.
 // root_token: device pointer to the last committed token.
@@ -156,6 +158,8 @@ hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root
 // = the committed tokens; cu_src[0..L] = feature rows feeding the catch-up.
 // The tokens are also written to seq_out[0..L]. host (mapped host memory, or
 // NULL) receives host[1] = L and host[2..2+L] = the tokens, then host[0] = tag.
+// Rows L+1 .. max_depth of new_tok / cu_src get the bonus token and source
+// row 0, so a catch-up over max_depth + 1 rows reads valid inputs.
 // Sampling mode (temperature > 0). launch_row_exp: for each of `rows`
 // logit rows (logits [rows, V] fp32, g = each row's argmax), e = exp((l -
 // max) / T) into ebuf [rows, V] and fp64 sums of e per 1024-token block into

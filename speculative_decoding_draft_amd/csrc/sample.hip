@@ -281,6 +281,11 @@ __global__ __launch_bounds__(NT) void accept_sample_kernel(TreeDev t, const floa
       new_tok[L] = bonus;
       cu_src[0] = 0;
       seq_out[L] = bonus;
+      // rows L+1 .. max_depth of a fixed-size catch-up: valid tokens and sources
+      for (int j = L + 1; j <= max_depth; ++j) {
+        new_tok[j] = bonus;
+        cu_src[j] = 0;
+      }
       if (host) {
         host[2 + L] = bonus;
         host[1] = L;

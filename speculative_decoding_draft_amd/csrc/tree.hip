@@ -17,10 +17,12 @@ __device__ __forceinline__ void set_bit(uint64_t* m, int j) {
 
 __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams p,
                                                           const int32_t* ids, const float* lps,
-                                                          int pass, int ctx) {
+                                                          int pass, int ctx,
+                                                          const int32_t* ctx_len) {
   __shared__ int s_base, s_nrows, s_nnew, s_nsel, s_tbase;
   __shared__ int sel[TREE_MAXEXP];
   const int tid = threadIdx.x;
+  if (ctx_len) ctx += ctx_len[0] + 1;   // the root sits after the ctx_len[0] + 1 tokens just committed
   if (tid == 0) {
     if (pass == 1) {
       t.counts[0] = 0;
@@ -265,6 +267,11 @@ __global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g,
     new_tok[L] = bonus;
     cu_src[0] = 0;
     seq_out[L] = bonus;
+    // rows L+1 .. max_depth of a fixed-size catch-up: valid tokens and sources
+    for (int j = L + 1; j <= max_depth; ++j) {
+      new_tok[j] = bonus;
+      cu_src[j] = 0;
+    }
     if (host) {
       host[2 + L] = bonus;
       host[1] = L;
@@ -277,8 +284,9 @@ __global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g,
 }  // namespace
 
 hipError_t launch_tree_append(TreeDev t, TreeParams p, const int32_t* ids, const float* logp,
-                              int pass, int ctx, hipStream_t st) {
-  hipLaunchKernelGGL(tree_append_kernel, dim3(1), dim3(256), 0, st, t, p, ids, logp, pass, ctx);
+                              int pass, int ctx, hipStream_t st, const int32_t* ctx_len) {
+  hipLaunchKernelGGL(tree_append_kernel, dim3(1), dim3(256), 0, st, t, p, ids, logp, pass, ctx,
+                     ctx_len);
   return hipGetLastError();
 }
 
