@@ -219,3 +219,41 @@ __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// (value desc, id asc) as one 64-bit key, larger = better: candidates then
+// compare with one 64-bit comparison, and a wave-wide maximum takes four DPP
+// steps on the two halves.
+__device__ __forceinline__ uint64_t vid_key(float v, int id) {
+  return ((uint64_t)float_key(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+// key 0 is below every real key (no candidate): value -inf, id 0x7fffffff
+__device__ __forceinline__ float vid_value(uint64_t k) {
+  return k ? key_float((uint32_t)(k >> 32)) : -INFINITY;
+}
+__device__ __forceinline__ int vid_id(uint64_t k) {
+  return k ? (int)(0xFFFFFFFFu - (uint32_t)k) : 0x7fffffff;
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  uint64_t o;
+  o = dpp_u64<DPP_QUAD_XOR1>(x); x = o > x ? o : x;
+  o = dpp_u64<DPP_QUAD_XOR2>(x); x = o > x ? o : x;
+  o = dpp_u64<DPP_HALF_MIRROR>(x); x = o > x ? o : x;
+  o = dpp_u64<DPP_MIRROR>(x); x = o > x ? o : x;
+  const uint64_t a = lane_u64(x, 0), b = lane_u64(x, 16), c = lane_u64(x, 32), d = lane_u64(x, 48);
+  const uint64_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}

@@ -495,16 +495,16 @@ __global__ __launch_bounds__(256) void argmax_combine(const float* part, int n_t
 // the buffer). A threshold T, the k-th largest of the tile maxima, bounds the
 // merge: k distinct values are >= T, so no value below T is among the k
 // best, and since every tile list is sorted a tile stops at its first
-// candidate under T. Each thread keeps its best candidates in registers
-// (bubble insertion with static indices); each wave pops its k best with
-// wave-wide argmax rounds (shuffles), and wave 0 merges the four lists.
+// candidate under T. Each thread keeps its best candidates in registers as
+// sorted 64-bit (value desc, id asc) keys (bubble insertion with static
+// indices); each wave pops its k best with wave-wide 64-bit DPP maxima, and
+// wave 0 merges the four lists.
 __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_tiles, int M, int k,
                                                     int32_t* ids, float* logp) {
   constexpr int KMAX = 16, BUF = 16384, NT = 256, NWV = NT / 64;
   __shared__ __attribute__((aligned(16))) float buf[BUF];
   __shared__ float s_red[2 * NWV];
-  __shared__ float s_cv[NWV * KMAX];
-  __shared__ int s_ci[NWV * KMAX];
+  __shared__ uint64_t s_key[NWV * KMAX];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rec = topk_record(k), seg = BUF / rec;
   const float* row = part + (int64_t)m * n_tiles * rec;
@@ -525,77 +525,68 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
     }
     __syncthreads();
   };
-  float lv[KMAX];
-  int li[KMAX];
+  // this thread's best candidates as (value desc, id asc) keys, sorted
+  constexpr uint64_t NONE = 0;   // below every real key
+  uint64_t lk[KMAX];
   auto reset = [&]() {
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) { lv[i] = -INFINITY; li[i] = 0x7fffffff; }
+    for (int i = 0; i < KMAX; ++i) lk[i] = NONE;
   };
-  // (value desc, id asc) insertion of (cv, ci) into the sorted list lv/li
-  auto insert = [&](float cv, int ci) {
+  auto insert = [&](uint64_t key) {
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       if (i < k) {
-        const bool better = cv > lv[i] || (cv == lv[i] && ci < li[i]);
-        const float tv = better ? lv[i] : cv;
-        const int ti = better ? li[i] : ci;
-        lv[i] = better ? cv : lv[i];
-        li[i] = better ? ci : li[i];
-        cv = tv;
-        ci = ti;
+        const uint64_t cur = lk[i];
+        lk[i] = key > cur ? key : cur;
+        key = key > cur ? cur : key;
       }
     }
   };
-  // k rounds of a wave-wide argmax over the lanes' list heads; emit(r, v, id)
+  // k rounds of a wave-wide maximum over the lanes' list heads; the lane
+  // holding it (keys are unique) pops it; emit(r, key)
   auto pop_k = [&](auto&& emit) {
     for (int r = 0; r < k; ++r) {
-      float bv = lv[0];
-      int bi = li[0], bl = lane;
-      wave_argmax(bv, bi, bl);
-      emit(r, bv, bi);
-      if (lane == bl) {
+      const uint64_t best = wave_max_u64(lk[0]);
+      emit(r, best);
+      if (lk[0] == best && best != NONE) {
 #pragma unroll
-        for (int i = 0; i + 1 < KMAX; ++i) { lv[i] = lv[i + 1]; li[i] = li[i + 1]; }
-        lv[KMAX - 1] = -INFINITY;
-        li[KMAX - 1] = 0x7fffffff;
+        for (int i = 0; i + 1 < KMAX; ++i) lk[i] = lk[i + 1];
+        lk[KMAX - 1] = NONE;
       }
     }
   };
   // every wave's k best go to LDS; wave 0 then holds them one per lane
   // (4k <= 64) and pops the k best of the workgroup
   auto merge_waves = [&](auto&& emit) {
-    pop_k([&](int r, float v, int id) {
-      if (lane == 0) { s_cv[wave * KMAX + r] = v; s_ci[wave * KMAX + r] = id; }
+    pop_k([&](int r, uint64_t key) {
+      if (lane == 0) s_key[wave * KMAX + r] = key;
     });
     __syncthreads();
     if (wave == 0) {
       reset();
       const int w = lane / KMAX, r = lane % KMAX;
-      if (r < k) { lv[0] = s_cv[w * KMAX + r]; li[0] = s_ci[w * KMAX + r]; }
+      if (r < k) lk[0] = s_key[w * KMAX + r];
       pop_k(emit);
     }
     __syncthreads();
   };
   // pass 1: the global max and the threshold T from the tile maxima
   reset();
-  float mx = -INFINITY, kth = -INFINITY;   // kth: this thread's k-th largest so far
+  float mx = -INFINITY;
   for (int t0 = 0; t0 < n_tiles; t0 += seg) {
     const int nt = min(seg, n_tiles - t0);
     stage(t0, nt);
     for (int t = tid; t < nt; t += NT) {
       const float v = buf[t * rec];
       mx = fmaxf(mx, v);
-      if (v > kth) {
-        insert(v, t0 + t);
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i)
-          if (i == k - 1) kth = lv[i];
-      }
+      insert(vid_key(v, t0 + t));
     }
   }
   mx = wave_max(mx);
   if (lane == 0) s_red[wave] = mx;
-  merge_waves([&](int r, float v, int) { if (r == k - 1 && lane == 0) s_red[NWV] = v; });
+  merge_waves([&](int r, uint64_t key) {
+    if (r == k - 1 && lane == 0) s_red[NWV] = vid_value(key);
+  });
   const float gmax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   const float thr = s_red[NWV];
   // pass 2: sum of exp and the k best among candidates >= T
@@ -611,7 +602,7 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
         const float cv = p[2 + c];
         const int ci = __float_as_int(p[2 + k + c]);
         if (ci == 0x7fffffff || cv < thr) break;   // tile lists are sorted
-        insert(cv, ci);
+        insert(vid_key(cv, ci));
       }
     }
   }
@@ -620,10 +611,10 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
   if (lane == 0) s_red[wave] = se;
   __syncthreads();
   const float lse = logf((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
-  merge_waves([&](int r, float v, int id) {
+  merge_waves([&](int r, uint64_t key) {
     if (lane == 0) {
-      ids[m * k + r] = id;
-      logp[m * k + r] = (v - gmax) - lse;
+      ids[m * k + r] = vid_id(key);
+      logp[m * k + r] = (vid_value(key) - gmax) - lse;
     }
   });
 }
