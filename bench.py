@@ -1,10 +1,13 @@
-"""Throughput of one EAGLE draft-and-verify cycle at batch 1 on one MI355X.
+"""Throughput of one EAGLE draft-and-verify cycle on one MI355X (batch 1 by
+default; --batch B serves B sequences per cycle).
 
 A step is one cycle: the draft passes and tree build (eagle_draft_tree) plus
 the target verify pass, acceptance, KV compaction and the draft catch-up
-(eagle_verify), on seeded synthetic weights and prompts already resident in
-HBM. Prints one JSON line (see README of the driver contract):
-  value       committed tokens/s (tau x cycles/s; tau ~ 1 with random weights)
+(eagle_verify, or eagle_verify_batch for every lane of a batch), on seeded
+synthetic weights and prompts already resident in HBM. Prints one JSON line
+(see README of the driver contract):
+  value       committed tokens/s over all lanes (tau x lanes x cycles/s; tau ~
+              1 with random weights)
   roofline    the dominant kernel: the split-K projection of the target
               layers (q|k|v, o and down at M = tree rows), its algorithmic
               bytes / its device time from HIP events recorded around each of
@@ -63,10 +66,11 @@ def stored_traffic(kernel_key: str):
     return None
 
 
-def cycle_bytes(w: dict, ctx: int) -> float:
+def cycle_bytes(w: dict, ctx: int, lanes: int = 1) -> float:
     """Algorithmic HBM bytes of one cycle at context ctx: every weight byte the
     cycle must read (target layers + LM head once; draft layer + LM head +
-    FC per draft pass), plus the KV cache reads (4 bytes per K/V element)."""
+    FC per draft pass), plus the KV cache reads (4 bytes per K/V element) of
+    each of `lanes` sequences."""
     H, nq, nkv, F, V, L = (w[k] for k in ("hidden", "n_heads", "n_kv_heads", "ffn", "vocab", "n_layers"))
     d = H // nq
     esz = 2 if w["dtype"] == "bf16" else 4
@@ -76,7 +80,7 @@ def cycle_bytes(w: dict, ctx: int) -> float:
     target = L * layer(H) + V * H
     draft = D * (layer(kin) + V * H)
     fc = D * H * 2 * H if w["head"] == "e1" else H * 3 * H
-    kv = 2 * nkv * d * 4 * (L * ctx + D * ctx)
+    kv = 2 * nkv * d * 4 * (L * ctx + D * ctx) * lanes
     return esz * (target + draft + fc) + kv
 
 
@@ -138,6 +142,8 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: sampling-mode verification (rejection sampling over the tree)")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="sequences served per cycle (lanes; each its own prompt)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (the known-size "
                          "kernel that scales the HBM byte counters) and exit")
@@ -167,6 +173,8 @@ def main():
     w = synth.workloads.get(args.config)
     if args.temperature > 0:
         w.update(temperature=args.temperature, seed=args.seed)
+    B = args.batch
+    w["batch"] = B
     cycles_needed = args.warmup + args.steps + max(0, args.profile_cycles) + 2 + 5   # + speedup-model cycles
     max_new = max(w["gen"], cycles_needed * (w["depth"] + 1))
     max_ctx = w["prompt_len"] + max_new + w["depth"] + 2
@@ -174,7 +182,9 @@ def main():
     synth.fill_weights(eng.table, eng.weights.data_ptr(), w["weight_seed"], eng.stream.cuda_stream)
     torch.cuda.synchronize()
     eng.load()
-    prompt = synth.prompt(args.seed, w["prompt_len"], w["vocab"])
+    # lane b's prompt comes from seed + b (lane 0: the batch-1 prompt)
+    prompts = [synth.prompt(args.seed + b, w["prompt_len"], w["vocab"]) for b in range(B)]
+    prompt = prompts[0]
     # the first prefill loads the kernels; the second (it restarts the
     # sequence) is the timed one
     eng.prefill(prompt)
@@ -183,11 +193,19 @@ def main():
     eng.prefill(prompt)
     torch.cuda.synchronize()
     prefill_ms = (time.perf_counter() - tp0) * 1e3
-    print(f"# {args.config}: prefill done, ctx {len(prompt)}, {prefill_ms:.1f} ms", file=sys.stderr, flush=True)
+    for b in range(1, B):
+        eng.prefill(prompts[b], lane=b)
+    print(f"# {args.config}: prefill done, ctx {len(prompt)}, {prefill_ms:.1f} ms, {B} lane(s)",
+          file=sys.stderr, flush=True)
 
     def cycle():
         eng.draft_tree(want=False)
-        return len(eng.verify())
+        if B == 1:
+            return len(eng.verify())
+        return sum(len(n) for n in eng.verify_batch())
+
+    def mean_ctx():
+        return sum(len(eng.committed(b)) for b in range(B)) / B + len(prompt) - 1
 
     # the dominant kernel's launches carry HIP events from warmup on, so the
     # event pool is allocated before the timed region
@@ -196,7 +214,7 @@ def main():
         cycle()
     torch.cuda.synchronize()
     eng.profile(["gemm"], every=ROOF_EVERY)   # reset the counters; keep the class enabled
-    ctx0 = len(eng.committed()) + len(prompt) - 1
+    ctx0 = mean_ctx()
     t0 = time.perf_counter()
     committed = 0
     for _ in range(args.steps):
@@ -206,14 +224,14 @@ def main():
     dt = t1 - t0
     g = eng.profile_read()["gemm"]
     eng.profile(False)
-    ctx1 = len(eng.committed()) + len(prompt) - 1
+    ctx1 = mean_ctx()
     print(f"# timed {args.steps} cycles in {dt * 1e3:.1f} ms", file=sys.stderr, flush=True)
 
     # algorithmic bytes of the timed cycles (context grows by L+1 per cycle)
     avg_ctx = 0.5 * (ctx0 + ctx1)
-    bytes_cycle = cycle_bytes(w, int(avg_ctx))
+    bytes_cycle = cycle_bytes(w, int(avg_ctx), B)
     gemm_gbps = g["bytes"] / (g["ms"] * 1e-3) / 1e9 if g["ms"] > 0 else 0.0
-    mv = 1 + w["budget"]
+    mv = B * (1 + w["budget"])    # target rows of a verify pass
     mt = (mv + 15) // 16 if mv <= 80 else 4
 
     # breakdown window after the timed region: events around every launch
@@ -228,7 +246,7 @@ def main():
     # passes in eagle_draft_tree; the target pass plus one catch-up draft
     # pass in eagle_verify
     model = None
-    if w["depth"] >= 2 and w["budget"] > 0:
+    if w["depth"] >= 2 and w["budget"] > 0 and B == 1:
         from speculative_decoding_draft_amd import speedup as spm
         td = tv = 0.0
         n_model = 5
@@ -246,11 +264,13 @@ def main():
         t_draft = td / n_model / (w["depth"] - 1)
         model = spm.report(t_draft, tv / n_model - t_draft, w["depth"])
     cycles_s = args.steps / dt
-    tau = committed / args.steps
+    tau = committed / args.steps / B
     roof_key = (f"proj_kernel<{'bf16' if w['dtype'] == 'bf16' else 'f32'}, MT={mt}, EPI_PART> M={mv}")
     traffic = stored_traffic(roof_key)
     out = {
-        "metric": "committed tokens/sec + draft/verify cycles/sec at bs=1; % of HBM roofline",
+        "metric": ("committed tokens/sec + draft/verify cycles/sec at bs=1; % of HBM roofline"
+                   if B == 1 else
+                   f"committed tokens/sec + draft/verify cycles/sec at bs={B}; % of HBM roofline"),
         "value": round(committed / dt, 3),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -259,8 +279,9 @@ def main():
         "dtype": w["dtype"],
         "data": "synthetic (seeded N(0,0.02)-like weights, uniform random prompt)",
         "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}"
-                               + (f"; sampling at temperature {args.temperature}" if args.temperature > 0 else ""),
-                   "global_batch": 1, "seq_len": int(avg_ctx), "parallelism": "none (1 GPU)"},
+                               + (f"; sampling at temperature {args.temperature}" if args.temperature > 0 else "")
+                               + (f"; {B} sequences per cycle" if B > 1 else ""),
+                   "global_batch": B, "seq_len": int(avg_ctx), "parallelism": "none (1 GPU)"},
         "cycles_per_s": round(cycles_s, 3),
         "tau": round(tau, 4),
         "cycle_hbm": {"bytes_per_cycle": bytes_cycle,
@@ -280,6 +301,7 @@ def main():
     if prof is not None:
         out["profile_ms_per_cycle"] = {k: round(v["ms"] / args.profile_cycles, 4) for k, v in prof.items()}
     if not args.no_cpu:
+        # sequences are independent: the oracle's tokens/s is the same at any batch
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
     eng.close()

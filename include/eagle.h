@@ -1,6 +1,6 @@
 /*
- * eagle.h - C interface of one EAGLE / EAGLE-2 draft-and-verify cycle at
- * batch 1 on one AMD Instinct MI355X (gfx950).
+ * eagle.h - C interface of one EAGLE / EAGLE-2 draft-and-verify cycle on one
+ * AMD Instinct MI355X (gfx950), for one sequence or a small batch of them.
  *
  * What the calls compute (the method, from the source pages):
  *  - "Lesson 13.11 - EAGLE: Feature-Level Drafting for Faster Inference",
@@ -25,9 +25,16 @@
  *    level, tree depth, number of verified draft tokens).
  *
  * Conventions
- *  - Batch 1. One context belongs to one host thread; all device work is
- *    ordered on the stream given to eagle_load. Token ids are int32 in
- *    [0, vocab). Positions are 0-based.
+ *  - One context belongs to one host thread; all device work is ordered on
+ *    the stream given to eagle_load. Token ids are int32 in [0, vocab).
+ *    Positions are 0-based.
+ *  - Batch: a context serves `batch` independent sequences (lanes 0 ..
+ *    batch - 1), each with its own prompt, KV cache, tree and committed
+ *    stream. Every draft pass and the verify pass run all lanes' rows in one
+ *    pass over the weights (the draft and verify row counts are the same for
+ *    every lane; the context lengths may differ). A lane computes exactly
+ *    what a batch-1 context computes for its sequence, up to the rounding
+ *    of split-K sums whose split count depends on the total row count.
  *  - Memory: the library allocates no device memory. The caller allocates
  *    the three device buffers whose sizes eagle_query reports and keeps them
  *    alive until eagle_free. Host pointers are only read during the call.
@@ -40,8 +47,10 @@
  *    call leaves the context unchanged. After EAGLE_E_HIP or EAGLE_E_DEVICE
  *    the context is FAILED: only eagle_prefill (which resets it) and
  *    eagle_free are accepted. eagle_last_error gives a message.
- *  - Greedy (temperature 0) only: the committed stream equals plain greedy
- *    decoding of the target (ties to the lowest token id).
+ *  - Greedy (temperature 0, the default): the committed stream equals plain
+ *    greedy decoding of the target (ties to the lowest token id). Sampling
+ *    (temperature > 0, see eagle_config): it is distributed as plain
+ *    sampling from the target.
  */
 #ifndef EAGLE_H
 #define EAGLE_H
@@ -71,6 +80,7 @@ enum { EAGLE_TREE_DYNAMIC = 0, EAGLE_TREE_STATIC = 1 };
 #define EAGLE_MAX_VERIFY 128  /* verify rows = 1 + budget */
 #define EAGLE_MAX_NODES 1024  /* generated nodes per cycle */
 #define EAGLE_MAX_TOPK 16     /* children per expanded row */
+#define EAGLE_MAX_BATCH 8     /* sequences per context */
 
 /* Model and policy. Shapes follow the Llama layout: RMSNorm (gain tensors),
  * rotate-half RoPE, GQA attention, SwiGLU FFN, untied LM head. */
@@ -101,12 +111,16 @@ typedef struct eagle_config {
    * ("EAGLE: Feature-Level Drafting for Faster Inference", section
    * "Speculative decoding in four moves"; EAGLE-2 page, "How it works").
    * Draws come from Philox4x32-10 keyed by (seed_lo, seed_hi) with counter
-   * (step, depth, draw, 0): step 0 is the prefill's token, step i the i-th
-   * verify after it; draw j tests child j, 0xFFFF draws the residual token.
-   * The draft tree is built as in greedy mode. vocab <= 131072 when
-   * sampling. */
+   * (step, depth, draw, lane): step 0 is the lane's prefill token, step i
+   * its i-th verify after it; draw j tests child j, 0xFFFF draws the
+   * residual token; lane is the sequence's index (0 at batch 1). The draft
+   * tree is built as in greedy mode. vocab <= 131072 when sampling. */
   float temperature;
   uint32_t seed_lo, seed_hi;
+  /* Sequences served together, 1 .. EAGLE_MAX_BATCH (0 = 1). Device buffers
+   * grow with it: KV by `batch` caches, scratch by batch times the rows of a
+   * pass. */
+  int32_t batch;
 } eagle_config;
 
 /* Sizes of the caller-owned device buffers, in bytes. */
@@ -208,18 +222,25 @@ eagle_status eagle_tensor_info(const eagle_config* cfg, int32_t index, eagle_ten
 eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void* hip_stream,
                         eagle_ctx** out);
 
-/* Starts a sequence: target prefill over prompt[0..n), the first committed
- * token b = greedy choice after the prompt, and the draft's catch-up over
- * the n (feature, next-token) pairs, which leaves the depth-1 candidates
- * ready. Resets any earlier sequence. If first_token is not NULL the call
- * synchronises the stream and writes b. EAGLE_E_CAPACITY if
- * n + 1 > max_ctx. */
+/* Starts a sequence in lane 0: target prefill over prompt[0..n), the first
+ * committed token b = greedy choice after the prompt (sampled when
+ * temperature > 0), and the draft's catch-up over the n (feature,
+ * next-token) pairs, which leaves the depth-1 candidates ready. Resets any
+ * earlier sequence of the lane. The call synchronises the stream and, if
+ * first_token is not NULL, writes b. EAGLE_E_CAPACITY if n + 1 > max_ctx. */
 eagle_status eagle_prefill(eagle_ctx* ctx, const int32_t* prompt, int32_t n,
                            int32_t* first_token);
+/* eagle_prefill for lane `lane` (0 <= lane < batch); the other lanes keep
+ * their state, so a finished sequence can be replaced between cycles. */
+eagle_status eagle_prefill_lane(eagle_ctx* ctx, int32_t lane, const int32_t* prompt, int32_t n,
+                                int32_t* first_token);
 
-/* Runs the draft passes and the rerank of one cycle (state READY ->
- * DRAFTED). If `out` is not NULL the call synchronises and fills it. */
+/* Runs the draft passes and the rerank of one cycle for every lane (each
+ * lane READY -> DRAFTED). If `out` is not NULL the call synchronises and
+ * fills it with lane 0's tree. */
 eagle_status eagle_draft_tree(eagle_ctx* ctx, eagle_tree* out);
+/* Copies lane `lane`'s drafted tree (state DRAFTED) to `out`. Synchronises. */
+eagle_status eagle_read_tree(eagle_ctx* ctx, int32_t lane, eagle_tree* out);
 
 /* Verifies the drafted tree (state DRAFTED), or `planted` when not NULL
  * (state READY or DRAFTED; only n_rows, token and parent are read, rows must
@@ -233,6 +254,14 @@ eagle_status eagle_draft_tree(eagle_ctx* ctx, eagle_tree* out);
  * exceed max_ctx. */
 eagle_status eagle_verify(eagle_ctx* ctx, const eagle_tree* planted, int32_t* out_tokens,
                           int32_t* n_committed);
+/* Batch form of eagle_verify (any batch; no planted tree): verifies every
+ * lane's drafted tree in one target pass and returns once every lane's
+ * acceptance result is known. Lane b's L_b + 1 committed tokens go to
+ * out_tokens[b * (EAGLE_MAX_DEPTH + 1) ...] (capacity batch *
+ * (EAGLE_MAX_DEPTH + 1)) and the count to n_committed[b] (capacity batch);
+ * either may be NULL. eagle_verify itself is the batch-1 call
+ * (EAGLE_E_STATE when batch > 1), and so is eagle_generate. */
+eagle_status eagle_verify_batch(eagle_ctx* ctx, int32_t* out_tokens, int32_t* n_committed);
 
 /* eagle_prefill, then cycles until at least max_new tokens are committed
  * (the prefill's token is the first); writes exactly max_new tokens to out
@@ -240,15 +269,18 @@ eagle_status eagle_verify(eagle_ctx* ctx, const eagle_tree* planted, int32_t* ou
 eagle_status eagle_generate(eagle_ctx* ctx, const int32_t* prompt, int32_t n, int32_t max_new,
                             int32_t* out, int32_t* n_out, eagle_stats* stats);
 
-/* Copies the committed tokens of the current sequence (prefill's first) to
- * out (capacity cap); *n gets the total count. Synchronises. */
+/* Copies the committed tokens of lane 0's sequence (prefill's first) to
+ * out (capacity cap); *n gets the total count. Host-side copy. */
 eagle_status eagle_committed(eagle_ctx* ctx, int32_t* out, int32_t cap, int32_t* n);
+/* eagle_committed for lane `lane`. */
+eagle_status eagle_committed_lane(eagle_ctx* ctx, int32_t lane, int32_t* out, int32_t cap,
+                                  int32_t* n);
 
 /* Debug read-back of the last target or draft pass, for parity tests:
  * what = 0: target features f [rows, hidden] fp32 of the last target pass;
  * what = 1: target logits [rows, vocab] fp32 of the last verify pass
  *           (recorded after eagle_set_debug(ctx, 1), and always when
- *           sampling);
+ *           sampling); a batch's verify rows are lane by lane;
  * what = 2: greedy choice g [rows] int32 of the last verify pass;
  * what = 3: top-1 minus top-2 logit [rows] fp32 of the last verify pass.
  * Copies min(bytes, available) and writes the row count. Synchronises. */

@@ -32,9 +32,11 @@ from . import tree as T
 
 
 class Session:
-    """Oracle state for one sequence: target + draft KV, committed tokens."""
+    """Oracle state for one sequence: target + draft KV, committed tokens.
+    `lane` is the sequence's index in a batch; it only selects the stream of
+    random draws in sampling mode (oracle/sampling.py)."""
 
-    def __init__(self, w: dict, weights: Weights = None, max_new: int = None):
+    def __init__(self, w: dict, weights: Weights = None, max_new: int = None, lane: int = 0):
         self.w = dict(w)
         self.cfg = Config(w)
         self.W = weights if weights is not None else Weights(self.cfg)
@@ -48,6 +50,7 @@ class Session:
         # sampling mode (oracle/sampling.py) when temperature > 0
         self.temperature = float(w.get("temperature", 0.0))
         self.seed = int(w.get("seed", 0))
+        self.lane = int(lane)
         self.n_verify = 0
         self.history = []
 
@@ -85,7 +88,7 @@ class Session:
         b = int(g[0])
         self.n_verify = 0
         if self.temperature > 0:   # sampling mode: the prefill's token is draw step 0
-            b = SMP.sample_token(last[0], self.temperature, self.seed, 0)
+            b = SMP.sample_token(last[0], self.temperature, self.seed, 0, lane=self.lane)
         self.prefill_margin = float(margin[0])
         self.tokens = prompt + [b]
         self.committed = [b]
@@ -171,7 +174,7 @@ class Session:
         self.n_verify += 1
         if self.temperature > 0:
             path, bonus = SMP.accept_sample(rows["token"], rows["parent"], logits, self.temperature,
-                                            self.seed, self.n_verify, self.depth)
+                                            self.seed, self.n_verify, self.depth, lane=self.lane)
         else:
             path, bonus = T.accept(rows["token"], rows["parent"], g)
         L = len(path)

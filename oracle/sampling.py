@@ -28,9 +28,12 @@ sampling from the target.
 
 Random numbers: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
 random numbers: as easy as 1, 2, 3", SC'11), key = the 64-bit seed (low word
-first), counter = (step, depth, draw, 0); u = (first output word >> 8) * 2^-24,
-in [0, 1). step 0 is the prefill's token and step i the i-th verify; draw j is
-the test of the j-th child at that depth, 0xFFFF the residual draw.
+first), counter = (step, depth, draw, lane); u = (first output word >> 8) *
+2^-24, in [0, 1). step 0 is the prefill's token and step i the i-th verify;
+draw j is the test of the j-th child at that depth, 0xFFFF the residual draw;
+lane is the sequence's index when several sequences are served together (0
+for one). The pages speak of one sequence; the fourth counter word giving
+each sequence of a batch its own stream is this implementation's choice.
 
 Precision (the GPU takes these decisions in fp32, so the oracle takes them
 in the same precision): e(v) = exp((l(v) - max l) / T) in float32, Z = the
@@ -66,9 +69,9 @@ def philox4x32(ctr, key, rounds: int = 10):
     return c0, c1, c2, c3
 
 
-def uniform(seed: int, step: int, depth: int, draw: int) -> np.float32:
-    """u in [0, 1) with 24 random bits, from the counter (step, depth, draw, 0)."""
-    w = philox4x32((step, depth, draw, 0), (seed & MASK32, (seed >> 32) & MASK32))[0]
+def uniform(seed: int, step: int, depth: int, draw: int, lane: int = 0) -> np.float32:
+    """u in [0, 1) with 24 random bits, from the counter (step, depth, draw, lane)."""
+    w = philox4x32((step, depth, draw, lane), (seed & MASK32, (seed >> 32) & MASK32))[0]
     return np.float32((w >> 8) * (1.0 / 16777216.0))
 
 
@@ -99,14 +102,15 @@ def residual_draw(e, z, removed, S: np.float32, u: np.float32) -> int:
     return last
 
 
-def sample_token(logits_row, temperature: float, seed: int, step: int, depth: int = 0) -> int:
+def sample_token(logits_row, temperature: float, seed: int, step: int, depth: int = 0,
+                 lane: int = 0) -> int:
     """One token drawn from softmax(logits / T) (the prefill's token)."""
     e, z = row_probs(logits_row, temperature)
-    return residual_draw(e, z, (), np.float32(1.0), uniform(seed, step, depth, RESIDUAL_DRAW))
+    return residual_draw(e, z, (), np.float32(1.0), uniform(seed, step, depth, RESIDUAL_DRAW, lane))
 
 
 def accept_sample(token_rows, parent_rows, logits, temperature: float, seed: int, step: int,
-                  max_depth: int):
+                  max_depth: int, lane: int = 0):
     """Sampling-mode acceptance walk over the verify rows.
 
     logits[r] are the target's logits at verify row r. Returns (accepted rows
@@ -123,13 +127,14 @@ def accept_sample(token_rows, parent_rows, logits, temperature: float, seed: int
         for j, r in enumerate(children):
             x = int(token_rows[r])
             px = np.float32(e[x] / z)
-            if np.float32(uniform(seed, step, depth, j) * S) < px:
+            if np.float32(uniform(seed, step, depth, j, lane) * S) < px:
                 nxt = r
                 break
             S = np.float32(S - px)
             removed.append(x)
         if nxt < 0:
-            return path, residual_draw(e, z, removed, S, uniform(seed, step, depth, RESIDUAL_DRAW))
+            return path, residual_draw(e, z, removed, S,
+                                       uniform(seed, step, depth, RESIDUAL_DRAW, lane))
         path.append(nxt)
         cur = nxt
         depth += 1

@@ -1,5 +1,5 @@
 """Python binding of libeagle.so: one EAGLE / EAGLE-2 draft-and-verify cycle
-at batch 1 on an MI355X (gfx950).
+on an MI355X (gfx950), for one sequence or a batch of lanes.
 
 Argument marshalling only: every step of the cycle runs in the library's
 HIP kernels. PyTorch provides device memory (three uint8 tensors sized by
@@ -16,7 +16,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libeagle.so")
 
-MAX_STATIC, MAX_DEPTH, MAX_VERIFY, MAX_NODES, MAX_TOPK = 64, 16, 128, 1024, 16
+MAX_STATIC, MAX_DEPTH, MAX_VERIFY, MAX_NODES, MAX_TOPK, MAX_BATCH = 64, 16, 128, 1024, 16, 8
 F32, BF16 = 0, 1
 OK, E_INVALID, E_STATE, E_CAPACITY, E_BUFFER, E_HIP, E_DEVICE = range(7)
 HEAD_E1, HEAD_E3 = 0, 1
@@ -34,7 +34,8 @@ class Config(ctypes.Structure):
                 ("topk", i32), ("expand", i32), ("depth", i32), ("budget", i32),
                 ("n_static", i32), ("static_parent", i32 * MAX_STATIC),
                 ("static_rank", i32 * MAX_STATIC), ("max_ctx", i32), ("prefill_chunk", i32),
-                ("temperature", f32), ("seed_lo", ctypes.c_uint32), ("seed_hi", ctypes.c_uint32)]
+                ("temperature", f32), ("seed_lo", ctypes.c_uint32), ("seed_hi", ctypes.c_uint32),
+                ("batch", i32)]
 
 
 class Sizes(ctypes.Structure):
@@ -95,10 +96,14 @@ def lib():
         L.eagle_tensor_info.argtypes = [P(Config), i32, P(Tensor)]
         L.eagle_load.argtypes = [P(Config), P(Buffers), vp, P(vp)]
         L.eagle_prefill.argtypes = [vp, P(i32), i32, P(i32)]
+        L.eagle_prefill_lane.argtypes = [vp, i32, P(i32), i32, P(i32)]
         L.eagle_draft_tree.argtypes = [vp, P(Tree)]
+        L.eagle_read_tree.argtypes = [vp, i32, P(Tree)]
         L.eagle_verify.argtypes = [vp, P(Tree), P(i32), P(i32)]
+        L.eagle_verify_batch.argtypes = [vp, P(i32), P(i32)]
         L.eagle_generate.argtypes = [vp, P(i32), i32, i32, P(i32), P(i32), P(Stats)]
         L.eagle_committed.argtypes = [vp, P(i32), i32, P(i32)]
+        L.eagle_committed_lane.argtypes = [vp, i32, P(i32), i32, P(i32)]
         L.eagle_debug_read.argtypes = [vp, i32, vp, u64, P(i32)]
         L.eagle_set_debug.argtypes = [vp, i32]
         L.eagle_set_sampling.argtypes = [vp, f32, ctypes.c_uint32, ctypes.c_uint32]
@@ -148,6 +153,7 @@ def make_config(w: dict, max_ctx: int = None, prefill_chunk: int = 0) -> Config:
     c.temperature = float(w.get("temperature", 0.0))
     seed = int(w.get("seed", 0))
     c.seed_lo, c.seed_hi = seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF
+    c.batch = int(w.get("batch", 1))
     return c
 
 
@@ -224,17 +230,32 @@ class Engine:
             pass
 
     # ------------------------------------------------------------ calls
-    def prefill(self, prompt) -> int:
+    def prefill(self, prompt, lane: int = 0) -> int:
         p = np.ascontiguousarray(prompt, dtype=np.int32)
         b = i32()
-        self._check(lib().eagle_prefill(self.ctx, _i32p(p), len(p), ctypes.byref(b)), "eagle_prefill")
+        self._check(lib().eagle_prefill_lane(self.ctx, lane, _i32p(p), len(p), ctypes.byref(b)),
+                    "eagle_prefill_lane")
         return int(b.value)
 
     def draft_tree(self, want: bool = True):
+        """Drafts every lane's tree; returns lane 0's (or None)."""
         t = Tree() if want else None
         self._check(lib().eagle_draft_tree(self.ctx, ctypes.byref(t) if want else None),
                     "eagle_draft_tree")
         return tree_to_dict(t) if want else None
+
+    def read_tree(self, lane: int):
+        t = Tree()
+        self._check(lib().eagle_read_tree(self.ctx, lane, ctypes.byref(t)), "eagle_read_tree")
+        return tree_to_dict(t)
+
+    def verify_batch(self):
+        """Verifies every lane's drafted tree; returns each lane's committed tokens."""
+        B = max(self.cfg.batch, 1)
+        out = (i32 * (B * (MAX_DEPTH + 1)))()
+        n = (i32 * B)()
+        self._check(lib().eagle_verify_batch(self.ctx, out, n), "eagle_verify_batch")
+        return [list(out[b * (MAX_DEPTH + 1):b * (MAX_DEPTH + 1) + n[b]]) for b in range(B)]
 
     def verify(self, planted: dict = None):
         tp = None
@@ -262,12 +283,13 @@ class Engine:
                      accept_hist=list(st.accept_hist))
         return out[:n.value].tolist(), stats
 
-    def committed(self):
+    def committed(self, lane: int = 0):
         n = i32()
-        self._check(lib().eagle_committed(self.ctx, None, 0, ctypes.byref(n)), "eagle_committed")
+        self._check(lib().eagle_committed_lane(self.ctx, lane, None, 0, ctypes.byref(n)),
+                    "eagle_committed_lane")
         out = np.zeros(max(n.value, 1), dtype=np.int32)
-        self._check(lib().eagle_committed(self.ctx, _i32p(out), n.value, ctypes.byref(n)),
-                    "eagle_committed")
+        self._check(lib().eagle_committed_lane(self.ctx, lane, _i32p(out), n.value, ctypes.byref(n)),
+                    "eagle_committed_lane")
         return out[:n.value].tolist()
 
     def profile(self, on=True, every: int = 1):
@@ -305,7 +327,9 @@ class Engine:
         width = {0: self.cfg.hidden, 1: self.cfg.vocab, 2: 1, 3: 1}[code]
         dt = np.int32 if code == 2 else np.float32
         rows = i32()
-        buf = np.zeros(MAX_VERIFY * width if code else max(self.sizes.verify_rows, 1024) * width, dtype=dt)
+        B = max(self.cfg.batch, 1)
+        rows_cap = B * MAX_VERIFY if code else max(B * self.sizes.verify_rows, 1024)
+        buf = np.zeros(rows_cap * width, dtype=dt)
         self._check(lib().eagle_debug_read(self.ctx, code, buf.ctypes.data, buf.nbytes,
                                            ctypes.byref(rows)), "eagle_debug_read")
         return buf[:rows.value * width].reshape(rows.value, width) if width > 1 else buf[:rows.value]

@@ -56,6 +56,31 @@ __device__ __forceinline__ bool row_sees(const RowVis& rv, int prehi, uint64_t m
   return ((j < 64 ? (m0 >> j) : (m1 >> (j - 64))) & 1ull) != 0;
 }
 
+// Sequence b of a multi-sequence launch: row range, per-row inputs, cache
+// and key positions (see Lanes). The lane's offset is picked with selects,
+// not a dynamic index into the kernel arguments.
+__device__ __forceinline__ int lane_off(const Lanes& ln, int lane) {
+  int o = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_LANES; ++i) o = i == lane ? ln.off[i] : o;
+  return o;
+}
+__device__ __forceinline__ RowVis lane_vis(const RowVis& v, const Lanes& ln, int lane) {
+  RowVis r = v;
+  const int o = lane_off(ln, lane);
+  r.tree_base += o;
+  r.key_end += o;
+  r.prehi = (const int32_t*)((const char*)v.prehi + lane * ln.bytes);
+  r.mask = (const uint64_t*)((const char*)v.mask + lane * ln.bytes);
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ KVView lane_kv(const KVView& v, int lane) {
+  KVView r = v;
+  r.base = (T*)v.base + lane * v.lane_elems;
+  return r;
+}
+
 struct AttnArgs {
   const bf16_t* q; int64_t qlo;
   KVView kv;
@@ -65,6 +90,8 @@ struct AttnArgs {
   float scale;
   float* opart;
   float* mlpart;
+  Lanes ln;
+  int n_groups;   // pair groups per sequence: blockIdx.z = sequence * n_groups + group
 };
 
 // 16-byte column c of a staged K row of key index `key`: XOR-swizzled so the
@@ -78,8 +105,14 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int chunk = blockIdx.x, hk = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
-  const int k0 = a.vis.pre_lo + chunk * CK;
-  const int k1 = min(a.vis.key_end, k0 + CK);
+  // this workgroup's sequence: its rows r0 .. r0 + Ml - 1 of the launch's Mt
+  const int seq = blockIdx.z / a.n_groups, grp = blockIdx.z - seq * a.n_groups;
+  const int Mt = a.M, Ml = a.ln.n > 1 ? a.ln.rows : a.M, r0 = seq * Ml;
+  const RowVis vis = lane_vis(a.vis, a.ln, seq);
+  const KVView kv = lane_kv<bf16_t>(a.kv, seq);
+  const int k0 = vis.pre_lo + chunk * CK;
+  if (k0 >= vis.key_end) return;   // a shorter sequence: uniform over the workgroup
+  const int k1 = min(vis.key_end, k0 + CK);
 
   // ---- stage the chunk (keys past k1 repeat the last key; they are masked).
   // Every load of this thread is issued before the first LDS store, so the
@@ -88,18 +121,18 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   // A chunk spans at most two KV pages (the launcher checks page >= CHUNK):
   // both page-table entries are read once, up front, so no KV address waits
   // on a per-element table load.
-  const int pgsz = a.kv.page, psh = page_shift(a.kv), pA = k0 >> psh;
-  const int pgA = a.kv.page_table[pA], pgB = a.kv.page_table[(k1 - 1) >> psh];
+  const int pgsz = kv.page, psh = page_shift(kv), pA = k0 >> psh;
+  const int pgA = kv.page_table[pA], pgB = kv.page_table[(k1 - 1) >> psh];
   auto kvp = [&](int key, int plane) {
     const int pg = ((key >> psh) == pA) ? pgA : pgB;
-    return (const bf16_t*)a.kv.base + (int64_t)pg * a.kv.page_elems +
-           ((int64_t)(plane * a.kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
+    return (const bf16_t*)kv.base + (int64_t)pg * kv.page_elems +
+           ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
   };
   // (query head, row block) pairs; fewer pairs than waves: split keys
   // pairs of this workgroup: group blockIdx.z of a.ppg (query head, row
   // block) pairs; a GQA head with many pairs and few chunks spreads its pairs
   // over several workgroups
-  const int nrb = (a.M + 15) / 16, pbase = blockIdx.z * a.ppg;
+  const int nrb = (Ml + 15) / 16, pbase = grp * a.ppg;
   const int P = min(a.ppg, a.group * nrb - pbase);
   int kw = 1;
   while (P * kw * 2 <= 4 && kw * 2 <= CK / 32) kw *= 2;
@@ -114,16 +147,16 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   uint64_t mk0 = 0, mk1 = 0;
   auto load_pair = [&](int pr) {
     const int h = hk * a.group + (pbase + pr) / nrb, rb = (pbase + pr) % nrb;
-    const int rowc = min(rb * 16 + lr, a.M - 1);
-    const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
+    const int rowc = min(rb * 16 + lr, Ml - 1);
+    const bf16_t* qp = a.q + ((int64_t)(r0 + rowc) * a.nq + h) * D + 8 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       qf[s] = ld16(qp + 32 * s);
       ql[s] = ld16(qp + a.qlo + 32 * s);
     }
-    prehi = a.vis.prehi[rowc];
-    mk0 = a.vis.mask[2 * rowc];
-    mk1 = a.vis.mask[2 * rowc + 1];
+    prehi = vis.prehi[rowc];
+    mk0 = vis.mask[2 * rowc];
+    mk1 = vis.mask[2 * rowc + 1];
   };
   if (active) load_pair(pr0);
   uint4 kr[8], va[4], vb[4];
@@ -202,7 +235,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = k0 + kb0 + 8 * g + 4 * hh + e;
-            const bool ok = key < k1 && row_sees(a.vis, prehi, mk0, mk1, key);
+            const bool ok = key < k1 && row_sees(vis, prehi, mk0, mk1, key);
             p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
             bm = fmaxf(bm, p[4 * hh + e]);
           }
@@ -246,14 +279,14 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       }
     }
     if (kw == 1) {
-      if (row < a.M) {
-        float* op = a.opart + (((int64_t)chunk * a.M + row) * a.nq + h) * D;
+      if (row < Ml) {
+        float* op = a.opart + (((int64_t)chunk * Mt + r0 + row) * a.nq + h) * D;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) op[16 * dt + 4 * g + e] = o[dt][e];
         if (g == 0) {
-          float* ml = a.mlpart + (((int64_t)chunk * a.M + row) * a.nq + h) * 2;
+          float* ml = a.mlpart + (((int64_t)chunk * Mt + r0 + row) * a.nq + h) * 2;
           ml[0] = m_run;
           ml[1] = l_run;
         }
@@ -294,8 +327,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       wk[k] = mk == -INFINITY ? 0.f : exp2f(mk - gm);
       lsum += wk[k] * mm[((wave + k * P) * 16 + lr) * 2 + 1];
     }
-    if (row < a.M) {
-      float* op = a.opart + (((int64_t)chunk * a.M + row) * a.nq + h) * D;
+    if (row < Ml) {
+      float* op = a.opart + (((int64_t)chunk * Mt + r0 + row) * a.nq + h) * D;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
@@ -306,7 +339,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
           op[dd] = acc;
         }
       if (g == 0) {
-        float* ml = a.mlpart + (((int64_t)chunk * a.M + row) * a.nq + h) * 2;
+        float* ml = a.mlpart + (((int64_t)chunk * Mt + r0 + row) * a.nq + h) * 2;
         ml[0] = gm;
         ml[1] = lsum;
       }
@@ -319,13 +352,24 @@ constexpr int ATTN_MAX_CHUNKS = 2048;
 // Merges the per-chunk (max, sum, O) partials of one (row, head): the chunk
 // weights exp(m_c - max) are computed once into LDS, then each thread sums
 // its output element over the chunks in chunk order, eight loads in flight.
+// Key chunks of each sequence of a launch.
+struct LaneChunks {
+  int rows;                // rows per sequence (every row is sequence 0's when n == 1)
+  int n;
+  int chunks[MAX_LANES];
+};
+
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* opart, const float* mlpart,
-                                                           int n_chunks, int M, int nq, int d,
+                                                           LaneChunks lc, int M, int nq, int d,
                                                            T* out, int64_t lo) {
   __shared__ float sw[ATTN_MAX_CHUNKS];
   __shared__ float red[4];
   const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seq = lc.n > 1 ? r / lc.rows : 0;
+  int n_chunks = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_LANES; ++i) n_chunks = i == seq ? lc.chunks[i] : n_chunks;
   const int64_t cs = (int64_t)M * nq;   // (row, head) records per chunk
   const float* ml0 = mlpart + ((int64_t)r * nq + h) * 2;
   float mx = -INFINITY;
@@ -363,13 +407,16 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* opart, c
 }
 
 // fp32 path: one 64-lane wave per (row, head), keys in order, online softmax.
-__global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, KVView kv, RowVis vis, int M,
-                                                      int nq, int group, int d, float scale,
-                                                      float* out) {
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, KVView kv_all, RowVis vis_all,
+                                                      Lanes ln, int M, int nq, int group, int d,
+                                                      float scale, float* out) {
   const int r = blockIdx.x, h = blockIdx.y, hk = h / group;
   const int lane = threadIdx.x;
-  const int prehi = vis.prehi[r];
-  const uint64_t mk0 = vis.mask[2 * r], mk1 = vis.mask[2 * r + 1];
+  const int seq = ln.n > 1 ? r / ln.rows : 0, j = ln.n > 1 ? r - seq * ln.rows : r;
+  const RowVis vis = lane_vis(vis_all, ln, seq);
+  const KVView kv = lane_kv<float>(kv_all, seq);
+  const int prehi = vis.prehi[j];
+  const uint64_t mk0 = vis.mask[2 * j], mk1 = vis.mask[2 * j + 1];
   const float* qr = q + ((int64_t)r * nq + h) * d;
   float qv[4], ov[4] = {0.f, 0.f, 0.f, 0.f};
   const int nper = (d + 63) / 64;
@@ -517,9 +564,15 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
                                                       int nkv, int d, const int32_t* pos,
                                                       const int32_t* slot,
                                                       const float* cos_t, const float* sin_t,
-                                                      T* q_out, int64_t qlo, KVView kv) {
+                                                      T* q_out, int64_t qlo, KVView kv_all,
+                                                      Lanes ln) {
   __shared__ float xs[1024];
   const int r = blockIdx.x;
+  // the row's sequence: its position / slot entries and its cache
+  const int seq = ln.n > 1 ? r / ln.rows : 0, j = ln.n > 1 ? r - seq * ln.rows : r;
+  pos = (const int32_t*)((const char*)pos + seq * ln.bytes);
+  slot = (const int32_t*)((const char*)slot + seq * ln.bytes);
+  const KVView kv = lane_kv<T>(kv_all, seq);
   const int half = d / 2;
   const int hpw = 1024 / d;
   const int n_heads = nq + 2 * nkv;
@@ -535,9 +588,9 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
     if (ok[0]) *reinterpret_cast<float4*>(xs + e) = acc[0];
   }
   __syncthreads();
-  const float* c = cos_t + (int64_t)pos[r] * half;
-  const float* s = sin_t + (int64_t)pos[r] * half;
-  const int sl = slot[r];
+  const float* c = cos_t + (int64_t)pos[j] * half;
+  const float* s = sin_t + (int64_t)pos[j] * half;
+  const int sl = slot[j];
   for (int idx = threadIdx.x; idx < nh * half; idx += 256) {
     const int lh = idx / half, i = idx % half;
     const int head = h0 + lh;
@@ -730,48 +783,61 @@ hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int
 
 hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int M, int nq, int nkv,
                           int d, const int32_t* pos, const int32_t* slot, const float* cos_t,
-                          const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st) {
+                          const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st,
+                          const Lanes& ln) {
   if (kv_page_bad(kv)) return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
+  if (ln.n < 1 || ln.n > MAX_LANES || (ln.n > 1 && ln.rows * ln.n != M)) return hipErrorInvalidValue;
   if (d < 4 || d > 1024 || 1024 % d != 0 || ((nq + 2 * nkv) * d) % 4 != 0) return hipErrorInvalidValue;
   const int hpw = 1024 / d;
   const dim3 grid(M, (nq + 2 * nkv + hpw - 1) / hpw);
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv),
-              hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv));
+              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv, ln),
+              hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv, ln));
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, RowVis vis, int M,
                             int nq, int d, float scale, float* opart, float* mlpart, void* out_t,
-                            int64_t olo, hipStream_t st) {
+                            int64_t olo, hipStream_t st, const Lanes& ln) {
   if (kv_page_bad(kv)) return hipErrorInvalidValue;
   if (M <= 0) return hipSuccess;
+  if (ln.n < 1 || ln.n > MAX_LANES || (ln.n > 1 && ln.rows * ln.n != M)) return hipErrorInvalidValue;
   const int group = nq / kv.n_kv;
+  // every sequence needs at least one key; the grid covers the longest
+  LaneChunks lc{ln.n > 1 ? ln.rows : M, ln.n, {}};
+  int n_chunks = 0;
+  for (int b = 0; b < ln.n; ++b) {
+    const int c = (vis.key_end + ln.off[b] - vis.pre_lo + CHUNK - 1) / CHUNK;
+    if (c <= 0) return hipErrorInvalidValue;
+    lc.chunks[b] = c;
+    n_chunks = std::max(n_chunks, c);
+  }
   if (dtype == 1) {
     if (d != 128) return hipErrorInvalidValue;
-    const int n_chunks = (vis.key_end - vis.pre_lo + CHUNK - 1) / CHUNK;
-    if (n_chunks <= 0 || n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK) return hipErrorInvalidValue;
+    if (n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK) return hipErrorInvalidValue;
     // scores are taken in log2 units (scale * log2 e) so the softmax uses the
     // native exp2; chunk maxima in mlpart are in the same units
     // split a head's pairs over more workgroups only while the (chunk, KV
     // head) grid is short of two workgroups per CU: every extra group stages
     // the chunk again
-    const int pairs = group * ((M + 15) / 16);
-    const int want = (512 + n_chunks * kv.n_kv - 1) / (n_chunks * kv.n_kv);
+    const int pairs = group * ((lc.rows + 15) / 16);   // per sequence
+    const int wgs = n_chunks * kv.n_kv * ln.n;
+    const int want = (512 + wgs - 1) / wgs;
     int n_groups = std::max(1, std::min((pairs + 3) / 4, want));
     const int ppg = (pairs + n_groups - 1) / n_groups;
     n_groups = (pairs + ppg - 1) / ppg;
-    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, ppg, scale * 1.4426950408889634f, opart, mlpart};
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv, n_groups), dim3(256), 0, st, a);
+    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, ppg, scale * 1.4426950408889634f,
+               opart, mlpart, ln, n_groups};
+    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv, n_groups * ln.n), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(M, nq), dim3(128), 0, st, opart, mlpart,
-                       n_chunks, M, nq, d, (bf16_t*)out_t, olo);
+                       lc, M, nq, d, (bf16_t*)out_t, olo);
   } else {
     if (d > 256) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(attn_f32_kernel, dim3(M, nq), dim3(64), 0, st, (const float*)q, kv, vis, M,
-                       nq, group, d, scale, (float*)out_t);
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(M, nq), dim3(64), 0, st, (const float*)q, kv, vis, ln,
+                       M, nq, group, d, scale, (float*)out_t);
   }
   return hipGetLastError();
 }

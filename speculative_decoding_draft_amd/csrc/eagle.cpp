@@ -31,7 +31,8 @@ struct Derived {
   int qkv_rows, kin_draft, fc_in;
   int k_b, k_e, D, budget, dynamic;
   int Mv, n_nodes_max, tree_rows_max;
-  int chunk, Mmax;
+  int B;           // sequences served together (eagle_config.batch)
+  int chunk, Mmax, lane_rows;
   int t_slots, d_slots, t_pages, d_pages, max_pos, max_chunks;
   int rows_per_pass[EAGLE_MAX_DEPTH + 1];   // rows of draft pass p (p >= 2)
   // static plan
@@ -84,6 +85,9 @@ bool derive(const eagle_config* c, Derived* z, std::string* why) {
   if (c->topk < 1 || c->topk > EAGLE_MAX_TOPK) return fail(why, "topk must be in [1, %d]", EAGLE_MAX_TOPK);
   if (c->topk > c->vocab) return fail(why, "topk must be <= vocab");
   if (c->depth < 1 || c->depth > EAGLE_MAX_DEPTH) return fail(why, "depth must be in [1, %d]", EAGLE_MAX_DEPTH);
+  static_assert(EAGLE_MAX_BATCH <= MAX_LANES, "a launch serves at most MAX_LANES sequences");
+  if (c->batch < 0 || c->batch > EAGLE_MAX_BATCH) return fail(why, "batch must be in [0, %d] (0 = 1)", EAGLE_MAX_BATCH);
+  z->B = c->batch > 0 ? c->batch : 1;
 
   z->H = c->hidden; z->nq = c->n_heads; z->nkv = c->n_kv_heads; z->d = d; z->F = c->ffn;
   z->V = c->vocab; z->NL = c->n_layers; z->dt = c->dtype; z->esz = c->dtype == EAGLE_BF16 ? 2 : 4;
@@ -162,7 +166,9 @@ bool derive(const eagle_config* c, Derived* z, std::string* why) {
   z->chunk = c->prefill_chunk > 0 ? c->prefill_chunk : 256;
   int pass_rows = 1;
   for (int p = 2; p <= z->D; ++p) pass_rows = std::max(pass_rows, z->rows_per_pass[p]);
-  z->Mmax = std::max({z->chunk, z->Mv, z->D + 1, pass_rows});
+  // one pass serves every sequence: B times the rows of one
+  z->Mmax = std::max({z->chunk, z->B * z->Mv, z->B * (z->D + 1), z->B * pass_rows});
+  z->lane_rows = std::max(z->chunk, z->D + 1);   // rows of a prefill chunk or a catch-up
   z->t_slots = c->max_ctx + z->Mv + 1;
   z->d_slots = c->max_ctx + 2 + z->tree_rows_max + z->D + 1;
   z->t_pages = (z->t_slots + KV_PAGE - 1) / KV_PAGE;
@@ -239,6 +245,28 @@ uint64_t gemm_ws_floats(const Derived& z) {
   return mx;
 }
 
+// One sequence of a batch: its host state and its device state (tree,
+// acceptance result, committed tokens, per-row descriptors). The device
+// arrays of every sequence share one layout, lane_bytes apart (see
+// carve_lane), so one launch can serve all sequences.
+struct Lane {
+  TreeDev t;
+  int32_t *acc, *new_tok, *cu_src, *seq;
+  int32_t *rpos, *rslot, *rprehi;
+  uint64_t* rmask;
+  float* dout;   // draft outputs: row 0 = the root row, then each pass's rows
+  // acceptance result in pinned, coherent host memory: [0] tag, [1] L,
+  // [2 ..] committed tokens; written by the acceptance kernel through hres_dev
+  int32_t* hres = nullptr;
+  int32_t* hres_dev = nullptr;
+  uint32_t step = 0;   // sampling draw step: 0 = the prefill's token, i = the i-th verify
+  int state = ST_EMPTY;
+  int ctx_len = 0;
+  std::vector<int32_t> committed;
+};
+constexpr int HRES_INTS = 64;   // pinned result ints per sequence (one 256-byte line)
+static_assert(HRES_INTS >= 2 + EAGLE_MAX_DEPTH + 2, "result block too small");
+
 }  // namespace
 
 // ------------------------------------------------------------ context
@@ -262,25 +290,17 @@ struct eagle_ctx {
   float *cos_t, *sin_t;
   int32_t *tpt, *dpt;
   float *h, *tfeat, *gbuf, *hcat, *dout, *opart, *mlpart, *gpart, *hpart, *logits, *margin, *logp;
+  int64_t dout_stride = 0;   // floats between two sequences' draft outputs
   float* ebuf;
   double* zpart;
   void *xop, *qop, *aop, *fop, *lmh, *lmh2;   // activation operands (two planes for bf16)
   int64_t xlo = 0, qlo = 0, alo = 0, flo = 0, lmhlo = 0, lmh2lo = 0;  // lo-plane offsets (elements)
-  int32_t *g, *ids, *acc, *new_tok, *cu_src, *iota, *seq;
-  int32_t *rpos, *rslot, *rprehi;
-  uint64_t* rmask;
-  TreeDev t;
+  int32_t *g, *ids, *iota;
   TreeParams tp;
-  // acceptance result in pinned, coherent host memory: [0] tag, [1] L,
-  // [2 ..] committed tokens; written by the acceptance kernel through hres_dev
-  int32_t* hres = nullptr;
-  int32_t* hres_dev = nullptr;
+  std::vector<Lane> lanes;   // one per sequence (config batch)
+  int64_t lane_bytes = 0;    // distance between two sequences' device state
+  int32_t* hres = nullptr;   // pinned block of every sequence's result
   int32_t verify_tag = 0;
-  uint32_t step = 0;   // sampling draw step: 0 = the prefill's token, i = the i-th verify
-  // host state
-  int state = ST_EMPTY;
-  int ctx_len = 0;
-  std::vector<int32_t> committed;
   bool debug = false;
   int last_target_rows = 0, last_verify_rows = 0;
   std::string err;
@@ -306,10 +326,68 @@ namespace {
     if (x) x->field = p_;                          \
   } while (0)
 
+#define LTAKE(field, T, count)                     \
+  do {                                             \
+    T* p_ = cv.take<T>((uint64_t)(count));         \
+    if (l) l->field = p_;                          \
+  } while (0)
+
+// The device state of one sequence, carved from `base` (NULL: sizing only).
+// Every sequence's block has this layout, so sequence b's copy of an array
+// sits b * lane_bytes after sequence 0's.
+uint64_t carve_lane(const Derived& z, char* base, Lane* l) {
+  Carve cv;
+  cv.base = base;
+  LTAKE(acc, int32_t, 2 + EAGLE_MAX_DEPTH + 2);
+  LTAKE(new_tok, int32_t, EAGLE_MAX_DEPTH + 2);
+  LTAKE(cu_src, int32_t, EAGLE_MAX_DEPTH + 2);
+  LTAKE(seq, int32_t, (uint64_t)z.t_slots + z.D + 4);
+  LTAKE(rpos, int32_t, z.lane_rows);
+  LTAKE(rslot, int32_t, z.lane_rows);
+  LTAKE(rprehi, int32_t, z.lane_rows);
+  LTAKE(rmask, uint64_t, 2 * (uint64_t)z.lane_rows);
+  LTAKE(t.tok, int32_t, TREE_MAXN);
+  LTAKE(t.parent, int32_t, TREE_MAXN);
+  LTAKE(t.depth, int32_t, TREE_MAXN);
+  LTAKE(t.srcrow, int32_t, TREE_MAXN);
+  LTAKE(t.rank, int32_t, TREE_MAXN);
+  LTAKE(t.row_of_node, int32_t, TREE_MAXN);
+  LTAKE(t.v_row_of_node, int32_t, TREE_MAXN);
+  LTAKE(t.logv, float, TREE_MAXN);
+  LTAKE(t.logp, float, TREE_MAXN);
+  LTAKE(t.counts, int32_t, 8);
+  LTAKE(t.exp_nodes, int32_t, TREE_MAXEXP);
+  LTAKE(t.row_tok, int32_t, TREE_MAXEXP);
+  LTAKE(t.row_src, int32_t, TREE_MAXEXP);
+  LTAKE(t.row_pos, int32_t, TREE_MAXEXP);
+  LTAKE(t.row_slot, int32_t, TREE_MAXEXP);
+  LTAKE(t.row_prehi, int32_t, TREE_MAXEXP);
+  LTAKE(t.row_mask, uint64_t, 2 * TREE_MAXEXP);
+  LTAKE(t.tmask, uint64_t, 2 * TREE_MAXROWS);
+  LTAKE(t.v_tok, int32_t, TREE_MAXROWS);
+  LTAKE(t.v_parent, int32_t, TREE_MAXROWS);
+  LTAKE(t.v_depth, int32_t, TREE_MAXROWS);
+  LTAKE(t.v_node, int32_t, TREE_MAXROWS);
+  LTAKE(t.v_pos, int32_t, TREE_MAXROWS);
+  LTAKE(t.v_slot, int32_t, TREE_MAXROWS);
+  LTAKE(t.v_prehi, int32_t, TREE_MAXROWS);
+  LTAKE(t.v_logv, float, TREE_MAXROWS);
+  LTAKE(t.v_mask, uint64_t, 2 * TREE_MAXROWS);
+  LTAKE(t.s_parent, int32_t, EAGLE_MAX_STATIC);
+  LTAKE(t.s_rank, int32_t, EAGLE_MAX_STATIC);
+  LTAKE(t.s_depth, int32_t, EAGLE_MAX_STATIC);
+  LTAKE(t.s_prow, int32_t, EAGLE_MAX_STATIC);
+  LTAKE(t.s_exp, int32_t, (EAGLE_MAX_DEPTH + 1) * TREE_MAXEXP);
+  LTAKE(t.s_nexp, int32_t, EAGLE_MAX_DEPTH + 1);
+  return cv.off;
+}
+#undef LTAKE
+
 uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
   Carve cv;
   cv.base = x ? x->S : nullptr;
   const int M = z.Mmax;
+  const uint64_t B = z.B;
   const uint64_t kmax = std::max({z.H, z.fc_in, z.kin_draft, z.F, z.nq * z.d});
   const uint64_t es = z.esz;
   TAKE(cos_t, float, (uint64_t)z.max_pos * z.d / 2);
@@ -320,84 +398,58 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
   TAKE(tfeat, float, (uint64_t)M * z.H);
   TAKE(gbuf, float, (uint64_t)M * z.H);
   TAKE(hcat, float, (uint64_t)M * z.H);
-  TAKE(dout, float, (uint64_t)(1 + z.tree_rows_max) * z.H);
+  TAKE(dout, float, B * (1 + z.tree_rows_max) * z.H);
   TAKE(opart, float, (uint64_t)z.max_chunks * M * z.nq * z.d);
   TAKE(mlpart, float, (uint64_t)z.max_chunks * M * z.nq * 2);
   TAKE(gpart, float, gemm_ws_floats(z));
-  TAKE(hpart, float, lmhead_part_floats(std::max(z.Mv, TREE_MAXEXP), z.V, z.k_b));
-  TAKE(logits, float, (uint64_t)z.Mv * z.V);
-  TAKE(ebuf, float, (uint64_t)z.Mv * z.V);                        // sampling: exp((l - max) / T)
-  TAKE(zpart, double, sample_zpart_doubles(z.Mv, z.V));            // sampling: block sums of e
-  TAKE(margin, float, z.Mv);
-  TAKE(logp, float, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
+  // LM-head partials: the largest need over every row count a call can take
+  // (calls above 80 rows run in 64-row passes)
+  uint64_t hp = 0;
+  for (int m = 1; m <= (int)B * std::max(z.Mv, TREE_MAXEXP); ++m)
+    hp = std::max(hp, lmhead_part_floats(m, z.V, z.k_b));
+  TAKE(hpart, float, hp);
+  TAKE(logits, float, B * z.Mv * z.V);
+  TAKE(ebuf, float, B * z.Mv * z.V);                              // sampling: exp((l - max) / T)
+  TAKE(zpart, double, sample_zpart_doubles((int)B * z.Mv, z.V));  // sampling: block sums of e
+  TAKE(margin, float, B * z.Mv);
+  TAKE(logp, float, B * TREE_MAXEXP * EAGLE_MAX_TOPK);
   TAKE(xop, char, 2 * (uint64_t)M * kmax * es);
   TAKE(qop, char, 2 * (uint64_t)M * z.nq * z.d * es);
   TAKE(aop, char, 2 * (uint64_t)M * z.nq * z.d * es);
   TAKE(fop, char, 2 * (uint64_t)M * z.F * es);
   TAKE(lmh, char, 2 * (uint64_t)M * 3 * z.H * es);
-  TAKE(lmh2, char, 2 * (uint64_t)(z.D + 1) * 3 * z.H * es);
+  TAKE(lmh2, char, 2 * B * (z.D + 1) * 3 * z.H * es);
   if (x) {
     x->xlo = (int64_t)M * kmax;
     x->qlo = x->alo = (int64_t)M * z.nq * z.d;
     x->flo = (int64_t)M * z.F;
     x->lmhlo = (int64_t)M * 3 * z.H;
-    x->lmh2lo = (int64_t)(z.D + 1) * 3 * z.H;
+    x->lmh2lo = (int64_t)B * (z.D + 1) * 3 * z.H;
+    x->dout_stride = (int64_t)(1 + z.tree_rows_max) * z.H;
   }
-  TAKE(g, int32_t, z.Mv);
-  TAKE(ids, int32_t, (uint64_t)TREE_MAXEXP * EAGLE_MAX_TOPK);
-  TAKE(acc, int32_t, 2 + EAGLE_MAX_DEPTH + 2);
-  TAKE(new_tok, int32_t, EAGLE_MAX_DEPTH + 2);
-  TAKE(cu_src, int32_t, EAGLE_MAX_DEPTH + 2);
+  TAKE(g, int32_t, B * z.Mv);
+  TAKE(ids, int32_t, B * TREE_MAXEXP * EAGLE_MAX_TOPK);
   TAKE(iota, int32_t, M);
-  TAKE(seq, int32_t, (uint64_t)z.t_slots + z.D + 4);
-  TAKE(rpos, int32_t, M);
-  TAKE(rslot, int32_t, M);
-  TAKE(rprehi, int32_t, M);
-  TAKE(rmask, uint64_t, 2 * (uint64_t)M);
-  // tree state
-  TAKE(t.tok, int32_t, TREE_MAXN);
-  TAKE(t.parent, int32_t, TREE_MAXN);
-  TAKE(t.depth, int32_t, TREE_MAXN);
-  TAKE(t.srcrow, int32_t, TREE_MAXN);
-  TAKE(t.rank, int32_t, TREE_MAXN);
-  TAKE(t.row_of_node, int32_t, TREE_MAXN);
-  TAKE(t.v_row_of_node, int32_t, TREE_MAXN);
-  TAKE(t.logv, float, TREE_MAXN);
-  TAKE(t.logp, float, TREE_MAXN);
-  TAKE(t.counts, int32_t, 8);
-  TAKE(t.exp_nodes, int32_t, TREE_MAXEXP);
-  TAKE(t.row_tok, int32_t, TREE_MAXEXP);
-  TAKE(t.row_src, int32_t, TREE_MAXEXP);
-  TAKE(t.row_pos, int32_t, TREE_MAXEXP);
-  TAKE(t.row_slot, int32_t, TREE_MAXEXP);
-  TAKE(t.row_prehi, int32_t, TREE_MAXEXP);
-  TAKE(t.row_mask, uint64_t, 2 * TREE_MAXEXP);
-  TAKE(t.tmask, uint64_t, 2 * TREE_MAXROWS);
-  TAKE(t.v_tok, int32_t, TREE_MAXROWS);
-  TAKE(t.v_parent, int32_t, TREE_MAXROWS);
-  TAKE(t.v_depth, int32_t, TREE_MAXROWS);
-  TAKE(t.v_node, int32_t, TREE_MAXROWS);
-  TAKE(t.v_pos, int32_t, TREE_MAXROWS);
-  TAKE(t.v_slot, int32_t, TREE_MAXROWS);
-  TAKE(t.v_prehi, int32_t, TREE_MAXROWS);
-  TAKE(t.v_logv, float, TREE_MAXROWS);
-  TAKE(t.v_mask, uint64_t, 2 * TREE_MAXROWS);
-  TAKE(t.s_parent, int32_t, EAGLE_MAX_STATIC);
-  TAKE(t.s_rank, int32_t, EAGLE_MAX_STATIC);
-  TAKE(t.s_depth, int32_t, EAGLE_MAX_STATIC);
-  TAKE(t.s_prow, int32_t, EAGLE_MAX_STATIC);
-  TAKE(t.s_exp, int32_t, (EAGLE_MAX_DEPTH + 1) * TREE_MAXEXP);
-  TAKE(t.s_nexp, int32_t, EAGLE_MAX_DEPTH + 1);
+  // per-sequence state
+  const uint64_t lb = carve_lane(z, nullptr, nullptr);
+  char* l0 = cv.take<char>(B * lb);
+  if (x) {
+    x->lane_bytes = (int64_t)lb;
+    x->lanes.assign(B, Lane());
+    for (uint64_t b = 0; b < B; ++b) carve_lane(z, l0 + b * lb, &x->lanes[b]);
+    for (uint64_t b = 0; b < B; ++b) x->lanes[b].dout = x->dout + b * x->dout_stride;
+  }
   // eagle_load stages weight blocks of 16 rows through scratch when it
   // packs bf16 matrices: keep room for at least one block of the widest.
   return std::max<uint64_t>(cv.off, 16 * kmax * es);
 }
 #undef TAKE
 
+// Target cache [layer][sequence][page], then draft cache [sequence][page].
 uint64_t kv_bytes_of(const Derived& z) {
   const uint64_t page_elems = (uint64_t)kv_planes(z.dt) * z.nkv * KV_PAGE * z.d;
-  return align_up((uint64_t)z.NL * z.t_pages * page_elems * z.esz) +
-         align_up((uint64_t)z.d_pages * page_elems * z.esz);
+  return align_up((uint64_t)z.NL * z.B * z.t_pages * page_elems * z.esz) +
+         align_up((uint64_t)z.B * z.d_pages * page_elems * z.esz);
 }
 
 eagle_status set_err(eagle_ctx* c, eagle_status s, const char* fmt, ...) {
@@ -408,7 +460,8 @@ eagle_status set_err(eagle_ctx* c, eagle_status s, const char* fmt, ...) {
     vsnprintf(buf, sizeof(buf), fmt, ap);
     va_end(ap);
     c->err = buf;
-    if (s == EAGLE_E_HIP || s == EAGLE_E_DEVICE) c->state = ST_FAILED;
+    if (s == EAGLE_E_HIP || s == EAGLE_E_DEVICE)
+      for (Lane& l : c->lanes) l.state = ST_FAILED;
   }
   return s;
 }
@@ -522,9 +575,43 @@ double gemm_bytes(const Derived& z, int M, int rows, int K, int n_out, int epi) 
   const double y = (double)M * n_out * 4.0;
   return w + x + y;
 }
-double attn_bytes(const Derived& z, int M, const RowVis& v) {
-  const double keys = (double)(v.key_end - v.pre_lo);
+double attn_bytes(const Derived& z, int M, const RowVis& v, const Lanes& ln) {
+  double keys = 0.0;
+  for (int b = 0; b < ln.n; ++b) keys += (double)(v.key_end + ln.off[b] - v.pre_lo);
   return keys * z.nkv * z.d * 2.0 * 4.0 + 2.0 * M * z.nq * z.d * 4.0;   // K,V: fp32 or hi + lo
+}
+
+// ------------------------------------------------------------ sequences
+// The sequences one pass serves: lanes [first, first + n), `rows` rows each,
+// sequence by sequence.
+struct Span {
+  int first, n, rows;
+  int M() const { return n * rows; }
+};
+
+// Per-launch description of a span for the kernels that serve several
+// sequences: row split, per-row input stride and each sequence's key shift
+// relative to the first (their context lengths differ).
+Lanes lanes_of(const eagle_ctx* c, Span s) {
+  Lanes ln;
+  ln.n = s.n;
+  ln.rows = s.rows;
+  ln.bytes = c->lane_bytes;
+  for (int b = 0; b < s.n; ++b)
+    ln.off[b] = c->lanes[s.first + b].ctx_len - c->lanes[s.first].ctx_len;
+  return ln;
+}
+
+// A cache view that starts at sequence `b`.
+KVView lane_view(KVView v, int b, int esz) {
+  v.base = (char*)v.base + (int64_t)b * v.lane_elems * esz;
+  return v;
+}
+
+// Sequence b's copy of a per-sequence device array given sequence 0's.
+template <typename T>
+T* lane_ptr(T* p, int b, int64_t bytes) {
+  return (T*)((char*)p + (int64_t)b * bytes);
 }
 
 // ------------------------------------------------------------ passes
@@ -540,12 +627,13 @@ eagle_status resnorm(eagle_ctx* c, float* h, int M, int S, bool set, const float
   return EAGLE_OK;
 }
 
-// One decoder layer over M rows. On entry xop holds the normed layer input
-// (row width kin); on exit the down-projection partials are pending in gpart
-// (*s_down planes) for the caller's resnorm.
+// One decoder layer over M rows (the rows of every sequence of `ln`). On
+// entry xop holds the normed layer input (row width kin); on exit the
+// down-projection partials are pending in gpart (*s_down planes) for the
+// caller's resnorm.
 eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, float* h,
                         const int32_t* pos, const int32_t* slot, KVView kv, RowVis vis,
-                        bool target, int* s_down) {
+                        const Lanes& ln, bool target, int* s_down) {
   const Derived& z = c->z;
   const int dt = z.dt;
   const int cls_part = target ? EAGLE_PROF_GEMM : EAGLE_PROF_DRAFT;
@@ -556,11 +644,11 @@ eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, fl
                        z.qkv_rows, nullptr, 0, &S, c->st, tm_));
   PROFILED(EAGLE_PROF_ROWS, (double)M * z.qkv_rows * 4.0 * (S + 1),
            launch_rope_kv(dt, c->gpart, S, (int64_t)M * z.qkv_rows, M, z.nq, z.nkv, z.d, pos, slot,
-                          c->cos_t, c->sin_t, c->qop, c->qlo, kv, c->st));
-  PROFILED(EAGLE_PROF_ATTN, attn_bytes(z, M, vis),
+                          c->cos_t, c->sin_t, c->qop, c->qlo, kv, c->st, ln));
+  PROFILED(EAGLE_PROF_ATTN, attn_bytes(z, M, vis, ln),
            launch_attention(dt, c->qop, c->qlo, kv, vis, M, z.nq, z.d,
                             1.0f / std::sqrt((float)z.d), c->opart, c->mlpart, c->aop, c->alo,
-                            c->st));
+                            c->st, ln));
   PROFILED_KERNEL(cls_part, gemm_bytes(z, M, z.H, z.nq * z.d, z.H, EPI_PART),
            launch_gemm(dt, EPI_PART, w.wo, c->aop, c->alo, M, z.H, z.nq * z.d, c->gpart, z.H,
                        nullptr, 0, &S, c->st, tm_));
@@ -574,18 +662,24 @@ eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, fl
   return EAGLE_OK;
 }
 
-// Target forward over M rows; leaves f in tfeat and its operand in xop.
-eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t* pos,
+// Target forward over the rows of span s; leaves f in tfeat and its operand
+// in xop. tok, pos, slot and vis's per-row arrays are the first sequence's.
+eagle_status target_pass(eagle_ctx* c, Span s, const int32_t* tok, const int32_t* pos,
                          const int32_t* slot, RowVis vis) {
   const Derived& z = c->z;
-  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 4.0,
-           launch_embed(z.dt, c->embed, z.H, tok, M, c->h, c->st));
+  const int M = s.M();
+  const Lanes ln = lanes_of(c, s);
+  for (int b = 0; b < s.n; ++b)
+    PROFILED(EAGLE_PROF_ROWS, (double)s.rows * z.H * 4.0,
+             launch_embed(z.dt, c->embed, z.H, lane_ptr(tok, b, c->lane_bytes), s.rows,
+                          c->h + (int64_t)b * s.rows * z.H, c->st));
   SCHK(resnorm(c, c->h, M, 0, false, c->tl[0].attn_norm, nullptr));
   for (int l = 0; l < z.NL; ++l) {
     KVView kv = c->tkv0;
     kv.base = (char*)c->tkv0.base + (int64_t)l * c->t_layer_elems * z.esz;
+    kv = lane_view(kv, s.first, z.esz);
     int sd = 1;
-    SCHK(layer_core(c, c->tl[l], z.H, M, c->h, pos, slot, kv, vis, true, &sd));
+    SCHK(layer_core(c, c->tl[l], z.H, M, c->h, pos, slot, kv, vis, ln, true, &sd));
     const bool last = l + 1 == z.NL;
     SCHK(resnorm(c, c->h, M, sd, false, last ? c->final_norm : c->tl[l + 1].attn_norm,
                  last ? c->tfeat : nullptr));
@@ -600,74 +694,104 @@ eagle_status target_pass(eagle_ctx* c, int M, const int32_t* tok, const int32_t*
   return EAGLE_OK;
 }
 
-// Draft rows (feature feat[idx[r]], token tok[r]) -> residual stream hout;
-// leaves the LM-head operand of every row in xop.
-eagle_status draft_pass(eagle_ctx* c, int M, const int32_t* tok, const float* feat,
-                        const int32_t* idx, const int32_t* pos, const int32_t* slot, RowVis vis,
-                        float* hout) {
+// Draft rows of span s -> residual stream hout (M rows); leaves the LM-head
+// operand of every row in xop. Row r of sequence b pairs token tok_b[r] with
+// the feature row idx_b[r] of feat + b * feat_stride, where tok_b, idx_b are
+// sequence b's copies (idx: idx_bytes apart; 0 = one shared index array).
+eagle_status draft_pass(eagle_ctx* c, Span s, const int32_t* tok, const float* feat,
+                        int64_t feat_stride, const int32_t* idx, int64_t idx_bytes,
+                        const int32_t* pos, const int32_t* slot, RowVis vis, float* hout) {
   const Derived& z = c->z;
+  const int M = s.M();
+  const int64_t xrow = 2 * (int64_t)z.H;   // draft input operand row: [emb; feature]
   if (c->cfg.head == EAGLE_HEAD_E1) {
     int S = 1;
-    PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
-             launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->xlo, c->st));
+    for (int b = 0; b < s.n; ++b)
+      PROFILED(EAGLE_PROF_ROWS, (double)s.rows * z.H * 12.0,
+               launch_draft_input_e1(z.dt, c->embed, lane_ptr(tok, b, c->lane_bytes),
+                                     feat + b * feat_stride, lane_ptr(idx, b, idx_bytes), s.rows,
+                                     z.H, (char*)c->xop + (int64_t)b * s.rows * xrow * z.esz,
+                                     c->xlo, c->st));
     PROFILED_KERNEL(EAGLE_PROF_DRAFT, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_PART),
              launch_gemm(z.dt, EPI_PART, c->fc, c->xop, c->xlo, M, z.H, 2 * z.H, c->gpart, z.H,
                          nullptr, 0, &S, c->st, tm_));
     SCHK(resnorm(c, hout, M, S, true, c->dl.attn_norm, nullptr));
   } else {
-    PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 16.0,
-             launch_draft_input_e3(z.dt, c->embed, tok, feat, idx, c->dl.attn_norm,
-                                   c->cfg.rms_eps, M, z.H, c->xop, c->xlo, hout, c->st));
+    for (int b = 0; b < s.n; ++b)
+      PROFILED(EAGLE_PROF_ROWS, (double)s.rows * z.H * 16.0,
+               launch_draft_input_e3(z.dt, c->embed, lane_ptr(tok, b, c->lane_bytes),
+                                     feat + b * feat_stride, lane_ptr(idx, b, idx_bytes),
+                                     c->dl.attn_norm, c->cfg.rms_eps, s.rows, z.H,
+                                     (char*)c->xop + (int64_t)b * s.rows * xrow * z.esz, c->xlo,
+                                     hout + (int64_t)b * s.rows * z.H, c->st));
   }
   int sd = 1;
-  SCHK(layer_core(c, c->dl, z.kin_draft, M, hout, pos, slot, c->dkv, vis, false, &sd));
+  SCHK(layer_core(c, c->dl, z.kin_draft, M, hout, pos, slot, lane_view(c->dkv, s.first, z.esz),
+                  vis, lanes_of(c, s), false, &sd));
   SCHK(resnorm(c, hout, M, sd, false, nullptr, nullptr));
   return EAGLE_OK;
 }
 
-// Draft catch-up over M committed pairs at positions first..first+M-1; the
-// features are feat[idx[r]] (true target features, EAGLE-3: fused). If
-// final, the last row becomes the root row: its top-k are the depth-1 nodes.
-eagle_status catch_up(eagle_ctx* c, int M, int first, const int32_t* tok, const float* feat,
+// Draft catch-up of sequence b over M committed pairs at positions
+// first..first+M-1; the features are feat[idx[r]] (true target features,
+// EAGLE-3: fused). If final, the last row becomes the root row: its top-k
+// are the depth-1 nodes.
+eagle_status catch_up(eagle_ctx* c, int b, int M, int first, const int32_t* tok, const float* feat,
                       const int32_t* idx, bool final, int ctx_after) {
   const Derived& z = c->z;
-  HCHK(launch_rows_causal(first, M, c->rpos, c->rslot, c->rprehi, c->rmask, c->st));
-  RowVis vis{c->rprehi, c->rmask, 1, 0, 0, first + M};
-  SCHK(draft_pass(c, M, tok, feat, idx, c->rpos, c->rslot, vis, c->hcat));
+  Lane& q = c->lanes[b];
+  HCHK(launch_rows_causal(first, M, q.rpos, q.rslot, q.rprehi, q.rmask, c->st));
+  RowVis vis{q.rprehi, q.rmask, 1, 0, 0, first + M};
+  SCHK(draft_pass(c, Span{b, 1, M}, tok, feat, 0, idx, 0, q.rpos, q.rslot, vis, c->hcat));
   if (!final) return EAGLE_OK;
-  HCHK(hipMemcpyAsync(c->dout, c->hcat + (int64_t)(M - 1) * z.H, sizeof(float) * z.H,
+  HCHK(hipMemcpyAsync(q.dout, c->hcat + (int64_t)(M - 1) * z.H, sizeof(float) * z.H,
                       hipMemcpyDeviceToDevice, c->st));
   const void* xl = (const char*)c->xop + (int64_t)(M - 1) * z.H * z.esz;
   PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)z.H * 4.0,
            launch_lmhead_topk(z.dt, c->lm, xl, c->xlo, 1, z.V, z.H, z.k_b, c->hpart, c->ids,
                               c->logp, c->st));
-  PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_append(c->t, c->tp, c->ids, c->logp, 1, ctx_after, c->st));
+  PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_append(q.t, c->tp, c->ids, c->logp, 1, ctx_after, c->st));
   return EAGLE_OK;
 }
 
-// The verify's catch-up before the acceptance length is known on the host:
-// all depth + 1 rows after the root are drafted (rows past the committed
-// ones read the filler the acceptance kernel wrote and only touch draft KV
-// slots that the next cycle overwrites before reading; every row attends
-// causally, so the committed rows are exactly what a catch-up over them
-// alone computes). The new root row is row L = acc[0], picked on the device
-// for the LM head, and the tree is restarted at position ctx + L + 1.
-eagle_status catch_up_fixed(eagle_ctx* c, int ctx, const float* feat, const int32_t* idx) {
+// The verify's catch-up, for every sequence, before the acceptance lengths
+// are known on the host: all depth + 1 rows after each root are drafted
+// (rows past the committed ones read the filler the acceptance kernel wrote
+// and only touch draft KV slots that the next cycle overwrites before
+// reading; every row attends causally, so the committed rows are exactly
+// what a catch-up over them alone computes). Sequence b's new root row is
+// its row L = acc[0], picked on the device for the LM head, and its tree is
+// restarted at position ctx + L + 1. Features: feat + b * feat_stride,
+// rows idx_b[r] (idx_bytes apart per sequence).
+eagle_status catch_up_fixed(eagle_ctx* c, const float* feat, int64_t feat_stride,
+                            const int32_t* idx, int64_t idx_bytes) {
   const Derived& z = c->z;
-  const int M = z.D + 1;
-  HCHK(launch_rows_causal(ctx + 1, M, c->rpos, c->rslot, c->rprehi, c->rmask, c->st));
-  RowVis vis{c->rprehi, c->rmask, 1, 0, 0, ctx + 1 + M};
-  SCHK(draft_pass(c, M, c->new_tok, feat, idx, c->rpos, c->rslot, vis, c->hcat));
-  PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
-           launch_gather_f32(c->hcat, z.H, c->acc, 1, z.H, c->dout, c->st));
-  // the root row's LM-head operand, gathered to the (now free) q operand buffer
-  PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
-           launch_gather_t(z.dt, c->xop, z.H, c->xlo, c->acc, 1, z.H, c->qop, c->qlo, c->st));
-  PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)z.H * 4.0,
-           launch_lmhead_topk(z.dt, c->lm, c->qop, c->qlo, 1, z.V, z.H, z.k_b, c->hpart, c->ids,
+  const int M1 = z.D + 1, B = z.B;
+  const Lane& q0 = c->lanes[0];
+  for (const Lane& q : c->lanes)
+    HCHK(launch_rows_causal(q.ctx_len + 1, M1, q.rpos, q.rslot, q.rprehi, q.rmask, c->st));
+  RowVis vis{q0.rprehi, q0.rmask, 1, 0, 0, q0.ctx_len + 1 + M1};
+  SCHK(draft_pass(c, Span{0, B, M1}, q0.new_tok, feat, feat_stride, idx, idx_bytes, q0.rpos,
+                  q0.rslot, vis, c->hcat));
+  for (int b = 0; b < B; ++b) {
+    const Lane& q = c->lanes[b];
+    PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
+             launch_gather_f32(c->hcat + (int64_t)b * M1 * z.H, z.H, q.acc, 1, z.H, q.dout, c->st));
+    // the root row's LM-head operand, gathered to row b of the (now free) q operand buffer
+    PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
+             launch_gather_t(z.dt, (const char*)c->xop + (int64_t)b * M1 * z.H * z.esz, z.H, c->xlo,
+                             q.acc, 1, z.H, (char*)c->qop + (int64_t)b * z.H * z.esz, c->qlo,
+                             c->st));
+  }
+  PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)B * z.H * 4.0,
+           launch_lmhead_topk(z.dt, c->lm, c->qop, c->qlo, B, z.V, z.H, z.k_b, c->hpart, c->ids,
                               c->logp, c->st));
-  PROFILED(EAGLE_PROF_TREE, 0.0,
-           launch_tree_append(c->t, c->tp, c->ids, c->logp, 1, ctx, c->st, c->acc));
+  for (int b = 0; b < B; ++b) {
+    const Lane& q = c->lanes[b];
+    PROFILED(EAGLE_PROF_TREE, 0.0,
+             launch_tree_append(q.t, c->tp, c->ids + b * z.k_b, c->logp + b * z.k_b, 1, q.ctx_len,
+                                c->st, q.acc));
+  }
   return EAGLE_OK;
 }
 
@@ -685,7 +809,8 @@ eagle_status fuse_rows(eagle_ctx* c, int M, const void* src, int64_t src_lo) {
 
 eagle_status check_ready(eagle_ctx* c) {
   if (!c) return EAGLE_E_INVALID;
-  if (c->state == ST_FAILED) return set_err(c, EAGLE_E_STATE, "context failed earlier; call eagle_prefill");
+  for (const Lane& l : c->lanes)
+    if (l.state == ST_FAILED) return set_err(c, EAGLE_E_STATE, "context failed earlier; call eagle_prefill");
   return EAGLE_OK;
 }
 
@@ -754,14 +879,16 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
   c->W = (char*)bufs->weights;
   c->KV = (char*)bufs->kv;
   c->S = (char*)bufs->scratch;
+  int32_t* hres_dev = nullptr;
+  const size_t hres_bytes = sizeof(int32_t) * HRES_INTS * z.B;
   if (hipGetDevice(&c->device) != hipSuccess ||
-      hipHostMalloc((void**)&c->hres, sizeof(int32_t) * (2 + EAGLE_MAX_DEPTH + 2),
-                    hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
-      hipHostGetDevicePointer((void**)&c->hres_dev, c->hres, 0) != hipSuccess) {
+      hipHostMalloc((void**)&c->hres, hres_bytes, hipHostMallocMapped | hipHostMallocCoherent) !=
+          hipSuccess ||
+      hipHostGetDevicePointer((void**)&hres_dev, c->hres, 0) != hipSuccess) {
     delete c;
     return EAGLE_E_HIP;
   }
-  std::memset(c->hres, 0, sizeof(int32_t) * (2 + EAGLE_MAX_DEPTH + 2));
+  std::memset(c->hres, 0, hres_bytes);
   // weights
   auto ptr = [&](int kind, int group, int layer) -> const void* {
     for (const eagle_tensor& e : tab)
@@ -785,12 +912,17 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
   for (int l = 0; l < z.NL; ++l) c->tl.push_back(lw(EAGLE_G_TARGET, l));
   c->dl = lw(EAGLE_G_DRAFT, 0);
   // KV views
+  // KV views: each sequence has its own pages (the page tables are shared)
   const int64_t page_elems = (int64_t)kv_planes(z.dt) * z.nkv * KV_PAGE * z.d;
-  c->t_layer_elems = (int64_t)z.t_pages * page_elems;
+  c->t_layer_elems = (int64_t)z.B * z.t_pages * page_elems;
   plan_scratch(z, c);
-  c->tkv0 = KVView{c->KV, c->tpt, page_elems, KV_PAGE, z.nkv, z.d};
+  for (int b = 0; b < z.B; ++b) {
+    c->lanes[b].hres = c->hres + HRES_INTS * b;
+    c->lanes[b].hres_dev = hres_dev + HRES_INTS * b;
+  }
+  c->tkv0 = KVView{c->KV, c->tpt, page_elems, KV_PAGE, z.nkv, z.d, (int64_t)z.t_pages * page_elems};
   c->dkv = KVView{c->KV + align_up((uint64_t)z.NL * c->t_layer_elems * z.esz), c->dpt, page_elems,
-                  KV_PAGE, z.nkv, z.d};
+                  KV_PAGE, z.nkv, z.d, (int64_t)z.d_pages * page_elems};
   // bf16 matrices the GEMM and LM-head kernels stream are fragment-packed in
   // place, a batch of 16-row blocks at a time through the (still unused)
   // scratch buffer; the embedding stays row-major (rows are gathered).
@@ -857,12 +989,14 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
     up(c->tpt, tp.data(), tp.size() * 4);
     up(c->dpt, dp.data(), dp.size() * 4);
     up(c->iota, io.data(), io.size() * 4);
-    up(c->t.s_parent, sp.data(), sp.size() * 4);
-    up(c->t.s_rank, sr.data(), sr.size() * 4);
-    up(c->t.s_depth, sd.data(), sd.size() * 4);
-    up(c->t.s_prow, sw.data(), sw.size() * 4);
-    up(c->t.s_exp, se.data(), se.size() * 4);
-    up(c->t.s_nexp, sne.data(), sne.size() * 4);
+    for (const Lane& q : c->lanes) {
+      up(q.t.s_parent, sp.data(), sp.size() * 4);
+      up(q.t.s_rank, sr.data(), sr.size() * 4);
+      up(q.t.s_depth, sd.data(), sd.size() * 4);
+      up(q.t.s_prow, sw.data(), sw.size() * 4);
+      up(q.t.s_exp, se.data(), se.size() * 4);
+      up(q.t.s_nexp, sne.data(), sne.size() * 4);
+    }
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
       delete c;
@@ -873,23 +1007,27 @@ eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void
   return EAGLE_OK;
 }
 
-eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32_t* first_token) {
+eagle_status eagle_prefill_lane(eagle_ctx* c, int32_t lane, const int32_t* prompt, int32_t n,
+                                int32_t* first_token) {
   if (!c) return EAGLE_E_INVALID;
   const Derived& z = c->z;
+  if (lane < 0 || lane >= z.B) return set_err(c, EAGLE_E_INVALID, "lane %d is not in [0, batch = %d)", lane, z.B);
   if (!prompt || n < 1) return set_err(c, EAGLE_E_INVALID, "prompt must hold at least one token");
   if (n + 1 > c->cfg.max_ctx) return set_err(c, EAGLE_E_CAPACITY, "prompt of %d tokens exceeds max_ctx", n);
   for (int i = 0; i < n; ++i)
     if (prompt[i] < 0 || prompt[i] >= z.V) return set_err(c, EAGLE_E_INVALID, "prompt[%d] = %d is not in [0, vocab)", i, prompt[i]);
-  c->state = ST_EMPTY;
-  c->committed.clear();
-  c->step = 0;
-  HCHK(hipMemcpyAsync(c->seq, prompt, sizeof(int32_t) * n, hipMemcpyHostToDevice, c->st));
+  Lane& q = c->lanes[lane];
+  q.state = ST_EMPTY;
+  q.committed.clear();
+  q.step = 0;
+  q.ctx_len = 0;
+  HCHK(hipMemcpyAsync(q.seq, prompt, sizeof(int32_t) * n, hipMemcpyHostToDevice, c->st));
   for (int c0 = 0; c0 < n; c0 += z.chunk) {
     const int M = std::min(z.chunk, n - c0);
     const bool last = c0 + M == n;
-    HCHK(launch_rows_causal(c0, M, c->rpos, c->rslot, c->rprehi, c->rmask, c->st));
-    RowVis vis{c->rprehi, c->rmask, 0, 0, 0, c0 + M};
-    SCHK(target_pass(c, M, c->seq + c0, c->rpos, c->rslot, vis));
+    HCHK(launch_rows_causal(c0, M, q.rpos, q.rslot, q.rprehi, q.rmask, c->st));
+    RowVis vis{q.rprehi, q.rmask, 0, 0, 0, c0 + M};
+    SCHK(target_pass(c, Span{lane, 1, M}, q.seq + c0, q.rpos, q.rslot, vis));
     if (last) {
       const void* xl = (const char*)c->xop + (int64_t)(M - 1) * z.H * z.esz;
       const bool smp = sampling(c);
@@ -897,10 +1035,11 @@ eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32
                                 smp ? c->logits : nullptr, c->st));
       if (smp) {
         HCHK(launch_row_exp(c->logits, c->g, 1, z.V, c->cfg.temperature, c->ebuf, c->zpart, c->st));
-        HCHK(launch_sample_token(c->ebuf, c->zpart, z.V, seed_of(c), 0, c->seq + n, c->st));
+        HCHK(launch_sample_token(c->ebuf, c->zpart, z.V, seed_of(c), 0, (uint32_t)lane, q.seq + n,
+                                 c->st));
       }
       else
-        HCHK(hipMemcpyAsync(c->seq + n, c->g, 4, hipMemcpyDeviceToDevice, c->st));
+        HCHK(hipMemcpyAsync(q.seq + n, c->g, 4, hipMemcpyDeviceToDevice, c->st));
     }
     if (plain_mode(c)) continue;
     const float* feat = c->tfeat;
@@ -908,23 +1047,27 @@ eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32
       SCHK(fuse_rows(c, M, c->lmh, c->lmhlo));
       feat = c->gbuf;
     }
-    SCHK(catch_up(c, M, c0 + 1, c->seq + c0 + 1, feat, c->iota, last, n));
+    SCHK(catch_up(c, lane, M, c0 + 1, q.seq + c0 + 1, feat, c->iota, last, n));
   }
   int32_t b = 0;
-  HCHK(hipMemcpyAsync(&b, c->seq + n, 4, hipMemcpyDeviceToHost, c->st));
+  HCHK(hipMemcpyAsync(&b, q.seq + n, 4, hipMemcpyDeviceToHost, c->st));
   HCHK(hipStreamSynchronize(c->st));
-  c->committed.push_back(b);
-  c->ctx_len = n;
-  c->state = ST_READY;
+  q.committed.push_back(b);
+  q.ctx_len = n;
+  q.state = ST_READY;
   if (first_token) *first_token = b;
   return EAGLE_OK;
 }
 
+eagle_status eagle_prefill(eagle_ctx* c, const int32_t* prompt, int32_t n, int32_t* first_token) {
+  return eagle_prefill_lane(c, 0, prompt, n, first_token);
+}
+
 namespace {
-eagle_status copy_tree_out(eagle_ctx* c, eagle_tree* out) {
-  const Derived& z = c->z;
+eagle_status copy_tree_out(eagle_ctx* c, int lane, eagle_tree* out) {
+  const Lane& q = c->lanes[lane];
   int32_t counts[8];
-  HCHK(hipMemcpyAsync(counts, c->t.counts, sizeof(counts), hipMemcpyDeviceToHost, c->st));
+  HCHK(hipMemcpyAsync(counts, q.t.counts, sizeof(counts), hipMemcpyDeviceToHost, c->st));
   HCHK(hipStreamSynchronize(c->st));
   std::memset(out, 0, sizeof(*out));
   const int nr = counts[3], nn = counts[0];
@@ -933,78 +1076,111 @@ eagle_status copy_tree_out(eagle_ctx* c, eagle_tree* out) {
   auto d2h = [&](void* dst, const void* src, size_t bytes) {
     return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, c->st);
   };
-  HCHK(d2h(out->token, c->t.v_tok, 4 * nr));
-  HCHK(d2h(out->parent, c->t.v_parent, 4 * nr));
-  HCHK(d2h(out->depth, c->t.v_depth, 4 * nr));
-  HCHK(d2h(out->logv, c->t.v_logv, 4 * nr));
-  HCHK(d2h(out->node, c->t.v_node, 4 * nr));
+  HCHK(d2h(out->token, q.t.v_tok, 4 * nr));
+  HCHK(d2h(out->parent, q.t.v_parent, 4 * nr));
+  HCHK(d2h(out->depth, q.t.v_depth, 4 * nr));
+  HCHK(d2h(out->logv, q.t.v_logv, 4 * nr));
+  HCHK(d2h(out->node, q.t.v_node, 4 * nr));
   if (nn > 0) {
-    HCHK(d2h(out->node_token, c->t.tok, 4 * nn));
-    HCHK(d2h(out->node_parent, c->t.parent, 4 * nn));
-    HCHK(d2h(out->node_depth, c->t.depth, 4 * nn));
-    HCHK(d2h(out->node_logv, c->t.logv, 4 * nn));
-    HCHK(d2h(out->node_logp, c->t.logp, 4 * nn));
+    HCHK(d2h(out->node_token, q.t.tok, 4 * nn));
+    HCHK(d2h(out->node_parent, q.t.parent, 4 * nn));
+    HCHK(d2h(out->node_depth, q.t.depth, 4 * nn));
+    HCHK(d2h(out->node_logv, q.t.logv, 4 * nn));
+    HCHK(d2h(out->node_logp, q.t.logp, 4 * nn));
   }
   HCHK(hipStreamSynchronize(c->st));
-  (void)z;
   return EAGLE_OK;
 }
 }  // namespace
 
 eagle_status eagle_draft_tree(eagle_ctx* c, eagle_tree* out) {
   SCHK(check_ready(c));
-  if (c->state != ST_READY) return set_err(c, EAGLE_E_STATE, "eagle_draft_tree needs a READY context (call eagle_prefill / eagle_verify)");
+  for (const Lane& q : c->lanes)
+    if (q.state != ST_READY)
+      return set_err(c, EAGLE_E_STATE, "eagle_draft_tree needs every sequence READY (call eagle_prefill / eagle_verify)");
   const Derived& z = c->z;
-  const int ctx = c->ctx_len;
+  const int B = z.B;
   if (plain_mode(c)) {
-    HCHK(launch_tree_masks(c->t, 1, ctx, c->seq + ctx, c->st));
+    for (const Lane& q : c->lanes)
+      HCHK(launch_tree_masks(q.t, 1, q.ctx_len, q.seq + q.ctx_len, c->st));
   } else {
+    // each pass drafts the same number of rows for every sequence
+    const Lane& q0 = c->lanes[0];
+    const int ctx0 = q0.ctx_len;
     int t0 = 0;
     for (int pass = 2; pass <= z.D; ++pass) {
       const int M = z.rows_per_pass[pass];
       if (M <= 0) break;
-      RowVis vis{c->t.row_prehi, c->t.row_mask, 1, ctx + 1, t0 + M, ctx + 1 + t0 + M};
-      SCHK(draft_pass(c, M, c->t.row_tok, c->dout, c->t.row_src, c->t.row_pos, c->t.row_slot, vis,
-                      c->dout + (int64_t)(1 + t0) * z.H));
-      PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)M * z.H * 4.0,
-               launch_lmhead_topk(z.dt, c->lm, c->xop, c->xlo, M, z.V, z.H, z.k_b, c->hpart,
+      RowVis vis{q0.t.row_prehi, q0.t.row_mask, 1, ctx0 + 1, t0 + M, ctx0 + 1 + t0 + M};
+      // one sequence writes its draft outputs in place; several go through
+      // hcat and are scattered to each sequence's rows afterwards
+      float* hout = B == 1 ? q0.dout + (int64_t)(1 + t0) * z.H : c->hcat;
+      SCHK(draft_pass(c, Span{0, B, M}, q0.t.row_tok, q0.dout, c->dout_stride, q0.t.row_src,
+                      c->lane_bytes, q0.t.row_pos, q0.t.row_slot, vis, hout));
+      if (B > 1)
+        HCHK(hipMemcpy2DAsync(q0.dout + (int64_t)(1 + t0) * z.H, sizeof(float) * c->dout_stride,
+                              c->hcat, sizeof(float) * M * z.H, sizeof(float) * M * z.H, B,
+                              hipMemcpyDeviceToDevice, c->st));
+      PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)B * M * z.H * 4.0,
+               launch_lmhead_topk(z.dt, c->lm, c->xop, c->xlo, B * M, z.V, z.H, z.k_b, c->hpart,
                                   c->ids, c->logp, c->st));
-      PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_append(c->t, c->tp, c->ids, c->logp, pass, ctx, c->st));
+      for (int b = 0; b < B; ++b) {
+        const Lane& q = c->lanes[b];
+        PROFILED(EAGLE_PROF_TREE, 0.0,
+                 launch_tree_append(q.t, c->tp, c->ids + (int64_t)b * M * z.k_b,
+                                    c->logp + (int64_t)b * M * z.k_b, pass, q.ctx_len, c->st));
+      }
       t0 += M;
     }
-    PROFILED(EAGLE_PROF_TREE, 0.0, launch_tree_finalize(c->t, c->tp, ctx, c->seq + ctx, c->st));
+    for (const Lane& q : c->lanes)
+      PROFILED(EAGLE_PROF_TREE, 0.0,
+               launch_tree_finalize(q.t, c->tp, q.ctx_len, q.seq + q.ctx_len, c->st));
   }
-  c->state = ST_DRAFTED;
-  if (out) SCHK(copy_tree_out(c, out));
+  for (Lane& q : c->lanes) q.state = ST_DRAFTED;
+  if (out) SCHK(copy_tree_out(c, 0, out));
   return EAGLE_OK;
 }
 
+eagle_status eagle_read_tree(eagle_ctx* c, int32_t lane, eagle_tree* out) {
+  if (!c || !out) return EAGLE_E_INVALID;
+  if (lane < 0 || lane >= c->z.B) return set_err(c, EAGLE_E_INVALID, "lane %d is not in [0, batch = %d)", lane, c->z.B);
+  if (c->lanes[lane].state != ST_DRAFTED)
+    return set_err(c, EAGLE_E_STATE, "eagle_read_tree needs a drafted tree (call eagle_draft_tree)");
+  return copy_tree_out(c, lane, out);
+}
+
 namespace {
-// Spins until the acceptance kernel has posted `tag` to the pinned result
-// block. Every 4096 polls it asks whether the stream has drained: a drained
-// stream without the tag (an earlier kernel failed) or a stream error ends
-// the wait with an error instead of spinning forever.
-eagle_status wait_result(eagle_ctx* c, int32_t tag) {
+// Spins until sequence `lane`'s acceptance kernel has posted `tag` to its
+// pinned result block. Every 4096 polls it asks whether the stream has
+// drained: a drained stream without the tag (an earlier kernel failed) or a
+// stream error ends the wait with an error instead of spinning forever.
+eagle_status wait_result(eagle_ctx* c, int lane, int32_t tag) {
+  const int32_t* h = c->lanes[lane].hres;
   for (uint32_t spin = 1;; ++spin) {
-    if (__atomic_load_n(c->hres, __ATOMIC_ACQUIRE) == tag) return EAGLE_OK;
+    if (__atomic_load_n(h, __ATOMIC_ACQUIRE) == tag) return EAGLE_OK;
     if ((spin & 4095) == 0) {
-      const hipError_t q = hipStreamQuery(c->st);
-      if (q == hipErrorNotReady) continue;
-      if (__atomic_load_n(c->hres, __ATOMIC_ACQUIRE) == tag) return EAGLE_OK;
-      if (q != hipSuccess) return set_err(c, EAGLE_E_HIP, "stream failed during verify: %s", hipGetErrorString(q));
+      const hipError_t qs = hipStreamQuery(c->st);
+      if (qs == hipErrorNotReady) continue;
+      if (__atomic_load_n(h, __ATOMIC_ACQUIRE) == tag) return EAGLE_OK;
+      if (qs != hipSuccess) return set_err(c, EAGLE_E_HIP, "stream failed during verify: %s", hipGetErrorString(qs));
       return set_err(c, EAGLE_E_DEVICE, "acceptance result was not posted");
     }
   }
 }
-}  // namespace
 
-eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_tokens,
-                          int32_t* n_committed) {
+// Verify of every sequence's drafted tree (or, with one sequence, the
+// planted tree) in one target pass. Sequence b's committed tokens go to
+// out_tokens + b * (EAGLE_MAX_DEPTH + 1) and their count to n_committed[b]
+// (either may be NULL).
+eagle_status verify_all(eagle_ctx* c, const eagle_tree* planted, int32_t* out_tokens,
+                        int32_t* n_committed) {
   SCHK(check_ready(c));
   const Derived& z = c->z;
-  if (planted ? (c->state != ST_READY && c->state != ST_DRAFTED) : c->state != ST_DRAFTED)
-    return set_err(c, EAGLE_E_STATE, "eagle_verify needs a drafted tree (or a planted tree after prefill)");
-  const int ctx = c->ctx_len;
+  const int B = z.B;
+  for (const Lane& q : c->lanes)
+    if (planted ? (q.state != ST_READY && q.state != ST_DRAFTED) : q.state != ST_DRAFTED)
+      return set_err(c, EAGLE_E_STATE, "eagle_verify needs a drafted tree (or a planted tree after prefill)");
+  Lane& q0 = c->lanes[0];
   int Mv;
   if (planted) {
     const int n = planted->n_rows;
@@ -1024,74 +1200,110 @@ eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_
   } else {
     Mv = z.Mv;
   }
-  // the cycle may commit up to depth + 1 tokens after the root at ctx
-  if (ctx + z.D + 2 > c->cfg.max_ctx)
-    return set_err(c, EAGLE_E_CAPACITY, "sequence would exceed max_ctx (%d)", c->cfg.max_ctx);
+  // the cycle may commit up to depth + 1 tokens after each root
+  for (const Lane& q : c->lanes)
+    if (q.ctx_len + z.D + 2 > c->cfg.max_ctx)
+      return set_err(c, EAGLE_E_CAPACITY, "sequence would exceed max_ctx (%d)", c->cfg.max_ctx);
   if (planted) {
     std::vector<int32_t> par(planted->parent, planted->parent + Mv);
     par[0] = -1;
-    HCHK(hipMemcpyAsync(c->t.v_tok, planted->token, 4 * Mv, hipMemcpyHostToDevice, c->st));
-    HCHK(hipMemcpyAsync(c->t.v_parent, par.data(), 4 * Mv, hipMemcpyHostToDevice, c->st));
-    HCHK(launch_tree_masks(c->t, Mv, ctx, c->seq + ctx, c->st));
+    HCHK(hipMemcpyAsync(q0.t.v_tok, planted->token, 4 * Mv, hipMemcpyHostToDevice, c->st));
+    HCHK(hipMemcpyAsync(q0.t.v_parent, par.data(), 4 * Mv, hipMemcpyHostToDevice, c->st));
+    HCHK(launch_tree_masks(q0.t, Mv, q0.ctx_len, q0.seq + q0.ctx_len, c->st));
   }
-  RowVis vis{c->t.v_prehi, c->t.v_mask, 0, ctx, Mv, ctx + Mv};
-  SCHK(target_pass(c, Mv, c->t.v_tok, c->t.v_pos, c->t.v_slot, vis));
+  const int ctx0 = q0.ctx_len;
+  RowVis vis{q0.t.v_prehi, q0.t.v_mask, 0, ctx0, Mv, ctx0 + Mv};
+  SCHK(target_pass(c, Span{0, B, Mv}, q0.t.v_tok, q0.t.v_pos, q0.t.v_slot, vis));
   const bool smp = sampling(c);
-  PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)Mv * z.H * 4.0,
-           launch_lmhead_argmax(z.dt, c->lm, c->xop, c->xlo, Mv, z.V, z.H, c->hpart, c->g,
+  PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)B * Mv * z.H * 4.0,
+           launch_lmhead_argmax(z.dt, c->lm, c->xop, c->xlo, B * Mv, z.V, z.H, c->hpart, c->g,
                                 c->margin, (c->debug || smp) ? c->logits : nullptr, c->st));
-  c->last_verify_rows = Mv;
-  // The acceptance kernel commits the tokens into seq on the device and posts
-  // (L, tokens) to pinned host memory under a fresh tag. The host waits for
-  // that tag only, so the KV compaction queued behind it overlaps the wait and
-  // the catch-up launches queue behind it with no stream drain in between.
+  c->last_verify_rows = B * Mv;
+  // Each acceptance kernel commits its sequence's tokens into seq on the
+  // device and posts (L, tokens) to pinned host memory under a fresh tag. The
+  // host waits for that tag only, so the KV compaction queued behind it
+  // overlaps the wait and the catch-up launches queue behind it with no
+  // stream drain in between.
   const int32_t tag = c->verify_tag = c->verify_tag == INT32_MAX ? 1 : c->verify_tag + 1;
   if (smp) {
-    ++c->step;
+    const int64_t nb = (int64_t)sample_zpart_doubles(1, z.V);
     PROFILED(EAGLE_PROF_TREE, 0.0,
-             launch_row_exp(c->logits, c->g, Mv, z.V, c->cfg.temperature, c->ebuf, c->zpart, c->st));
-    PROFILED(EAGLE_PROF_TREE, 0.0,
-             launch_accept_sample(c->t, c->ebuf, c->zpart, z.V, seed_of(c), c->step, z.D, c->acc,
-                                  c->new_tok, c->cu_src, c->seq + ctx + 1, c->hres_dev, tag,
-                                  c->st));
+             launch_row_exp(c->logits, c->g, B * Mv, z.V, c->cfg.temperature, c->ebuf, c->zpart,
+                            c->st));
+    for (int b = 0; b < B; ++b) {
+      Lane& q = c->lanes[b];
+      ++q.step;
+      PROFILED(EAGLE_PROF_TREE, 0.0,
+               launch_accept_sample(q.t, c->ebuf + (int64_t)b * Mv * z.V, c->zpart + b * Mv * nb,
+                                    z.V, seed_of(c), q.step, (uint32_t)b, z.D, q.acc, q.new_tok,
+                                    q.cu_src, q.seq + q.ctx_len + 1, q.hres_dev, tag, c->st));
+    }
   } else {
-    PROFILED(EAGLE_PROF_TREE, 0.0,
-             launch_accept(c->t, c->g, z.D, c->acc, c->new_tok, c->cu_src, c->seq + ctx + 1,
-                           c->hres_dev, tag, c->st));
+    for (int b = 0; b < B; ++b) {
+      const Lane& q = c->lanes[b];
+      PROFILED(EAGLE_PROF_TREE, 0.0,
+               launch_accept(q.t, c->g + b * Mv, z.D, q.acc, q.new_tok, q.cu_src,
+                             q.seq + q.ctx_len + 1, q.hres_dev, tag, c->st));
+    }
   }
-  PROFILED(EAGLE_PROF_KV, 0.0,
-           launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, c->acc, c->acc + 2, ctx, c->st));
+  for (int b = 0; b < B; ++b) {
+    const Lane& q = c->lanes[b];
+    PROFILED(EAGLE_PROF_KV, 0.0,
+             launch_kv_compact(z.dt, lane_view(c->tkv0, b, z.esz), c->t_layer_elems, z.NL, q.acc,
+                               q.acc + 2, q.ctx_len, c->st));
+  }
   if (!plain_mode(c)) {
     // the catch-up is queued before the host learns L, so the GPU runs on
-    // while the host waits for the acceptance result
-    const float* feat = c->tfeat;
-    const int32_t* idx = c->cu_src;
+    // while the host waits for the acceptance results
     if (c->cfg.head == EAGLE_HEAD_E3) {
-      HCHK(launch_gather_t(z.dt, c->lmh, 3 * z.H, c->lmhlo, c->cu_src, z.D + 1, 3 * z.H, c->lmh2,
-                           c->lmh2lo, c->st));
-      SCHK(fuse_rows(c, z.D + 1, c->lmh2, c->lmh2lo));
-      feat = c->gbuf;
-      idx = c->iota;
+      const int64_t w3 = 3 * (int64_t)z.H;
+      for (int b = 0; b < B; ++b)
+        HCHK(launch_gather_t(z.dt, (const char*)c->lmh + (int64_t)b * Mv * w3 * z.esz, w3,
+                             c->lmhlo, c->lanes[b].cu_src, z.D + 1, (int)w3,
+                             (char*)c->lmh2 + (int64_t)b * (z.D + 1) * w3 * z.esz, c->lmh2lo,
+                             c->st));
+      SCHK(fuse_rows(c, B * (z.D + 1), c->lmh2, c->lmh2lo));
+      SCHK(catch_up_fixed(c, c->gbuf, (int64_t)(z.D + 1) * z.H, c->iota, 0));
+    } else {
+      SCHK(catch_up_fixed(c, c->tfeat, (int64_t)Mv * z.H, q0.cu_src, c->lane_bytes));
     }
-    SCHK(catch_up_fixed(c, ctx, feat, idx));
   }
-  SCHK(wait_result(c, tag));
-  int32_t nt[EAGLE_MAX_DEPTH + 2];
-  const int L = c->hres[1];
-  if (L < 0 || L > z.D) return set_err(c, EAGLE_E_DEVICE, "acceptance length %d out of range", L);
-  std::memcpy(nt, c->hres + 2, sizeof(int32_t) * (L + 1));
-  const int ctx_new = ctx + L + 1;
-  for (int i = 0; i <= L; ++i) c->committed.push_back(nt[i]);
-  c->ctx_len = ctx_new;
-  c->state = ST_READY;
-  if (out_tokens) std::memcpy(out_tokens, nt, sizeof(int32_t) * (L + 1));
-  if (n_committed) *n_committed = L + 1;
+  for (int b = 0; b < B; ++b) SCHK(wait_result(c, b, tag));
+  int Ls[EAGLE_MAX_BATCH];
+  for (int b = 0; b < B; ++b) {
+    Ls[b] = c->lanes[b].hres[1];
+    if (Ls[b] < 0 || Ls[b] > z.D) return set_err(c, EAGLE_E_DEVICE, "acceptance length %d out of range", Ls[b]);
+  }
+  for (int b = 0; b < B; ++b) {
+    Lane& q = c->lanes[b];
+    const int L = Ls[b];
+    const int32_t* nt = q.hres + 2;
+    for (int i = 0; i <= L; ++i) q.committed.push_back(nt[i]);
+    q.ctx_len += L + 1;
+    q.state = ST_READY;
+    if (out_tokens) std::memcpy(out_tokens + b * (EAGLE_MAX_DEPTH + 1), nt, sizeof(int32_t) * (L + 1));
+    if (n_committed) n_committed[b] = L + 1;
+  }
   return EAGLE_OK;
+}
+}  // namespace
+
+eagle_status eagle_verify(eagle_ctx* c, const eagle_tree* planted, int32_t* out_tokens,
+                          int32_t* n_committed) {
+  if (!c) return EAGLE_E_INVALID;
+  if (c->z.B != 1) return set_err(c, EAGLE_E_STATE, "eagle_verify serves batch 1; use eagle_verify_batch");
+  return verify_all(c, planted, out_tokens, n_committed);
+}
+
+eagle_status eagle_verify_batch(eagle_ctx* c, int32_t* out_tokens, int32_t* n_committed) {
+  if (!c) return EAGLE_E_INVALID;
+  return verify_all(c, nullptr, out_tokens, n_committed);
 }
 
 eagle_status eagle_generate(eagle_ctx* c, const int32_t* prompt, int32_t n, int32_t max_new,
                             int32_t* out, int32_t* n_out, eagle_stats* stats) {
   if (!c) return EAGLE_E_INVALID;
+  if (c->z.B != 1) return set_err(c, EAGLE_E_STATE, "eagle_generate serves batch 1");
   if (max_new < 1 || !out) return set_err(c, EAGLE_E_INVALID, "max_new must be >= 1 and out non-NULL");
   if (n + max_new + c->z.D > c->cfg.max_ctx)
     return set_err(c, EAGLE_E_CAPACITY, "prompt + max_new + depth exceeds max_ctx");
@@ -1102,7 +1314,8 @@ eagle_status eagle_generate(eagle_ctx* c, const int32_t* prompt, int32_t n, int3
   HCHK(hipEventCreate(&e0));
   HCHK(hipEventCreate(&e1));
   HCHK(hipEventRecord(e0, c->st));
-  while ((int)c->committed.size() < max_new) {
+  const Lane& q = c->lanes[0];
+  while ((int)q.committed.size() < max_new) {
     SCHK(eagle_draft_tree(c, nullptr));
     int32_t cnt = 0;
     SCHK(eagle_verify(c, nullptr, nullptr, &cnt));
@@ -1116,19 +1329,25 @@ eagle_status eagle_generate(eagle_ctx* c, const int32_t* prompt, int32_t n, int3
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   s.seconds = ms * 1e-3;
-  s.committed = (int64_t)c->committed.size();
-  std::memcpy(out, c->committed.data(), sizeof(int32_t) * max_new);
+  s.committed = (int64_t)q.committed.size();
+  std::memcpy(out, q.committed.data(), sizeof(int32_t) * max_new);
   if (n_out) *n_out = max_new;
   if (stats) *stats = s;
   return EAGLE_OK;
 }
 
-eagle_status eagle_committed(eagle_ctx* c, int32_t* out, int32_t cap, int32_t* n) {
+eagle_status eagle_committed_lane(eagle_ctx* c, int32_t lane, int32_t* out, int32_t cap, int32_t* n) {
   if (!c || (!out && cap > 0)) return EAGLE_E_INVALID;
-  const int k = std::min<int>(cap, (int)c->committed.size());
-  if (k > 0) std::memcpy(out, c->committed.data(), sizeof(int32_t) * k);
-  if (n) *n = (int32_t)c->committed.size();
+  if (lane < 0 || lane >= c->z.B) return set_err(c, EAGLE_E_INVALID, "lane %d is not in [0, batch = %d)", lane, c->z.B);
+  const std::vector<int32_t>& v = c->lanes[lane].committed;
+  const int k = std::min<int>(cap, (int)v.size());
+  if (k > 0) std::memcpy(out, v.data(), sizeof(int32_t) * k);
+  if (n) *n = (int32_t)v.size();
   return EAGLE_OK;
+}
+
+eagle_status eagle_committed(eagle_ctx* c, int32_t* out, int32_t cap, int32_t* n) {
+  return eagle_committed_lane(c, 0, out, cap, n);
 }
 
 eagle_status eagle_set_sampling(eagle_ctx* c, float temperature, uint32_t seed_lo,

@@ -56,6 +56,7 @@ struct KVView {
   const int32_t* page_table;
   int64_t page_elems;   // planes * n_kv * page * d
   int page, n_kv, d;
+  int64_t lane_elems = 0;   // sequence b's cache starts b * lane_elems elements after base
 };
 inline int kv_planes(int dtype) { return dtype == 1 ? 4 : 2; }
 
@@ -66,6 +67,19 @@ struct RowVis {
   const int32_t* prehi;
   const uint64_t* mask;
   int pre_lo, tree_base, n_tree, key_end;
+};
+
+// Several sequences in one launch. Rows [b * rows, (b + 1) * rows) belong to
+// sequence b (b < n). Its per-row inputs (pos, slot, prehi, mask) start
+// `bytes` bytes after sequence 0's, its cache at KVView::lane_elems * b, and
+// its key positions are shifted by off[b]: sequence b sees the tree slots
+// from tree_base + off[b] and keys up to key_end + off[b]. The default is one
+// sequence whose rows are all M rows of the launch.
+#define MAX_LANES 8
+struct Lanes {
+  int n = 1, rows = 0;
+  int64_t bytes = 0;
+  int off[MAX_LANES] = {};
 };
 
 hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int M, float* h,
@@ -86,14 +100,15 @@ hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int
 // planes [M, (nq + 2 nkv) d].
 hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int M, int nq, int nkv,
                           int d, const int32_t* pos, const int32_t* slot, const float* cos_t,
-                          const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st);
+                          const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st,
+                          const Lanes& ln = Lanes());
 uint64_t attn_part_floats(int max_chunks, int M, int nq, int d);
 int attn_chunk_keys();
 // Most key chunks one attention call may split a row's keys into.
 int attn_max_chunks();
 hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, RowVis vis, int M,
                             int nq, int d, float scale, float* opart, float* mlpart, void* out_t,
-                            int64_t olo, hipStream_t st);
+                            int64_t olo, hipStream_t st, const Lanes& ln = Lanes());
 hipError_t launch_draft_input_e1(int dtype, const void* E, const int32_t* tok, const float* feat,
                                  const int32_t* idx, int M, int H, void* x, int64_t lo,
                                  hipStream_t st);
@@ -167,18 +182,19 @@ hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root
 // outputs as launch_accept, with the tree's candidates tested by rejection
 // sampling against e / Z of each verify row and the last token drawn from
 // what is left; draws from Philox4x32-10 keyed by seed, counter (step, depth,
-// draw, 0). launch_sample_token draws one token from row 0 (counter (step,
-// 0, 0xFFFF, 0)) into out[0]. V must pass sample_vocab_ok.
+// draw, lane), lane = the sequence's index in a batch (0 alone).
+// launch_sample_token draws one token from row 0 (counter (step, 0, 0xFFFF,
+// lane)) into out[0]. V must pass sample_vocab_ok.
 bool sample_vocab_ok(int V);
 uint64_t sample_zpart_doubles(int rows, int V);
 hipError_t launch_row_exp(const float* logits, const int32_t* g, int rows, int V, float temperature,
                           float* ebuf, double* zpart, hipStream_t st);
 hipError_t launch_accept_sample(TreeDev t, const float* ebuf, const double* zpart, int V,
-                                uint64_t seed, uint32_t step, int max_depth, int32_t* acc,
-                                int32_t* new_tok, int32_t* cu_src, int32_t* seq_out,
+                                uint64_t seed, uint32_t step, uint32_t lane, int max_depth,
+                                int32_t* acc, int32_t* new_tok, int32_t* cu_src, int32_t* seq_out,
                                 int32_t* host, int32_t tag, hipStream_t st);
 hipError_t launch_sample_token(const float* ebuf, const double* zpart, int V, uint64_t seed,
-                               uint32_t step, int32_t* out, hipStream_t st);
+                               uint32_t step, uint32_t lane, int32_t* out, hipStream_t st);
 hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
                          int32_t* new_tok, int32_t* cu_src, int32_t* seq_out, int32_t* host,
                          int32_t tag, hipStream_t st);

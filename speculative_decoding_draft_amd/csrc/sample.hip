@@ -13,7 +13,9 @@
 // order; with no child accepted the token is drawn from what is left.
 //
 // Random numbers: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11), key =
-// the 64-bit seed, counter = (step, depth, draw, 0), u = (word 0 >> 8) / 2^24.
+// the 64-bit seed, counter = (step, depth, draw, sequence), u = (word 0 >> 8)
+// / 2^24; the sequence index (0 for a single sequence) gives each sequence
+// of a batch its own stream.
 // Decisions are taken in fp32: e = exp((l - max) / T), Z = fp64 sum of e
 // rounded to fp32, p = e / Z, child test u * S < p(x). The residual walk
 // accumulates e in fp64 in token order against (u * S) * Z.
@@ -55,8 +57,9 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
   return c0;
 }
 
-__device__ __forceinline__ float philox_u(uint64_t seed, uint32_t step, uint32_t depth, uint32_t draw) {
-  const uint32_t w = philox_word0(step, depth, draw, 0u, (uint32_t)seed, (uint32_t)(seed >> 32));
+__device__ __forceinline__ float philox_u(uint64_t seed, uint32_t step, uint32_t depth, uint32_t draw,
+                                         uint32_t lane) {
+  const uint32_t w = philox_word0(step, depth, draw, lane, (uint32_t)seed, (uint32_t)(seed >> 32));
   return (float)(w >> 8) * (1.0f / 16777216.0f);
 }
 
@@ -206,7 +209,8 @@ __device__ void residual_pick(const float* e, int V, int nb, float u, WalkLds& s
 __global__ __launch_bounds__(NT) void accept_sample_kernel(TreeDev t, const float* ebuf,
                                                            const double* zpart, int V, int nb,
                                                            uint64_t seed, uint32_t step,
-                                                           int max_depth, int32_t* acc,
+                                                           uint32_t lane, int max_depth,
+                                                           int32_t* acc,
                                                            int32_t* new_tok, int32_t* cu_src,
                                                            int32_t* seq_out, int32_t* host,
                                                            int32_t tag) {
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(NT) void accept_sample_kernel(TreeDev t, const floa
       const int x = t.v_tok[s.children[j]];
       s.ctok[j] = x;
       s.cp[j] = e[x] / s.z;
-      s.cu[j] = philox_u(seed, step, (uint32_t)depth, (uint32_t)j);
+      s.cu[j] = philox_u(seed, step, (uint32_t)depth, (uint32_t)j, lane);
     }
     __syncthreads();
     if (tid == 0) {
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(NT) void accept_sample_kernel(TreeDev t, const floa
       __syncthreads();
       continue;
     }
-    residual_pick(e, V, nb, philox_u(seed, step, (uint32_t)depth, RESIDUAL_DRAW), s);
+    residual_pick(e, V, nb, philox_u(seed, step, (uint32_t)depth, RESIDUAL_DRAW, lane), s);
     if (tid == 0) {
       const int bonus = s.pick;
       acc[0] = L;
@@ -299,7 +303,8 @@ __global__ __launch_bounds__(NT) void accept_sample_kernel(TreeDev t, const floa
 
 __global__ __launch_bounds__(NT) void sample_token_kernel(const float* ebuf, const double* zpart,
                                                           int V, int nb, uint64_t seed,
-                                                          uint32_t step, int32_t* out) {
+                                                          uint32_t step, uint32_t lane,
+                                                          int32_t* out) {
   __shared__ WalkLds s;
   row_setup(zpart, 0, nb, V, s);
   if (threadIdx.x == 0) {
@@ -307,7 +312,7 @@ __global__ __launch_bounds__(NT) void sample_token_kernel(const float* ebuf, con
     s.n_removed = 0;
   }
   __syncthreads();
-  residual_pick(ebuf, V, nb, philox_u(seed, step, 0u, RESIDUAL_DRAW), s);
+  residual_pick(ebuf, V, nb, philox_u(seed, step, 0u, RESIDUAL_DRAW, lane), s);
   if (threadIdx.x == 0) out[0] = s.pick;
 }
 
@@ -327,20 +332,20 @@ hipError_t launch_row_exp(const float* logits, const int32_t* g, int rows, int V
 }
 
 hipError_t launch_accept_sample(TreeDev t, const float* ebuf, const double* zpart, int V,
-                                uint64_t seed, uint32_t step, int max_depth, int32_t* acc,
-                                int32_t* new_tok, int32_t* cu_src, int32_t* seq_out,
+                                uint64_t seed, uint32_t step, uint32_t lane, int max_depth,
+                                int32_t* acc, int32_t* new_tok, int32_t* cu_src, int32_t* seq_out,
                                 int32_t* host, int32_t tag, hipStream_t st) {
   if (!sample_vocab_ok(V)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(accept_sample_kernel, dim3(1), dim3(NT), 0, st, t, ebuf, zpart, V,
-                     (V + BLK - 1) / BLK, seed, step, max_depth, acc, new_tok, cu_src, seq_out,
-                     host, tag);
+                     (V + BLK - 1) / BLK, seed, step, lane, max_depth, acc, new_tok, cu_src,
+                     seq_out, host, tag);
   return hipGetLastError();
 }
 
 hipError_t launch_sample_token(const float* ebuf, const double* zpart, int V, uint64_t seed,
-                               uint32_t step, int32_t* out, hipStream_t st) {
+                               uint32_t step, uint32_t lane, int32_t* out, hipStream_t st) {
   if (!sample_vocab_ok(V)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sample_token_kernel, dim3(1), dim3(NT), 0, st, ebuf, zpart, V,
-                     (V + BLK - 1) / BLK, seed, step, out);
+                     (V + BLK - 1) / BLK, seed, step, lane, out);
   return hipGetLastError();
 }

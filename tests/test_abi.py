@@ -55,7 +55,7 @@ STRUCTS = {
     "eagle_config": (E.Config, ["n_layers", "hidden", "rope_base", "dtype", "head", "feat_layers",
                                 "tree", "topk", "expand", "depth", "budget", "n_static",
                                 "static_parent", "static_rank", "max_ctx", "prefill_chunk",
-                                "temperature", "seed_lo", "seed_hi"]),
+                                "temperature", "seed_lo", "seed_hi", "batch"]),
     "eagle_sizes": (E.Sizes, ["weight_bytes", "kv_bytes", "scratch_bytes", "n_tensors",
                               "verify_rows", "max_nodes", "kv_page"]),
     "eagle_tensor": (E.Tensor, ["kind", "group", "layer", "dtype", "rows", "cols", "offset"]),
@@ -206,7 +206,29 @@ def test_null_context_and_status_strings():
     assert L.eagle_verify(None, None, None, None) == E.E_INVALID
     assert L.eagle_generate(None, None, 0, 0, None, None, None) == E.E_INVALID
     assert L.eagle_profile_enable(None, 0, 1) == E.E_INVALID
+    assert L.eagle_prefill_lane(None, 0, None, 0, None) == E.E_INVALID
+    assert L.eagle_read_tree(None, 0, None) == E.E_INVALID
+    assert L.eagle_verify_batch(None, None, None) == E.E_INVALID
+    assert L.eagle_committed_lane(None, 0, None, 0, None) == E.E_INVALID
     L.eagle_free(None)
     assert L.eagle_last_error(None) == b"null context"
     names = [L.eagle_status_string(i).decode() for i in range(7)]
     assert names[0] == "ok" and len(set(names)) == 7
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_batch_sizes_scale_per_sequence(name):
+    """A batch of B sequences holds B KV caches (target and draft), each of
+    the batch-1 size, and more scratch; batch outside [0, 8] is rejected."""
+    w = synth.workloads.get(name)
+    s1 = E.query(E.make_config(dict(w, batch=1)))
+    s0 = E.query(E.make_config(dict(w, batch=0)))     # 0 means 1
+    assert (s0.kv_bytes, s0.scratch_bytes) == (s1.kv_bytes, s1.scratch_bytes)
+    for B in (2, 4, 8):
+        sb = E.query(E.make_config(dict(w, batch=B)))
+        assert abs(sb.kv_bytes - B * s1.kv_bytes) <= 512, B   # two 256-byte alignments
+        assert sb.scratch_bytes > s1.scratch_bytes
+        assert sb.verify_rows == s1.verify_rows and sb.weight_bytes == s1.weight_bytes
+    for bad in (-1, 9):
+        cfg = E.make_config(dict(w, batch=bad))
+        assert E.lib().eagle_query(ctypes.byref(cfg), ctypes.byref(E.Sizes())) == E.E_INVALID

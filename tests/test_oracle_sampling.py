@@ -32,6 +32,11 @@ def test_uniform_is_24_bit_and_varies_with_every_counter_word():
     assert len(set(u)) > 0.99 * len(u)
     assert S.uniform(7, 1, 2, 3) != S.uniform(8, 1, 2, 3)      # the seed is the key
     assert S.uniform(7 << 32, 1, 2, 3) != S.uniform(0, 1, 2, 3)
+    # the fourth counter word is the sequence (lane) of a batch: lane 0 is the
+    # single-sequence stream, other lanes are streams of their own
+    assert S.uniform(7, 1, 2, 3, 0) == S.uniform(7, 1, 2, 3)
+    lanes = [S.uniform(7, s, 0, 0, b) for b in range(8) for s in range(50)]
+    assert len(set(lanes)) > 0.99 * len(lanes)
 
 
 def test_residual_draw_small_case():
