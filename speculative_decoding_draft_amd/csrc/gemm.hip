@@ -24,12 +24,20 @@
 namespace {
 
 // LDS address (elements) of 16-byte chunk q of staged row r. Rows are KCH
-// elements wide; the chunk index is XOR-swizzled with the row.
+// elements wide (C 16-byte chunks); the chunk index is XOR-swizzled with the
+// row. LDS has 32 banks of 4 bytes, so a 16-byte access serves eight lanes
+// per cycle: the operand reads (eight consecutive rows, one chunk) and the
+// stores (consecutive chunks of one or two rows) must fall in eight
+// distinct 16-byte bank groups. With C >= 8 a row spans whole bank rounds
+// and chunk q ^ (r mod 8) does it; with C = 4 two rows share a round and
+// q ^ ((r / 2) mod 4) does it (C = 2: q ^ ((r / 4) mod 2)).
 template <typename T, int KCH>
 __device__ __forceinline__ int xs_addr(int r, int q) {
   constexpr int EPL = 16 / sizeof(T);
-  constexpr int QM = KCH / EPL - 1;
-  return r * KCH + ((q ^ (((r & 15) << 1) & QM)) * EPL);
+  constexpr int C = KCH / EPL;
+  constexpr int SH = C >= 8 ? 0 : C == 4 ? 1 : C == 2 ? 2 : 3;
+  constexpr int SM = (C >= 8 ? 8 : C) - 1;
+  return r * KCH + ((q ^ ((r >> SH) & SM)) * EPL);
 }
 
 struct ProjArgs {
@@ -178,28 +186,38 @@ __device__ __forceinline__ void lds_barrier() {
 // four times; loads past the last chunk re-read it (cache hits) instead of
 // sitting under a branch, so every wait is a partial vmcnt and one
 // LDS-only barrier per chunk orders the activation buffers.
-template <int MT, int NW, int CS>
+//
+// A wave owns NB consecutive 16-row weight blocks (rows row0 .. row0 +
+// 16 NB): every activation fragment read from LDS feeds NB products. Many
+// activation rows (a batch of verify rows, a prefill chunk) make the MFMAs
+// wait on LDS reads, one 1 KB fragment per product at NB = 1; NB > 1 divides
+// that traffic.
+template <int MT, int NW, int CS, int NB>
 __device__ __forceinline__ void proj_core_bf16(const ProjArgs& a, int row0, int s_lo, int s_hi,
-                                               bf16_t* xs, f32x4 (&acc)[MT]) {
+                                               bf16_t* xs, f32x4 (&acc)[NB][MT]) {
   using S = ProjShape<bf16_t, MT, NW, CS>;
   constexpr int PPL = S::MP * S::KCH / S::EPL;   // 16-byte pieces per plane
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
   const bf16_t* W = (const bf16_t*)a.W;
   const bf16_t* X = (const bf16_t*)a.X;
-  const bf16_t* wp;
-  int64_t wstep;
-  {
-    const int rb = min(row0, a.rows - 1) >> 4;
+  const bf16_t* wp[NB];
+  int64_t wstep[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r0 = row0 + 16 * j;
+    const int rb = min(r0, a.rows - 1) >> 4;
     if ((rb + 1) * 16 <= a.rows) {   // fragment-packed block
-      wp = W + (int64_t)rb * 16 * a.K + lane * S::EPL;
-      wstep = 16 * S::KS;
+      wp[j] = W + (int64_t)rb * 16 * a.K + lane * S::EPL;
+      wstep[j] = 16 * S::KS;
     } else {                         // ragged last block: row-major rows
-      wp = W + (int64_t)min(row0 + lr, a.rows - 1) * a.K + lg * S::EPL;
-      wstep = S::KS;
+      wp[j] = W + (int64_t)min(r0 + lr, a.rows - 1) * a.K + lg * S::EPL;
+      wstep[j] = S::KS;
     }
   }
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nch = (s_hi - s_lo + CS - 1) / CS;
   if (nch <= 0) return;
   auto xload = [&](uint4 (&xr)[S::NX], int c) {
@@ -213,26 +231,55 @@ __device__ __forceinline__ void proj_core_bf16(const ProjArgs& a, int row0, int 
       xr[i] = ld16(X + plane * a.xlo + (int64_t)row * a.K + col);
     }
   };
-  auto wload = [&](uint4 (&w)[CS], int c) {
+  auto wload = [&](uint4 (&w)[NB][CS], int c) {
     const int cc = min(c, nch - 1);
 #pragma unroll
-    for (int u = 0; u < CS; ++u) w[u] = ld16(wp + (int64_t)min(s_lo + cc * CS + u, s_hi - 1) * wstep);
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int u = 0; u < CS; ++u)
+        w[j][u] = ld16(wp[j] + (int64_t)min(s_lo + cc * CS + u, s_hi - 1) * wstep[j]);
   };
-  auto compute = [&](const uint4 (&w)[CS], const bf16_t* x, int c) {
+  // one K step, m-tiles in groups of up to four: a group's activation
+  // fragments are read first, then its products are issued hi-plane first,
+  // so consecutive MFMAs rarely feed one accumulator and no MFMA waits on
+  // the read just before it (the group bounds the registers this takes)
+  auto step = [&](const uint4 (&w)[NB][CS], const bf16_t* x, int u) {
+    // (the many-row tiles, MT >= 8, are short of registers: one tile at a time)
+    constexpr int G = MT < 4 ? MT : MT < 8 ? 4 : 1;
 #pragma unroll
-    for (int u = 0; u < CS; ++u) {
-      if (s_lo + c * CS + u < s_hi) {
+    for (int t0 = 0; t0 < MT; t0 += G) {
+      uint4 xh[G], xl[G];
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const uint4 xh = *reinterpret_cast<const uint4*>(x + xs_addr<bf16_t, S::KCH>(16 * t + lr, 4 * u + lg));
-          const uint4 xl = *reinterpret_cast<const uint4*>(x + xs_addr<bf16_t, S::KCH>(S::MP + 16 * t + lr, 4 * u + lg));
-          Mma<bf16_t>::mma(w[u], xh, acc[t]);
-          Mma<bf16_t>::mma(w[u], xl, acc[t]);
-        }
+      for (int g = 0; g < G; ++g) {
+        const int t = t0 + g < MT ? t0 + g : MT - 1;
+        xh[g] = *reinterpret_cast<const uint4*>(x + xs_addr<bf16_t, S::KCH>(16 * t + lr, 4 * u + lg));
+        xl[g] = *reinterpret_cast<const uint4*>(x + xs_addr<bf16_t, S::KCH>(S::MP + 16 * t + lr, 4 * u + lg));
       }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (t0 + g < MT)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) Mma<bf16_t>::mma(w[j][u], xh[g], acc[j][t0 + g]);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        if (t0 + g < MT)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) Mma<bf16_t>::mma(w[j][u], xl[g], acc[j][t0 + g]);
     }
   };
-  uint4 w[4][CS], xr[2][S::NX];
+  auto compute = [&](const uint4 (&w)[NB][CS], const bf16_t* x, int c) {
+    // a whole chunk: straight-line code (not for the many-row tiles, whose
+    // registers cannot hold a second copy of the step)
+    if (MT < 8 && s_lo + (c + 1) * CS <= s_hi) {
+#pragma unroll
+      for (int u = 0; u < CS; ++u) step(w, x, u);
+    } else {
+#pragma unroll
+      for (int u = 0; u < CS; ++u)
+        if (s_lo + c * CS + u < s_hi) step(w, x, u);
+    }
+  };
+  uint4 w[4][NB][CS], xr[2][S::NX];
   xload(xr[0], 0);
   wload(w[0], 0);
   xload(xr[1], 1);
@@ -254,10 +301,22 @@ __device__ __forceinline__ void proj_core_bf16(const ProjArgs& a, int row0, int 
   }
 }
 
-template <typename T, int MT, int NW, int CS, int EPI>
+// LDS elements of a projection workgroup: the two activation buffers, or
+// for SwiGLU the gate values [NW/2 * 16 * NB columns][MP] fp32 if they need
+// more.
+template <typename T, int MT, int NW, int CS, int NB, int EPI>
+constexpr int proj_lds_elems() {
+  using S = ProjShape<T, MT, NW, CS>;
+  constexpr int act = 2 * S::LDS_ELEMS;
+  constexpr int gate = EPI == EPI_SWIGLU ? (NW / 2) * 16 * NB * S::MP * 4 / (int)sizeof(T) : 0;
+  return act > gate ? act : gate;
+}
+
+template <typename T, int MT, int NW, int CS, int NB, int EPI>
 __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   using S = ProjShape<T, MT, NW, CS>;
-  __shared__ __attribute__((aligned(16))) T xs[2 * S::LDS_ELEMS];
+  static_assert(NB == 1 || Opnd<T>::SPLIT, "several row blocks per wave: bf16 only");
+  __shared__ __attribute__((aligned(16))) T xs[proj_lds_elems<T, MT, NW, CS, NB, EPI>()];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
@@ -271,64 +330,77 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   const int s_hi = min(total, s_lo + a.steps_per_split);
   // SwiGLU tiles: waves [0, NW/2) take gate rows, waves [NW/2, NW) the
   // matching up rows, so one tile yields NW/2 * 16 output columns.
+  // a wave's rows: NB consecutive 16-row blocks from row0
+  constexpr int WR = 16 * NB;
   int row0;
   if (EPI == EPI_SWIGLU) {
     const int half = NW / 2;
-    const int col0 = tile * half * 16 + (wave % half) * 16;
+    const int col0 = tile * half * WR + (wave % half) * WR;
     row0 = (wave < half) ? col0 : a.F + col0;
   } else {
-    row0 = (tile * NW + wave) * 16;
+    row0 = (tile * NW + wave) * WR;
   }
-  f32x4 acc[MT];
-  if constexpr (Opnd<T>::SPLIT)
-    proj_core_bf16<MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc);
-  else
-    proj_core<T, MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc);
+  f32x4 acc[NB][MT];
+  if constexpr (Opnd<T>::SPLIT) {
+    proj_core_bf16<MT, NW, CS, NB>(b, row0, s_lo, s_hi, xs, acc);
+  } else {
+    static_assert(NB == 1, "fp32 projections take one row block per wave");
+    proj_core<T, MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc[0]);
+  }
 
   if (EPI == EPI_SWIGLU) {
     constexpr int half = NW / 2;
     __syncthreads();   // xs is reused for the gate values
-    float* gate = reinterpret_cast<float*>(xs);   // [half*16 cols][MP]
+    float* gate = reinterpret_cast<float*>(xs);   // [half * WR cols][MP]
     if (wave < half) {
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
+      for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) gate[(wave * 16 + 4 * lg + j) * S::MP + 16 * t + lr] = acc[t][j];
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            gate[(wave * WR + 16 * jb + 4 * lg + j) * S::MP + 16 * t + lr] = acc[jb][t][j];
     }
     __syncthreads();
     if (wave >= half) {
       const int w2 = wave - half;
 #pragma unroll
-      for (int t = 0; t < MT; ++t)
+      for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int c = w2 * 16 + 4 * lg + j;
-          const int col = tile * half * 16 + c;
-          const int m = 16 * t + lr;
-          if (m < b.M && col < a.F) {
-            const float g = gate[c * S::MP + m];
-            const float v = g / (1.0f + expf(-g)) * acc[t][j];
-            Opnd<T>::store((T*)a.Yt, a.ytlo, (int64_t)(m0 + m) * a.F + col, v);
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int c = w2 * WR + 16 * jb + 4 * lg + j;
+            const int col = tile * half * WR + c;
+            const int m = 16 * t + lr;
+            if (m < b.M && col < a.F) {
+              const float g = gate[c * S::MP + m];
+              const float v = g / (1.0f + expf(-g)) * acc[jb][t][j];
+              Opnd<T>::store((T*)a.Yt, a.ytlo, (int64_t)(m0 + m) * a.F + col, v);
+            }
           }
-        }
     }
   } else {
     float* Y = a.Y + (int64_t)split * a.plane;
     // one 16-byte store per lane and m-tile (four consecutive rows) when the
     // plane allows it: scalar stores cost a measurable share of the kernel
-    const bool vec = (a.ldy & 3) == 0 && (a.plane & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 &&
-                     row0 + 16 <= a.rows;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int m = 16 * t + lr;
-      if (m >= b.M) continue;
-      float* yr = Y + (int64_t)(m0 + m) * a.ldy + row0 + 4 * lg;
-      if (vec) {
-        *reinterpret_cast<f32x4*>(yr) = acc[t];
-      } else {
+    for (int jb = 0; jb < NB; ++jb) {
+      const int r0 = row0 + 16 * jb;
+      const bool vec = (a.ldy & 3) == 0 && (a.plane & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 &&
+                       r0 + 16 <= a.rows;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (row0 + 4 * lg + j < a.rows) yr[j] = acc[t][j];
+      for (int t = 0; t < MT; ++t) {
+        const int m = 16 * t + lr;
+        if (m >= b.M) continue;
+        float* yr = Y + (int64_t)(m0 + m) * a.ldy + r0 + 4 * lg;
+        if (vec) {
+          *reinterpret_cast<f32x4*>(yr) = acc[jb][t];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (r0 + 4 * lg + j < a.rows) yr[j] = acc[jb][t][j];
+        }
       }
     }
   }
@@ -626,19 +698,26 @@ __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_til
 // the weight stream needs more than a deep per-wave prefetch (measured on
 // the 7B shapes).
 constexpr int KIND_HEAD = 3;
-template <int MT, int KIND> struct Cfg { static constexpr int NW = 8, CS = 4; };
-template <> struct Cfg<1, EPI_PART> { static constexpr int NW = 4, CS = 4; };
-template <> struct Cfg<1, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4; };
-template <> struct Cfg<1, KIND_HEAD> { static constexpr int NW = 4, CS = 16; };
-template <> struct Cfg<2, EPI_PART> { static constexpr int NW = 4, CS = 4; };
-template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4; };
-template <> struct Cfg<2, KIND_HEAD> { static constexpr int NW = 4, CS = 8; };
-template <> struct Cfg<3, EPI_PART> { static constexpr int NW = 4, CS = 2; };
-template <> struct Cfg<3, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2; };
-template <> struct Cfg<4, EPI_PART> { static constexpr int NW = 8, CS = 2; };
-template <> struct Cfg<4, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2; };
-template <> struct Cfg<5, EPI_PART> { static constexpr int NW = 4, CS = 2; };
-template <> struct Cfg<5, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2; };
+template <int MT, int KIND> struct Cfg { static constexpr int NW = 8, CS = 4, NB = 1; };
+template <> struct Cfg<1, EPI_PART> { static constexpr int NW = 4, CS = 4, NB = 1; };
+template <> struct Cfg<1, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4, NB = 1; };
+template <> struct Cfg<1, KIND_HEAD> { static constexpr int NW = 4, CS = 16, NB = 1; };
+template <> struct Cfg<2, EPI_PART> { static constexpr int NW = 4, CS = 4, NB = 1; };
+template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4, NB = 1; };
+template <> struct Cfg<2, KIND_HEAD> { static constexpr int NW = 4, CS = 8, NB = 1; };
+template <> struct Cfg<3, EPI_PART> { static constexpr int NW = 4, CS = 2, NB = 1; };
+template <> struct Cfg<3, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
+template <> struct Cfg<4, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
+template <> struct Cfg<4, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
+template <> struct Cfg<5, EPI_PART> { static constexpr int NW = 4, CS = 2, NB = 1; };
+template <> struct Cfg<5, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
+// bf16 q|k|v over many activation rows (batched verify rows, prefill
+// chunks): one pass over up to 256 rows, each wave two 16-row weight blocks
+// (see proj_core_bf16). Measured against 64-row passes on the 7B shapes:
+// -10% at 108 rows, -20% at 216 and 256; the narrower projections and the
+// gate/up kernel gained nothing in the full cycle and keep 64-row passes.
+template <> struct Cfg<8, EPI_PART> { static constexpr int NW = 8, CS = 1, NB = 2; };
+template <> struct Cfg<16, EPI_PART> { static constexpr int NW = 8, CS = 1, NB = 2; };
 
 template <int KIND>
 int waves_t(int mt) {
@@ -647,6 +726,8 @@ int waves_t(int mt) {
     case 2: return Cfg<2, KIND>::NW;
     case 3: return Cfg<3, KIND>::NW;
     case 4: return Cfg<4, KIND>::NW;
+    case 8: return Cfg<8, KIND>::NW;
+    case 16: return Cfg<16, KIND>::NW;
     default: return Cfg<5, KIND>::NW;
   }
 }
@@ -657,7 +738,17 @@ int chunk_t(int mt) {
     case 2: return Cfg<2, KIND>::CS;
     case 3: return Cfg<3, KIND>::CS;
     case 4: return Cfg<4, KIND>::CS;
+    case 8: return Cfg<8, KIND>::CS;
+    case 16: return Cfg<16, KIND>::CS;
     default: return Cfg<5, KIND>::CS;
+  }
+}
+template <int KIND>
+int blocks_t(int mt) {
+  switch (mt) {
+    case 8: return Cfg<8, KIND>::NB;
+    case 16: return Cfg<16, KIND>::NB;
+    default: return 1;
   }
 }
 int waves_for(int mt, int kind) {
@@ -666,27 +757,36 @@ int waves_for(int mt, int kind) {
 int chunk_for(int mt, int kind) {
   return kind == EPI_SWIGLU ? chunk_t<EPI_SWIGLU>(mt) : kind == KIND_HEAD ? chunk_t<KIND_HEAD>(mt) : chunk_t<EPI_PART>(mt);
 }
+int blocks_for(int mt, int kind) {
+  return kind == EPI_SWIGLU ? blocks_t<EPI_SWIGLU>(mt) : blocks_t<EPI_PART>(mt);
+}
 
 template <typename T, int MT, int EPI>
 hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st, const KTiming* tm) {
   constexpr int NW = Cfg<MT, EPI>::NW, CS = Cfg<MT, EPI>::CS;
+  constexpr int NB = Opnd<T>::SPLIT ? Cfg<MT, EPI>::NB : 1;
   const dim3 grid(tiles * a.splits, m_chunks), block(NW * 64);
   if (tm)
-    hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, EPI>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+    hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI>), grid, block, 0, st, tm->start, tm->stop, 0, a);
   else
-    hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, EPI>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
 template <typename T, int EPI>
 hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hipStream_t st,
                          const KTiming* tm) {
+  if constexpr (Opnd<T>::SPLIT && EPI == EPI_PART) {   // many-row q|k|v: bf16 only
+    if (mt == 8) return launch_proj_mt<T, 8, EPI_PART>(a, tiles, m_chunks, st, tm);
+    if (mt == 16) return launch_proj_mt<T, 16, EPI_PART>(a, tiles, m_chunks, st, tm);
+  }
   switch (mt) {
     case 1: return launch_proj_mt<T, 1, EPI>(a, tiles, m_chunks, st, tm);
     case 2: return launch_proj_mt<T, 2, EPI>(a, tiles, m_chunks, st, tm);
     case 3: return launch_proj_mt<T, 3, EPI>(a, tiles, m_chunks, st, tm);
     case 4: return launch_proj_mt<T, 4, EPI>(a, tiles, m_chunks, st, tm);
-    default: return launch_proj_mt<T, 5, EPI>(a, tiles, m_chunks, st, tm);
+    case 5: return launch_proj_mt<T, 5, EPI>(a, tiles, m_chunks, st, tm);
+    default: return hipErrorInvalidValue;
   }
 }
 
@@ -714,11 +814,18 @@ int head_rows(int M) { return 16 * waves_for(M > 64 ? 5 : (M + 15) / 16, KIND_HE
 
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
   GemmPlan p;
-  if (M <= 80) { p.mt = (M + 15) / 16; p.m_chunks = 1; }
-  else { p.mt = 4; p.m_chunks = (M + 63) / 64; }
+  if (M <= 80) {
+    p.mt = (M + 15) / 16;
+  } else if (dtype == 1 && epi == EPI_PART && N_rows >= 8192) {
+    // wide projections (q|k|v) over many rows: one pass of up to 256 rows
+    p.mt = M <= 128 ? 8 : 16;
+  } else {
+    p.mt = 4;   // passes of 64 rows
+  }
+  p.m_chunks = (M + 16 * p.mt - 1) / (16 * p.mt);
   const int nw = waves_for(p.mt, epi);
-  const int rows_per_tile = 16 * nw;
-  p.nb = 1;
+  p.nb = dtype == 1 ? blocks_for(p.mt, epi) : 1;
+  const int rows_per_tile = 16 * nw * p.nb;
   if (epi == EPI_SWIGLU) {
     const int F = N_rows / 2;
     p.n_tiles = (F + rows_per_tile / 2 - 1) / (rows_per_tile / 2);
@@ -732,10 +839,11 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
     // [M, N] fp32 plane of HBM writes (measured on the 7B shapes).
     const int cs = chunk_for(p.mt, epi);
     const int chunks = (steps + cs - 1) / cs;
-    const int target = p.mt <= 2 ? 8 : 16;
+    const int target = p.mt <= 2 ? 8 : p.mt < 8 ? 16 : 32;
     int s = 1;
     while (s < 16 && chunks / (2 * s) >= target) s *= 2;
-    while (p.n_tiles * s < 256 && s < 16 && chunks / (2 * s) >= 4) s *= 2;
+    if (p.mt < 8)   // the many-row tiles keep the MFMAs busy without a wider grid
+      while (p.n_tiles * s < 256 && s < 16 && chunks / (2 * s) >= 4) s *= 2;
     while (p.n_tiles * s > 1024 && s > 1) s /= 2;
     p.splits = s;
   }

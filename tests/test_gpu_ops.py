@@ -82,6 +82,11 @@ LINEAR = [  # (dtype, M, N, K): split-K, tails, several M tiles, prefill-sized M
     (BF16, 1, 4096, 4096), (BF16, 10, 4096, 8192), (BF16, 27, 12288, 4096),
     (BF16, 61, 4096, 11008), (BF16, 65, 1000, 1024), (BF16, 100, 256, 512),
     (BF16, 256, 512, 4096), (F32, 17, 256, 256), (F32, 17, 256, 688), (F32, 33, 1024, 512),
+    # many rows (a batch's verify rows, prefill chunks): wide projections take
+    # 128- and 256-row tiles with two weight blocks per wave; ragged N and a
+    # second row pass
+    (BF16, 108, 12288, 4096), (BF16, 216, 8200, 1024), (BF16, 300, 8192, 512),
+    (BF16, 130, 4096, 1024),
 ]
 
 
@@ -111,7 +116,8 @@ def test_linear(dtype, M, N, K, epi):
 
 
 @pytest.mark.parametrize("dtype,M,N,K", [(BF16, 61, 11008, 4096), (BF16, 10, 1376, 1024),
-                                         (BF16, 1, 11008, 4096), (F32, 17, 688, 256)])
+                                         (BF16, 1, 11008, 4096), (F32, 17, 688, 256),
+                                         (BF16, 100, 2720, 1024), (BF16, 200, 1376, 1024)])
 def test_swiglu(dtype, M, N, K):
     print(f"swiglu dtype={dtype} M={M} N={N} K={K}", flush=True)
     gen = torch.Generator().manual_seed(M + N + K)
