@@ -84,6 +84,25 @@ def cycle_bytes(w: dict, ctx: int, lanes: int = 1) -> float:
     return esz * (target + draft + fc) + kv
 
 
+PEAK_BF16_TFLOPS = 2500.0   # dense MFMA, bf16
+
+
+def prefill_flops(w: dict, n: int) -> float:
+    """Algorithmic FLOPs of a prefill over n prompt tokens: every target
+    projection and the LM head row of the last token (2 x weights x rows),
+    causal attention (QK^T and PV over n(n+1)/2 visible pairs per head), and
+    the draft catch-up over the n (feature, token) pairs (FC + draft layer)."""
+    H, nq, nkv, F, V, L = (w[k] for k in ("hidden", "n_heads", "n_kv_heads", "ffn", "vocab", "n_layers"))
+    d = H // nq
+    kin = 2 * H if w["head"] == "e3" else H
+    layer = lambda k: k * (nq + 2 * nkv) * d + nq * d * H + 3 * H * F
+    fc = H * (3 * H if w["head"] == "e3" else 2 * H)
+    pairs = n * (n + 1) / 2
+    attn = 4.0 * pairs * d * nq
+    return (2.0 * n * (L * layer(H) + layer(kin) + fc) + 2.0 * V * H * 2
+            + attn * (L + 1))
+
+
 def cpu_baseline(w: dict, budget_layers: int = 2) -> dict:
     """The oracle on this host: draft passes and verify of one cycle timed on a
     slice with `budget_layers` target layers (same width, tree, vocabulary;
@@ -296,6 +315,12 @@ def main():
                      "bytes_per_launch": round(g["bytes"] / max(1, g["launches"]))},
     }
     out["prefill_ms"] = round(prefill_ms, 3)
+    # the prefill (one lane, the timed second run) against the dense bf16 MFMA peak
+    pf = prefill_flops(w, len(prompt))
+    out["prefill_roofline"] = {"bound": "mfma", "achieved": round(pf / (prefill_ms * 1e-3) / 1e12, 1),
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(pf / (prefill_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               "flops": pf, "tokens": len(prompt)}
     if model is not None:
         out["speedup_model"] = model
     if prof is not None:

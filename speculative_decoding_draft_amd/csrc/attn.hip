@@ -57,17 +57,10 @@ __device__ __forceinline__ bool row_sees(const RowVis& rv, int prehi, uint64_t m
 }
 
 // Sequence b of a multi-sequence launch: row range, per-row inputs, cache
-// and key positions (see Lanes). The lane's offset is picked with selects,
-// not a dynamic index into the kernel arguments.
-__device__ __forceinline__ int lane_off(const Lanes& ln, int lane) {
-  int o = 0;
-#pragma unroll
-  for (int i = 0; i < MAX_LANES; ++i) o = i == lane ? ln.off[i] : o;
-  return o;
-}
+// and key positions (see Lanes).
 __device__ __forceinline__ RowVis lane_vis(const RowVis& v, const Lanes& ln, int lane) {
   RowVis r = v;
-  const int o = lane_off(ln, lane);
+  const int o = lane_shift(ln, lane);
   r.tree_base += o;
   r.key_end += o;
   r.prehi = (const int32_t*)((const char*)v.prehi + lane * ln.bytes);
@@ -444,9 +437,10 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, KVView kv_
 
 // ---------------------------------------------------------------- rows
 template <typename T>
-__global__ void embed_kernel(const T* E, int H, const int32_t* tok, float* h) {
+__global__ void embed_kernel(const T* E, int H, const int32_t* tok, float* h, Lanes ln) {
   const int r = blockIdx.x;
-  const T* e = E + (int64_t)tok[r] * H;
+  const int b = ln.n > 1 ? r / ln.rows : 0, j = r - b * (ln.n > 1 ? ln.rows : 0);
+  const T* e = E + (int64_t)lane_at(tok, b, ln.bytes)[j] * H;
   for (int i = threadIdx.x; i < H; i += blockDim.x) h[(int64_t)r * H + i] = Elem<T>::to_f(e[i]);
 }
 
@@ -616,10 +610,12 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
 
 template <typename T>
 __global__ void draft_input_e1_kernel(const T* E, const int32_t* tok, const float* feat,
-                                      const int32_t* idx, int H, T* x, int64_t lo) {
+                                      const int32_t* idx, int H, T* x, int64_t lo, Lanes ln,
+                                      int64_t feat_stride, int64_t idx_bytes) {
   const int r = blockIdx.x;
-  const T* e = E + (int64_t)tok[r] * H;
-  const float* f = feat + (int64_t)idx[r] * H;
+  const int b = ln.n > 1 ? r / ln.rows : 0, j = r - b * (ln.n > 1 ? ln.rows : 0);
+  const T* e = E + (int64_t)lane_at(tok, b, ln.bytes)[j] * H;
+  const float* f = feat + b * feat_stride + (int64_t)lane_at(idx, b, idx_bytes)[j] * H;
   const int64_t row = (int64_t)r * 2 * H;
   if constexpr (Opnd<T>::SPLIT) {
     // bf16 (H a multiple of 8): eight elements per thread and step, one
@@ -650,11 +646,13 @@ template <typename T>
 __global__ __launch_bounds__(256) void draft_input_e3_kernel(const T* E, const int32_t* tok,
                                                              const float* feat, const int32_t* idx,
                                                              const float* gain, float eps, int H,
-                                                             T* x, int64_t lo, float* h) {
+                                                             T* x, int64_t lo, float* h, Lanes ln,
+                                                             int64_t feat_stride, int64_t idx_bytes) {
   __shared__ float sh[256];
   const int r = blockIdx.x;
-  const T* e = E + (int64_t)tok[r] * H;
-  const float* f = feat + (int64_t)idx[r] * H;
+  const int b = ln.n > 1 ? r / ln.rows : 0, j = r - b * (ln.n > 1 ? ln.rows : 0);
+  const T* e = E + (int64_t)lane_at(tok, b, ln.bytes)[j] * H;
+  const float* f = feat + b * feat_stride + (int64_t)lane_at(idx, b, idx_bytes)[j] * H;
   float ss = 0.f;
   for (int i = threadIdx.x; i < H; i += 256) {
     const float a = Elem<T>::to_f(e[i]);
@@ -688,6 +686,21 @@ __global__ void gather_t_kernel(const T* src, int64_t ld, int64_t src_lo, const 
   }
 }
 
+// Row b: sequence b's root row (row b * src_rows + acc_b[0]) of the fp32
+// rows src_f and of the operand rows src_t (width W each).
+template <typename T>
+__global__ void gather_roots_kernel(const float* src_f, const T* src_t, int64_t src_lo, int src_rows,
+                                    const int32_t* acc, int W, float* dst_f, int64_t dst_stride,
+                                    T* dst_t, int64_t dst_lo, Lanes ln) {
+  const int b = blockIdx.x;
+  const int64_t row = (int64_t)b * src_rows + lane_at(acc, b, ln.bytes)[0];
+  for (int i = threadIdx.x; i < W; i += blockDim.x) {
+    dst_f[b * dst_stride + i] = src_f[row * W + i];
+    dst_t[(int64_t)b * W + i] = src_t[row * W + i];
+    if (Opnd<T>::SPLIT) dst_t[dst_lo + (int64_t)b * W + i] = src_t[src_lo + row * W + i];
+  }
+}
+
 template <typename T>
 __global__ void store_feat_kernel(const float* h, int H, T* dst, int64_t ldd, int64_t lo) {
   const int r = blockIdx.x;
@@ -696,7 +709,13 @@ __global__ void store_feat_kernel(const float* h, int H, T* dst, int64_t ldd, in
 }
 
 __global__ void rows_causal_kernel(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
-                                   uint64_t* mask) {
+                                   uint64_t* mask, Lanes ln) {
+  const int b = blockIdx.y;
+  first += lane_shift(ln, b);
+  pos = lane_at(pos, b, ln.bytes);
+  slot = lane_at(slot, b, ln.bytes);
+  prehi = lane_at(prehi, b, ln.bytes);
+  mask = lane_at(mask, b, ln.bytes);
   for (int r = threadIdx.x + blockIdx.x * blockDim.x; r < M; r += blockDim.x * gridDim.x) {
     pos[r] = first + r;
     slot[r] = first + r;
@@ -712,12 +731,15 @@ __global__ void rows_causal_kernel(int first, int M, int32_t* pos, int32_t* slot
 // since a destination may be an earlier source.
 template <typename T>
 __global__ void kv_compact_kernel(KVView v, int64_t layer_elems, const int32_t* Lp,
-                                  const int32_t* path, int ctx, int planes) {
-  const int layer = blockIdx.x, h = blockIdx.y;
+                                  const int32_t* path, int ctx, int planes, Lanes ln) {
+  const int layer = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  Lp = lane_at(Lp, b, ln.bytes);
+  path = lane_at(path, b, ln.bytes);
+  ctx += lane_shift(ln, b);
   const int L = *Lp;
   if (L <= 0) return;
   KVView lv = v;
-  lv.base = (T*)v.base + (int64_t)layer * layer_elems;
+  lv.base = (T*)v.base + (int64_t)layer * layer_elems + b * v.lane_elems;
   for (int e = threadIdx.x; e < planes * v.d; e += blockDim.x) {
     const int sel = e / v.d, i = e % v.d;
     T vals[EAGLE_COMPACT_MAX];
@@ -742,12 +764,17 @@ uint64_t attn_part_floats(int max_chunks, int M, int nq, int d) {
 
 static bool kv_page_bad(const KVView& v) { return v.page <= 0 || (v.page & (v.page - 1)) != 0; }
 
+static bool lanes_bad(const Lanes& ln, int M) {
+  return ln.n < 1 || ln.n > MAX_LANES || (ln.n > 1 && ln.rows * ln.n != M);
+}
+
 hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int M, float* h,
-                        hipStream_t st) {
+                        hipStream_t st, const Lanes& ln) {
   if (M <= 0) return hipSuccess;
+  if (lanes_bad(ln, M)) return hipErrorInvalidValue;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, H, tok, h),
-              hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, H, tok, h));
+              hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, H, tok, h, ln),
+              hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, H, tok, h, ln));
   return hipGetLastError();
 }
 
@@ -844,21 +871,36 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
 
 hipError_t launch_draft_input_e1(int dtype, const void* E, const int32_t* tok, const float* feat,
                                  const int32_t* idx, int M, int H, void* x, int64_t lo,
-                                 hipStream_t st) {
+                                 hipStream_t st, const Lanes& ln, int64_t feat_stride,
+                                 int64_t idx_bytes) {
   if (M <= 0) return hipSuccess;
+  if (lanes_bad(ln, M)) return hipErrorInvalidValue;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(draft_input_e1_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, H, (bf16_t*)x, lo),
-              hipLaunchKernelGGL(draft_input_e1_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, H, (float*)x, lo));
+              hipLaunchKernelGGL(draft_input_e1_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, H, (bf16_t*)x, lo, ln, feat_stride, idx_bytes),
+              hipLaunchKernelGGL(draft_input_e1_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, H, (float*)x, lo, ln, feat_stride, idx_bytes));
   return hipGetLastError();
 }
 
 hipError_t launch_draft_input_e3(int dtype, const void* E, const int32_t* tok, const float* feat,
                                  const int32_t* idx, const float* gain, float eps, int M, int H,
-                                 void* x, int64_t lo, float* h, hipStream_t st) {
+                                 void* x, int64_t lo, float* h, hipStream_t st, const Lanes& ln,
+                                 int64_t feat_stride, int64_t idx_bytes) {
   if (M <= 0) return hipSuccess;
+  if (lanes_bad(ln, M)) return hipErrorInvalidValue;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(draft_input_e3_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, gain, eps, H, (bf16_t*)x, lo, h),
-              hipLaunchKernelGGL(draft_input_e3_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, gain, eps, H, (float*)x, lo, h));
+              hipLaunchKernelGGL(draft_input_e3_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, gain, eps, H, (bf16_t*)x, lo, h, ln, feat_stride, idx_bytes),
+              hipLaunchKernelGGL(draft_input_e3_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, gain, eps, H, (float*)x, lo, h, ln, feat_stride, idx_bytes));
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_roots(int dtype, const float* src_f, const void* src_t, int64_t src_lo,
+                               int src_rows, const int32_t* acc, int W, float* dst_f,
+                               int64_t dst_stride, void* dst_t, int64_t dst_lo, const Lanes& ln,
+                               hipStream_t st) {
+  if (ln.n < 1 || ln.n > MAX_LANES || src_rows < 1) return hipErrorInvalidValue;
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(gather_roots_kernel<bf16_t>, dim3(ln.n), dim3(256), 0, st, src_f, (const bf16_t*)src_t, src_lo, src_rows, acc, W, dst_f, dst_stride, (bf16_t*)dst_t, dst_lo, ln),
+              hipLaunchKernelGGL(gather_roots_kernel<float>, dim3(ln.n), dim3(256), 0, st, src_f, (const float*)src_t, src_lo, src_rows, acc, W, dst_f, dst_stride, (float*)dst_t, dst_lo, ln));
   return hipGetLastError();
 }
 
@@ -888,18 +930,21 @@ hipError_t launch_store_feat(int dtype, const float* h, int H, int M, void* dst,
 }
 
 hipError_t launch_rows_causal(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
-                              uint64_t* mask, hipStream_t st) {
+                              uint64_t* mask, hipStream_t st, const Lanes& ln) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(rows_causal_kernel, dim3((M + 255) / 256), dim3(256), 0, st, first, M, pos,
-                     slot, prehi, mask);
+  if (ln.n < 1 || ln.n > MAX_LANES) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rows_causal_kernel, dim3((M + 255) / 256, ln.n), dim3(256), 0, st, first, M, pos,
+                     slot, prehi, mask, ln);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int n_layers,
-                             const int32_t* L, const int32_t* path, int ctx, hipStream_t st) {
+                             const int32_t* L, const int32_t* path, int ctx, hipStream_t st,
+                             const Lanes& ln) {
   if (kv_page_bad(layer0)) return hipErrorInvalidValue;
+  if (ln.n < 1 || ln.n > MAX_LANES) return hipErrorInvalidValue;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv), dim3(512), 0, st, layer0, layer_elems, L, path, ctx, 4),
-              hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(n_layers, layer0.n_kv), dim3(256), 0, st, layer0, layer_elems, L, path, ctx, 2));
+              hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv, ln.n), dim3(512), 0, st, layer0, layer_elems, L, path, ctx, 4, ln),
+              hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(n_layers, layer0.n_kv, ln.n), dim3(256), 0, st, layer0, layer_elems, L, path, ctx, 2, ln));
   return hipGetLastError();
 }

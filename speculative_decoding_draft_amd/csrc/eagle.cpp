@@ -608,11 +608,6 @@ KVView lane_view(KVView v, int b, int esz) {
   return v;
 }
 
-// Sequence b's copy of a per-sequence device array given sequence 0's.
-template <typename T>
-T* lane_ptr(T* p, int b, int64_t bytes) {
-  return (T*)((char*)p + (int64_t)b * bytes);
-}
 
 // ------------------------------------------------------------ passes
 // Applies the pending split-K partial planes of a projection to the
@@ -669,10 +664,8 @@ eagle_status target_pass(eagle_ctx* c, Span s, const int32_t* tok, const int32_t
   const Derived& z = c->z;
   const int M = s.M();
   const Lanes ln = lanes_of(c, s);
-  for (int b = 0; b < s.n; ++b)
-    PROFILED(EAGLE_PROF_ROWS, (double)s.rows * z.H * 4.0,
-             launch_embed(z.dt, c->embed, z.H, lane_ptr(tok, b, c->lane_bytes), s.rows,
-                          c->h + (int64_t)b * s.rows * z.H, c->st));
+  PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 4.0,
+           launch_embed(z.dt, c->embed, z.H, tok, M, c->h, c->st, ln));
   SCHK(resnorm(c, c->h, M, 0, false, c->tl[0].attn_norm, nullptr));
   for (int l = 0; l < z.NL; ++l) {
     KVView kv = c->tkv0;
@@ -703,31 +696,25 @@ eagle_status draft_pass(eagle_ctx* c, Span s, const int32_t* tok, const float* f
                         const int32_t* pos, const int32_t* slot, RowVis vis, float* hout) {
   const Derived& z = c->z;
   const int M = s.M();
-  const int64_t xrow = 2 * (int64_t)z.H;   // draft input operand row: [emb; feature]
+  const Lanes ln = lanes_of(c, s);
   if (c->cfg.head == EAGLE_HEAD_E1) {
     int S = 1;
-    for (int b = 0; b < s.n; ++b)
-      PROFILED(EAGLE_PROF_ROWS, (double)s.rows * z.H * 12.0,
-               launch_draft_input_e1(z.dt, c->embed, lane_ptr(tok, b, c->lane_bytes),
-                                     feat + b * feat_stride, lane_ptr(idx, b, idx_bytes), s.rows,
-                                     z.H, (char*)c->xop + (int64_t)b * s.rows * xrow * z.esz,
-                                     c->xlo, c->st));
+    PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
+             launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->xlo, c->st,
+                                   ln, feat_stride, idx_bytes));
     PROFILED_KERNEL(EAGLE_PROF_DRAFT, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_PART),
              launch_gemm(z.dt, EPI_PART, c->fc, c->xop, c->xlo, M, z.H, 2 * z.H, c->gpart, z.H,
                          nullptr, 0, &S, c->st, tm_));
     SCHK(resnorm(c, hout, M, S, true, c->dl.attn_norm, nullptr));
   } else {
-    for (int b = 0; b < s.n; ++b)
-      PROFILED(EAGLE_PROF_ROWS, (double)s.rows * z.H * 16.0,
-               launch_draft_input_e3(z.dt, c->embed, lane_ptr(tok, b, c->lane_bytes),
-                                     feat + b * feat_stride, lane_ptr(idx, b, idx_bytes),
-                                     c->dl.attn_norm, c->cfg.rms_eps, s.rows, z.H,
-                                     (char*)c->xop + (int64_t)b * s.rows * xrow * z.esz, c->xlo,
-                                     hout + (int64_t)b * s.rows * z.H, c->st));
+    PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 16.0,
+             launch_draft_input_e3(z.dt, c->embed, tok, feat, idx, c->dl.attn_norm, c->cfg.rms_eps,
+                                   M, z.H, c->xop, c->xlo, hout, c->st, ln, feat_stride,
+                                   idx_bytes));
   }
   int sd = 1;
   SCHK(layer_core(c, c->dl, z.kin_draft, M, hout, pos, slot, lane_view(c->dkv, s.first, z.esz),
-                  vis, lanes_of(c, s), false, &sd));
+                  vis, ln, false, &sd));
   SCHK(resnorm(c, hout, M, sd, false, nullptr, nullptr));
   return EAGLE_OK;
 }
@@ -768,30 +755,22 @@ eagle_status catch_up_fixed(eagle_ctx* c, const float* feat, int64_t feat_stride
   const Derived& z = c->z;
   const int M1 = z.D + 1, B = z.B;
   const Lane& q0 = c->lanes[0];
-  for (const Lane& q : c->lanes)
-    HCHK(launch_rows_causal(q.ctx_len + 1, M1, q.rpos, q.rslot, q.rprehi, q.rmask, c->st));
+  const Lanes ln = lanes_of(c, Span{0, B, M1});
+  HCHK(launch_rows_causal(q0.ctx_len + 1, M1, q0.rpos, q0.rslot, q0.rprehi, q0.rmask, c->st, ln));
   RowVis vis{q0.rprehi, q0.rmask, 1, 0, 0, q0.ctx_len + 1 + M1};
   SCHK(draft_pass(c, Span{0, B, M1}, q0.new_tok, feat, feat_stride, idx, idx_bytes, q0.rpos,
                   q0.rslot, vis, c->hcat));
-  for (int b = 0; b < B; ++b) {
-    const Lane& q = c->lanes[b];
-    PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
-             launch_gather_f32(c->hcat + (int64_t)b * M1 * z.H, z.H, q.acc, 1, z.H, q.dout, c->st));
-    // the root row's LM-head operand, gathered to row b of the (now free) q operand buffer
-    PROFILED(EAGLE_PROF_ROWS, (double)z.H * 8.0,
-             launch_gather_t(z.dt, (const char*)c->xop + (int64_t)b * M1 * z.H * z.esz, z.H, c->xlo,
-                             q.acc, 1, z.H, (char*)c->qop + (int64_t)b * z.H * z.esz, c->qlo,
-                             c->st));
-  }
+  // each sequence's root row: its draft output to dout row 0 and its LM-head
+  // operand to row b of the (now free) q operand buffer
+  PROFILED(EAGLE_PROF_ROWS, (double)B * z.H * 16.0,
+           launch_gather_roots(z.dt, c->hcat, c->xop, c->xlo, M1, q0.acc, z.H, q0.dout,
+                               c->dout_stride, c->qop, c->qlo, ln, c->st));
   PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)B * z.H * 4.0,
            launch_lmhead_topk(z.dt, c->lm, c->qop, c->qlo, B, z.V, z.H, z.k_b, c->hpart, c->ids,
                               c->logp, c->st));
-  for (int b = 0; b < B; ++b) {
-    const Lane& q = c->lanes[b];
-    PROFILED(EAGLE_PROF_TREE, 0.0,
-             launch_tree_append(q.t, c->tp, c->ids + b * z.k_b, c->logp + b * z.k_b, 1, q.ctx_len,
-                                c->st, q.acc));
-  }
+  PROFILED(EAGLE_PROF_TREE, 0.0,
+           launch_tree_append(q0.t, c->tp, c->ids, c->logp, 1, q0.ctx_len, c->st, q0.acc, ln,
+                              z.k_b));
   return EAGLE_OK;
 }
 
@@ -1100,12 +1079,12 @@ eagle_status eagle_draft_tree(eagle_ctx* c, eagle_tree* out) {
       return set_err(c, EAGLE_E_STATE, "eagle_draft_tree needs every sequence READY (call eagle_prefill / eagle_verify)");
   const Derived& z = c->z;
   const int B = z.B;
+  const Lane& q0 = c->lanes[0];
   if (plain_mode(c)) {
-    for (const Lane& q : c->lanes)
-      HCHK(launch_tree_masks(q.t, 1, q.ctx_len, q.seq + q.ctx_len, c->st));
+    HCHK(launch_tree_masks(q0.t, 1, q0.ctx_len, q0.seq + q0.ctx_len, c->st,
+                           lanes_of(c, Span{0, B, 1})));
   } else {
     // each pass drafts the same number of rows for every sequence
-    const Lane& q0 = c->lanes[0];
     const int ctx0 = q0.ctx_len;
     int t0 = 0;
     for (int pass = 2; pass <= z.D; ++pass) {
@@ -1124,17 +1103,14 @@ eagle_status eagle_draft_tree(eagle_ctx* c, eagle_tree* out) {
       PROFILED(EAGLE_PROF_LMHEAD, (double)z.V * z.H * z.esz + (double)B * M * z.H * 4.0,
                launch_lmhead_topk(z.dt, c->lm, c->xop, c->xlo, B * M, z.V, z.H, z.k_b, c->hpart,
                                   c->ids, c->logp, c->st));
-      for (int b = 0; b < B; ++b) {
-        const Lane& q = c->lanes[b];
-        PROFILED(EAGLE_PROF_TREE, 0.0,
-                 launch_tree_append(q.t, c->tp, c->ids + (int64_t)b * M * z.k_b,
-                                    c->logp + (int64_t)b * M * z.k_b, pass, q.ctx_len, c->st));
-      }
+      PROFILED(EAGLE_PROF_TREE, 0.0,
+               launch_tree_append(q0.t, c->tp, c->ids, c->logp, pass, ctx0, c->st, nullptr,
+                                  lanes_of(c, Span{0, B, M}), (int64_t)M * z.k_b));
       t0 += M;
     }
-    for (const Lane& q : c->lanes)
-      PROFILED(EAGLE_PROF_TREE, 0.0,
-               launch_tree_finalize(q.t, c->tp, q.ctx_len, q.seq + q.ctx_len, c->st));
+    PROFILED(EAGLE_PROF_TREE, 0.0,
+             launch_tree_finalize(q0.t, c->tp, ctx0, q0.seq + ctx0, c->st,
+                                  lanes_of(c, Span{0, B, 1})));
   }
   for (Lane& q : c->lanes) q.state = ST_DRAFTED;
   if (out) SCHK(copy_tree_out(c, 0, out));
@@ -1239,19 +1215,13 @@ eagle_status verify_all(eagle_ctx* c, const eagle_tree* planted, int32_t* out_to
                                     q.cu_src, q.seq + q.ctx_len + 1, q.hres_dev, tag, c->st));
     }
   } else {
-    for (int b = 0; b < B; ++b) {
-      const Lane& q = c->lanes[b];
-      PROFILED(EAGLE_PROF_TREE, 0.0,
-               launch_accept(q.t, c->g + b * Mv, z.D, q.acc, q.new_tok, q.cu_src,
-                             q.seq + q.ctx_len + 1, q.hres_dev, tag, c->st));
-    }
+    PROFILED(EAGLE_PROF_TREE, 0.0,
+             launch_accept(q0.t, c->g, z.D, q0.acc, q0.new_tok, q0.cu_src, q0.seq + ctx0 + 1,
+                           q0.hres_dev, tag, c->st, lanes_of(c, Span{0, B, Mv}), Mv, HRES_INTS));
   }
-  for (int b = 0; b < B; ++b) {
-    const Lane& q = c->lanes[b];
-    PROFILED(EAGLE_PROF_KV, 0.0,
-             launch_kv_compact(z.dt, lane_view(c->tkv0, b, z.esz), c->t_layer_elems, z.NL, q.acc,
-                               q.acc + 2, q.ctx_len, c->st));
-  }
+  PROFILED(EAGLE_PROF_KV, 0.0,
+           launch_kv_compact(z.dt, c->tkv0, c->t_layer_elems, z.NL, q0.acc, q0.acc + 2, ctx0,
+                             c->st, lanes_of(c, Span{0, B, Mv})));
   if (!plain_mode(c)) {
     // the catch-up is queued before the host learns L, so the GPU runs on
     // while the host waits for the acceptance results

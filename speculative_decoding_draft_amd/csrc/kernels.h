@@ -82,8 +82,25 @@ struct Lanes {
   int off[MAX_LANES] = {};
 };
 
+// Device side of Lanes: sequence b's key shift (picked with selects, not a
+// dynamic index into the kernel arguments) and sequence b's copy of a
+// per-sequence array given sequence 0's.
+__device__ __forceinline__ int lane_shift(const Lanes& ln, int b) {
+  int o = 0;
+#pragma unroll
+  for (int i = 0; i < MAX_LANES; ++i) o = i == b ? ln.off[i] : o;
+  return o;
+}
+template <typename T>
+__device__ __forceinline__ T* lane_at(T* p, int b, int64_t bytes) {
+  return (T*)((char*)p + (int64_t)b * bytes);
+}
+
+// Sequence-aware forms (ln.n > 1): row r of sequence b = r / ln.rows takes
+// its token (and feature index) from sequence b's copy of the array
+// (ln.bytes apart) and its feature from feat + b * feat_stride.
 hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int M, float* h,
-                        hipStream_t st);
+                        hipStream_t st, const Lanes& ln = Lanes());
 // Operand outputs (out_t, q_out, x, dst of store_feat / gather_t) take
 // their lo-plane offset `lo` in elements (ignored for fp32).
 //
@@ -111,20 +128,34 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
                             int64_t olo, hipStream_t st, const Lanes& ln = Lanes());
 hipError_t launch_draft_input_e1(int dtype, const void* E, const int32_t* tok, const float* feat,
                                  const int32_t* idx, int M, int H, void* x, int64_t lo,
-                                 hipStream_t st);
+                                 hipStream_t st, const Lanes& ln = Lanes(),
+                                 int64_t feat_stride = 0, int64_t idx_bytes = 0);
 hipError_t launch_draft_input_e3(int dtype, const void* E, const int32_t* tok, const float* feat,
                                  const int32_t* idx, const float* gain, float eps, int M, int H,
-                                 void* x, int64_t lo, float* h, hipStream_t st);
+                                 void* x, int64_t lo, float* h, hipStream_t st,
+                                 const Lanes& ln = Lanes(), int64_t feat_stride = 0,
+                                 int64_t idx_bytes = 0);
 hipError_t launch_gather_f32(const float* src, int64_t ld, const int32_t* idx, int M, int W,
                              float* dst, hipStream_t st);
 hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, int64_t src_lo, const int32_t* idx,
                            int M, int W, void* dst, int64_t dst_lo, hipStream_t st);
 hipError_t launch_store_feat(int dtype, const float* h, int H, int M, void* dst, int64_t ldd,
                              int64_t lo, hipStream_t st);
+// One root row per sequence: row b of dst (dst_f: b * dst_stride floats;
+// dst_t: an operand row of width W) = row b * src_rows + r_b of src, where
+// r_b = sequence b's acc[0] (acc: sequence 0's copy, ln.bytes apart).
+hipError_t launch_gather_roots(int dtype, const float* src_f, const void* src_t, int64_t src_lo,
+                               int src_rows, const int32_t* acc, int W, float* dst_f,
+                               int64_t dst_stride, void* dst_t, int64_t dst_lo, const Lanes& ln,
+                               hipStream_t st);
+// Sequence-aware forms: sequence b's rows start at first + ln.off[b] (its
+// arrays ln.bytes apart); its cache compaction uses its own cache
+// (KVView::lane_elems), L / path copies and context ctx + ln.off[b].
 hipError_t launch_rows_causal(int first, int M, int32_t* pos, int32_t* slot, int32_t* prehi,
-                              uint64_t* mask, hipStream_t st);
+                              uint64_t* mask, hipStream_t st, const Lanes& ln = Lanes());
 hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int n_layers,
-                             const int32_t* L, const int32_t* path, int ctx, hipStream_t st);
+                             const int32_t* L, const int32_t* path, int ctx, hipStream_t st,
+                             const Lanes& ln = Lanes());
 
 // ---------------------------------------------------------------- tree
 #define TREE_MAXN 1024
@@ -158,16 +189,24 @@ struct TreeParams {
 // write its row descriptors. ids/logp: [rows of the pass, k_b]. The root
 // sits at position ctx, or at ctx + ctx_len[0] + 1 when ctx_len (a device
 // int, the acceptance length) is given.
+// Sequence-aware forms of the tree kernels: one workgroup per sequence b <
+// ln.n, whose tree state is t shifted by b * ln.bytes (every TreeDev array)
+// and whose context is ctx + ln.off[b]; ids / logp of sequence b start b *
+// ids_stride elements in, its root token pointer (and ctx_len, g, acc,
+// new_tok, cu_src, seq_out) are sequence 0's shifted by b * ln.bytes (plus
+// ln.off[b] elements for pointers into the sequence), g by b * g_stride and
+// host by b * host_stride.
 hipError_t launch_tree_append(TreeDev t, TreeParams p, const int32_t* ids, const float* logp,
-                              int pass, int ctx, hipStream_t st, const int32_t* ctx_len = nullptr);
+                              int pass, int ctx, hipStream_t st, const int32_t* ctx_len = nullptr,
+                              const Lanes& ln = Lanes(), int64_t ids_stride = 0);
 // Rerank to the best `budget` nodes, flatten to verify rows (root first,
 // then by depth and rerank order), build positions and ancestry masks.
 // root_token: device pointer to the last committed token.
 hipError_t launch_tree_finalize(TreeDev t, TreeParams p, int ctx, const int32_t* root_token,
-                                hipStream_t st);
+                                hipStream_t st, const Lanes& ln = Lanes());
 // Masks/positions for verify rows already in v_tok / v_parent (planted tree).
 hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root_token,
-                             hipStream_t st);
+                             hipStream_t st, const Lanes& ln = Lanes());
 // Greedy acceptance walk over the verify rows given the target's choices g.
 // acc[0] = L, acc[1] = bonus, acc[2..2+L) = accepted rows; new_tok[0..L]
 // = the committed tokens; cu_src[0..L] = feature rows feeding the catch-up.
@@ -197,4 +236,5 @@ hipError_t launch_sample_token(const float* ebuf, const double* zpart, int V, ui
                                uint32_t step, uint32_t lane, int32_t* out, hipStream_t st);
 hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
                          int32_t* new_tok, int32_t* cu_src, int32_t* seq_out, int32_t* host,
-                         int32_t tag, hipStream_t st);
+                         int32_t tag, hipStream_t st, const Lanes& ln = Lanes(),
+                         int64_t g_stride = 0, int64_t host_stride = 0);

@@ -10,6 +10,45 @@
 
 namespace {
 
+// Sequence b's tree state: every array of sequence 0's shifted by b * bytes.
+__device__ __forceinline__ TreeDev tree_lane(TreeDev t, int b, int64_t bytes) {
+  if (b == 0) return t;
+  t.tok = lane_at(t.tok, b, bytes);
+  t.parent = lane_at(t.parent, b, bytes);
+  t.depth = lane_at(t.depth, b, bytes);
+  t.srcrow = lane_at(t.srcrow, b, bytes);
+  t.rank = lane_at(t.rank, b, bytes);
+  t.row_of_node = lane_at(t.row_of_node, b, bytes);
+  t.v_row_of_node = lane_at(t.v_row_of_node, b, bytes);
+  t.logv = lane_at(t.logv, b, bytes);
+  t.logp = lane_at(t.logp, b, bytes);
+  t.counts = lane_at(t.counts, b, bytes);
+  t.exp_nodes = lane_at(t.exp_nodes, b, bytes);
+  t.row_tok = lane_at(t.row_tok, b, bytes);
+  t.row_src = lane_at(t.row_src, b, bytes);
+  t.row_pos = lane_at(t.row_pos, b, bytes);
+  t.row_slot = lane_at(t.row_slot, b, bytes);
+  t.row_prehi = lane_at(t.row_prehi, b, bytes);
+  t.row_mask = lane_at(t.row_mask, b, bytes);
+  t.tmask = lane_at(t.tmask, b, bytes);
+  t.v_tok = lane_at(t.v_tok, b, bytes);
+  t.v_parent = lane_at(t.v_parent, b, bytes);
+  t.v_depth = lane_at(t.v_depth, b, bytes);
+  t.v_node = lane_at(t.v_node, b, bytes);
+  t.v_pos = lane_at(t.v_pos, b, bytes);
+  t.v_slot = lane_at(t.v_slot, b, bytes);
+  t.v_prehi = lane_at(t.v_prehi, b, bytes);
+  t.v_logv = lane_at(t.v_logv, b, bytes);
+  t.v_mask = lane_at(t.v_mask, b, bytes);
+  t.s_parent = lane_at(t.s_parent, b, bytes);
+  t.s_rank = lane_at(t.s_rank, b, bytes);
+  t.s_depth = lane_at(t.s_depth, b, bytes);
+  t.s_prow = lane_at(t.s_prow, b, bytes);
+  t.s_exp = lane_at(t.s_exp, b, bytes);
+  t.s_nexp = lane_at(t.s_nexp, b, bytes);
+  return t;
+}
+
 __device__ __forceinline__ void set_bit(uint64_t* m, int j) {
   if (j < 64) m[0] |= (1ull << j);
   else m[1] |= (1ull << (j - 64));
@@ -18,10 +57,18 @@ __device__ __forceinline__ void set_bit(uint64_t* m, int j) {
 __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams p,
                                                           const int32_t* ids, const float* lps,
                                                           int pass, int ctx,
-                                                          const int32_t* ctx_len) {
+                                                          const int32_t* ctx_len, Lanes ln,
+                                                          int64_t ids_stride) {
   __shared__ int s_base, s_nrows, s_nnew, s_nsel, s_tbase;
   __shared__ int sel[TREE_MAXEXP];
   const int tid = threadIdx.x;
+  // this workgroup's sequence
+  const int b = blockIdx.x;
+  t = tree_lane(t, b, ln.bytes);
+  ids += b * ids_stride;
+  lps += b * ids_stride;
+  ctx += lane_shift(ln, b);
+  if (ctx_len) ctx_len = lane_at(ctx_len, b, ln.bytes);
   if (ctx_len) ctx += ctx_len[0] + 1;   // the root sits after the ctx_len[0] + 1 tokens just committed
   if (tid == 0) {
     if (pass == 1) {
@@ -150,11 +197,16 @@ __device__ void build_masks(TreeDev& t, int n, int ctx) {
 }
 
 __global__ __launch_bounds__(1024) void tree_finalize_kernel(TreeDev t, TreeParams p, int ctx,
-                                                             const int32_t* root_token) {
+                                                             const int32_t* root_token, Lanes ln) {
   __shared__ uint64_t keys[TREE_MAXN];
   __shared__ int kept[TREE_MAXROWS];
   __shared__ int s_n, s_m;
   const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  const int sh = lane_shift(ln, b);
+  t = tree_lane(t, b, ln.bytes);
+  ctx += sh;
+  root_token = lane_at(root_token, b, ln.bytes) + sh;
   if (tid == 0) {
     s_n = t.counts[0];
     s_m = p.dynamic ? min(p.budget, s_n) : s_n;
@@ -221,7 +273,12 @@ __global__ __launch_bounds__(1024) void tree_finalize_kernel(TreeDev t, TreePara
 }
 
 __global__ __launch_bounds__(128) void tree_masks_kernel(TreeDev t, int n_rows, int ctx,
-                                                        const int32_t* root) {
+                                                        const int32_t* root, Lanes ln) {
+  const int b = blockIdx.x;
+  const int sh = lane_shift(ln, b);
+  t = tree_lane(t, b, ln.bytes);
+  ctx += sh;
+  root = lane_at(root, b, ln.bytes) + sh;
   if (threadIdx.x == 0) {
     t.v_tok[0] = *root;
     t.v_parent[0] = -1;
@@ -239,8 +296,18 @@ __global__ __launch_bounds__(128) void tree_masks_kernel(TreeDev t, int n_rows, 
 // system-scope fence, so the host can read the result while the stream runs on.
 __global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g, int max_depth,
                                                     int32_t* acc, int32_t* new_tok, int32_t* cu_src,
-                                                    int32_t* seq_out, int32_t* host, int32_t tag) {
+                                                    int32_t* seq_out, int32_t* host, int32_t tag,
+                                                    Lanes ln, int64_t g_stride, int64_t host_stride) {
   const int lane = threadIdx.x;
+  // this workgroup's sequence
+  const int b = blockIdx.x;
+  t = tree_lane(t, b, ln.bytes);
+  g += b * g_stride;
+  acc = lane_at(acc, b, ln.bytes);
+  new_tok = lane_at(new_tok, b, ln.bytes);
+  cu_src = lane_at(cu_src, b, ln.bytes);
+  seq_out = lane_at(seq_out, b, ln.bytes) + lane_shift(ln, b);
+  if (host) host += b * host_stride;
   const int n = t.counts[3];
   int cur = 0, L = 0;
   for (int step = 0; step < max_depth; ++step) {
@@ -283,29 +350,37 @@ __global__ __launch_bounds__(64) void accept_kernel(TreeDev t, const int32_t* g,
 
 }  // namespace
 
+static bool lanes_bad(const Lanes& ln) { return ln.n < 1 || ln.n > MAX_LANES; }
+
 hipError_t launch_tree_append(TreeDev t, TreeParams p, const int32_t* ids, const float* logp,
-                              int pass, int ctx, hipStream_t st, const int32_t* ctx_len) {
-  hipLaunchKernelGGL(tree_append_kernel, dim3(1), dim3(256), 0, st, t, p, ids, logp, pass, ctx,
-                     ctx_len);
+                              int pass, int ctx, hipStream_t st, const int32_t* ctx_len,
+                              const Lanes& ln, int64_t ids_stride) {
+  if (lanes_bad(ln)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tree_append_kernel, dim3(ln.n), dim3(256), 0, st, t, p, ids, logp, pass, ctx,
+                     ctx_len, ln, ids_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_tree_finalize(TreeDev t, TreeParams p, int ctx, const int32_t* root_token,
-                                hipStream_t st) {
-  hipLaunchKernelGGL(tree_finalize_kernel, dim3(1), dim3(1024), 0, st, t, p, ctx, root_token);
+                                hipStream_t st, const Lanes& ln) {
+  if (lanes_bad(ln)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tree_finalize_kernel, dim3(ln.n), dim3(1024), 0, st, t, p, ctx, root_token, ln);
   return hipGetLastError();
 }
 
 hipError_t launch_tree_masks(TreeDev t, int n_rows, int ctx, const int32_t* root_token,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(tree_masks_kernel, dim3(1), dim3(128), 0, st, t, n_rows, ctx, root_token);
+                             hipStream_t st, const Lanes& ln) {
+  if (lanes_bad(ln)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(tree_masks_kernel, dim3(ln.n), dim3(128), 0, st, t, n_rows, ctx, root_token, ln);
   return hipGetLastError();
 }
 
 hipError_t launch_accept(TreeDev t, const int32_t* g, int max_depth, int32_t* acc,
                          int32_t* new_tok, int32_t* cu_src, int32_t* seq_out, int32_t* host,
-                         int32_t tag, hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(1), dim3(64), 0, st, t, g, max_depth, acc, new_tok, cu_src,
-                     seq_out, host, tag);
+                         int32_t tag, hipStream_t st, const Lanes& ln, int64_t g_stride,
+                         int64_t host_stride) {
+  if (lanes_bad(ln)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(accept_kernel, dim3(ln.n), dim3(64), 0, st, t, g, max_depth, acc, new_tok, cu_src,
+                     seq_out, host, tag, ln, g_stride, host_stride);
   return hipGetLastError();
 }
