@@ -702,8 +702,8 @@ template <int MT, int KIND> struct Cfg { static constexpr int NW = 8, CS = 4, NB
 template <> struct Cfg<1, EPI_PART> { static constexpr int NW = 4, CS = 4, NB = 1; };
 template <> struct Cfg<1, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4, NB = 1; };
 template <> struct Cfg<1, KIND_HEAD> { static constexpr int NW = 4, CS = 16, NB = 1; };
-template <> struct Cfg<2, EPI_PART> { static constexpr int NW = 4, CS = 4, NB = 1; };
-template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4, NB = 1; };
+template <> struct Cfg<2, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
+template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<2, KIND_HEAD> { static constexpr int NW = 4, CS = 8, NB = 1; };
 template <> struct Cfg<3, EPI_PART> { static constexpr int NW = 4, CS = 2, NB = 1; };
 template <> struct Cfg<3, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
