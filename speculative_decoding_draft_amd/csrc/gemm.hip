@@ -709,7 +709,7 @@ template <> struct Cfg<3, EPI_PART> { static constexpr int NW = 4, CS = 2, NB = 
 template <> struct Cfg<3, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<4, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<4, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
-template <> struct Cfg<5, EPI_PART> { static constexpr int NW = 4, CS = 2, NB = 1; };
+template <> struct Cfg<5, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<5, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
 // bf16 q|k|v over many activation rows (batched verify rows, prefill
 // chunks): one pass over up to 256 rows, each wave two 16-row weight blocks
