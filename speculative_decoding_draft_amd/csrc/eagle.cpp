@@ -608,7 +608,6 @@ KVView lane_view(KVView v, int b, int esz) {
   return v;
 }
 
-
 // ------------------------------------------------------------ passes
 // Applies the pending split-K partial planes of a projection to the
 // residual stream h (or sets h to their sum) and writes the next operand:
