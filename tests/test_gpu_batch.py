@@ -20,6 +20,9 @@ one pass over the weights.
 * full-size c2 at batch 4 (launched as the benchmark runs it): tree policy
   and acceptance bit-exact per lane, and each lane's stream equals a batch-1
   engine's stream on the same prompt up to a near-tie.
+* sampling in a batch on reduced c2 (EAGLE-1) and c4 (EAGLE-3): each lane's
+  tokens equal the oracle's rejection-sampling walk on that lane's GPU
+  logits with the lane's own draw stream.
 """
 import numpy as np
 import pytest
@@ -253,3 +256,35 @@ def test_full_c2_batch4_lanes_equal_batch1():
         print(f"c2 lane {b} (prompt {lens[b]}): batch 4 == batch 1 on {same}/{n - 1} tokens",
               flush=True)
     one.close()
+
+
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_bf16_batch_sampling_decisions_match_oracle(name):
+    """Sampling in a batch (reduced c2: static tree, EAGLE-1; reduced c4:
+    dynamic tree, EAGLE-3): every lane's committed tokens equal the oracle's
+    rejection-sampling walk over that lane's tree, on the GPU's own verify
+    logits of that lane, with the lane's own draw stream (counter word 3 =
+    lane)."""
+    from gpu_helpers import engine
+    from oracle import sampling as S
+    B = 3 if name == "c2" else 2
+    w = dict(synth.workloads.reduced(name, prompt_len=60, gen=16), batch=B, temperature=0.7,
+             seed=77)
+    eng = engine(w, max_ctx=_max_ctx(w, B), prefill_chunk=32)
+    prompts = _ragged_prompts(w, B, seed0=51)
+    print(f"{w['name']} batch {B} sampling", flush=True)
+    for b, p in enumerate(prompts):
+        eng.prefill(p, lane=b)
+    for step in range(1, 5):
+        eng.draft_tree(want=False)
+        trees = [eng.read_tree(b) for b in range(B)]
+        news = eng.verify_batch()
+        lg = eng.debug_read("logits")
+        mv = len(trees[0]["token"])
+        assert lg.shape == (B * mv, w["vocab"])
+        for b, tree in enumerate(trees):
+            path, bonus = S.accept_sample(tree["token"], tree["parent"], lg[b * mv:(b + 1) * mv],
+                                          w["temperature"], w["seed"], step, w["depth"], lane=b)
+            assert news[b] == [tree["token"][r] for r in path] + [bonus], (step, b)
+        print(f"{w['name']} sampled cycle {step}: accepted {[len(n) - 1 for n in news]}", flush=True)
+    eng.close()
