@@ -773,9 +773,38 @@ hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_
   return hipGetLastError();
 }
 
+// SwiGLU with six waves (48 output columns per workgroup): for an FFN width
+// whose eight-wave grid leaves CUs idle (F = 11008: 172 workgroups against
+// 230), measured 8-11% faster at 7, 27 and 61 rows.
+template <int MT> struct Swiglu6 { static constexpr int CS = MT == 2 ? 4 : 2; };
+
+template <typename T, int MT>
+hipError_t launch_swiglu6(const ProjArgs& a, int tiles, hipStream_t st, const KTiming* tm) {
+  constexpr int CS = Swiglu6<MT>::CS;
+  const dim3 grid(tiles), block(6 * 64);
+  if (tm)
+    hipExtLaunchKernelGGL((proj_kernel<T, MT, 6, CS, 1, EPI_SWIGLU>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+  else
+    hipLaunchKernelGGL((proj_kernel<T, MT, 6, CS, 1, EPI_SWIGLU>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int EPI>
 hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hipStream_t st,
-                         const KTiming* tm) {
+                         const KTiming* tm, int nw) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    if (nw == 6) {
+      if (m_chunks != 1) return hipErrorInvalidValue;
+      switch (mt) {
+        case 1: return launch_swiglu6<T, 1>(a, tiles, st, tm);
+        case 2: return launch_swiglu6<T, 2>(a, tiles, st, tm);
+        case 3: return launch_swiglu6<T, 3>(a, tiles, st, tm);
+        case 4: return launch_swiglu6<T, 4>(a, tiles, st, tm);
+        case 5: return launch_swiglu6<T, 5>(a, tiles, st, tm);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   if constexpr (Opnd<T>::SPLIT && EPI == EPI_PART) {   // many-row q|k|v: bf16 only
     if (mt == 8) return launch_proj_mt<T, 8, EPI_PART>(a, tiles, m_chunks, st, tm);
     if (mt == 16) return launch_proj_mt<T, 16, EPI_PART>(a, tiles, m_chunks, st, tm);
@@ -823,13 +852,20 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
     p.mt = 4;   // passes of 64 rows
   }
   p.m_chunks = (M + 16 * p.mt - 1) / (16 * p.mt);
-  const int nw = waves_for(p.mt, epi);
+  p.nw = waves_for(p.mt, epi);
   p.nb = dtype == 1 ? blocks_for(p.mt, epi) : 1;
-  const int rows_per_tile = 16 * nw * p.nb;
+  const int rows_per_tile = 16 * p.nw * p.nb;
   if (epi == EPI_SWIGLU) {
     const int F = N_rows / 2;
     p.n_tiles = (F + rows_per_tile / 2 - 1) / (rows_per_tile / 2);
     p.splits = 1;
+    // one pass of row tiles: take six waves when their grid still fits one
+    // workgroup per CU and is larger than the eight-wave grid
+    const int t6 = (F + 47) / 48;
+    if (p.m_chunks == 1 && p.mt <= 5 && p.nb == 1 && p.nw == 8 && t6 <= 256 && t6 > p.n_tiles) {
+      p.nw = 6;
+      p.n_tiles = t6;
+    }
   } else {
     p.n_tiles = (N_rows + rows_per_tile - 1) / rows_per_tile;
     const int steps = K / (dtype == 1 ? 32 : 16);
@@ -869,11 +905,11 @@ hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t
   a.Yt = Yt; a.ytlo = ytlo;
   if (splits_out) splits_out[0] = p.splits;
   if (dtype == 1) {
-    return epi == EPI_SWIGLU ? launch_proj_t<bf16_t, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm)
-                             : launch_proj_t<bf16_t, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm);
+    return epi == EPI_SWIGLU ? launch_proj_t<bf16_t, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm, p.nw)
+                             : launch_proj_t<bf16_t, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm, p.nw);
   }
-  return epi == EPI_SWIGLU ? launch_proj_t<float, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm)
-                           : launch_proj_t<float, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm);
+  return epi == EPI_SWIGLU ? launch_proj_t<float, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm, p.nw)
+                           : launch_proj_t<float, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm, p.nw);
 }
 
 uint64_t lmhead_part_floats(int M, int V, int k) {
