@@ -773,19 +773,19 @@ hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_
   return hipGetLastError();
 }
 
-// SwiGLU with six waves (48 output columns per workgroup): for an FFN width
-// whose eight-wave grid leaves CUs idle (F = 11008: 172 workgroups against
-// 230), measured 8-11% faster at 7, 27 and 61 rows.
-template <int MT> struct Swiglu6 { static constexpr int CS = MT == 2 ? 4 : 2; };
-
-template <typename T, int MT>
-hipError_t launch_swiglu6(const ProjArgs& a, int tiles, hipStream_t st, const KTiming* tm) {
-  constexpr int CS = Swiglu6<MT>::CS;
-  const dim3 grid(tiles), block(6 * 64);
+// SwiGLU with six or fourteen waves (48 or 112 output columns per
+// workgroup) in place of eight, for FFN widths whose eight-wave grid leaves
+// CUs idle or spills into a second round: F = 11008 takes 230 workgroups
+// (eight waves: 172; measured 8-11% faster at 7, 27 and 61 rows) and F =
+// 28672 takes 256 (eight waves: 448; 9% faster at 61 rows).
+template <typename T, int MT, int NW>
+hipError_t launch_swiglu_w(const ProjArgs& a, int tiles, hipStream_t st, const KTiming* tm) {
+  constexpr int CS = (NW == 6 && MT == 2) ? 4 : 2;
+  const dim3 grid(tiles), block(NW * 64);
   if (tm)
-    hipExtLaunchKernelGGL((proj_kernel<T, MT, 6, CS, 1, EPI_SWIGLU>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+    hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, 1, EPI_SWIGLU>), grid, block, 0, st, tm->start, tm->stop, 0, a);
   else
-    hipLaunchKernelGGL((proj_kernel<T, MT, 6, CS, 1, EPI_SWIGLU>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, 1, EPI_SWIGLU>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -793,14 +793,23 @@ template <typename T, int EPI>
 hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hipStream_t st,
                          const KTiming* tm, int nw) {
   if constexpr (EPI == EPI_SWIGLU) {
-    if (nw == 6) {
+    if (nw == 6 || nw == 14) {
       if (m_chunks != 1) return hipErrorInvalidValue;
-      switch (mt) {
-        case 1: return launch_swiglu6<T, 1>(a, tiles, st, tm);
-        case 2: return launch_swiglu6<T, 2>(a, tiles, st, tm);
-        case 3: return launch_swiglu6<T, 3>(a, tiles, st, tm);
-        case 4: return launch_swiglu6<T, 4>(a, tiles, st, tm);
-        case 5: return launch_swiglu6<T, 5>(a, tiles, st, tm);
+      if (nw == 6) {
+        switch (mt) {
+          case 1: return launch_swiglu_w<T, 1, 6>(a, tiles, st, tm);
+          case 2: return launch_swiglu_w<T, 2, 6>(a, tiles, st, tm);
+          case 3: return launch_swiglu_w<T, 3, 6>(a, tiles, st, tm);
+          case 4: return launch_swiglu_w<T, 4, 6>(a, tiles, st, tm);
+          case 5: return launch_swiglu_w<T, 5, 6>(a, tiles, st, tm);
+          default: return hipErrorInvalidValue;
+        }
+      }
+      switch (mt) {   // fourteen waves leave 128 registers per lane: up to four m-tiles
+        case 1: return launch_swiglu_w<T, 1, 14>(a, tiles, st, tm);
+        case 2: return launch_swiglu_w<T, 2, 14>(a, tiles, st, tm);
+        case 3: return launch_swiglu_w<T, 3, 14>(a, tiles, st, tm);
+        case 4: return launch_swiglu_w<T, 4, 14>(a, tiles, st, tm);
         default: return hipErrorInvalidValue;
       }
     }
@@ -859,12 +868,19 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
     const int F = N_rows / 2;
     p.n_tiles = (F + rows_per_tile / 2 - 1) / (rows_per_tile / 2);
     p.splits = 1;
-    // one pass of row tiles: take six waves when their grid still fits one
-    // workgroup per CU and is larger than the eight-wave grid
-    const int t6 = (F + 47) / 48;
-    if (p.m_chunks == 1 && p.mt <= 5 && p.nb == 1 && p.nw == 8 && t6 <= 256 && t6 > p.n_tiles) {
-      p.nw = 6;
-      p.n_tiles = t6;
+    // one pass of row tiles: of six, eight and fourteen waves take the
+    // largest grid that still fits one workgroup per CU (eight if none does)
+    if (p.m_chunks == 1 && p.mt <= 5 && p.nb == 1 && p.nw == 8) {
+      int best = p.n_tiles <= 256 ? p.n_tiles : 0;
+      for (int w : {6, 14}) {
+        if (w == 14 && p.mt > 4) continue;
+        const int t = (F + 8 * w - 1) / (8 * w);
+        if (t <= 256 && t > best) {
+          best = t;
+          p.nw = w;
+          p.n_tiles = t;
+        }
+      }
     }
   } else {
     p.n_tiles = (N_rows + rows_per_tile - 1) / rows_per_tile;

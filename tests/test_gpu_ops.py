@@ -117,7 +117,9 @@ def test_linear(dtype, M, N, K, epi):
 
 @pytest.mark.parametrize("dtype,M,N,K", [(BF16, 61, 11008, 4096), (BF16, 10, 1376, 1024),
                                          (BF16, 1, 11008, 4096), (F32, 17, 688, 256),
-                                         (BF16, 100, 2720, 1024), (BF16, 200, 1376, 1024)])
+                                         (BF16, 100, 2720, 1024), (BF16, 200, 1376, 1024),
+                                         # wide FFNs: fourteen-wave workgroups
+                                         (BF16, 27, 17008, 512), (F32, 17, 17000, 256)])
 def test_swiglu(dtype, M, N, K):
     print(f"swiglu dtype={dtype} M={M} N={N} K={K}", flush=True)
     gen = torch.Generator().manual_seed(M + N + K)
