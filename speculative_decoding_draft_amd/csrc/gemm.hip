@@ -406,6 +406,171 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- many rows
+// Split-K projection over many activation rows (a batch's verify rows, a
+// prefill chunk), bf16 only. The WC * XG waves of a workgroup form a WC x XG
+// grid: wave (c, g) multiplies the four 16-row weight blocks [64 c, 64 c +
+// 64) of the tile by staged rows [16 MT g, 16 MT (g + 1)), so each 1 KB
+// activation fragment read from LDS feeds eight products (hi and lo planes,
+// four blocks; two in proj_kernel's many-row tiles) and the XG groups share
+// one activation stage.
+//
+// The activation chunk (32 K columns of every staged row, hi and lo) goes
+// from global memory straight into LDS (global_load_lds_dwordx4: lane l of
+// a wave's copy lands at the wave's LDS base + 16 l), so no registers hold
+// it in flight and no LDS stores are issued. Each 1 KB block of the stage is
+// 16 rows x 4 chunks in the xs_addr swizzle, so lane l of block b copies
+// staged row R = 16 b + l / 4 at logical chunk (l % 4) ^ ((R / 2) % 4).
+// Weight fragments stream into a register ring two chunks ahead; the LDS
+// reads of m-tile t + 1 are issued before the products of m-tile t.
+// Measured on the 7B shapes against proj_kernel at 216-512 rows: q|k|v
+// -8..-15%, o -11%, down -17..-20%. (Staging through registers instead
+// spilled at MT = 8 and ran 15-25% slower; SwiGLU tiles of this shape gained
+// nothing over 64-row passes.)
+template <int MT, int WC, int XG>
+__device__ __forceinline__ void rows_core(const ProjArgs& a, int row0, int s_lo, int s_hi, int xg,
+                                          bf16_t* xs0, bf16_t* xs1, f32x4 (&acc)[4][MT]) {
+  constexpr int NW = WC * XG, NB = 4, KS = 32;
+  constexpr int MP = 16 * MT * XG;   // staged rows of one plane
+  constexpr int NBLK = 2 * MP / 16;  // 1 KB blocks of one stage buffer
+  static_assert(NBLK % NW == 0, "stage blocks must split evenly over the waves");
+  constexpr int BPW = NBLK / NW;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bf16_t* W = (const bf16_t*)a.W;
+  const bf16_t* X = (const bf16_t*)a.X;
+  const bf16_t* wp[NB];
+  int64_t wstep[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r0 = row0 + 16 * j;
+    const int rb = min(r0, a.rows - 1) >> 4;
+    if ((rb + 1) * 16 <= a.rows) {   // fragment-packed block
+      wp[j] = W + (int64_t)rb * 16 * a.K + lane * 8;
+      wstep[j] = 16 * KS;
+    } else {                         // ragged last block: row-major rows
+      wp[j] = W + (int64_t)min(r0 + lr, a.rows - 1) * a.K + lg * 8;
+      wstep[j] = KS;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nch = s_hi - s_lo;
+  if (nch <= 0) return;
+  int64_t xoff[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    const int R = 16 * (wave * BPW + i) + (lane >> 2);
+    const int plane = R / MP;
+    const int row = min(R - plane * MP, a.M - 1);
+    const int q = (lane & 3) ^ ((R >> 1) & 3);
+    xoff[i] = plane * a.xlo + (int64_t)row * a.K + q * 8;
+  }
+  // (inline assembly: the compiler then leaves the wait for these copies to
+  // the explicit vmcnt below instead of draining every outstanding load
+  // before each LDS read; the M0 write needs one wait state)
+  auto xdma = [&](bf16_t* buf, int c) {
+    const int k0 = (s_lo + min(c, nch - 1)) * KS;
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
+      const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)(buf + (wave * BPW + i) * 512);
+      const bf16_t* src = X + xoff[i] + k0;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+                   : "memory", "m0");
+    }
+  };
+  auto wload = [&](uint4 (&w)[NB], int c) {
+    const int s = s_lo + min(c, nch - 1);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) w[j] = ld16(wp[j] + (int64_t)s * wstep[j]);
+  };
+  const int xr0 = 16 * MT * xg;
+  auto rd = [&](const bf16_t* x, int r) {
+    return *reinterpret_cast<const uint4*>(x + xs_addr<bf16_t, KS>(r, lg));
+  };
+  auto compute = [&](const uint4 (&w)[NB], const bf16_t* x) {
+    uint4 h[2], l[2];
+    h[0] = rd(x, xr0 + lr);
+    l[0] = rd(x, MP + xr0 + lr);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t + 1 < MT) {
+        h[(t + 1) & 1] = rd(x, xr0 + 16 * (t + 1) + lr);
+        l[(t + 1) & 1] = rd(x, MP + xr0 + 16 * (t + 1) + lr);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) Mma<bf16_t>::mma(w[j], h[t & 1], acc[j][t]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) Mma<bf16_t>::mma(w[j], l[t & 1], acc[j][t]);
+    }
+  };
+  // the stage of chunk c + 1 is complete once only the NB weight loads
+  // issued after it (chunk c + 2) may still be in flight; the barrier then
+  // also ends every wave's reads of the buffer the next copy overwrites
+  uint4 w[4][NB];
+  xdma(xs0, 0);
+  wload(w[0], 0);
+  wload(w[1], 1);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NB) : "memory");
+  for (int c0 = 0; c0 < nch; c0 += 4) {
+#define ROWS_STEP(J)                                                           \
+    {                                                                          \
+      const int c = c0 + J;                                                    \
+      xdma((J % 2) ? xs0 : xs1, c + 1);                                        \
+      wload(w[(J + 2) % 4], c + 2);                                            \
+      if (c < nch) compute(w[J], (J % 2) ? xs1 : xs0);                         \
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NB) : "memory");   \
+    }
+    ROWS_STEP(0) ROWS_STEP(1) ROWS_STEP(2) ROWS_STEP(3)
+#undef ROWS_STEP
+  }
+}
+
+template <int MT, int WC, int XG>
+__global__ __launch_bounds__(WC * XG * 64) void rows_kernel(ProjArgs a) {
+  constexpr int NB = 4, MP = 16 * MT * XG, BUF = 2 * MP * 32;
+  __shared__ __attribute__((aligned(1024))) bf16_t xs0[BUF];
+  __shared__ __attribute__((aligned(1024))) bf16_t xs1[BUF];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wc = wave % WC, xg = wave / WC;
+  const int tile = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+  const int m0 = blockIdx.y * MP;
+  ProjArgs b = a;
+  b.X = (const bf16_t*)a.X + (int64_t)m0 * a.K;
+  b.M = min(MP, a.M - m0);
+  const int total = a.K / 32;
+  const int s_lo = split * a.steps_per_split;
+  const int s_hi = min(total, s_lo + a.steps_per_split);
+  const int xrow0 = 16 * MT * xg;
+  const int row0 = (tile * WC + wc) * 16 * NB;
+  f32x4 acc[NB][MT];
+  rows_core<MT, WC, XG>(b, row0, s_lo, s_hi, xg, xs0, xs1, acc);
+  float* Y = a.Y + (int64_t)split * a.plane;
+#pragma unroll
+  for (int jb = 0; jb < NB; ++jb) {
+    const int r0 = row0 + 16 * jb;
+    const bool vec = (a.ldy & 3) == 0 && (a.plane & 3) == 0 && ((uintptr_t)a.Y & 15) == 0 &&
+                     r0 + 16 <= a.rows;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const int m = xrow0 + 16 * t + lr;
+      if (m >= b.M) continue;
+      float* yr = Y + (int64_t)(m0 + m) * a.ldy + r0 + 4 * lg;
+      if (vec) {
+        *reinterpret_cast<f32x4*>(yr) = acc[jb][t];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (r0 + 4 * lg + j < a.rows) yr[j] = acc[jb][t][j];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- packing
 // Fragment packing of a bf16 matrix [rows, K] (K a multiple of 32): full
 // 16-row block rb is stored as K/32 fragments of 1 KB, fragment s holding
@@ -711,13 +876,11 @@ template <> struct Cfg<4, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 
 template <> struct Cfg<4, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<5, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<5, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
-// bf16 q|k|v over many activation rows (batched verify rows, prefill
-// chunks): one pass over up to 256 rows, each wave two 16-row weight blocks
-// (see proj_core_bf16). Measured against 64-row passes on the 7B shapes:
-// -10% at 108 rows, -20% at 216 and 256; the narrower projections and the
-// gate/up kernel gained nothing in the full cycle and keep 64-row passes.
+// bf16 q|k|v over 81-128 activation rows (batched verify rows): one pass,
+// each wave two 16-row weight blocks (see proj_core_bf16); measured -10%
+// against 64-row passes at 108 rows. Above 128 rows the PART projections
+// take rows_kernel.
 template <> struct Cfg<8, EPI_PART> { static constexpr int NW = 8, CS = 1, NB = 2; };
-template <> struct Cfg<16, EPI_PART> { static constexpr int NW = 8, CS = 1, NB = 2; };
 
 template <int KIND>
 int waves_t(int mt) {
@@ -727,7 +890,6 @@ int waves_t(int mt) {
     case 3: return Cfg<3, KIND>::NW;
     case 4: return Cfg<4, KIND>::NW;
     case 8: return Cfg<8, KIND>::NW;
-    case 16: return Cfg<16, KIND>::NW;
     default: return Cfg<5, KIND>::NW;
   }
 }
@@ -739,7 +901,6 @@ int chunk_t(int mt) {
     case 3: return Cfg<3, KIND>::CS;
     case 4: return Cfg<4, KIND>::CS;
     case 8: return Cfg<8, KIND>::CS;
-    case 16: return Cfg<16, KIND>::CS;
     default: return Cfg<5, KIND>::CS;
   }
 }
@@ -747,7 +908,6 @@ template <int KIND>
 int blocks_t(int mt) {
   switch (mt) {
     case 8: return Cfg<8, KIND>::NB;
-    case 16: return Cfg<16, KIND>::NB;
     default: return 1;
   }
 }
@@ -816,7 +976,6 @@ hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hip
   }
   if constexpr (Opnd<T>::SPLIT && EPI == EPI_PART) {   // many-row q|k|v: bf16 only
     if (mt == 8) return launch_proj_mt<T, 8, EPI_PART>(a, tiles, m_chunks, st, tm);
-    if (mt == 16) return launch_proj_mt<T, 16, EPI_PART>(a, tiles, m_chunks, st, tm);
   }
   switch (mt) {
     case 1: return launch_proj_mt<T, 1, EPI>(a, tiles, m_chunks, st, tm);
@@ -826,6 +985,18 @@ hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hip
     case 5: return launch_proj_mt<T, 5, EPI>(a, tiles, m_chunks, st, tm);
     default: return hipErrorInvalidValue;
   }
+}
+
+// rows_kernel with four wave columns (256 weight rows per tile) and two
+// row groups (16 MT * 2 rows per m-chunk)
+template <int MT>
+hipError_t launch_rows_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st, const KTiming* tm) {
+  const dim3 grid(tiles * a.splits, m_chunks), block(8 * 64);
+  if (tm)
+    hipExtLaunchKernelGGL((rows_kernel<MT, 4, 2>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+  else
+    hipLaunchKernelGGL((rows_kernel<MT, 4, 2>), grid, block, 0, st, a);
+  return hipGetLastError();
 }
 
 template <typename T, bool TOPK, int MT>
@@ -852,11 +1023,28 @@ int head_rows(int M) { return 16 * waves_for(M > 64 ? 5 : (M + 15) / 16, KIND_HE
 
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
   GemmPlan p;
+  if (dtype == 1 && epi == EPI_PART && M > 128) {
+    // rows_kernel: 256 weight rows per tile, m-chunks of 256 rows (wide
+    // outputs such as q|k|v) or 128 (more tiles for narrow ones); split K
+    // until the grid covers the CUs, keeping >= 16 steps per split (and at
+    // most four splits of the 256-row chunks: more measured slower)
+    p.xg = 2;
+    p.nb = 4;
+    p.nw = 8;
+    p.mt = N_rows >= 8192 ? 8 : 4;
+    p.m_chunks = (M + 32 * p.mt - 1) / (32 * p.mt);
+    p.n_tiles = (N_rows + 255) / 256;
+    const int steps = K / 32;
+    int s = 1;
+    while (s < (p.mt == 8 ? 4 : 16) && p.n_tiles * p.m_chunks * s < 256 && steps / (2 * s) >= 16) s *= 2;
+    p.splits = s;
+    return p;
+  }
   if (M <= 80) {
     p.mt = (M + 15) / 16;
   } else if (dtype == 1 && epi == EPI_PART && N_rows >= 8192) {
-    // wide projections (q|k|v) over many rows: one pass of up to 256 rows
-    p.mt = M <= 128 ? 8 : 16;
+    // wide projections (q|k|v) over 81-128 rows: one pass
+    p.mt = 8;
   } else {
     p.mt = 4;   // passes of 64 rows
   }
@@ -920,6 +1108,9 @@ hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t
   a.Y = Y; a.ldy = ldy; a.plane = (int64_t)M * ldy;
   a.Yt = Yt; a.ytlo = ytlo;
   if (splits_out) splits_out[0] = p.splits;
+  if (p.xg == 2)
+    return p.mt == 8 ? launch_rows_mt<8>(a, p.n_tiles, p.m_chunks, stream, tm)
+                     : launch_rows_mt<4>(a, p.n_tiles, p.m_chunks, stream, tm);
   if (dtype == 1) {
     return epi == EPI_SWIGLU ? launch_proj_t<bf16_t, EPI_SWIGLU>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm, p.nw)
                              : launch_proj_t<bf16_t, EPI_PART>(p.mt, a, p.n_tiles, p.m_chunks, stream, tm, p.nw);

@@ -13,7 +13,7 @@ enum { EPI_PART = 0, EPI_SWIGLU = 2 };
 //               written as an operand (two bf16 planes, lo at Yt + ytlo)
 // dtype 0 = fp32, 1 = bf16 for W. x is an operand (see Opnd in common.h):
 // for bf16 two planes, the lo plane xlo elements after the hi plane.
-struct GemmPlan { int mt, nb, splits, m_chunks, n_tiles, nw; };
+struct GemmPlan { int mt, nb, splits, m_chunks, n_tiles, nw, xg = 1; };
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi);
 uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M);
 // Optional device timestamps of one kernel dispatch: the events ride on the

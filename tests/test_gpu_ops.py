@@ -82,11 +82,14 @@ LINEAR = [  # (dtype, M, N, K): split-K, tails, several M tiles, prefill-sized M
     (BF16, 1, 4096, 4096), (BF16, 10, 4096, 8192), (BF16, 27, 12288, 4096),
     (BF16, 61, 4096, 11008), (BF16, 65, 1000, 1024), (BF16, 100, 256, 512),
     (BF16, 256, 512, 4096), (F32, 17, 256, 256), (F32, 17, 256, 688), (F32, 33, 1024, 512),
-    # many rows (a batch's verify rows, prefill chunks): wide projections take
-    # 128- and 256-row tiles with two weight blocks per wave; ragged N and a
-    # second row pass
+    # many rows (a batch's verify rows, prefill chunks): 81-128 rows of a wide
+    # projection take one 128-row pass; above 128 rows the 256-row weight
+    # tiles with activations copied straight into LDS (256-row chunks for
+    # wide outputs, 128 for narrow ones): ragged N (a half block, a partial
+    # tile), a second and third row chunk with one row, a single split
     (BF16, 108, 12288, 4096), (BF16, 216, 8200, 1024), (BF16, 300, 8192, 512),
-    (BF16, 130, 4096, 1024),
+    (BF16, 130, 4096, 1024), (BF16, 257, 4104, 2048), (BF16, 129, 1000, 256),
+    (BF16, 512, 4096, 11008),
 ]
 
 
