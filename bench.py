@@ -163,6 +163,8 @@ def main():
                     help="> 0: sampling-mode verification (rejection sampling over the tree)")
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences served per cycle (lanes; each its own prompt)")
+    ap.add_argument("--prefill-chunk", type=int, default=0,
+                    help="prompt rows per prefill pass (0: the library default, 512)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (the known-size "
                          "kernel that scales the HBM byte counters) and exit")
@@ -197,7 +199,7 @@ def main():
     cycles_needed = args.warmup + args.steps + max(0, args.profile_cycles) + 2 + 5   # + speedup-model cycles
     max_new = max(w["gen"], cycles_needed * (w["depth"] + 1))
     max_ctx = w["prompt_len"] + max_new + w["depth"] + 2
-    eng = E.Engine(w, max_ctx=max_ctx)
+    eng = E.Engine(w, max_ctx=max_ctx, prefill_chunk=args.prefill_chunk)
     synth.fill_weights(eng.table, eng.weights.data_ptr(), w["weight_seed"], eng.stream.cuda_stream)
     torch.cuda.synchronize()
     eng.load()
@@ -320,7 +322,8 @@ def main():
     out["prefill_roofline"] = {"bound": "mfma", "achieved": round(pf / (prefill_ms * 1e-3) / 1e12, 1),
                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(pf / (prefill_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                               "flops": pf, "tokens": len(prompt)}
+                               "flops": pf, "tokens": len(prompt),
+                               "chunk": args.prefill_chunk or 512}
     if model is not None:
         out["speedup_model"] = model
     if prof is not None:

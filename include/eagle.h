@@ -103,7 +103,7 @@ typedef struct eagle_config {
   int32_t static_rank[EAGLE_MAX_STATIC];   /* static: child rank in the
                                               parent's draft top-k */
   int32_t max_ctx;             /* capacity: prompt + generated tokens */
-  int32_t prefill_chunk;       /* rows per prefill pass (0 = 256) */
+  int32_t prefill_chunk;       /* rows per prefill pass (0 = 512) */
   /* Sampling. temperature 0 = greedy verification (the default). temperature
    * > 0 = sampling from softmax(logits / temperature): the prefill's token is
    * drawn, and verify tests the tree's candidates by rejection sampling, so

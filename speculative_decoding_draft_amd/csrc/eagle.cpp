@@ -163,7 +163,7 @@ bool derive(const eagle_config* c, Derived* z, std::string* why) {
   } else {
     return fail(why, "tree must be EAGLE_TREE_DYNAMIC or EAGLE_TREE_STATIC");
   }
-  z->chunk = c->prefill_chunk > 0 ? c->prefill_chunk : 256;
+  z->chunk = c->prefill_chunk > 0 ? c->prefill_chunk : 512;
   int pass_rows = 1;
   for (int p = 2; p <= z->D; ++p) pass_rows = std::max(pass_rows, z->rows_per_pass[p]);
   // one pass serves every sequence: B times the rows of one

@@ -876,11 +876,6 @@ template <> struct Cfg<4, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 
 template <> struct Cfg<4, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<5, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<5, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
-// bf16 q|k|v over 81-128 activation rows (batched verify rows): one pass,
-// each wave two 16-row weight blocks (see proj_core_bf16); measured -10%
-// against 64-row passes at 108 rows. Above 128 rows the PART projections
-// take rows_kernel.
-template <> struct Cfg<8, EPI_PART> { static constexpr int NW = 8, CS = 1, NB = 2; };
 
 template <int KIND>
 int waves_t(int mt) {
@@ -889,7 +884,6 @@ int waves_t(int mt) {
     case 2: return Cfg<2, KIND>::NW;
     case 3: return Cfg<3, KIND>::NW;
     case 4: return Cfg<4, KIND>::NW;
-    case 8: return Cfg<8, KIND>::NW;
     default: return Cfg<5, KIND>::NW;
   }
 }
@@ -900,15 +894,7 @@ int chunk_t(int mt) {
     case 2: return Cfg<2, KIND>::CS;
     case 3: return Cfg<3, KIND>::CS;
     case 4: return Cfg<4, KIND>::CS;
-    case 8: return Cfg<8, KIND>::CS;
     default: return Cfg<5, KIND>::CS;
-  }
-}
-template <int KIND>
-int blocks_t(int mt) {
-  switch (mt) {
-    case 8: return Cfg<8, KIND>::NB;
-    default: return 1;
   }
 }
 int waves_for(int mt, int kind) {
@@ -916,9 +902,6 @@ int waves_for(int mt, int kind) {
 }
 int chunk_for(int mt, int kind) {
   return kind == EPI_SWIGLU ? chunk_t<EPI_SWIGLU>(mt) : kind == KIND_HEAD ? chunk_t<KIND_HEAD>(mt) : chunk_t<EPI_PART>(mt);
-}
-int blocks_for(int mt, int kind) {
-  return kind == EPI_SWIGLU ? blocks_t<EPI_SWIGLU>(mt) : blocks_t<EPI_PART>(mt);
 }
 
 template <typename T, int MT, int EPI>
@@ -974,9 +957,6 @@ hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hip
       }
     }
   }
-  if constexpr (Opnd<T>::SPLIT && EPI == EPI_PART) {   // many-row q|k|v: bf16 only
-    if (mt == 8) return launch_proj_mt<T, 8, EPI_PART>(a, tiles, m_chunks, st, tm);
-  }
   switch (mt) {
     case 1: return launch_proj_mt<T, 1, EPI>(a, tiles, m_chunks, st, tm);
     case 2: return launch_proj_mt<T, 2, EPI>(a, tiles, m_chunks, st, tm);
@@ -1023,34 +1003,43 @@ int head_rows(int M) { return 16 * waves_for(M > 64 ? 5 : (M + 15) / 16, KIND_HE
 
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
   GemmPlan p;
-  if (dtype == 1 && epi == EPI_PART && M > 128) {
-    // rows_kernel: 256 weight rows per tile, m-chunks of 256 rows (wide
-    // outputs such as q|k|v) or 128 (more tiles for narrow ones); split K
-    // until the grid covers the CUs, keeping >= 16 steps per split (and at
-    // most four splits of the 256-row chunks: more measured slower)
+  if (dtype == 1 && epi == EPI_PART && (M > 128 || (M > 80 && (N_rows >= 8192 || K >= 8192)))) {
+    // rows_kernel (above 128 rows; from 81 rows for wide or deep shapes, the
+    // 4096 x 4096 one measured faster in 64-row passes there): 256 weight
+    // rows per tile; split K until the grid covers three quarters of the
+    // CUs, keeping >= 16 steps per split. m-chunks of 256 rows when that
+    // takes at most four splits (more measured slower), else of 128 rows
+    // (more m-chunks for narrow outputs)
     p.xg = 2;
     p.nb = 4;
     p.nw = 8;
-    p.mt = N_rows >= 8192 ? 8 : 4;
-    p.m_chunks = (M + 32 * p.mt - 1) / (32 * p.mt);
     p.n_tiles = (N_rows + 255) / 256;
     const int steps = K / 32;
-    int s = 1;
-    while (s < (p.mt == 8 ? 4 : 16) && p.n_tiles * p.m_chunks * s < 256 && steps / (2 * s) >= 16) s *= 2;
-    p.splits = s;
+    auto splits_for = [&](int m_chunks, int cap) {
+      int s = 1;
+      while (s < cap && p.n_tiles * m_chunks * s * 4 < 3 * 256 && steps / (2 * s) >= 16) s *= 2;
+      return s;
+    };
+    const int mc8 = (M + 255) / 256, s8 = splits_for(mc8, 4);
+    if (M > 128 && p.n_tiles * mc8 * s8 * 4 >= 3 * 256) {
+      p.mt = 8;
+      p.m_chunks = mc8;
+      p.splits = s8;
+    } else {
+      p.mt = 4;
+      p.m_chunks = (M + 127) / 128;
+      p.splits = splits_for(p.m_chunks, 16);
+    }
     return p;
   }
   if (M <= 80) {
     p.mt = (M + 15) / 16;
-  } else if (dtype == 1 && epi == EPI_PART && N_rows >= 8192) {
-    // wide projections (q|k|v) over 81-128 rows: one pass
-    p.mt = 8;
   } else {
     p.mt = 4;   // passes of 64 rows
   }
   p.m_chunks = (M + 16 * p.mt - 1) / (16 * p.mt);
   p.nw = waves_for(p.mt, epi);
-  p.nb = dtype == 1 ? blocks_for(p.mt, epi) : 1;
+  p.nb = 1;
   const int rows_per_tile = 16 * p.nw * p.nb;
   if (epi == EPI_SWIGLU) {
     const int F = N_rows / 2;

@@ -82,14 +82,15 @@ LINEAR = [  # (dtype, M, N, K): split-K, tails, several M tiles, prefill-sized M
     (BF16, 1, 4096, 4096), (BF16, 10, 4096, 8192), (BF16, 27, 12288, 4096),
     (BF16, 61, 4096, 11008), (BF16, 65, 1000, 1024), (BF16, 100, 256, 512),
     (BF16, 256, 512, 4096), (F32, 17, 256, 256), (F32, 17, 256, 688), (F32, 33, 1024, 512),
-    # many rows (a batch's verify rows, prefill chunks): 81-128 rows of a wide
-    # projection take one 128-row pass; above 128 rows the 256-row weight
-    # tiles with activations copied straight into LDS (256-row chunks for
-    # wide outputs, 128 for narrow ones): ragged N (a half block, a partial
-    # tile), a second and third row chunk with one row, a single split
+    # many rows (a batch's verify rows, prefill chunks): the 256-row weight
+    # tiles with activations copied straight into LDS, above 128 rows and
+    # from 81 rows for wide or deep shapes (128- or 256-row chunks): ragged N
+    # (a half block, a partial tile), a second and third row chunk with one
+    # row, a single split; 81-128 rows of a 4096 x 4096 shape stay on 64-row
+    # passes
     (BF16, 108, 12288, 4096), (BF16, 216, 8200, 1024), (BF16, 300, 8192, 512),
     (BF16, 130, 4096, 1024), (BF16, 257, 4104, 2048), (BF16, 129, 1000, 256),
-    (BF16, 512, 4096, 11008),
+    (BF16, 512, 4096, 11008), (BF16, 100, 4096, 11008), (BF16, 90, 4096, 4096),
 ]
 
 
