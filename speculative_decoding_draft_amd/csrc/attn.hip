@@ -340,6 +340,279 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
+// Causal attention over many rows with no tree keys (prefill chunks and the
+// draft catch-up over them), in flash form: one workgroup of four waves per
+// (KV head, block of 16 RB query rows) walks the key chunks from the visible
+// prefix start to its rows' last visible key. Each chunk's K and V^T (hi
+// and lo) are staged in LDS in attn_bf16_kernel's layout while the next
+// chunk's loads are in flight; every wave keeps the running max, sum and O
+// of its (query head, 16-row block) pairs in registers, with the same MFMA
+// products and log2-unit online softmax as attn_bf16_kernel, and writes the
+// normalized rows once: no per-chunk partials and no merge pass. A row sees
+// key k iff pre_lo <= k < prehi[row]. Workgroups are dispatched to the 8
+// XCDs round-robin by index, so the index is mapped to put every row block
+// of a KV head on one XCD: they walk the same keys at about the same time
+// and read them from that XCD's L2 instead of each from memory.
+struct FlashArgs {
+  const bf16_t* q; int64_t qlo;
+  KVView kv;
+  RowVis vis;
+  int M, nq, group;
+  int rb;       // 16-row blocks per workgroup
+  float scale;  // log2 units
+  bf16_t* out; int64_t olo;
+};
+
+template <int PW>   // (query head, row block) pairs per wave
+__global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
+  constexpr int D = 128, CK = CHUNK, VP = CK + 8;
+  __shared__ uint4 ks[2][CK][16];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];
+  __shared__ int kend_sh;
+  const RowVis& vis = a.vis;
+  const KVView& kv = a.kv;
+  int hk, rbi;
+  if ((kv.n_kv & 7) == 0) {
+    const int hpx = kv.n_kv >> 3, j = blockIdx.x >> 3;
+    hk = (blockIdx.x & 7) * hpx + j % hpx;
+    rbi = j / hpx;
+  } else {
+    hk = blockIdx.x % kv.n_kv;
+    rbi = blockIdx.x / kv.n_kv;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+  const int row_lo = rbi * 16 * a.rb;
+  const int nrows = min(16 * a.rb, a.M - row_lo);
+  // the block's last visible key: the largest prehi over its rows
+  if (tid < 64) {
+    int e = tid < nrows ? vis.prehi[row_lo + tid] : 0;
+    e = max(e, __shfl_xor(e, 1));
+    e = max(e, __shfl_xor(e, 2));
+    e = max(e, __shfl_xor(e, 4));
+    e = max(e, __shfl_xor(e, 8));
+    e = max(e, __shfl_xor(e, 16));
+    e = max(e, __shfl_xor(e, 32));
+    if (tid == 0) kend_sh = min(e, vis.key_end);
+  }
+  __syncthreads();
+  const int kend = kend_sh;
+  const int nch = kend > vis.pre_lo ? (kend - vis.pre_lo + CK - 1) / CK : 0;
+
+  // this wave's pairs: p = wave + 4 i, head j = p / rb, row block p % rb
+  const int npairs = a.group * a.rb;
+  uint4 qf[PW][4], ql[PW][4];
+  int prehi[PW], pmin[PW];
+  float m_run[PW], l_run[PW];
+  f32x4 o[PW][8];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int p = min(wave + 4 * i, npairs - 1);
+    const int h = hk * a.group + p / a.rb;
+    const int rowc = min(row_lo + 16 * (p % a.rb) + lr, a.M - 1);
+    const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[i][s] = ld16(qp + 32 * s);
+      ql[i][s] = ld16(qp + a.qlo + 32 * s);
+    }
+    prehi[i] = vis.prehi[rowc];
+    pmin[i] = wave_min_i(prehi[i]);
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int pgsz = kv.page, psh = page_shift(kv);
+  // Chunk c + 2's K/V loads are issued while chunk c is multiplied (two
+  // register buffers), and the page-table entries they need were read one
+  // step earlier, so no KV load waits on a table load.
+  struct Stage { uint4 kr[8], va[4], vb[4]; };
+  Stage st[2];
+  int2 pgn = make_int2(0, 0);   // page entries of the next chunk to load
+  auto pages = [&](int c) {
+    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+    return make_int2(kv.page_table[k0 >> psh], kv.page_table[(k1 - 1) >> psh]);
+  };
+  // loads of chunk c into registers (keys past the chunk's end repeat its
+  // last key; they are masked); a chunk spans at most two KV pages
+  auto load_chunk = [&](Stage& b, int c, int2 pg) {
+    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+    const int pA = k0 >> psh;
+    auto kvp = [&](int key, int plane) {
+      const int page = ((key >> psh) == pA) ? pg.x : pg.y;
+      return (const bf16_t*)kv.base + (int64_t)page * kv.page_elems +
+             ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
+    };
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int i = tid + 256 * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      b.kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + 256 * it;
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      b.va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
+      b.vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
+    }
+  };
+  auto store_chunk = [&](const Stage& b) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int i = tid + 256 * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      ks[plane][key][c16 ^ k_swz(key)] = b.kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + 256 * it;
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      const uint32_t wa[4] = {b.va[it].x, b.va[it].y, b.va[it].z, b.va[it].w};
+      const uint32_t wb[4] = {b.vb[it].x, b.vb[it].y, b.vb[it].z, b.vb[it].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
+      }
+    }
+  };
+  auto compute = [&](int c) {
+    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      if (wave + 4 * i >= npairs) continue;   // uniform over the wave
+#pragma unroll
+      for (int bi = 0; bi < CK / 32; ++bi) {
+        const int kb0 = bi * 32;
+        // the two 16-key halves accumulate in turn (two independent MFMA
+        // chains; each half's order is attn_bf16_kernel's)
+        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+          uint4 kf[2], kl[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
+            kf[hh] = ks[0][key][(4 * s + g) ^ k_swz(key)];
+            kl[hh] = ks[1][key][(4 * s + g) ^ k_swz(key)];
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], qf[i][s], sc[hh]);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], ql[i][s], sc[hh]);
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kl[hh], qf[i][s], sc[hh]);
+        }
+        float p[8];
+        float bm = -INFINITY;
+        if (k0 + kb0 + 32 <= min(pmin[i], k1)) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = sc[e >> 2][e & 3] * a.scale;
+            bm = fmaxf(bm, p[e]);
+          }
+        } else {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = k0 + kb0 + 8 * g + 4 * hh + e;
+              const bool ok = key < k1 && key < prehi[i];
+              p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
+              bm = fmaxf(bm, p[4 * hh + e]);
+            }
+        }
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float m_new = fmaxf(m_run[i], bm);
+        float alpha = 1.f, ps = 0.f;
+        if (m_new != -INFINITY) {
+          alpha = exp2f(m_run[i] - m_new);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = exp2f(p[e] - m_new);
+            ps += p[e];
+          }
+          m_run[i] = m_new;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = 0.f;
+        }
+        ps += __shfl_xor(ps, 16);
+        ps += __shfl_xor(ps, 32);
+        l_run[i] = l_run[i] * alpha + ps;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+          pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
+        }
+        const uint4 phi = uint4{ph[0], ph[1], ph[2], ph[3]};
+        const uint4 plo = uint4{pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+          const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
+          const uint4 v1 = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
+          Mma<bf16_t>::mma(v0, phi, o[i][dt]);
+          Mma<bf16_t>::mma(v0, plo, o[i][dt]);
+          Mma<bf16_t>::mma(v1, phi, o[i][dt]);
+        }
+      }
+    }
+  };
+
+  if (nch > 0) {
+    load_chunk(st[0], 0, pages(0));
+    if (nch > 1) load_chunk(st[1], 1, pages(1));
+    if (nch > 2) pgn = pages(2);
+    store_chunk(st[0]);
+  }
+  __syncthreads();
+  // step c: loads of chunk c + 2 into the buffer chunk c came from (already
+  // in LDS), the products of chunk c, then chunk c + 1 from the other buffer
+  // into LDS
+  for (int c0 = 0; c0 < nch; c0 += 2) {
+#define FLASH_STEP(J)                                                       \
+    {                                                                       \
+      const int c = c0 + J;                                                 \
+      if (c < nch) {                                                        \
+        if (c + 2 < nch) {                                                  \
+          load_chunk(st[J], c + 2, pgn);                                    \
+          if (c + 3 < nch) pgn = pages(c + 3);                              \
+        }                                                                   \
+        compute(c);                                                         \
+        __syncthreads();                                                    \
+        if (c + 1 < nch) {                                                  \
+          store_chunk(st[1 - J]);                                           \
+          __syncthreads();                                                  \
+        }                                                                   \
+      }                                                                     \
+    }
+    FLASH_STEP(0) FLASH_STEP(1)
+#undef FLASH_STEP
+  }
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int p = wave + 4 * i;
+    if (p >= npairs) continue;
+    const int h = hk * a.group + p / a.rb;
+    const int row = row_lo + 16 * (p % a.rb) + lr;
+    if (row >= a.M) continue;
+    const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        Opnd<bf16_t>::store(a.out, a.olo, ((int64_t)row * a.nq + h) * D + 16 * dt + 4 * g + e,
+                            o[i][dt][e] * inv);
+  }
+}
+
 constexpr int ATTN_MAX_CHUNKS = 2048;
 
 // Merges the per-chunk (max, sum, O) partials of one (row, head): the chunk
@@ -843,6 +1116,19 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
   if (dtype == 1) {
     if (d != 128) return hipErrorInvalidValue;
     if (n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK) return hipErrorInvalidValue;
+    if (vis.n_tree == 0 && ln.n == 1 && M >= 32 && group <= 8) {
+      // causal rows without tree keys (prefill chunks): flash form, 16 rb
+      // rows per workgroup, at least four (head, row block) pairs
+      const int rb = group >= 4 ? 1 : 4 / group;
+      FlashArgs f{(const bf16_t*)q, qlo, kv, vis, M, nq, group, rb, scale * 1.4426950408889634f,
+                  (bf16_t*)out_t, olo};
+      const dim3 grid((M + 16 * rb - 1) / (16 * rb) * kv.n_kv);
+      if (group * rb > 4)
+        hipLaunchKernelGGL(attn_flash_kernel<2>, grid, dim3(256), 0, st, f);
+      else
+        hipLaunchKernelGGL(attn_flash_kernel<1>, grid, dim3(256), 0, st, f);
+      return hipGetLastError();
+    }
     // scores are taken in log2 units (scale * log2 e) so the softmax uses the
     // native exp2; chunk maxima in mlpart are in the same units
     // split a head's pairs over more workgroups only while the (chunk, KV
