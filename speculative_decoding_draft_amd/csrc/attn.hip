@@ -74,6 +74,29 @@ __device__ __forceinline__ KVView lane_kv(const KVView& v, int lane) {
   return r;
 }
 
+// Max and sum of a value with the lane 16 or 32 away (the score rows of one
+// MFMA tile are spread over the four 16-lane rows of the wave). gfx950's
+// permlane swaps exchange whole 16-lane rows in registers, where __shfl_xor
+// makes a round trip through the LDS crossbar; each lane ends with its own
+// value and its partner's, in some order, and max / + are commutative, so
+// the results equal the shuffle versions bit for bit.
+__device__ __forceinline__ float xrow16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xrow16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xrow32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 struct AttnArgs {
   const bf16_t* q; int64_t qlo;
   KVView kv;
@@ -233,8 +256,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
             bm = fmaxf(bm, p[4 * hh + e]);
           }
       }
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      bm = xrow16_max(bm);
+      bm = xrow32_max(bm);
       const float m_new = fmaxf(m_run, bm);
       float alpha = 1.f, ps = 0.f;
       if (m_new != -INFINITY) {
@@ -249,8 +272,8 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) p[i] = 0.f;
       }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps = xrow16_sum(ps);
+      ps = xrow32_sum(ps);
       l_run = l_run * alpha + ps;
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] *= alpha;
@@ -341,14 +364,15 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Causal attention over many rows with no tree keys (prefill chunks and the
-// draft catch-up over them), in flash form: one workgroup of four waves per
+// draft catch-up over them), in flash form: one workgroup per
 // (KV head, block of 16 RB query rows) walks the key chunks from the visible
 // prefix start to its rows' last visible key. Each chunk's K and V^T (hi
 // and lo) are staged in LDS in attn_bf16_kernel's layout while the next
 // chunk's loads are in flight; every wave keeps the running max, sum and O
-// of its (query head, 16-row block) pairs in registers, with the same MFMA
-// products and log2-unit online softmax as attn_bf16_kernel, and writes the
-// normalized rows once: no per-chunk partials and no merge pass. A row sees
+// of its (query head, 16-row block) pairs over its half of each chunk's keys
+// in registers, with the same MFMA products and log2-unit online softmax as
+// attn_bf16_kernel; the two halves merge in LDS and the normalized rows are
+// written once: no per-chunk partials in memory and no merge kernel. A row sees
 // key k iff pre_lo <= k < prehi[row]. Workgroups are dispatched to the 8
 // XCDs round-robin by index, so the index is mapped to put every row block
 // of a KV head on one XCD: they walk the same keys at about the same time
@@ -364,8 +388,11 @@ struct FlashArgs {
 };
 
 template <int PW>   // (query head, row block) pairs per wave
-__global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
-  constexpr int D = 128, CK = CHUNK, VP = CK + 8;
+__global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
+  // Eight waves: wave w takes pair slot w % 4 and the key half w / 4 of every
+  // chunk (32 of its 64 keys), so two waves share each SIMD; the halves keep
+  // their own running (max, sum, O) and are merged through LDS at the end.
+  constexpr int D = 128, CK = CHUNK, VP = CK + 8, NT = 512;
   __shared__ uint4 ks[2][CK][16];
   __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];
   __shared__ int kend_sh;
@@ -381,6 +408,7 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
     rbi = blockIdx.x / kv.n_kv;
   }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = wave & 3, kh = wave >> 2;
   const int lr = lane & 15, g = lane >> 4;
   const int row_lo = rbi * 16 * a.rb;
   const int nrows = min(16 * a.rb, a.M - row_lo);
@@ -399,7 +427,7 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
   const int kend = kend_sh;
   const int nch = kend > vis.pre_lo ? (kend - vis.pre_lo + CK - 1) / CK : 0;
 
-  // this wave's pairs: p = wave + 4 i, head j = p / rb, row block p % rb
+  // this wave's pairs: p = slot + 4 i, head j = p / rb, row block p % rb
   const int npairs = a.group * a.rb;
   uint4 qf[PW][4], ql[PW][4];
   int prehi[PW], pmin[PW];
@@ -407,7 +435,7 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
   f32x4 o[PW][8];
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const int p = min(wave + 4 * i, npairs - 1);
+    const int p = min(slot + 4 * i, npairs - 1);
     const int h = hk * a.group + p / a.rb;
     const int rowc = min(row_lo + 16 * (p % a.rb) + lr, a.M - 1);
     const bf16_t* qp = a.q + ((int64_t)rowc * a.nq + h) * D + 8 * g;
@@ -425,53 +453,45 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
   }
 
   const int pgsz = kv.page, psh = page_shift(kv);
-  // Chunk c + 2's K/V loads are issued while chunk c is multiplied (two
-  // register buffers), and the page-table entries they need were read one
-  // step earlier, so no KV load waits on a table load.
-  struct Stage { uint4 kr[8], va[4], vb[4]; };
-  Stage st[2];
-  int2 pgn = make_int2(0, 0);   // page entries of the next chunk to load
-  auto pages = [&](int c) {
-    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
-    return make_int2(kv.page_table[k0 >> psh], kv.page_table[(k1 - 1) >> psh]);
-  };
+  uint4 kr[4], va[2], vb[2];
   // loads of chunk c into registers (keys past the chunk's end repeat its
   // last key; they are masked); a chunk spans at most two KV pages
-  auto load_chunk = [&](Stage& b, int c, int2 pg) {
+  auto load_chunk = [&](int c) {
     const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
     const int pA = k0 >> psh;
+    const int pgA = kv.page_table[pA], pgB = kv.page_table[(k1 - 1) >> psh];
     auto kvp = [&](int key, int plane) {
-      const int page = ((key >> psh) == pA) ? pg.x : pg.y;
-      return (const bf16_t*)kv.base + (int64_t)page * kv.page_elems +
+      const int pg = ((key >> psh) == pA) ? pgA : pgB;
+      return (const bf16_t*)kv.base + (int64_t)pg * kv.page_elems +
              ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
     };
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int i = tid + 256 * it;
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NT * it;
       const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
-      b.kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
+      kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
     }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = tid + 256 * it;
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + NT * it;
       const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
-      b.va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
-      b.vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
+      va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
+      vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
     }
   };
-  auto store_chunk = [&](const Stage& b) {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int i = tid + 256 * it;
-      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
-      ks[plane][key][c16 ^ k_swz(key)] = b.kr[it];
-    }
+  auto store_chunk = [&]() {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int i = tid + 256 * it;
+      const int i = tid + NT * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      ks[plane][key][c16 ^ k_swz(key)] = kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + NT * it;
       const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
-      const uint32_t wa[4] = {b.va[it].x, b.va[it].y, b.va[it].z, b.va[it].w};
-      const uint32_t wb[4] = {b.vb[it].x, b.vb[it].y, b.vb[it].z, b.vb[it].w};
+      const uint32_t wa[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
+      const uint32_t wb[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
         *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
@@ -479,137 +499,142 @@ __global__ __launch_bounds__(256) void attn_flash_kernel(FlashArgs a) {
       }
     }
   };
-  auto compute = [&](int c) {
-    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
-#pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      if (wave + 4 * i >= npairs) continue;   // uniform over the wave
-#pragma unroll
-      for (int bi = 0; bi < CK / 32; ++bi) {
-        const int kb0 = bi * 32;
-        // the two 16-key halves accumulate in turn (two independent MFMA
-        // chains; each half's order is attn_bf16_kernel's)
-        f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
-          uint4 kf[2], kl[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
-            kf[hh] = ks[0][key][(4 * s + g) ^ k_swz(key)];
-            kl[hh] = ks[1][key][(4 * s + g) ^ k_swz(key)];
-          }
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], qf[i][s], sc[hh]);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], ql[i][s], sc[hh]);
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kl[hh], qf[i][s], sc[hh]);
-        }
-        float p[8];
-        float bm = -INFINITY;
-        if (k0 + kb0 + 32 <= min(pmin[i], k1)) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = sc[e >> 2][e & 3] * a.scale;
-            bm = fmaxf(bm, p[e]);
-          }
-        } else {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int key = k0 + kb0 + 8 * g + 4 * hh + e;
-              const bool ok = key < k1 && key < prehi[i];
-              p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
-              bm = fmaxf(bm, p[4 * hh + e]);
-            }
-        }
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float m_new = fmaxf(m_run[i], bm);
-        float alpha = 1.f, ps = 0.f;
-        if (m_new != -INFINITY) {
-          alpha = exp2f(m_run[i] - m_new);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = exp2f(p[e] - m_new);
-            ps += p[e];
-          }
-          m_run[i] = m_new;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = 0.f;
-        }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        l_run[i] = l_run[i] * alpha + ps;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
-        uint32_t ph[4], pl[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
-          pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
-        }
-        const uint4 phi = uint4{ph[0], ph[1], ph[2], ph[3]};
-        const uint4 plo = uint4{pl[0], pl[1], pl[2], pl[3]};
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
-          const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
-          const uint4 v1 = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
-          Mma<bf16_t>::mma(v0, phi, o[i][dt]);
-          Mma<bf16_t>::mma(v0, plo, o[i][dt]);
-          Mma<bf16_t>::mma(v1, phi, o[i][dt]);
-        }
-      }
-    }
-  };
 
   if (nch > 0) {
-    load_chunk(st[0], 0, pages(0));
-    if (nch > 1) load_chunk(st[1], 1, pages(1));
-    if (nch > 2) pgn = pages(2);
-    store_chunk(st[0]);
+    load_chunk(0);
+    store_chunk();
   }
   __syncthreads();
-  // step c: loads of chunk c + 2 into the buffer chunk c came from (already
-  // in LDS), the products of chunk c, then chunk c + 1 from the other buffer
-  // into LDS
-  for (int c0 = 0; c0 < nch; c0 += 2) {
-#define FLASH_STEP(J)                                                       \
-    {                                                                       \
-      const int c = c0 + J;                                                 \
-      if (c < nch) {                                                        \
-        if (c + 2 < nch) {                                                  \
-          load_chunk(st[J], c + 2, pgn);                                    \
-          if (c + 3 < nch) pgn = pages(c + 3);                              \
-        }                                                                   \
-        compute(c);                                                         \
-        __syncthreads();                                                    \
-        if (c + 1 < nch) {                                                  \
-          store_chunk(st[1 - J]);                                           \
-          __syncthreads();                                                  \
-        }                                                                   \
-      }                                                                     \
+  const int kb0 = 32 * kh;   // this wave's 32 keys of every chunk
+  for (int c = 0; c < nch; ++c) {
+    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+    if (c + 1 < nch) load_chunk(c + 1);
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      if (slot + 4 * i >= npairs) continue;   // uniform over the wave
+      // the two 16-key halves accumulate in turn (two independent MFMA
+      // chains; each half's order is attn_bf16_kernel's)
+      f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+        uint4 kf[2], kl[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
+          kf[hh] = ks[0][key][(4 * s + g) ^ k_swz(key)];
+          kl[hh] = ks[1][key][(4 * s + g) ^ k_swz(key)];
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], qf[i][s], sc[hh]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], ql[i][s], sc[hh]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kl[hh], qf[i][s], sc[hh]);
+      }
+      float p[8];
+      float bm = -INFINITY;
+      if (k0 + kb0 + 32 <= min(pmin[i], k1)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = sc[e >> 2][e & 3] * a.scale;
+          bm = fmaxf(bm, p[e]);
+        }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = k0 + kb0 + 8 * g + 4 * hh + e;
+            const bool ok = key < k1 && key < prehi[i];
+            p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
+            bm = fmaxf(bm, p[4 * hh + e]);
+          }
+      }
+      bm = xrow16_max(bm);
+      bm = xrow32_max(bm);
+      const float m_new = fmaxf(m_run[i], bm);
+      float alpha = 1.f, ps = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_run[i] - m_new);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2f(p[e] - m_new);
+          ps += p[e];
+        }
+        m_run[i] = m_new;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = 0.f;
+      }
+      ps = xrow16_sum(ps);
+      ps = xrow32_sum(ps);
+      l_run[i] = l_run[i] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
+      }
+      const uint4 phi = uint4{ph[0], ph[1], ph[2], ph[3]};
+      const uint4 plo = uint4{pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+        const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
+        Mma<bf16_t>::mma(v0, phi, o[i][dt]);
+        Mma<bf16_t>::mma(v0, plo, o[i][dt]);
+        Mma<bf16_t>::mma(v1, phi, o[i][dt]);
+      }
     }
-    FLASH_STEP(0) FLASH_STEP(1)
-#undef FLASH_STEP
+    __syncthreads();   // every wave is done with this chunk's LDS
+    if (c + 1 < nch) {
+      store_chunk();
+      __syncthreads();
+    }
   }
+  // merge the two key halves of each pair (the K area holds the second
+  // half's O, the V area its max and sum), then write the normalized rows
+  float* mo = reinterpret_cast<float*>(&ks[0][0][0]);   // [slot][16 rows][128]
+  float* mm = reinterpret_cast<float*>(&vt[0][0][0]);   // [slot][16 rows][2]
+  static_assert(4 * 16 * D * 4 <= (int)sizeof(ks), "merge buffer must fit");
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
-    const int p = wave + 4 * i;
-    if (p >= npairs) continue;
-    const int h = hk * a.group + p / a.rb;
-    const int row = row_lo + 16 * (p % a.rb) + lr;
-    if (row >= a.M) continue;
-    const float inv = l_run[i] > 0.f ? 1.f / l_run[i] : 0.f;
+    const int p = slot + 4 * i;
+    const bool has = p < npairs;   // uniform over the wave
+    if (kh == 1 && has) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        Opnd<bf16_t>::store(a.out, a.olo, ((int64_t)row * a.nq + h) * D + 16 * dt + 4 * g + e,
-                            o[i][dt][e] * inv);
+        for (int e = 0; e < 4; ++e) mo[(slot * 16 + lr) * D + 16 * dt + 4 * g + e] = o[i][dt][e];
+      if (g == 0) {
+        mm[(slot * 16 + lr) * 2] = m_run[i];
+        mm[(slot * 16 + lr) * 2 + 1] = l_run[i];
+      }
+    }
+    __syncthreads();
+    if (kh == 0 && has) {
+      const int h = hk * a.group + p / a.rb;
+      const int row = row_lo + 16 * (p % a.rb) + lr;
+      const float m1 = mm[(slot * 16 + lr) * 2], l1 = mm[(slot * 16 + lr) * 2 + 1];
+      const float mx = fmaxf(m_run[i], m1);
+      const float w0 = m_run[i] == -INFINITY ? 0.f : exp2f(m_run[i] - mx);
+      const float w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - mx);
+      const float l = w0 * l_run[i] + w1 * l1;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      if (row < a.M) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int dd = 16 * dt + 4 * g + e;
+            const float v = (w0 * o[i][dt][e] + w1 * mo[(slot * 16 + lr) * D + dd]) * inv;
+            Opnd<bf16_t>::store(a.out, a.olo, ((int64_t)row * a.nq + h) * D + dd, v);
+          }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -1124,9 +1149,9 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
                   (bf16_t*)out_t, olo};
       const dim3 grid((M + 16 * rb - 1) / (16 * rb) * kv.n_kv);
       if (group * rb > 4)
-        hipLaunchKernelGGL(attn_flash_kernel<2>, grid, dim3(256), 0, st, f);
+        hipLaunchKernelGGL(attn_flash_kernel<2>, grid, dim3(512), 0, st, f);
       else
-        hipLaunchKernelGGL(attn_flash_kernel<1>, grid, dim3(256), 0, st, f);
+        hipLaunchKernelGGL(attn_flash_kernel<1>, grid, dim3(512), 0, st, f);
       return hipGetLastError();
     }
     // scores are taken in log2 units (scale * log2 e) so the softmax uses the
