@@ -182,7 +182,7 @@ def main():
         print(json.dumps({"copy_bytes": n, "copies": 3}))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is design-only)"}))
         sys.exit(2)
 
