@@ -242,6 +242,12 @@ uint64_t gemm_ws_floats(const Derived& z) {
       GemmPlan p = gemm_plan(M, s.rows, s.K, z.dt, EPI_PART);
       mx = std::max(mx, gemm_part_floats(p, s.rows, M));
     }
+  // SwiGLU over many rows: the gate|up partial planes (2F wide)
+  for (int M = 1; M <= z.Mmax; ++M)
+    if (swiglu_by_planes(z.dt, M)) {
+      GemmPlan p = gemm_plan(M, 2 * z.F, z.H, z.dt, EPI_PART);
+      mx = std::max(mx, gemm_part_floats(p, 2 * z.F, M));
+    }
   return mx;
 }
 
@@ -648,8 +654,8 @@ eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, fl
                        nullptr, 0, &S, c->st, tm_));
   SCHK(resnorm(c, h, M, S, false, w.ffn_norm, nullptr));
   PROFILED_KERNEL(cls_glu, gemm_bytes(z, M, 2 * z.F, z.H, z.F, EPI_SWIGLU),
-           launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, c->xlo, M, z.F, z.H, nullptr, 0, c->fop,
-                       c->flo, nullptr, c->st, tm_));
+           launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, c->xlo, M, z.F, z.H, c->gpart, 2 * z.F,
+                       c->fop, c->flo, nullptr, c->st, tm_));
   PROFILED_KERNEL(cls_part, gemm_bytes(z, M, z.H, z.F, z.H, EPI_PART),
            launch_gemm(dt, EPI_PART, w.wdown, c->fop, c->flo, M, z.H, z.F, c->gpart, z.H, nullptr,
                        0, s_down, c->st, tm_));

@@ -571,6 +571,29 @@ __global__ __launch_bounds__(WC * XG * 64) void rows_kernel(ProjArgs a) {
   }
 }
 
+// SwiGLU over many rows, second half: the gate|up projection left S partial
+// planes [S][M][2F] (gate columns, then up); this pass sums each column's
+// planes in plane order and writes SiLU(g) * u as the next operand (bf16 hi
+// and lo planes). Four consecutive columns per thread, 16-byte loads.
+__global__ __launch_bounds__(256) void silu_mul_planes_kernel(const float* __restrict__ part, int S,
+                                                              int64_t plane, int M, int F,
+                                                              bf16_t* __restrict__ out, int64_t lo) {
+  const int m = blockIdx.y;
+  const int j = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (j >= F) return;
+  const float* pr = part + (int64_t)m * 2 * F;
+  float4 g = ld4(pr + j), u = ld4(pr + F + j);
+  for (int s = 1; s < S; ++s) {
+    const float4 a = ld4(pr + s * plane + j), b = ld4(pr + s * plane + F + j);
+    g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+    u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+  }
+  const float v[4] = {g.x / (1.0f + expf(-g.x)) * u.x, g.y / (1.0f + expf(-g.y)) * u.y,
+                      g.z / (1.0f + expf(-g.z)) * u.z, g.w / (1.0f + expf(-g.w)) * u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Opnd<bf16_t>::store(out, lo, (int64_t)m * F + j + e, v[e]);
+}
+
 // ---------------------------------------------------------------- packing
 // Fragment packing of a bf16 matrix [rows, K] (K a multiple of 32): full
 // 16-row block rb is stored as K/32 fragments of 1 KB, fragment s holding
@@ -1083,10 +1106,28 @@ uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M) {
   return (uint64_t)p.splits * M * N_rows;
 }
 
+bool swiglu_by_planes(int dtype, int M) { return dtype == 1 && M > 128; }
+
 hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
                        int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int splits_out[1],
                        hipStream_t stream, const KTiming* tm) {
   if (M <= 0) return hipSuccess;
+  if (epi == EPI_SWIGLU && swiglu_by_planes(dtype, M)) {
+    // many rows: gate|up as one split-K projection (rows_kernel) into the
+    // caller's partial-plane scratch Y, then SiLU(g) * u into Yt. Measured
+    // against 64-row passes of the fused kernel: -17..-24% at 256-512 rows
+    // on the 7B and 8B FFN shapes.
+    if (!Y || (N & 3)) return hipErrorInvalidValue;
+    int S = 1;
+    hipError_t e = launch_gemm(dtype, EPI_PART, W, x, xlo, M, 2 * N, K, Y, 2 * N, nullptr, 0, &S,
+                               stream, tm);
+    if (e != hipSuccess) return e;
+    const dim3 grid((N / 4 + 255) / 256, M);
+    hipLaunchKernelGGL(silu_mul_planes_kernel, grid, dim3(256), 0, stream, Y, S, (int64_t)M * 2 * N, M,
+                       N, (bf16_t*)Yt, ytlo);
+    if (splits_out) splits_out[0] = S;
+    return hipGetLastError();
+  }
   const int rows = (epi == EPI_SWIGLU) ? 2 * N : N;
   GemmPlan p = gemm_plan(M, rows, K, dtype, epi);
   ProjArgs a;

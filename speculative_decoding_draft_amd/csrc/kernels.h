@@ -16,6 +16,9 @@ enum { EPI_PART = 0, EPI_SWIGLU = 2 };
 struct GemmPlan { int mt, nb, splits, m_chunks, n_tiles, nw, xg = 1; };
 GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi);
 uint64_t gemm_part_floats(const GemmPlan& p, int N_rows, int M);
+// SwiGLU projections of M rows that run as a split-K gate|up projection plus
+// a SiLU pass: they need split * M * 2F floats of partial-plane scratch in Y.
+bool swiglu_by_planes(int dtype, int M);
 // Optional device timestamps of one kernel dispatch: the events ride on the
 // dispatch itself (hipExtLaunchKernel), so they time that kernel alone.
 struct KTiming {

@@ -39,7 +39,11 @@ eagle_status eagle_op_pack(const void* src, void* dst, int32_t N, int32_t K, voi
 
 uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epi, int32_t M, int32_t N, int32_t K) {
   if (!linear_ok(dtype, epi, M, N, K)) return 0;
-  if (epi == EAGLE_EPI_SWIGLU) return 0;
+  if (epi == EAGLE_EPI_SWIGLU) {
+    if (!swiglu_by_planes(dtype, M)) return 0;
+    GemmPlan p = gemm_plan(M, 2 * N, K, dtype, EPI_PART);
+    return align256(gemm_part_floats(p, 2 * N, M) * 4);
+  }
   GemmPlan p = gemm_plan(M, N, K, dtype, EPI_PART);
   return align256(gemm_part_floats(p, N, M) * 4);
 }
@@ -53,8 +57,8 @@ eagle_status eagle_op_linear(int32_t dtype, int32_t epi, const void* x, const vo
   const int64_t xlo = (int64_t)M * K;   // bf16: lo plane follows the hi plane
   hipStream_t st = (hipStream_t)stream;
   if (epi == EAGLE_EPI_SWIGLU) {
-    hipError_t e = launch_gemm(dtype, EPI_SWIGLU, w, x, xlo, M, N, K, nullptr, 0, y, (int64_t)M * N,
-                               nullptr, st);
+    hipError_t e = launch_gemm(dtype, EPI_SWIGLU, w, x, xlo, M, N, K, (float*)workspace, 2 * N, y,
+                               (int64_t)M * N, nullptr, st);
     return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
   }
   float* part = (float*)workspace;
