@@ -1047,7 +1047,10 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
     if (M > 128 && p.n_tiles * mc8 * s8 * 4 >= 3 * 256) {
       p.mt = 8;
       p.m_chunks = mc8;
-      p.splits = s8;
+      // several 256-row chunks whose unsplit grid already covers most CUs
+      // (the gate|up shapes at 512 rows) run unsplit: measured 3-10% faster,
+      // and the consumer sums one plane
+      p.splits = mc8 >= 2 && p.n_tiles * mc8 >= 160 ? 1 : s8;
     } else {
       p.mt = 4;
       p.m_chunks = (M + 127) / 128;
