@@ -34,5 +34,7 @@ Modules:
   speedup   the lesson's expected-tokens / speedup formula
 
 Parity status: every function is pinned by a test in ``tests/`` except where
-its docstring says "parity unpinned".
+its docstring says "parity unpinned": the draft heads' wiring
+(``model.Draft``, the E1 concat/FC and the E3 2H-input layer), which is held
+only to internal consistency (tree rows equal chains, the lossless loop).
 """

@@ -21,6 +21,15 @@ g = FC([l; m; h]) (3H -> H) from three target layers; tree rows use the
 parent row's own output a in place of g. The decoder layer reads [E[t]; s]
 (2H wide input norm and QKV) with residual stream starting at s; its output
 is a, and logits = a W_lm^T.
+
+Parity unpinned: the draft heads' wiring. The pages give the data flow but
+not every detail ([E3] lists only "FC 12288->4096, 1 decoder layer" for
+EAGLE-3; the concat order and whether the FC output passes through the
+layer's input norm are not stated). The readings taken here (concat
+[E[t]; s]; E1 FC 2H->H feeding a full Llama layer; E3 with a 2H-wide input
+norm and QKV and the residual stream starting at s) are checked only for
+internal consistency: tree drafting equals chain drafting along each path,
+and the lossless loop. No printed value exists to pin them to.
 """
 from __future__ import annotations
 
@@ -215,7 +224,10 @@ class Target:
 
 
 class Draft:
-    """EAGLE-1 or EAGLE-3 draft head sharing the target's embedding and LM head."""
+    """EAGLE-1 or EAGLE-3 draft head sharing the target's embedding and LM head.
+
+    Parity unpinned (the wiring; see the module docstring): its tree rows
+    are pinned to chain drafting, not to values printed on the pages."""
 
     def __init__(self, cfg: Config, W: Weights):
         self.cfg, self.W = cfg, W

@@ -246,3 +246,90 @@ def test_accept_walk_closed_form():
         L = max(l for l in range(len(cont)) if tuple(cont[:l]) in seqs)
         assert L == len(path)
         assert bonus == cont[len(path)]
+
+
+# ------------------------------------------------------------------ static tree (reading 15)
+def test_grow_static_hand_example():
+    """EAGLE-1's fixed tree ([L13] "EAGLE-2 and dynamic draft trees": the
+    static shape EAGLE-2 replaces) grown by a toy drafter whose child tokens
+    encode the parent's token (child = 10 * parent + rank + 1), with
+    confidences that differ per expanded node. Expected nodes, parents and
+    path values are worked out by hand below, so a swapped parent, a wrong
+    rank index or a mis-ordered expansion fails."""
+    paths = [(0,), (1,), (2,), (0, 0), (0, 2), (1, 1), (0, 0, 1)]
+    probs = {1: [0.7, 0.2, 0.05, 0.05], 2: [0.4, 0.35, 0.2, 0.05],
+             11: [0.9, 0.05, 0.03, 0.02]}
+    t = T.Tree()
+
+    def expand(chosen):
+        ids, lps = [], []
+        for e in chosen:
+            tok = t.nodes[e].token
+            ids.append([10 * tok + r + 1 for r in range(4)])
+            lps.append([np.float32(np.log(p)) for p in probs[tok]])
+        return ids, lps
+
+    root_p = [0.5, 0.3, 0.15, 0.05]
+    T.grow_static([1, 2, 3, 4], [np.float32(np.log(p)) for p in root_p], expand, paths, t)
+    # node order follows the list; parents are node indices
+    assert [n.token for n in t.nodes] == [1, 2, 3, 11, 13, 22, 112]
+    assert [n.parent for n in t.nodes] == [-1, -1, -1, 0, 0, 1, 3]
+    assert [n.depth for n in t.nodes] == [1, 1, 1, 2, 2, 2, 3]
+    assert [n.rank for n in t.nodes] == [0, 1, 2, 0, 2, 1, 1]
+    # expanded per pass: depth 1 nodes with listed children (in list order), then (0, 0)
+    assert t.expanded == [[0, 1], [3]]
+    # path values: products of the confidences on the path
+    want = [0.5, 0.3, 0.15, 0.5 * 0.7, 0.5 * 0.05, 0.3 * 0.35, 0.5 * 0.7 * 0.05]
+    assert np.allclose([np.exp(np.float64(n.logv)) for n in t.nodes], want, rtol=1e-6)
+    # every node is kept; verify rows are breadth first in list order
+    rows = T.flatten(t.nodes, list(range(len(t.nodes))), 0)
+    assert rows["token"] == [0, 1, 2, 3, 11, 13, 22, 112]
+    assert rows["parent"] == [-1, 0, 0, 0, 1, 1, 2, 4]
+
+
+def test_grow_static_c2_under_its_prior():
+    """The c2 static list grown by a drafter that always returns the prior
+    (0.6, 0.2, 0.1, 0.05) over child ranks: every node's log path value is
+    the sum of log q over its rank path, the passes expand 4, 5, 4, 2 rows,
+    and every expanded row is the parent of at least one listed node."""
+    import synth
+    q = [0.6, 0.2, 0.1, 0.05]
+    lq = [np.float32(np.log(p)) for p in q]
+    t = T.Tree()
+
+    def expand(chosen):
+        return [[10 * (e + 1) + r for r in range(4)] for e in chosen], [lq] * len(chosen)
+
+    paths = [tuple(p) for p in synth.STATIC_TREE_C2]
+    T.grow_static(list(range(4)), lq, expand, paths, t)
+    assert len(t.nodes) == 26
+    assert [len(x) for x in t.expanded] == [4, 5, 4, 2]
+    for i, p in enumerate(paths):
+        n = t.nodes[i]
+        assert _path(t.nodes, i) == p
+        assert n.depth == len(p)
+        assert float(n.logv) == pytest.approx(float(np.sum(np.log(np.array(q)[list(p)]))), abs=1e-5)
+        if n.parent >= 0:   # child token names its parent node and rank
+            assert n.token == 10 * (n.parent + 1) + p[-1]
+    for d, exp in enumerate(t.expanded, start=2):
+        assert all(t.nodes[e].depth == d - 1 for e in exp)
+        assert all(any(n.parent == e for n in t.nodes) for e in exp)
+
+
+# ------------------------------------------------------------------ P1 (distribution form)
+@pytest.mark.parametrize("alpha", [0.0, 0.25, 0.6, 0.8, 1.0])
+@pytest.mark.parametrize("k", [0, 1, 3, 5])
+def test_accepted_length_distribution_by_enumeration(alpha, k):
+    """The speedup oracle's distribution of accepted lengths against an
+    enumeration of every accept/reject outcome of k independent drafts (the
+    step stops at the first rejection)."""
+    pmf = speedup.accepted_length_pmf(alpha, k)
+    assert sum(pmf) == pytest.approx(1.0)
+    want = [0.0] * (k + 1)
+    for outcome in itertools.product([True, False], repeat=k):
+        p = 1.0
+        for ok in outcome:
+            p *= alpha if ok else 1.0 - alpha
+        L = next((i for i, ok in enumerate(outcome) if not ok), k)
+        want[L] += p
+    assert pmf == pytest.approx(want)
