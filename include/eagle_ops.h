@@ -35,9 +35,10 @@ enum { EAGLE_EPI_STORE = 0, EAGLE_EPI_ADD = 1, EAGLE_EPI_SWIGLU = 2 };
  * overlapping buffers, EAGLE_E_HIP on a launch failure. */
 eagle_status eagle_op_pack(const void* src, void* dst, int32_t N, int32_t K, void* stream);
 
-/* Workspace bytes eagle_op_linear needs for this shape (may be 0). The
- * workspace must be zero-filled before its first use; calls leave its
- * counters at zero, so it can be reused without clearing. */
+/* Workspace bytes eagle_op_linear needs for this shape (0 for a bad shape,
+ * or when the shape needs none). The workspace holds the split-K partial
+ * planes of one call; every byte a call reads there it has written first,
+ * so it needs no clearing and carries nothing between calls. */
 uint64_t eagle_op_linear_workspace(int32_t dtype, int32_t epilogue, int32_t M, int32_t N, int32_t K);
 
 /* Projection of M activation rows by a weight W, as in a Linear layer
@@ -73,6 +74,50 @@ uint64_t eagle_op_lmhead_workspace(int32_t M, int32_t V, int32_t k);
 eagle_status eagle_op_lmhead(int32_t dtype, int32_t k, const void* x, const void* w_lm, int32_t M,
                              int32_t V, int32_t H, int32_t* out_ids, float* out_vals, float* logits,
                              void* workspace, uint64_t ws_bytes, void* stream);
+
+/* Keys per page of the paged KV layout eagle_op_attention reads. */
+#define EAGLE_OP_KV_PAGE 64
+
+/* Workspace bytes of eagle_op_attention (per-chunk partial outputs and
+ * softmax statistics of the split-KV form; 0 for EAGLE_F32). */
+uint64_t eagle_op_attention_workspace(int32_t dtype, int32_t M, int32_t n_heads, int32_t head_dim,
+                                      int32_t key_end);
+
+/* Tree-masked attention of M query rows over one layer's paged KV cache: the
+ * verify pass's attention ("EAGLE-2: Context-Aware Dynamic Draft Trees",
+ * section "The Mask Preserves Tree Semantics in One Target Pass": each
+ * flattened row sees the context, its ancestors and itself), and the causal
+ * attention of prefill rows when there are no tree keys.
+ *   q: [M, n_heads * head_dim] query operand after RoPE (bf16: hi plane then
+ *      lo plane, see above; fp32: one array).
+ *   kv: the cache; key slot s of KV head h, plane p, element i lives at
+ *      page_table[s / 64] * (planes * n_kv_heads * 64 * head_dim)
+ *        + ((p * n_kv_heads + h) * 64 + s % 64) * head_dim + i
+ *      with planes K_hi, K_lo, V_hi, V_lo (bf16 raw bits; value = hi + lo) or
+ *      K, V (fp32). page_table: device int32 [key_end / 64 rounded up].
+ *   Row r sees key slots [pre_lo, prehi[r]) and the tree slots tree_base + j
+ *   (j < n_tree <= 128) whose bit j is set in tree_mask[2r] (j < 64) or
+ *   tree_mask[2r + 1] (j >= 64); key_end = one past the last slot any row
+ *   sees. prehi [M] int32 and tree_mask [2M] uint64 are device arrays
+ *   (tree_mask is read for every row: all zero when n_tree = 0). Query head j reads KV head
+ *   j / (n_heads / n_kv_heads) (GQA).
+ *   out: [M, n_heads * head_dim] softmax(q k^T * scale) v over the visible
+ *      keys, as an operand (bf16: hi and lo planes; fp32: one array).
+ * page_table has one entry per 64 slots up to key_end (rounded up), each a
+ * page index inside kv: the kernels read whole 64-slot chunks, masked slots
+ * included. Requires head_dim = 128 for EAGLE_BF16 (<= 256 for EAGLE_F32),
+ * every row with at least one visible key, and key_end - pre_lo <= 131072
+ * (2048 chunks of 64 keys). With bf16, no
+ * tree keys, M >= 32 and at most 8 query heads per KV head it runs the
+ * one-pass (flash) form; otherwise split-KV chunks of 64 keys and a combine.
+ * EAGLE_E_INVALID on bad sizes, EAGLE_E_BUFFER if the workspace is too small,
+ * EAGLE_E_HIP on a launch failure. */
+eagle_status eagle_op_attention(int32_t dtype, const void* q, const void* kv,
+                                const int32_t* page_table, int32_t n_kv_heads, int32_t n_heads,
+                                int32_t head_dim, int32_t M, int32_t pre_lo, const int32_t* prehi,
+                                const uint64_t* tree_mask, int32_t tree_base, int32_t n_tree,
+                                int32_t key_end, float scale, void* out, void* workspace,
+                                uint64_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

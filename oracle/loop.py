@@ -228,9 +228,11 @@ def greedy_decode(w: dict, prompt, max_new: int, weights: Weights = None):
     return out, margins, kv
 
 
-def teacher_forced(w: dict, prompt, stream, weights: Weights = None, chunk: int = 512):
+def teacher_forced(w: dict, prompt, stream, weights: Weights = None, on_layer=None):
     """One causal pass over prompt + stream[:-1]: the greedy choice and the
-    top-1/top-2 margin at every generated position, given that prefix."""
+    top-1/top-2 margin at every generated position, given that prefix.
+    Every row of a causal pass computes what one-token-at-a-time decoding
+    computes for it, so this equals greedy decode's choices on that prefix."""
     cfg = Config(w)
     W = weights if weights is not None else Weights(cfg)
     tgt = Target(cfg, W)
@@ -238,7 +240,7 @@ def teacher_forced(w: dict, prompt, stream, weights: Weights = None, chunk: int 
     n = len(seq)
     kv = tgt.new_kv(n)
     pos = np.arange(n)
-    f, _ = tgt.forward(seq, pos, pos, causal_vis(n, 0, n), kv)
+    f, _ = tgt.forward(seq, pos, pos, causal_vis(n, 0, n), kv, on_layer=on_layer)
     rows = f[len(prompt) - 1:]
     g, margin = argmax_lowest(tgt.logits(rows))
     return g, margin

@@ -206,8 +206,9 @@ class Target:
         shp = (c.n_layers, n_slots, c.n_kv_heads, c.head_dim)
         return np.zeros(shp), np.zeros(shp)
 
-    def forward(self, tokens, pos, slots, vis, kv, keep=()):
-        """Rows (token, position) -> (f [M,H] post final norm, {layer: h after it})."""
+    def forward(self, tokens, pos, slots, vis, kv, keep=(), on_layer=None):
+        """Rows (token, position) -> (f [M,H] post final norm, {layer: h after it}).
+        on_layer(i), when given, is called after layer i (progress of long passes)."""
         c = self.cfg
         h = self.W.get(EMBED, GLOBAL)[np.asarray(tokens)].astype(np.float64)
         kept = {}
@@ -216,6 +217,8 @@ class Target:
                               slots, vis)
             if layer in keep:
                 kept[layer] = h.copy()
+            if on_layer is not None:
+                on_layer(layer)
         f = to_f32(rmsnorm(h, self.W.get(FINAL_NORM, GLOBAL), c.eps))
         return f, kept
 

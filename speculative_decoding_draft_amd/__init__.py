@@ -401,6 +401,31 @@ def op_lmhead(dtype: int, k: int, x, w, M: int, V: int, H: int, ids, vals, logit
         raise EagleError(rc, "eagle_op_lmhead")
 
 
+def op_attention_workspace(dtype, M, n_heads, head_dim, key_end) -> int:
+    L = lib()
+    L.eagle_op_attention_workspace.argtypes = [i32, i32, i32, i32, i32]
+    L.eagle_op_attention_workspace.restype = u64
+    return int(L.eagle_op_attention_workspace(dtype, M, n_heads, head_dim, key_end))
+
+
+def op_attention(dtype: int, q, kv, page_table, n_kv_heads: int, n_heads: int, head_dim: int,
+                 M: int, pre_lo: int, prehi, tree_mask, tree_base: int, n_tree: int, key_end: int,
+                 scale: float, out, workspace=None, stream=None):
+    """eagle_op_attention on torch tensors (device pointers)."""
+    L = lib()
+    vp = ctypes.c_void_p
+    L.eagle_op_attention.argtypes = [i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, i32, i32,
+                                     i32, f32, vp, vp, u64, vp]
+    st = stream.cuda_stream if stream is not None else _torch_stream()
+    ws_ptr, ws_bytes = (workspace.data_ptr(), workspace.numel()) if workspace is not None else (None, 0)
+    rc = L.eagle_op_attention(dtype, q.data_ptr(), kv.data_ptr(), page_table.data_ptr(), n_kv_heads,
+                              n_heads, head_dim, M, pre_lo, prehi.data_ptr(),
+                              tree_mask.data_ptr(), tree_base,
+                              n_tree, key_end, scale, out.data_ptr(), ws_ptr, ws_bytes, st)
+    if rc:
+        raise EagleError(rc, "eagle_op_attention")
+
+
 def op_lmhead_workspace(M, V, k) -> int:
     L = lib()
     L.eagle_op_lmhead_workspace.argtypes = [i32, i32, i32]

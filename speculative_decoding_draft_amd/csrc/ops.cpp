@@ -93,4 +93,46 @@ eagle_status eagle_op_lmhead(int32_t dtype, int32_t k, const void* x, const void
   return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
 }
 
+uint64_t eagle_op_attention_workspace(int32_t dtype, int32_t M, int32_t n_heads, int32_t head_dim,
+                                      int32_t key_end) {
+  if (dtype != EAGLE_BF16 || M < 1 || n_heads < 1 || head_dim < 1 || key_end < 1) return 0;
+  const int64_t chunks = (key_end + attn_chunk_keys() - 1) / attn_chunk_keys();
+  return align256(attn_part_floats((int)chunks, M, n_heads, head_dim) * 4);
+}
+
+eagle_status eagle_op_attention(int32_t dtype, const void* q, const void* kv,
+                                const int32_t* page_table, int32_t n_kv_heads, int32_t n_heads,
+                                int32_t head_dim, int32_t M, int32_t pre_lo, const int32_t* prehi,
+                                const uint64_t* tree_mask, int32_t tree_base, int32_t n_tree,
+                                int32_t key_end, float scale, void* out, void* workspace,
+                                uint64_t ws_bytes, void* stream) {
+  if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return EAGLE_E_INVALID;
+  if (!q || !kv || !page_table || !prehi || !tree_mask || !out || M < 1 || n_kv_heads < 1 ||
+      n_heads < n_kv_heads || n_heads % n_kv_heads || pre_lo < 0 || key_end <= pre_lo ||
+      n_tree < 0 || n_tree > 128 ||
+      (n_tree > 0 && (tree_base < pre_lo || tree_base + n_tree > key_end)))
+    return EAGLE_E_INVALID;
+  if (dtype == EAGLE_BF16 ? head_dim != 128 : (head_dim < 1 || head_dim > 256))
+    return EAGLE_E_INVALID;
+  const int chunks = (key_end - pre_lo + attn_chunk_keys() - 1) / attn_chunk_keys();
+  if (chunks > attn_max_chunks()) return EAGLE_E_INVALID;
+  const uint64_t need = eagle_op_attention_workspace(dtype, M, n_heads, head_dim, key_end);
+  if (need > 0 && (!workspace || ws_bytes < need)) return EAGLE_E_BUFFER;
+  KVView v;
+  v.base = const_cast<void*>(kv);
+  v.page_table = page_table;
+  v.page = EAGLE_OP_KV_PAGE;
+  v.n_kv = n_kv_heads;
+  v.d = head_dim;
+  v.page_elems = (int64_t)kv_planes(dtype) * n_kv_heads * EAGLE_OP_KV_PAGE * head_dim;
+  RowVis vis{prehi, tree_mask, pre_lo, tree_base, n_tree, key_end};
+  const int64_t width = (int64_t)n_heads * head_dim;
+  float* opart = (float*)workspace;
+  const int64_t kc = (key_end + attn_chunk_keys() - 1) / attn_chunk_keys();
+  float* mlpart = opart ? opart + kc * M * width : nullptr;
+  hipError_t e = launch_attention(dtype, q, (int64_t)M * width, v, vis, M, n_heads, head_dim, scale,
+                                  opart, mlpart, out, (int64_t)M * width, (hipStream_t)stream);
+  return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
+}
+
 }  // extern "C"

@@ -62,12 +62,29 @@ def gpu_tree_check(tree: dict, k: int, depth: int, budget: int, static=None):
     return rows
 
 
-def stream_check(w, prompt, stream, weights=None, tol=1e-3):
+def progress(msg: str):
+    """Print a progress line and, when the run keeps a gpurun_out/ folder in
+    the working directory, append it to gpurun_out/test_progress.log (long
+    oracle passes otherwise print nothing for minutes under pytest -q)."""
+    import os
+    import time
+    print(msg, flush=True)
+    if os.path.isdir("gpurun_out"):
+        with open(os.path.join("gpurun_out", "test_progress.log"), "a") as f:
+            f.write(f"{time.strftime('%H:%M:%S')} {msg}\n")
+
+
+def stream_check(w, prompt, stream, weights=None, tol=1e-3, label=None):
     """Teacher-forced check: every token is the oracle's greedy choice on the
     GPU's own prefix, or sits where the oracle's top-1/top-2 margin < tol.
     Returns the number of such near-tie positions (a mismatch elsewhere fails)."""
     from oracle.loop import teacher_forced
-    g, margin = teacher_forced(w, prompt, stream, weights)
+    on_layer = None
+    if label is not None:
+        def on_layer(i):
+            if i % 4 == 3:
+                progress(f"{label}: oracle layer {i + 1}/{w['n_layers']}")
+    g, margin = teacher_forced(w, prompt, stream, weights, on_layer=on_layer)
     near = 0
     for i, tok in enumerate(stream):
         if tok != int(g[i]):

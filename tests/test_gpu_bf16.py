@@ -100,3 +100,76 @@ def test_cycle_parity(setup):
     assert np.array_equal(gg[ok], g[ok])
     if np.all(ok):
         assert new == [tree["token"][r] for r in path] + [bonus]
+
+
+def _planted_greedy_tree(want, L, D, V):
+    """Root, the target's greedy tokens want[1..L] as a chain with a wrong
+    sibling at each depth, and (L < D) a wrong child under the chain's end, so
+    the acceptance walk must stop after exactly L accepted rows."""
+    token, parent, depth = [want[0]], [-1], [0]
+    prev = 0
+    for d in range(1, L + 1):
+        token += [want[d], (want[d] + 1) % V]
+        parent += [prev, prev]
+        depth += [d, d]
+        prev = len(token) - 2
+    if L < D:
+        token.append((want[L + 1] + 7) % V)
+        parent.append(prev)
+        depth.append(L + 1)
+    return dict(token=token, parent=parent, depth=depth, node=[-1] * len(token))
+
+
+@pytest.mark.parametrize("accept_len", ["full", "partial"])
+def test_accepted_path_compaction_and_catch_up(setup, accept_len):
+    """A cycle that accepts L > 0 rows ([E2] "Putting It Together": the next
+    verified state). The GPU and the oracle verify the same planted tree;
+    then the next cycle (whose draft catch-up runs over the L + 1 committed
+    rows with true features -- E3: fused from the three target layers -- and
+    whose target attention reads the compacted KV of the accepted path) is
+    compared: committed tokens, drafted nodes and log-probabilities, verify
+    logits and features."""
+    from gpu_helpers import gpu_tree_check
+    from oracle.loop import Session, greedy_decode
+    w, eng, W = setup
+    D, V = w["depth"], w["vocab"]
+    L = D if accept_len == "full" else max(1, D // 2)
+    p = synth.prompt(6, w["prompt_len"], V)
+    print(f"{w['name']} planted L={L}", flush=True)
+    want, margins, _ = greedy_decode(w, p, D + 2, W)
+    if min(margins[:L + 2]) < 1e-3:
+        pytest.skip("near-tie on the greedy path: acceptance length not determined")
+    ref = Session(w, W)
+    assert ref.prefill(p) == want[0]
+    assert eng.prefill(p) == want[0]
+    planted = _planted_greedy_tree(want, L, D, V)
+    eng.set_debug(True)
+    try:
+        new = eng.verify(planted)
+        path, bonus, g, margin = ref.verify(planted)
+        assert len(path) == L and new == want[1:L + 2], (new, want[:L + 2])
+        rel = _rel_rows(eng.debug_read("logits"), ref.last_logits)
+        f_rel = _rel_rows(eng.debug_read("features"), ref.last_features)
+        print(f"{w['name']}: planted verify logits {rel:.2e} features {f_rel:.2e}", flush=True)
+        assert rel < 1e-3 and f_rel < 1e-3
+        # next cycle: draft over the catch-up of the L + 1 committed rows
+        tree = eng.draft_tree()
+        static = w["static"] if w["tree"] == "static" else None
+        gpu_tree_check(tree, w["topk"], D, w["budget"], static)
+        t, rows = ref.draft_tree()
+        same, near = compare_drafts(tree, t, ref.row_logits)
+        print(f"{w['name']}: after L={L}: {same}/{len(t.nodes)} drafted nodes equal ({near})",
+              flush=True)
+        assert same >= w["topk"]
+        # and its verify reads the compacted target KV
+        new2 = eng.verify()
+        path2, bonus2, g2, margin2 = ref.verify(dict(token=tree["token"], parent=tree["parent"],
+                                                     depth=tree["depth"], node=tree["node"]))
+        rel = _rel_rows(eng.debug_read("logits"), ref.last_logits)
+        f_rel = _rel_rows(eng.debug_read("features"), ref.last_features)
+        print(f"{w['name']}: next verify logits {rel:.2e} features {f_rel:.2e}", flush=True)
+        assert rel < 1e-3 and f_rel < 1e-3
+        if np.all(margin2 >= 1e-3):
+            assert new2 == [tree["token"][r] for r in path2] + [bonus2]
+    finally:
+        eng.set_debug(False)

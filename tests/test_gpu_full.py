@@ -18,9 +18,14 @@ and oracle recomputations of sampled outputs:
   as a chain ([E2] "The Mask Preserves Tree Semantics in One Target Pass");
 * LM head: the oracle's logits from the GPU's own final features on
   sampled rows (the full vocabulary, 128256 rows at the 8B shape);
-and, with every layer but a short prompt, the oracle's teacher-forced greedy
-choices over the GPU's stream.
+and the oracle's teacher-forced greedy choices over the GPU's stream: at the
+configs' own prompt and generation lengths for the 7B shapes (512 + 256 and
+1536 + 512 tokens; set EAGLE_ORACLE_LONG=c4,c5 to run the 8B and 70B shapes'
+3584 + 512 and 1024 + 256 as well, 15-40 minutes of CPU work), and with every
+layer but a short prompt for all four.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -147,3 +152,32 @@ def test_full_depth_teacher_forced(setup):
     near = stream_check(w, p, got, W)
     print(f"{w['name']}: {len(got)} tokens, near-ties {near}", flush=True)
     assert near <= 1
+
+
+# configs whose full-length oracle pass fits the default test run
+FULL_LENGTH_DEFAULT = ("c2", "c3")
+
+
+@pytest.mark.timeout(1500)
+def test_full_length_stream_teacher_forced(setup):
+    """The spec check at the config's own size: the committed stream of
+    a full-length generation (prompt seed 1) is, token by token, the oracle's
+    greedy choice on the GPU's own prefix ([L13] "Speculative decoding in four
+    moves": the speculative output equals plain greedy decoding), except at
+    positions whose oracle top-1/top-2 margin is below 1e-3, which are counted.
+    By induction, a stream that passes at every position is the greedy stream."""
+    from gpu_helpers import progress, stream_check
+    from oracle.model import Config, Weights
+    w, eng = setup
+    name = w["name"]
+    extra = [c for c in os.environ.get("EAGLE_ORACLE_LONG", "").split(",") if c]
+    if name not in FULL_LENGTH_DEFAULT and name not in extra:
+        pytest.skip(f"{name}: full-length oracle pass is long; set EAGLE_ORACLE_LONG={name}")
+    p = synth.prompt(1, w["prompt_len"], w["vocab"])
+    got, stats = eng.generate(p, w["gen"])
+    progress(f"{name}: generated {len(got)} tokens in {stats['cycles']} cycles; oracle "
+             f"teacher-forced pass over {len(p) + len(got) - 1} tokens")
+    W = Weights(Config(w), cache_bytes=4 << 30)
+    near = stream_check(w, p, got, W, label=name)
+    progress(f"{name}: full-length stream: {len(got)} tokens equal the oracle's greedy choice, "
+             f"near-ties {near}")

@@ -91,6 +91,9 @@ LINEAR = [  # (dtype, M, N, K): split-K, tails, several M tiles, prefill-sized M
     (BF16, 108, 12288, 4096), (BF16, 216, 8200, 1024), (BF16, 300, 8192, 512),
     (BF16, 130, 4096, 1024), (BF16, 257, 4104, 2048), (BF16, 129, 1000, 256),
     (BF16, 512, 4096, 11008), (BF16, 100, 4096, 11008), (BF16, 90, 4096, 4096),
+    # the prefill chunk shapes: 256-row m-chunks (MT = 8), two of them, with
+    # two K splits (512 rows) and a ragged second chunk (300 rows)
+    (BF16, 512, 12288, 4096), (BF16, 300, 12288, 4096),
 ]
 
 
@@ -123,7 +126,13 @@ def test_linear(dtype, M, N, K, epi):
                                          (BF16, 1, 11008, 4096), (F32, 17, 688, 256),
                                          (BF16, 100, 2720, 1024), (BF16, 200, 1376, 1024),
                                          # wide FFNs: fourteen-wave workgroups
-                                         (BF16, 27, 17008, 512), (F32, 17, 17000, 256)])
+                                         (BF16, 27, 17008, 512), (F32, 17, 17000, 256),
+                                         # prefill chunks: gate|up unsplit over two 256-row
+                                         # m-chunks plus the SiLU pass (512 rows, 7B FFN),
+                                         # a ragged second chunk (300 rows, 8B FFN), one
+                                         # chunk with four splits (200 rows)
+                                         (BF16, 512, 11008, 4096), (BF16, 300, 14336, 4096),
+                                         (BF16, 200, 11008, 4096)])
 def test_swiglu(dtype, M, N, K):
     print(f"swiglu dtype={dtype} M={M} N={N} K={K}", flush=True)
     gen = torch.Generator().manual_seed(M + N + K)
