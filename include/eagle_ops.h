@@ -58,6 +58,25 @@ eagle_status eagle_op_linear(int32_t dtype, int32_t epilogue, const void* x, con
                              int32_t M, int32_t N, int32_t K, void* workspace, uint64_t ws_bytes,
                              void* stream);
 
+/* Largest workspace eagle_op_linear_noalloc can serve (32 MiB). */
+#define EAGLE_OP_NOALLOC_SCRATCH_BYTES (32ull << 20)
+
+/* eagle_op_linear without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results (bit for bit)
+ * and kernels as eagle_op_linear; the partial planes go to a fixed array of
+ * EAGLE_OP_NOALLOC_SCRATCH_BYTES that the library holds on each device it
+ * runs on until the process ends. The call allocates nothing. It runs on
+ * the device current at the call (the stream must belong to it). Every call
+ * on one device shares that device's array, so calls that may overlap on a
+ * device (different streams, or host threads) race; calls on one stream are
+ * ordered and safe. EAGLE_E_CAPACITY, before any launch, if the shape needs
+ * more than EAGLE_OP_NOALLOC_SCRATCH_BYTES (eagle_op_linear_workspace gives
+ * the need); EAGLE_E_INVALID on bad sizes; EAGLE_E_HIP if the array's
+ * address cannot be obtained or a launch fails. */
+eagle_status eagle_op_linear_noalloc(int32_t dtype, int32_t epilogue, const void* x, const void* w,
+                                     void* y, int32_t M, int32_t N, int32_t K, void* stream);
+
 /* Workspace bytes of eagle_op_lmhead (k = 0 for the greedy variant). */
 uint64_t eagle_op_lmhead_workspace(int32_t M, int32_t V, int32_t k);
 

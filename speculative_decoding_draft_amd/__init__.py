@@ -375,6 +375,22 @@ def op_linear(dtype: int, epilogue: int, x, w, y, M: int, N: int, K: int, worksp
         raise EagleError(rc, "eagle_op_linear")
 
 
+NOALLOC_SCRATCH_BYTES = 32 << 20   # EAGLE_OP_NOALLOC_SCRATCH_BYTES
+
+
+def op_linear_noalloc(dtype: int, epilogue: int, x, w, y, M: int, N: int, K: int, stream=None):
+    """eagle_op_linear_noalloc: eagle_op_linear with the library's own fixed
+    device array as its workspace (no allocation anywhere)."""
+    L = lib()
+    L.eagle_op_linear_noalloc.argtypes = [i32, i32, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, i32, i32, i32, ctypes.c_void_p]
+    st = stream.cuda_stream if stream is not None else _torch_stream()
+    rc = L.eagle_op_linear_noalloc(dtype, epilogue, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                                   M, N, K, st)
+    if rc:
+        raise EagleError(rc, "eagle_op_linear_noalloc")
+
+
 def op_linear_workspace(dtype, epilogue, M, N, K) -> int:
     L = lib()
     L.eagle_op_linear_workspace.argtypes = [i32, i32, i32, i32, i32]

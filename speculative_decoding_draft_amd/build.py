@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libeagle.so")
 HIPCC = "/opt/rocm/bin/hipcc"
-SOURCES = ["gemm.hip", "attn.hip", "tree.hip", "sample.hip", "eagle.cpp", "ops.cpp"]
+SOURCES = ["gemm.hip", "attn.hip", "tree.hip", "sample.hip", "eagle.cpp", "ops.cpp",
+           "noalloc.hip"]
 # packed fp32 instructions are disabled for every device pass
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
