@@ -4,10 +4,13 @@ default; --batch B serves B sequences per cycle).
 A step is one cycle: the draft passes and tree build (eagle_draft_tree) plus
 the target verify pass, acceptance, KV compaction and the draft catch-up
 (eagle_verify, or eagle_verify_batch for every lane of a batch), on seeded
-synthetic weights and prompts already resident in HBM. Prints one JSON line
-(see README of the driver contract):
+synthetic weights and prompts already resident in HBM. For each prompt seed
+(1, 2, 3 by default) the sequence is prefilled, advanced by untimed cycles to
+the config's mean context (prompt + half the generation) less half the timed
+cycles, warmed up, and K cycles are timed. Prints one JSON line:
   value       committed tokens/s over all lanes (tau x lanes x cycles/s; tau ~
-              1 with random weights)
+              1 with random weights), from the median seed's timed cycles;
+              every seed's figure is under "seeds"
   roofline    the dominant kernel: the split-K projection of the target
               layers (q|k|v, o and down at M = tree rows), its algorithmic
               bytes / its device time from HIP events recorded around each of
@@ -66,11 +69,13 @@ def stored_traffic(kernel_key: str):
     return None
 
 
-def cycle_bytes(w: dict, ctx: int, lanes: int = 1) -> float:
+def cycle_bytes(w: dict, ctx: int, lanes: int = 1, kv_elem_bytes: int = None) -> float:
     """Algorithmic HBM bytes of one cycle at context ctx: every weight byte the
     cycle must read (target layers + LM head once; draft layer + LM head +
-    FC per draft pass), plus the KV cache reads (4 bytes per K/V element) of
-    each of `lanes` sequences."""
+    FC per draft pass), plus the KV cache reads of each of `lanes` sequences at
+    the method's element size (2 bytes for bf16; the hi + lo planes this
+    implementation keeps are 4 bytes per element, passed as kv_elem_bytes
+    to count its KV traffic instead)."""
     H, nq, nkv, F, V, L = (w[k] for k in ("hidden", "n_heads", "n_kv_heads", "ffn", "vocab", "n_layers"))
     d = H // nq
     esz = 2 if w["dtype"] == "bf16" else 4
@@ -80,8 +85,19 @@ def cycle_bytes(w: dict, ctx: int, lanes: int = 1) -> float:
     target = L * layer(H) + V * H
     draft = D * (layer(kin) + V * H)
     fc = D * H * 2 * H if w["head"] == "e1" else H * 3 * H
-    kv = 2 * nkv * d * 4 * (L * ctx + D * ctx) * lanes
+    kv = 2 * nkv * d * (kv_elem_bytes or esz) * (L * ctx + D * ctx) * lanes
     return esz * (target + draft + fc) + kv
+
+
+def plain_token_bytes(w: dict, ctx: int) -> float:
+    """Algorithmic HBM bytes of one plain greedy decode step at context ctx:
+    target layers and LM head once, plus the target KV at the method's
+    element size."""
+    H, nq, nkv, F, V, L = (w[k] for k in ("hidden", "n_heads", "n_kv_heads", "ffn", "vocab", "n_layers"))
+    d = H // nq
+    esz = 2 if w["dtype"] == "bf16" else 4
+    layer = nq * d * H + 2 * nkv * d * H + nq * d * H + 3 * H * F
+    return esz * (L * layer + V * H + 2 * nkv * d * L * ctx)
 
 
 PEAK_BF16_TFLOPS = 2500.0   # dense MFMA, bf16
@@ -138,16 +154,91 @@ def cpu_baseline(w: dict, budget_layers: int = 2) -> dict:
     t4 = time.perf_counter()
     per_cycle = (t1 - t0) + (t2 - t1) + (w["n_layers"] - budget_layers) * (t4 - t3)
     cores = len(os.sched_getaffinity(0))
+    model_name = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model_name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         if os.environ.get(var, "").isdigit():
             cores = min(cores, int(os.environ[var]))   # BLAS threads actually used
             break
     return {"value": round(1.0 / per_cycle, 5), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model_name,
             "sample": (f"one cycle of {w['name']} (tau=1): draft passes {t1 - t0:.2f}s and verify "
                        f"{t2 - t1:.2f}s timed on a {budget_layers}-layer slice (full width, tree, "
                        f"vocab; prompt 64) + {w['n_layers'] - budget_layers} x {t4 - t3:.2f}s per "
                        f"target layer at {M} rows; numpy fp64, {cores} threads")}
+
+
+def make_engine(w: dict, cycles: int, prefill_chunk: int = 0):
+    """A loaded engine with the seeded weights, sized for the prompt plus
+    `cycles` cycles of up to depth + 1 tokens each (and the generation)."""
+    import torch
+    import synth
+    import speculative_decoding_draft_amd as E
+    max_new = max(w["gen"], cycles * (w["depth"] + 1))
+    max_ctx = w["prompt_len"] + max_new + w["depth"] + 2
+    eng = E.Engine(w, max_ctx=max_ctx, prefill_chunk=prefill_chunk)
+    synth.fill_weights(eng.table, eng.weights.data_ptr(), w["weight_seed"], eng.stream.cuda_stream)
+    torch.cuda.synchronize()
+    eng.load()
+    return eng
+
+
+def run_cycles(eng, B: int, n: int) -> int:
+    """n cycles of every lane; returns the tokens committed."""
+    committed = 0
+    for _ in range(n):
+        eng.draft_tree(want=False)
+        if B == 1:
+            committed += len(eng.verify())
+        else:
+            committed += sum(len(t) for t in eng.verify_batch())
+    return committed
+
+
+def mean_ctx(eng, B: int, prompt_len: int) -> float:
+    """Mean context length over the lanes: prompt + committed tokens - 1 (the
+    last committed token is the next cycle's root)."""
+    return sum(len(eng.committed(b)) for b in range(B)) / B + prompt_len - 1
+
+
+def timed_window(eng, w: dict, B: int, seed: int, steps: int, warmup: int, roof: bool):
+    """Prefill every lane (lane b: prompt seed + b), advance to the config's
+    mean context less half the timed cycles, warm up, then time `steps`
+    cycles between stream synchronisations. Returns the window's figures."""
+    import torch
+    import synth
+    P = w["prompt_len"]
+    for b in range(B):
+        eng.prefill(synth.prompt(seed + b, P, w["vocab"]), lane=b)
+    target = P + w["gen"] / 2.0 - steps / 2.0
+    while mean_ctx(eng, B, P) + warmup < target:
+        # tau ~ 1: one cycle moves the context by one token, so advance in
+        # batches of the remaining distance, re-reading the context after each
+        run_cycles(eng, B, max(1, min(64, int(target - warmup - mean_ctx(eng, B, P)))))
+    if roof:
+        eng.profile(["gemm"], every=ROOF_EVERY)
+    run_cycles(eng, B, warmup)
+    torch.cuda.synchronize()
+    if roof:
+        eng.profile(["gemm"], every=ROOF_EVERY)   # reset the counters; keep the class enabled
+    ctx0 = mean_ctx(eng, B, P)
+    t0 = time.perf_counter()
+    committed = run_cycles(eng, B, steps)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    g = eng.profile_read()["gemm"] if roof else None
+    if roof:
+        eng.profile(False)
+    ctx1 = mean_ctx(eng, B, P)
+    return dict(seed=seed, seconds=dt, committed=committed, ctx0=ctx0, ctx1=ctx1, gemm=g,
+                cycles_per_s=steps / dt)
 
 
 def main():
@@ -159,6 +250,12 @@ def main():
     ap.add_argument("--profile-cycles", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--seeds", type=int, default=3,
+                    help="prompt seeds seed .. seed + seeds - 1, each timed over --steps cycles")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra figures (whole generation, plain decode, second config)")
+    ap.add_argument("--extra-config", default="c3",
+                    help="second workload timed as an extra key (batch 1, greedy); '' for none")
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="> 0: sampling-mode verification (rejection sampling over the tree)")
     ap.add_argument("--batch", type=int, default=1,
@@ -189,23 +286,17 @@ def main():
     import numpy as np
     import torch
     import synth
-    import speculative_decoding_draft_amd as E
 
     w = synth.workloads.get(args.config)
     if args.temperature > 0:
         w.update(temperature=args.temperature, seed=args.seed)
     B = args.batch
     w["batch"] = B
-    cycles_needed = args.warmup + args.steps + max(0, args.profile_cycles) + 2 + 5   # + speedup-model cycles
-    max_new = max(w["gen"], cycles_needed * (w["depth"] + 1))
-    max_ctx = w["prompt_len"] + max_new + w["depth"] + 2
-    eng = E.Engine(w, max_ctx=max_ctx, prefill_chunk=args.prefill_chunk)
-    synth.fill_weights(eng.table, eng.weights.data_ptr(), w["weight_seed"], eng.stream.cuda_stream)
-    torch.cuda.synchronize()
-    eng.load()
-    # lane b's prompt comes from seed + b (lane 0: the batch-1 prompt)
-    prompts = [synth.prompt(args.seed + b, w["prompt_len"], w["vocab"]) for b in range(B)]
-    prompt = prompts[0]
+    P = w["prompt_len"]
+    # advance to mid-generation, warm-up, timed, profile and speedup-model cycles
+    cycles_needed = w["gen"] // 2 + args.warmup + args.steps + max(0, args.profile_cycles) + 8
+    eng = make_engine(w, cycles_needed, args.prefill_chunk)
+    prompt = synth.prompt(args.seed, P, w["vocab"])
     # the first prefill loads the kernels; the second (it restarts the
     # sequence) is the timed one
     eng.prefill(prompt)
@@ -214,43 +305,23 @@ def main():
     eng.prefill(prompt)
     torch.cuda.synchronize()
     prefill_ms = (time.perf_counter() - tp0) * 1e3
-    for b in range(1, B):
-        eng.prefill(prompts[b], lane=b)
-    print(f"# {args.config}: prefill done, ctx {len(prompt)}, {prefill_ms:.1f} ms, {B} lane(s)",
+    print(f"# {args.config}: prefill {P} tokens in {prefill_ms:.1f} ms, {B} lane(s)",
           file=sys.stderr, flush=True)
 
-    def cycle():
-        eng.draft_tree(want=False)
-        if B == 1:
-            return len(eng.verify())
-        return sum(len(n) for n in eng.verify_batch())
-
-    def mean_ctx():
-        return sum(len(eng.committed(b)) for b in range(B)) / B + len(prompt) - 1
-
-    # the dominant kernel's launches carry HIP events from warmup on, so the
-    # event pool is allocated before the timed region
-    eng.profile(["gemm"], every=ROOF_EVERY)
-    for _ in range(args.warmup):
-        cycle()
-    torch.cuda.synchronize()
-    eng.profile(["gemm"], every=ROOF_EVERY)   # reset the counters; keep the class enabled
-    ctx0 = mean_ctx()
-    t0 = time.perf_counter()
-    committed = 0
-    for _ in range(args.steps):
-        committed += cycle()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    dt = t1 - t0
-    g = eng.profile_read()["gemm"]
-    eng.profile(False)
-    ctx1 = mean_ctx()
-    print(f"# timed {args.steps} cycles in {dt * 1e3:.1f} ms", file=sys.stderr, flush=True)
-
-    # algorithmic bytes of the timed cycles (context grows by L+1 per cycle)
-    avg_ctx = 0.5 * (ctx0 + ctx1)
+    windows = []
+    for k in range(max(1, args.seeds)):
+        win = timed_window(eng, w, B, args.seed + k, args.steps, args.warmup, roof=True)
+        windows.append(win)
+        print(f"# seed {win['seed']}: {args.steps} cycles at ctx {win['ctx0']:.0f}..{win['ctx1']:.0f} "
+              f"in {win['seconds'] * 1e3:.1f} ms ({win['cycles_per_s']:.2f} cycles/s)",
+              file=sys.stderr, flush=True)
+    order = sorted(range(len(windows)), key=lambda i: windows[i]["cycles_per_s"])
+    med = windows[order[len(order) // 2]]
+    dt, committed, g = med["seconds"], med["committed"], med["gemm"]
+    avg_ctx = 0.5 * (med["ctx0"] + med["ctx1"])
     bytes_cycle = cycle_bytes(w, int(avg_ctx), B)
+    kv_planes = 4 if w["dtype"] == "bf16" else None
+    traffic_cycle = cycle_bytes(w, int(avg_ctx), B, kv_elem_bytes=kv_planes)
     gemm_gbps = g["bytes"] / (g["ms"] * 1e-3) / 1e9 if g["ms"] > 0 else 0.0
     mv = B * (1 + w["budget"])    # target rows of a verify pass
     mt = (mv + 15) // 16 if mv <= 80 else 4
@@ -259,8 +330,7 @@ def main():
     prof = None
     if args.profile_cycles > 0:
         eng.profile(True)
-        for _ in range(args.profile_cycles):
-            cycle()
+        run_cycles(eng, B, args.profile_cycles)
         prof = eng.profile_read()
         eng.profile(False)
     # draft-pass and target-pass times for the speedup model: D - 1 tree
@@ -288,6 +358,7 @@ def main():
     tau = committed / args.steps / B
     roof_key = (f"proj_kernel<{'bf16' if w['dtype'] == 'bf16' else 'f32'}, MT={mt}, EPI_PART> M={mv}")
     traffic = stored_traffic(roof_key)
+    cps = [x["cycles_per_s"] for x in windows]
     out = {
         "metric": ("committed tokens/sec + draft/verify cycles/sec at bs=1; % of HBM roofline"
                    if B == 1 else
@@ -298,16 +369,23 @@ def main():
         "ms_per_step": round(dt / args.steps * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w["dtype"],
-        "data": "synthetic (seeded N(0,0.02)-like weights, uniform random prompt)",
+        "data": "synthetic (seeded N(0,0.02)-like weights, uniform random prompts)",
         "config": {"workload": f"{args.config}: {WORKLOAD_TEXT[args.config]}"
                                + (f"; sampling at temperature {args.temperature}" if args.temperature > 0 else "")
                                + (f"; {B} sequences per cycle" if B > 1 else ""),
                    "global_batch": B, "seq_len": int(avg_ctx), "parallelism": "none (1 GPU)"},
         "cycles_per_s": round(cycles_s, 3),
         "tau": round(tau, 4),
+        "seeds": {"timed_seed": med["seed"], "median_cycles_per_s": round(cps[order[len(order) // 2]], 3),
+                  "min_cycles_per_s": round(min(cps), 3), "max_cycles_per_s": round(max(cps), 3),
+                  "per_seed": [{"seed": x["seed"], "cycles_per_s": round(x["cycles_per_s"], 3),
+                                "tokens_per_s": round(x["committed"] / x["seconds"], 3),
+                                "ctx": [round(x["ctx0"]), round(x["ctx1"])]} for x in windows]},
         "cycle_hbm": {"bytes_per_cycle": bytes_cycle,
                       "achieved_GBps": round(bytes_cycle * cycles_s / 1e9, 1),
-                      "frac": round(bytes_cycle * cycles_s / 1e9 / PEAK_GBPS, 4)},
+                      "frac": round(bytes_cycle * cycles_s / 1e9 / PEAK_GBPS, 4),
+                      "kv_bytes_per_element": 2 if w["dtype"] == "bf16" else 4,
+                      "bytes_per_cycle_with_kv_planes": traffic_cycle},
         "roofline": {"bound": "hbm",
                      "kernel": (f"proj_kernel<{'bf16' if w['dtype'] == 'bf16' else 'f32'}, MT={mt}, EPI_PART>: "
                                 f"target q|k|v, o and down projections at M={mv}"),
@@ -328,11 +406,56 @@ def main():
         out["speedup_model"] = model
     if prof is not None:
         out["profile_ms_per_cycle"] = {k: round(v["ms"] / args.profile_cycles, 4) for k, v in prof.items()}
+
+    if not args.no_extra and B == 1 and args.temperature == 0:
+        # the whole generation of the config (prompt seed `seed`): eagle_generate
+        # times its cycle loop on the device (prefill excluded)
+        toks, st = eng.generate(prompt, w["gen"])
+        out["generation"] = {"tokens": len(toks), "cycles": st["cycles"],
+                             "cycle_loop_s": round(st["seconds"], 5),
+                             "tokens_per_s": round((st["committed"] - 1) / st["seconds"], 3),
+                             "cycles_per_s": round(st["cycles"] / st["seconds"], 3),
+                             "ctx": [P, P + len(toks)]}
+        eng.close()
+        del eng
+        torch.cuda.empty_cache()
+        # plain greedy decode on the GPU (budget 0: one token per target pass,
+        # no drafting) over the same generation: the in-house speedup baseline
+        wp = dict(w, tree="dynamic", static=None, budget=0)
+        pe = make_engine(wp, 8)
+        toks_p, stp = pe.generate(prompt, w["gen"])
+        plain_tps = (stp["committed"] - 1) / stp["seconds"]
+        mid = P + w["gen"] // 2
+        out["plain_decode"] = {"tokens_per_s": round(plain_tps, 3),
+                               "bytes_per_token": plain_token_bytes(w, mid),
+                               "frac": round(plain_token_bytes(w, mid) * plain_tps / 1e9 / PEAK_GBPS, 4),
+                               "same_tokens": toks_p == toks,
+                               "speculative_over_plain": round(out["generation"]["tokens_per_s"] / plain_tps, 4)}
+        pe.close()
+        del pe
+        torch.cuda.empty_cache()
+        if args.extra_config and args.extra_config != args.config:
+            wx = synth.workloads.get(args.extra_config)
+            xe = make_engine(wx, wx["gen"] // 2 + args.warmup + args.steps + 8)
+            xwin = timed_window(xe, wx, 1, args.seed, args.steps, args.warmup, roof=False)
+            xctx = 0.5 * (xwin["ctx0"] + xwin["ctx1"])
+            xb = cycle_bytes(wx, int(xctx))
+            out["extra_config"] = {"workload": f"{args.extra_config}: {WORKLOAD_TEXT[args.extra_config]}",
+                                   "seed": args.seed, "steps": args.steps,
+                                   "cycles_per_s": round(xwin["cycles_per_s"], 3),
+                                   "tokens_per_s": round(xwin["committed"] / xwin["seconds"], 3),
+                                   "ctx": [round(xwin["ctx0"]), round(xwin["ctx1"])],
+                                   "bytes_per_cycle": xb,
+                                   "frac": round(xb * xwin["cycles_per_s"] / 1e9 / PEAK_GBPS, 4)}
+            xe.close()
+            del xe
+            torch.cuda.empty_cache()
+    else:
+        eng.close()
     if not args.no_cpu:
         # sequences are independent: the oracle's tokens/s is the same at any batch
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out))
-    eng.close()
 
 
 if __name__ == "__main__":
