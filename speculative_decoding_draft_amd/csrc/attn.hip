@@ -2,18 +2,25 @@
 // per-row kernels around it (embedding, RMSNorm, RoPE + KV append, draft
 // input assembly, row gathers, KV compaction).
 //
-// bf16 attention (head_dim 128): one workgroup of four waves per (KV head,
-// chunk of 64 keys, group of four (query head, 16-row block) pairs). The
-// chunk's K (hi and lo planes, XOR-swizzled rows) and V^T (hi and lo) are
-// staged in LDS once and shared by the group's pairs; a GQA head with more
-// pairs spreads them over several workgroups. Per 32-key block a wave
-// computes S^T = K Q^T and O^T += V^T P^T on 16x16x32 bf16 MFMA; keys are
-// read in an order that makes each lane's 8 scores exactly the P^T operand
-// of the PV product, so P never leaves registers. Q, K, V and P are carried
-// as bf16 hi + lo parts (three products; lo*lo dropped), which keeps ~16
-// mantissa bits. When a chunk has fewer (head, row block) pairs than waves,
-// the waves split its keys and merge through LDS, so each chunk leaves one
-// (max, sum, O) partial per row and head; a second kernel merges chunks.
+// bf16 attention (head_dim 128) has three forms, all with the same per-block
+// arithmetic: per 32-key block a wave computes S^T = K Q^T and O^T += V^T P^T
+// on 16x16x32 bf16 MFMA; keys are read in an order that makes each lane's 8
+// scores exactly the P^T operand of the PV product, so P never leaves
+// registers. Q, K, V and P are carried as bf16 hi + lo parts (three
+// products; lo*lo dropped), which keeps ~16 mantissa bits. A chunk's K (hi
+// and lo planes, XOR-swizzled rows) and V^T (hi and lo) are staged in LDS
+// once and shared by every query row of the KV head that reads it.
+//  - attn_bf16_kernel: one workgroup of four waves per (64-key chunk, KV
+//    head, group of (query head, 16-row block) pairs); every chunk's loads
+//    go out at once, each chunk leaves a (max, sum, O) partial per row and
+//    head, and attn_combine_kernel merges them. For few rows per sequence
+//    (static-tree verify, draft passes), where latency bounds the launch.
+//  - attn_split_kernel: one workgroup of eight waves per (KV head, key
+//    split, row group) walks the chunks of its split; the query rows of a GQA
+//    group are packed densely into 16-row tiles. For many rows per sequence
+//    (dynamic-tree verify), where the KV stream bounds the launch.
+//  - attn_flash_kernel: causal prefill rows (no tree keys), one pass over
+//    the keys per (KV head, row block), no partials.
 #include "common.h"
 #include "kernels.h"
 
@@ -638,6 +645,339 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
   }
 }
 
+// Tree-masked attention for verify and draft rows (and short catch-ups), in
+// split form: one workgroup of eight waves per (KV head, key split, row
+// group) walks the 64-key chunks of its split with the flash kernel's chunk
+// pipeline (K and V^T hi/lo staged in LDS, the next chunk's loads in flight
+// meanwhile) and the same MFMA products and log2-unit online softmax. The
+// query rows of one KV head -- its `group` query heads times the sequence's
+// rows -- are packed densely into 16-row tiles (query row qr = j * rows + r
+// for query head j of the group and row r), so a GQA group's rows fill the
+// MFMA tiles instead of each head padding its rows to 16. A row group holds
+// up to 4 * PW tiles; wave w takes tile slot w % 4 (PW tiles each) and the
+// key half w / 4 of every chunk, and the halves merge through LDS. When no
+// sequence of the launch splits its keys the normalized rows are written as
+// the next projection's operand; otherwise each split leaves one (max, sum,
+// O) partial per row and query head in attn_bf16_kernel's chunk layout for
+// attn_combine_kernel. The split
+// count depends only on the sequence's own key count, tiles and KV heads, so
+// a sequence gets the same bits alone or in a batch. Workgroup indices are
+// mapped so that the row groups of one (KV head, split) share an XCD and
+// read its keys from that XCD's L2.
+struct SplitArgs {
+  const bf16_t* q; int64_t qlo;
+  KVView kv;
+  RowVis vis;
+  Lanes ln;
+  int M, nq, group;
+  int ntile;                  // 16-row tiles per (sequence, KV head)
+  int tpg;                    // tiles per row group
+  int rg;                     // row groups per (sequence, KV head)
+  int smax;                   // splits in the grid (the largest over sequences)
+  int splits[MAX_LANES];      // sequence b's split count
+  float scale;                // log2 units
+  bf16_t* out; int64_t olo;   // one split: the normalized output operand
+  float* opart; float* mlpart;  // several: partials [split][M][nq][D], [split][M][nq][2]
+};
+
+template <int PW>
+__global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
+  constexpr int D = 128, CK = CHUNK, VP = CK + 8, NT = 512;
+  __shared__ uint4 ks[2][CK][16];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];
+  const int seq = blockIdx.z;
+  int S = 1;
+#pragma unroll
+  for (int i = 0; i < MAX_LANES; ++i) S = i == seq ? a.splits[i] : S;
+  // workgroup -> (unit = KV head * smax + split, row group)
+  const int U = a.kv.n_kv * a.smax;
+  int unit, rgi;
+  if ((U & 7) == 0) {
+    const int w = blockIdx.x, j = w >> 3;
+    unit = (w & 7) + 8 * (j / a.rg);
+    rgi = j % a.rg;
+  } else {
+    unit = blockIdx.x / a.rg;
+    rgi = blockIdx.x % a.rg;
+  }
+  const int hk = unit / a.smax, sp = unit % a.smax;
+  if (sp >= S) return;   // a sequence with fewer splits: uniform over the workgroup
+  const RowVis vis = lane_vis(a.vis, a.ln, seq);
+  const KVView kv = lane_kv<bf16_t>(a.kv, seq);
+  const int Ml = a.ln.n > 1 ? a.ln.rows : a.M, r0 = seq * Ml;
+  const int nqr = a.group * Ml;   // query rows of this KV head
+  const int nch = (vis.key_end - vis.pre_lo + CK - 1) / CK;
+  const int c_lo = (int)((int64_t)sp * nch / S), c_hi = (int)((int64_t)(sp + 1) * nch / S);
+  const int kend = vis.key_end;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int slot = wave & 3, kh = wave >> 2;
+  const int lr = lane & 15, g = lane >> 4;
+  const int t0 = rgi * a.tpg, ntg = min(a.tpg, a.ntile - t0);   // this group's tiles
+
+  // chunk staging (keys past the chunk's end repeat its last key; they are
+  // masked); a chunk spans at most two KV pages
+  const int pgsz = kv.page, psh = page_shift(kv);
+  struct Stage { uint4 kr[4], va[2], vb[2]; };
+  Stage st0, st1;
+  auto load_chunk = [&](int c, Stage& sg) {
+    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+    const int pA = k0 >> psh;
+    const int pgA = kv.page_table[pA], pgB = kv.page_table[(k1 - 1) >> psh];
+    auto kvp = [&](int key, int plane) {
+      const int pg = ((key >> psh) == pA) ? pgA : pgB;
+      return (const bf16_t*)kv.base + (int64_t)pg * kv.page_elems +
+             ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
+    };
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      sg.kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      sg.va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
+      sg.vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
+    }
+  };
+  auto store_chunk = [&](const Stage& sg) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      ks[plane][key][c16 ^ k_swz(key)] = sg.kr[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      const uint32_t wa[4] = {sg.va[it].x, sg.va[it].y, sg.va[it].z, sg.va[it].w};
+      const uint32_t wb[4] = {sg.vb[it].x, sg.vb[it].y, sg.vb[it].z, sg.vb[it].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
+      }
+    }
+  };
+  uint4 qf[PW][4], ql[PW][4];
+  int prehi[PW], pmin[PW], rowr[PW], headj[PW];
+  bool valid[PW];
+  uint64_t mk0[PW], mk1[PW];
+  float m_run[PW], l_run[PW];
+  f32x4 o[PW][8];
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const int t = t0 + min(slot + 4 * i, max(ntg - 1, 0));
+    const int qr = 16 * t + lr;
+    valid[i] = slot + 4 * i < ntg && qr < nqr;
+    const int qc = min(qr, nqr - 1);
+    headj[i] = qc / Ml;
+    rowr[i] = qc - headj[i] * Ml;
+    const int h = hk * a.group + headj[i];
+    const bf16_t* qp = a.q + ((int64_t)(r0 + rowr[i]) * a.nq + h) * D + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qf[i][s] = ld16(qp + 32 * s);
+      ql[i][s] = ld16(qp + a.qlo + 32 * s);
+    }
+    prehi[i] = vis.prehi[rowr[i]];
+    mk0[i] = vis.n_tree > 0 ? vis.mask[2 * rowr[i]] : 0ull;
+    mk1[i] = vis.n_tree > 0 ? vis.mask[2 * rowr[i] + 1] : 0ull;
+    pmin[i] = wave_min_i(prehi[i]);
+    m_run[i] = -INFINITY;
+    l_run[i] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // the first two chunks' loads go out after the query rows' loads: loads
+  // return in order, so the first use of the query rows (the visibility
+  // minimum above) then waits for them alone, and staging chunk 0 leaves
+  // chunk 1 in flight
+  if (c_lo < c_hi) load_chunk(c_lo, st0);
+  if (c_lo + 1 < c_hi) load_chunk(c_lo + 1, st1);
+  const int kb0 = 32 * kh;   // this wave's 32 keys of every chunk
+  // per chunk: S^T = K Q^T for the wave's tiles (each K fragment read from
+  // LDS once for all of them), masking and the online softmax, then
+  // O^T += V^T P^T (each V^T fragment read once)
+  auto compute = [&](int c) {
+    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+    f32x4 sc[PW][2];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) sc[i][0] = sc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+      uint4 kf[2], kl[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
+        kf[hh] = ks[0][key][(4 * s + g) ^ k_swz(key)];
+        kl[hh] = ks[1][key][(4 * s + g) ^ k_swz(key)];
+      }
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        if (slot + 4 * i >= ntg) continue;   // uniform over the wave
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], qf[i][s], sc[i][hh]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], ql[i][s], sc[i][hh]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kl[hh], qf[i][s], sc[i][hh]);
+      }
+    }
+    uint4 phi[PW], plo[PW];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      phi[i] = plo[i] = uint4{0u, 0u, 0u, 0u};
+      if (slot + 4 * i >= ntg) continue;
+      float p[8];
+      float bm = -INFINITY;
+      if (k0 + kb0 + 32 <= min(pmin[i], k1)) {
+        // every key of the block is in every row's visible prefix
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = sc[i][e >> 2][e & 3] * a.scale;
+          bm = fmaxf(bm, p[e]);
+        }
+      } else {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = k0 + kb0 + 8 * g + 4 * hh + e;
+            const bool ok = key < k1 && row_sees(vis, prehi[i], mk0[i], mk1[i], key);
+            p[4 * hh + e] = ok ? sc[i][hh][e] * a.scale : -INFINITY;
+            bm = fmaxf(bm, p[4 * hh + e]);
+          }
+      }
+      bm = xrow16_max(bm);
+      bm = xrow32_max(bm);
+      const float m_new = fmaxf(m_run[i], bm);
+      float alpha = 1.f, ps = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_run[i] - m_new);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2f(p[e] - m_new);
+          ps += p[e];
+        }
+        m_run[i] = m_new;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = 0.f;
+      }
+      ps = xrow16_sum(ps);
+      ps = xrow32_sum(ps);
+      l_run[i] = l_run[i] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[i][dt] *= alpha;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
+      }
+      phi[i] = uint4{ph[0], ph[1], ph[2], ph[3]};
+      plo[i] = uint4{pl[0], pl[1], pl[2], pl[3]};
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+      const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
+#pragma unroll
+      for (int i = 0; i < PW; ++i) {
+        if (slot + 4 * i >= ntg) continue;
+        Mma<bf16_t>::mma(v0, phi[i], o[i][dt]);
+        Mma<bf16_t>::mma(v0, plo[i], o[i][dt]);
+        Mma<bf16_t>::mma(v1, phi[i], o[i][dt]);
+      }
+    }
+  };
+
+  // Two register sets stage chunks on their way to LDS, so the loads of the
+  // next two chunks are in flight while one is computed (a load takes about
+  // as long as two chunks' products here). The loop is unrolled by two to
+  // keep the sets in fixed registers.
+  if (c_lo < c_hi) store_chunk(st0);
+  __syncthreads();
+  for (int c = c_lo; c < c_hi; c += 2) {
+    if (c + 2 < c_hi) load_chunk(c + 2, st0);
+    compute(c);
+    __syncthreads();   // every wave is done with chunk c's LDS
+    if (c + 1 >= c_hi) break;
+    store_chunk(st1);
+    __syncthreads();
+    if (c + 3 < c_hi) load_chunk(c + 3, st1);
+    compute(c + 1);
+    __syncthreads();
+    if (c + 2 >= c_hi) break;
+    store_chunk(st0);
+    __syncthreads();
+  }
+  // merge the two key halves of each tile (the K area holds the second
+  // half's O, the V area its max and sum), then write the rows
+  float* mo = reinterpret_cast<float*>(&ks[0][0][0]);   // [slot][16 rows][128]
+  float* mm = reinterpret_cast<float*>(&vt[0][0][0]);   // [slot][16 rows][2]
+  static_assert(4 * 16 * D * 4 <= (int)sizeof(ks), "merge buffer must fit");
+#pragma unroll
+  for (int i = 0; i < PW; ++i) {
+    const bool has = slot + 4 * i < ntg;   // uniform over the wave
+    if (kh == 1 && has) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mo[(slot * 16 + lr) * D + 16 * dt + 4 * g + e] = o[i][dt][e];
+      if (g == 0) {
+        mm[(slot * 16 + lr) * 2] = m_run[i];
+        mm[(slot * 16 + lr) * 2 + 1] = l_run[i];
+      }
+    }
+    __syncthreads();
+    if (kh == 0 && has) {
+      const int h = hk * a.group + headj[i];
+      const int row = r0 + rowr[i];
+      const float m1 = mm[(slot * 16 + lr) * 2], l1 = mm[(slot * 16 + lr) * 2 + 1];
+      const float mx = fmaxf(m_run[i], m1);
+      const float w0 = m_run[i] == -INFINITY ? 0.f : exp2f(m_run[i] - mx);
+      const float w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - mx);
+      const float l = w0 * l_run[i] + w1 * l1;
+      if (valid[i]) {
+        if (a.smax == 1) {
+          const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int dd = 16 * dt + 4 * g + e;
+              const float v = (w0 * o[i][dt][e] + w1 * mo[(slot * 16 + lr) * D + dd]) * inv;
+              Opnd<bf16_t>::store(a.out, a.olo, ((int64_t)row * a.nq + h) * D + dd, v);
+            }
+        } else {
+          const int64_t rec = ((int64_t)sp * a.M + row) * a.nq + h;
+          float* op = a.opart + rec * D;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              v[e] = w0 * o[i][dt][e] + w1 * mo[(slot * 16 + lr) * D + 16 * dt + 4 * g + e];
+            *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = v;
+          }
+          if (g == 0) {
+            a.mlpart[rec * 2] = mx;
+            a.mlpart[rec * 2 + 1] = l;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 constexpr int ATTN_MAX_CHUNKS = 2048;
 
 // Merges the per-chunk (max, sum, O) partials of one (row, head): the chunk
@@ -1154,22 +1494,52 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
         hipLaunchKernelGGL(attn_flash_kernel<1>, grid, dim3(512), 0, st, f);
       return hipGetLastError();
     }
-    // scores are taken in log2 units (scale * log2 e) so the softmax uses the
-    // native exp2; chunk maxima in mlpart are in the same units
-    // split a head's pairs over more workgroups only while the (chunk, KV
-    // head) grid is short of two workgroups per CU: every extra group stages
-    // the chunk again
-    const int pairs = group * ((lc.rows + 15) / 16);   // per sequence
-    const int wgs = n_chunks * kv.n_kv * ln.n;
-    const int want = (512 + wgs - 1) / wgs;
-    int n_groups = std::max(1, std::min((pairs + 3) / 4, want));
-    const int ppg = (pairs + n_groups - 1) / n_groups;
-    n_groups = (pairs + ppg - 1) / ppg;
-    AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, ppg, scale * 1.4426950408889634f,
-               opart, mlpart, ln, n_groups};
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv, n_groups * ln.n), dim3(256), 0, st, a);
+    if (lc.rows < 48) {
+      // few rows per sequence (a static tree's verify, every draft pass):
+      // one workgroup per (64-key chunk, KV head) so every chunk's loads go
+      // out at once -- these launches are bound by memory latency, and a
+      // walk over several chunks per workgroup measured slower here; then
+      // the chunk combine. Split a head's (query head, row block) pairs over
+      // more workgroups only while the grid is short of two workgroups per
+      // CU: every extra group stages the chunk again.
+      const int pairs = group * ((lc.rows + 15) / 16);   // per sequence
+      const int wgs = n_chunks * kv.n_kv * ln.n;
+      const int want = (512 + wgs - 1) / wgs;
+      int n_groups = std::max(1, std::min((pairs + 3) / 4, want));
+      const int ppg = (pairs + n_groups - 1) / n_groups;
+      n_groups = (pairs + ppg - 1) / ppg;
+      AttnArgs a{(const bf16_t*)q, qlo, kv, vis, M, nq, group, ppg, scale * 1.4426950408889634f,
+                 opart, mlpart, ln, n_groups};
+      hipLaunchKernelGGL(attn_bf16_kernel, dim3(n_chunks, kv.n_kv, n_groups * ln.n), dim3(256), 0,
+                         st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(M, nq), dim3(128), 0, st, opart, mlpart,
+                         lc, M, nq, d, (bf16_t*)out_t, olo);
+      return hipGetLastError();
+    }
+    // many rows per sequence (dynamic-tree verify passes): the split form.
+    // Query rows of a KV head packed into 16-row tiles, up to four tiles per
+    // row group (balanced; one per wave slot), and each sequence's key chunks
+    // split so the grid holds at most 256 workgroups (the kernel runs one per
+    // CU: a 257th would wait for a second round), at least two chunks per
+    // split. Scores are taken in log2 units (scale * log2 e) so the softmax
+    // uses the native exp2; maxima in mlpart are in the same units.
+    const int ntile = (group * lc.rows + 15) / 16;
+    const int rg = (ntile + 3) / 4, tpg = (ntile + rg - 1) / rg;
+    const int units = kv.n_kv * rg;
+    SplitArgs sa{(const bf16_t*)q, qlo, kv, vis, ln, M, nq, group, ntile, tpg, rg, 1, {},
+                 scale * 1.4426950408889634f, (bf16_t*)out_t, olo, opart, mlpart};
+    for (int b = 0; b < ln.n; ++b) {
+      const int want = 256 / units;   // one 512-thread workgroup per CU
+      sa.splits[b] = std::max(1, std::min(want, lc.chunks[b] / 2));
+      lc.chunks[b] = sa.splits[b];
+      sa.smax = std::max(sa.smax, sa.splits[b]);
+    }
+    const dim3 grid(kv.n_kv * sa.smax * rg, 1, ln.n);
+    hipLaunchKernelGGL(attn_split_kernel<1>, grid, dim3(512), 0, st, sa);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || sa.smax == 1) return e;
     hipLaunchKernelGGL(attn_combine_kernel<bf16_t>, dim3(M, nq), dim3(128), 0, st, opart, mlpart,
                        lc, M, nq, d, (bf16_t*)out_t, olo);
   } else {
