@@ -132,6 +132,10 @@ typedef struct eagle_sizes {
   int32_t verify_rows;     /* 1 + kept nodes */
   int32_t max_nodes;       /* generated nodes per cycle */
   int32_t kv_page;         /* slots per KV page */
+  int32_t ctx_headroom;    /* KV slots a generation needs beyond its tokens:
+                              max_ctx must be >= prompt + generated +
+                              ctx_headroom (the draft depth: the last cycle
+                              may commit depth + 1 tokens) */
 } eagle_sizes;
 
 /* Weight tensor kinds (one table entry each). */
@@ -201,14 +205,22 @@ typedef struct eagle_stats {
 typedef struct eagle_ctx eagle_ctx;
 
 /* Sizes of the three device buffers for `cfg`; validates `cfg`.
- * Pure host call. EAGLE_E_INVALID on a bad config. */
+ * The configuration carries the options the pages name for a serving
+ * engine: branches per level (topk), draft steps (depth) and verified draft
+ * tokens (budget) -- "05 - EAGLE 三代", section 3 (the engine's three
+ * options); "Lesson 13.11", section "How EAGLE lives on today" (load the
+ * target and a small draft head, set the number of draft steps and the tree
+ * size). Pure host call. EAGLE_E_INVALID on a bad config. */
 eagle_status eagle_query(const eagle_config* cfg, eagle_sizes* out);
 
 /* Entry `index` (0 <= index < n_tensors) of the weight table of `cfg`.
  * Pure host call. The caller writes each tensor at its offset. */
 eagle_status eagle_tensor_info(const eagle_config* cfg, int32_t index, eagle_tensor* out);
 
-/* Creates a context over caller-owned buffers (sizes >= eagle_query's) on
+/* Loads the target and the draft head ("Lesson 13.11", section "How EAGLE
+ * lives on today"; the draft shares the target's embedding and frozen LM
+ * head: section "The big idea: draft at the feature level").
+ * Creates a context over caller-owned buffers (sizes >= eagle_query's) on
  * HIP stream `hip_stream` (NULL = the default stream). The weights must be
  * in place, in the row-major layout of eagle_tensor, before this call: for
  * EAGLE_BF16 it rewrites every matrix except the embedding, in place, into
@@ -222,7 +234,11 @@ eagle_status eagle_tensor_info(const eagle_config* cfg, int32_t index, eagle_ten
 eagle_status eagle_load(const eagle_config* cfg, const eagle_buffers* bufs, void* hip_stream,
                         eagle_ctx** out);
 
-/* Starts a sequence in lane 0: target prefill over prompt[0..n), the first
+/* Prefill: the target's pass over the prompt gives the features f and the
+ * first token; the draft then runs over the (f_j, t_{j+1}) pairs with the
+ * token shifted by one ("Lesson 13.11", section "Resolving the uncertainty
+ * by feeding back the token"; "05 - EAGLE 三代", section 2.3).
+ * Starts a sequence in lane 0: target prefill over prompt[0..n), the first
  * committed token b = greedy choice after the prompt (sampled when
  * temperature > 0), and the draft's catch-up over the n (feature,
  * next-token) pairs, which leaves the depth-1 candidates ready. Resets any
@@ -235,14 +251,27 @@ eagle_status eagle_prefill(eagle_ctx* ctx, const int32_t* prompt, int32_t n,
 eagle_status eagle_prefill_lane(eagle_ctx* ctx, int32_t lane, const int32_t* prompt, int32_t n,
                                 int32_t* first_token);
 
-/* Runs the draft passes and the rerank of one cycle for every lane (each
+/* Draft: grow the tree by path value, expand the best k newest nodes per
+ * step, rerank everything generated to the best m and flatten it with an
+ * ancestry mask ("EAGLE-2: Context-Aware Dynamic Draft Trees", sections
+ * "Path Value Ranks Prefixes, Not Isolated Tokens", "Global Reranking
+ * Separates Exploration from Verification", "The Mask Preserves Tree
+ * Semantics in One Target Pass"; a static tree when the config says so:
+ * "Lesson 13.11", section "EAGLE-2 and dynamic draft trees").
+ * Runs the draft passes and the rerank of one cycle for every lane (each
  * lane READY -> DRAFTED). If `out` is not NULL the call synchronises and
  * fills it with lane 0's tree. */
 eagle_status eagle_draft_tree(eagle_ctx* ctx, eagle_tree* out);
 /* Copies lane `lane`'s drafted tree (state DRAFTED) to `out`. Synchronises. */
 eagle_status eagle_read_tree(eagle_ctx* ctx, int32_t lane, eagle_tree* out);
 
-/* Verifies the drafted tree (state DRAFTED), or `planted` when not NULL
+/* Verify: one target pass over the flattened tree, accept from the root
+ * while the drafted token equals the target's greedy choice, add the
+ * target's own token, and carry the accepted path's KV and features into
+ * the next cycle ("Lesson 13.11", section "Speculative decoding in four
+ * moves"; "EAGLE-2: Context-Aware Dynamic Draft Trees", section "Putting It
+ * Together": verifier, next verified state).
+ * Verifies the drafted tree (state DRAFTED), or `planted` when not NULL
  * (state READY or DRAFTED; only n_rows, token and parent are read, rows must
  * be in order with parent[r] < r, siblings with distinct tokens, n_rows <=
  * 1 + budget, depth <= the config depth; token[0] is ignored and taken as
@@ -263,7 +292,11 @@ eagle_status eagle_verify(eagle_ctx* ctx, const eagle_tree* planted, int32_t* ou
  * (EAGLE_E_STATE when batch > 1), and so is eagle_generate. */
 eagle_status eagle_verify_batch(eagle_ctx* ctx, int32_t* out_tokens, int32_t* n_committed);
 
-/* eagle_prefill, then cycles until at least max_new tokens are committed
+/* Generate: the draft-verify loop until max_new tokens, whose output equals
+ * plain greedy decoding of the target ("Lesson 13.11", sections "Speculative
+ * decoding in four moves" and "The big idea"; budget 0 is plain decoding,
+ * one token per target pass: the measurement baseline).
+ * eagle_prefill, then cycles until at least max_new tokens are committed
  * (the prefill's token is the first); writes exactly max_new tokens to out
  * (capacity max_new) and their count to n_out. stats may be NULL. */
 eagle_status eagle_generate(eagle_ctx* ctx, const int32_t* prompt, int32_t n, int32_t max_new,

@@ -40,7 +40,8 @@ class Config(ctypes.Structure):
 
 class Sizes(ctypes.Structure):
     _fields_ = [("weight_bytes", u64), ("kv_bytes", u64), ("scratch_bytes", u64),
-                ("n_tensors", i32), ("verify_rows", i32), ("max_nodes", i32), ("kv_page", i32)]
+                ("n_tensors", i32), ("verify_rows", i32), ("max_nodes", i32), ("kv_page", i32),
+                ("ctx_headroom", i32)]
 
 
 class Tensor(ctypes.Structure):

@@ -832,6 +832,7 @@ eagle_status eagle_query(const eagle_config* cfg, eagle_sizes* out) {
   out->verify_rows = z.Mv;
   out->max_nodes = z.n_nodes_max;
   out->kv_page = KV_PAGE;
+  out->ctx_headroom = z.D;
   return EAGLE_OK;
 }
 
