@@ -107,15 +107,13 @@ uint64_t eagle_op_attention_workspace(int32_t dtype, int32_t M, int32_t n_heads,
  * section "The Mask Preserves Tree Semantics in One Target Pass": each
  * flattened row sees the context, its ancestors and itself), and the causal
  * attention of prefill rows when there are no tree keys.
- *   q: [M, n_heads * head_dim] query operand after RoPE: for EAGLE_BF16 two
- *      IEEE half (fp16) planes, hi = f16(q) then lo = f16(q - hi); for
- *      EAGLE_F32 one fp32 array.
- *   kv: the cache; key slot s of KV head h, plane p (0 = K, 1 = V), element
- *      i lives at
- *        page_table[s / 64] * (2 * n_kv_heads * 64 * head_dim)
+ *   q: [M, n_heads * head_dim] query operand after RoPE (bf16: hi plane then
+ *      lo plane, see above; fp32: one array).
+ *   kv: the cache; key slot s of KV head h, plane p, element i lives at
+ *      page_table[s / 64] * (planes * n_kv_heads * 64 * head_dim)
  *        + ((p * n_kv_heads + h) * 64 + s % 64) * head_dim + i
- *      with elements in IEEE half (EAGLE_BF16) or fp32 (EAGLE_F32).
- *      page_table: device int32 [key_end / 64 rounded up].
+ *      with planes K_hi, K_lo, V_hi, V_lo (bf16 raw bits; value = hi + lo) or
+ *      K, V (fp32). page_table: device int32 [key_end / 64 rounded up].
  *   Row r sees key slots [pre_lo, prehi[r]) and the tree slots tree_base + j
  *   (j < n_tree <= 128) whose bit j is set in tree_mask[2r] (j < 64) or
  *   tree_mask[2r + 1] (j >= 64); key_end = one past the last slot any row
@@ -123,8 +121,7 @@ uint64_t eagle_op_attention_workspace(int32_t dtype, int32_t M, int32_t n_heads,
  *   (tree_mask is read for every row: all zero when n_tree = 0). Query head j reads KV head
  *   j / (n_heads / n_kv_heads) (GQA).
  *   out: [M, n_heads * head_dim] softmax(q k^T * scale) v over the visible
- *      keys, as the next projection's operand (EAGLE_BF16: bf16 hi and lo
- *      planes as above; EAGLE_F32: one array).
+ *      keys, as an operand (bf16: hi and lo planes; fp32: one array).
  * page_table has one entry per 64 slots up to key_end (rounded up), each a
  * page index inside kv: the kernels read whole 64-slot chunks, masked slots
  * included. Requires head_dim = 128 for EAGLE_BF16 (<= 256 for EAGLE_F32),

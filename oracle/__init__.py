@@ -12,15 +12,12 @@ in fp64 and rounding at the points fixed by the numerics contract:
   activations, q/k/v, attention output, SwiGLU product, residual stream,
   features, logits, log-probabilities);
 * bf16 configs store the weights (embedding and LM head included) in bf16
-  (round-to-nearest-even of the generated fp32 value) and the K/V cache in
-  IEEE half (fp16: the cache's 2 bytes per element with 11 significant
-  bits); activations stay fp32. Rounding activations to bf16 would make any
+  (round-to-nearest-even of the generated fp32 value); activations and the
+  K/V cache stay fp32. Rounding activations or K/V to bf16 would make any
   two implementations that sum in different orders drift apart to the bf16
   noise floor within a few layers (a rounding flip moves the next layer's
   values by far more than the accumulation difference that caused it), so
-  it is not part of the contract. Both sides round the same fp32 K/V value
-  to fp16, so the cache itself adds no disagreement beyond rare last-bit
-  flips at rounding boundaries.
+  it is not part of the contract.
 
 Sources (web pages on EAGLE, EAGLE-2 and EAGLE-3):
   [L13] "Lesson 13.11 - EAGLE: Feature-Level Drafting for Faster Inference"

@@ -27,17 +27,9 @@ def operand(x, dtype: str):
     return to_f32(x)
 
 
-def to_f16(x):
-    """Round to fp32, then to IEEE binary16 (round-to-nearest-even; 11
-    significant bits, largest finite value 65504)."""
-    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float16).astype(np.float64)
-
-
 def kv_store(x, dtype: str):
-    """K and V as written to the cache: fp32 values for fp32 configs; for
-    bf16 configs IEEE half, 2 bytes per element like a bf16 cache but with
-    11 significant bits instead of 8."""
-    return to_f16(x) if dtype == "bf16" else to_f32(x)
+    """K and V as written to the cache: fp32 for both dtypes."""
+    return to_f32(x)
 
 
 def rmsnorm(h, gain, eps: float):

@@ -2,16 +2,14 @@
 // per-row kernels around it (embedding, RMSNorm, RoPE + KV append, draft
 // input assembly, row gathers, KV compaction).
 //
-// bf16 configs keep the K/V cache in IEEE half (fp16, 2 bytes per element,
-// 11 significant bits). Their attention (head_dim 128) has three forms, all
-// with the same per-block arithmetic: per 32-key block a wave computes
-// S^T = K Q^T and O^T += V^T P^T on 16x16x32 fp16 MFMA; keys are read in an
-// order that makes each lane's 8 scores exactly the P^T operand of the PV
-// product, so P never leaves registers. Q and P are carried as fp16 hi + lo
-// parts (two products each, against the single fp16 K or V), which keeps
-// ~22 significant bits where the lo part is a normal number. A chunk's K
-// (XOR-swizzled rows) and V^T are staged in LDS once and shared by every
-// query row of the KV head that reads it.
+// bf16 attention (head_dim 128) has three forms, all with the same per-block
+// arithmetic: per 32-key block a wave computes S^T = K Q^T and O^T += V^T P^T
+// on 16x16x32 bf16 MFMA; keys are read in an order that makes each lane's 8
+// scores exactly the P^T operand of the PV product, so P never leaves
+// registers. Q, K, V and P are carried as bf16 hi + lo parts (three
+// products; lo*lo dropped), which keeps ~16 mantissa bits. A chunk's K (hi
+// and lo planes, XOR-swizzled rows) and V^T (hi and lo) are staged in LDS
+// once and shared by every query row of the KV head that reads it.
 //  - attn_bf16_kernel: one workgroup of four waves per (64-key chunk, KV
 //    head, group of (query head, 16-row block) pairs); every chunk's loads
 //    go out at once, each chunk leaves a (max, sum, O) partial per row and
@@ -49,21 +47,11 @@ template <> struct KVStore<float> {
     kv_ptr<float>(v, slot, which, h)[i] = x;
   }
 };
-template <> struct KVStore<bf16_t> {   // bf16 configs: IEEE half planes
+template <> struct KVStore<bf16_t> {
   __device__ static void put(const KVView& v, int slot, int which, int h, int i, float x) {
-    kv_ptr<f16_t>(v, slot, which, h)[i] = f32_to_f16(x);
-  }
-};
-
-// The query operand of attention: one fp32 array (fp32 configs) or fp16 hi +
-// lo planes (bf16 configs, multiplied with the fp16 K cache).
-template <typename T> struct QStore;
-template <> struct QStore<float> {
-  __device__ static void store(float* p, int64_t, int64_t i, float v) { p[i] = v; }
-};
-template <> struct QStore<bf16_t> {
-  __device__ static void store(bf16_t* p, int64_t lo, int64_t i, float v) {
-    f16_split_store((f16_t*)p, lo, i, v);
+    const bf16_t hi = f32_to_bf16(x);
+    kv_ptr<bf16_t>(v, slot, 2 * which, h)[i] = hi;
+    kv_ptr<bf16_t>(v, slot, 2 * which + 1, h)[i] = f32_to_bf16(x - bf16_to_f32(hi));
   }
 };
 
@@ -135,12 +123,8 @@ __device__ __forceinline__ int k_swz(int key) { return (key & 3) | ((key >> 1) &
 
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   constexpr int D = 128, CK = CHUNK, VP = CK + 8;   // V^T row pitch (elements)
-  // K [key][16-byte column ^ swz] and V^T [d][key] (fp16), reused by the
-  // key-group merge at the end
-  constexpr int KSB = CK * 16 * 16, VTB = D * VP * 2, MOB = 4 * 16 * D * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[KSB + VTB > MOB + 512 ? KSB + VTB : MOB + 512];
-  uint4 (*ks)[16] = reinterpret_cast<uint4 (*)[16]>(smem);
-  f16_t (*vt)[VP] = reinterpret_cast<f16_t (*)[VP]>(smem + KSB);
+  __shared__ uint4 ks[2][CK][16];                  // K hi/lo: [key][16-byte column ^ swz]
+  __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];   // V^T hi/lo
   const int chunk = blockIdx.x, hk = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
@@ -156,7 +140,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   // ---- stage the chunk (keys past k1 repeat the last key; they are masked).
   // Every load of this thread is issued before the first LDS store, so the
   // workgroup waits for one memory latency instead of one per piece.
-  static_assert(CK * 16 == 4 * 256 && (CK / 2) * 16 == 2 * 256, "staging assumes 256 threads");
+  static_assert(2 * CK * 16 == 8 * 256 && 2 * (CK / 2) * 16 == 4 * 256, "staging assumes 256 threads");
   // A chunk spans at most two KV pages (the launcher checks page >= CHUNK):
   // both page-table entries are read once, up front, so no KV address waits
   // on a per-element table load.
@@ -198,36 +182,36 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     mk1 = vis.mask[2 * rowc + 1];
   };
   if (active) load_pair(pr0);
-  uint4 kr[4], va[2], vb[2];
+  uint4 kr[8], va[4], vb[4];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < 8; ++it) {
     const int i = tid + 256 * it;
-    const int key = i / 16, c = i % 16;
-    kr[it] = ld16(kvp(min(k0 + key, k1 - 1), 0) + 8 * c);
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int i = tid + 256 * it;
-    const int kp = i % (CK / 2), c = i / (CK / 2);
-    va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 1) + 8 * c);
-    vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 1) + 8 * c);
+    const int plane = i / (CK * 16), key = (i / 16) % CK, c = i % 16;
+    kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c);
   }
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int i = tid + 256 * it;
-    const int key = i / 16, c = i % 16;
-    ks[key][c ^ k_swz(key)] = kr[it];
+    const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
+    va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c);
+    vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c);
   }
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
+  for (int it = 0; it < 8; ++it) {
     const int i = tid + 256 * it;
-    const int kp = i % (CK / 2), c = i / (CK / 2);
+    const int plane = i / (CK * 16), key = (i / 16) % CK, c = i % 16;
+    ks[plane][key][c ^ k_swz(key)] = kr[it];
+  }
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int i = tid + 256 * it;
+    const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
     const uint32_t wa[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
     const uint32_t wb[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
-      *reinterpret_cast<uint32_t*>(&vt[8 * c + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
-      *reinterpret_cast<uint32_t*>(&vt[8 * c + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&vt[plane][8 * c + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
+      *reinterpret_cast<uint32_t*>(&vt[plane][8 * c + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
     }
   }
   __syncthreads();
@@ -251,10 +235,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
         const int sw = k_swz(key);
         sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {  // K (Q_hi + Q_lo)
-          const uint4 kf = ks[key][(4 * s + g) ^ sw];
-          mma_f16(kf, qf[s], sc[hh]);
-          mma_f16(kf, ql[s], sc[hh]);
+        for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+          const uint4 kf = ks[0][key][(4 * s + g) ^ sw];
+          const uint4 kl = ks[1][key][(4 * s + g) ^ sw];
+          Mma<bf16_t>::mma(kf, qf[s], sc[hh]);
+          Mma<bf16_t>::mma(kf, ql[s], sc[hh]);
+          Mma<bf16_t>::mma(kl, qf[s], sc[hh]);
         }
       }
       float p[8];
@@ -301,16 +287,18 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        ph[j] = pack_f16x2(p[2 * j], p[2 * j + 1]);
-        pl[j] = pack_f16x2(p[2 * j] - f16_lo_f(ph[j]), p[2 * j + 1] - f16_hi_f(ph[j]));
+        ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
       }
       const uint4 phi = uint4{ph[0], ph[1], ph[2], ph[3]};
       const uint4 plo = uint4{pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {  // V (P_hi + P_lo)
-        const uint4 va = *reinterpret_cast<const uint4*>(&vt[16 * dt + lr][kb0 + 8 * g]);
-        mma_f16(va, phi, o[dt]);
-        mma_f16(va, plo, o[dt]);
+      for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+        const uint4 va = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
+        const uint4 val = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
+        Mma<bf16_t>::mma(va, phi, o[dt]);
+        Mma<bf16_t>::mma(va, plo, o[dt]);
+        Mma<bf16_t>::mma(val, phi, o[dt]);
       }
     }
     if (kw == 1) {
@@ -337,8 +325,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
 
   // ---- merge the key groups of each pair through LDS (reuses the K area)
   __syncthreads();
-  float* mo = reinterpret_cast<float*>(smem);            // [wave][16 rows][128]
-  float* mm = reinterpret_cast<float*>(smem + MOB);      // [wave][16 rows][2]
+  float* mo = reinterpret_cast<float*>(&ks[0][0][0]);     // [wave][16 rows][128]
+  float* mm = reinterpret_cast<float*>(&vt[0][0][0]);     // [wave][16 rows][2]
+  static_assert(4 * 16 * D * 4 <= (int)sizeof(ks), "merge buffer must fit");
   if (pair_keep >= 0) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -411,12 +400,8 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
   // chunk (32 of its 64 keys), so two waves share each SIMD; the halves keep
   // their own running (max, sum, O) and are merged through LDS at the end.
   constexpr int D = 128, CK = CHUNK, VP = CK + 8, NT = 512;
-  // K [key][16-byte column ^ swz] and V^T [d][key] (fp16), reused by the
-  // key-half merge at the end
-  constexpr int KSB = CK * 16 * 16, VTB = D * VP * 2, MOB = 4 * 16 * D * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[KSB + VTB > MOB + 512 ? KSB + VTB : MOB + 512];
-  uint4 (*ks)[16] = reinterpret_cast<uint4 (*)[16]>(smem);
-  f16_t (*vt)[VP] = reinterpret_cast<f16_t (*)[VP]>(smem + KSB);
+  __shared__ uint4 ks[2][CK][16];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];
   __shared__ int kend_sh;
   const RowVis& vis = a.vis;
   const KVView& kv = a.kv;
@@ -475,7 +460,7 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
   }
 
   const int pgsz = kv.page, psh = page_shift(kv);
-  uint4 kr[2], va[1], vb[1];
+  uint4 kr[4], va[2], vb[2];
   // loads of chunk c into registers (keys past the chunk's end repeat its
   // last key; they are masked); a chunk spans at most two KV pages
   auto load_chunk = [&](int c) {
@@ -488,32 +473,36 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
              ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
     };
 #pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
+    }
+#pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int i = tid + NT * it;
-      const int key = i / 16, c16 = i % 16;
-      kr[it] = ld16(kvp(min(k0 + key, k1 - 1), 0) + 8 * c16);
-    }
-    {
-      const int kp = tid % (CK / 2), c16 = tid / (CK / 2);
-      va[0] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 1) + 8 * c16);
-      vb[0] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 1) + 8 * c16);
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
+      vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
     }
   };
   auto store_chunk = [&]() {
 #pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      ks[plane][key][c16 ^ k_swz(key)] = kr[it];
+    }
+#pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int i = tid + NT * it;
-      const int key = i / 16, c16 = i % 16;
-      ks[key][c16 ^ k_swz(key)] = kr[it];
-    }
-    {
-      const int kp = tid % (CK / 2), c16 = tid / (CK / 2);
-      const uint32_t wa[4] = {va[0].x, va[0].y, va[0].z, va[0].w};
-      const uint32_t wb[4] = {vb[0].x, vb[0].y, vb[0].z, vb[0].w};
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      const uint32_t wa[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
+      const uint32_t wb[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
-        *reinterpret_cast<uint32_t*>(&vt[8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
-        *reinterpret_cast<uint32_t*>(&vt[8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
       }
     }
   };
@@ -534,17 +523,20 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
       // chains; each half's order is attn_bf16_kernel's)
       f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {  // K (Q_hi + Q_lo)
-        uint4 kf[2];
+      for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+        uint4 kf[2], kl[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
-          kf[hh] = ks[key][(4 * s + g) ^ k_swz(key)];
+          kf[hh] = ks[0][key][(4 * s + g) ^ k_swz(key)];
+          kl[hh] = ks[1][key][(4 * s + g) ^ k_swz(key)];
         }
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) mma_f16(kf[hh], qf[i][s], sc[hh]);
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], qf[i][s], sc[hh]);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) mma_f16(kf[hh], ql[i][s], sc[hh]);
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], ql[i][s], sc[hh]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kl[hh], qf[i][s], sc[hh]);
       }
       float p[8];
       float bm = -INFINITY;
@@ -589,16 +581,18 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        ph[j] = pack_f16x2(p[2 * j], p[2 * j + 1]);
-        pl[j] = pack_f16x2(p[2 * j] - f16_lo_f(ph[j]), p[2 * j + 1] - f16_hi_f(ph[j]));
+        ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
       }
       const uint4 phi = uint4{ph[0], ph[1], ph[2], ph[3]};
       const uint4 plo = uint4{pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {  // V (P_hi + P_lo)
-        const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[16 * dt + lr][kb0 + 8 * g]);
-        mma_f16(v0, phi, o[i][dt]);
-        mma_f16(v0, plo, o[i][dt]);
+      for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+        const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
+        Mma<bf16_t>::mma(v0, phi, o[i][dt]);
+        Mma<bf16_t>::mma(v0, plo, o[i][dt]);
+        Mma<bf16_t>::mma(v1, phi, o[i][dt]);
       }
     }
     __syncthreads();   // every wave is done with this chunk's LDS
@@ -609,8 +603,9 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
   }
   // merge the two key halves of each pair (the K area holds the second
   // half's O, the V area its max and sum), then write the normalized rows
-  float* mo = reinterpret_cast<float*>(smem);         // [slot][16 rows][128]
-  float* mm = reinterpret_cast<float*>(smem + MOB);   // [slot][16 rows][2]
+  float* mo = reinterpret_cast<float*>(&ks[0][0][0]);   // [slot][16 rows][128]
+  float* mm = reinterpret_cast<float*>(&vt[0][0][0]);   // [slot][16 rows][2]
+  static_assert(4 * 16 * D * 4 <= (int)sizeof(ks), "merge buffer must fit");
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const int p = slot + 4 * i;
@@ -688,12 +683,8 @@ struct SplitArgs {
 template <int PW>
 __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
   constexpr int D = 128, CK = CHUNK, VP = CK + 8, NT = 512;
-  // K [key][16-byte column ^ swz] and V^T [d][key] (fp16), reused by the
-  // key-half merge at the end
-  constexpr int KSB = CK * 16 * 16, VTB = D * VP * 2, MOB = 4 * 16 * D * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[KSB + VTB > MOB + 512 ? KSB + VTB : MOB + 512];
-  uint4 (*ks)[16] = reinterpret_cast<uint4 (*)[16]>(smem);
-  f16_t (*vt)[VP] = reinterpret_cast<f16_t (*)[VP]>(smem + KSB);
+  __shared__ uint4 ks[2][CK][16];
+  __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];
   const int seq = blockIdx.z;
   int S = 1;
 #pragma unroll
@@ -727,7 +718,7 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
   // chunk staging (keys past the chunk's end repeat its last key; they are
   // masked); a chunk spans at most two KV pages
   const int pgsz = kv.page, psh = page_shift(kv);
-  struct Stage { uint4 kr[2], va, vb; };
+  struct Stage { uint4 kr[4], va[2], vb[2]; };
   Stage st0, st1;
   auto load_chunk = [&](int c, Stage& sg) {
     const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
@@ -739,29 +730,37 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
              ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
     };
 #pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      sg.kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
+    }
+#pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int i = tid + NT * it;
-      const int key = i / 16, c16 = i % 16;
-      sg.kr[it] = ld16(kvp(min(k0 + key, k1 - 1), 0) + 8 * c16);
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      sg.va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
+      sg.vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
     }
-    const int kp = tid % (CK / 2), c16 = tid / (CK / 2);
-    sg.va = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 1) + 8 * c16);
-    sg.vb = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 1) + 8 * c16);
   };
   auto store_chunk = [&](const Stage& sg) {
 #pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int i = tid + NT * it;
+      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
+      ks[plane][key][c16 ^ k_swz(key)] = sg.kr[it];
+    }
+#pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int i = tid + NT * it;
-      const int key = i / 16, c16 = i % 16;
-      ks[key][c16 ^ k_swz(key)] = sg.kr[it];
-    }
-    const int kp = tid % (CK / 2), c16 = tid / (CK / 2);
-    const uint32_t wa[4] = {sg.va.x, sg.va.y, sg.va.z, sg.va.w};
-    const uint32_t wb[4] = {sg.vb.x, sg.vb.y, sg.vb.z, sg.vb.w};
+      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
+      const uint32_t wa[4] = {sg.va[it].x, sg.va[it].y, sg.va[it].z, sg.va[it].w};
+      const uint32_t wb[4] = {sg.vb[it].x, sg.vb[it].y, sg.vb[it].z, sg.vb[it].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
-      *reinterpret_cast<uint32_t*>(&vt[8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
-      *reinterpret_cast<uint32_t*>(&vt[8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
+      for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
+        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
+      }
     }
   };
   uint4 qf[PW][4], ql[PW][4];
@@ -811,20 +810,23 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
 #pragma unroll
     for (int i = 0; i < PW; ++i) sc[i][0] = sc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {  // K (Q_hi + Q_lo)
-      uint4 kf[2];
+    for (int s = 0; s < 4; ++s) {  // (K_hi + K_lo)(Q_hi + Q_lo), lo*lo dropped
+      uint4 kf[2], kl[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
-        kf[hh] = ks[key][(4 * s + g) ^ k_swz(key)];
+        kf[hh] = ks[0][key][(4 * s + g) ^ k_swz(key)];
+        kl[hh] = ks[1][key][(4 * s + g) ^ k_swz(key)];
       }
 #pragma unroll
       for (int i = 0; i < PW; ++i) {
         if (slot + 4 * i >= ntg) continue;   // uniform over the wave
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) mma_f16(kf[hh], qf[i][s], sc[i][hh]);
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], qf[i][s], sc[i][hh]);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) mma_f16(kf[hh], ql[i][s], sc[i][hh]);
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kf[hh], ql[i][s], sc[i][hh]);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) Mma<bf16_t>::mma(kl[hh], qf[i][s], sc[i][hh]);
       }
     }
     uint4 phi[PW], plo[PW];
@@ -876,20 +878,22 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        ph[j] = pack_f16x2(p[2 * j], p[2 * j + 1]);
-        pl[j] = pack_f16x2(p[2 * j] - f16_lo_f(ph[j]), p[2 * j + 1] - f16_hi_f(ph[j]));
+        ph[j] = pack_bf16x2(p[2 * j], p[2 * j + 1]);
+        pl[j] = pack_bf16x2(p[2 * j] - bf16_lo_f(ph[j]), p[2 * j + 1] - bf16_hi_f(ph[j]));
       }
       phi[i] = uint4{ph[0], ph[1], ph[2], ph[3]};
       plo[i] = uint4{pl[0], pl[1], pl[2], pl[3]};
     }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {  // V (P_hi + P_lo)
-      const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[16 * dt + lr][kb0 + 8 * g]);
+    for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
+      const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
+      const uint4 v1 = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
 #pragma unroll
       for (int i = 0; i < PW; ++i) {
         if (slot + 4 * i >= ntg) continue;
-        mma_f16(v0, phi[i], o[i][dt]);
-        mma_f16(v0, plo[i], o[i][dt]);
+        Mma<bf16_t>::mma(v0, phi[i], o[i][dt]);
+        Mma<bf16_t>::mma(v0, plo[i], o[i][dt]);
+        Mma<bf16_t>::mma(v1, phi[i], o[i][dt]);
       }
     }
   };
@@ -916,8 +920,9 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
   }
   // merge the two key halves of each tile (the K area holds the second
   // half's O, the V area its max and sum), then write the rows
-  float* mo = reinterpret_cast<float*>(smem);         // [slot][16 rows][128]
-  float* mm = reinterpret_cast<float*>(smem + MOB);   // [slot][16 rows][2]
+  float* mo = reinterpret_cast<float*>(&ks[0][0][0]);   // [slot][16 rows][128]
+  float* mm = reinterpret_cast<float*>(&vt[0][0][0]);   // [slot][16 rows][2]
+  static_assert(4 * 16 * D * 4 <= (int)sizeof(ks), "merge buffer must fit");
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
     const bool has = slot + 4 * i < ntg;   // uniform over the wave
@@ -1228,8 +1233,8 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
       const float y2 = x2 * c[i] + x1 * s[i];
       if (head < nq) {
         const int64_t base = ((int64_t)r * nq + head) * d;
-        QStore<T>::store(q_out, qlo, base + i, y1);
-        QStore<T>::store(q_out, qlo, base + i + half, y2);
+        Opnd<T>::store(q_out, qlo, base + i, y1);
+        Opnd<T>::store(q_out, qlo, base + i + half, y2);
       } else {
         KVStore<T>::put(kv, sl, 0, head - nq, i, y1);
         KVStore<T>::put(kv, sl, 0, head - nq, i + half, y2);
@@ -1620,7 +1625,7 @@ hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int 
   if (kv_page_bad(layer0)) return hipErrorInvalidValue;
   if (ln.n < 1 || ln.n > MAX_LANES) return hipErrorInvalidValue;
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv, ln.n), dim3(256), 0, st, layer0, layer_elems, L, path, ctx, 2, ln),
+              hipLaunchKernelGGL(kv_compact_kernel<bf16_t>, dim3(n_layers, layer0.n_kv, ln.n), dim3(512), 0, st, layer0, layer_elems, L, path, ctx, 4, ln),
               hipLaunchKernelGGL(kv_compact_kernel<float>, dim3(n_layers, layer0.n_kv, ln.n), dim3(256), 0, st, layer0, layer_elems, L, path, ctx, 2, ln));
   return hipGetLastError();
 }

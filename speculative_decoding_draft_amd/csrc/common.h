@@ -31,35 +31,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo_f(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_f(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// IEEE half (fp16): the K/V cache of bf16 configs and the attention
-// operands multiplied with it. Conversions round to nearest even
-// (v_cvt_f16_f32 in the default rounding mode).
-typedef uint16_t f16_t;                        // raw binary16 bits
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2_hw __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ f16_t f32_to_f16(float f) { return __builtin_bit_cast(f16_t, (_Float16)f); }
-__device__ __forceinline__ float f16_to_f32(f16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-// Two values in one 32-bit word, element a in the low half.
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  const f16x2_hw v = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ float f16_lo_f(uint32_t w) { return f16_to_f32((f16_t)(w & 0xffffu)); }
-__device__ __forceinline__ float f16_hi_f(uint32_t w) { return f16_to_f32((f16_t)(w >> 16)); }
-// A value as two fp16 parts, hi = f16(v), lo = f16(v - hi): ~22 significant
-// bits where lo stays a normal number (|v| above ~0.125), and an absolute
-// error below 2^-24 everywhere.
-__device__ __forceinline__ void f16_split_store(f16_t* p, int64_t lo, int64_t i, float v) {
-  const f16_t h = f32_to_f16(v);
-  p[i] = h;
-  p[lo + i] = f32_to_f16(v - f16_to_f32(h));
-}
-// 16x16x32 MFMA on fp16 operands (same lane layout as the bf16 one below).
-__device__ __forceinline__ void mma_f16(const uint4& a, const uint4& b, f32x4& c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                             __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
 // Element type T of weights / KV / matrix operands: float or bf16_t.
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -51,8 +51,9 @@ uint64_t lmhead_part_floats(int M, int V, int k);
 // One layer of a paged KV cache. Element (slot, plane, kv head h, i) lives at
 //   base + page_table[slot / page] * page_elems
 //        + ((plane * n_kv + h) * page + slot % page) * d + i
-// so each (page, plane, head) is a contiguous [page, d] tile, with planes K
-// and V: fp32 for fp32 configs, IEEE half (fp16) for bf16 configs.
+// so each (page, plane, head) is a contiguous [page, d] tile. fp32 caches
+// have planes K, V; bf16 caches keep each fp32 value as a hi + lo pair with
+// planes K_hi, K_lo, V_hi, V_lo (16 significant bits).
 struct KVView {
   void* base;
   const int32_t* page_table;
@@ -60,7 +61,7 @@ struct KVView {
   int page, n_kv, d;
   int64_t lane_elems = 0;   // sequence b's cache starts b * lane_elems elements after base
 };
-inline int kv_planes(int) { return 2; }
+inline int kv_planes(int dtype) { return dtype == 1 ? 4 : 2; }
 
 // ---------------------------------------------------------------- rows
 // Attention visibility of row r: key slots [pre_lo, prehi[r]) plus the
@@ -116,8 +117,7 @@ hipError_t launch_resnorm(int dtype, float* h, int H, int M, const float* part, 
 hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int W, float* dst,
                              int add, hipStream_t st);
 // RoPE on q and k and append of k, v to the cache; qkv = sum of S partial
-// planes [M, (nq + 2 nkv) d]. q_out is attention's query operand: fp32, or
-// for bf16 configs two fp16 planes (hi, lo = f16(q - hi), lo at q_out + qlo).
+// planes [M, (nq + 2 nkv) d].
 hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int M, int nq, int nkv,
                           int d, const int32_t* pos, const int32_t* slot, const float* cos_t,
                           const float* sin_t, void* q_out, int64_t qlo, KVView kv, hipStream_t st,

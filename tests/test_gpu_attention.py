@@ -6,8 +6,8 @@ chunk after a 3072-key prefix, draft-style rows (keys from slot 1, a few tree
 keys), ragged context lengths, and the fp32 kernel.
 
 Inputs are seeded; K/V go through a shuffled page table. The oracle gets the
-exact values the kernels see (for bf16 configs the fp16 K/V cache values and
-the fp16 hi + lo query planes, summed in fp64) and computes softmax(q k^T / sqrt(d)) v over each row's visible keys
+exact values the kernels see (for bf16 the hi + lo operand planes, summed in
+fp64) and computes softmax(q k^T / sqrt(d)) v over each row's visible keys
 ([E2] "The Mask Preserves Tree Semantics in One Target Pass": each row sees
 the context, its ancestors and itself)."""
 import math
@@ -24,20 +24,12 @@ BF16, F32 = 1, 0
 PAGE = 64
 
 
-def _kv_plane(x, dtype):
-    """(cache plane, exact fp64 value): fp32, or IEEE half for bf16 configs."""
+def _planes(x, dtype):
+    """(device operand planes, exact fp64 value) of an fp32 tensor."""
     if dtype == F32:
         return [x], x.double()
-    h = x.to(torch.float16)
-    return [h], h.double()
-
-
-def _q_planes(x, dtype):
-    """(query operand planes, exact fp64 value): fp32, or fp16 hi + lo."""
-    if dtype == F32:
-        return [x], x.double()
-    hi = x.to(torch.float16)
-    lo = (x - hi.float()).to(torch.float16)
+    hi = x.to(torch.bfloat16)
+    lo = (x - hi.float()).to(torch.bfloat16)
     return [hi, lo], hi.double() + lo.double()
 
 
@@ -63,9 +55,9 @@ def _run(dtype, nq, nkv, d, M, pre_lo, prehi, tree_base, n_tree, masks, key_end,
     q = torch.randn((M, nq, d), generator=gen) * 1.3
     K = torch.randn((key_end, nkv, d), generator=gen) * 1.3
     Vv = torch.randn((key_end, nkv, d), generator=gen)
-    qp, q64 = _q_planes(q, dtype)
-    kp, k64 = _kv_plane(K, dtype)
-    vp, v64 = _kv_plane(Vv, dtype)
+    qp, q64 = _planes(q, dtype)
+    kp, k64 = _planes(K, dtype)
+    vp, v64 = _planes(Vv, dtype)
     # paged cache: physical page perm[p] holds logical page p, planes K.., V..
     n_pages = (key_end + PAGE - 1) // PAGE
     perm = torch.randperm(n_pages, generator=gen)
@@ -81,8 +73,7 @@ def _run(dtype, nq, nkv, d, M, pre_lo, prehi, tree_base, n_tree, masks, key_end,
     kv = phys.contiguous().cuda()
     table = perm.to(torch.int32).cuda()
     qd = torch.cat([p.reshape(-1) for p in qp]).cuda()
-    out = torch.zeros(len(qp) * M * nq * d, dtype=torch.bfloat16 if dtype == BF16 else torch.float32,
-                      device="cuda")
+    out = torch.zeros(len(qp) * M * nq * d, dtype=qp[0].dtype, device="cuda")
     prehi_d = torch.tensor(prehi, dtype=torch.int32, device="cuda")
     if masks is None:
         masks = np.zeros((M, 2), dtype=np.uint64)
