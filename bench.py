@@ -356,7 +356,8 @@ def main():
         model = spm.report(t_draft, tv / n_model - t_draft, w["depth"])
     cycles_s = args.steps / dt
     tau = committed / args.steps / B
-    roof_key = (f"proj_kernel<{'bf16' if w['dtype'] == 'bf16' else 'f32'}, MT={mt}, EPI_PART> M={mv}")
+    roof_key = (f"proj_kernel<{'bf16' if w['dtype'] == 'bf16' else 'f32'}, MT={mt}, EPI_PART> "
+                f"M={mv} {args.config}")
     traffic = stored_traffic(roof_key)
     cps = [x["cycles_per_s"] for x in windows]
     out = {
