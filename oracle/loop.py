@@ -34,9 +34,13 @@ from . import tree as T
 class Session:
     """Oracle state for one sequence: target + draft KV, committed tokens.
     `lane` is the sequence's index in a batch; it only selects the stream of
-    random draws in sampling mode (oracle/sampling.py)."""
+    random draws in sampling mode (oracle/sampling.py). `follow`, in sampling
+    mode, is another implementation's committed stream: at a sampling
+    decision that is a near-tie (oracle/sampling.py) the session takes the
+    outcome that stream shows, and its own everywhere else."""
 
-    def __init__(self, w: dict, weights: Weights = None, max_new: int = None, lane: int = 0):
+    def __init__(self, w: dict, weights: Weights = None, max_new: int = None, lane: int = 0,
+                 follow=None):
         self.w = dict(w)
         self.cfg = Config(w)
         self.W = weights if weights is not None else Weights(self.cfg)
@@ -51,6 +55,8 @@ class Session:
         self.temperature = float(w.get("temperature", 0.0))
         self.seed = int(w.get("seed", 0))
         self.lane = int(lane)
+        self.follow = None if follow is None else [int(t) for t in follow]
+        self.sample_margins = []
         self.n_verify = 0
         self.history = []
 
@@ -88,7 +94,10 @@ class Session:
         b = int(g[0])
         self.n_verify = 0
         if self.temperature > 0:   # sampling mode: the prefill's token is draw step 0
-            b = SMP.sample_token(last[0], self.temperature, self.seed, 0, lane=self.lane)
+            want = self.follow[0] if self.follow else None
+            b, m = SMP.sample_token(last[0], self.temperature, self.seed, 0, lane=self.lane,
+                                    follow=want)
+            self.sample_margins = [m]
         self.prefill_margin = float(margin[0])
         self.tokens = prompt + [b]
         self.committed = [b]
@@ -173,8 +182,11 @@ class Session:
         g, margin = argmax_lowest(logits)
         self.n_verify += 1
         if self.temperature > 0:
-            path, bonus = SMP.accept_sample(rows["token"], rows["parent"], logits, self.temperature,
-                                            self.seed, self.n_verify, self.depth, lane=self.lane)
+            want = None if self.follow is None else self.follow[len(self.committed):]
+            path, bonus, m = SMP.walk(rows["token"], rows["parent"], logits, self.temperature,
+                                      self.seed, self.n_verify, self.depth, lane=self.lane,
+                                      follow=want)
+            self.sample_margins += m
         else:
             path, bonus = T.accept(rows["token"], rows["parent"], g)
         L = len(path)

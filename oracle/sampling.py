@@ -21,10 +21,10 @@ current row (softmax of logits / T) and S the mass not yet rejected at that
 row. A rejected candidate's token leaves the distribution (S -= p(x)). The
 children of a row are tried in row order. When every child is rejected, or
 the row has none, the token is drawn from p restricted to the tokens not
-rejected (renormalised by S). Taking x1 with probability p(x1), else x2 with
-p(x2) / (1 - p(x1)), ..., else the rest, gives every token probability
-exactly p, at every depth: the committed stream is distributed as plain
-sampling from the target.
+rejected, by inverting its cumulative distribution in token-id order.
+Taking x1 with probability p(x1), else x2 with p(x2) / (1 - p(x1)), ...,
+else the rest, gives every token probability exactly p, at every depth: the
+committed stream is distributed as plain sampling from the target.
 
 Random numbers: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
 random numbers: as easy as 1, 2, 3", SC'11), key = the 64-bit seed (low word
@@ -35,15 +35,20 @@ lane is the sequence's index when several sequences are served together (0
 for one). The pages speak of one sequence; the fourth counter word giving
 each sequence of a batch its own stream is this implementation's choice.
 
-Precision (the GPU takes these decisions in fp32, so the oracle takes them
-in the same precision): e(v) = exp((l(v) - max l) / T) in float32, Z = the
-float64 sum of e rounded to float32, p(v) = e(v) / Z in float32; the child
-test is u * S < p(x) with S in float32; the residual draw walks the tokens
-in id order accumulating e(v) in float64 and takes the first v whose running
-sum exceeds (u * S) * Z (the product u * S in float32, then times Z in
-float64), or the last token left with e(v) > 0 if rounding leaves the sum
-short. (In exact arithmetic this is the walk over p = e / Z with target
-u * S; counting in units of e spares a division per token.)
+Precision: everything here is float64 and follows the definitions above
+literally (p = exp(l / T - max) / sum, the test u * S < p(x), the residual
+target u * S against the running sum of p). An implementation that takes
+these decisions in float32 can only differ from them where the two compared
+quantities are closer than its rounding error. That error is bounded, in
+probability units, by about 2e-7 * (sum over v of p(v) * |l(v) - max| / T)
++ 4e-7: the float32 exponent argument and exp, the normalising sum and the
+product u * S. The sum is at most 2 ln V (the entropy plus ln Z), so the
+bound stays under 5.1e-6 for V <= 2^17. Every decision therefore carries a
+margin (the distance between its two compared quantities), and a decision
+whose margin is at most TIE = 1e-5, about twice that bound, is a near-tie:
+either outcome is correct there. The walk takes the oracle's own outcome
+unless it is told which outcome an implementation took (`follow`), in which
+case it takes that one at near-ties and its own everywhere else.
 """
 from __future__ import annotations
 
@@ -53,6 +58,7 @@ MASK32 = 0xFFFFFFFF
 PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57
 PHILOX_W0, PHILOX_W1 = 0x9E3779B9, 0xBB67AE85
 RESIDUAL_DRAW = 0xFFFF
+TIE = 1e-5
 
 
 def philox4x32(ctr, key, rounds: int = 10):
@@ -69,72 +75,131 @@ def philox4x32(ctr, key, rounds: int = 10):
     return c0, c1, c2, c3
 
 
-def uniform(seed: int, step: int, depth: int, draw: int, lane: int = 0) -> np.float32:
+def uniform(seed: int, step: int, depth: int, draw: int, lane: int = 0) -> float:
     """u in [0, 1) with 24 random bits, from the counter (step, depth, draw, lane)."""
     w = philox4x32((step, depth, draw, lane), (seed & MASK32, (seed >> 32) & MASK32))[0]
-    return np.float32((w >> 8) * (1.0 / 16777216.0))
+    return (w >> 8) * (1.0 / 16777216.0)
 
 
-def row_probs(logits_row, temperature: float):
-    """(e, Z): e(v) = exp((l(v) - max) / T) in float32 and Z = sum e (float64 sum, float32)."""
-    l = np.asarray(logits_row, dtype=np.float32)
-    inv_t = np.float32(1.0) / np.float32(temperature)
-    e = np.exp((l - l.max()) * inv_t).astype(np.float32)
-    z = np.float32(np.sum(e.astype(np.float64)))
-    return e, z
+def probs(logits_row, temperature: float) -> np.ndarray:
+    """p = softmax(logits / T), float64."""
+    x = np.asarray(logits_row, dtype=np.float64) / float(temperature)
+    e = np.exp(x - x.max())
+    return e / e.sum()
 
 
-def residual_draw(e, z, removed, S: np.float32, u: np.float32) -> int:
-    """Token drawn from p = e / Z restricted to tokens not in `removed`."""
-    t = float(np.float32(u * S)) * float(z)
-    keep = np.ones(len(e), dtype=bool)
+def residual_draw(p, removed, S: float, u: float):
+    """Token drawn from p restricted to the tokens not in `removed` (whose
+    mass is S): the first token, in id order, whose running sum of p exceeds
+    u * S. Returns (token, margin), the margin being the distance from u * S
+    to the nearer end of that token's interval. If rounding leaves the
+    running sum short of u * S, the last token left with p > 0 is taken,
+    with margin 0."""
+    t = u * S
+    keep = np.ones(len(p), dtype=bool)
     keep[list(removed)] = False
     cum = 0.0
     last = -1
-    for v in range(len(e)):
+    for v in range(len(p)):
         if not keep[v]:
             continue
-        if e[v] > 0:
+        if p[v] > 0:
             last = v
-        cum += float(e[v])
+        before = cum
+        cum += float(p[v])
         if cum > t:
-            return v
-    return last
+            return v, min(t - before, cum - t)
+    return last, 0.0
+
+
+def residual_interval(p, removed, v: int):
+    """[cum_before, cum_after) of token v in the restricted running sum."""
+    keep = np.ones(len(p), dtype=bool)
+    keep[list(removed)] = False
+    before = float(np.sum(p[:v][keep[:v]]))
+    return before, before + float(p[v])
+
+
+def _residual(p, removed, S, u, want):
+    """The residual draw, taking `want` instead where u * S lies within TIE of
+    want's interval (a near-tie with the oracle's own choice)."""
+    v, margin = residual_draw(p, removed, S, u)
+    if want is not None and want != v and 0 <= want < len(p) and want not in removed:
+        lo, hi = residual_interval(p, removed, want)
+        t = u * S
+        if lo - TIE <= t < hi + TIE and p[want] > 0:
+            return want, margin
+    return v, margin
 
 
 def sample_token(logits_row, temperature: float, seed: int, step: int, depth: int = 0,
-                 lane: int = 0) -> int:
-    """One token drawn from softmax(logits / T) (the prefill's token)."""
-    e, z = row_probs(logits_row, temperature)
-    return residual_draw(e, z, (), np.float32(1.0), uniform(seed, step, depth, RESIDUAL_DRAW, lane))
+                 lane: int = 0, follow: int = None):
+    """One token drawn from softmax(logits / T) (the prefill's token).
+    Returns (token, margin)."""
+    p = probs(logits_row, temperature)
+    return _residual(p, (), 1.0, uniform(seed, step, depth, RESIDUAL_DRAW, lane), follow)
+
+
+def walk(token_rows, parent_rows, logits, temperature: float, seed: int, step: int,
+         max_depth: int, lane: int = 0, follow=None):
+    """Sampling-mode acceptance walk over the verify rows.
+
+    logits[r] are the target's logits at verify row r. Returns (accepted rows
+    in order, the token drawn at the last row, margins), margins[d] being the
+    smallest margin of the decisions that chose committed token d (every
+    child test at that depth and the residual draw if one was made).
+
+    `follow` is another implementation's committed tokens for the same walk;
+    at a near-tie the walk takes the outcome those tokens show. Siblings
+    carry distinct tokens and a rejected token leaves the residual, so child
+    x was accepted exactly when the committed token at its depth is x.
+    """
+    n = len(token_rows)
+    cur, path, depth, margins = 0, [], 0, []
+    while True:
+        p = probs(logits[cur], temperature)
+        want = int(follow[depth]) if follow is not None and depth < len(follow) else None
+        S = 1.0
+        removed = []
+        children = [r for r in range(1, n) if parent_rows[r] == cur] if depth < max_depth else []
+        nxt, m_d = -1, np.inf
+        for j, r in enumerate(children):
+            x = int(token_rows[r])
+            us = uniform(seed, step, depth, j, lane) * S
+            m_d = min(m_d, abs(us - p[x]))
+            take = us < p[x]
+            if abs(us - p[x]) <= TIE and want is not None:
+                take = want == x
+            if take:
+                nxt = r
+                break
+            S -= p[x]
+            removed.append(x)
+        if nxt < 0:
+            v, m = _residual(p, removed, S, uniform(seed, step, depth, RESIDUAL_DRAW, lane), want)
+            margins.append(min(m_d, m))
+            return path, v, margins
+        margins.append(m_d)
+        path.append(nxt)
+        cur = nxt
+        depth += 1
 
 
 def accept_sample(token_rows, parent_rows, logits, temperature: float, seed: int, step: int,
                   max_depth: int, lane: int = 0):
-    """Sampling-mode acceptance walk over the verify rows.
+    """(accepted rows in order, the token drawn at the last row), like the
+    greedy walk."""
+    path, bonus, _ = walk(token_rows, parent_rows, logits, temperature, seed, step, max_depth, lane)
+    return path, bonus
 
-    logits[r] are the target's logits at verify row r. Returns (accepted rows
-    in order, the token drawn at the last row) like the greedy walk.
-    """
-    n = len(token_rows)
-    cur, path, depth = 0, [], 0
-    while True:
-        e, z = row_probs(logits[cur], temperature)
-        S = np.float32(1.0)
-        removed = []
-        children = [r for r in range(1, n) if parent_rows[r] == cur] if depth < max_depth else []
-        nxt = -1
-        for j, r in enumerate(children):
-            x = int(token_rows[r])
-            px = np.float32(e[x] / z)
-            if np.float32(uniform(seed, step, depth, j, lane) * S) < px:
-                nxt = r
-                break
-            S = np.float32(S - px)
-            removed.append(x)
-        if nxt < 0:
-            return path, residual_draw(e, z, removed, S,
-                                       uniform(seed, step, depth, RESIDUAL_DRAW, lane))
-        path.append(nxt)
-        cur = nxt
-        depth += 1
+
+def check_walk(got, token_rows, parent_rows, logits, temperature: float, seed: int, step: int,
+               max_depth: int, lane: int = 0):
+    """Whether `got` (another implementation's committed tokens for this walk)
+    is a correct outcome: equal to the oracle's walk, where every near-tie is
+    resolved as `got` resolves it. Returns (ok, the oracle's tokens, the
+    smallest decision margin on the walk)."""
+    path, bonus, margins = walk(token_rows, parent_rows, logits, temperature, seed, step,
+                                max_depth, lane, follow=list(got))
+    want = [int(token_rows[r]) for r in path] + [int(bonus)]
+    return [int(t) for t in got] == want, want, float(min(margins))

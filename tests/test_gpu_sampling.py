@@ -1,11 +1,15 @@
 """Sampling-mode (temperature > 0) verification on the GPU against the oracle
-(oracle/sampling.py):
+(oracle/sampling.py, float64 definitions):
 * the acceptance walk and the drawn token, taken from the GPU's own verify
-  logits, equal the oracle's decisions on the same logits (drafted trees,
+  logits, equal the oracle's decisions on the same logits, a decision whose
+  two compared quantities lie within the oracle's near-tie allowance (1e-5
+  in probability; the GPU decides in float32) counting as correct either
+  way (drafted trees,
   and planted trees built from the target's top tokens so that several
   depths are accepted), at c1 (fp32, V=1024) and the reduced c2 (bf16,
   V=32000);
-* the c1 stream equals the oracle session's stream with the same seed;
+* the c1 stream equals the oracle session's stream with the same seed
+  (near-ties again resolved as the GPU resolved them);
 * losslessness on the device: over many seeds the prefill's token and the
   first committed token of a verify follow softmax(logits / T) (chi-square).
 """
@@ -17,11 +21,14 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_walk(tree, lg, w, step):
+def _check_walk(got, tree, lg, w, step):
+    """The oracle's walk on the GPU's logits, near-ties resolved as `got`
+    resolves them; returns the accepted depth."""
     from oracle import sampling as S
-    path, bonus = S.accept_sample(tree["token"], tree["parent"], lg, w["temperature"], w["seed"],
-                                  step, w["depth"])
-    return [tree["token"][r] for r in path] + [bonus], path
+    ok, want, margin = S.check_walk(got, tree["token"], tree["parent"], lg, w["temperature"],
+                                    w["seed"], step, w["depth"])
+    assert ok, (step, got, want, margin)
+    return len(want) - 1
 
 
 def _top_tree(eng, w, p, width, levels):
@@ -72,8 +79,7 @@ def test_drafted_trees_match_oracle_decisions(sampler):
         new = eng.verify()
         lg = eng.debug_read("logits")
         assert lg.shape == (len(tree["token"]), w["vocab"])
-        want, _ = _oracle_walk(tree, lg, w, step)
-        assert new == want, step
+        _check_walk(new, tree, lg, w, step)
 
 
 def test_planted_top_trees_accept_deep_and_match_oracle(sampler):
@@ -96,9 +102,7 @@ def test_planted_top_trees_accept_deep_and_match_oracle(sampler):
         print(f"{w['name']} planted trial {trial}", flush=True)
         new = eng.verify(tree)
         lg = eng.debug_read("logits")
-        want, path = _oracle_walk(tree, lg, dict(wc, seed=w["seed"] + trial), 1)
-        assert new == want, trial
-        depths.append(len(path))
+        depths.append(_check_walk(new, tree, lg, dict(wc, seed=w["seed"] + trial), 1))
     eng.set_sampling(w["temperature"], w["seed"])
     eng.set_debug(False)
     assert max(depths) >= 2, depths     # the accepting branch is exercised
@@ -114,8 +118,9 @@ def test_c1_stream_equals_oracle_session():
         print(f"c1 sampled stream seed {seed}", flush=True)
         got, _ = eng.generate(p, w["gen"])
         eng.close()
-        want = Session(w).generate(p)
-        assert got == want
+        ref = Session(w, follow=got)
+        assert ref.generate(p) == got
+        print(f"smallest sampling margin {min(ref.sample_margins):.2e}", flush=True)
 
 
 def _chi2_ok(counts, probs, n):
@@ -145,16 +150,14 @@ def test_first_tokens_follow_target_softmax():
     tgt = Target(cfg, Weights(cfg))
     n = len(p)
     f, _ = tgt.forward(p, np.arange(n), np.arange(n), causal_vis(n, 0, n), tgt.new_kv(n))
-    e, z = S.row_probs(tgt.logits(f[-1:])[0], T)
-    p_pre = (e / z).astype(np.float64)
+    p_pre = S.probs(tgt.logits(f[-1:])[0], T)
     # the first verified token: the root row after a greedy prefill, whose
     # distribution comes from the GPU's own logits
     eng.set_sampling(0.0, 0)
     eng.set_debug(True)
     eng.prefill(p)
     eng.verify({"token": [0], "parent": [-1]})
-    e, z = S.row_probs(eng.debug_read("logits")[0], T)
-    p_root = (e / z).astype(np.float64)
+    p_root = S.probs(eng.debug_read("logits")[0], T)
     top = [int(x) for x in np.argsort(-p_root, kind="stable")[:3]]
     planted = {"token": [0] + top, "parent": [-1, 0, 0, 0]}
     N = 1500

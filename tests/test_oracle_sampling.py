@@ -1,6 +1,6 @@
 """Pins of the sampling-mode oracle (oracle/sampling.py): the published
 Philox known answers, the greedy limit, exact residual draws on a small case,
-and losslessness: the committed tokens are distributed as the target's own
+the near-tie allowance, and losslessness: the committed tokens are distributed as the target's own
 softmax ([L13] "Speculative decoding in four moves"; glossary "Lossless")."""
 import json
 import os
@@ -40,15 +40,59 @@ def test_uniform_is_24_bit_and_varies_with_every_counter_word():
 
 
 def test_residual_draw_small_case():
-    e = np.array([1, 2, 3, 4], dtype=np.float32)
-    z = np.float32(10)
+    p = np.array([1, 2, 3, 4], dtype=np.float64) / 10
     # token 1 rejected: S = 0.8; tokens 0, 2, 3 carry 0.1, 0.3, 0.4
-    s_left = np.float32(0.8)
-    assert S.residual_draw(e, z, [1], s_left, np.float32(0.0)) == 0
-    assert S.residual_draw(e, z, [1], s_left, np.float32(0.2)) == 2      # 0.16 in (0.1, 0.4]
-    assert S.residual_draw(e, z, [1], s_left, np.float32(0.6)) == 3      # 0.48 in (0.4, 0.8]
-    assert S.residual_draw(e, z, [], np.float32(1.0), np.float32(0.95)) == 3
-    assert S.residual_draw(e, z, [3], np.float32(0.6), np.float32(0.9999)) == 2   # sum short: last left
+    assert S.residual_draw(p, [1], 0.8, 0.0)[0] == 0
+    v, m = S.residual_draw(p, [1], 0.8, 0.2)           # 0.16 in (0.1, 0.4]
+    assert v == 2 and abs(m - 0.06) < 1e-12
+    v, m = S.residual_draw(p, [1], 0.8, 0.6)           # 0.48 in (0.4, 0.8]
+    assert v == 3 and abs(m - 0.08) < 1e-12
+    assert S.residual_draw(p, [], 1.0, 0.95)[0] == 3
+    # a mass larger than what is left (rounding): the last token left, margin 0
+    assert S.residual_draw(p, [3], 0.61, 0.9999) == (2, 0.0)
+    assert S.residual_interval(p, [1], 3) == (0.4, 0.8)
+
+
+def _u(seed, step, depth, draw):
+    return S.uniform(seed, step, depth, draw)
+
+
+def test_near_ties_take_the_followed_outcome_and_nothing_else():
+    """A child whose p(x) sits 4e-6 above u (a near-tie): the oracle accepts
+    it, and a walk told that the other side rejected it follows that; at
+    1e-3 above u the followed rejection is refused. The same for a residual
+    draw landing 4e-6 inside a token's interval."""
+    seed, step = 3, 9
+    u0 = _u(seed, step, 0, 0)
+    assert 0.05 < u0 < 0.95
+    for gap, tie in ((4e-6, True), (1e-3, False)):
+        px = u0 + gap
+        # three tokens: x = 0 with p(x) = px, the rest split evenly (T = 1)
+        logits = np.log(np.array([[px, (1 - px) / 2, (1 - px) / 2]]))
+        tokens, parent = [0, 0], [-1, 0]
+        lg = np.repeat(logits, 2, axis=0)
+        path, bonus, margins = S.walk(tokens, parent, lg, 1.0, seed, step, max_depth=1)
+        assert path == [1] and abs(margins[0] - gap) < 1e-9
+        # the other outcome: x rejected, then the residual draw at depth 0
+        ur = _u(seed, step, 0, S.RESIDUAL_DRAW)
+        alt = 1 + int(ur * (1 - px) >= (1 - px) / 2)
+        ok, want, m = S.check_walk([alt], tokens, parent, lg, 1.0, seed, step, 1)
+        assert ok == tie and m <= gap + 1e-9
+        ok, want, _ = S.check_walk([0, int(bonus)], tokens, parent, lg, 1.0, seed, step, 1)
+        assert ok and want == [0, int(bonus)]
+    ur = _u(seed, step, 0, S.RESIDUAL_DRAW)
+    for gap, tie in ((4e-6, True), (1e-3, False)):
+        # no children: the residual draw over p = (ur - gap, the rest / 2, the rest / 2)
+        # lands `gap` past the end of token 0's interval
+        p0 = ur - gap
+        lg = np.log(np.array([[p0, (1 - p0) / 2, (1 - p0) / 2]]))
+        v, m = S.residual_draw(S.probs(lg[0], 1.0), [], 1.0, ur)
+        assert v == 1 and abs(m - gap) < 1e-9
+        ok, _, _ = S.check_walk([0], [0], [-1], lg, 1.0, seed, step, 1)
+        assert ok == tie
+        # a token whose interval is far from u * S is never accepted
+        ok, _, _ = S.check_walk([2], [0], [-1], lg, 1.0, seed, step, 1)
+        assert not ok
 
 
 def _random_tree(rng, n, depth_max):
@@ -99,10 +143,8 @@ def test_committed_tokens_follow_the_target_distribution():
     tokens = [0, 2, 0, 5, 1, 4]
     parent = [-1, 0, 0, 0, 1, 1]
     logits = (rng.standard_normal((6, V)) * 1.5).astype(np.float32)
-    e0, z0 = S.row_probs(logits[0], T_)
-    p0 = (e0 / z0).astype(np.float64)
-    e1, z1 = S.row_probs(logits[1], T_)
-    p1 = (e1 / z1).astype(np.float64)
+    p0 = S.probs(logits[0], T_)
+    p1 = S.probs(logits[1], T_)
     N = 20000
     first = np.zeros(V)
     second = np.zeros(V)
@@ -123,12 +165,11 @@ def test_committed_tokens_follow_the_target_distribution():
 def test_sample_token_follows_softmax():
     rng = np.random.default_rng(5)
     l = rng.standard_normal(8).astype(np.float32)
-    e, z = S.row_probs(l, 0.7)
-    p = (e / z).astype(np.float64)
+    p = S.probs(l, 0.7)
     N = 20000
     c = np.zeros(8)
     for step in range(N):
-        c[S.sample_token(l, 0.7, seed=4, step=step)] += 1
+        c[S.sample_token(l, 0.7, seed=4, step=step)[0]] += 1
     ok, chi2, dof = _chi2_ok(c, p, N)
     assert ok, (chi2, dof)
 
