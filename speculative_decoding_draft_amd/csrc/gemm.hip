@@ -1100,6 +1100,13 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
     if (p.mt < 8)   // the many-row tiles keep the MFMAs busy without a wider grid
       while (p.n_tiles * s < 256 && s < 16 && chunks / (2 * s) >= 4) s *= 2;
     while (p.n_tiles * s > 1024 && s > 1) s /= 2;
+    // Four or more m-tiles (49-80 rows): one round of workgroups, the
+    // largest split count (any integer) that keeps the grid within 256.
+    // A second partial round measured slower at these heavier workgroups
+    // (q|k|v at 65 rows: 5 splits 20.6 us against 8 splits 24.1; the 70B
+    // down at 61 rows: 4 splits 100 us against 16 splits 106); at one or two
+    // m-tiles several workgroups per CU hide more latency and win.
+    if (p.mt >= 4 && p.n_tiles * s > 256) s = std::max(1, 256 / p.n_tiles);
     p.splits = s;
   }
   return p;
