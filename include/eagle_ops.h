@@ -111,9 +111,15 @@ uint64_t eagle_op_attention_workspace(int32_t dtype, int32_t M, int32_t n_heads,
  *      lo plane, see above; fp32: one array).
  *   kv: the cache; key slot s of KV head h, plane p, element i lives at
  *      page_table[s / 64] * (planes * n_kv_heads * 64 * head_dim)
- *        + ((p * n_kv_heads + h) * 64 + s % 64) * head_dim + i
+ *        + (p * n_kv_heads + h) * 64 * head_dim + (s % 64) * head_dim + i
  *      with planes K_hi, K_lo, V_hi, V_lo (bf16 raw bits; value = hi + lo) or
- *      K, V (fp32). page_table: device int32 [key_end / 64 rounded up].
+ *      K, V (fp32), except that bf16 V planes are transposed within the page:
+ *      element i of slot s of V_hi or V_lo lives at
+ *        ... + (p * n_kv_heads + h) * 64 * head_dim + i * 64 + s % 64.
+ *      page_table: device int32 [key_end / 64 rounded up]. bf16 reads whole
+ *      pages: the keys of the first page below pre_lo and of the last page
+ *      from key_end on are read and masked, so those slots need no set
+ *      contents.
  *   Row r sees key slots [pre_lo, prehi[r]) and the tree slots tree_base + j
  *   (j < n_tree <= 128) whose bit j is set in tree_mask[2r] (j < 64) or
  *   tree_mask[2r + 1] (j >= 64); key_end = one past the last slot any row

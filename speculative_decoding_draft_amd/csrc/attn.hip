@@ -40,20 +40,70 @@ __device__ __forceinline__ T* kv_ptr(const KVView& v, int slot, int sel, int h) 
          ((int64_t)(sel * v.n_kv + h) * v.page + (slot & (v.page - 1))) * v.d;
 }
 
+// Element i of cache row `slot` in plane `sel` of KV head h. A page holds,
+// per plane and KV head, `page` rows of d elements; bf16 caches keep their V
+// planes (sel 2 and 3) transposed within the page: d rows of `page` slots,
+// so the V^T operand of the attention products is a contiguous run of
+// slots in memory.
+template <typename T>
+__device__ __forceinline__ T* kv_elem(const KVView& v, int slot, int sel, int h, int i) {
+  const int sh = page_shift(v);
+  T* pl = (T*)v.base + (int64_t)v.page_table[slot >> sh] * v.page_elems +
+          (int64_t)(sel * v.n_kv + h) * v.page * v.d;
+  if (sizeof(T) == 2 && sel >= 2) return pl + (int64_t)i * v.page + (slot & (v.page - 1));
+  return pl + (int64_t)(slot & (v.page - 1)) * v.d + i;
+}
+
 // K (which = 0) or V (which = 1) element of one cache row.
 template <typename T> struct KVStore;
 template <> struct KVStore<float> {
   __device__ static void put(const KVView& v, int slot, int which, int h, int i, float x) {
-    kv_ptr<float>(v, slot, which, h)[i] = x;
+    *kv_elem<float>(v, slot, which, h, i) = x;
   }
 };
 template <> struct KVStore<bf16_t> {
   __device__ static void put(const KVView& v, int slot, int which, int h, int i, float x) {
     const bf16_t hi = f32_to_bf16(x);
-    kv_ptr<bf16_t>(v, slot, 2 * which, h)[i] = hi;
-    kv_ptr<bf16_t>(v, slot, 2 * which + 1, h)[i] = f32_to_bf16(x - bf16_to_f32(hi));
+    *kv_elem<bf16_t>(v, slot, 2 * which, h, i) = hi;
+    *kv_elem<bf16_t>(v, slot, 2 * which + 1, h, i) = f32_to_bf16(x - bf16_to_f32(hi));
   }
 };
+
+// bf16 key chunks start on page boundaries (pages hold a power-of-two
+// number of slots, at least CHUNK), so a chunk lies in one page and its V^T
+// rows are aligned runs of CHUNK slots; keys of the first chunk below
+// pre_lo are masked like any key a row does not see.
+__device__ __forceinline__ int chunk_base(int pre_lo) { return pre_lo & ~(CHUNK - 1); }
+
+// 16-byte piece p of a chunk's V^T (hi and lo planes, 128 dimensions):
+// plane p / 1024, dimension (p / 8) % 128, slots 8 (p % 8) .. + 7 of the
+// chunk that starts at slot k0 of page pg.
+__device__ __forceinline__ const bf16_t* vt_piece(const KVView& kv, int pg, int hk, int k0, int p) {
+  constexpr int D = 128;
+  const int plane = p / (D * 8), dim = (p / 8) % D, kg = p % 8;
+  return (const bf16_t*)kv.base + (int64_t)pg * kv.page_elems +
+         ((int64_t)((2 + plane) * kv.n_kv + hk) * D + dim) * kv.page + (k0 & (kv.page - 1)) + 8 * kg;
+}
+// Stores piece p into the staged V^T (rows padded to `VP` elements). Only
+// chunk slots [lo, hi) hold keys (the chunk's keys from pre_lo to the
+// launch's last key); the others are written as zeros, so whatever a cache
+// holds there never meets a zero probability (0 * NaN would be NaN).
+template <int VP>
+__device__ __forceinline__ void vt_put(bf16_t (&vt)[2][128][VP], int p, uint4 v, int lo, int hi) {
+  const int plane = p / 1024, dim = (p / 8) % 128, kg = p % 8;
+  const int a = lo - 8 * kg, b = hi - 8 * kg;   // this piece keeps elements [a, b)
+  if (a > 0 || b < 8) {
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t m0 = (2 * j >= a && 2 * j < b) ? 0xffffu : 0u;
+      const uint32_t m1 = (2 * j + 1 >= a && 2 * j + 1 < b) ? 0xffff0000u : 0u;
+      w[j] &= m0 | m1;
+    }
+    v = uint4{w[0], w[1], w[2], w[3]};
+  }
+  *reinterpret_cast<uint4*>(&vt[plane][dim][8 * kg]) = v;
+}
 
 __device__ __forceinline__ bool row_sees(const RowVis& rv, int prehi, uint64_t m0, uint64_t m1,
                                          int key) {
@@ -133,7 +183,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   const int Mt = a.M, Ml = a.ln.n > 1 ? a.ln.rows : a.M, r0 = seq * Ml;
   const RowVis vis = lane_vis(a.vis, a.ln, seq);
   const KVView kv = lane_kv<bf16_t>(a.kv, seq);
-  const int k0 = vis.pre_lo + chunk * CK;
+  const int k0 = chunk_base(vis.pre_lo) + chunk * CK;
   if (k0 >= vis.key_end) return;   // a shorter sequence: uniform over the workgroup
   const int k1 = min(vis.key_end, k0 + CK);
 
@@ -141,13 +191,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
   // Every load of this thread is issued before the first LDS store, so the
   // workgroup waits for one memory latency instead of one per piece.
   static_assert(2 * CK * 16 == 8 * 256 && 2 * (CK / 2) * 16 == 4 * 256, "staging assumes 256 threads");
-  // A chunk spans at most two KV pages (the launcher checks page >= CHUNK):
-  // both page-table entries are read once, up front, so no KV address waits
-  // on a per-element table load.
-  const int pgsz = kv.page, psh = page_shift(kv), pA = k0 >> psh;
-  const int pgA = kv.page_table[pA], pgB = kv.page_table[(k1 - 1) >> psh];
+  // The chunk lies in one KV page: its page-table entry is read once, up
+  // front, so no KV address waits on a per-element table load.
+  const int pgsz = kv.page, pg = kv.page_table[k0 >> page_shift(kv)];
   auto kvp = [&](int key, int plane) {
-    const int pg = ((key >> psh) == pA) ? pgA : pgB;
     return (const bf16_t*)kv.base + (int64_t)pg * kv.page_elems +
            ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
   };
@@ -182,7 +229,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     mk1 = vis.mask[2 * rowc + 1];
   };
   if (active) load_pair(pr0);
-  uint4 kr[8], va[4], vb[4];
+  uint4 kr[8], vr[8];
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int i = tid + 256 * it;
@@ -190,12 +237,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c);
   }
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int i = tid + 256 * it;
-    const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
-    va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c);
-    vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c);
-  }
+  for (int it = 0; it < 8; ++it) vr[it] = ld16(vt_piece(kv, pg, hk, k0, tid + 256 * it));
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int i = tid + 256 * it;
@@ -203,17 +245,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     ks[plane][key][c ^ k_swz(key)] = kr[it];
   }
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int i = tid + 256 * it;
-    const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c = (i / (CK / 2)) % 16;
-    const uint32_t wa[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
-    const uint32_t wb[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
-      *reinterpret_cast<uint32_t*>(&vt[plane][8 * c + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
-      *reinterpret_cast<uint32_t*>(&vt[plane][8 * c + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
-    }
-  }
+  for (int it = 0; it < 8; ++it) vt_put(vt, tid + 256 * it, vr[it], vis.pre_lo - k0, k1 - k0);
   __syncthreads();
 
   float m_keep = -INFINITY, l_keep = 0.f;
@@ -245,7 +277,7 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
       }
       float p[8];
       float bm = -INFINITY;
-      if (k0 + kb0 + 32 <= min(pmin, k1)) {
+      if (k0 + kb0 >= vis.pre_lo && k0 + kb0 + 32 <= min(pmin, k1)) {
         // every key of the block is in every row's visible prefix
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -432,7 +464,8 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
   }
   __syncthreads();
   const int kend = kend_sh;
-  const int nch = kend > vis.pre_lo ? (kend - vis.pre_lo + CK - 1) / CK : 0;
+  const int cb = chunk_base(vis.pre_lo);
+  const int nch = kend > vis.pre_lo ? (kend - cb + CK - 1) / CK : 0;
 
   // this wave's pairs: p = slot + 4 i, head j = p / rb, row block p % rb
   const int npairs = a.group * a.rb;
@@ -460,15 +493,14 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
   }
 
   const int pgsz = kv.page, psh = page_shift(kv);
-  uint4 kr[4], va[2], vb[2];
+  uint4 kr[4], vr[4];
+  int v_lo = 0, v_hi = 0;   // the staged chunk's key slots
   // loads of chunk c into registers (keys past the chunk's end repeat its
-  // last key; they are masked); a chunk spans at most two KV pages
+  // last key; they are masked); the chunk lies in one KV page
   auto load_chunk = [&](int c) {
-    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
-    const int pA = k0 >> psh;
-    const int pgA = kv.page_table[pA], pgB = kv.page_table[(k1 - 1) >> psh];
+    const int k0 = cb + c * CK, k1 = min(kend, k0 + CK);
+    const int pg = kv.page_table[k0 >> psh];
     auto kvp = [&](int key, int plane) {
-      const int pg = ((key >> psh) == pA) ? pgA : pgB;
       return (const bf16_t*)kv.base + (int64_t)pg * kv.page_elems +
              ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
     };
@@ -479,12 +511,9 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
       kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + NT * it;
-      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
-      va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
-      vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
-    }
+    for (int it = 0; it < 4; ++it) vr[it] = ld16(vt_piece(kv, pg, hk, k0, tid + NT * it));
+    v_lo = vis.pre_lo - k0;
+    v_hi = k1 - k0;
   };
   auto store_chunk = [&]() {
 #pragma unroll
@@ -494,17 +523,7 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
       ks[plane][key][c16 ^ k_swz(key)] = kr[it];
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + NT * it;
-      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
-      const uint32_t wa[4] = {va[it].x, va[it].y, va[it].z, va[it].w};
-      const uint32_t wb[4] = {vb[it].x, vb[it].y, vb[it].z, vb[it].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
-        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
-        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
-      }
-    }
+    for (int it = 0; it < 4; ++it) vt_put(vt, tid + NT * it, vr[it], v_lo, v_hi);
   };
 
   if (nch > 0) {
@@ -514,7 +533,7 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
   __syncthreads();
   const int kb0 = 32 * kh;   // this wave's 32 keys of every chunk
   for (int c = 0; c < nch; ++c) {
-    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+    const int k0 = cb + c * CK, k1 = min(kend, k0 + CK);
     if (c + 1 < nch) load_chunk(c + 1);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
@@ -540,7 +559,7 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
       }
       float p[8];
       float bm = -INFINITY;
-      if (k0 + kb0 + 32 <= min(pmin[i], k1)) {
+      if (k0 + kb0 >= vis.pre_lo && k0 + kb0 + 32 <= min(pmin[i], k1)) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           p[e] = sc[e >> 2][e & 3] * a.scale;
@@ -552,7 +571,7 @@ __global__ __launch_bounds__(512) void attn_flash_kernel(FlashArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int key = k0 + kb0 + 8 * g + 4 * hh + e;
-            const bool ok = key < k1 && key < prehi[i];
+            const bool ok = key >= vis.pre_lo && key < k1 && key < prehi[i];
             p[4 * hh + e] = ok ? sc[hh][e] * a.scale : -INFINITY;
             bm = fmaxf(bm, p[4 * hh + e]);
           }
@@ -680,11 +699,20 @@ struct SplitArgs {
   float* opart; float* mlpart;  // several: partials [split][M][nq][D], [split][M][nq][2]
 };
 
+// Most key chunks one workgroup of attn_split_kernel walks (its page list
+// sits in LDS); the launcher raises the split count to keep within it.
+constexpr int ATTN_SPLIT_CHUNKS = 1024;
+
 template <int PW>
 __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
-  constexpr int D = 128, CK = CHUNK, VP = CK + 8, NT = 512;
-  __shared__ uint4 ks[2][CK][16];
-  __shared__ __attribute__((aligned(16))) bf16_t vt[2][D][VP];
+  constexpr int D = 128, CK = CHUNK, NT = 512;
+  // two chunk buffers, filled straight from the cache (see copy_chunk): K
+  // hi/lo as [key][16-byte column ^ k_swz(key)] and V^T hi/lo as
+  // [dimension][8-slot group ^ (dimension mod 8)]; the XOR swizzles keep
+  // the operand reads free of bank conflicts
+  __shared__ uint4 ks[2][2][CK][16];
+  __shared__ uint4 vs[2][2][D][8];
+  __shared__ int pgs[ATTN_SPLIT_CHUNKS];   // page of each of this workgroup's chunks
   const int seq = blockIdx.z;
   int S = 1;
 #pragma unroll
@@ -706,7 +734,8 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
   const KVView kv = lane_kv<bf16_t>(a.kv, seq);
   const int Ml = a.ln.n > 1 ? a.ln.rows : a.M, r0 = seq * Ml;
   const int nqr = a.group * Ml;   // query rows of this KV head
-  const int nch = (vis.key_end - vis.pre_lo + CK - 1) / CK;
+  const int cb = chunk_base(vis.pre_lo);
+  const int nch = (vis.key_end - cb + CK - 1) / CK;
   const int c_lo = (int)((int64_t)sp * nch / S), c_hi = (int)((int64_t)(sp + 1) * nch / S);
   const int kend = vis.key_end;
 
@@ -715,54 +744,8 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
   const int lr = lane & 15, g = lane >> 4;
   const int t0 = rgi * a.tpg, ntg = min(a.tpg, a.ntile - t0);   // this group's tiles
 
-  // chunk staging (keys past the chunk's end repeat its last key; they are
-  // masked); a chunk spans at most two KV pages
   const int pgsz = kv.page, psh = page_shift(kv);
-  struct Stage { uint4 kr[4], va[2], vb[2]; };
-  Stage st0, st1;
-  auto load_chunk = [&](int c, Stage& sg) {
-    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
-    const int pA = k0 >> psh;
-    const int pgA = kv.page_table[pA], pgB = kv.page_table[(k1 - 1) >> psh];
-    auto kvp = [&](int key, int plane) {
-      const int pg = ((key >> psh) == pA) ? pgA : pgB;
-      return (const bf16_t*)kv.base + (int64_t)pg * kv.page_elems +
-             ((int64_t)(plane * kv.n_kv + hk) * pgsz + (key & (pgsz - 1))) * D;
-    };
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = tid + NT * it;
-      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
-      sg.kr[it] = ld16(kvp(min(k0 + key, k1 - 1), plane) + 8 * c16);
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + NT * it;
-      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
-      sg.va[it] = ld16(kvp(min(k0 + 2 * kp, k1 - 1), 2 + plane) + 8 * c16);
-      sg.vb[it] = ld16(kvp(min(k0 + 2 * kp + 1, k1 - 1), 2 + plane) + 8 * c16);
-    }
-  };
-  auto store_chunk = [&](const Stage& sg) {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int i = tid + NT * it;
-      const int plane = i / (CK * 16), key = (i / 16) % CK, c16 = i % 16;
-      ks[plane][key][c16 ^ k_swz(key)] = sg.kr[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int i = tid + NT * it;
-      const int plane = i / ((CK / 2) * 16), kp = i % (CK / 2), c16 = (i / (CK / 2)) % 16;
-      const uint32_t wa[4] = {sg.va[it].x, sg.va[it].y, sg.va[it].z, sg.va[it].w};
-      const uint32_t wb[4] = {sg.vb[it].x, sg.vb[it].y, sg.vb[it].z, sg.vb[it].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {   // d = 8c + 2j and 8c + 2j + 1
-        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j][2 * kp]) = (wa[j] & 0xffffu) | (wb[j] << 16);
-        *reinterpret_cast<uint32_t*>(&vt[plane][8 * c16 + 2 * j + 1][2 * kp]) = (wa[j] >> 16) | (wb[j] & 0xffff0000u);
-      }
-    }
-  };
+  for (int i = tid; i < c_hi - c_lo; i += NT) pgs[i] = kv.page_table[(cb + (c_lo + i) * CK) >> psh];
   uint4 qf[PW][4], ql[PW][4];
   int prehi[PW], pmin[PW], rowr[PW], headj[PW];
   bool valid[PW];
@@ -794,18 +777,77 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
     for (int dt = 0; dt < 8; ++dt) o[i][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // the first two chunks' loads go out after the query rows' loads: loads
-  // return in order, so the first use of the query rows (the visibility
-  // minimum above) then waits for them alone, and staging chunk 0 leaves
-  // chunk 1 in flight
-  if (c_lo < c_hi) load_chunk(c_lo, st0);
-  if (c_lo + 1 < c_hi) load_chunk(c_lo + 1, st1);
+  // Chunks are copied from the cache straight into LDS: wave w issues 1 KB
+  // blocks 8w .. 8w + 7 of the chunk's 64 (0-31: the K planes, four keys a
+  // block; 32-63: the V^T planes, eight dimensions a block), each lane
+  // reading the 16 bytes that belong at lane * 16 of its block under the
+  // swizzles. The copies are asm (global_load_lds_dwordx4 writes no
+  // register) and are waited for with explicit vmcnt counts, so one chunk
+  // is in flight while the previous one is multiplied: the compiler's own
+  // wait tracking cannot see them, and every load it tracks (the query rows,
+  // the masks, the page entries) is complete before the first copy.
+  auto lds_u32 = [](const void* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+  };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto copy_chunk = [&](int c, int b) {
+    const int ko = (cb + c * CK) & (pgsz - 1);
+    const bf16_t* pb = (const bf16_t*)kv.base + (int64_t)pgs[c - c_lo] * kv.page_elems;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = wave_u * 8 + j;
+      uint32_t lds;
+      const bf16_t* src;
+      if (q < 32) {
+        const int plane = q >> 4, key = 4 * (q & 15) + (lane >> 4);
+        lds = lds_u32(&ks[b][plane][4 * (q & 15)][0]);
+        src = pb + ((int64_t)(plane * kv.n_kv + hk) * pgsz + ko + key) * D + 8 * ((lane & 15) ^ k_swz(key));
+      } else {
+        const int qv = q - 32, plane = qv >> 4, dim = 8 * (qv & 15) + (lane >> 3);
+        lds = lds_u32(&vs[b][plane][8 * (qv & 15)][0]);
+        src = pb + ((int64_t)((2 + plane) * kv.n_kv + hk) * D + dim) * pgsz + ko + 8 * ((lane & 7) ^ (dim & 7));
+      }
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(src)
+                   : "memory", "m0");
+    }
+  };
+  // V^T slots of chunk c outside [pre_lo, kend) (the first chunk's below
+  // pre_lo, the last chunk's past the last key) are set to zero once the
+  // copy has landed: a cache may hold anything there, and 0 * NaN is NaN
+  auto clear_vt = [&](int c, int b) {
+    const int k0 = cb + c * CK;
+    const int lo = vis.pre_lo - k0, hi = min(kend, k0 + CK) - k0;
+    if (lo <= 0 && hi >= CK) return;   // uniform
+    if (tid < 2 * D) {
+      const int plane = tid / D, dim = tid % D;
+#pragma unroll
+      for (int col = 0; col < 8; ++col) {
+        const int kg = col ^ (dim & 7);
+        const int x = lo - 8 * kg, y = hi - 8 * kg;   // keep elements [x, y)
+        if (x <= 0 && y >= 8) continue;
+        uint4 v = vs[b][plane][dim][col];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t m0 = (2 * e >= x && 2 * e < y) ? 0xffffu : 0u;
+          const uint32_t m1 = (2 * e + 1 >= x && 2 * e + 1 < y) ? 0xffff0000u : 0u;
+          w[e] &= m0 | m1;
+        }
+        vs[b][plane][dim][col] = uint4{w[0], w[1], w[2], w[3]};
+      }
+    }
+    lds_barrier();
+  };
+  __syncthreads();                     // pgs
+  __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): every tracked load is done
+  if (c_lo < c_hi) copy_chunk(c_lo, 0);
   const int kb0 = 32 * kh;   // this wave's 32 keys of every chunk
   // per chunk: S^T = K Q^T for the wave's tiles (each K fragment read from
   // LDS once for all of them), masking and the online softmax, then
   // O^T += V^T P^T (each V^T fragment read once)
-  auto compute = [&](int c) {
-    const int k0 = vis.pre_lo + c * CK, k1 = min(kend, k0 + CK);
+  auto compute = [&](int c, int b) {
+    const int k0 = cb + c * CK, k1 = min(kend, k0 + CK);
     f32x4 sc[PW][2];
 #pragma unroll
     for (int i = 0; i < PW; ++i) sc[i][0] = sc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -815,8 +857,8 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int key = kb0 + 8 * (lr >> 2) + 4 * hh + (lr & 3);
-        kf[hh] = ks[0][key][(4 * s + g) ^ k_swz(key)];
-        kl[hh] = ks[1][key][(4 * s + g) ^ k_swz(key)];
+        kf[hh] = ks[b][0][key][(4 * s + g) ^ k_swz(key)];
+        kl[hh] = ks[b][1][key][(4 * s + g) ^ k_swz(key)];
       }
 #pragma unroll
       for (int i = 0; i < PW; ++i) {
@@ -836,7 +878,7 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
       if (slot + 4 * i >= ntg) continue;
       float p[8];
       float bm = -INFINITY;
-      if (k0 + kb0 + 32 <= min(pmin[i], k1)) {
+      if (k0 + kb0 >= vis.pre_lo && k0 + kb0 + 32 <= min(pmin[i], k1)) {
         // every key of the block is in every row's visible prefix
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -886,8 +928,9 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
     }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {  // (V_hi + V_lo)(P_hi + P_lo), lo*lo dropped
-      const uint4 v0 = *reinterpret_cast<const uint4*>(&vt[0][16 * dt + lr][kb0 + 8 * g]);
-      const uint4 v1 = *reinterpret_cast<const uint4*>(&vt[1][16 * dt + lr][kb0 + 8 * g]);
+      const int vr = 16 * dt + lr, vc = ((kb0 >> 3) + g) ^ (vr & 7);
+      const uint4 v0 = vs[b][0][vr][vc];
+      const uint4 v1 = vs[b][1][vr][vc];
 #pragma unroll
       for (int i = 0; i < PW; ++i) {
         if (slot + 4 * i >= ntg) continue;
@@ -898,30 +941,25 @@ __global__ __launch_bounds__(512) void attn_split_kernel(SplitArgs a) {
     }
   };
 
-  // Two register sets stage chunks on their way to LDS, so the loads of the
-  // next two chunks are in flight while one is computed (a load takes about
-  // as long as two chunks' products here). The loop is unrolled by two to
-  // keep the sets in fixed registers.
-  if (c_lo < c_hi) store_chunk(st0);
-  __syncthreads();
-  for (int c = c_lo; c < c_hi; c += 2) {
-    if (c + 2 < c_hi) load_chunk(c + 2, st0);
-    compute(c);
-    __syncthreads();   // every wave is done with chunk c's LDS
-    if (c + 1 >= c_hi) break;
-    store_chunk(st1);
-    __syncthreads();
-    if (c + 3 < c_hi) load_chunk(c + 3, st1);
-    compute(c + 1);
-    __syncthreads();
-    if (c + 2 >= c_hi) break;
-    store_chunk(st0);
-    __syncthreads();
+  // chunk c + 1 is copied while chunk c is multiplied; each wave waits for
+  // its own copies of chunk c (eight blocks younger than them may be in
+  // flight), and the barrier makes every wave's copies visible
+  for (int c = c_lo; c < c_hi; ++c) {
+    const int b = (c - c_lo) & 1;
+    if (c + 1 < c_hi) {
+      copy_chunk(c + 1, b ^ 1);
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    clear_vt(c, b);
+    compute(c, b);
+    lds_barrier();   // every wave is done with buffer b before chunk c + 2 overwrites it
   }
   // merge the two key halves of each tile (the K area holds the second
   // half's O, the V area its max and sum), then write the rows
-  float* mo = reinterpret_cast<float*>(&ks[0][0][0]);   // [slot][16 rows][128]
-  float* mm = reinterpret_cast<float*>(&vt[0][0][0]);   // [slot][16 rows][2]
+  float* mo = reinterpret_cast<float*>(&ks[0][0][0][0]);   // [slot][16 rows][128]
+  float* mm = reinterpret_cast<float*>(&vs[0][0][0][0]);   // [slot][16 rows][2]
   static_assert(4 * 16 * D * 4 <= (int)sizeof(ks), "merge buffer must fit");
 #pragma unroll
   for (int i = 0; i < PW; ++i) {
@@ -1189,28 +1227,77 @@ __global__ __launch_bounds__(256) void sum_planes_kernel(const float* part, int 
 
 // Sums the split-K planes of the fused q|k|v projection, applies the rotary
 // embedding (rotate-half pairing) to q and k, writes q as an operand and k, v
-// into the cache slot of each row. Grid (rows, head groups): a workgroup of 256
-// threads covers 1024 / d consecutive heads of the q|k|v row.
+// into the cache slot of each row. Workgroups [0, M n_qk): one row and 1024 / d
+// consecutive q or k heads of it. The rest: 32 dimensions of one V head over
+// a block of rb rows of one sequence, so that the transposed V planes of a
+// bf16 cache are written by consecutive lanes at consecutive slots.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, int64_t plane, int nq,
                                                       int nkv, int d, const int32_t* pos,
                                                       const int32_t* slot,
                                                       const float* cos_t, const float* sin_t,
                                                       T* q_out, int64_t qlo, KVView kv_all,
-                                                      Lanes ln) {
-  __shared__ float xs[1024];
-  const int r = blockIdx.x;
+                                                      Lanes ln, int M, int n_qk, int rb) {
+  // q/k workgroups use the first 1024 floats; V workgroups rb rows of dg
+  // floats at a pitch of dg + 1 (the transposed reads fall in distinct banks)
+  __shared__ float xs[64 * 33];
+  const int width = (nq + 2 * nkv) * d;
+  const int half = d / 2;
+  if ((int)blockIdx.x >= M * n_qk) {
+    // ---- dimensions [i0, i0 + dg) of V head h over block blk of rb rows
+    // of one sequence (rb * dg <= 2048: two float4 of each plane per thread,
+    // all loads of the workgroup in one round)
+    const int dg = min(32, d), ndg = d / dg;
+    int vb = blockIdx.x - M * n_qk;
+    const int i0 = (vb % ndg) * dg;
+    vb /= ndg;
+    const int h = vb % nkv, blk = vb / nkv;
+    const int rps = ln.n > 1 ? ln.rows : M;   // rows per sequence
+    const int bps = (rps + rb - 1) / rb;
+    const int seq = blk / bps, j0 = (blk % bps) * rb, nr = min(rb, rps - j0);
+    const int r0 = seq * rps + j0;
+    const int32_t* sl = (const int32_t*)((const char*)slot + seq * ln.bytes);
+    const KVView kv = lane_kv<T>(kv_all, seq);
+    const int col0 = (nq + nkv + h) * d + i0;
+    {
+      bool ok[2];
+      const float* pp[2];
+      float4 acc[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 4 * (threadIdx.x + 256 * u);
+        ok[u] = e < nr * dg;
+        const int ec = ok[u] ? e : 0;
+        pp[u] = qkv + (int64_t)(r0 + ec / dg) * width + col0 + ec % dg;
+      }
+      plane_sums<2>(pp, ok, S, plane, acc);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 4 * (threadIdx.x + 256 * u);
+        if (!ok[u]) continue;
+        float* x = xs + (e / dg) * (dg + 1) + e % dg;
+        x[0] = acc[u].x; x[1] = acc[u].y; x[2] = acc[u].z; x[3] = acc[u].w;
+      }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nr * dg; e += 256) {
+      // bf16: consecutive lanes on consecutive rows (slots) of one dimension
+      // of the transposed V planes; fp32: along the row
+      const int rr = sizeof(T) == 2 ? e % nr : e / dg, i = sizeof(T) == 2 ? e / nr : e % dg;
+      KVStore<T>::put(kv, sl[j0 + rr], 1, h, i0 + i, xs[rr * (dg + 1) + i]);
+    }
+    return;
+  }
+  // ---- one row, q or k heads [h0, h0 + nh)
+  const int r = blockIdx.x / n_qk, grp = blockIdx.x % n_qk;
   // the row's sequence: its position / slot entries and its cache
   const int seq = ln.n > 1 ? r / ln.rows : 0, j = ln.n > 1 ? r - seq * ln.rows : r;
   pos = (const int32_t*)((const char*)pos + seq * ln.bytes);
   slot = (const int32_t*)((const char*)slot + seq * ln.bytes);
   const KVView kv = lane_kv<T>(kv_all, seq);
-  const int half = d / 2;
   const int hpw = 1024 / d;
-  const int n_heads = nq + 2 * nkv;
-  const int h0 = blockIdx.y * hpw;
-  const int nh = min(hpw, n_heads - h0);
-  const int width = n_heads * d;
+  const int h0 = grp * hpw;
+  const int nh = min(hpw, nq + nkv - h0);
   {
     const int e = 4 * threadIdx.x;
     const bool ok[1] = {e < nh * d};
@@ -1227,21 +1314,16 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
     const int lh = idx / half, i = idx % half;
     const int head = h0 + lh;
     const float* src = xs + lh * d;
-    if (head < nq + nkv) {
-      const float x1 = src[i], x2 = src[i + half];
-      const float y1 = x1 * c[i] - x2 * s[i];
-      const float y2 = x2 * c[i] + x1 * s[i];
-      if (head < nq) {
-        const int64_t base = ((int64_t)r * nq + head) * d;
-        Opnd<T>::store(q_out, qlo, base + i, y1);
-        Opnd<T>::store(q_out, qlo, base + i + half, y2);
-      } else {
-        KVStore<T>::put(kv, sl, 0, head - nq, i, y1);
-        KVStore<T>::put(kv, sl, 0, head - nq, i + half, y2);
-      }
+    const float x1 = src[i], x2 = src[i + half];
+    const float y1 = x1 * c[i] - x2 * s[i];
+    const float y2 = x2 * c[i] + x1 * s[i];
+    if (head < nq) {
+      const int64_t base = ((int64_t)r * nq + head) * d;
+      Opnd<T>::store(q_out, qlo, base + i, y1);
+      Opnd<T>::store(q_out, qlo, base + i + half, y2);
     } else {
-      KVStore<T>::put(kv, sl, 1, head - nq - nkv, i, src[i]);
-      KVStore<T>::put(kv, sl, 1, head - nq - nkv, i + half, src[i + half]);
+      KVStore<T>::put(kv, sl, 0, head - nq, i, y1);
+      KVStore<T>::put(kv, sl, 0, head - nq, i + half, y2);
     }
   }
 }
@@ -1381,8 +1463,8 @@ __global__ void kv_compact_kernel(KVView v, int64_t layer_elems, const int32_t* 
   for (int e = threadIdx.x; e < planes * v.d; e += blockDim.x) {
     const int sel = e / v.d, i = e % v.d;
     T vals[EAGLE_COMPACT_MAX];
-    for (int j = 0; j < L; ++j) vals[j] = kv_ptr<T>(lv, ctx + path[j], sel, h)[i];
-    for (int j = 0; j < L; ++j) kv_ptr<T>(lv, ctx + 1 + j, sel, h)[i] = vals[j];
+    for (int j = 0; j < L; ++j) vals[j] = *kv_elem<T>(lv, ctx + path[j], sel, h, i);
+    for (int j = 0; j < L; ++j) *kv_elem<T>(lv, ctx + 1 + j, sel, h, i) = vals[j];
   }
 }
 
@@ -1455,10 +1537,14 @@ hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int
   if (ln.n < 1 || ln.n > MAX_LANES || (ln.n > 1 && ln.rows * ln.n != M)) return hipErrorInvalidValue;
   if (d < 4 || d > 1024 || 1024 % d != 0 || ((nq + 2 * nkv) * d) % 4 != 0) return hipErrorInvalidValue;
   const int hpw = 1024 / d;
-  const dim3 grid(M, (nq + 2 * nkv + hpw - 1) / hpw);
+  const int n_qk = (nq + nkv + hpw - 1) / hpw;               // q/k workgroups per row
+  const int dg = std::min(32, d), rb = 64;                   // dims and rows per V workgroup
+  const int rps = ln.n > 1 ? ln.rows : M;
+  const int n_v = (d / dg) * nkv * ln.n * ((rps + rb - 1) / rb);
+  const dim3 grid(M * n_qk + n_v);
   DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv, ln),
-              hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv, ln));
+              hipLaunchKernelGGL(rope_kv_kernel<bf16_t>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (bf16_t*)q_out, qlo, kv, ln, M, n_qk, rb),
+              hipLaunchKernelGGL(rope_kv_kernel<float>, grid, dim3(256), 0, st, qkv, S, plane, nq, nkv, d, pos, slot, cos_t, sin_t, (float*)q_out, qlo, kv, ln, M, n_qk, rb));
   return hipGetLastError();
 }
 
@@ -1473,14 +1559,16 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
   LaneChunks lc{ln.n > 1 ? ln.rows : M, ln.n, {}};
   int n_chunks = 0;
   for (int b = 0; b < ln.n; ++b) {
-    const int c = (vis.key_end + ln.off[b] - vis.pre_lo + CHUNK - 1) / CHUNK;
+    // bf16 chunks start on page boundaries (chunk_base); fp32 rows walk keys from pre_lo
+    const int c0 = dtype == 1 ? (vis.pre_lo & ~(CHUNK - 1)) : vis.pre_lo;
+    const int c = (vis.key_end + ln.off[b] - c0 + CHUNK - 1) / CHUNK;
     if (c <= 0) return hipErrorInvalidValue;
     lc.chunks[b] = c;
     n_chunks = std::max(n_chunks, c);
   }
   if (dtype == 1) {
     if (d != 128) return hipErrorInvalidValue;
-    if (n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK) return hipErrorInvalidValue;
+    if (n_chunks > ATTN_MAX_CHUNKS || kv.page < CHUNK || kv.page % CHUNK) return hipErrorInvalidValue;
     if (vis.n_tree == 0 && ln.n == 1 && M >= 32 && group <= 8) {
       // causal rows without tree keys (prefill chunks): flash form, 16 rb
       // rows per workgroup, at least four (head, row block) pairs
@@ -1533,6 +1621,7 @@ hipError_t launch_attention(int dtype, const void* q, int64_t qlo, KVView kv, Ro
     for (int b = 0; b < ln.n; ++b) {
       const int want = 256 / units;   // one 512-thread workgroup per CU
       sa.splits[b] = std::max(1, std::min(want, lc.chunks[b] / 2));
+      sa.splits[b] = std::max(sa.splits[b], (lc.chunks[b] + ATTN_SPLIT_CHUNKS - 1) / ATTN_SPLIT_CHUNKS);
       lc.chunks[b] = sa.splits[b];
       sa.smax = std::max(sa.smax, sa.splits[b]);
     }

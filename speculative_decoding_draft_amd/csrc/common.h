@@ -135,6 +135,13 @@ template <> struct Mma<float> {
   }
 };
 
+// Workgroup barrier that waits only for this wave's LDS operations: global
+// loads still in flight (weights, cache chunks being copied) stay in flight
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

@@ -173,11 +173,6 @@ __device__ __forceinline__ void proj_core(const ProjArgs& a, int row0, int s_lo,
   }
 }
 
-__device__ __forceinline__ void lds_barrier() {
-  // Workgroup barrier that waits only for this wave's LDS operations: the
-  // weight and activation loads still in flight stay in flight across it.
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // bf16 version of proj_core with a software pipeline the compiler can keep
 // full: chunk c is multiplied while the weight fragments of chunks c+1 and

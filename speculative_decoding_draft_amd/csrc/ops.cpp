@@ -114,7 +114,10 @@ eagle_status eagle_op_attention(int32_t dtype, const void* q, const void* kv,
     return EAGLE_E_INVALID;
   if (dtype == EAGLE_BF16 ? head_dim != 128 : (head_dim < 1 || head_dim > 256))
     return EAGLE_E_INVALID;
-  const int chunks = (key_end - pre_lo + attn_chunk_keys() - 1) / attn_chunk_keys();
+  // bf16 key chunks start on page boundaries at or below pre_lo
+  const int ck = attn_chunk_keys();
+  const int c0 = dtype == EAGLE_BF16 ? pre_lo / ck * ck : pre_lo;
+  const int chunks = (key_end - c0 + ck - 1) / ck;
   if (chunks > attn_max_chunks()) return EAGLE_E_INVALID;
   const uint64_t need = eagle_op_attention_workspace(dtype, M, n_heads, head_dim, key_end);
   if (need > 0 && (!workspace || ws_bytes < need)) return EAGLE_E_BUFFER;

@@ -59,15 +59,25 @@ def _run(dtype, nq, nkv, d, M, pre_lo, prehi, tree_base, n_tree, masks, key_end,
     kp, k64 = _planes(K, dtype)
     vp, v64 = _planes(Vv, dtype)
     # paged cache: physical page perm[p] holds logical page p, planes K.., V..
+    # (bf16 V planes transposed within the page). Slots no row sees -- below
+    # pre_lo, and past key_end in the last page -- hold NaN in bf16 caches:
+    # the kernels read whole pages and must keep those slots out of the sums.
     n_pages = (key_end + PAGE - 1) // PAGE
     perm = torch.randperm(n_pages, generator=gen)
     planes = kp + vp
     pad = n_pages * PAGE - key_end
+    fill = float("nan") if dtype == BF16 else 0.0
     tiles = []
-    for pl in planes:
-        t = torch.cat([pl, torch.zeros((pad, nkv, d), dtype=pl.dtype)]) if pad else pl
-        tiles.append(t.reshape(n_pages, PAGE, nkv, d).permute(0, 2, 1, 3))   # [page, nkv, 64, d]
-    logical = torch.stack(tiles, dim=1)                                       # [page, planes, ...]
+    for n_pl, pl in enumerate(planes):
+        t = torch.cat([pl, torch.full((pad, nkv, d), fill, dtype=pl.dtype)]) if pad else pl.clone()
+        if dtype == BF16:
+            t[:pre_lo] = fill
+        t = t.reshape(n_pages, PAGE, nkv, d)
+        if dtype == BF16 and n_pl >= 2:
+            tiles.append(t.permute(0, 2, 3, 1))   # V^T: [page, nkv, d, 64]
+        else:
+            tiles.append(t.permute(0, 2, 1, 3))   # [page, nkv, 64, d]
+    logical = torch.stack([t.reshape(n_pages, -1) for t in tiles], dim=1)    # [page, planes, ...]
     phys = torch.empty_like(logical)
     phys[perm] = logical
     kv = phys.contiguous().cuda()
@@ -107,6 +117,7 @@ VERIFY = [
     ("c5_ctx1280_m61_gqa8", BF16, 64, 8, 128, 1280, 61),
     ("c2_ctx517_m27", BF16, 32, 32, 128, 517, 27),
     ("ragged_ctx70_m5", BF16, 32, 8, 128, 70, 5),
+    ("c3_ctx700_m61_from5", BF16, 32, 32, 128, 700, 61),
     ("c1_f32_ctx96_m17", F32, 4, 4, 64, 96, 17),
 ]
 
@@ -118,18 +129,21 @@ def test_verify_attention(name, dtype, nq, nkv, d, ctx, M):
     print(f"attention {name}", flush=True)
     gen = torch.Generator().manual_seed(ctx + M)
     parent, anc, masks = _random_tree(M, gen)
-    err = _run(dtype, nq, nkv, d, M, 0, [ctx] * M, ctx, M, masks, ctx + M, seed=ctx * 3 + M)
+    pre_lo = 5 if name.endswith("_from5") else 0   # a visible prefix not starting at a page
+    err = _run(dtype, nq, nkv, d, M, pre_lo, [ctx] * M, ctx, M, masks, ctx + M, seed=ctx * 3 + M)
     print(f"{name}: rel err {err:.2e}", flush=True)
     assert err < 1e-3
 
 
-@pytest.mark.parametrize("nq,nkv", [(32, 8), (32, 32)])
-def test_prefill_chunk_after_long_prefix(nq, nkv):
+@pytest.mark.parametrize("nq,nkv,pre_lo", [(32, 8, 0), (32, 32, 0), (32, 32, 1)])
+def test_prefill_chunk_after_long_prefix(nq, nkv, pre_lo):
     """A 512-row prefill chunk after 3072 cached keys: causal rows, no tree
-    keys (the one-pass form). Row r at slot 3072 + r sees slots 0..3072 + r."""
-    print(f"flash nq={nq} nkv={nkv}", flush=True)
+    keys (the one-pass form). Row r at slot 3072 + r sees slots
+    pre_lo..3072 + r (pre_lo = 1: the draft's catch-up over a prompt, whose
+    first token never enters the draft)."""
+    print(f"flash nq={nq} nkv={nkv} pre_lo={pre_lo}", flush=True)
     P, M = 3072, 512
-    err = _run(BF16, nq, nkv, 128, M, 0, [P + r + 1 for r in range(M)], 0, 0, None, P + M,
+    err = _run(BF16, nq, nkv, 128, M, pre_lo, [P + r + 1 for r in range(M)], 0, 0, None, P + M,
                seed=nq + nkv)
     print(f"flash 512 rows after {P}: rel err {err:.2e}", flush=True)
     assert err < 1e-3
