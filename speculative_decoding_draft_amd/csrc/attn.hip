@@ -1229,8 +1229,8 @@ __global__ __launch_bounds__(256) void sum_planes_kernel(const float* part, int 
 // embedding (rotate-half pairing) to q and k, writes q as an operand and k, v
 // into the cache slot of each row. Workgroups [0, M n_qk): one row and 1024 / d
 // consecutive q or k heads of it. The rest: 32 dimensions of one V head over
-// a block of rb rows of one sequence, so that the transposed V planes of a
-// bf16 cache are written by consecutive lanes at consecutive slots.
+// a block of rb = 32 rows of one sequence, so that the transposed V planes of
+// a bf16 cache are written by consecutive lanes at consecutive slots.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, int64_t plane, int nq,
                                                       int nkv, int d, const int32_t* pos,
@@ -1240,13 +1240,13 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
                                                       Lanes ln, int M, int n_qk, int rb) {
   // q/k workgroups use the first 1024 floats; V workgroups rb rows of dg
   // floats at a pitch of dg + 1 (the transposed reads fall in distinct banks)
-  __shared__ float xs[64 * 33];
+  __shared__ float xs[32 * 33];
   const int width = (nq + 2 * nkv) * d;
   const int half = d / 2;
   if ((int)blockIdx.x >= M * n_qk) {
     // ---- dimensions [i0, i0 + dg) of V head h over block blk of rb rows
-    // of one sequence (rb * dg <= 2048: two float4 of each plane per thread,
-    // all loads of the workgroup in one round)
+    // of one sequence (rb * dg <= 1024: one float4 of each plane per thread,
+    // its planes' loads in one round)
     const int dg = min(32, d), ndg = d / dg;
     int vb = blockIdx.x - M * n_qk;
     const int i0 = (vb % ndg) * dg;
@@ -1260,23 +1260,15 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
     const KVView kv = lane_kv<T>(kv_all, seq);
     const int col0 = (nq + nkv + h) * d + i0;
     {
-      bool ok[2];
-      const float* pp[2];
-      float4 acc[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 4 * (threadIdx.x + 256 * u);
-        ok[u] = e < nr * dg;
-        const int ec = ok[u] ? e : 0;
-        pp[u] = qkv + (int64_t)(r0 + ec / dg) * width + col0 + ec % dg;
-      }
-      plane_sums<2>(pp, ok, S, plane, acc);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 4 * (threadIdx.x + 256 * u);
-        if (!ok[u]) continue;
+      const int e = 4 * threadIdx.x;
+      const bool ok[1] = {e < nr * dg};
+      const int ec = ok[0] ? e : 0;
+      const float* pp[1] = {qkv + (int64_t)(r0 + ec / dg) * width + col0 + ec % dg};
+      float4 acc[1];
+      plane_sums<1>(pp, ok, S, plane, acc);
+      if (ok[0]) {
         float* x = xs + (e / dg) * (dg + 1) + e % dg;
-        x[0] = acc[u].x; x[1] = acc[u].y; x[2] = acc[u].z; x[3] = acc[u].w;
+        x[0] = acc[0].x; x[1] = acc[0].y; x[2] = acc[0].z; x[3] = acc[0].w;
       }
     }
     __syncthreads();
@@ -1538,7 +1530,7 @@ hipError_t launch_rope_kv(int dtype, const float* qkv, int S, int64_t plane, int
   if (d < 4 || d > 1024 || 1024 % d != 0 || ((nq + 2 * nkv) * d) % 4 != 0) return hipErrorInvalidValue;
   const int hpw = 1024 / d;
   const int n_qk = (nq + nkv + hpw - 1) / hpw;               // q/k workgroups per row
-  const int dg = std::min(32, d), rb = 64;                   // dims and rows per V workgroup
+  const int dg = std::min(32, d), rb = 32;                   // dims and rows per V workgroup
   const int rps = ln.n > 1 ? ln.rows : M;
   const int n_v = (d / dg) * nkv * ln.n * ((rps + rb - 1) / rb);
   const dim3 grid(M * n_qk + n_v);
