@@ -975,6 +975,17 @@ hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hip
       }
     }
   }
+  if constexpr (EPI == EPI_PART) {
+    if (nw == 6) {   // the two-m-tile six-wave shape of gemm_plan (one m-chunk)
+      if (mt != 2 || m_chunks != 1) return hipErrorInvalidValue;
+      const dim3 grid(tiles * a.splits), block(6 * 64);
+      if (tm)
+        hipExtLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+      else
+        hipLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, a);
+      return hipGetLastError();
+    }
+  }
   switch (mt) {
     case 1: return launch_proj_mt<T, 1, EPI>(a, tiles, m_chunks, st, tm);
     case 2: return launch_proj_mt<T, 2, EPI>(a, tiles, m_chunks, st, tm);
@@ -1081,6 +1092,18 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
       }
     }
   } else {
+    // bf16, two m-tiles, an output whose 96-row tiles number 96-128: six
+    // waves and two splits (192-256 workgroups of long pipelines, two
+    // partial planes for the consumer). The 27-row q|k|v projection: 20.8 us
+    // against 22.5 with eight waves and eight splits; narrower outputs (o,
+    // down) stay faster with eight waves.
+    if (dtype == 1 && p.mt == 2 && p.m_chunks == 1 && N_rows % 96 == 0 && N_rows / 96 >= 96 &&
+        N_rows / 96 <= 128 && K / 32 >= 64) {
+      p.nw = 6;
+      p.n_tiles = N_rows / 96;
+      p.splits = 2;
+      return p;
+    }
     p.n_tiles = (N_rows + rows_per_tile - 1) / rows_per_tile;
     const int steps = K / (dtype == 1 ? 32 : 16);
     // Split K as little as keeps each workgroup's pipeline long (>= 8 chunks
