@@ -976,13 +976,20 @@ hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hip
     }
   }
   if constexpr (EPI == EPI_PART) {
-    if (nw == 6) {   // the two-m-tile six-wave shape of gemm_plan (one m-chunk)
-      if (mt != 2 || m_chunks != 1) return hipErrorInvalidValue;
+    if (nw == 6) {   // the six-wave shape of gemm_plan (two or four m-tiles, one m-chunk)
+      if ((mt != 2 && mt != 4) || m_chunks != 1) return hipErrorInvalidValue;
       const dim3 grid(tiles * a.splits), block(6 * 64);
-      if (tm)
-        hipExtLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, tm->start, tm->stop, 0, a);
-      else
-        hipLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, a);
+      if (mt == 2) {
+        if (tm)
+          hipExtLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+        else
+          hipLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, a);
+      } else {
+        if (tm)
+          hipExtLaunchKernelGGL((proj_kernel<T, 4, 6, 2, 1, EPI_PART>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+        else
+          hipLaunchKernelGGL((proj_kernel<T, 4, 6, 2, 1, EPI_PART>), grid, block, 0, st, a);
+      }
       return hipGetLastError();
     }
   }
@@ -1092,13 +1099,14 @@ GemmPlan gemm_plan(int M, int N_rows, int K, int dtype, int epi) {
       }
     }
   } else {
-    // bf16, two m-tiles, an output whose 96-row tiles number 96-128: six
-    // waves and two splits (192-256 workgroups of long pipelines, two
-    // partial planes for the consumer). The 27-row q|k|v projection: 20.8 us
-    // against 22.5 with eight waves and eight splits; narrower outputs (o,
+    // bf16, two or four m-tiles, an output whose 96-row tiles number
+    // 96-128: six waves and two splits (192-256 workgroups of long
+    // pipelines, two partial planes for the consumer). The q|k|v projection:
+    // 20.8 us against 22.5 (eight waves, eight splits) at 27 rows, 26.0
+    // against 28.6 (eight waves, two splits) at 61; narrower outputs (o,
     // down) stay faster with eight waves.
-    if (dtype == 1 && p.mt == 2 && p.m_chunks == 1 && N_rows % 96 == 0 && N_rows / 96 >= 96 &&
-        N_rows / 96 <= 128 && K / 32 >= 64) {
+    if (dtype == 1 && (p.mt == 2 || p.mt == 4) && p.m_chunks == 1 && N_rows % 96 == 0 &&
+        N_rows / 96 >= 96 && N_rows / 96 <= 128 && K / 32 >= 64) {
       p.nw = 6;
       p.n_tiles = N_rows / 96;
       p.splits = 2;

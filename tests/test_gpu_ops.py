@@ -82,6 +82,8 @@ LINEAR = [  # (dtype, M, N, K): split-K, tails, several M tiles, prefill-sized M
     (BF16, 1, 4096, 4096), (BF16, 10, 4096, 8192), (BF16, 27, 12288, 4096),
     (BF16, 61, 4096, 11008), (BF16, 65, 1000, 1024), (BF16, 100, 256, 512),
     (BF16, 256, 512, 4096), (F32, 17, 256, 256), (F32, 17, 256, 688), (F32, 33, 1024, 512),
+    # the six-wave, two-split q|k|v shape at two and four m-tiles
+    (BF16, 61, 12288, 4096), (BF16, 54, 12288, 4096),
     # many rows (a batch's verify rows, prefill chunks): the 256-row weight
     # tiles with activations copied straight into LDS, above 128 rows and
     # from 81 rows for wide or deep shapes (128- or 256-row chunks): ragged N
