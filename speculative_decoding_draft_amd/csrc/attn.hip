@@ -1146,12 +1146,19 @@ __global__ __launch_bounds__(1024) void resnorm_kernel(float* h, int H, const fl
   float* x = h + (int64_t)r * H;
   const float* p[NV];
   bool ok[NV];
-  float4 v[NV];
+  float4 v[NV], g[NV];
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
     const int j = threadIdx.x + 1024 * u;
     ok[u] = j < n4;
     p[u] = part + (int64_t)r * H + 4 * j;
+  }
+  // the gain is requested with the row's first loads, not after the block
+  // reduction: a load issued behind the barrier would be one more memory
+  // round trip on the kernel's critical path
+  if (gain) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) g[u] = ld4(gain + 4 * min((int)threadIdx.x + 1024 * u, n4 - 1));
   }
   if (S > 0) {
     // the residual row is requested before the partial planes so the two
@@ -1194,10 +1201,55 @@ __global__ __launch_bounds__(1024) void resnorm_kernel(float* h, int H, const fl
   for (int u = 0; u < NV; ++u) {
     if (!ok[u]) continue;
     const int i = 4 * (threadIdx.x + 1024 * u);
-    const float4 g = ld4(gain + i);
-    const float4 y = make_float4(v[u].x * inv * g.x, v[u].y * inv * g.y, v[u].z * inv * g.z, v[u].w * inv * g.w);
+    const float4 y = make_float4(v[u].x * inv * g[u].x, v[u].y * inv * g[u].y, v[u].z * inv * g[u].z,
+                                 v[u].w * inv * g[u].w);
     if (out_f) *reinterpret_cast<float4*>(out_f + rb + i) = y;
     opnd_store4(out_t, lo, rb + i, y);
+  }
+}
+
+// resnorm_kernel's residual update with the normalization split over
+// RS_SLICES workgroups per row: workgroup (r, sl) of H / (4 RS_SLICES)
+// threads owns columns [sl H / RS_SLICES, (sl + 1) H / RS_SLICES) of row r,
+// four per thread. It writes h, the operand gain * h (the RMSNorm numerator)
+// and the slice's sum of squares to ss[RS_SLICES r + sl]; the projection
+// that consumes the operand multiplies its output rows by the RMSNorm
+// factor (RowScale). One workgroup per row pulls all of a row's partial
+// planes through one CU; RS_SLICES workgroups share them.
+template <typename T>
+__global__ __launch_bounds__(1024) void resnorm_slice_kernel(float* h, int H, const float* part, int S,
+                                                             int64_t plane, int set,
+                                                             const float* gain, T* out_t, int64_t lo,
+                                                             float* ss) {
+  __shared__ float red[16];
+  const int r = blockIdx.x, sl = blockIdx.y;
+  const int c = 4 * (sl * (int)blockDim.x + (int)threadIdx.x);   // < H: the grid tiles the row
+  const int64_t rc = (int64_t)r * H + c;
+  float* x = h + rc;
+  // the gain with the row's loads: none waits behind the reduction
+  const float4 g = gain ? ld4(gain + c) : make_float4(1.f, 1.f, 1.f, 1.f);
+  float4 v = set ? make_float4(0.f, 0.f, 0.f, 0.f) : ld4(x);
+  if (S > 0) {
+    const float* p[1] = {part + rc};
+    const bool ok[1] = {true};
+    float4 acc[1];
+    plane_sums<1>(p, ok, S, plane, acc);
+    add4(v, acc[0]);
+  }
+  if (S > 0 || set) *reinterpret_cast<float4*>(x) = v;
+  if (!gain) {
+    opnd_store4(out_t, lo, rc, v);
+    return;
+  }
+  opnd_store4(out_t, lo, rc, make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w));
+  float s2 = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  s2 = wave_sum(s2);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s2;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < (int)blockDim.x / 64; ++w) t += red[w];   // fixed order
+    ss[RS_SLICES * r + sl] = t;
   }
 }
 
@@ -1259,6 +1311,14 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
     const int32_t* sl = (const int32_t*)((const char*)slot + seq * ln.bytes);
     const KVView kv = lane_kv<T>(kv_all, seq);
     const int col0 = (nq + nkv + h) * d + i0;
+    // the cache slots of this thread's stores are requested with the plane
+    // loads (rb * dg <= 1024: at most four stores per thread)
+    int slt[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = min((int)threadIdx.x + 256 * k, nr * dg - 1);
+      slt[k] = sl[j0 + (sizeof(T) == 2 ? e % nr : e / dg)];
+    }
     {
       const int e = 4 * threadIdx.x;
       const bool ok[1] = {e < nr * dg};
@@ -1272,11 +1332,14 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
       }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < nr * dg; e += 256) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
       // bf16: consecutive lanes on consecutive rows (slots) of one dimension
       // of the transposed V planes; fp32: along the row
+      const int e = (int)threadIdx.x + 256 * k;
+      if (e >= nr * dg) break;
       const int rr = sizeof(T) == 2 ? e % nr : e / dg, i = sizeof(T) == 2 ? e / nr : e % dg;
-      KVStore<T>::put(kv, sl[j0 + rr], 1, h, i0 + i, xs[rr * (dg + 1) + i]);
+      KVStore<T>::put(kv, slt[k], 1, h, i0 + i, xs[rr * (dg + 1) + i]);
     }
     return;
   }
@@ -1290,6 +1353,15 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
   const int hpw = 1024 / d;
   const int h0 = grp * hpw;
   const int nh = min(hpw, nq + nkv - h0);
+  // the row's position and slot, then its cos / sin entries, are requested
+  // while the plane loads are in flight, not behind the barrier; when half
+  // divides 256 every pair this thread rotates has the same i
+  const int pj = pos[j], sl = slot[j];
+  const float* c = cos_t + (int64_t)pj * half;
+  const float* s = sin_t + (int64_t)pj * half;
+  const bool one_i = 256 % half == 0;
+  const int it = (int)threadIdx.x % half;
+  const float ci = one_i ? c[it] : 0.f, si = one_i ? s[it] : 0.f;
   {
     const int e = 4 * threadIdx.x;
     const bool ok[1] = {e < nh * d};
@@ -1299,16 +1371,14 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const float* qkv, int S, i
     if (ok[0]) *reinterpret_cast<float4*>(xs + e) = acc[0];
   }
   __syncthreads();
-  const float* c = cos_t + (int64_t)pos[j] * half;
-  const float* s = sin_t + (int64_t)pos[j] * half;
-  const int sl = slot[j];
   for (int idx = threadIdx.x; idx < nh * half; idx += 256) {
     const int lh = idx / half, i = idx % half;
     const int head = h0 + lh;
     const float* src = xs + lh * d;
     const float x1 = src[i], x2 = src[i + half];
-    const float y1 = x1 * c[i] - x2 * s[i];
-    const float y2 = x2 * c[i] + x1 * s[i];
+    const float cc = one_i ? ci : c[i], ss = one_i ? si : s[i];
+    const float y1 = x1 * cc - x2 * ss;
+    const float y2 = x2 * cc + x1 * ss;
     if (head < nq) {
       const int64_t base = ((int64_t)r * nq + head) * d;
       Opnd<T>::store(q_out, qlo, base + i, y1);
@@ -1509,6 +1579,20 @@ hipError_t launch_resnorm(int dtype, float* h, int H, int M, const float* part, 
     default: RN(4); break;
   }
 #undef RN
+  return hipGetLastError();
+}
+
+bool resnorm_slices_fit(int H) { return H > 0 && H % (64 * RS_SLICES * 4) == 0 && H <= 16384; }
+
+hipError_t launch_resnorm_slices(int dtype, float* h, int H, int M, const float* part, int S,
+                                 int64_t plane, int set, const float* gain, void* out_t, int64_t lo,
+                                 float* ss, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (!resnorm_slices_fit(H) || (gain && !ss)) return hipErrorInvalidValue;
+  const dim3 grid(M, RS_SLICES), block(H / (4 * RS_SLICES));
+  DT_DISPATCH(dtype,
+              hipLaunchKernelGGL(resnorm_slice_kernel<bf16_t>, grid, block, 0, st, h, H, part, S, plane, set, gain, (bf16_t*)out_t, lo, ss),
+              hipLaunchKernelGGL(resnorm_slice_kernel<float>, grid, block, 0, st, h, H, part, S, plane, set, gain, (float*)out_t, lo, ss));
   return hipGetLastError();
 }
 

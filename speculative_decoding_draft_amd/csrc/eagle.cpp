@@ -297,6 +297,8 @@ struct eagle_ctx {
   int32_t *tpt, *dpt;
   float *h, *tfeat, *gbuf, *hcat, *dout, *opart, *mlpart, *gpart, *hpart, *logits, *margin, *logp;
   int64_t dout_stride = 0;   // floats between two sequences' draft outputs
+  float* rss;                // per-slice sums of squares of the sliced RMSNorm
+  const float* xrs = nullptr;   // rss when xop holds RMSNorm numerators, else null
   float* ebuf;
   double* zpart;
   void *xop, *qop, *aop, *fop, *lmh, *lmh2;   // activation operands (two planes for bf16)
@@ -408,6 +410,7 @@ uint64_t plan_scratch(const Derived& z, eagle_ctx* x) {
   TAKE(opart, float, (uint64_t)z.max_chunks * M * z.nq * z.d);
   TAKE(mlpart, float, (uint64_t)z.max_chunks * M * z.nq * 2);
   TAKE(gpart, float, gemm_ws_floats(z));
+  TAKE(rss, float, (uint64_t)M * RS_SLICES);
   // LM-head partials: the largest need over every row count a call can take
   // (calls above 80 rows run in 64-row passes)
   uint64_t hp = 0;
@@ -618,13 +621,34 @@ KVView lane_view(KVView v, int b, int esz) {
 // Applies the pending split-K partial planes of a projection to the
 // residual stream h (or sets h to their sum) and writes the next operand:
 // RMSNorm(h) * gain, or h itself when gain is null.
+// bf16 rows without an fp32 copy of the result take the sliced form: the
+// operand is then gain * h and xrs points at the sums of squares, which the
+// projection that reads xop next (q|k|v or gate|up) turns into each row's
+// RMSNorm factor (RowScale).
 eagle_status resnorm(eagle_ctx* c, float* h, int M, int S, bool set, const float* gain,
                      float* out_f) {
   const Derived& z = c->z;
+  if (z.dt == 1 && !out_f && resnorm_slices_fit(z.H)) {
+    PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * (12.0 + 4.0 * S),
+             launch_resnorm_slices(z.dt, h, z.H, M, c->gpart, S, (int64_t)M * z.H, set ? 1 : 0,
+                                   gain, c->xop, c->xlo, c->rss, c->st));
+    c->xrs = gain ? c->rss : nullptr;
+    return EAGLE_OK;
+  }
   PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * (12.0 + 4.0 * S),
            launch_resnorm(z.dt, h, z.H, M, c->gpart, S, (int64_t)M * z.H, set ? 1 : 0, gain,
                           c->cfg.rms_eps, c->xop, c->xlo, out_f, c->st));
+  c->xrs = nullptr;
   return EAGLE_OK;
+}
+
+// The RowScale of a projection whose operand is xop.
+RowScale xop_scale(const eagle_ctx* c) {
+  RowScale r;
+  r.ss = c->xrs;
+  r.H = c->z.H;
+  r.eps = c->cfg.rms_eps;
+  return r;
 }
 
 // One decoder layer over M rows (the rows of every sequence of `ln`). On
@@ -641,7 +665,7 @@ eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, fl
   int S = 1;
   PROFILED_KERNEL(cls_part, gemm_bytes(z, M, z.qkv_rows, kin, z.qkv_rows, EPI_PART),
            launch_gemm(dt, EPI_PART, w.wqkv, c->xop, c->xlo, M, z.qkv_rows, kin, c->gpart,
-                       z.qkv_rows, nullptr, 0, &S, c->st, tm_));
+                       z.qkv_rows, nullptr, 0, &S, c->st, tm_, xop_scale(c)));
   PROFILED(EAGLE_PROF_ROWS, (double)M * z.qkv_rows * 4.0 * (S + 1),
            launch_rope_kv(dt, c->gpart, S, (int64_t)M * z.qkv_rows, M, z.nq, z.nkv, z.d, pos, slot,
                           c->cos_t, c->sin_t, c->qop, c->qlo, kv, c->st, ln));
@@ -655,7 +679,7 @@ eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, fl
   SCHK(resnorm(c, h, M, S, false, w.ffn_norm, nullptr));
   PROFILED_KERNEL(cls_glu, gemm_bytes(z, M, 2 * z.F, z.H, z.F, EPI_SWIGLU),
            launch_gemm(dt, EPI_SWIGLU, w.wgu, c->xop, c->xlo, M, z.F, z.H, c->gpart, 2 * z.F,
-                       c->fop, c->flo, nullptr, c->st, tm_));
+                       c->fop, c->flo, nullptr, c->st, tm_, xop_scale(c)));
   PROFILED_KERNEL(cls_part, gemm_bytes(z, M, z.H, z.F, z.H, EPI_PART),
            launch_gemm(dt, EPI_PART, w.wdown, c->fop, c->flo, M, z.H, z.F, c->gpart, z.H, nullptr,
                        0, s_down, c->st, tm_));
@@ -707,6 +731,7 @@ eagle_status draft_pass(eagle_ctx* c, Span s, const int32_t* tok, const float* f
     PROFILED(EAGLE_PROF_ROWS, (double)M * z.H * 12.0,
              launch_draft_input_e1(z.dt, c->embed, tok, feat, idx, M, z.H, c->xop, c->xlo, c->st,
                                    ln, feat_stride, idx_bytes));
+    c->xrs = nullptr;   // [E[t]; f] feeds the FC unscaled
     PROFILED_KERNEL(EAGLE_PROF_DRAFT, gemm_bytes(z, M, z.H, 2 * z.H, z.H, EPI_PART),
              launch_gemm(z.dt, EPI_PART, c->fc, c->xop, c->xlo, M, z.H, 2 * z.H, c->gpart, z.H,
                          nullptr, 0, &S, c->st, tm_));
@@ -716,6 +741,7 @@ eagle_status draft_pass(eagle_ctx* c, Span s, const int32_t* tok, const float* f
              launch_draft_input_e3(z.dt, c->embed, tok, feat, idx, c->dl.attn_norm, c->cfg.rms_eps,
                                    M, z.H, c->xop, c->xlo, hout, c->st, ln, feat_stride,
                                    idx_bytes));
+    c->xrs = nullptr;   // that operand is normalized
   }
   int sd = 1;
   SCHK(layer_core(c, c->dl, z.kin_draft, M, hout, pos, slot, lane_view(c->dkv, s.first, z.esz),

@@ -51,7 +51,16 @@ struct ProjArgs {
   int64_t ldy, plane;
   void* Yt;             // EPI_SWIGLU: operand [M, F] (lo plane at Yt + ytlo)
   int64_t ytlo;
+  const float* rs = nullptr;   // RowScale: sums of squares, RS_SLICES per row (or none)
+  int rs_h = 0;
+  float rs_eps = 0.f;
 };
+static_assert(RS_SLICES == 4, "the projections read a row's sums of squares as one float4");
+
+// RowScale factor of a row from its per-slice sums of squares (fixed order).
+__device__ __forceinline__ float row_scale(float4 v, int H, float eps) {
+  return 1.0f / sqrtf((v.x + v.y + v.z + v.w) / (float)H + eps);
+}
 
 template <typename T, int MT, int NW, int CS>
 struct ProjShape {
@@ -307,7 +316,10 @@ constexpr int proj_lds_elems() {
   return act > gate ? act : gate;
 }
 
-template <typename T, int MT, int NW, int CS, int NB, int EPI>
+// RS: the operand rows are RMSNorm numerators and a.rs holds their sums of
+// squares (RowScale); a separate instantiation, so projections without it
+// keep no registers for it.
+template <typename T, int MT, int NW, int CS, int NB, int EPI, bool RS = false>
 __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   using S = ProjShape<T, MT, NW, CS>;
   static_assert(NB == 1 || Opnd<T>::SPLIT, "several row blocks per wave: bf16 only");
@@ -335,12 +347,28 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   } else {
     row0 = (tile * NW + wave) * WR;
   }
+  // RowScale: this lane's rows' sums of squares, requested before the main
+  // loop (they are the oldest loads, so the loop's waits cover them) and
+  // turned into the factor after it
+  float4 rsv[RS ? MT : 1];
+  if constexpr (RS) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) rsv[t] = ld4(a.rs + RS_SLICES * min(m0 + 16 * t + lr, a.M - 1));
+  }
   f32x4 acc[NB][MT];
   if constexpr (Opnd<T>::SPLIT) {
     proj_core_bf16<MT, NW, CS, NB>(b, row0, s_lo, s_hi, xs, acc);
   } else {
     static_assert(NB == 1, "fp32 projections take one row block per wave");
     proj_core<T, MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc[0]);
+  }
+  if constexpr (RS) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float f = row_scale(rsv[t], a.rs_h, a.rs_eps);
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) acc[jb][t] *= f;
+    }
   }
 
   if (EPI == EPI_SWIGLU) {
@@ -544,6 +572,15 @@ __global__ __launch_bounds__(WC * XG * 64) void rows_kernel(ProjArgs a) {
   const int row0 = (tile * WC + wc) * 16 * NB;
   f32x4 acc[NB][MT];
   rows_core<MT, WC, XG>(b, row0, s_lo, s_hi, xg, xs0, xs1, acc);
+  if (a.rs) {   // RowScale (uniform); loaded here: this kernel's registers are spoken for
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float f = row_scale(ld4(a.rs + RS_SLICES * min(m0 + xrow0 + 16 * t + lr, a.M - 1)),
+                                a.rs_h, a.rs_eps);
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) acc[jb][t] *= f;
+    }
+  }
   float* Y = a.Y + (int64_t)split * a.plane;
 #pragma unroll
   for (int jb = 0; jb < NB; ++jb) {
@@ -922,16 +959,33 @@ int chunk_for(int mt, int kind) {
   return kind == EPI_SWIGLU ? chunk_t<EPI_SWIGLU>(mt) : kind == KIND_HEAD ? chunk_t<KIND_HEAD>(mt) : chunk_t<EPI_PART>(mt);
 }
 
-template <typename T, int MT, int EPI>
-hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st, const KTiming* tm) {
-  constexpr int NW = Cfg<MT, EPI>::NW, CS = Cfg<MT, EPI>::CS;
-  constexpr int NB = Opnd<T>::SPLIT ? Cfg<MT, EPI>::NB : 1;
-  const dim3 grid(tiles * a.splits, m_chunks), block(NW * 64);
+// One dispatch of proj_kernel<T, MT, NW, CS, NB, EPI, RS>, with RS chosen by
+// whether the projection scales its rows (bf16 only).
+template <typename T, int MT, int NW, int CS, int NB, int EPI>
+hipError_t proj_dispatch(const ProjArgs& a, dim3 grid, dim3 block, hipStream_t st, const KTiming* tm) {
+  if constexpr (Opnd<T>::SPLIT) {
+    if (a.rs) {
+      if (tm)
+        hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI, true>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+      else
+        hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI, true>), grid, block, 0, st, a);
+      return hipGetLastError();
+    }
+  } else {
+    if (a.rs) return hipErrorInvalidValue;
+  }
   if (tm)
     hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI>), grid, block, 0, st, tm->start, tm->stop, 0, a);
   else
     hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+template <typename T, int MT, int EPI>
+hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_t st, const KTiming* tm) {
+  constexpr int NW = Cfg<MT, EPI>::NW, CS = Cfg<MT, EPI>::CS;
+  constexpr int NB = Opnd<T>::SPLIT ? Cfg<MT, EPI>::NB : 1;
+  return proj_dispatch<T, MT, NW, CS, NB, EPI>(a, dim3(tiles * a.splits, m_chunks), dim3(NW * 64), st, tm);
 }
 
 // SwiGLU with six or fourteen waves (48 or 112 output columns per
@@ -942,12 +996,7 @@ hipError_t launch_proj_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_
 template <typename T, int MT, int NW>
 hipError_t launch_swiglu_w(const ProjArgs& a, int tiles, hipStream_t st, const KTiming* tm) {
   constexpr int CS = (NW == 6 && MT == 2) ? 4 : 2;
-  const dim3 grid(tiles), block(NW * 64);
-  if (tm)
-    hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, 1, EPI_SWIGLU>), grid, block, 0, st, tm->start, tm->stop, 0, a);
-  else
-    hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, 1, EPI_SWIGLU>), grid, block, 0, st, a);
-  return hipGetLastError();
+  return proj_dispatch<T, MT, NW, CS, 1, EPI_SWIGLU>(a, dim3(tiles), dim3(NW * 64), st, tm);
 }
 
 template <typename T, int EPI>
@@ -979,18 +1028,8 @@ hipError_t launch_proj_t(int mt, const ProjArgs& a, int tiles, int m_chunks, hip
     if (nw == 6) {   // the six-wave shape of gemm_plan (two or four m-tiles, one m-chunk)
       if ((mt != 2 && mt != 4) || m_chunks != 1) return hipErrorInvalidValue;
       const dim3 grid(tiles * a.splits), block(6 * 64);
-      if (mt == 2) {
-        if (tm)
-          hipExtLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, tm->start, tm->stop, 0, a);
-        else
-          hipLaunchKernelGGL((proj_kernel<T, 2, 6, 2, 1, EPI_PART>), grid, block, 0, st, a);
-      } else {
-        if (tm)
-          hipExtLaunchKernelGGL((proj_kernel<T, 4, 6, 2, 1, EPI_PART>), grid, block, 0, st, tm->start, tm->stop, 0, a);
-        else
-          hipLaunchKernelGGL((proj_kernel<T, 4, 6, 2, 1, EPI_PART>), grid, block, 0, st, a);
-      }
-      return hipGetLastError();
+      return mt == 2 ? proj_dispatch<T, 2, 6, 2, 1, EPI_PART>(a, grid, block, st, tm)
+                     : proj_dispatch<T, 4, 6, 2, 1, EPI_PART>(a, grid, block, st, tm);
     }
   }
   switch (mt) {
@@ -1146,7 +1185,7 @@ bool swiglu_by_planes(int dtype, int M) { return dtype == 1 && M > 128; }
 
 hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
                        int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int splits_out[1],
-                       hipStream_t stream, const KTiming* tm) {
+                       hipStream_t stream, const KTiming* tm, RowScale rsc) {
   if (M <= 0) return hipSuccess;
   if (epi == EPI_SWIGLU && swiglu_by_planes(dtype, M)) {
     // many rows: gate|up as one split-K projection (rows_kernel) into the
@@ -1156,7 +1195,7 @@ hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t
     if (!Y || (N & 3)) return hipErrorInvalidValue;
     int S = 1;
     hipError_t e = launch_gemm(dtype, EPI_PART, W, x, xlo, M, 2 * N, K, Y, 2 * N, nullptr, 0, &S,
-                               stream, tm);
+                               stream, tm, rsc);
     if (e != hipSuccess) return e;
     const dim3 grid((N / 4 + 255) / 256, M);
     hipLaunchKernelGGL(silu_mul_planes_kernel, grid, dim3(256), 0, stream, Y, S, (int64_t)M * 2 * N, M,
@@ -1173,6 +1212,8 @@ hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t
   a.steps_per_split = (steps + p.splits - 1) / p.splits;
   a.Y = Y; a.ldy = ldy; a.plane = (int64_t)M * ldy;
   a.Yt = Yt; a.ytlo = ytlo;
+  a.rs = rsc.ss; a.rs_h = rsc.H; a.rs_eps = rsc.eps;
+  if (rsc.ss && rsc.H <= 0) return hipErrorInvalidValue;
   if (splits_out) splits_out[0] = p.splits;
   if (p.xg == 2)
     return p.mt == 8 ? launch_rows_mt<8>(a, p.n_tiles, p.m_chunks, stream, tm)

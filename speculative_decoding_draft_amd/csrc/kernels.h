@@ -25,9 +25,21 @@ struct KTiming {
   hipEvent_t start, stop;
 };
 
+// Optional scale of output rows, for an operand whose rows are the RMSNorm
+// numerators gain * h (launch_resnorm_slices): the sums of squares of row m
+// sit in ss[RS_SLICES m .. RS_SLICES m + RS_SLICES - 1], and output row m is
+// multiplied by 1 / sqrt((their sum) / H + eps), the row's RMSNorm factor.
+// By linearity every partial plane, and so their sum, carries the factor.
+constexpr int RS_SLICES = 4;
+struct RowScale {
+  const float* ss = nullptr;   // null: no scaling
+  int H = 0;
+  float eps = 0.f;
+};
+
 hipError_t launch_gemm(int dtype, int epi, const void* W, const void* x, int64_t xlo, int M, int N,
                        int K, float* Y, int64_t ldy, void* Yt, int64_t ytlo, int* splits_out,
-                       hipStream_t stream, const KTiming* tm = nullptr);
+                       hipStream_t stream, const KTiming* tm = nullptr, RowScale rs = RowScale());
 
 // Fragment packing of the first 16*n_blocks rows of a bf16 [*, K] matrix
 // from row-major `src` to `dst` (non-overlapping; same byte range per block).
@@ -113,6 +125,16 @@ hipError_t launch_embed(int dtype, const void* E, int H, const int32_t* tok, int
 hipError_t launch_resnorm(int dtype, float* h, int H, int M, const float* part, int S,
                           int64_t plane, int set, const float* gain, float eps, void* out_t,
                           int64_t lo, float* out_f, hipStream_t st);
+// The same residual update with the RMSNorm spread over RS_SLICES
+// workgroups per row (a row's partial planes are more bytes than one CU
+// pulls quickly): out = gain * h[r], the RMSNorm numerator, and ss[r] gets
+// the per-slice sums of squares of h[r] for the projection that consumes
+// out (RowScale). Without a gain out = h[r] and ss is not written. Needs
+// H % (64 * RS_SLICES * 4) == 0 and H <= 16384.
+bool resnorm_slices_fit(int H);
+hipError_t launch_resnorm_slices(int dtype, float* h, int H, int M, const float* part, int S,
+                                 int64_t plane, int set, const float* gain, void* out_t, int64_t lo,
+                                 float* ss, hipStream_t st);
 // dst[r] = (add ? dst[r] : 0) + sum_s part[s][r] for M rows of width W.
 hipError_t launch_sum_planes(const float* part, int S, int64_t plane, int M, int W, float* dst,
                              int add, hipStream_t st);
