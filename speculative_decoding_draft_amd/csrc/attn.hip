@@ -1424,30 +1424,63 @@ __global__ void draft_input_e1_kernel(const T* E, const int32_t* tok, const floa
   }
 }
 
-template <typename T>
+// Four consecutive elements of a weight row as floats (bf16: one 8-byte load).
+template <typename T> __device__ __forceinline__ float4 ld4e(const T* p);
+template <> __device__ __forceinline__ float4 ld4e<float>(const float* p) { return ld4(p); }
+template <> __device__ __forceinline__ float4 ld4e<bf16_t>(const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_lo_f(w.x), bf16_hi_f(w.x), bf16_lo_f(w.y), bf16_hi_f(w.y));
+}
+
+// E3 draft input of one row: x = RMSNorm([E[t]; g]) * gain over the 2H-wide
+// concatenation (operand), h = g. Thread t owns float4 groups t + 256 u of
+// each half; all of its loads (embedding, feature, both gain halves) go
+// out in one round, and the row's sum of squares is one wave reduction
+// plus a four-way sum in LDS.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void draft_input_e3_kernel(const T* E, const int32_t* tok,
                                                              const float* feat, const int32_t* idx,
                                                              const float* gain, float eps, int H,
                                                              T* x, int64_t lo, float* h, Lanes ln,
                                                              int64_t feat_stride, int64_t idx_bytes) {
-  __shared__ float sh[256];
+  __shared__ float sh[4];
   const int r = blockIdx.x;
   const int b = ln.n > 1 ? r / ln.rows : 0, j = r - b * (ln.n > 1 ? ln.rows : 0);
   const T* e = E + (int64_t)lane_at(tok, b, ln.bytes)[j] * H;
   const float* f = feat + b * feat_stride + (int64_t)lane_at(idx, b, idx_bytes)[j] * H;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += 256) {
-    const float a = Elem<T>::to_f(e[i]);
-    ss += a * a;
+  const int n4 = H / 4;
+  float4 ev[NV], fv[NV], ge[NV], gf[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int q = 4 * min((int)threadIdx.x + 256 * u, n4 - 1);   // past the end: a repeat, not used
+    ev[u] = ld4e(e + q);
+    fv[u] = ld4(f + q);
+    ge[u] = ld4(gain + q);
+    gf[u] = ld4(gain + H + q);
   }
-  for (int i = threadIdx.x; i < H; i += 256) ss += f[i] * f[i];
-  ss = block_sum_256(ss, sh);
-  const float inv = 1.0f / sqrtf(ss / (float)(2 * H) + eps);
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < NV; ++u)
+    if ((int)threadIdx.x + 256 * u < n4)
+      ss += ev[u].x * ev[u].x + ev[u].y * ev[u].y + ev[u].z * ev[u].z + ev[u].w * ev[u].w +
+            fv[u].x * fv[u].x + fv[u].y * fv[u].y + fv[u].z * fv[u].z + fv[u].w * fv[u].w;
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf(((sh[0] + sh[1]) + (sh[2] + sh[3])) / (float)(2 * H) + eps);
   const int64_t row = (int64_t)r * 2 * H;
-  for (int i = threadIdx.x; i < H; i += 256) {
-    Opnd<T>::store(x, lo, row + i, Elem<T>::to_f(e[i]) * inv * gain[i]);
-    Opnd<T>::store(x, lo, row + H + i, f[i] * inv * gain[H + i]);
-    h[(int64_t)r * H + i] = f[i];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int g4 = (int)threadIdx.x + 256 * u;
+    if (g4 >= n4) continue;
+    const int q = 4 * g4;
+    opnd_store4(x, lo, row + q,
+                make_float4(ev[u].x * inv * ge[u].x, ev[u].y * inv * ge[u].y, ev[u].z * inv * ge[u].z,
+                            ev[u].w * inv * ge[u].w));
+    opnd_store4(x, lo, row + H + q,
+                make_float4(fv[u].x * inv * gf[u].x, fv[u].y * inv * gf[u].y, fv[u].z * inv * gf[u].z,
+                            fv[u].w * inv * gf[u].w));
+    *reinterpret_cast<float4*>(h + (int64_t)r * H + q) = fv[u];
   }
 }
 
@@ -1470,6 +1503,37 @@ __global__ void gather_t_kernel(const T* src, int64_t ld, int64_t src_lo, const 
 
 // Row b: sequence b's root row (row b * src_rows + acc_b[0]) of the fp32
 // rows src_f and of the operand rows src_t (width W each).
+// gather_t_kernel in 16-byte pieces (widths, pitches and plane offsets in
+// whole pieces, 16-byte aligned buffers): eight pieces of each plane in
+// flight per thread; threads past the end repeat the last piece (same value,
+// same place) so no load waits behind a conditional store.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_t16_kernel(const T* src, int64_t ld, int64_t src_lo,
+                                                         const int32_t* idx, int W, T* dst,
+                                                         int64_t dst_lo) {
+  constexpr int EPV = 16 / sizeof(T);
+  constexpr int PL = Opnd<T>::SPLIT ? 2 : 1;
+  const int r = blockIdx.x;
+  const T* s = src + (int64_t)idx[r] * ld;
+  T* d = dst + (int64_t)r * W;
+  const int nv = W / EPV;
+  for (int i0 = 0; i0 < nv; i0 += 256 * 8) {
+    uint4 v[8][PL];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + 256 * u + (int)threadIdx.x, nv - 1) * EPV;
+#pragma unroll
+      for (int pl = 0; pl < PL; ++pl) v[u][pl] = *reinterpret_cast<const uint4*>(s + pl * src_lo + i);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + 256 * u + (int)threadIdx.x, nv - 1) * EPV;
+#pragma unroll
+      for (int pl = 0; pl < PL; ++pl) *reinterpret_cast<uint4*>(d + pl * dst_lo + i) = v[u][pl];
+    }
+  }
+}
+
 template <typename T>
 __global__ void gather_roots_kernel(const float* src_f, const T* src_t, int64_t src_lo, int src_rows,
                                     const int32_t* acc, int W, float* dst_f, int64_t dst_stride,
@@ -1733,9 +1797,23 @@ hipError_t launch_draft_input_e3(int dtype, const void* E, const int32_t* tok, c
                                  int64_t feat_stride, int64_t idx_bytes) {
   if (M <= 0) return hipSuccess;
   if (lanes_bad(ln, M)) return hipErrorInvalidValue;
-  DT_DISPATCH(dtype,
-              hipLaunchKernelGGL(draft_input_e3_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)E, tok, feat, idx, gain, eps, H, (bf16_t*)x, lo, h, ln, feat_stride, idx_bytes),
-              hipLaunchKernelGGL(draft_input_e3_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)E, tok, feat, idx, gain, eps, H, (float*)x, lo, h, ln, feat_stride, idx_bytes));
+  // float4 groups: H a multiple of 4 (and of the 16-byte feature rows), at most 8 groups per
+  // thread and half
+  if (H % 4 != 0 || H > 8 * 1024 || feat_stride % 4 != 0) return hipErrorInvalidValue;
+  const int nv = (H / 4 + 255) / 256;
+#define E3(NV)                                                                                        \
+  DT_DISPATCH(dtype,                                                                                  \
+              hipLaunchKernelGGL((draft_input_e3_kernel<bf16_t, NV>), dim3(M), dim3(256), 0, st,      \
+                                 (const bf16_t*)E, tok, feat, idx, gain, eps, H, (bf16_t*)x, lo, h,   \
+                                 ln, feat_stride, idx_bytes),                                         \
+              hipLaunchKernelGGL((draft_input_e3_kernel<float, NV>), dim3(M), dim3(256), 0, st,       \
+                                 (const float*)E, tok, feat, idx, gain, eps, H, (float*)x, lo, h, ln, \
+                                 feat_stride, idx_bytes))
+  if (nv <= 1) E3(1);
+  else if (nv <= 2) E3(2);
+  else if (nv <= 4) E3(4);
+  else E3(8);
+#undef E3
   return hipGetLastError();
 }
 
@@ -1760,6 +1838,15 @@ hipError_t launch_gather_f32(const float* src, int64_t ld, const int32_t* idx, i
 hipError_t launch_gather_t(int dtype, const void* src, int64_t ld, int64_t src_lo, const int32_t* idx,
                            int M, int W, void* dst, int64_t dst_lo, hipStream_t st) {
   if (M <= 0) return hipSuccess;
+  const int epv = dtype == 1 ? 8 : 4;
+  const bool vec = W % epv == 0 && ld % epv == 0 && src_lo % epv == 0 && dst_lo % epv == 0 &&
+                   ((uintptr_t)src & 15) == 0 && ((uintptr_t)dst & 15) == 0;
+  if (vec) {
+    DT_DISPATCH(dtype,
+                hipLaunchKernelGGL(gather_t16_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)src, ld, src_lo, idx, W, (bf16_t*)dst, dst_lo),
+                hipLaunchKernelGGL(gather_t16_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)src, ld, src_lo, idx, W, (float*)dst, dst_lo));
+    return hipGetLastError();
+  }
   DT_DISPATCH(dtype,
               hipLaunchKernelGGL(gather_t_kernel<bf16_t>, dim3(M), dim3(256), 0, st, (const bf16_t*)src, ld, src_lo, idx, W, (bf16_t*)dst, dst_lo),
               hipLaunchKernelGGL(gather_t_kernel<float>, dim3(M), dim3(256), 0, st, (const float*)src, ld, src_lo, idx, W, (float*)dst, dst_lo));
