@@ -1112,12 +1112,26 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float* q, KVView kv_
 }
 
 // ---------------------------------------------------------------- rows
+// Four consecutive elements of a weight row as floats (bf16: one 8-byte load).
+template <typename T> __device__ __forceinline__ float4 ld4e(const T* p);
+template <> __device__ __forceinline__ float4 ld4e<float>(const float* p) { return ld4(p); }
+template <> __device__ __forceinline__ float4 ld4e<bf16_t>(const bf16_t* p) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  return make_float4(bf16_lo_f(w.x), bf16_hi_f(w.x), bf16_lo_f(w.y), bf16_hi_f(w.y));
+}
+
 template <typename T>
 __global__ void embed_kernel(const T* E, int H, const int32_t* tok, float* h, Lanes ln) {
   const int r = blockIdx.x;
   const int b = ln.n > 1 ? r / ln.rows : 0, j = r - b * (ln.n > 1 ? ln.rows : 0);
   const T* e = E + (int64_t)lane_at(tok, b, ln.bytes)[j] * H;
-  for (int i = threadIdx.x; i < H; i += blockDim.x) h[(int64_t)r * H + i] = Elem<T>::to_f(e[i]);
+  float* d = h + (int64_t)r * H;
+  if (H % 4 == 0) {   // four elements per thread and step (uniform)
+    for (int i = 4 * threadIdx.x; i < H; i += 4 * blockDim.x)
+      *reinterpret_cast<float4*>(d + i) = ld4e(e + i);
+    return;
+  }
+  for (int i = threadIdx.x; i < H; i += blockDim.x) d[i] = Elem<T>::to_f(e[i]);
 }
 
 __device__ __forceinline__ float block_sum_256(float v, float* sh) {
@@ -1424,14 +1438,6 @@ __global__ void draft_input_e1_kernel(const T* E, const int32_t* tok, const floa
   }
 }
 
-// Four consecutive elements of a weight row as floats (bf16: one 8-byte load).
-template <typename T> __device__ __forceinline__ float4 ld4e(const T* p);
-template <> __device__ __forceinline__ float4 ld4e<float>(const float* p) { return ld4(p); }
-template <> __device__ __forceinline__ float4 ld4e<bf16_t>(const bf16_t* p) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  return make_float4(bf16_lo_f(w.x), bf16_hi_f(w.x), bf16_lo_f(w.y), bf16_hi_f(w.y));
-}
-
 // E3 draft input of one row: x = RMSNorm([E[t]; g]) * gain over the 2H-wide
 // concatenation (operand), h = g. Thread t owns float4 groups t + 256 u of
 // each half; all of its loads (embedding, feature, both gain halves) go
@@ -1540,6 +1546,19 @@ __global__ void gather_roots_kernel(const float* src_f, const T* src_t, int64_t 
                                     T* dst_t, int64_t dst_lo, Lanes ln) {
   const int b = blockIdx.x;
   const int64_t row = (int64_t)b * src_rows + lane_at(acc, b, ln.bytes)[0];
+  constexpr int EPV = 16 / sizeof(T);
+  if (W % EPV == 0 && dst_stride % 4 == 0 && src_lo % EPV == 0 && dst_lo % EPV == 0) {
+    // 16-byte pieces (uniform): the fp32 row, then the operand planes
+    for (int i = 4 * threadIdx.x; i < W; i += 4 * blockDim.x)
+      *reinterpret_cast<float4*>(dst_f + b * dst_stride + i) = ld4(src_f + row * W + i);
+    for (int i = EPV * threadIdx.x; i < W; i += EPV * blockDim.x) {
+      *reinterpret_cast<uint4*>(dst_t + (int64_t)b * W + i) = *reinterpret_cast<const uint4*>(src_t + row * W + i);
+      if (Opnd<T>::SPLIT)
+        *reinterpret_cast<uint4*>(dst_t + dst_lo + (int64_t)b * W + i) =
+            *reinterpret_cast<const uint4*>(src_t + src_lo + row * W + i);
+    }
+    return;
+  }
   for (int i = threadIdx.x; i < W; i += blockDim.x) {
     dst_f[b * dst_stride + i] = src_f[row * W + i];
     dst_t[(int64_t)b * W + i] = src_t[row * W + i];

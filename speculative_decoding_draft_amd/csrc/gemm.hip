@@ -784,7 +784,8 @@ __global__ __launch_bounds__(256) void argmax_combine(const float* part, int n_t
 // the vocabulary tiles, then the k best (val desc, id asc) merged from the
 // tiles' sorted lists. The row's records are first copied to LDS with
 // 16-byte loads, sixteen in flight per thread (in segments when they exceed
-// the buffer). A threshold T, the k-th largest of the tile maxima, bounds the
+// the 96 KB buffer; a 128k vocabulary's 1002 tiles of top-8 records fit in
+// one). A threshold T, the k-th largest of the tile maxima, bounds the
 // merge: k distinct values are >= T, so no value below T is among the k
 // best, and since every tile list is sorted a tile stops at its first
 // candidate under T. Each thread keeps its best candidates in registers as
@@ -793,7 +794,7 @@ __global__ __launch_bounds__(256) void argmax_combine(const float* part, int n_t
 // wave 0 merges the four lists.
 __global__ __launch_bounds__(256) void topk_combine(const float* part, int n_tiles, int M, int k,
                                                     int32_t* ids, float* logp) {
-  constexpr int KMAX = 16, BUF = 16384, NT = 256, NWV = NT / 64;
+  constexpr int KMAX = 16, BUF = 24576, NT = 256, NWV = NT / 64;
   __shared__ __attribute__((aligned(16))) float buf[BUF];
   __shared__ float s_red[2 * NWV];
   __shared__ uint64_t s_key[NWV * KMAX];
