@@ -317,9 +317,17 @@ constexpr int proj_lds_elems() {
 }
 
 // RS: the operand rows are RMSNorm numerators and a.rs holds their sums of
-// squares (RowScale); a separate instantiation, so projections without it
-// keep no registers for it.
-template <typename T, int MT, int NW, int CS, int NB, int EPI, bool RS = false>
+// squares (RowScale); separate instantiations, so projections without it
+// keep no registers for it. RS_REG: each lane holds its own rows' sums
+// through the main loop (4 MT registers); RS_LDS: one float4 per thread,
+// the factors published in LDS after the loop (4 registers, one barrier).
+// Same-box cycles: RS_LDS keeps the eight-wave SwiGLU at 108 rows within two
+// workgroups per CU (RS_REG took it from 114 to 131 registers and a second
+// round of workgroups: c2 batch 4 at 432 against 447 tokens/s); at five
+// m-tiles (one workgroup per CU) RS_REG measured faster (c4 gate|up 2.07
+// against 2.18 ms per cycle).
+enum { RS_NONE = 0, RS_REG = 1, RS_LDS = 2 };
+template <typename T, int MT, int NW, int CS, int NB, int EPI, int RS = RS_NONE>
 __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   using S = ProjShape<T, MT, NW, CS>;
   static_assert(NB == 1 || Opnd<T>::SPLIT, "several row blocks per wave: bf16 only");
@@ -347,11 +355,16 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
   } else {
     row0 = (tile * NW + wave) * WR;
   }
-  // RowScale: this lane's rows' sums of squares, requested before the main
-  // loop (they are the oldest loads, so the loop's waits cover them) and
-  // turned into the factor after it
-  float4 rsv[RS ? MT : 1];
-  if constexpr (RS) {
+  // RowScale: thread i < MP requests staged row i's sums of squares before
+  // the main loop (the oldest load, so the loop's waits cover it), turns
+  // them into the row's factor after it and publishes it in LDS: one float4
+  // per thread through the loop instead of one per m-tile and lane, so the
+  // instance keeps the registers (and workgroups per CU) of the plain one
+  float4 rsv[RS == RS_REG ? MT : 1];
+  rsv[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if constexpr (RS == RS_LDS) {
+    if ((int)threadIdx.x < S::MP) rsv[0] = ld4(a.rs + RS_SLICES * min(m0 + (int)threadIdx.x, a.M - 1));
+  } else if constexpr (RS == RS_REG) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) rsv[t] = ld4(a.rs + RS_SLICES * min(m0 + 16 * t + lr, a.M - 1));
   }
@@ -362,7 +375,17 @@ __global__ __launch_bounds__(NW * 64) void proj_kernel(ProjArgs a) {
     static_assert(NB == 1, "fp32 projections take one row block per wave");
     proj_core<T, MT, NW, CS>(b, row0, s_lo, s_hi, xs, acc[0]);
   }
-  if constexpr (RS) {
+  if constexpr (RS == RS_LDS) {
+    __shared__ float rsf[S::MP];
+    if ((int)threadIdx.x < S::MP) rsf[threadIdx.x] = row_scale(rsv[0], a.rs_h, a.rs_eps);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const float f = rsf[16 * t + lr];
+#pragma unroll
+      for (int jb = 0; jb < NB; ++jb) acc[jb][t] *= f;
+    }
+  } else if constexpr (RS == RS_REG) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const float f = row_scale(rsv[t], a.rs_h, a.rs_eps);
@@ -966,10 +989,11 @@ template <typename T, int MT, int NW, int CS, int NB, int EPI>
 hipError_t proj_dispatch(const ProjArgs& a, dim3 grid, dim3 block, hipStream_t st, const KTiming* tm) {
   if constexpr (Opnd<T>::SPLIT) {
     if (a.rs) {
+      constexpr int R = MT >= 5 ? RS_REG : RS_LDS;
       if (tm)
-        hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI, true>), grid, block, 0, st, tm->start, tm->stop, 0, a);
+        hipExtLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI, R>), grid, block, 0, st, tm->start, tm->stop, 0, a);
       else
-        hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI, true>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((proj_kernel<T, MT, NW, CS, NB, EPI, R>), grid, block, 0, st, a);
       return hipGetLastError();
     }
   } else {
