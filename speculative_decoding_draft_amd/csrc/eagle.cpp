@@ -652,9 +652,10 @@ RowScale xop_scale(const eagle_ctx* c) {
 }
 
 // One decoder layer over M rows (the rows of every sequence of `ln`). On
-// entry xop holds the normed layer input (row width kin); on exit the
-// down-projection partials are pending in gpart (*s_down planes) for the
-// caller's resnorm.
+// entry xop holds the normed layer input (row width kin), or its RMSNorm
+// numerator with xrs set (the q|k|v projection then applies the factor); on
+// exit the down-projection partials are pending in gpart (*s_down planes)
+// for the caller's resnorm.
 eagle_status layer_core(eagle_ctx* c, const eagle_ctx::LW& w, int kin, int M, float* h,
                         const int32_t* pos, const int32_t* slot, KVView kv, RowVis vis,
                         const Lanes& ln, bool target, int* s_down) {
