@@ -58,6 +58,39 @@ eagle_status eagle_op_linear(int32_t dtype, int32_t epilogue, const void* x, con
                              int32_t M, int32_t N, int32_t K, void* workspace, uint64_t ws_bytes,
                              void* stream);
 
+/* Workspace bytes eagle_op_norm_linear needs for this shape (0 for a bad
+ * shape). It holds the normed operand, the per-row sums of squares and the
+ * projection's partial planes of one call; every byte a call reads there it
+ * has written first. */
+uint64_t eagle_op_norm_linear_workspace(int32_t epilogue, int32_t M, int32_t N, int32_t H);
+
+/* The pre-norm step of a decoder layer in the Llama layout the models follow
+ * (eagle_config): the residual update, RMSNorm, and the projection that
+ * reads the normed rows -- the q|k|v and gate|up inputs of every target and
+ * draft layer ("Lesson 13.11 - EAGLE", section "The big idea": the draft
+ * head is one such decoder layer). bf16, in the form the layers run it: the
+ * norm is spread over four workgroups per row, which write gain * h and
+ * each quarter row's sum of squares, and the projection multiplies its
+ * output rows by the rows' RMSNorm factors.
+ *   h: [M, H] fp32 residual rows, updated in place:
+ *      h += part[0] + ... + part[S-1]  (planes of [M, H] fp32, plane s at
+ *      part + s*M*H, added in plane order; S may be 0, then part may be NULL)
+ *   gain: [H] fp32. w: bf16 packed by eagle_op_pack, [N, H] (EPI_SWIGLU:
+ *      [2N, H], the N gate rows then the N up rows).
+ *   x = RMSNorm(h) * gain, RMSNorm(h) = h / sqrt(mean(h^2) + eps)
+ *   EPI_STORE : y fp32 [M, N] = x w^T
+ *   EPI_SWIGLU: y [M, N] bf16 operand (hi plane, then the lo plane M*N
+ *               elements later) = silu(x wg^T) * (x wu^T)
+ * Accumulation is fp32 in a fixed order, so results repeat bit for bit.
+ * Requires M >= 1, N >= 1 (EPI_SWIGLU: a multiple of 16) and H a multiple
+ * of 1024, at most 16384. EAGLE_E_INVALID on bad sizes or a NULL pointer,
+ * EAGLE_E_BUFFER if the workspace is too small, EAGLE_E_HIP on a launch
+ * failure. */
+eagle_status eagle_op_norm_linear(int32_t epilogue, float* h, const float* part, int32_t S,
+                                  const float* gain, float eps, const void* w, void* y, int32_t M,
+                                  int32_t N, int32_t H, void* workspace, uint64_t ws_bytes,
+                                  void* stream);
+
 /* Largest workspace eagle_op_linear_noalloc can serve (32 MiB). */
 #define EAGLE_OP_NOALLOC_SCRATCH_BYTES (32ull << 20)
 

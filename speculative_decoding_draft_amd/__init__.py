@@ -376,6 +376,34 @@ def op_linear(dtype: int, epilogue: int, x, w, y, M: int, N: int, K: int, worksp
         raise EagleError(rc, "eagle_op_linear")
 
 
+def op_norm_linear_workspace(epilogue: int, M: int, N: int, H: int) -> int:
+    L = lib()
+    L.eagle_op_norm_linear_workspace.argtypes = [i32, i32, i32, i32]
+    L.eagle_op_norm_linear_workspace.restype = u64
+    return int(L.eagle_op_norm_linear_workspace(epilogue, M, N, H))
+
+
+def op_norm_linear(epilogue: int, h, part, S: int, gain, eps: float, w, y, M: int, N: int, H: int,
+                   workspace, stream=None):
+    """eagle_op_norm_linear on torch tensors (device pointers): h += planes,
+    then the projection of RMSNorm(h) * gain (bf16)."""
+    L = lib()
+    L.eagle_op_norm_linear.argtypes = [i32, ctypes.c_void_p, ctypes.c_void_p, i32, ctypes.c_void_p,
+                                       f32, ctypes.c_void_p, ctypes.c_void_p, i32, i32, i32,
+                                       ctypes.c_void_p, u64, ctypes.c_void_p]
+    need = op_norm_linear_workspace(epilogue, M, N, H)
+    if need == 0:
+        raise EagleError(1, "eagle_op_norm_linear: bad shape")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        raise EagleError(4, f"norm_linear workspace needs {need} bytes")
+    st = stream.cuda_stream if stream is not None else _torch_stream()
+    rc = L.eagle_op_norm_linear(epilogue, h.data_ptr(), part.data_ptr() if part is not None else None,
+                                S, gain.data_ptr(), eps, w.data_ptr(), y.data_ptr(), M, N, H,
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(), st)
+    if rc:
+        raise EagleError(rc, "eagle_op_norm_linear")
+
+
 NOALLOC_SCRATCH_BYTES = 32 << 20   # EAGLE_OP_NOALLOC_SCRATCH_BYTES
 
 

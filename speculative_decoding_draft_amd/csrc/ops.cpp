@@ -69,6 +69,53 @@ eagle_status eagle_op_linear(int32_t dtype, int32_t epi, const void* x, const vo
   return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
 }
 
+uint64_t eagle_op_norm_linear_workspace(int32_t epi, int32_t M, int32_t N, int32_t H) {
+  if (epi != EAGLE_EPI_STORE && epi != EAGLE_EPI_SWIGLU) return 0;
+  if (!linear_ok(EAGLE_BF16, epi, M, N, H) || !resnorm_slices_fit(H)) return 0;
+  const uint64_t x = align256((uint64_t)M * H * 2 * 2);   // hi and lo planes
+  const uint64_t ss = align256((uint64_t)M * RS_SLICES * 4);
+  uint64_t planes;
+  if (epi == EAGLE_EPI_SWIGLU) {
+    planes = swiglu_by_planes(EAGLE_BF16, M)
+                 ? gemm_part_floats(gemm_plan(M, 2 * N, H, EAGLE_BF16, EPI_PART), 2 * N, M) * 4
+                 : 0;
+  } else {
+    planes = gemm_part_floats(gemm_plan(M, N, H, EAGLE_BF16, EPI_PART), N, M) * 4;
+  }
+  return x + ss + align256(planes);
+}
+
+eagle_status eagle_op_norm_linear(int32_t epi, float* h, const float* part, int32_t S,
+                                  const float* gain, float eps, const void* w, void* y, int32_t M,
+                                  int32_t N, int32_t H, void* workspace, uint64_t ws_bytes,
+                                  void* stream) {
+  const uint64_t need = eagle_op_norm_linear_workspace(epi, M, N, H);
+  if (need == 0 || S < 0 || !h || !gain || !w || !y || (S > 0 && !part)) return EAGLE_E_INVALID;
+  if (!workspace || ws_bytes < need) return EAGLE_E_BUFFER;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  void* xop = ws;
+  float* ss = (float*)(ws + align256((uint64_t)M * H * 2 * 2));
+  float* planes = (float*)((char*)ss + align256((uint64_t)M * RS_SLICES * 4));
+  const int64_t xlo = (int64_t)M * H;
+  hipError_t e = launch_resnorm_slices(EAGLE_BF16, h, H, M, part, S, (int64_t)M * H, 0, gain, xop,
+                                       xlo, ss, st);
+  RowScale rs;
+  rs.ss = ss;
+  rs.H = H;
+  rs.eps = eps;
+  if (e == hipSuccess && epi == EAGLE_EPI_SWIGLU) {
+    e = launch_gemm(EAGLE_BF16, EPI_SWIGLU, w, xop, xlo, M, N, H, planes, 2 * N, y, (int64_t)M * N,
+                    nullptr, st, nullptr, rs);
+  } else if (e == hipSuccess) {
+    int SP = 1;
+    e = launch_gemm(EAGLE_BF16, EPI_PART, w, xop, xlo, M, N, H, planes, N, nullptr, 0, &SP, st,
+                    nullptr, rs);
+    if (e == hipSuccess) e = launch_sum_planes(planes, SP, (int64_t)M * N, M, N, (float*)y, 0, st);
+  }
+  return e == hipSuccess ? EAGLE_OK : EAGLE_E_HIP;
+}
+
 uint64_t eagle_op_lmhead_workspace(int32_t M, int32_t V, int32_t k) {
   if (M < 1 || V < 1 || k < 0 || k > EAGLE_MAX_TOPK) return 0;
   return align256(lmhead_part_floats(M, V, k) * 4);

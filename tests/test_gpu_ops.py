@@ -202,3 +202,71 @@ def test_lmhead_argmax(dtype, M, V, H):
     ok = ref_margin > 1e-4
     assert np.array_equal(g[ok], np.argmax(lg, axis=1)[ok])
     assert np.allclose(mg, ref_margin, atol=2e-4)
+
+
+# residual update + sliced RMSNorm + the projection that applies the rows'
+# RMSNorm factors (eagle_op_norm_linear), one case per launch form the
+# decoder layers take: (epilogue, M, N, H, planes)
+NORM_LINEAR = [
+    (0, 27, 12288, 4096, 16),   # 27 verify rows: six-wave q|k|v plan, factors through LDS
+    (0, 27, 4096, 4096, 8),     # eight waves, eight splits
+    (0, 61, 12288, 4096, 8),    # four m-tiles
+    (0, 65, 6144, 4096, 5),     # five m-tiles: factors in registers
+    (0, 108, 4096, 4096, 2),    # two 64-row m-chunks
+    (0, 216, 12288, 4096, 4),   # many rows: rows_kernel
+    (0, 61, 10240, 8192, 3),    # H = 8192: 512-thread slices
+    (0, 10, 12288, 4096, 0),    # no planes (the embedding's norm)
+    (2, 27, 11008, 4096, 8),    # SwiGLU, six waves
+    (2, 65, 14336, 4096, 8),    # SwiGLU, five m-tiles
+    (2, 108, 11008, 4096, 8),   # SwiGLU, two m-chunks of eight waves
+    (2, 216, 11008, 4096, 16),  # SwiGLU over planes (rows_kernel + SiLU pass)
+]
+
+
+@pytest.mark.parametrize("epi,M,N,H,S", NORM_LINEAR)
+def test_norm_linear(epi, M, N, H, S):
+    from oracle.numerics import rmsnorm, silu
+    print(f"norm_linear epi={epi} M={M} N={N} H={H} S={S}", flush=True)
+    gen = torch.Generator().manual_seed(M * 17 + N + H + S + epi)
+    eps = 1e-5
+    h0 = torch.randn((M, H), generator=gen)
+    part = torch.randn((max(S, 1), M, H), generator=gen) * 0.25
+    gain = 1.0 + 0.1 * torch.randn(H, generator=gen)
+    rows = 2 * N if epi == 2 else N
+    w = _rand((rows, H), gen, 0.02, BF16)
+    h_ref = h0.double().numpy() + part[:S].double().numpy().sum(axis=0) if S else h0.double().numpy()
+    x = rmsnorm(h_ref, gain.double().numpy(), eps)
+    wt = w.double().numpy()
+    if epi == 2:
+        ref = silu(x @ wt[:N].T) * (x @ wt[N:].T)
+    else:
+        ref = x @ wt.T
+    wd = _dev_weight(w, BF16)
+    ws = _ws(E.op_norm_linear_workspace(epi, M, N, H))
+    partd, gaind = part.cuda(), gain.cuda()
+    outs = []
+    for _ in range(2):   # the same bits on a second run
+        hd = h0.clone().cuda()
+        if epi == 2:
+            y = torch.zeros(2 * M * N, dtype=torch.bfloat16, device="cuda")
+        else:
+            y = torch.zeros(M, N, device="cuda")
+        E.op_norm_linear(epi, hd, partd if S else None, S, gaind, eps, wd, y, M, N, H, ws)
+        torch.cuda.synchronize()
+        outs.append((hd.cpu(), y.cpu()))
+    h_got = outs[0][0].double().numpy()
+    assert np.abs(h_got - h_ref).max() <= 1e-6 * np.abs(h_ref).max()
+    if epi == 2:
+        got = _from_planes(outs[0][1], (M, N), BF16)
+        tol = 1e-5 * np.abs(ref) + 1e-4 * np.abs(ref).max()
+        assert np.all(np.abs(got - ref) <= tol)
+    else:
+        assert _rel(outs[0][1].double().numpy(), ref) < 1e-4
+    assert torch.equal(outs[0][1], outs[1][1]) and torch.equal(outs[0][0], outs[1][0])
+
+
+def test_norm_linear_rejects_bad_shapes():
+    assert E.op_norm_linear_workspace(0, 27, 4096, 4000) == 0    # H not a multiple of 1024
+    assert E.op_norm_linear_workspace(1, 27, 4096, 4096) == 0    # no EPI_ADD form
+    assert E.op_norm_linear_workspace(2, 27, 4090, 4096) == 0    # SwiGLU N not a multiple of 16
+    assert E.op_norm_linear_workspace(0, 27, 4096, 4096) > 0
