@@ -216,10 +216,13 @@ NORM_LINEAR = [
     (0, 216, 12288, 4096, 4),   # many rows: rows_kernel
     (0, 61, 10240, 8192, 3),    # H = 8192: 512-thread slices
     (0, 10, 12288, 4096, 0),    # no planes (the embedding's norm)
+    (0, 1, 4096, 4096, 2),      # one row (the draft's first pass)
+    (0, 27, 4100, 4096, 8),     # ragged output rows (not a whole 16-row block)
     (2, 27, 11008, 4096, 8),    # SwiGLU, six waves
     (2, 65, 14336, 4096, 8),    # SwiGLU, five m-tiles
     (2, 108, 11008, 4096, 8),   # SwiGLU, two m-chunks of eight waves
     (2, 216, 11008, 4096, 16),  # SwiGLU over planes (rows_kernel + SiLU pass)
+    (2, 1, 11008, 4096, 8),     # SwiGLU, one row
 ]
 
 
