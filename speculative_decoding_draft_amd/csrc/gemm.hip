@@ -945,10 +945,9 @@ constexpr int KIND_HEAD = 3;
 template <int MT, int KIND> struct Cfg { static constexpr int NW = 8, CS = 4, NB = 1; };
 template <> struct Cfg<1, EPI_PART> { static constexpr int NW = 4, CS = 4, NB = 1; };
 template <> struct Cfg<1, EPI_SWIGLU> { static constexpr int NW = 8, CS = 4, NB = 1; };
-template <> struct Cfg<1, KIND_HEAD> { static constexpr int NW = 4, CS = 16, NB = 1; };
+template <> struct Cfg<1, KIND_HEAD> { static constexpr int NW = 8, CS = 8, NB = 1; };
 template <> struct Cfg<2, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<2, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
-template <> struct Cfg<2, KIND_HEAD> { static constexpr int NW = 4, CS = 8, NB = 1; };
 template <> struct Cfg<3, EPI_PART> { static constexpr int NW = 4, CS = 2, NB = 1; };
 template <> struct Cfg<3, EPI_SWIGLU> { static constexpr int NW = 8, CS = 2, NB = 1; };
 template <> struct Cfg<4, EPI_PART> { static constexpr int NW = 8, CS = 2, NB = 1; };
@@ -1079,17 +1078,26 @@ hipError_t launch_rows_mt(const ProjArgs& a, int tiles, int m_chunks, hipStream_
   return hipGetLastError();
 }
 
-template <typename T, bool TOPK, int MT>
+template <typename T, bool TOPK, int MT, int NW = Cfg<MT, KIND_HEAD>::NW, int CS = Cfg<MT, KIND_HEAD>::CS>
 hipError_t launch_head_mt(const HeadArgs& h, int tiles, hipStream_t st) {
-  constexpr int NW = Cfg<MT, KIND_HEAD>::NW, CS = Cfg<MT, KIND_HEAD>::CS;
   hipLaunchKernelGGL((lmhead_kernel<T, MT, NW, CS, TOPK>), dim3(tiles), dim3(NW * 64), 0, st, h);
   return hipGetLastError();
 }
 
+// LM-head tiles. Every workgroup stages all of the call's activation rows
+// over the full hidden width, so these reads grow with the number of
+// workgroups and of distinct rows. Up to HEAD_FEW_ROWS rows they mostly hit
+// in the vector cache and four-wave tiles of 64 vocabulary rows with deep
+// chunks stream the weight best; above that, eight-wave tiles of 128
+// vocabulary rows halve the activation reads per weight byte and the merge's
+// per-tile records.
+constexpr int HEAD_FEW_ROWS = 4;
+
 template <typename T, bool TOPK>
 hipError_t launch_head_t(int mt, const HeadArgs& h, int tiles, hipStream_t st) {
   switch (mt) {
-    case 1: return launch_head_mt<T, TOPK, 1>(h, tiles, st);
+    case 1: return h.p.M <= HEAD_FEW_ROWS ? launch_head_mt<T, TOPK, 1, 4, 16>(h, tiles, st)
+                                          : launch_head_mt<T, TOPK, 1>(h, tiles, st);
     case 2: return launch_head_mt<T, TOPK, 2>(h, tiles, st);
     case 3: return launch_head_mt<T, TOPK, 3>(h, tiles, st);
     case 4: return launch_head_mt<T, TOPK, 4>(h, tiles, st);
@@ -1097,7 +1105,7 @@ hipError_t launch_head_t(int mt, const HeadArgs& h, int tiles, hipStream_t st) {
   }
 }
 
-int head_rows(int M) { return 16 * waves_for(M > 64 ? 5 : (M + 15) / 16, KIND_HEAD); }
+int head_rows(int M) { return M <= HEAD_FEW_ROWS ? 64 : 16 * waves_for(M > 64 ? 5 : (M + 15) / 16, KIND_HEAD); }
 
 }  // namespace
 

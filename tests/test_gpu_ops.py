@@ -157,7 +157,9 @@ def test_swiglu(dtype, M, N, K):
 @pytest.mark.parametrize("dtype,M,V,H,k", [(BF16, 1, 32000, 4096, 10), (BF16, 10, 32000, 4096, 10),
                                            (BF16, 8, 5000, 1024, 8), (F32, 4, 1024, 256, 4),
                                            (F32, 1, 1000, 256, 16), (BF16, 40, 32000, 4096, 10),
-                                           (F32, 70, 2000, 256, 5), (BF16, 90, 5000, 1024, 16)])
+                                           (F32, 70, 2000, 256, 5), (BF16, 90, 5000, 1024, 16),
+                                           (BF16, 4, 3001, 1024, 7), (BF16, 5, 3001, 1024, 7),
+                                           (BF16, 20, 32000, 4096, 10), (F32, 12, 1500, 256, 6)])
 def test_lmhead_topk(dtype, M, V, H, k):
     print(f"topk dtype={dtype} M={M} V={V} H={H} k={k}", flush=True)
     gen = torch.Generator().manual_seed(M + V + H + k)
@@ -182,7 +184,8 @@ def test_lmhead_topk(dtype, M, V, H, k):
 
 @pytest.mark.parametrize("dtype,M,V,H", [(BF16, 61, 32000, 4096), (BF16, 100, 3000, 1024),
                                          (F32, 17, 1024, 256), (BF16, 33, 1000, 512),
-                                         (F32, 75, 777, 256)])
+                                         (F32, 75, 777, 256), (BF16, 27, 32000, 4096),
+                                         (BF16, 3, 2000, 512), (F32, 9, 999, 256)])
 def test_lmhead_argmax(dtype, M, V, H):
     print(f"argmax dtype={dtype} M={M} V={V} H={H}", flush=True)
     gen = torch.Generator().manual_seed(M * V + H)
