@@ -159,7 +159,8 @@ def test_swiglu(dtype, M, N, K):
                                            (F32, 1, 1000, 256, 16), (BF16, 40, 32000, 4096, 10),
                                            (F32, 70, 2000, 256, 5), (BF16, 90, 5000, 1024, 16),
                                            (BF16, 4, 3001, 1024, 7), (BF16, 5, 3001, 1024, 7),
-                                           (BF16, 20, 32000, 4096, 10), (F32, 12, 1500, 256, 6)])
+                                           (BF16, 20, 32000, 4096, 10), (F32, 12, 1500, 256, 6),
+                                           (BF16, 80, 32000, 4096, 10), (BF16, 10, 32000, 8192, 10)])
 def test_lmhead_topk(dtype, M, V, H, k):
     print(f"topk dtype={dtype} M={M} V={V} H={H} k={k}", flush=True)
     gen = torch.Generator().manual_seed(M + V + H + k)
