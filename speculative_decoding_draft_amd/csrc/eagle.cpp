@@ -360,7 +360,6 @@ uint64_t carve_lane(const Derived& z, char* base, Lane* l) {
   LTAKE(t.srcrow, int32_t, TREE_MAXN);
   LTAKE(t.rank, int32_t, TREE_MAXN);
   LTAKE(t.row_of_node, int32_t, TREE_MAXN);
-  LTAKE(t.v_row_of_node, int32_t, TREE_MAXN);
   LTAKE(t.logv, float, TREE_MAXN);
   LTAKE(t.logp, float, TREE_MAXN);
   LTAKE(t.counts, int32_t, 8);

@@ -189,7 +189,7 @@ hipError_t launch_kv_compact(int dtype, KVView layer0, int64_t layer_elems, int 
 
 // Device-side tree state (all arrays in the scratch buffer).
 struct TreeDev {
-  int32_t *tok, *parent, *depth, *srcrow, *rank, *row_of_node, *v_row_of_node;  // [TREE_MAXN]
+  int32_t *tok, *parent, *depth, *srcrow, *rank, *row_of_node;  // [TREE_MAXN]
   float *logv, *logp;                                                           // [TREE_MAXN]
   int32_t* counts;     // [0] nodes, [1] rows of the next pass, [2] tree rows used, [3] verify rows
   int32_t* exp_nodes;  // [TREE_MAXEXP] nodes expanded by the next pass, in order

@@ -5,10 +5,16 @@
 //   expansion: (log V desc, generation asc)
 //   rerank:    (log V desc, depth asc, generation asc)
 //   rows:      (depth asc, rerank order)
+#include "eagle.h"
 #include "common.h"
 #include "kernels.h"
 
 namespace {
+
+// the rerank's LDS arrays hold every node a cycle can generate and every
+// verify row a cycle can have
+static_assert(EAGLE_MAX_NODES <= TREE_MAXN && EAGLE_MAX_STATIC <= TREE_MAXN, "node arrays");
+static_assert(EAGLE_MAX_VERIFY <= TREE_MAXROWS && EAGLE_MAX_STATIC < TREE_MAXROWS, "row arrays");
 
 // Sequence b's tree state: every array of sequence 0's shifted by b * bytes.
 __device__ __forceinline__ TreeDev tree_lane(TreeDev t, int b, int64_t bytes) {
@@ -19,7 +25,6 @@ __device__ __forceinline__ TreeDev tree_lane(TreeDev t, int b, int64_t bytes) {
   t.srcrow = lane_at(t.srcrow, b, bytes);
   t.rank = lane_at(t.rank, b, bytes);
   t.row_of_node = lane_at(t.row_of_node, b, bytes);
-  t.v_row_of_node = lane_at(t.v_row_of_node, b, bytes);
   t.logv = lane_at(t.logv, b, bytes);
   t.logp = lane_at(t.logp, b, bytes);
   t.counts = lane_at(t.counts, b, bytes);
@@ -61,6 +66,8 @@ __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams 
                                                           int64_t ids_stride) {
   __shared__ int s_base, s_nrows, s_nnew, s_nsel, s_tbase;
   __shared__ int sel[TREE_MAXEXP];
+  // expansion keys of the new generation, ranked from LDS
+  __shared__ uint32_t s_key[TREE_MAXEXP * EAGLE_MAX_TOPK];
   const int tid = threadIdx.x;
   // this workgroup's sequence
   const int b = blockIdx.x;
@@ -92,14 +99,16 @@ __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams 
       const int gen = base + e;
       const int par = (pass == 1) ? -1 : t.exp_nodes[i];
       const float lp = lps[i * k + r];
+      const float lv = (par < 0) ? lp : (t.logv[par] + lp);
       t.tok[gen] = ids[i * k + r];
       t.parent[gen] = par;
       t.depth[gen] = pass;
       t.rank[gen] = r;
       t.logp[gen] = lp;
-      t.logv[gen] = (par < 0) ? lp : (t.logv[par] + lp);
+      t.logv[gen] = lv;
       t.srcrow[gen] = (par < 0) ? 0 : 1 + t.row_of_node[par];
       t.row_of_node[gen] = -1;
+      s_key[e] = ~float_key(lv);
     }
     if (tid == 0) { s_nnew = nrows * k; t.counts[0] = base + nrows * k; }
   } else {
@@ -133,14 +142,13 @@ __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams 
     const int nnew = s_nnew;
     if (tid == 0) s_nsel = min(p.k_e, nnew);
     for (int e = tid; e < nnew; e += blockDim.x) {
-      const int gi = base + e;
-      const uint32_t ki = ~float_key(t.logv[gi]);
+      const uint32_t ki = s_key[e];
       int rank = 0;
       for (int f = 0; f < nnew; ++f) {
-        const uint32_t kf = ~float_key(t.logv[base + f]);
+        const uint32_t kf = s_key[f];
         rank += (kf < ki) || (kf == ki && f < e);
       }
-      if (rank < p.k_e) sel[rank] = gi;
+      if (rank < p.k_e) sel[rank] = base + e;
     }
   } else {
     if (tid == 0) s_nsel = t.s_nexp[pass];
@@ -176,13 +184,14 @@ __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams 
   }
 }
 
-// masks for verify rows whose parents precede them (level order not needed)
-__device__ void build_masks(TreeDev& t, int n, int ctx) {
+// masks for verify rows whose parents precede them (level order not needed);
+// vpar: the rows' parent rows (LDS in the rerank, the device array otherwise)
+__device__ __forceinline__ void build_masks(TreeDev& t, int n, int ctx, const int* vpar) {
   // depth by pointer chasing (n <= 128, depth <= 16)
   for (int r = threadIdx.x; r < n; r += blockDim.x) {
     uint64_t m[2] = {0ull, 0ull};
     int d = 0;
-    for (int a = r; a >= 0; a = t.v_parent[a]) {
+    for (int a = r; a >= 0; a = vpar[a]) {
       set_bit(m, a);
       if (a != 0) ++d;
       if (a == 0) break;
@@ -199,7 +208,8 @@ __device__ void build_masks(TreeDev& t, int n, int ctx) {
 __global__ __launch_bounds__(1024) void tree_finalize_kernel(TreeDev t, TreeParams p, int ctx,
                                                              const int32_t* root_token, Lanes ln) {
   __shared__ uint64_t keys[TREE_MAXN];
-  __shared__ int kept[TREE_MAXROWS];
+  __shared__ int kept[TREE_MAXROWS], kdep[TREE_MAXROWS], vpar[TREE_MAXROWS];
+  __shared__ int row_of[TREE_MAXN];   // verify row of each kept node, -1 otherwise
   __shared__ int s_n, s_m;
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
@@ -213,17 +223,21 @@ __global__ __launch_bounds__(1024) void tree_finalize_kernel(TreeDev t, TreePara
   }
   __syncthreads();
   const int n = s_n, m = s_m;
+  for (int i = tid; i < n; i += blockDim.x) row_of[i] = -1;
   if (p.dynamic) {
-    for (int i = tid; i < TREE_MAXN; i += blockDim.x) {
+    // bitonic sort, ascending, of the first power of two >= n keys (padding
+    // keys ~0 sort last, as they would in any longer sort)
+    int np2 = 2;
+    while (np2 < n) np2 <<= 1;
+    for (int i = tid; i < np2; i += blockDim.x) {
       keys[i] = (i < n) ? (((uint64_t)(~float_key(t.logv[i])) << 32) |
                            ((uint64_t)t.depth[i] << 20) | (uint64_t)i)
                         : ~0ull;
     }
     __syncthreads();
-    // bitonic sort, ascending
-    for (int size = 2; size <= TREE_MAXN; size <<= 1) {
+    for (int size = 2; size <= np2; size <<= 1) {
       for (int stride = size >> 1; stride > 0; stride >>= 1) {
-        for (int i = tid; i < TREE_MAXN; i += blockDim.x) {
+        for (int i = tid; i < np2; i += blockDim.x) {
           const int j = i ^ stride;
           if (j > i) {
             const bool up = (i & size) == 0;
@@ -239,37 +253,40 @@ __global__ __launch_bounds__(1024) void tree_finalize_kernel(TreeDev t, TreePara
     for (int i = tid; i < m; i += blockDim.x) kept[i] = i;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += blockDim.x) t.v_row_of_node[i] = -1;
+  for (int i = tid; i < m; i += blockDim.x) kdep[i] = t.depth[kept[i]];
   __syncthreads();
   // row of kept node i: 1 + #{kept j with (depth, order) smaller}
   for (int i = tid; i < m; i += blockDim.x) {
-    const int di = t.depth[kept[i]];
+    const int di = kdep[i];
     int c = 0;
     for (int j = 0; j < m; ++j) {
-      const int dj = t.depth[kept[j]];
+      const int dj = kdep[j];
       c += (dj < di) || (dj == di && j < i);
     }
-    t.v_row_of_node[kept[i]] = 1 + c;
+    row_of[kept[i]] = 1 + c;
   }
   __syncthreads();
   for (int i = tid; i < m; i += blockDim.x) {
     const int nd = kept[i];
-    const int r = t.v_row_of_node[nd];
+    const int r = row_of[nd];
     const int par = t.parent[nd];
+    const int pr = (par < 0) ? 0 : row_of[par];
     t.v_tok[r] = t.tok[nd];
     t.v_node[r] = nd;
     t.v_logv[r] = t.logv[nd];
-    t.v_parent[r] = (par < 0) ? 0 : t.v_row_of_node[par];
+    t.v_parent[r] = pr;
+    vpar[r] = pr;
   }
   if (tid == 0) {
     t.v_tok[0] = *root_token;
     t.v_node[0] = -1;
     t.v_logv[0] = 0.f;
     t.v_parent[0] = -1;
+    vpar[0] = -1;
     t.counts[3] = 1 + m;
   }
   __syncthreads();
-  build_masks(t, 1 + m, ctx);
+  build_masks(t, 1 + m, ctx, vpar);
 }
 
 __global__ __launch_bounds__(128) void tree_masks_kernel(TreeDev t, int n_rows, int ctx,
@@ -285,7 +302,7 @@ __global__ __launch_bounds__(128) void tree_masks_kernel(TreeDev t, int n_rows, 
     t.counts[3] = n_rows;
   }
   __syncthreads();
-  build_masks(t, n_rows, ctx);
+  build_masks(t, n_rows, ctx, t.v_parent);
 }
 
 // Walks the verified tree from the root: at each step the child whose token
