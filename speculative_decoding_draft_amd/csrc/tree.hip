@@ -66,8 +66,13 @@ __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams 
                                                           int64_t ids_stride) {
   __shared__ int s_base, s_nrows, s_nnew, s_nsel, s_tbase;
   __shared__ int sel[TREE_MAXEXP];
-  // expansion keys of the new generation, ranked from LDS
-  __shared__ uint32_t s_key[TREE_MAXEXP * EAGLE_MAX_TOPK];
+  // the new generation (dynamic tree) in LDS: expansion keys, ranked from
+  // here, and the token, source row and source-row mask the next pass's rows
+  // take, so no row waits on a device re-read
+  constexpr int NNEW = TREE_MAXEXP * EAGLE_MAX_TOPK;
+  __shared__ uint32_t s_key[NNEW];
+  __shared__ int s_tok[NNEW], s_src[NNEW];
+  __shared__ uint64_t s_pm[2 * NNEW];
   const int tid = threadIdx.x;
   // this workgroup's sequence
   const int b = blockIdx.x;
@@ -100,15 +105,23 @@ __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams 
       const int par = (pass == 1) ? -1 : t.exp_nodes[i];
       const float lp = lps[i * k + r];
       const float lv = (par < 0) ? lp : (t.logv[par] + lp);
-      t.tok[gen] = ids[i * k + r];
+      const int tok = ids[i * k + r];
+      const int src = (par < 0) ? 0 : 1 + t.row_of_node[par];
+      uint64_t m0 = 0ull, m1 = 0ull;
+      if (src > 0) { m0 = t.tmask[2 * (src - 1)]; m1 = t.tmask[2 * (src - 1) + 1]; }
+      t.tok[gen] = tok;
       t.parent[gen] = par;
       t.depth[gen] = pass;
       t.rank[gen] = r;
       t.logp[gen] = lp;
       t.logv[gen] = lv;
-      t.srcrow[gen] = (par < 0) ? 0 : 1 + t.row_of_node[par];
+      t.srcrow[gen] = src;
       t.row_of_node[gen] = -1;
       s_key[e] = ~float_key(lv);
+      s_tok[e] = tok;
+      s_src[e] = src;
+      s_pm[2 * e] = m0;
+      s_pm[2 * e + 1] = m1;
     }
     if (tid == 0) { s_nnew = nrows * k; t.counts[0] = base + nrows * k; }
   } else {
@@ -162,16 +175,28 @@ __global__ __launch_bounds__(256) void tree_append_kernel(TreeDev t, TreeParams 
   for (int i = tid; i < nsel; i += blockDim.x) {
     const int e = sel[i];
     const int tr = s_tbase + i;
+    int tok, src, dep;
+    uint64_t m[2] = {0ull, 0ull};
+    if (p.dynamic) {   // a node of the generation written above
+      const int le = e - base;
+      tok = s_tok[le];
+      src = s_src[le];
+      dep = pass;
+      m[0] = s_pm[2 * le];
+      m[1] = s_pm[2 * le + 1];
+    } else {
+      tok = t.tok[e];
+      src = t.srcrow[e];
+      dep = t.depth[e];
+      if (src > 0) { m[0] = t.tmask[2 * (src - 1)]; m[1] = t.tmask[2 * (src - 1) + 1]; }
+    }
     t.exp_nodes[i] = e;
     t.row_of_node[e] = tr;
-    t.row_tok[i] = t.tok[e];
-    t.row_src[i] = t.srcrow[e];
-    t.row_pos[i] = ctx + t.depth[e];
+    t.row_tok[i] = tok;
+    t.row_src[i] = src;
+    t.row_pos[i] = ctx + dep;
     t.row_slot[i] = ctx + 1 + tr;
     t.row_prehi[i] = ctx + 1;
-    uint64_t m[2] = {0ull, 0ull};
-    const int src = t.srcrow[e];
-    if (src > 0) { m[0] = t.tmask[2 * (src - 1)]; m[1] = t.tmask[2 * (src - 1) + 1]; }
     set_bit(m, tr);
     t.tmask[2 * tr] = m[0];
     t.tmask[2 * tr + 1] = m[1];
